@@ -1,0 +1,204 @@
+// Joint Lagrangian rank/bit allocation (Sec. 3, Eqs. (1)-(4), "Solving the allocation").
+//
+// One workgroup: (1) suffix sums of every cell's token and feature spectra (sequential from
+// the last entry, fp64), (2) the distortion/byte table over the (b, r_T, r_d) grid of every cell,
+// e = eps^2(b) * ((tailT[r_T] + tailD[r_d]) / ||X||^2) and s = Eq. (1) bytes (exact integers),
+// (3) geometric bisection on lambda with an exact per-cell argmin of e + lambda s (ties: smaller
+// s, then b, r_T, r_d).  Every floating-point operation is explicitly rounded (no contraction) so
+// the result is reproducible and independent of the launch shape.
+#include <math.h>
+
+#include "common.hpp"
+#include "alloc.hpp"
+
+namespace jolt {
+
+namespace {
+
+constexpr int AT = 1024;
+
+struct Best {
+  double cost;
+  long long s;
+  int b, rT, rd, idx;
+};
+
+__device__ __forceinline__ bool less_than(const Best &x, const Best &y) {
+  if (x.cost != y.cost) return x.cost < y.cost;
+  if (x.s != y.s) return x.s < y.s;
+  if (x.b != y.b) return x.b < y.b;
+  if (x.rT != y.rT) return x.rT < y.rT;
+  return x.rd < y.rd;
+}
+
+__device__ Best shfl_best(const Best &v, int o) {
+  Best r;
+  r.cost = __shfl_xor(v.cost, o, 64);
+  r.s = __shfl_xor(v.s, o, 64);
+  r.b = __shfl_xor(v.b, o, 64);
+  r.rT = __shfl_xor(v.rT, o, 64);
+  r.rd = __shfl_xor(v.rd, o, 64);
+  r.idx = __shfl_xor(v.idx, o, 64);
+  return r;
+}
+
+__global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
+  __shared__ int pick[AllocArgs::kMaxCells];
+  __shared__ double lam_s;
+  __shared__ int done_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = AT / 64;
+  const int nc = a.n_cells, nb = a.n_bits, nT = a.n_rT, nD = a.n_rd;
+  const int per = nb * nT * nD;
+
+  // (1) suffix sums at the grid ranks (one thread per cell and mode; sequential order)
+  for (int w = tid; w < 2 * nc; w += AT) {
+    const int c = w >> 1, mode = w & 1;
+    const double *sp = mode == 0 ? a.specT + a.specT_off[c] : a.specD + a.specD_off[c];
+    const int len = mode == 0 ? (int)(a.specT_off[c + 1] - a.specT_off[c]) : (int)(a.specD_off[c + 1] - a.specD_off[c]);
+    const int *grid = mode == 0 ? a.rT_grid : a.rd_grid;
+    const int ng = mode == 0 ? nT : nD;
+    double *outp = mode == 0 ? a.tailT + (long long)c * nT : a.tailD + (long long)c * nD;
+    double acc = 0.0;
+    int gi = ng - 1;
+    // ranks beyond the spectrum length discard nothing
+    while (gi >= 0 && grid[gi] >= len) outp[gi--] = 0.0;
+    for (int i = len - 1; i >= 0 && gi >= 0; --i) {
+      acc = __dadd_rn(acc, sp[i]);
+      while (gi >= 0 && grid[gi] == i) outp[gi--] = acc;
+    }
+    while (gi >= 0) outp[gi--] = acc;
+  }
+  __syncthreads();
+  // (2) table
+  for (long long w = tid; w < (long long)nc * per; w += AT) {
+    const int c = (int)(w / per), rem = (int)(w % per);
+    const int bi = rem / (nT * nD), ti = (rem / nD) % nT, di = rem % nD;
+    const double n2 = a.norm2[c];
+    const double tsum = __dadd_rn(a.tailT[(long long)c * nT + ti], a.tailD[(long long)c * nD + di]);
+    const double tau = (n2 > 0.0) ? __ddiv_rn(tsum, n2) : 0.0;
+    a.e[w] = __dmul_rn(a.eps2[a.bits[bi]], tau);
+    const long long G = a.shape[4 * c], H = a.shape[4 * c + 1], T = a.shape[4 * c + 2], D = a.shape[4 * c + 3];
+    const long long rT = a.rT_grid[ti], rd = a.rd_grid[di], b = a.bits[bi];
+    long long s = (G * H * rT * rd + T * rT + D * rd) * a.elem_bytes;
+    if (b > 0) s += G * H * T * (b * D / 8 + 4);
+    a.s[w] = s;
+  }
+  __syncthreads();
+
+  // (3) evaluation of the per-cell minimisers at lambda: one wave per cell
+  auto evaluate = [&](double lam) {
+    for (int c = wave; c < nc; c += nw) {
+      Best best;
+      best.cost = INFINITY;
+      best.s = LLONG_MAX;
+      best.b = best.rT = best.rd = INT_MAX;
+      best.idx = -1;
+      for (int i = lane; i < per; i += 64) {
+        const long long w = (long long)c * per + i;
+        Best cand;
+        cand.s = a.s[w];
+        cand.cost = __dadd_rn(a.e[w], __dmul_rn(lam, (double)cand.s));
+        cand.b = a.bits[i / (nT * nD)];
+        cand.rT = a.rT_grid[(i / nD) % nT];
+        cand.rd = a.rd_grid[i % nD];
+        cand.idx = i;
+        if (less_than(cand, best)) best = cand;
+      }
+      for (int o = 32; o > 0; o >>= 1) {
+        Best oth = shfl_best(best, o);
+        if (less_than(oth, best)) best = oth;
+      }
+      if (lane == 0) pick[c] = best.idx;
+    }
+    __syncthreads();
+  };
+  auto totals = [&](long long &S, double &E) {
+    S = 0;
+    E = 0.0;
+    for (int c = 0; c < nc; ++c) {
+      const long long w = (long long)c * per + pick[c];
+      S += a.s[w];
+      E = __dadd_rn(E, a.e[w]);
+    }
+  };
+  auto store = [&](int status, double lam, int iters) {
+    if (tid == 0) {
+      long long S;
+      double E;
+      totals(S, E);
+      a.out->status = status;
+      a.out->lambda = lam;
+      a.out->S = S;
+      a.out->E = E;
+      a.out->iters = iters;
+    }
+    for (int c = tid; c < nc; c += AT) a.out_pick[c] = pick[c];
+    __syncthreads();
+  };
+
+  const double B = a.budget;
+  double lo = 1e-30, hi = 1e10;
+  evaluate(lo);
+  long long S;
+  double E;
+  if (tid == 0) {
+    totals(S, E);
+    done_s = ((double)S <= B) ? 1 : 0;
+  }
+  __syncthreads();
+  if (done_s) {
+    store(0, lo, 0);
+    return;
+  }
+  evaluate(hi);
+  if (tid == 0) {
+    totals(S, E);
+    done_s = ((double)S > B) ? 1 : 0;
+  }
+  __syncthreads();
+  if (done_s) {
+    store(JOLT_EINFEASIBLE, hi, 0);
+    return;
+  }
+  // keep the feasible end's picks in out_pick while bisecting
+  for (int c = tid; c < nc; c += AT) a.out_pick[c] = pick[c];
+  __syncthreads();
+  double hi_lam = hi;
+  for (int it = 0; it < 50; ++it) {
+    const double mid = __dsqrt_rn(__dmul_rn(lo, hi));
+    evaluate(mid);
+    if (tid == 0) {
+      totals(S, E);
+      const double Sd = (double)S;
+      if (__dmul_rn(0.995, B) <= Sd && Sd <= B) done_s = 2;
+      else if (Sd > B) { done_s = 0; lam_s = mid; }
+      else { done_s = 1; lam_s = mid; }
+    }
+    __syncthreads();
+    if (done_s == 2) {
+      store(0, mid, it + 1);
+      return;
+    }
+    if (done_s == 0) lo = lam_s;
+    else {
+      hi = lam_s;
+      hi_lam = hi;
+      for (int c = tid; c < nc; c += AT) a.out_pick[c] = pick[c];
+    }
+    __syncthreads();
+  }
+  // no accept: the feasible end
+  for (int c = tid; c < nc; c += AT) pick[c] = a.out_pick[c];
+  __syncthreads();
+  store(0, hi_lam, 50);
+}
+
+}  // namespace
+
+void run_alloc(const AllocArgs &a, hipStream_t st) {
+  JOLT_REQUIRE(a.n_cells > 0 && a.n_cells <= AllocArgs::kMaxCells, JOLT_EINVAL, "allocate: too many cells");
+  hipLaunchKernelGGL(alloc_kernel, dim3(1), dim3(AT), 0, st, a);
+  HIP_LAUNCH_CHECK();
+}
+
+}  // namespace jolt

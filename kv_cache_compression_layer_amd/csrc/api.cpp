@@ -1,0 +1,1208 @@
+// C ABI of libjolt: argument validation, workspace carving and stage sequencing on one stream.
+//
+// Pipeline of jolt_compress (Krishnan & Schulz, "A JoLT for the KV Cache", Sec. 3 and 3.1):
+//   spectra   feature Gram -> ||X||^2, unprojected feature spectrum;
+//             FlashJoLT: Y = X_(T) Omega, Cholesky-QR, power iteration, B = Q^T X_(T),
+//             eig(B B^T) -> q_cap values + tail entry;  exact: eig(X_(T) X_(T)^T)
+//   allocate  distortion/byte table + Lagrangian bisection (one stream sync for the picks)
+//   fit       token factor, token projection, projected feature Gram -> U_d, core,
+//             rounding into the blob
+//   residual  [X | U_T][Q ; -D_j Q] -> per-row b-bit codes and fp32 scales
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "alloc.hpp"
+#include "codec.hpp"
+#include "common.hpp"
+#include "linalg.hpp"
+#include "misc.hpp"
+#include "setup.hpp"
+
+namespace jolt {
+
+static thread_local std::string g_err;
+void set_error(const std::string &msg) { g_err = msg; }
+const char *get_error() { return g_err.c_str(); }
+
+namespace {
+
+constexpr int BIG = 1 << 30;
+
+inline long long rup(long long x, long long a) { return (x + a - 1) / a * a; }
+
+// ------------------------------------------------------------------------------------ workspace
+struct Arena {
+  char *base = nullptr;
+  size_t cap = 0, off = 0;
+  bool dry = true;
+  template <class T>
+  T *take(long long count) {
+    size_t bytes = (size_t)rup(std::max<long long>(count, 1) * (long long)sizeof(T), 256);
+    T *p = dry ? nullptr : (T *)(base + off);
+    off += bytes;
+    if (!dry && off > cap) {
+      set_error("workspace too small: need more than " + std::to_string(cap) + " bytes");
+      throw Fail{JOLT_EWORKSPACE};
+    }
+    return p;
+  }
+};
+
+// ------------------------------------------------------------------------------------ plan
+struct Plan {
+  int n_seq, L, H, T, D, dtype, n_groups, G, GH, M, n_cells, c;
+  int mode, q, ell, ell_ld, T_ld, power_iters, nT;
+  std::vector<int> rT, rd, bits;
+  double eps2[9];
+  double C;
+  uint64_t rot_seed, sketch_seed;
+  long long cell_elems() const { return (long long)GH * T * D; }
+  int xmf() const { return dtype == JOLT_F16 ? MF_F16 : MF_BF16; }
+  int xsrc() const { return dtype == JOLT_F16 ? SRC_F16 : (dtype == JOLT_BF16 ? SRC_BF16 : SRC_F32); }
+};
+
+void check_grid(const int32_t *g, int n, const char *name, std::vector<int> &out) {
+  JOLT_REQUIRE(g != nullptr && n > 0, JOLT_EINVAL, std::string(name) + ": empty grid");
+  out.assign(g, g + n);
+  for (int i = 0; i < n; ++i) {
+    JOLT_REQUIRE(out[i] >= 8 && out[i] % 8 == 0, JOLT_EINVAL, std::string(name) + ": ranks must be positive multiples of 8");
+    if (i) JOLT_REQUIRE(out[i] > out[i - 1], JOLT_EINVAL, std::string(name) + ": grid must be strictly ascending");
+  }
+}
+
+void fill_bits_eps(const jolt_params *p, int D, Plan &pl) {
+  std::vector<int> b;
+  if (p->bits && p->n_bits > 0) b.assign(p->bits, p->bits + p->n_bits);
+  JOLT_REQUIRE(p->n_bits >= 0, JOLT_EINVAL, "bits: negative count");
+  b.push_back(0);
+  for (int v : b) JOLT_REQUIRE(v >= 0 && v <= 8, JOLT_EINVAL, "bits must lie in 0..8");
+  std::sort(b.begin(), b.end());
+  b.erase(std::unique(b.begin(), b.end()), b.end());
+  pl.bits = b;
+  if (p->eps2) {
+    JOLT_REQUIRE(p->eps2[0] == 1.0, JOLT_EINVAL, "eps2[0] must be 1");
+    for (int v : b) JOLT_REQUIRE(isfinite(p->eps2[v]) && p->eps2[v] >= 0.0, JOLT_EINVAL, "eps2 must be finite and >= 0");
+    for (int i = 0; i < 9; ++i) pl.eps2[i] = p->eps2[i];
+  } else {
+    const std::vector<double> &t = eps2_table(D);
+    for (int i = 0; i < 9; ++i) pl.eps2[i] = t[i];
+  }
+}
+
+Plan make_plan(const jolt_cache_desc *d, const jolt_params *p) {
+  JOLT_REQUIRE(d && p, JOLT_EINVAL, "null descriptor or params");
+  Plan pl;
+  pl.n_seq = d->n_seq;
+  pl.L = d->n_layers;
+  pl.H = d->n_heads;
+  pl.T = d->n_tokens;
+  pl.D = d->d_head;
+  pl.dtype = d->dtype;
+  JOLT_REQUIRE(pl.n_seq >= 1 && pl.L >= 1 && pl.H >= 1 && pl.T >= 1, JOLT_EINVAL, "cache shape must be positive");
+  JOLT_REQUIRE(pl.D == 64 || pl.D == 128, JOLT_EINVAL, "d_head must be 64 or 128");
+  JOLT_REQUIRE(pl.dtype == JOLT_F16 || pl.dtype == JOLT_BF16 || pl.dtype == JOLT_F32, JOLT_EINVAL, "bad dtype");
+  JOLT_REQUIRE(d->n_groups >= 1 && d->group_start, JOLT_EINVAL, "no layer groups");
+  pl.n_groups = d->n_groups;
+  JOLT_REQUIRE(d->group_start[0] == 0 && d->group_start[pl.n_groups] == pl.L, JOLT_EINVAL,
+               "group_start must run from 0 to n_layers");
+  pl.G = d->group_start[1] - d->group_start[0];
+  for (int g = 0; g < pl.n_groups; ++g) {
+    JOLT_REQUIRE(d->group_start[g + 1] > d->group_start[g], JOLT_EINVAL, "group_start must be increasing");
+    JOLT_REQUIRE(d->group_start[g + 1] - d->group_start[g] == pl.G, JOLT_EINVAL,
+                 "layer groups must all have the same size");
+  }
+  pl.GH = pl.G * pl.H;
+  pl.M = pl.GH * pl.D;
+  pl.n_cells = pl.n_seq * pl.n_groups * 2;
+  JOLT_REQUIRE(pl.n_cells <= AllocArgs::kMaxCells, JOLT_EINVAL, "too many cells");
+  pl.c = dtype_bytes(pl.dtype);
+  pl.mode = p->mode;
+  JOLT_REQUIRE(pl.mode == JOLT_EXACT || pl.mode == JOLT_FLASH, JOLT_EINVAL, "bad mode");
+  JOLT_REQUIRE(p->target_ratio > 1.0 && isfinite(p->target_ratio), JOLT_EINVAL, "target_ratio must exceed 1");
+  pl.C = p->target_ratio;
+  check_grid(p->rT_grid, p->n_rT, "rT_grid", pl.rT);
+  check_grid(p->rd_grid, p->n_rd, "rd_grid", pl.rd);
+  JOLT_REQUIRE(pl.rd.back() <= pl.D, JOLT_EINVAL, "rd_grid exceeds d_head");
+  fill_bits_eps(p, pl.D, pl);
+  pl.rot_seed = p->rot_seed;
+  pl.sketch_seed = p->sketch_seed;
+  pl.T_ld = (int)rup(pl.T, 8);
+  if (pl.mode == JOLT_FLASH) {
+    JOLT_REQUIRE(p->oversample >= 0 && p->power_iters >= 0, JOLT_EINVAL, "oversample / power_iters must be >= 0");
+    int q = p->qcap > 0 ? p->qcap : std::min(std::max(pl.C <= 4.0 ? 32 : 64, (pl.T + 31) / 32), 512);
+    int ell = std::min({q + p->oversample, pl.T, pl.M});
+    q = std::min(q, ell);
+    pl.q = q;
+    pl.ell = ell;
+    pl.power_iters = p->power_iters;
+    pl.nT = q + 1;
+    JOLT_REQUIRE(pl.rT.back() <= q, JOLT_EINVAL, "rT_grid exceeds q_cap");
+  } else {
+    JOLT_REQUIRE(pl.T <= pl.M, JOLT_EINVAL, "exact mode needs T <= |g| n_h d_h");
+    pl.q = pl.T;
+    pl.ell = pl.T;
+    pl.power_iters = 0;
+    pl.nT = pl.T;
+    JOLT_REQUIRE(pl.rT.back() <= pl.T, JOLT_EINVAL, "rT_grid exceeds min(T, M)");
+  }
+  pl.ell_ld = (int)rup(pl.ell, 16);
+  return pl;
+}
+
+// ------------------------------------------------------------------------------------ buffers
+struct Bufs {
+  // common
+  float *part;
+  double *Gd64, *dD, *eD, *betaD, *evD;
+  double *specT, *specD, *norm2;
+  // flash / exact token stage
+  void *omegaT;
+  float *bufA, *bufB, *Pt, *Zt, *RinvT;
+  double *G64, *Rw, *dT, *eT, *betaT, *evT;
+  float *amax;  // [8][n_cells]
+  // fit
+  float *Wrows, *Udrows, *Cp, *Udr, *Cr, *Vt, *Bcat, *bamax, *Qf, *Qtf;
+  double *Zw, *work, *ZwD, *workD;
+  // alloc
+  double *tailT, *tailD, *tab_e;
+  long long *tab_s;
+  int *pick;
+  AllocOut *aout;
+  // device parameter area
+  char *params;
+  size_t params_bytes;
+  long long part_elems;
+};
+
+int nsplit_for(long long K, long long tiles, int batch, long long min_chunk) {
+  long long want = (2048 + tiles * batch - 1) / (tiles * batch);
+  long long maxs = std::max<long long>(1, K / min_chunk);
+  return (int)std::max<long long>(1, std::min<long long>(want, std::min<long long>(maxs, 256)));
+}
+
+long long tiles_of(long long M, long long N) { return ((M + 127) / 128) * ((N + 127) / 128); }
+
+struct Sizes {
+  int kmax, kmax_d, Kb;
+  long long part_elems;
+};
+
+Sizes sizes_for(const Plan &pl, int kmax, int kmax_d) {
+  Sizes s;
+  s.kmax = kmax;
+  s.kmax_d = kmax_d;
+  s.Kb = (int)rup(pl.D + kmax, 8);
+  const int nb = pl.n_cells;
+  long long pe = 0;
+  {  // feature Gram partials
+    int ns = nsplit_for((long long)pl.GH * pl.T, 1, nb, 8192);
+    pe = std::max(pe, (long long)nb * ns * pl.D * pl.D);
+    int ns2 = nsplit_for((long long)kmax * pl.GH, 1, nb, 1024);
+    pe = std::max(pe, (long long)nb * ns2 * pl.D * pl.D);
+  }
+  if (pl.mode == JOLT_FLASH) {
+    int ns = nsplit_for(pl.T, tiles_of(pl.ell, pl.ell), nb, 2048);
+    pe = std::max(pe, (long long)nb * ns * pl.ell * pl.ell_ld);
+    int ns2 = nsplit_for(pl.M, tiles_of(pl.ell, pl.ell), nb, 1024);
+    pe = std::max(pe, (long long)nb * ns2 * pl.ell * pl.ell_ld);
+  } else {
+    int ns = nsplit_for(pl.M, tiles_of(pl.T, pl.T), nb, 1024);
+    pe = std::max(pe, (long long)nb * ns * pl.T * pl.T_ld);
+  }
+  s.part_elems = pe;
+  return s;
+}
+
+Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
+  Bufs b{};
+  const int nb = pl.n_cells, D = pl.D;
+  const long long ell = pl.ell, ld = pl.ell_ld;
+  b.part = ar.take<float>(sz.part_elems);
+  b.Gd64 = ar.take<double>((long long)nb * D * D);
+  b.dD = ar.take<double>((long long)nb * D);
+  b.eD = ar.take<double>((long long)nb * D);
+  b.betaD = ar.take<double>((long long)nb * D);
+  b.evD = ar.take<double>((long long)nb * D);
+  b.specT = ar.take<double>((long long)nb * pl.nT);
+  b.specD = ar.take<double>((long long)nb * D);
+  b.norm2 = ar.take<double>(nb);
+  b.amax = ar.take<float>(8LL * nb);
+  const long long n_tok = pl.mode == JOLT_FLASH ? ell : pl.T;  // size of the token-side eigenproblem
+  b.G64 = ar.take<double>((long long)nb * n_tok * n_tok);
+  b.dT = ar.take<double>((long long)nb * n_tok);
+  b.eT = ar.take<double>((long long)nb * n_tok);
+  b.betaT = ar.take<double>((long long)nb * n_tok);
+  b.evT = ar.take<double>((long long)nb * n_tok);
+  if (pl.mode == JOLT_FLASH) {
+    b.omegaT = ar.take<char>(ell * pl.M * pl.c);
+    b.bufA = ar.take<float>((long long)nb * ell * pl.T_ld);
+    b.bufB = ar.take<float>((long long)nb * ell * pl.T_ld);
+    b.Pt = ar.take<float>((long long)nb * ell * pl.M);
+    b.Zt = ar.take<float>((long long)nb * ell * pl.M);
+    b.Rw = ar.take<double>((long long)nb * 2 * ell * ell);
+    b.RinvT = ar.take<float>((long long)nb * ell * ld);
+    b.Wrows = ar.take<float>((long long)nb * sz.kmax * ld);
+  } else {
+    b.bufB = ar.take<float>((long long)nb * sz.kmax * pl.T_ld);  // token factor rows
+    b.Zt = ar.take<float>((long long)nb * sz.kmax * pl.M);       // token-projected tensor
+  }
+  b.Zw = ar.take<double>((long long)nb * sz.kmax * n_tok);
+  b.work = ar.take<double>((long long)nb * invit_work_doubles((int)n_tok, sz.kmax));
+  b.ZwD = ar.take<double>((long long)nb * sz.kmax_d * D);
+  b.workD = ar.take<double>((long long)nb * invit_work_doubles(D, sz.kmax_d));
+  b.Udrows = ar.take<float>((long long)nb * sz.kmax_d * D);
+  b.Cp = ar.take<float>((long long)nb * sz.kmax * pl.GH * sz.kmax_d);
+  b.Udr = ar.take<float>((long long)nb * sz.kmax_d * D);
+  b.Cr = ar.take<float>((long long)nb * pl.GH * sz.kmax * sz.kmax_d);
+  b.Vt = ar.take<float>((long long)nb * D * sz.kmax_d);
+  b.Bcat = ar.take<float>((long long)nb * pl.GH * D * sz.Kb);
+  b.bamax = ar.take<float>(nb);
+  b.Qf = ar.take<float>((long long)D * D);
+  b.Qtf = ar.take<float>((long long)D * D);
+  const long long per = (long long)pl.bits.size() * pl.rT.size() * pl.rd.size();
+  b.tailT = ar.take<double>((long long)nb * pl.rT.size());
+  b.tailD = ar.take<double>((long long)nb * pl.rd.size());
+  b.tab_e = ar.take<double>(nb * per);
+  b.tab_s = ar.take<long long>(nb * per);
+  b.pick = ar.take<int>(nb);
+  b.aout = ar.take<AllocOut>(1);
+  b.params_bytes = (size_t)rup(64 * 1024 + 2LL * D * D * 4 +
+                                   (long long)nb * (sizeof(EncCell) + sizeof(DecCell) + sizeof(FactorCell) + 64) +
+                                   (pl.rT.size() + pl.rd.size() + 16) * 4,
+                               256);
+  b.params = ar.take<char>((long long)b.params_bytes);
+  b.part_elems = sz.part_elems;
+  return b;
+}
+
+// ------------------------------------------------------------------------------------ helpers
+GemmArgs ga() {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.a_blk = g.b_blk = BIG;
+  g.a_amax_c = g.b_amax_c = 1.f;
+  g.ab_amax_bs = g.c_amax_bs = 1;
+  g.inner = 1;
+  g.alpha = 1.f;
+  return g;
+}
+
+// Run the same X-operand GEMM for the K cells (t = 0) and the V cells (t = 1): cells are
+// c = 2 i + t, so per-cell outputs use stride 2 and offset t.
+template <class F>
+void for_kv(const void *K, const void *V, F f) {
+  f(0, K);
+  f(1, V);
+}
+
+struct Upload {
+  std::vector<char> host;
+  size_t add(const void *p, size_t n) {
+    size_t o = (host.size() + 255) / 256 * 256;
+    host.resize(o + n);
+    memcpy(host.data() + o, p, n);
+    return o;
+  }
+};
+
+void upload(Bufs &b, Upload &u, hipStream_t st) {
+  JOLT_REQUIRE(u.host.size() <= b.params_bytes, JOLT_EWORKSPACE, "parameter area too small");
+  if (!u.host.empty()) HIP_TRY(hipMemcpyAsync(b.params, u.host.data(), u.host.size(), hipMemcpyHostToDevice, st));
+}
+
+void gram_f32(const Plan &pl, Bufs &b, const float *X, long long ldx, long long xbs, int rows, int K, const float *amax,
+              double *out, long long out_bs, int ldo, int batch, hipStream_t st) {
+  // out[b] (fp64, rows x rows) = X[b] X[b]^T for fp32 rows X[b] [rows][ldx] (K columns)
+  GemmArgs g = ga();
+  g.A = X; g.B = X;
+  g.M = rows; g.N = rows; g.K = K;
+  g.a_ld = ldx; g.b_ld = ldx; g.a_bs = xbs; g.b_bs = xbs;
+  g.a_amax = amax; g.b_amax = amax; g.ab_amax_bs = 1;
+  int ns = nsplit_for(K, tiles_of(rows, rows), batch, 1024);
+  g.k_chunk = (int)rup((K + ns - 1) / ns, 32);
+  ns = (int)((K + g.k_chunk - 1) / g.k_chunk);
+  const long long rl = rup(rows, 16);
+  JOLT_REQUIRE((long long)batch * ns * rows * rl <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
+  g.C = b.part; g.c_ld = rl; g.c_split = (long long)rows * rl; g.c_bs = (long long)ns * rows * rl;
+  g.m_fastest = 1;
+  gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, batch, ns, st);
+  reduce_splits(b.part, g.c_bs, g.c_split, ns, 0, rows, rows, rl, out, true, out_bs, ldo, batch, st);
+}
+
+// C[b] = A[b] B[b]  with A = RinvT-like [M][lda] K-contig fp32 and B N-contig fp32 rows
+void apply_f32(const float *A, long long lda, long long abs_, const float *a_amax, const float *B, long long ldb,
+               long long bbs, const float *b_amax, float *C, long long ldc, long long cbs, float *c_amax, int M, int N,
+               int K, int batch, hipStream_t st) {
+  GemmArgs g = ga();
+  g.A = A; g.B = B; g.C = C;
+  g.M = M; g.N = N; g.K = K;
+  g.a_ld = lda; g.a_bs = abs_; g.a_amax = a_amax;
+  g.b_ld = ldb; g.b_bs = bbs; g.b_amax = b_amax; g.ab_amax_bs = 1;
+  g.c_ld = ldc; g.c_bs = cbs; g.c_amax = c_amax; g.c_amax_bs = 1;
+  g.m_fastest = 1;
+  gemm(MF_F16, SRC_F32, true, SRC_F32, false, g, batch, 1, st);
+}
+
+// --------------------------------------------------------------------------- spectra stage
+void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
+  const int nkv = pl.n_cells / 2, D = pl.D;
+  const long long Kdim = (long long)pl.GH * pl.T;
+  int ns = nsplit_for(Kdim, 1, pl.n_cells, 8192);
+  GemmArgs g = ga();
+  g.M = D; g.N = D; g.K = (int)Kdim;
+  g.k_chunk = (int)rup((Kdim + ns - 1) / ns, 32);
+  ns = (int)((Kdim + g.k_chunk - 1) / g.k_chunk);
+  g.a_ld = D; g.b_ld = D;
+  g.a_bs = g.b_bs = pl.cell_elems();
+  g.c_ld = D; g.c_split = (long long)D * D; g.c_bs = 2LL * ns * D * D;
+  JOLT_REQUIRE((long long)pl.n_cells * ns * D * D <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
+  for_kv(K, V, [&](int t, const void *X) {
+    GemmArgs h = g;
+    h.A = X; h.B = X;
+    h.C = b.part + (long long)t * ns * D * D;
+    gemm(pl.xmf(), pl.xsrc(), false, pl.xsrc(), false, h, nkv, ns, st);
+  });
+  reduce_splits(b.part, (long long)ns * D * D, (long long)D * D, ns, 0, D, D, D, b.Gd64, true, (long long)D * D, D,
+                pl.n_cells, st);
+  trace_f64(b.Gd64, (long long)D * D, D, pl.n_cells, b.norm2, st);
+  sym_eigvals(b.Gd64, (long long)D * D, D, D, pl.n_cells, b.dD, b.eD, b.Gd64, b.betaD, D, b.specD, D, true, st);
+}
+
+// X-operand GEMM: C = A * X^T-ish variants share the cell bookkeeping
+void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
+  const int nb = pl.n_cells, nkv = nb / 2;
+  const long long ell = pl.ell, ld = pl.ell_ld, Tld = pl.T_ld, Mf = pl.M;
+  const long long cellX = pl.cell_elems();
+  float *amY = b.amax, *amR = b.amax + nb, *amQ = b.amax + 2 * nb, *amP = b.amax + 3 * nb, *amZ = b.amax + 4 * nb;
+  gen_omega(b.omegaT, pl.dtype, pl.M, pl.ell, stream_key(pl.sketch_seed, 2), st);
+  fill_f32(b.amax, 8LL * nb, 0.f, st);
+
+  // Y^T = A X_(T)^T with A = Omega^T (16-bit / fp32) or Z^T (fp32)
+  auto sketch = [&](const void *A, int a_src, long long a_bs, const float *a_amax, float *out, float *c_amax) {
+    for_kv(K, V, [&](int t, const void *X) {
+      GemmArgs g = ga();
+      g.A = (const char *)A + (a_bs ? t * a_bs * (a_src == SRC_F32 ? 4 : 2) : 0);
+      g.B = X; g.M = (int)ell; g.N = pl.T; g.K = (int)Mf;
+      g.a_ld = Mf; g.a_bs = 2 * a_bs;
+      g.a_amax = a_amax ? a_amax + t : nullptr; g.ab_amax_bs = 2;
+      g.b_ld = pl.D; g.b_blk = pl.D; g.b_blk_stride = (long long)pl.T * pl.D; g.b_bs = cellX;
+      g.C = out + t * ell * Tld; g.c_ld = Tld; g.c_bs = 2 * ell * Tld;
+      g.c_amax = c_amax ? c_amax + t : nullptr; g.c_amax_bs = 2;
+      g.m_fastest = 1;
+      int mf = pl.xmf();
+      gemm(mf, a_src, true, pl.xsrc(), true, g, nkv, 1, st);
+    });
+  };
+  // P^T = Q^T X_(T)  (ell x M), Q^T fp32 rows of length T
+  auto project = [&](const float *Qt, const float *q_amax, float *out, float *c_amax) {
+    for_kv(K, V, [&](int t, const void *X) {
+      GemmArgs g = ga();
+      g.A = Qt + t * ell * Tld; g.M = (int)ell; g.N = (int)Mf; g.K = pl.T;
+      g.a_ld = Tld; g.a_bs = 2 * ell * Tld; g.a_amax = q_amax + t; g.ab_amax_bs = 2;
+      g.B = X; g.b_ld = pl.D; g.b_blk = pl.D; g.b_blk_stride = (long long)pl.T * pl.D; g.b_bs = cellX;
+      g.C = out + t * ell * Mf; g.c_ld = Mf; g.c_bs = 2 * ell * Mf;
+      g.c_amax = c_amax ? c_amax + t : nullptr; g.c_amax_bs = 2;
+      g.m_fastest = 1;
+      gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), false, g, nkv, 1, st);
+    });
+  };
+  // rows of Y^T (ell x T) -> orthonormal rows by Cholesky QR (passes times)
+  auto cholqr = [&](float *Y, float *Yam, float *tmp, float *tmp_am, int passes) -> float * {
+    for (int p = 0; p < passes; ++p) {
+      gram_f32(pl, b, Y, Tld, ell * Tld, (int)ell, pl.T, Yam, b.G64, ell * ell, (int)ell, nb, st);
+      chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, 2 * ell * ell, b.RinvT, ell * ld, (int)ld, amR, st);
+      fill_f32(tmp_am, nb, 0.f, st);
+      apply_f32(b.RinvT, ld, ell * ld, amR, Y, Tld, ell * Tld, Yam, tmp, Tld, ell * Tld, tmp_am, (int)ell, pl.T,
+                (int)ell, nb, st);
+      std::swap(Y, tmp);
+      std::swap(Yam, tmp_am);
+    }
+    return Y;
+  };
+
+  sketch(b.omegaT, pl.xsrc(), 0, nullptr, b.bufA, amY);
+  float *Q = b.bufA, *Qam = amY;
+  {
+    float *other = b.bufB, *other_am = amQ;
+    Q = cholqr(b.bufA, amY, other, other_am, 1);
+    Qam = (Q == b.bufA) ? amY : amQ;
+  }
+  for (int it = 0; it < pl.power_iters; ++it) {
+    fill_f32(amP, nb, 0.f, st);
+    project(Q, Qam, b.Pt, amP);
+    // Z = orth(P): Cholesky QR on the rows of P^T (length M)
+    gram_f32(pl, b, b.Pt, Mf, ell * Mf, (int)ell, (int)Mf, amP, b.G64, ell * ell, (int)ell, nb, st);
+    chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, 2 * ell * ell, b.RinvT, ell * ld, (int)ld, amR, st);
+    fill_f32(amZ, nb, 0.f, st);
+    apply_f32(b.RinvT, ld, ell * ld, amR, b.Pt, Mf, ell * Mf, amP, b.Zt, Mf, ell * Mf, amZ, (int)ell, (int)Mf,
+              (int)ell, nb, st);
+    float *Y = (Q == b.bufA) ? b.bufB : b.bufA;
+    float *Yam = (Q == b.bufA) ? amQ : amY;
+    fill_f32(Yam, nb, 0.f, st);
+    sketch(b.Zt, SRC_F32, ell * Mf, amZ, Y, Yam);
+    float *other = (Y == b.bufA) ? b.bufB : b.bufA;
+    float *other_am = (Y == b.bufA) ? amQ : amY;
+    const int passes = (it + 1 == pl.power_iters) ? 2 : 1;
+    Q = cholqr(Y, Yam, other, other_am, passes);
+    Qam = (Q == b.bufA) ? amY : amQ;
+  }
+  if (pl.power_iters == 0) {  // the final basis is orthonormalised twice
+    float *other = (Q == b.bufA) ? b.bufB : b.bufA;
+    float *other_am = (Q == b.bufA) ? amQ : amY;
+    Q = cholqr(Q, Qam, other, other_am, 1);
+    Qam = (Q == b.bufA) ? amY : amQ;
+  }
+  // B = Q^T X_(T) -> H = B B^T (fp64) -> eigenvalues; spectrum = top q + tail entry
+  float *amP1 = b.amax + 5 * nb;
+  fill_f32(amP1, nb, 0.f, st);
+  project(Q, Qam, b.Pt, amP1);
+  gram64(b.Pt, ell * Mf, (int)Mf, (int)ell, (int)Mf, b.G64, ell * ell, (int)ell, nb, st);
+  sym_eigvals(b.G64, ell * ell, (int)ell, (int)ell, nb, b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, true, st);
+  flash_spec(b.evT, ell, pl.q, b.norm2, b.specT, pl.nT, nb, st);
+  // the fit reads Q^T from b.bufA
+  if (Q != b.bufA) std::swap(b.bufA, b.bufB);
+}
+
+void stage_exact(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
+  const int nb = pl.n_cells, nkv = nb / 2;
+  const long long T = pl.T, Tld = pl.T_ld, Mf = pl.M;
+  int ns = nsplit_for(Mf, tiles_of(T, T), nb, 1024);
+  GemmArgs g = ga();
+  g.M = (int)T; g.N = (int)T; g.K = (int)Mf;
+  g.k_chunk = (int)rup((Mf + ns - 1) / ns, 32);
+  ns = (int)((Mf + g.k_chunk - 1) / g.k_chunk);
+  g.a_ld = pl.D; g.a_blk = pl.D; g.a_blk_stride = T * pl.D; g.a_bs = pl.cell_elems();
+  g.b_ld = pl.D; g.b_blk = pl.D; g.b_blk_stride = T * pl.D; g.b_bs = pl.cell_elems();
+  g.c_ld = Tld; g.c_split = T * Tld; g.c_bs = 2LL * ns * T * Tld;
+  JOLT_REQUIRE((long long)nb * ns * T * Tld <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
+  for_kv(K, V, [&](int t, const void *X) {
+    GemmArgs h = g;
+    h.A = X; h.B = X;
+    h.C = b.part + (long long)t * ns * T * Tld;
+    gemm(pl.xmf(), pl.xsrc(), true, pl.xsrc(), true, h, nkv, ns, st);
+  });
+  reduce_splits(b.part, (long long)ns * T * Tld, T * Tld, ns, 0, (int)T, (int)T, Tld, b.G64, true, T * T, (int)T, nb,
+                st);
+  sym_eigvals(b.G64, T * T, (int)T, (int)T, nb, b.dT, b.eT, b.G64, b.betaT, T, b.specT, pl.nT, true, st);
+}
+
+// ----------------------------------------------------------------------------- allocation
+struct AllocDev {
+  int *shape, *rT, *rd, *bits;
+  long long *offT, *offD;
+  double *eps2;
+};
+
+void run_allocation(int nc, const AllocDev &ad, int elem_bytes, const double *specT, const double *specD,
+                    const double *norm2, int n_rT, int n_rd, int n_bits, double budget, Bufs &b, hipStream_t st) {
+  AllocArgs a;
+  a.n_cells = nc;
+  a.shape = ad.shape;
+  a.elem_bytes = elem_bytes;
+  a.specT = specT; a.specT_off = ad.offT;
+  a.specD = specD; a.specD_off = ad.offD;
+  a.norm2 = norm2;
+  a.rT_grid = ad.rT; a.n_rT = n_rT;
+  a.rd_grid = ad.rd; a.n_rd = n_rd;
+  a.bits = ad.bits; a.n_bits = n_bits;
+  a.eps2 = ad.eps2;
+  a.budget = budget;
+  a.tailT = b.tailT; a.tailD = b.tailD; a.e = b.tab_e; a.s = b.tab_s;
+  a.out_pick = b.pick; a.out = b.aout;
+  run_alloc(a, st);
+}
+
+struct Section {
+  long long off_UT, off_Ud, off_core, off_scales, off_codes, end;
+};
+Section layout(int G, int H, int T, int D, int c, int rT, int rd, int bits) {
+  Section s;
+  s.off_UT = 256;
+  s.off_Ud = s.off_UT + rup((long long)T * rT * c, 256);
+  s.off_core = s.off_Ud + rup((long long)D * rd * c, 256);
+  s.off_scales = s.off_core + rup((long long)G * H * rT * rd * c, 256);
+  if (bits > 0) {
+    s.off_codes = s.off_scales + rup((long long)G * H * T * 4, 256);
+    s.end = s.off_codes + rup((long long)G * H * T * D * bits / 8, 256);
+  } else {
+    s.off_codes = s.end = s.off_scales;
+  }
+  return s;
+}
+
+long long eq1_bytes(int G, int H, int T, int D, int c, int rT, int rd, int b) {
+  long long s = ((long long)G * H * rT * rd + (long long)T * rT + (long long)D * rd) * c;
+  if (b > 0) s += (long long)G * H * T * (b * D / 8 + 4);
+  return s;
+}
+
+AllocDev upload_alloc_tables(Upload &u, const Plan &pl, const std::vector<int> &shape, const std::vector<long long> &offT,
+                             const std::vector<long long> &offD, std::vector<size_t> &offs) {
+  offs.push_back(u.add(shape.data(), shape.size() * 4));
+  offs.push_back(u.add(pl.rT.data(), pl.rT.size() * 4));
+  offs.push_back(u.add(pl.rd.data(), pl.rd.size() * 4));
+  offs.push_back(u.add(pl.bits.data(), pl.bits.size() * 4));
+  offs.push_back(u.add(offT.data(), offT.size() * 8));
+  offs.push_back(u.add(offD.data(), offD.size() * 8));
+  offs.push_back(u.add(pl.eps2, 9 * 8));
+  return AllocDev{};
+}
+
+AllocDev bind_alloc(char *base, const std::vector<size_t> &o) {
+  AllocDev a;
+  a.shape = (int *)(base + o[0]);
+  a.rT = (int *)(base + o[1]);
+  a.rd = (int *)(base + o[2]);
+  a.bits = (int *)(base + o[3]);
+  a.offT = (long long *)(base + o[4]);
+  a.offD = (long long *)(base + o[5]);
+  a.eps2 = (double *)(base + o[6]);
+  return a;
+}
+
+void upload_rotation(const Plan &pl, Bufs &b, Upload &u, std::vector<size_t> &offs) {
+  const std::vector<double> &Q = rotation(pl.D, pl.rot_seed);
+  std::vector<float> qf(Q.size()), qt(Q.size());
+  for (int i = 0; i < pl.D; ++i)
+    for (int j = 0; j < pl.D; ++j) {
+      qf[(size_t)i * pl.D + j] = (float)Q[(size_t)i * pl.D + j];
+      qt[(size_t)j * pl.D + i] = (float)Q[(size_t)i * pl.D + j];
+    }
+  offs.push_back(u.add(qf.data(), qf.size() * 4));
+  offs.push_back(u.add(qt.data(), qt.size() * 4));
+}
+
+// ----------------------------------------------------------------------------- fit + residual
+struct CellPick {
+  int rT, rd, bits;
+  long long off;
+  Section sec;
+};
+
+void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const void *V, char *out,
+               const std::vector<CellPick> &picks, hipStream_t st) {
+  const int nb = pl.n_cells, nkv = nb / 2, D = pl.D, GH = pl.GH;
+  const long long Mf = pl.M, Tld = pl.T_ld, kmax = sz.kmax, kmd = sz.kmax_d;
+  const long long cellX = pl.cell_elems();
+  // ---- per-cell tables
+  Upload u;
+  std::vector<int> rTv(nb), rdv(nb);
+  std::vector<FactorCell> fc(nb);
+  for (int c = 0; c < nb; ++c) {
+    const CellPick &p = picks[c];
+    rTv[c] = p.rT;
+    rdv[c] = p.rd;
+    FactorCell &f = fc[c];
+    f.header = out + p.off;
+    f.UT = out + p.off + p.sec.off_UT;
+    f.Ud = out + p.off + p.sec.off_Ud;
+    f.core = out + p.off + p.sec.off_core;
+    f.rT = p.rT; f.rd = p.rd; f.bits = p.bits; f.pad = 0;
+    uint32_t h[10] = {0x544C4F4Au, 1u, (uint32_t)pl.G, (uint32_t)pl.H, (uint32_t)pl.T, (uint32_t)D,
+                      (uint32_t)p.rT, (uint32_t)p.rd, (uint32_t)p.bits, (uint32_t)pl.dtype};
+    memcpy(f.hdr, h, sizeof(h));
+  }
+  std::vector<size_t> offs;
+  size_t o_rT = u.add(rTv.data(), nb * 4), o_rd = u.add(rdv.data(), nb * 4), o_fc = u.add(fc.data(), nb * sizeof(FactorCell));
+  std::vector<size_t> rot_offs;
+  upload_rotation(pl, b, u, rot_offs);
+  // encode cells (b > 0)
+  std::vector<EncCell> enc;
+  std::vector<EncCell> encv;
+  upload(b, u, st);
+  int *d_rT = (int *)(b.params + o_rT), *d_rd = (int *)(b.params + o_rd);
+  FactorCell *d_fc = (FactorCell *)(b.params + o_fc);
+  const float *Qf = (const float *)(b.params + rot_offs[0]);
+  const float *Qtf = (const float *)(b.params + rot_offs[1]);
+
+  float *amYp = b.amax + 6 * nb, *amCr = b.amax + 7 * nb;
+  float *UTt = b.bufB;  // [nb][kmax][Tld]
+  float *Yp = b.Zt;     // [nb][kmax][Mf]
+  fill_f32(amYp, nb, 0.f, st);
+  if (pl.mode == JOLT_FLASH) {
+    const long long ell = pl.ell, ld = pl.ell_ld;
+    fill_f32(b.Wrows, (long long)nb * kmax * ld, 0.f, st);
+    sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, (int)ell, d_rT, (int)kmax, nb, b.Zw, kmax * ell, b.work,
+                (long long)invit_work_doubles((int)ell, (int)kmax), nullptr, b.Wrows, kmax * ld, (int)ld, st);
+    // U_T^T = W^T Q^T (rows of length T)
+    GemmArgs g = ga();
+    g.A = b.Wrows; g.a_ld = ld; g.a_bs = kmax * ld; g.a_amax_c = 1.f;
+    g.B = b.bufA; g.b_ld = Tld; g.b_bs = ell * Tld;
+    g.b_amax = nullptr; g.b_amax_c = 1.f;  // Q has orthonormal rows: |entries| <= 1
+    g.M = (int)kmax; g.N = pl.T; g.K = (int)ell;
+    g.C = UTt; g.c_ld = Tld; g.c_bs = kmax * Tld; g.m_fastest = 1;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, false, g, nb, 1, st);
+    // token-projected tensor Y_p = W^T P1^T  (kmax x M)
+    GemmArgs h = ga();
+    h.A = b.Wrows; h.a_ld = ld; h.a_bs = kmax * ld; h.a_amax_c = 1.f;
+    h.B = b.Pt; h.b_ld = Mf; h.b_bs = ell * Mf; h.b_amax = b.amax + 5 * nb; h.ab_amax_bs = 1;
+    h.M = (int)kmax; h.N = (int)Mf; h.K = (int)ell;
+    h.C = Yp; h.c_ld = Mf; h.c_bs = kmax * Mf; h.c_amax = amYp; h.c_amax_bs = 1; h.m_fastest = 1;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, false, h, nb, 1, st);
+  } else {
+    const long long T = pl.T;
+    fill_f32(UTt, (long long)nb * kmax * Tld, 0.f, st);
+    sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, T, b.specT, pl.nT, (int)T, d_rT, (int)kmax, nb, b.Zw, kmax * T, b.work,
+                (long long)invit_work_doubles((int)T, (int)kmax), nullptr, UTt, kmax * Tld, (int)Tld, st);
+    for_kv(K, V, [&](int t, const void *X) {
+      GemmArgs g = ga();
+      g.A = UTt + t * kmax * Tld; g.a_ld = Tld; g.a_bs = 2 * kmax * Tld; g.a_amax_c = 1.f;
+      g.B = X; g.b_ld = D; g.b_blk = D; g.b_blk_stride = T * D; g.b_bs = cellX;
+      g.M = (int)kmax; g.N = (int)Mf; g.K = (int)T;
+      g.C = Yp + t * kmax * Mf; g.c_ld = Mf; g.c_bs = 2 * kmax * Mf;
+      g.c_amax = amYp + t; g.c_amax_bs = 2; g.m_fastest = 1;
+      gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), false, g, nkv, 1, st);
+    });
+  }
+  // ---- projected feature Gram -> U_d
+  {
+    const long long Kd = kmax * GH;
+    int ns = nsplit_for(Kd, 1, nb, 1024);
+    GemmArgs g = ga();
+    g.A = Yp; g.B = Yp; g.M = D; g.N = D; g.K = (int)Kd;
+    g.a_ld = D; g.b_ld = D; g.a_bs = g.b_bs = kmax * Mf;
+    g.a_amax = amYp; g.b_amax = amYp; g.ab_amax_bs = 1;
+    g.k_chunk = (int)rup((Kd + ns - 1) / ns, 32);
+    ns = (int)((Kd + g.k_chunk - 1) / g.k_chunk);
+    JOLT_REQUIRE((long long)nb * ns * D * D <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
+    g.C = b.part; g.c_ld = D; g.c_split = (long long)D * D; g.c_bs = (long long)ns * D * D;
+    gemm(MF_F16, SRC_F32, false, SRC_F32, false, g, nb, ns, st);
+    reduce_splits(b.part, g.c_bs, g.c_split, ns, 0, D, D, D, b.Gd64, true, (long long)D * D, D, nb, st);
+    sym_eigvals(b.Gd64, (long long)D * D, D, D, nb, b.dD, b.eD, b.Gd64, b.betaD, D, b.evD, D, true, st);
+    fill_f32(b.Udrows, (long long)nb * kmd * D, 0.f, st);
+    sym_eigvecs(b.dD, b.eD, b.Gd64, b.betaD, D, b.evD, D, D, d_rd, (int)kmd, nb, b.ZwD, kmd * D, b.workD,
+                (long long)invit_work_doubles(D, (int)kmd), nullptr, b.Udrows, kmd * D, D, st);
+  }
+  // ---- core: Cp[(r, j)][kk] = Y_p[r][j][:] . U_d[:, kk]
+  {
+    GemmArgs g = ga();
+    g.A = Yp; g.a_ld = D; g.a_bs = kmax * Mf; g.a_amax = amYp; g.ab_amax_bs = 1;
+    g.B = b.Udrows; g.b_ld = D; g.b_bs = kmd * D;
+    g.M = (int)(kmax * GH); g.N = (int)kmd; g.K = D;
+    g.C = b.Cp; g.c_ld = kmd; g.c_bs = kmax * GH * kmd; g.m_fastest = 0;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
+  }
+  // ---- factors into the blob (rounded) + rounded copies for the residual
+  fill_f32(b.Udr, (long long)nb * kmd * D, 0.f, st);
+  fill_f32(b.Cr, (long long)nb * GH * kmax * kmd, 0.f, st);
+  put_ut(pl.dtype, d_fc, nb, UTt, kmax * Tld, (int)Tld, pl.T, (int)kmax, st);
+  put_small(pl.dtype, d_fc, nb, b.Udrows, kmd * D, b.Cp, kmax * GH * kmd, (int)kmax, (int)kmd, D, GH, b.Udr, b.Cr, st);
+  write_headers(d_fc, nb, st);
+
+  // ---- residual: Bcat = [Q^T | -(D_j Q)^T] per (cell, j), then the fused encode
+  bool any = false;
+  for (int c = 0; c < nb; ++c) any |= picks[c].bits > 0;
+  if (!any) return;
+  {
+    // Vt[n][kk] = sum_d Q[d][n] Udr[kk][d]
+    GemmArgs g = ga();
+    g.A = Qtf; g.a_ld = D; g.a_bs = 0; g.a_amax_c = 1.f;
+    g.B = b.Udr; g.b_ld = D; g.b_bs = kmd * D; g.b_amax_c = 1.f;
+    g.M = D; g.N = (int)kmd; g.K = D;
+    g.C = b.Vt; g.c_ld = kmd; g.c_bs = D * kmd;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
+    amax_cells(b.Cr, GH * kmax * kmd, GH * kmax * kmd, nb, amCr, st);
+    bcat_q(b.Bcat, nb, GH, D, sz.Kb, Qtf, st);
+    GemmArgs h = ga();
+    h.A = b.Vt; h.a_ld = kmd; h.a_bs = D * kmd; h.a_bs2 = 0; h.a_amax_c = 1.f;
+    h.B = b.Cr; h.b_ld = kmd; h.b_bs = GH * kmax * kmd; h.b_bs2 = kmax * kmd; h.b_amax = amCr; h.ab_amax_bs = 1;
+    h.inner = GH;
+    h.M = D; h.N = (int)kmax; h.K = (int)kmd;
+    h.C = b.Bcat + D; h.c_ld = sz.Kb; h.c_bs = (long long)GH * D * sz.Kb; h.c_bs2 = (long long)D * sz.Kb;
+    h.alpha = -1.f;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, true, h, nb * GH, 1, st);
+    amax_cells(b.Bcat, (long long)GH * D * sz.Kb, (long long)GH * D * sz.Kb, nb, b.bamax, st);
+  }
+  std::vector<EncCell> ec;
+  for (int c = 0; c < nb; ++c) {
+    const CellPick &p = picks[c];
+    if (p.bits == 0) continue;
+    const int s = c / (2 * pl.n_groups), g = (c / 2) % pl.n_groups, t = c % 2;
+    const char *Xb = (const char *)(t == 0 ? K : V);
+    EncCell e;
+    e.X = Xb + ((long long)s * pl.n_groups + g) * cellX * pl.c;
+    e.UT = out + p.off + p.sec.off_UT;
+    e.Bcat = b.Bcat + (long long)c * GH * D * sz.Kb;
+    e.b_amax = b.bamax + c;
+    e.scales = (float *)(out + p.off + p.sec.off_scales);
+    e.codes = (uint8_t *)(out + p.off + p.sec.off_codes);
+    e.GH = GH; e.rT = p.rT; e.bits = p.bits; e.Kb = sz.Kb;
+    ec.push_back(e);
+  }
+  Upload u2;
+  size_t o_ec = u2.add(ec.data(), ec.size() * sizeof(EncCell));
+  // second upload goes after the first one in the parameter area
+  char *dst = b.params + rup((long long)u.host.size(), 256);
+  JOLT_REQUIRE(rup((long long)u.host.size(), 256) + (long long)u2.host.size() <= (long long)b.params_bytes,
+               JOLT_EWORKSPACE, "parameter area too small");
+  HIP_TRY(hipMemcpyAsync(dst, u2.host.data(), u2.host.size(), hipMemcpyHostToDevice, st));
+  encode_cells(pl.dtype, (const EncCell *)(dst + o_ec), (int)ec.size(), pl.T, D, GH, st);
+}
+
+// ----------------------------------------------------------------------------- entry helpers
+hipStream_t S(void *s) { return (hipStream_t)s; }
+
+template <class F>
+int guarded(F f) {
+  try {
+    g_err.clear();
+    return f();
+  } catch (const Fail &e) {
+    return e.status;
+  } catch (const std::exception &e) {
+    set_error(std::string("internal error: ") + e.what());
+    return JOLT_EINVAL;
+  }
+}
+
+Sizes sizes_worst(const Plan &pl) { return sizes_for(pl, pl.rT.back(), pl.rd.back()); }
+
+void spectra_all(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
+  JOLT_REQUIRE(K && V, JOLT_EINVAL, "null cache pointer");
+  stage_feature(pl, b, K, V, st);
+  if (pl.mode == JOLT_FLASH) stage_flash(pl, b, K, V, st);
+  else stage_exact(pl, b, K, V, st);
+}
+
+}  // namespace
+}  // namespace jolt
+
+using namespace jolt;
+
+extern "C" {
+
+const char *jolt_last_error(void) { return get_error(); }
+
+size_t jolt_workspace_bytes(const jolt_cache_desc *desc, const jolt_params *params) {
+  size_t out = 0;
+  int st = guarded([&]() {
+    Plan pl = make_plan(desc, params);
+    Arena ar;
+    Sizes sz = sizes_worst(pl);
+    carve(ar, pl, sz);
+    out = ar.off + 4096;
+    return 0;
+  });
+  return st == 0 ? out : 0;
+}
+
+size_t jolt_output_bytes(const jolt_cache_desc *desc, const jolt_params *params) {
+  size_t out = 0;
+  int st = guarded([&]() {
+    Plan pl = make_plan(desc, params);
+    long long dense = (long long)pl.n_cells * pl.cell_elems() * pl.c;
+    double B = (double)dense / pl.C;
+    // every section: header + up to 5 parts padded to 256 bytes
+    out = (size_t)ceil(B) + (size_t)pl.n_cells * (256 + 5 * 256) + 256;
+    return 0;
+  });
+  return st == 0 ? out : 0;
+}
+
+int64_t jolt_token_spectrum_len(const jolt_cache_desc *desc, const jolt_params *params) {
+  int64_t n = -1;
+  int st = guarded([&]() {
+    Plan pl = make_plan(desc, params);
+    n = pl.nT;
+    return 0;
+  });
+  return st == 0 ? n : st;
+}
+
+int jolt_rotation(int32_t d_head, uint64_t seed, double *h_Q) {
+  return guarded([&]() {
+    JOLT_REQUIRE(d_head >= 1 && d_head <= 1024 && h_Q, JOLT_EINVAL, "bad rotation request");
+    const std::vector<double> &Q = rotation(d_head, seed);
+    memcpy(h_Q, Q.data(), Q.size() * sizeof(double));
+    return 0;
+  });
+}
+
+int jolt_eps2(int32_t d_head, double *h_eps2) {
+  return guarded([&]() {
+    JOLT_REQUIRE(d_head >= 8 && d_head <= 1024 && d_head % 8 == 0 && h_eps2, JOLT_EINVAL, "bad eps2 request");
+    const std::vector<double> &t = eps2_table(d_head);
+    memcpy(h_eps2, t.data(), 9 * sizeof(double));
+    return 0;
+  });
+}
+
+int jolt_spectra(const void *d_K, const void *d_V, const jolt_cache_desc *desc, const jolt_params *params,
+                 double *d_specT, double *d_specD, double *d_norm2, float *d_UT, int32_t n_vec, void *d_ws,
+                 size_t ws_bytes, void *stream) {
+  return guarded([&]() {
+    Plan pl = make_plan(desc, params);
+    hipStream_t st = S(stream);
+    Arena ar;
+    ar.dry = false;
+    ar.base = (char *)d_ws;
+    ar.cap = ws_bytes;
+    JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
+    JOLT_REQUIRE(d_UT == nullptr || (n_vec >= 1 && n_vec <= pl.q), JOLT_EINVAL, "n_vec out of range");
+    Sizes sz = sizes_worst(pl);
+    if (d_UT) sz = sizes_for(pl, std::max(pl.rT.back(), (int)rup(n_vec, 8)), pl.rd.back());
+    Bufs b = carve(ar, pl, sz);
+    spectra_all(pl, b, d_K, d_V, st);
+    const int nb = pl.n_cells;
+    HIP_TRY(hipMemcpyAsync(d_specT, b.specT, (size_t)nb * pl.nT * 8, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(d_specD, b.specD, (size_t)nb * pl.D * 8, hipMemcpyDeviceToDevice, st));
+    HIP_TRY(hipMemcpyAsync(d_norm2, b.norm2, (size_t)nb * 8, hipMemcpyDeviceToDevice, st));
+    if (d_UT) {
+      std::vector<int> kv(nb, n_vec);
+      Upload u;
+      size_t ok = u.add(kv.data(), nb * 4);
+      upload(b, u, st);
+      int *dk = (int *)(b.params + ok);
+      const long long kmax = sz.kmax, Tld = pl.T_ld;
+      if (pl.mode == JOLT_FLASH) {
+        const long long ell = pl.ell, ld = pl.ell_ld;
+        fill_f32(b.Wrows, (long long)nb * kmax * ld, 0.f, st);
+        sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, (int)ell, dk, (int)kmax, nb, b.Zw, kmax * ell, b.work,
+                    (long long)invit_work_doubles((int)ell, (int)kmax), nullptr, b.Wrows, kmax * ld, (int)ld, st);
+        GemmArgs g = ga();
+        g.A = b.Wrows; g.a_ld = ld; g.a_bs = kmax * ld; g.a_amax_c = 1.f;
+        g.B = b.bufA; g.b_ld = Tld; g.b_bs = ell * Tld; g.b_amax_c = 1.f;
+        g.M = n_vec; g.N = pl.T; g.K = (int)ell;
+        g.C = b.bufB; g.c_ld = Tld; g.c_bs = kmax * Tld; g.m_fastest = 1;
+        gemm(MF_F16, SRC_F32, true, SRC_F32, false, g, nb, 1, st);
+      } else {
+        sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, pl.T, b.specT, pl.nT, pl.T, dk, (int)kmax, nb, b.Zw, kmax * pl.T,
+                    b.work, (long long)invit_work_doubles(pl.T, (int)kmax), nullptr, b.bufB, kmax * Tld, (int)Tld, st);
+      }
+      for (int c = 0; c < nb; ++c)
+        HIP_TRY(hipMemcpy2DAsync(d_UT + (size_t)c * n_vec * pl.T, (size_t)pl.T * 4, b.bufB + (size_t)c * kmax * Tld,
+                                 (size_t)Tld * 4, (size_t)pl.T * 4, (size_t)n_vec, hipMemcpyDeviceToDevice, st));
+    }
+    return 0;
+  });
+}
+
+int jolt_allocate(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_bytes, const double *d_specT,
+                  const int64_t *h_specT_off, const double *d_specD, const int64_t *h_specD_off,
+                  const double *d_norm2, const jolt_params *params, double budget_bytes, jolt_pick *h_picks,
+                  double *h_lambda, void *d_ws, size_t ws_bytes, void *stream) {
+  return guarded([&]() {
+    JOLT_REQUIRE(n_cells >= 1 && n_cells <= AllocArgs::kMaxCells, JOLT_EINVAL, "n_cells out of range");
+    JOLT_REQUIRE(h_cell_shape && d_specT && h_specT_off && d_specD && h_specD_off && d_norm2 && params && h_picks,
+                 JOLT_EINVAL, "null argument");
+    JOLT_REQUIRE(elem_bytes == 2 || elem_bytes == 4, JOLT_EINVAL, "elem_bytes must be 2 or 4");
+    JOLT_REQUIRE(budget_bytes > 0 && isfinite(budget_bytes), JOLT_EINVAL, "budget must be positive");
+    hipStream_t st = S(stream);
+    Plan pl;
+    check_grid(params->rT_grid, params->n_rT, "rT_grid", pl.rT);
+    check_grid(params->rd_grid, params->n_rd, "rd_grid", pl.rd);
+    int Dmax = 0;
+    for (int c = 0; c < n_cells; ++c) {
+      const int32_t *s = h_cell_shape + 4 * c;
+      JOLT_REQUIRE(s[0] > 0 && s[1] > 0 && s[2] > 0 && s[3] > 0 && (s[3] * 1) % 8 == 0, JOLT_EINVAL, "bad cell shape");
+      JOLT_REQUIRE(h_specT_off[c + 1] > h_specT_off[c] && h_specD_off[c + 1] - h_specD_off[c] == s[3], JOLT_EINVAL,
+                   "bad spectrum offsets");
+      JOLT_REQUIRE(pl.rT.back() <= h_specT_off[c + 1] - h_specT_off[c], JOLT_EINVAL, "rT_grid exceeds a token spectrum");
+      JOLT_REQUIRE(pl.rd.back() <= s[3], JOLT_EINVAL, "rd_grid exceeds d_head");
+      Dmax = std::max(Dmax, (int)s[3]);
+    }
+    fill_bits_eps(params, Dmax, pl);
+    pl.n_cells = n_cells;
+    // workspace: tables + parameter area
+    Arena ar;
+    ar.dry = false;
+    ar.base = (char *)d_ws;
+    ar.cap = ws_bytes;
+    JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
+    const long long per = (long long)pl.bits.size() * pl.rT.size() * pl.rd.size();
+    Bufs b{};
+    b.tailT = ar.take<double>((long long)n_cells * pl.rT.size());
+    b.tailD = ar.take<double>((long long)n_cells * pl.rd.size());
+    b.tab_e = ar.take<double>(n_cells * per);
+    b.tab_s = ar.take<long long>(n_cells * per);
+    b.pick = ar.take<int>(n_cells);
+    b.aout = ar.take<AllocOut>(1);
+    b.params_bytes = (size_t)rup(4096 + (long long)n_cells * 40 + (pl.rT.size() + pl.rd.size()) * 4, 256);
+    b.params = ar.take<char>((long long)b.params_bytes);
+    std::vector<int> shape(h_cell_shape, h_cell_shape + 4 * n_cells);
+    std::vector<long long> offT(h_specT_off, h_specT_off + n_cells + 1), offD(h_specD_off, h_specD_off + n_cells + 1);
+    Upload u;
+    std::vector<size_t> o;
+    upload_alloc_tables(u, pl, shape, offT, offD, o);
+    upload(b, u, st);
+    AllocDev ad = bind_alloc(b.params, o);
+    run_allocation(n_cells, ad, elem_bytes, d_specT, d_specD, d_norm2, (int)pl.rT.size(), (int)pl.rd.size(),
+                   (int)pl.bits.size(), budget_bytes, b, st);
+    std::vector<int> pick(n_cells);
+    AllocOut ao;
+    HIP_TRY(hipMemcpyAsync(pick.data(), b.pick, n_cells * 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipMemcpyAsync(&ao, b.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    const int nT = (int)pl.rT.size(), nD = (int)pl.rd.size();
+    long long off = 0;
+    for (int c = 0; c < n_cells; ++c) {
+      const int i = pick[c];
+      const int bi = i / (nT * nD), ti = (i / nD) % nT, di = i % nD;
+      const int32_t *s = h_cell_shape + 4 * c;
+      jolt_pick &p = h_picks[c];
+      p.rT = pl.rT[ti]; p.rd = pl.rd[di]; p.bits = pl.bits[bi]; p.pad = 0;
+      p.bytes = eq1_bytes(s[0], s[1], s[2], s[3], elem_bytes, p.rT, p.rd, p.bits);
+      HIP_TRY(hipMemcpy(&p.err_pred, b.tab_e + (long long)c * per + i, 8, hipMemcpyDeviceToHost));
+      Section sec = layout(s[0], s[1], s[2], s[3], elem_bytes, p.rT, p.rd, p.bits);
+      p.offset = off;
+      p.section_bytes = sec.end;
+      off += sec.end;
+    }
+    if (h_lambda) *h_lambda = ao.lambda;
+    if (ao.status != 0) {
+      set_error("allocation infeasible: the smallest picks exceed the budget");
+      return (int)ao.status;
+    }
+    return 0;
+  });
+}
+
+int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc, const jolt_params *params,
+                  void *d_out, size_t out_bytes, void *d_ws, size_t ws_bytes, jolt_pick *h_picks, double *h_lambda,
+                  void *stream) {
+  return guarded([&]() {
+    Plan pl = make_plan(desc, params);
+    hipStream_t st = S(stream);
+    JOLT_REQUIRE(d_out && h_picks, JOLT_EINVAL, "null output");
+    JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
+    Arena ar;
+    ar.dry = false;
+    ar.base = (char *)d_ws;
+    ar.cap = ws_bytes;
+    Sizes sz = sizes_worst(pl);
+    Bufs b = carve(ar, pl, sz);
+    const int nb = pl.n_cells;
+    spectra_all(pl, b, d_K, d_V, st);
+    // ---- allocation
+    std::vector<int> shape(4 * nb);
+    std::vector<long long> offT(nb + 1), offD(nb + 1);
+    for (int c = 0; c < nb; ++c) {
+      shape[4 * c] = pl.G; shape[4 * c + 1] = pl.H; shape[4 * c + 2] = pl.T; shape[4 * c + 3] = pl.D;
+      offT[c] = (long long)c * pl.nT;
+      offD[c] = (long long)c * pl.D;
+    }
+    offT[nb] = (long long)nb * pl.nT;
+    offD[nb] = (long long)nb * pl.D;
+    Upload u;
+    std::vector<size_t> o;
+    upload_alloc_tables(u, pl, shape, offT, offD, o);
+    upload(b, u, st);
+    AllocDev ad = bind_alloc(b.params, o);
+    const long long dense = (long long)nb * pl.cell_elems() * pl.c;
+    const double budget = (double)dense / pl.C;
+    run_allocation(nb, ad, pl.c, b.specT, b.specD, b.norm2, (int)pl.rT.size(), (int)pl.rd.size(), (int)pl.bits.size(),
+                   budget, b, st);
+    std::vector<int> pick(nb);
+    std::vector<double> n2(nb);
+    AllocOut ao;
+    HIP_TRY(hipMemcpyAsync(pick.data(), b.pick, nb * 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipMemcpyAsync(n2.data(), b.norm2, nb * 8, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipMemcpyAsync(&ao, b.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
+    const long long per = (long long)pl.bits.size() * pl.rT.size() * pl.rd.size();
+    std::vector<double> tab_e((size_t)nb * per);
+    HIP_TRY(hipMemcpyAsync(tab_e.data(), b.tab_e, tab_e.size() * 8, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(n2[c]), JOLT_ENONFINITE, "non-finite ||X||^2 in a cell");
+    if (h_lambda) *h_lambda = ao.lambda;
+    JOLT_REQUIRE(ao.status == 0, JOLT_EINFEASIBLE, "allocation infeasible: the smallest picks exceed the budget");
+    const int nT = (int)pl.rT.size(), nD = (int)pl.rd.size();
+    std::vector<CellPick> cp(nb);
+    long long off = 0;
+    int kmax = 8, kmax_d = 8;
+    for (int c = 0; c < nb; ++c) {
+      const int i = pick[c];
+      CellPick &p = cp[c];
+      p.bits = pl.bits[i / (nT * nD)];
+      p.rT = pl.rT[(i / nD) % nT];
+      p.rd = pl.rd[i % nD];
+      p.sec = layout(pl.G, pl.H, pl.T, pl.D, pl.c, p.rT, p.rd, p.bits);
+      p.off = off;
+      off += p.sec.end;
+      kmax = std::max(kmax, p.rT);
+      kmax_d = std::max(kmax_d, p.rd);
+      jolt_pick &h = h_picks[c];
+      h.rT = p.rT; h.rd = p.rd; h.bits = p.bits; h.pad = 0;
+      h.bytes = eq1_bytes(pl.G, pl.H, pl.T, pl.D, pl.c, p.rT, p.rd, p.bits);
+      h.err_pred = tab_e[(size_t)c * per + i];
+      h.offset = p.off;
+      h.section_bytes = p.sec.end;
+    }
+    JOLT_REQUIRE((size_t)off <= out_bytes, JOLT_EBUFFER, "output buffer too small for the blob");
+    Sizes fsz = sizes_for(pl, kmax, kmax_d);
+    // the fit reuses the worst-case carving (sizes only shrink)
+    Sizes use = sz;
+    use.kmax = fsz.kmax;
+    use.kmax_d = fsz.kmax_d;
+    use.Kb = fsz.Kb;
+    stage_fit(pl, b, use, d_K, d_V, (char *)d_out, cp, st);
+    return 0;
+  });
+}
+
+int jolt_reconstruct(const void *d_blob, const jolt_cache_desc *desc, const jolt_params *params,
+                     const jolt_pick *h_picks, void *d_K_out, void *d_V_out, void *d_ws, size_t ws_bytes,
+                     void *stream) {
+  return guarded([&]() {
+    Plan pl = make_plan(desc, params);
+    hipStream_t st = S(stream);
+    JOLT_REQUIRE(d_blob && h_picks && d_K_out && d_V_out, JOLT_EINVAL, "null argument");
+    JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
+    const int nb = pl.n_cells, D = pl.D, GH = pl.GH;
+    int kmax = 8, kmd = 8;
+    for (int c = 0; c < nb; ++c) {
+      const jolt_pick &p = h_picks[c];
+      JOLT_REQUIRE(p.rT >= 8 && p.rT % 8 == 0 && p.rT <= pl.T && p.rd >= 8 && p.rd % 8 == 0 && p.rd <= D &&
+                       p.bits >= 0 && p.bits <= 8 && p.offset >= 0 && p.offset % 256 == 0,
+                   JOLT_EINVAL, "bad pick");
+      kmax = std::max(kmax, p.rT);
+      kmd = std::max(kmd, p.rd);
+    }
+    Arena ar;
+    ar.dry = false;
+    ar.base = (char *)d_ws;
+    ar.cap = ws_bytes;
+    const int Kd = (int)rup(kmax, 8);
+    float *Udr = ar.take<float>((long long)nb * kmd * D);
+    float *Cr = ar.take<float>((long long)nb * GH * kmax * kmd);
+    float *Dm = ar.take<float>((long long)nb * GH * D * Kd);
+    float *am = ar.take<float>(2LL * nb);
+    char *params_area = ar.take<char>(64 * 1024 + (long long)nb * (sizeof(FactorCell) + sizeof(DecCell)) + 2LL * D * D * 4);
+    Upload u;
+    std::vector<FactorCell> fc(nb);
+    std::vector<DecCell> dc(nb);
+    const long long cellX = pl.cell_elems();
+    const char *blob = (const char *)d_blob;
+    std::vector<size_t> rot_offs;
+    {
+      const std::vector<double> &Q = rotation(D, pl.rot_seed);
+      std::vector<float> qf(Q.size());
+      for (size_t i = 0; i < Q.size(); ++i) qf[i] = (float)Q[i];
+      rot_offs.push_back(u.add(qf.data(), qf.size() * 4));
+    }
+    for (int c = 0; c < nb; ++c) {
+      const jolt_pick &p = h_picks[c];
+      Section sec = layout(pl.G, pl.H, pl.T, D, pl.c, p.rT, p.rd, p.bits);
+      FactorCell &f = fc[c];
+      memset(&f, 0, sizeof(f));
+      f.UT = (void *)(blob + p.offset + sec.off_UT);
+      f.Ud = (void *)(blob + p.offset + sec.off_Ud);
+      f.core = (void *)(blob + p.offset + sec.off_core);
+      f.rT = p.rT; f.rd = p.rd; f.bits = p.bits;
+      const int s = c / (2 * pl.n_groups), g = (c / 2) % pl.n_groups, t = c % 2;
+      char *ob = (char *)(t == 0 ? d_K_out : d_V_out);
+      DecCell &d = dc[c];
+      d.UT = f.UT;
+      d.Dm = Dm + (long long)c * GH * D * Kd;
+      d.Q = nullptr;  // bound after upload
+      d.d_amax = nullptr;
+      d.scales = (const float *)(blob + p.offset + sec.off_scales);
+      d.codes = (const uint8_t *)(blob + p.offset + sec.off_codes);
+      d.out = ob + ((long long)s * pl.n_groups + g) * cellX * pl.c;
+      d.GH = GH; d.rT = p.rT; d.bits = p.bits; d.Kd = Kd;
+    }
+    size_t o_fc = u.add(fc.data(), nb * sizeof(FactorCell));
+    const float *Qdev = (const float *)(params_area + rot_offs[0]);
+    for (int c = 0; c < nb; ++c) {
+      dc[c].Q = Qdev;
+      dc[c].d_amax = am + c;
+    }
+    size_t o_dc = u.add(dc.data(), nb * sizeof(DecCell));
+    HIP_TRY(hipMemcpyAsync(params_area, u.host.data(), u.host.size(), hipMemcpyHostToDevice, st));
+    FactorCell *d_fc = (FactorCell *)(params_area + o_fc);
+    fill_f32(Udr, (long long)nb * kmd * D, 0.f, st);
+    fill_f32(Cr, (long long)nb * GH * kmax * kmd, 0.f, st);
+    get_small(pl.dtype, d_fc, nb, kmax, kmd, D, GH, Udr, Cr, st);
+    amax_cells(Cr, (long long)GH * kmax * kmd, (long long)GH * kmax * kmd, nb, am + nb, st);
+    // Dm[cell][j][n][r] = sum_kk Udr[kk][n] Cr[j][r][kk]
+    GemmArgs g = ga();
+    g.A = Udr; g.a_ld = D; g.a_bs = (long long)kmd * D; g.a_bs2 = 0; g.a_amax_c = 1.f;
+    g.B = Cr; g.b_ld = kmd; g.b_bs = (long long)GH * kmax * kmd; g.b_bs2 = (long long)kmax * kmd;
+    g.b_amax = am + nb; g.ab_amax_bs = 1;
+    g.inner = GH;
+    g.M = D; g.N = kmax; g.K = kmd;
+    g.C = Dm; g.c_ld = Kd; g.c_bs = (long long)GH * D * Kd; g.c_bs2 = (long long)D * Kd;
+    gemm(MF_F16, SRC_F32, false, SRC_F32, true, g, nb * GH, 1, st);
+    amax_cells(Dm, (long long)GH * D * Kd, (long long)GH * D * Kd, nb, am, st);
+    decode_cells(pl.dtype, (const DecCell *)(params_area + o_dc), nb, pl.T, D, GH, st);
+    return 0;
+  });
+}
+
+size_t jolt_encode_residual_workspace_bytes(int32_t G, int32_t H, int32_t T, int32_t D, int32_t rT, int32_t rd) {
+  if (G <= 0 || H <= 0 || T <= 0 || (D != 64 && D != 128) || rT < 8 || rd < 8) return 0;
+  const long long GH = (long long)G * H, Kb = rup(D + rT, 8);
+  long long bytes = 0;
+  auto add = [&](long long n) { bytes += rup(std::max<long long>(n, 1), 256); };
+  add(rd * D * 4LL); add(GH * rT * rd * 4LL); add(D * rd * 4LL); add(GH * D * Kb * 4LL); add(16);
+  add(64 * 1024 + 2LL * D * D * 4);
+  return (size_t)bytes + 4096;
+}
+
+int jolt_encode_residual(const void *d_X, int32_t G, int32_t H, int32_t T, int32_t D, int32_t dtype, const void *d_UT,
+                         const void *d_core, const void *d_Ud, int32_t rT, int32_t rd, int32_t bits, uint64_t rot_seed,
+                         float *d_scales, uint8_t *d_codes, void *d_ws, size_t ws_bytes, void *stream) {
+  return guarded([&]() {
+    JOLT_REQUIRE(d_X && d_UT && d_core && d_Ud && d_scales && d_codes, JOLT_EINVAL, "null argument");
+    JOLT_REQUIRE(G > 0 && H > 0 && T > 0 && (D == 64 || D == 128), JOLT_EINVAL, "bad shape");
+    JOLT_REQUIRE(dtype == JOLT_F16 || dtype == JOLT_BF16 || dtype == JOLT_F32, JOLT_EINVAL, "bad dtype");
+    JOLT_REQUIRE(rT >= 8 && rT % 8 == 0 && rT <= T && rd >= 8 && rd % 8 == 0 && rd <= D, JOLT_EINVAL, "bad ranks");
+    JOLT_REQUIRE(bits >= 1 && bits <= 8, JOLT_EINVAL, "bits must lie in 1..8");
+    JOLT_REQUIRE(d_ws != nullptr && ws_bytes >= jolt_encode_residual_workspace_bytes(G, H, T, D, rT, rd),
+                 JOLT_EWORKSPACE, "workspace too small");
+    hipStream_t st = S(stream);
+    const int GH = G * H, Kb = (int)rup(D + rT, 8);
+    Arena ar;
+    ar.dry = false;
+    ar.base = (char *)d_ws;
+    ar.cap = ws_bytes;
+    float *Udr = ar.take<float>((long long)rd * D);
+    float *Cr = ar.take<float>((long long)GH * rT * rd);
+    float *Vt = ar.take<float>((long long)D * rd);
+    float *Bcat = ar.take<float>((long long)GH * D * Kb);
+    float *am = ar.take<float>(4);
+    char *pa = ar.take<char>(64 * 1024 + 2LL * D * D * 4);
+    Upload u;
+    FactorCell f;
+    memset(&f, 0, sizeof(f));
+    f.UT = (void *)d_UT; f.Ud = (void *)d_Ud; f.core = (void *)d_core; f.rT = rT; f.rd = rd; f.bits = bits;
+    size_t o_fc = u.add(&f, sizeof(f));
+    const std::vector<double> &Q = rotation(D, rot_seed);
+    std::vector<float> qt(Q.size());
+    for (int i = 0; i < D; ++i)
+      for (int j = 0; j < D; ++j) qt[(size_t)j * D + i] = (float)Q[(size_t)i * D + j];
+    size_t o_qt = u.add(qt.data(), qt.size() * 4);
+    EncCell e;
+    e.X = d_X; e.UT = d_UT; e.Bcat = Bcat; e.b_amax = am; e.scales = d_scales; e.codes = d_codes;
+    e.GH = GH; e.rT = rT; e.bits = bits; e.Kb = Kb;
+    size_t o_ec = u.add(&e, sizeof(e));
+    HIP_TRY(hipMemcpyAsync(pa, u.host.data(), u.host.size(), hipMemcpyHostToDevice, st));
+    const float *Qtf = (const float *)(pa + o_qt);
+    get_small(dtype, (const FactorCell *)(pa + o_fc), 1, rT, rd, D, GH, Udr, Cr, st);
+    GemmArgs g = ga();
+    g.A = Qtf; g.a_ld = D; g.a_amax_c = 1.f;
+    g.B = Udr; g.b_ld = D; g.b_amax_c = 1.f;
+    g.M = D; g.N = rd; g.K = D;
+    g.C = Vt; g.c_ld = rd;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, 1, 1, st);
+    amax_cells(Cr, (long long)GH * rT * rd, 0, 1, am + 1, st);
+    bcat_q(Bcat, 1, GH, D, Kb, Qtf, st);
+    GemmArgs h = ga();
+    h.A = Vt; h.a_ld = rd; h.a_amax_c = 1.f;
+    h.B = Cr; h.b_ld = rd; h.b_bs2 = (long long)rT * rd; h.b_amax = am + 1; h.ab_amax_bs = 1;
+    h.inner = GH;
+    h.M = D; h.N = rT; h.K = rd;
+    h.C = Bcat + D; h.c_ld = Kb; h.c_bs2 = (long long)D * Kb;
+    h.alpha = -1.f;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, true, h, GH, 1, st);
+    amax_cells(Bcat, (long long)GH * D * Kb, 0, 1, am, st);
+    encode_cells(dtype, (const EncCell *)(pa + o_ec), 1, T, D, GH, st);
+    return 0;
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,385 @@
+// Residual codec of the method (Sec. 3, "Rotated low-bit residual"): fused encode and decode.
+//
+// Encode, per cell, per head-slice j = (l, h) and 128-token tile:
+//   E_rot = (X_j - U_T D_j) Q = [X_j | U_T] [Q ; -D_j Q]     (one MFMA pass, K = d_h + r_T)
+//   per row: absmax (wavefront + cross-wave reduction), s = absmax / q_max (fp32),
+//   code = clamp(rint(e / s)), packed b bits per element LSB-first, one fp32 scale per row.
+// Decode:
+//   X_hat_j = s (codes Q^T) + U_T D_j                         (two MFMA passes, one accumulator)
+// D_j = C_j U_d^T is the backbone slice; the operand [Q ; -D_j Q] is prepared per cell.
+// fp32 operands are split into 16-bit planes exactly as in the GEMM kernel; cache values and
+// codes are exact in 16 bits.
+#include "common.hpp"
+#include "gemm_core.hpp"
+#include "codec.hpp"
+
+namespace jolt {
+
+namespace {
+
+using namespace core;
+
+template <int MF>
+__device__ __forceinline__ void mma_step(const uint16_t *As, int pa_n, const uint16_t *Bs, int pb_n, int maxo,
+                                         int wm, int wn, int lane, f32x4 (&acc)[4][4]) {
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  uint4 af[3][4], bf[3][4];
+  for (int p = 0; p < pa_n; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) af[p][i] = *(const uint4 *)(As + p * BM * LDK + (wm * 64 + i * 16 + fr) * LDK + fk);
+  for (int p = 0; p < pb_n; ++p)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[p][j] = *(const uint4 *)(Bs + p * BN * LDK + (wn * 64 + j * 16 + fr) * LDK + fk);
+  for (int pa = pa_n - 1; pa >= 0; --pa)
+    for (int pb = pb_n - 1; pb >= 0; --pb)
+      if (pa + pb <= maxo)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma<MF>(af[pa][i], bf[pb][j], acc[i][j]);
+}
+
+// 16-bit plane count of a source under the MFMA type; for fp32 with f16 MFMA the B operand of
+// the codec uses NB16 planes (hi, lo[, lo2]).
+template <int S, int MF, int NB16>
+struct CPlanes {
+  static constexpr int n = (S == SRC_F32) ? (MF == MF_F16 ? NB16 : 3) : 1;
+};
+
+template <int S, int MF, int NB16>
+__device__ __forceinline__ void csplit(float x, float scale, uint16_t (&p)[3]) {
+  if constexpr (S == SRC_F32 && MF == MF_F16 && NB16 == 3) split3_f16(x, scale, p);
+  else split_planes<S, MF>(x, scale, p);
+}
+
+// ------------------------------------------------------------------------------------------ encode
+template <int MF, int SX, int NB16>
+__global__ void __launch_bounds__(NT) encode_kernel(const EncCell *cells, int T, int D, int ttiles) {
+  constexpr int PA = CPlanes<SX, MF, NB16>::n;
+  constexpr int PB = CPlanes<SRC_F32, MF, NB16>::n;
+  constexpr int MAXO = (MF == MF_F16) ? (NB16 - 1) : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t As[PA * BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[PB * BN * LDK];
+  __shared__ float smax[2][BM];
+  __shared__ uint8_t ucode[BM * 128];
+
+  const EncCell c = cells[blockIdx.z];
+  const int j = blockIdx.x / ttiles, tt = blockIdx.x % ttiles;
+  if (j >= c.GH) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = tt * BM;
+  const int K = D + c.rT;
+  const long long xoff = (long long)j * T * D;
+  const float *Bj = c.Bcat + (long long)j * D * c.Kb;
+  const float bscale = (MF == MF_F16) ? f16_split_scale(*c.b_amax) : 1.f;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float ra[2][8], rb[2][8];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      int v = tid + it * NT;
+      int r = v >> 2, kv = (v & 3) * 8;
+      int t = t0 + r;
+      int k = k0 + kv;
+      if (k < D) load8<SX>(c.X, xoff + (long long)t * D, k, D, t < T, 1 << 30, 0, ra[it]);
+      else load8<SX>(c.UT, (long long)t * c.rT, k - D, c.rT, t < T, 1 << 30, 0, ra[it]);
+      load8<SRC_F32>(Bj, (long long)r * c.Kb, k0 + kv, K, r < D, 1 << 30, 0, rb[it]);
+    }
+  };
+  auto lstore = [&](int) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      int v = tid + it * NT;
+      uint16_t pa[8][3], pb[8][3];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        split_planes<SX, MF>(ra[it][i], 1.f, pa[i]);
+        csplit<SRC_F32, MF, NB16>(rb[it][i], bscale, pb[i]);
+      }
+      lds_store8<PA, true>(As, BM, v >> 2, (v & 3) * 8, pa);
+      lds_store8<PB, true>(Bs, BN, v >> 2, (v & 3) * 8, pb);
+    }
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const bool more = k0 + BK < K;
+    if (more) gload(k0 + BK);
+    mma_step<MF>(As, PA, Bs, PB, MAXO, wm, wn, lane, acc);
+    __syncthreads();
+    if (more) {
+      lstore(k0 + BK);
+      __syncthreads();
+    }
+  }
+
+  // ---- quantisation epilogue -------------------------------------------------------------
+  const float inv = 1.f / bscale;
+  const int b = c.bits;
+  const int qm = (b >= 2) ? ((1 << (b - 1)) - 1) : 1;
+  const int fr = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float m = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int n = wn * 64 + q * 16 + fr;
+        float v = acc[i][q][r] * inv;
+        acc[i][q][r] = v;
+        if (n < D) m = fmaxf(m, fabsf(v));
+      }
+      m = fmaxf(m, __shfl_xor(m, 1, 64));
+      m = fmaxf(m, __shfl_xor(m, 2, 64));
+      m = fmaxf(m, __shfl_xor(m, 4, 64));
+      m = fmaxf(m, __shfl_xor(m, 8, 64));
+      if (fr == 0) smax[wn][wm * 64 + i * 16 + (lane >> 4) * 4 + r] = m;
+    }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+      const float amax = fmaxf(smax[0][row], smax[1][row]);
+      const float s = (b == 1) ? amax : amax / (float)qm;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        int n = wn * 64 + q * 16 + fr;
+        if (n < D) {
+          float v = acc[i][q][r];
+          int u;
+          if (b == 1) u = (v >= 0.f) ? 1 : 0;
+          else if (s > 0.f) {
+            float qv = rintf(v / s);
+            qv = fminf(fmaxf(qv, (float)-qm), (float)qm);
+            u = (int)qv + qm;
+          } else u = qm;
+          ucode[row * 128 + n] = (uint8_t)u;
+        }
+      }
+    }
+  __syncthreads();
+  const long long row0 = (long long)j * T + t0;
+  const int nrows = min(BM, T - t0);
+  for (int rr = tid; rr < nrows; rr += NT) {
+    float amax = fmaxf(smax[0][rr], smax[1][rr]);
+    c.scales[row0 + rr] = (b == 1) ? amax : amax / (float)qm;
+  }
+  const int wpr = D * b / 32;  // 32-bit words per row (D in {64,128}: integral)
+  uint32_t *out = (uint32_t *)(c.codes + row0 * (D * b / 8));
+  for (int w = tid; w < nrows * wpr; w += NT) {
+    const int rr = w / wpr, wi = w % wpr;
+    const int bit0 = wi * 32;
+    const int e0 = bit0 / b, e1 = min(D - 1, (bit0 + 31) / b);
+    uint32_t word = 0;
+    for (int e = e0; e <= e1; ++e) {
+      uint32_t u = ucode[rr * 128 + e];
+      int pos = e * b - bit0;
+      if (pos >= 0) word |= (pos < 32) ? (u << pos) : 0u;
+      else word |= u >> (-pos);
+    }
+    out[w] = word;
+  }
+}
+
+// ------------------------------------------------------------------------------------------ decode
+// unpack 8 codes (elements k0..k0+7 of row) to their signed values
+__device__ __forceinline__ void unpack8(const uint8_t *rowp, int k0, int b, float (&v)[8]) {
+  const uint8_t *p = rowp + (k0 * b) / 8;
+  uint64_t w = 0;
+  for (int i = 0; i < b; ++i) w |= (uint64_t)p[i] << (8 * i);
+  const int qm = (b >= 2) ? ((1 << (b - 1)) - 1) : 1;
+  const uint64_t mask = (1ull << b) - 1ull;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int u = (int)((w >> (i * b)) & mask);
+    v[i] = (b == 1) ? (u ? 1.f : -1.f) : (float)(u - qm);
+  }
+}
+
+template <int MF, int SX, int NB16>
+__global__ void __launch_bounds__(NT) decode_kernel(const DecCell *cells, int T, int D, int ttiles) {
+  constexpr int PA = CPlanes<SX, MF, NB16>::n;  // U_T part; the codes part uses one plane
+  constexpr int PB = CPlanes<SRC_F32, MF, NB16>::n;
+  constexpr int MAXO_U = (MF == MF_F16) ? (NB16 - 1) : 2;
+  constexpr int MAXO_C = (MF == MF_F16) ? (NB16 - 1) : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t As[PA * BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[PB * BN * LDK];
+  __shared__ float srow[BM];
+
+  const DecCell c = cells[blockIdx.z];
+  const int j = blockIdx.x / ttiles, tt = blockIdx.x % ttiles;
+  if (j >= c.GH) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = tt * BM;
+  const int fr = lane & 15;
+  const float qscale = (MF == MF_F16) ? f16_split_scale(1.f) : 1.f;
+  const float dscale = (MF == MF_F16) ? f16_split_scale(*c.d_amax) : 1.f;
+  const int b = c.bits;
+  const int rowbytes = D * b / 8;
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float ra[2][8], rb[2][8];
+  // ---- phase 1: codes Q^T, then scale rows ---------------------------------------------------
+  if (b > 0) {
+    auto gload = [&](int k0) {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        int v = tid + it * NT;
+        int r = v >> 2, kv = (v & 3) * 8;
+        int t = t0 + r;
+        if (t < T) unpack8(c.codes + ((long long)j * T + t) * rowbytes, k0 + kv, b, ra[it]);
+        else
+#pragma unroll
+          for (int i = 0; i < 8; ++i) ra[it][i] = 0.f;
+        load8<SRC_F32>(c.Q, (long long)r * D, k0 + kv, D, r < D, 1 << 30, 0, rb[it]);
+      }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        int v = tid + it * NT;
+        uint16_t pa[8][3], pb[8][3];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          split_planes<(MF == MF_F16 ? SRC_F16 : SRC_BF16), MF>(ra[it][i], 1.f, pa[i]);  // small integers: exact
+          csplit<SRC_F32, MF, NB16>(rb[it][i], qscale, pb[i]);
+        }
+        lds_store8<1, true>(As, BM, v >> 2, (v & 3) * 8, pa);
+        lds_store8<PB, true>(Bs, BN, v >> 2, (v & 3) * 8, pb);
+      }
+    };
+    gload(0);
+    lstore();
+    __syncthreads();
+    for (int k0 = 0; k0 < D; k0 += BK) {
+      const bool more = k0 + BK < D;
+      if (more) gload(k0 + BK);
+      mma_step<MF>(As, 1, Bs, PB, MAXO_C, wm, wn, lane, acc);
+      __syncthreads();
+      if (more) {
+        lstore();
+        __syncthreads();
+      }
+    }
+    for (int rr = tid; rr < BM; rr += NT) srow[rr] = (t0 + rr < T) ? c.scales[(long long)j * T + t0 + rr] : 0.f;
+    __syncthreads();
+    const float inv = 1.f / qscale;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s = srow[wm * 64 + i * 16 + (lane >> 4) * 4 + r] * inv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[i][q][r] *= s;
+      }
+  }
+  // ---- phase 2: + U_T D_j ------------------------------------------------------------------
+  {
+    // rescale the running accumulator into the (dscale-scaled) frame of phase 2
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[i][q] *= dscale;
+    const float *Dj = c.Dm + (long long)j * D * c.Kd;
+    auto gload = [&](int k0) {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        int v = tid + it * NT;
+        int r = v >> 2, kv = (v & 3) * 8;
+        int t = t0 + r;
+        load8<SX>(c.UT, (long long)t * c.rT, k0 + kv, c.rT, t < T, 1 << 30, 0, ra[it]);
+        load8<SRC_F32>(Dj, (long long)r * c.Kd, k0 + kv, c.rT, r < D, 1 << 30, 0, rb[it]);
+      }
+    };
+    auto lstore = [&]() {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        int v = tid + it * NT;
+        uint16_t pa[8][3], pb[8][3];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          split_planes<SX, MF>(ra[it][i], 1.f, pa[i]);
+          csplit<SRC_F32, MF, NB16>(rb[it][i], dscale, pb[i]);
+        }
+        lds_store8<PA, true>(As, BM, v >> 2, (v & 3) * 8, pa);
+        lds_store8<PB, true>(Bs, BN, v >> 2, (v & 3) * 8, pb);
+      }
+    };
+    gload(0);
+    lstore();
+    __syncthreads();
+    for (int k0 = 0; k0 < c.rT; k0 += BK) {
+      const bool more = k0 + BK < c.rT;
+      if (more) gload(k0 + BK);
+      mma_step<MF>(As, PA, Bs, PB, MAXO_U, wm, wn, lane, acc);
+      __syncthreads();
+      if (more) {
+        lstore();
+        __syncthreads();
+      }
+    }
+  }
+  const float inv = 1.f / dscale;
+  const long long obase = (long long)j * T * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+      if (t >= T) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = wn * 64 + q * 16 + fr;
+        if (n < D) store_elem<SX>(c.out, obase + (long long)t * D + n, acc[i][q][r] * inv);
+      }
+    }
+}
+
+template <int MF, int SX, int NB16>
+void launch_enc(const EncCell *cells, int ncells, int T, int D, int GHmax, hipStream_t st) {
+  int tt = (T + BM - 1) / BM;
+  hipLaunchKernelGGL((encode_kernel<MF, SX, NB16>), dim3(tt * GHmax, 1, ncells), dim3(NT), 0, st, cells, T, D, tt);
+}
+template <int MF, int SX, int NB16>
+void launch_dec(const DecCell *cells, int ncells, int T, int D, int GHmax, hipStream_t st) {
+  int tt = (T + BM - 1) / BM;
+  hipLaunchKernelGGL((decode_kernel<MF, SX, NB16>), dim3(tt * GHmax, 1, ncells), dim3(NT), 0, st, cells, T, D, tt);
+}
+
+}  // namespace
+
+void encode_cells(int dtype, const EncCell *d_cells, int ncells, int T, int D, int GHmax, hipStream_t st) {
+  JOLT_REQUIRE(D == 64 || D == 128, JOLT_EINVAL, "codec: d_head must be 64 or 128");
+  if (dtype == JOLT_F16) launch_enc<MF_F16, SRC_F16, 2>(d_cells, ncells, T, D, GHmax, st);
+  else if (dtype == JOLT_BF16) launch_enc<MF_BF16, SRC_BF16, 2>(d_cells, ncells, T, D, GHmax, st);
+  else launch_enc<MF_BF16, SRC_F32, 2>(d_cells, ncells, T, D, GHmax, st);
+  HIP_LAUNCH_CHECK();
+}
+
+void decode_cells(int dtype, const DecCell *d_cells, int ncells, int T, int D, int GHmax, hipStream_t st) {
+  JOLT_REQUIRE(D == 64 || D == 128, JOLT_EINVAL, "codec: d_head must be 64 or 128");
+  if (dtype == JOLT_F16) launch_dec<MF_F16, SRC_F16, 2>(d_cells, ncells, T, D, GHmax, st);
+  else if (dtype == JOLT_BF16) launch_dec<MF_BF16, SRC_BF16, 2>(d_cells, ncells, T, D, GHmax, st);
+  else launch_dec<MF_BF16, SRC_F32, 2>(d_cells, ncells, T, D, GHmax, st);
+  HIP_LAUNCH_CHECK();
+}
+
+}  // namespace jolt

@@ -1,0 +1,137 @@
+// Shared definitions of libjolt (host and device).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string>
+
+#include "../../include/jolt.h"
+
+namespace jolt {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf168 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum Src { SRC_F16 = 0, SRC_BF16 = 1, SRC_F32 = 2 };
+enum Mf { MF_F16 = 0, MF_BF16 = 1 };
+
+inline int dtype_bytes(int dt) { return dt == JOLT_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------------------------
+// error reporting (thread-local message; the status is the return value)
+// ---------------------------------------------------------------------------------------------
+void set_error(const std::string &msg);
+const char *get_error();
+
+struct Fail {
+  int status;
+};
+
+#define JOLT_REQUIRE(cond, status, msg)                                                         \
+  do {                                                                                          \
+    if (!(cond)) {                                                                              \
+      ::jolt::set_error(std::string(msg));                                                      \
+      throw ::jolt::Fail{status};                                                               \
+    }                                                                                           \
+  } while (0)
+
+#define HIP_TRY(expr)                                                                           \
+  do {                                                                                          \
+    hipError_t e_ = (expr);                                                                     \
+    if (e_ != hipSuccess) {                                                                     \
+      ::jolt::set_error(std::string(#expr) + ": " + hipGetErrorString(e_));                    \
+      throw ::jolt::Fail{JOLT_EHIP};                                                            \
+    }                                                                                           \
+  } while (0)
+
+#define HIP_LAUNCH_CHECK() HIP_TRY(hipGetLastError())
+
+// ---------------------------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t r = 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)((u + r) >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+template <int S>
+__device__ __forceinline__ float load_elem(const void *p, long long i) {
+  if constexpr (S == SRC_F32) return ((const float *)p)[i];
+  else if constexpr (S == SRC_F16) return f16_to_f32(((const uint16_t *)p)[i]);
+  else return bf16_to_f32(((const uint16_t *)p)[i]);
+}
+
+template <int S>
+__device__ __forceinline__ void store_elem(void *p, long long i, float v) {
+  if constexpr (S == SRC_F32) ((float *)p)[i] = v;
+  else if constexpr (S == SRC_F16) ((uint16_t *)p)[i] = f32_to_f16_rne(v);
+  else ((uint16_t *)p)[i] = f32_to_bf16_rne(v);
+}
+
+// power-of-two scale that maps amax into [2^14, 2^15) (fp16 split of fp32 operands)
+__device__ __forceinline__ float f16_split_scale(float amax) {
+  if (!(amax > 0.f) || !isfinite(amax)) return 1.f;
+  int e = ilogbf(amax);
+  return ldexpf(1.f, 14 - e);
+}
+
+__device__ __forceinline__ float warp_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ double warp_sum_d(double v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------------------------
+// GEMM on MFMA with exact splitting of fp32 operands into 16-bit planes
+// C[b](m, n) = c_scale * sum_k A[b](m, k) B[b](k, n), fp32 output.
+// ---------------------------------------------------------------------------------------------
+struct GemmArgs {
+  const void *A;
+  const void *B;
+  float *C;
+  int M, N, K;
+  long long a_bs, b_bs, c_bs;  // batch strides (elements)
+  long long a_ld;              // stride of A's strided dim
+  long long a_blk_stride;      // A's contiguous dim: index i -> (i / a_blk) * a_blk_stride + i % a_blk
+  int a_blk;
+  long long b_ld;
+  long long b_blk_stride;
+  int b_blk;
+  long long c_ld;
+  long long c_split;  // stride between split-K partial outputs (elements)
+  int k_chunk;        // K per split, multiple of 32
+  const float *a_amax;  // per-batch |A| bound for the fp16 split (device), or null -> a_amax_c
+  float a_amax_c;
+  const float *b_amax;
+  float b_amax_c;
+  float *c_amax;  // optional per-batch running max |C| (float bits, atomic max)
+  int m_fastest;  // tile order: m tiles adjacent (else n tiles adjacent)
+  // two-level batch: grid z = outer * inner + in; offsets outer*x_bs + in*x_bs2; amax pointers
+  // are indexed by outer * (ab_amax_bs | c_amax_bs)
+  int inner;
+  long long a_bs2, b_bs2, c_bs2;
+  int ab_amax_bs, c_amax_bs;
+  float alpha;  // output multiplier
+};
+
+// a_kc: A contiguous along K (else along M); b_kc: B contiguous along K (else along N)
+void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int batch, int nsplit,
+          hipStream_t st);
+
+// sum of split-K partials in fixed order: out[b][i] = sum_s part[b][s][i] (fp64 accumulate)
+void reduce_splits(const float *part, long long part_bs, long long part_ss, int nsplit, long long n,
+                   int rows, int cols, long long ld_in, void *out, bool out_f64, long long out_bs,
+                   long long ld_out, int batch, hipStream_t st);
+
+}  // namespace jolt

@@ -1,0 +1,237 @@
+// Dense contractions on gfx950 matrix cores (v_mfma_f32_16x16x32_{f16,bf16}).
+//
+// Every GEMM of the compressor (sketch, power-iteration and projection products against the
+// cache, Gram matrices, triangular applies of the thin QR) runs through this kernel.  The
+// cache enters at its own 16-bit precision (exact).  fp32 operands are split exactly into
+// 16-bit planes inside the LDS store (fp16: hi + lo after a power-of-two scale, 22 bits;
+// bf16: three planes, 24 bits) and the cross products that matter are accumulated in fp32,
+// which keeps fp32-class accuracy at matrix-core rates.
+//
+// Tile 128 x 128 x 32, 256 threads (4 waves in 2 x 2, each 64 x 64 = 4 x 4 MFMA tiles).
+// LDS holds every plane of the A and B tiles as [row][k] with k contiguous (row pitch 40
+// halves).  Sources contiguous along M or N are transposed while being stored.
+// Block ids are remapped so that tiles sharing an operand panel run on the same XCD.
+#include "common.hpp"
+#include "gemm_core.hpp"
+
+namespace jolt {
+
+namespace {
+
+using namespace core;
+
+template <int MF, int SA, bool AKC, int SB, bool BKC>
+__global__ void __launch_bounds__(NT) gemm_kernel(GemmArgs g) {
+  constexpr int PA = Planes<SA, MF>::n, PB = Planes<SB, MF>::n;
+  constexpr int MAXO = (MF == MF_F16) ? 1 : 2;  // keep cross products with plane order i+j <= MAXO
+  __shared__ __attribute__((aligned(16))) uint16_t As[PA * BM * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[PB * BN * LDK];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int zb = blockIdx.z, split = blockIdx.y;
+  const int inner = g.inner > 0 ? g.inner : 1;
+  const int batch = zb / inner, bin = zb % inner;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int ntiles = tiles_m * tiles_n;
+  // XCD-aware remap: hardware block b runs on XCD b % 8; give each XCD a contiguous range.
+  int b = blockIdx.x, t = b;
+  {
+    int per = ntiles / 8;
+    if (b < per * 8) t = (b % 8) * per + b / 8;
+  }
+  int tm, tn;
+  if (g.m_fastest) { tm = t % tiles_m; tn = t / tiles_m; }
+  else { tn = t % tiles_n; tm = t / tiles_n; }
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const int kbeg = split * g.k_chunk;
+  const int kend = min(g.K, kbeg + g.k_chunk);
+  if (kbeg >= kend && split > 0) return;
+
+  const char *Ab = (const char *)g.A + ((long long)batch * g.a_bs + (long long)bin * g.a_bs2) * (SA == SRC_F32 ? 4 : 2);
+  const char *Bb = (const char *)g.B + ((long long)batch * g.b_bs + (long long)bin * g.b_bs2) * (SB == SRC_F32 ? 4 : 2);
+  float ascale = 1.f, bscale = 1.f;
+  if constexpr (SA == SRC_F32 && MF == MF_F16)
+    ascale = f16_split_scale(g.a_amax ? g.a_amax[(long long)batch * g.ab_amax_bs] : g.a_amax_c);
+  if constexpr (SB == SRC_F32 && MF == MF_F16)
+    bscale = f16_split_scale(g.b_amax ? g.b_amax[(long long)batch * g.ab_amax_bs] : g.b_amax_c);
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  float ra[2][8], rb[2][8];
+
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      int v = tid + it * NT;
+      if constexpr (AKC) {
+        int r = v >> 2, kv = (v & 3) * 8;
+        int m = m0 + r;
+        load8<SA>(Ab, (long long)m * g.a_ld, k0 + kv, kend, m < g.M, g.a_blk, g.a_blk_stride, ra[it]);
+      } else {
+        int kr = v >> 4, mv = (v & 15) * 8;
+        int k = k0 + kr;
+        load8<SA>(Ab, (long long)k * g.a_ld, m0 + mv, g.M, k < kend, g.a_blk, g.a_blk_stride, ra[it]);
+      }
+      if constexpr (BKC) {
+        int r = v >> 2, kv = (v & 3) * 8;
+        int n = n0 + r;
+        load8<SB>(Bb, (long long)n * g.b_ld, k0 + kv, kend, n < g.N, g.b_blk, g.b_blk_stride, rb[it]);
+      } else {
+        int kr = v >> 4, nv = (v & 15) * 8;
+        int k = k0 + kr;
+        load8<SB>(Bb, (long long)k * g.b_ld, n0 + nv, g.N, k < kend, g.b_blk, g.b_blk_stride, rb[it]);
+      }
+    }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      int v = tid + it * NT;
+      uint16_t pa[8][3], pb[8][3];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { split_planes<SA, MF>(ra[it][i], ascale, pa[i]); split_planes<SB, MF>(rb[it][i], bscale, pb[i]); }
+      if constexpr (AKC) lds_store8<PA, true>(As, BM, v >> 2, (v & 3) * 8, pa);
+      else lds_store8<PA, false>(As, BM, (v & 15) * 8, v >> 4, pa);
+      if constexpr (BKC) lds_store8<PB, true>(Bs, BN, v >> 2, (v & 3) * 8, pb);
+      else lds_store8<PB, false>(Bs, BN, (v & 15) * 8, v >> 4, pb);
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+
+  if (kbeg < kend) {
+    gload(kbeg);
+    lstore();
+    __syncthreads();
+    for (int k0 = kbeg; k0 < kend; k0 += BK) {
+      const bool more = k0 + BK < kend;
+      if (more) gload(k0 + BK);
+      uint4 af[PA][4], bf[PB][4];
+#pragma unroll
+      for (int p = 0; p < PA; ++p)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          af[p][i] = *(const uint4 *)(As + p * BM * LDK + (wm * 64 + i * 16 + fr) * LDK + fk);
+#pragma unroll
+      for (int p = 0; p < PB; ++p)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          bf[p][j] = *(const uint4 *)(Bs + p * BN * LDK + (wn * 64 + j * 16 + fr) * LDK + fk);
+#pragma unroll
+      for (int pa = PA - 1; pa >= 0; --pa)
+#pragma unroll
+        for (int pb = PB - 1; pb >= 0; --pb)
+          if (pa + pb <= MAXO)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[i][j] = mfma<MF>(af[pa][i], bf[pb][j], acc[i][j]);
+      __syncthreads();
+      if (more) {
+        lstore();
+        __syncthreads();
+      }
+    }
+  }
+
+  const float cs = g.alpha / (ascale * bscale);
+  float *Cb = g.C + (long long)batch * g.c_bs + (long long)bin * g.c_bs2 + (long long)split * g.c_split;
+  float lmax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+        int n = n0 + wn * 64 + j * 16 + fr;
+        if (m < g.M && n < g.N) {
+          float v = acc[i][j][r] * cs;
+          Cb[(long long)m * g.c_ld + n] = v;
+          lmax = fmaxf(lmax, fabsf(v));
+        }
+      }
+  if (g.c_amax) {
+    lmax = warp_max(lmax);
+    if (lane == 0) atomicMax((unsigned int *)(g.c_amax + (long long)batch * g.c_amax_bs), __float_as_uint(lmax));
+  }
+}
+
+template <int MF, int SA, bool AKC, int SB, bool BKC>
+void launch_t(const GemmArgs &g, int batch, int nsplit, hipStream_t st) {
+  int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
+  dim3 grid(tiles, nsplit, batch);
+  hipLaunchKernelGGL((gemm_kernel<MF, SA, AKC, SB, BKC>), grid, dim3(NT), 0, st, g);
+}
+
+template <int MF, int SA, int SB>
+void launch_layout(bool akc, bool bkc, const GemmArgs &g, int batch, int nsplit, hipStream_t st) {
+  if (akc && bkc) launch_t<MF, SA, true, SB, true>(g, batch, nsplit, st);
+  else if (akc && !bkc) launch_t<MF, SA, true, SB, false>(g, batch, nsplit, st);
+  else if (!akc && bkc) launch_t<MF, SA, false, SB, true>(g, batch, nsplit, st);
+  else launch_t<MF, SA, false, SB, false>(g, batch, nsplit, st);
+}
+
+__global__ void reduce_splits_kernel(const float *part, long long part_bs, long long part_ss, int nsplit,
+                                     int rows, int cols, long long ld_in, void *out, int out_f64,
+                                     long long out_bs, long long ld_out) {
+  const int b = blockIdx.y;
+  long long n = (long long)rows * cols;
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) {
+    int r = (int)(i / cols), c = (int)(i % cols);
+    const float *p = part + b * part_bs + (long long)r * ld_in + c;
+    double s = 0.0;
+    for (int k = 0; k < nsplit; ++k) s += (double)p[k * part_ss];
+    if (out_f64) ((double *)out)[b * out_bs + (long long)r * ld_out + c] = s;
+    else ((float *)out)[b * out_bs + (long long)r * ld_out + c] = (float)s;
+  }
+}
+
+}  // namespace
+
+void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int batch, int nsplit,
+          hipStream_t st) {
+  JOLT_REQUIRE(g.M > 0 && g.N > 0 && g.K > 0 && batch > 0 && nsplit > 0, JOLT_EINVAL, "gemm: empty shape");
+  JOLT_REQUIRE(nsplit == 1 || (g.k_chunk % BK == 0 && (long long)g.k_chunk * nsplit >= g.K), JOLT_EINVAL,
+               "gemm: bad split");
+  JOLT_REQUIRE(g.a_blk % 8 == 0 && g.b_blk % 8 == 0 && g.a_ld % 8 == 0 && g.b_ld % 8 == 0 &&
+                   g.a_blk_stride % 8 == 0 && g.b_blk_stride % 8 == 0 && g.a_bs % 8 == 0 && g.b_bs % 8 == 0 &&
+                   g.a_bs2 % 8 == 0 && g.b_bs2 % 8 == 0 && ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.B % 16) == 0,
+               JOLT_EINVAL, "gemm: operands must be 16-byte aligned with strides in multiples of 8 elements");
+  JOLT_REQUIRE(g.inner >= 1 && batch % g.inner == 0, JOLT_EINVAL, "gemm: bad inner batch");
+  GemmArgs h = g;
+  if (nsplit == 1) h.k_chunk = ((g.K + BK - 1) / BK) * BK;
+  if (mf == MF_F16) {
+    if (sa == SRC_F16 && sb == SRC_F16) launch_layout<MF_F16, SRC_F16, SRC_F16>(a_kc, b_kc, h, batch, nsplit, st);
+    else if (sa == SRC_F16 && sb == SRC_F32) launch_layout<MF_F16, SRC_F16, SRC_F32>(a_kc, b_kc, h, batch, nsplit, st);
+    else if (sa == SRC_F32 && sb == SRC_F16) launch_layout<MF_F16, SRC_F32, SRC_F16>(a_kc, b_kc, h, batch, nsplit, st);
+    else if (sa == SRC_F32 && sb == SRC_F32) launch_layout<MF_F16, SRC_F32, SRC_F32>(a_kc, b_kc, h, batch, nsplit, st);
+    else JOLT_REQUIRE(false, JOLT_EINVAL, "gemm: bad f16 operand types");
+  } else {
+    if (sa == SRC_BF16 && sb == SRC_BF16) launch_layout<MF_BF16, SRC_BF16, SRC_BF16>(a_kc, b_kc, h, batch, nsplit, st);
+    else if (sa == SRC_F32 && sb == SRC_F32) launch_layout<MF_BF16, SRC_F32, SRC_F32>(a_kc, b_kc, h, batch, nsplit, st);
+    else if (sa == SRC_BF16 && sb == SRC_F32) launch_layout<MF_BF16, SRC_BF16, SRC_F32>(a_kc, b_kc, h, batch, nsplit, st);
+    else if (sa == SRC_F32 && sb == SRC_BF16) launch_layout<MF_BF16, SRC_F32, SRC_BF16>(a_kc, b_kc, h, batch, nsplit, st);
+    else JOLT_REQUIRE(false, JOLT_EINVAL, "gemm: bad bf16 operand types");
+  }
+  HIP_LAUNCH_CHECK();
+}
+
+void reduce_splits(const float *part, long long part_bs, long long part_ss, int nsplit, long long n,
+                   int rows, int cols, long long ld_in, void *out, bool out_f64, long long out_bs,
+                   long long ld_out, int batch, hipStream_t st) {
+  (void)n;
+  long long tot = (long long)rows * cols;
+  int blocks = (int)std::min<long long>((tot + 255) / 256, 4096);
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3(blocks, batch), dim3(256), 0, st, part, part_bs, part_ss, nsplit,
+                     rows, cols, ld_in, out, out_f64 ? 1 : 0, out_bs, ld_out);
+  HIP_LAUNCH_CHECK();
+}
+
+}  // namespace jolt

@@ -1,0 +1,555 @@
+// Small dense fp64 linear algebra on the GPU: symmetric eigenproblems (Householder
+// tridiagonalisation, Sturm bisection, inverse iteration, back-transformation), Cholesky with
+// triangular inverse for the thin QR, and an fp64 Gram of fp32 panels.
+//
+// These serve the mode spectra and factors of the method (token-mode and feature-mode
+// singular values/vectors from Gram matrices; the FlashJoLT Rayleigh-Ritz step on B B^T), the
+// matrices are at most a few thousand wide, and one workgroup owns one matrix for the
+// sequential parts.  Algorithms: Golub & Van Loan, "Matrix Computations", Sec. 8.3
+// (tridiagonalisation), Sec. 8.4 (Sturm-sequence bisection), Sec. 8.2/7.6 (inverse iteration);
+// Cholesky QR as in Fukaya et al. (2014).
+#include <math.h>
+
+#include "common.hpp"
+#include "linalg.hpp"
+
+namespace jolt {
+
+namespace {
+
+constexpr int LT = 1024;  // threads of the one-workgroup-per-matrix kernels
+
+__device__ double block_sum(double v, double *red) {
+  v = warp_sum_d(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int i = 0; i < nw; ++i) s += red[i];  // fixed order: deterministic
+  return s;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Householder tridiagonalisation + all eigenvalues by bisection.
+// A: [batch][n][lda] fp64 symmetric (overwritten).  Output per batch: d[n], e[n] (e[n-1]=0),
+// reflectors refl[n][n] (row k holds v_k for rows k+1.., v_k[0] = 1), beta[n],
+// evals[n] descending (clamped at >= 0 when clamp != 0).
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long a_bs, int lda, const int *n_of,
+                                                            int n_fixed, double *d_out, double *e_out,
+                                                            double *refl, double *beta, long long t_bs,
+                                                            double *evals, long long ev_bs, int clamp,
+                                                            int use_lds) {
+  extern __shared__ double smem[];
+  __shared__ double red[LT / 64];
+  const int b = blockIdx.x;
+  const int n = n_of ? n_of[b] : n_fixed;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  double *Ag = A + b * a_bs;
+  double *d = d_out + b * t_bs, *e = e_out + b * t_bs, *R = refl + b * t_bs * (long long)n_fixed,
+         *be = beta + b * t_bs;
+  // working copy: LDS if it fits, else in place in global memory
+  double *W;
+  int ldw;
+  double *vbuf, *pbuf;
+  if (use_lds) {
+    W = smem;
+    ldw = n;
+    vbuf = smem + (long long)n * n;
+    pbuf = vbuf + n;
+    for (int i = tid; i < n * n; i += nt) W[i] = Ag[(long long)(i / n) * lda + (i % n)];
+  } else {
+    W = Ag;
+    ldw = lda;
+    vbuf = smem;
+    pbuf = smem + n;
+  }
+  __syncthreads();
+
+  for (int k = 0; k + 2 < n; ++k) {
+    const int m = n - k - 1;  // trailing size
+    double *row = W + (long long)k * ldw + (k + 1);  // x = A[k][k+1..] (= column k by symmetry)
+    double part = 0.0;
+    for (int i = 1 + tid; i < m; i += nt) part += row[i] * row[i];
+    double sigma = block_sum(part, red);
+    double alpha = row[0];
+    __syncthreads();  // row k is overwritten by the reflector below (in place when not staged in LDS)
+    double bet, v0, mu;
+    if (sigma == 0.0) {
+      bet = 0.0;
+      v0 = 1.0;
+      mu = alpha;
+    } else {
+      mu = sqrt(alpha * alpha + sigma);
+      v0 = (alpha <= 0.0) ? (alpha - mu) : (-sigma / (alpha + mu));
+      bet = 2.0 * v0 * v0 / (sigma + v0 * v0);
+    }
+    for (int i = tid; i < m; i += nt) {
+      double vi = (i == 0) ? 1.0 : row[i] / v0;
+      vbuf[i] = vi;
+      R[(long long)k * n_fixed + k + 1 + i] = vi;
+    }
+    if (tid == 0) {
+      d[k] = W[(long long)k * ldw + k];
+      e[k] = (sigma == 0.0) ? alpha : mu;
+      be[k] = bet;
+    }
+    __syncthreads();
+    if (bet == 0.0) continue;
+    // p = beta * A22 v  (A22 symmetric: read column-wise for coalescing)
+    double *A22 = W + (long long)(k + 1) * ldw + (k + 1);
+    for (int i = tid; i < m; i += nt) {
+      double s = 0.0;
+      for (int j = 0; j < m; ++j) s += A22[(long long)j * ldw + i] * vbuf[j];
+      pbuf[i] = bet * s;
+    }
+    __syncthreads();
+    part = 0.0;
+    for (int i = tid; i < m; i += nt) part += pbuf[i] * vbuf[i];
+    double pv = block_sum(part, red);
+    const double c = 0.5 * bet * pv;
+    for (int i = tid; i < m; i += nt) pbuf[i] -= c * vbuf[i];  // w
+    __syncthreads();
+    for (long long idx = tid; idx < (long long)m * m; idx += nt) {
+      int i = (int)(idx / m), j = (int)(idx % m);
+      A22[(long long)i * ldw + j] -= vbuf[i] * pbuf[j] + pbuf[i] * vbuf[j];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    if (n >= 2) {
+      d[n - 2] = W[(long long)(n - 2) * ldw + (n - 2)];
+      d[n - 1] = W[(long long)(n - 1) * ldw + (n - 1)];
+      e[n - 2] = W[(long long)(n - 1) * ldw + (n - 2)];
+      be[n - 2] = 0.0;
+    } else {
+      d[0] = W[0];
+    }
+    e[n - 1] = 0.0;
+    be[n - 1] = 0.0;
+  }
+  __syncthreads();
+
+  // ---- bisection (Sturm counts) for every eigenvalue; d, e^2 staged in LDS ------------------
+  double *sd = smem, *se2 = smem + n;  // reuse LDS (working copy no longer needed)
+  for (int i = tid; i < n; i += nt) {
+    sd[i] = d[i];
+    se2[i] = (i + 1 < n) ? e[i] * e[i] : 0.0;
+  }
+  __syncthreads();
+  double lo0 = 1e300, hi0 = -1e300, tn = 0.0;
+  for (int i = 0; i < n; ++i) {
+    double r = (i > 0 ? sqrt(se2[i - 1]) : 0.0) + (i + 1 < n ? sqrt(se2[i]) : 0.0);
+    lo0 = fmin(lo0, sd[i] - r);
+    hi0 = fmax(hi0, sd[i] + r);
+  }
+  tn = fmax(fabs(lo0), fabs(hi0));
+  const double pivmin = fmax(1e-300, 1e-300 * tn * tn);
+  lo0 -= 2.2e-16 * tn * 4 + pivmin;
+  hi0 += 2.2e-16 * tn * 4 + pivmin;
+  double *ev = evals + b * ev_bs;
+  for (int j = tid; j < n; j += nt) {
+    const int s = n - 1 - j;  // j-th largest == s-th smallest (0-based)
+    double lo = lo0, hi = hi0;
+    for (int it = 0; it < 200; ++it) {
+      double mid = 0.5 * (lo + hi);
+      if (mid <= lo || mid >= hi) break;
+      if (hi - lo <= 2.2e-16 * fmax(fabs(lo), fabs(hi)) * 2 + pivmin) break;
+      int cnt = 0;
+      double q = sd[0] - mid;
+      if (fabs(q) < pivmin) q = -pivmin;
+      cnt += (q < 0.0);
+      for (int i = 1; i < n; ++i) {
+        q = (sd[i] - mid) - se2[i - 1] / q;
+        if (fabs(q) < pivmin) q = -pivmin;
+        cnt += (q < 0.0);
+      }
+      if (cnt <= s) lo = mid;
+      else hi = mid;
+    }
+    double v = 0.5 * (lo + hi);
+    if (clamp && v < 0.0) v = 0.0;
+    ev[j] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Inverse iteration for the k largest eigenvalues of the tridiagonal (d, e); one thread per
+// eigenvector, rows of Z [k][n] (fp64).  Work arrays interleaved [i][j] for coalescing.
+// Then clusters (relative gap <= 1e-7 ||T||) are re-orthogonalised by two passes of Gram-Schmidt.
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(LT) invit_kernel(const double *d_in, const double *e_in, long long t_bs,
+                                                   const double *evals_all, long long ev_bs, const int *k_of,
+                                                   const int *n_of, int n_fixed, double *Z, long long z_bs,
+                                                   double *work, long long w_bs, int kmax) {
+  extern __shared__ double smem[];
+  __shared__ double red[LT / 64];
+  __shared__ int cl_start[2];
+  const int b = blockIdx.x;
+  const int n = n_of ? n_of[b] : n_fixed;
+  const int k = min(k_of[b], n);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const double *d = d_in + b * t_bs, *e = e_in + b * t_bs, *ev = evals_all + b * ev_bs;
+  double *sd = smem, *se = smem + n;
+  for (int i = tid; i < n; i += nt) {
+    sd[i] = d[i];
+    se[i] = (i + 1 < n) ? e[i] : 0.0;
+  }
+  __syncthreads();
+  double tn = 0.0;
+  for (int i = 0; i < n; ++i) tn = fmax(tn, fabs(sd[i]) + fabs(se[i]) + (i ? fabs(se[i - 1]) : 0.0));
+  const double tiny = fmax(tn * 1e-15, 1e-300);
+  double *Zb = Z + b * z_bs;
+  double *wb = work + b * w_bs;
+  // work layout: u0,u1,u2 (upper bands) and x, each [n][kmax]
+  double *U0 = wb, *U1 = wb + (long long)n * kmax, *U2 = wb + 2LL * n * kmax, *Xv = wb + 3LL * n * kmax;
+  unsigned char *piv = (unsigned char *)(wb + 4LL * n * kmax);
+  for (int j = tid; j < k; j += nt) {
+    const double lam = ev[j];
+    // factor P (T - lam I) = L U with partial pivoting; L multipliers applied on the fly, so
+    // they are stored in U2's slot of the row below only through piv/U arrays.
+    // Elimination: rows i (current) and i+1.
+    double a = sd[0] - lam, bb = se[0], cc = 0.0;  // row i: [a at col i, bb at i+1, cc at i+2]
+    // storage for multipliers: reuse Xv temporarily is not possible (x needed), keep mult in U2 of next row
+    for (int i = 0; i < n - 1; ++i) {
+      const double sub = se[i];            // T[i+1][i]
+      const double nd = sd[i + 1] - lam;   // T[i+1][i+1]
+      const double ne = (i + 2 < n) ? se[i + 1] : 0.0;  // T[i+1][i+2]
+      if (fabs(a) >= fabs(sub)) {
+        // no swap
+        double aa = (a == 0.0) ? tiny : a;
+        double l = sub / aa;
+        U0[(long long)i * kmax + j] = aa;
+        U1[(long long)i * kmax + j] = bb;
+        U2[(long long)i * kmax + j] = cc;
+        piv[(long long)i * kmax + j] = 0;
+        Xv[(long long)i * kmax + j] = l;  // multiplier (x is filled later)
+        a = nd - l * bb;
+        bb = ne - l * cc;
+        cc = 0.0;
+      } else {
+        // swap rows i and i+1
+        double l = a / sub;
+        U0[(long long)i * kmax + j] = sub;
+        U1[(long long)i * kmax + j] = nd;
+        U2[(long long)i * kmax + j] = ne;
+        piv[(long long)i * kmax + j] = 1;
+        Xv[(long long)i * kmax + j] = l;
+        double na = bb - l * nd;
+        double nb = cc - l * ne;
+        a = na;
+        bb = nb;
+        cc = 0.0;
+      }
+    }
+    U0[(long long)(n - 1) * kmax + j] = (a == 0.0) ? tiny : a;
+    U1[(long long)(n - 1) * kmax + j] = 0.0;
+    U2[(long long)(n - 1) * kmax + j] = 0.0;
+    // multipliers live in Xv; keep them in Z row temporarily (Z row j is the output vector)
+    double *z = Zb + (long long)j * n;
+    // start vector: deterministic pseudo-random, entries in (0.5, 1.5)
+    for (int i = 0; i < n; ++i) {
+      uint64_t h = (uint64_t)(i + 1) * 0x9E3779B97F4A7C15ull ^ (uint64_t)(j + 7) * 0xBF58476D1CE4E5B9ull;
+      h ^= h >> 31;
+      h *= 0x94D049BB133111EBull;
+      h ^= h >> 29;
+      z[i] = 0.5 + (double)(h >> 11) * (1.0 / 9007199254740992.0);
+    }
+    for (int iter = 0; iter < 3; ++iter) {
+      // apply L^{-1} P
+      for (int i = 0; i < n - 1; ++i) {
+        double l = Xv[(long long)i * kmax + j];
+        if (piv[(long long)i * kmax + j]) {
+          double t = z[i];
+          z[i] = z[i + 1];
+          z[i + 1] = t - l * z[i];
+        } else {
+          z[i + 1] -= l * z[i];
+        }
+      }
+      // back substitution with U (bands u0, u1, u2)
+      double scale = 0.0;
+      for (int i = n - 1; i >= 0; --i) {
+        double s = z[i];
+        if (i + 1 < n) s -= U1[(long long)i * kmax + j] * z[i + 1];
+        if (i + 2 < n) s -= U2[(long long)i * kmax + j] * z[i + 2];
+        z[i] = s / U0[(long long)i * kmax + j];
+        scale = fmax(scale, fabs(z[i]));
+      }
+      // normalise to unit 2-norm (rescale by max first to avoid overflow)
+      double inv = (scale > 0.0) ? 1.0 / scale : 1.0;
+      double nrm = 0.0;
+      for (int i = 0; i < n; ++i) {
+        z[i] *= inv;
+        nrm += z[i] * z[i];
+      }
+      nrm = 1.0 / sqrt(nrm);
+      for (int i = 0; i < n; ++i) z[i] *= nrm;
+    }
+  }
+  __syncthreads();
+  __threadfence_block();
+  // cluster re-orthogonalisation (sequential over vectors, parallel over entries)
+  const double ctol = 1e-7 * fmax(tn, 1e-300);
+  for (int j = 1; j < k; ++j) {
+    if (tid == 0) {
+      int s = j;
+      while (s > 0 && fabs(ev[s - 1] - ev[s]) <= ctol) --s;
+      cl_start[0] = s;
+    }
+    __syncthreads();
+    const int s = cl_start[0];
+    if (s < j) {
+      double *zj = Zb + (long long)j * n;
+      for (int pass = 0; pass < 2; ++pass) {
+        for (int i = s; i < j; ++i) {
+          const double *zi = Zb + (long long)i * n;
+          double part = 0.0;
+          for (int q = tid; q < n; q += nt) part += zi[q] * zj[q];
+          double c = block_sum(part, red);
+          for (int q = tid; q < n; q += nt) zj[q] -= c * zi[q];
+          __syncthreads();
+        }
+        double part = 0.0;
+        for (int q = tid; q < n; q += nt) part += zj[q] * zj[q];
+        double nr = block_sum(part, red);
+        nr = (nr > 0.0) ? 1.0 / sqrt(nr) : 0.0;
+        for (int q = tid; q < n; q += nt) zj[q] *= nr;
+        __syncthreads();
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Back-transformation: z <- H_0 H_1 ... H_{n-3} z for every eigenvector row (block of VB rows
+// held in LDS per workgroup), then sign normalisation (largest-magnitude entry positive) and
+// output as fp64 and/or fp32 rows.
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) backtransform_kernel(const double *Zin, long long z_bs, const double *refl,
+                                                            const double *beta, long long t_bs, const int *n_of,
+                                                            int n_fixed, const int *k_of, int vb, double *out64,
+                                                            float *out32, long long out_bs, int out_ld) {
+  extern __shared__ double smem[];
+  const int b = blockIdx.y;
+  const int n = n_of ? n_of[b] : n_fixed;
+  const int k = min(k_of[b], n);
+  const int v0 = blockIdx.x * vb;
+  if (v0 >= k) return;
+  const int nv = min(vb, k - v0);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  double *zs = smem;                  // [nv][n]
+  double *vs = smem + (long long)vb * n;  // reflector
+  double *cs = vs + n;                // per-vector coefficients
+  const double *Zb = Zin + b * z_bs;
+  for (int i = tid; i < nv * n; i += nt) zs[i] = Zb[(long long)(v0 + i / n) * n + (i % n)];
+  const double *Rb = refl + b * t_bs * (long long)n_fixed;
+  const double *bb = beta + b * t_bs;
+  __syncthreads();
+  for (int kk = n - 3; kk >= 0; --kk) {
+    const double bt = bb[kk];
+    if (bt == 0.0) continue;  // uniform across the block
+    const int m = n - kk - 1;
+    for (int i = tid; i < m; i += nt) vs[i] = Rb[(long long)kk * n_fixed + kk + 1 + i];
+    __syncthreads();
+    // one wave per vector computes v^T z
+    const int lane = tid & 63, w = tid >> 6;
+    for (int q = w; q < nv; q += nt / 64) {
+      double s = 0.0;
+      for (int i = lane; i < m; i += 64) s += vs[i] * zs[(long long)q * n + kk + 1 + i];
+      s = warp_sum_d(s);
+      if (lane == 0) cs[q] = bt * s;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nv * m; idx += nt) {
+      int q = idx / m, i = idx % m;
+      zs[(long long)q * n + kk + 1 + i] -= cs[q] * vs[i];
+    }
+    __syncthreads();
+  }
+  // sign normalisation and output
+  const int lane = tid & 63, w = tid >> 6;
+  for (int q = w; q < nv; q += nt / 64) {
+    double best = -1.0, val = 0.0;
+    int bi = 0;
+    for (int i = lane; i < n; i += 64) {
+      double a = fabs(zs[(long long)q * n + i]);
+      if (a > best) { best = a; bi = i; }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      double ob = __shfl_xor(best, o, 64);
+      int oi = __shfl_xor(bi, o, 64);
+      if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    }
+    val = zs[(long long)q * n + bi];
+    const double sg = (val < 0.0) ? -1.0 : 1.0;
+    for (int i = lane; i < n; i += 64) {
+      double x = sg * zs[(long long)q * n + i];
+      long long o = b * out_bs + (long long)(v0 + q) * out_ld + i;
+      if (out64) out64[o] = x;
+      if (out32) out32[o] = (float)x;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Cholesky G = R^T R (R upper, fp64) and RinvT = (R^{-1})^T written as fp32 [n][ld_out]
+// (row c' holds column c' of R^{-1}); amax of RinvT for the fp16 split.  Non-positive pivots
+// are replaced by a tiny multiple of the largest diagonal (documented regularisation).
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(LT) chol_inv_kernel(const double *G, long long g_bs, int ldg, int n, double *Rw,
+                                                      long long r_bs, float *RinvT, long long o_bs, int ld_out,
+                                                      float *amax) {
+  __shared__ double red[LT / 64];
+  __shared__ double piv_s;
+  const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const double *Gb = G + b * g_bs;
+  double *R = Rw + b * r_bs;  // [n][n] upper, row-major; also holds R^{-1} later in lower? no: separate
+  double *Ri = R + (long long)n * n;  // R^{-1} upper [n][n]
+  double dmax = 0.0;
+  for (int i = 0; i < n; ++i) dmax = fmax(dmax, Gb[(long long)i * ldg + i]);
+  const double floor_piv = fmax(dmax * 1e-28, 1e-300);
+  // left-looking: row j of R from G[j][j..] minus contributions of rows < j
+  for (int j = 0; j < n; ++j) {
+    if (tid == 0) {
+      double s = Gb[(long long)j * ldg + j];
+      for (int kk = 0; kk < j; ++kk) s -= R[(long long)kk * n + j] * R[(long long)kk * n + j];
+      piv_s = sqrt(fmax(s, floor_piv));
+      R[(long long)j * n + j] = piv_s;
+    }
+    __syncthreads();
+    const double p = piv_s;
+    for (int i = j + 1 + tid; i < n; i += nt) {
+      double s = Gb[(long long)j * ldg + i];
+      for (int kk = 0; kk < j; ++kk) s -= R[(long long)kk * n + j] * R[(long long)kk * n + i];
+      R[(long long)j * n + i] = s / p;
+    }
+    __syncthreads();
+  }
+  // R^{-1} (upper): rows from the bottom up, all columns c >= i in parallel
+  for (int i = n - 1; i >= 0; --i) {
+    const double rii = R[(long long)i * n + i];
+    for (int c = i + tid; c < n; c += nt) {
+      double s = (c == i) ? 1.0 : 0.0;
+      for (int kk = i + 1; kk <= c; ++kk) s -= R[(long long)i * n + kk] * Ri[(long long)kk * n + c];
+      Ri[(long long)i * n + c] = s / rii;
+    }
+    __syncthreads();
+  }
+  float lmax = 0.f;
+  float *O = RinvT + b * o_bs;
+  for (long long idx = tid; idx < (long long)n * n; idx += nt) {
+    int cp = (int)(idx / n), c = (int)(idx % n);  // RinvT[cp][c] = Rinv[c][cp]
+    float v = (c <= cp) ? (float)Ri[(long long)c * n + cp] : 0.f;
+    O[(long long)cp * ld_out + c] = v;
+    lmax = fmaxf(lmax, fabsf(v));
+  }
+  lmax = warp_max(lmax);
+  __shared__ float fred[LT / 64];
+  if ((tid & 63) == 0) fred[tid >> 6] = lmax;
+  __syncthreads();
+  if (tid == 0) {
+    float m = 0.f;
+    for (int i = 0; i < nt / 64; ++i) m = fmaxf(m, fred[i]);
+    amax[b] = m;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// H[b][c][c'] = sum_m P[b][c][m] P[b][c'][m] in fp64 from fp32 rows (64 x 64 tiles, symmetric).
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) gram64_kernel(const float *P, long long p_bs, int ldp, int rows, int K,
+                                                     double *H, long long h_bs, int ldh) {
+  __shared__ double As[16][65], Bs[16][65];
+  const int b = blockIdx.z;
+  const int ti = blockIdx.y, tj = blockIdx.x;
+  if (tj > ti) return;
+  const int r0 = ti * 64, c0 = tj * 64;
+  const float *Pb = P + b * p_bs;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  double acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
+      int kk = idx & 15, r = idx >> 4;
+      int k = k0 + kk;
+      As[kk][r] = (r0 + r < rows && k < K) ? (double)Pb[(long long)(r0 + r) * ldp + k] : 0.0;
+      Bs[kk][r] = (c0 + r < rows && k < K) ? (double)Pb[(long long)(c0 + r) * ldp + k] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      double a[4], bb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = As[kk][ty * 4 + i]; bb[i] = Bs[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * bb[j];
+    }
+    __syncthreads();
+  }
+  double *Hb = H + b * h_bs;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int r = r0 + ty * 4 + i, c = c0 + tx * 4 + j;
+      if (r < rows && c < rows) {
+        Hb[(long long)r * ldh + c] = acc[i][j];
+        Hb[(long long)c * ldh + r] = acc[i][j];
+      }
+    }
+}
+
+}  // namespace
+
+size_t tridiag_lds_bytes(int n) { return ((size_t)n * n + 2 * (size_t)n) * sizeof(double); }
+
+void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d, double *e, double *refl,
+                 double *beta, long long t_bs, double *evals, long long ev_bs, bool clamp, hipStream_t st) {
+  JOLT_REQUIRE(n >= 1 && n <= 8192, JOLT_EINVAL, "eigensolver: unsupported size");
+  size_t lds_full = tridiag_lds_bytes(n);
+  const size_t lds_cap = 150 * 1024;
+  bool use_lds = lds_full <= lds_cap;
+  size_t shm = use_lds ? lds_full : std::max<size_t>(2 * (size_t)n * sizeof(double), 4096);
+  JOLT_REQUIRE(shm <= 160 * 1024, JOLT_EINVAL, "eigensolver: n too large for LDS staging");
+  hipLaunchKernelGGL(tridiag_values_kernel, dim3(batch), dim3(LT), shm, st, A, a_bs, lda, (const int *)nullptr, n,
+                     d, e, refl, beta, t_bs, evals, ev_bs, clamp ? 1 : 0, use_lds ? 1 : 0);
+  HIP_LAUNCH_CHECK();
+}
+
+size_t invit_work_doubles(int n, int kmax) { return 4ull * n * kmax + ((size_t)n * kmax + 7) / 8 + 8; }
+
+void sym_eigvecs(const double *d, const double *e, const double *refl, const double *beta, long long t_bs,
+                 const double *evals, long long ev_bs, int n, const int *k_dev, int kmax, int batch, double *Zw,
+                 long long z_bs, double *work, long long w_bs, double *out64, float *out32, long long out_bs,
+                 int out_ld, hipStream_t st) {
+  if (kmax <= 0) return;
+  hipLaunchKernelGGL(invit_kernel, dim3(batch), dim3(LT), 2 * (size_t)n * sizeof(double), st, d, e, t_bs, evals,
+                     ev_bs, k_dev, (const int *)nullptr, n, Zw, z_bs, work, w_bs, kmax);
+  HIP_LAUNCH_CHECK();
+  int vb = std::max(1, std::min(32, (int)((60 * 1024) / (n * 8)) - 1));
+  size_t shm = ((size_t)vb * n + n + 64) * sizeof(double);
+  dim3 grid((kmax + vb - 1) / vb, batch);
+  hipLaunchKernelGGL(backtransform_kernel, grid, dim3(256), shm, st, Zw, z_bs, refl, beta, t_bs,
+                     (const int *)nullptr, n, k_dev, vb, out64, out32, out_bs, out_ld);
+  HIP_LAUNCH_CHECK();
+}
+
+void chol_inv(const double *G, long long g_bs, int ldg, int n, int batch, double *Rw, long long r_bs, float *RinvT,
+              long long o_bs, int ld_out, float *amax, hipStream_t st) {
+  hipLaunchKernelGGL(chol_inv_kernel, dim3(batch), dim3(LT), 0, st, G, g_bs, ldg, n, Rw, r_bs, RinvT, o_bs, ld_out,
+                     amax);
+  HIP_LAUNCH_CHECK();
+}
+
+void gram64(const float *P, long long p_bs, int ldp, int rows, int K, double *H, long long h_bs, int ldh, int batch,
+            hipStream_t st) {
+  int t = (rows + 63) / 64;
+  hipLaunchKernelGGL(gram64_kernel, dim3(t, t, batch), dim3(256), 0, st, P, p_bs, ldp, rows, K, H, h_bs, ldh);
+  HIP_LAUNCH_CHECK();
+}
+
+}  // namespace jolt

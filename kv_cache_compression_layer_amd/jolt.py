@@ -1,0 +1,274 @@
+"""ctypes binding of libjolt (argument marshalling only).
+
+Every step of compression and reconstruction runs inside libjolt.so on the GPU; this module
+only converts Python/torch arguments into the C structs of include/jolt.h, allocates device
+buffers with torch and passes the current HIP stream.  If the library is missing it raises;
+there is no other code path.
+"""
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libjolt.so")
+
+F16, BF16, F32 = 0, 1, 2
+EXACT, FLASH = 0, 1
+STATUS = {0: "JOLT_OK", -1: "JOLT_EINVAL", -2: "JOLT_EINFEASIBLE", -3: "JOLT_EWORKSPACE", -4: "JOLT_EHIP",
+          -5: "JOLT_ENONFINITE", -6: "JOLT_EBUFFER"}
+TORCH_DTYPE = {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}
+DTYPE_OF = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+EXPORTS = ["jolt_workspace_bytes", "jolt_output_bytes", "jolt_allocate", "jolt_compress", "jolt_reconstruct",
+           "jolt_spectra", "jolt_token_spectrum_len", "jolt_encode_residual",
+           "jolt_encode_residual_workspace_bytes", "jolt_rotation", "jolt_eps2", "jolt_last_error"]
+
+
+class JoltError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("n_seq", ctypes.c_int32), ("n_layers", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_tokens", ctypes.c_int32), ("d_head", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("group_start", ctypes.POINTER(ctypes.c_int32))]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("oversample", ctypes.c_int32), ("power_iters", ctypes.c_int32),
+                ("qcap", ctypes.c_int32),
+                ("rT_grid", ctypes.POINTER(ctypes.c_int32)), ("n_rT", ctypes.c_int32),
+                ("rd_grid", ctypes.POINTER(ctypes.c_int32)), ("n_rd", ctypes.c_int32),
+                ("bits", ctypes.POINTER(ctypes.c_int32)), ("n_bits", ctypes.c_int32),
+                ("eps2", ctypes.POINTER(ctypes.c_double)), ("target_ratio", ctypes.c_double),
+                ("rot_seed", ctypes.c_uint64), ("sketch_seed", ctypes.c_uint64)]
+
+
+class Pick(ctypes.Structure):
+    _fields_ = [("rT", ctypes.c_int32), ("rd", ctypes.c_int32), ("bits", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("bytes", ctypes.c_int64), ("err_pred", ctypes.c_double), ("offset", ctypes.c_int64),
+                ("section_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load():
+    """Load libjolt.so (built by __graft_entry__.build()); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libjolt.so not built ({LIB_PATH}); run __graft_entry__.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i32, i64, dbl, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_size_t
+    pd, pp = ctypes.POINTER(CacheDesc), ctypes.POINTER(Params)
+    sig = {
+        "jolt_workspace_bytes": (sz, [pd, pp]),
+        "jolt_output_bytes": (sz, [pd, pp]),
+        "jolt_token_spectrum_len": (i64, [pd, pp]),
+        "jolt_allocate": (ctypes.c_int, [i32, ctypes.POINTER(i32), i32, P, ctypes.POINTER(i64), P,
+                                         ctypes.POINTER(i64), P, pp, dbl, ctypes.POINTER(Pick),
+                                         ctypes.POINTER(dbl), P, sz, P]),
+        "jolt_compress": (ctypes.c_int, [P, P, pd, pp, P, sz, P, sz, ctypes.POINTER(Pick), ctypes.POINTER(dbl), P]),
+        "jolt_reconstruct": (ctypes.c_int, [P, pd, pp, ctypes.POINTER(Pick), P, P, P, sz, P]),
+        "jolt_spectra": (ctypes.c_int, [P, P, pd, pp, P, P, P, P, i32, P, sz, P]),
+        "jolt_encode_residual": (ctypes.c_int, [P, i32, i32, i32, i32, i32, P, P, P, i32, i32, i32,
+                                                ctypes.c_uint64, P, P, P, sz, P]),
+        "jolt_encode_residual_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
+        "jolt_rotation": (ctypes.c_int, [i32, ctypes.c_uint64, ctypes.POINTER(dbl)]),
+        "jolt_eps2": (ctypes.c_int, [i32, ctypes.POINTER(dbl)]),
+        "jolt_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != 0:
+        msg = load().jolt_last_error().decode()
+        raise JoltError(status, msg)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _i32arr(vals):
+    a = (ctypes.c_int32 * len(vals))(*[int(v) for v in vals])
+    return a
+
+
+class Config:
+    """Cache descriptor + parameters, holding the ctypes arrays alive."""
+
+    def __init__(self, n_seq, n_layers, n_heads, n_tokens, d_head, dtype, group_start, mode, rT_grid, rd_grid,
+                 bits, target_ratio, oversample=10, power_iters=1, qcap=0, eps2=None, rot_seed=0, sketch_seed=0):
+        self._gs = _i32arr(group_start)
+        self.desc = CacheDesc(n_seq, n_layers, n_heads, n_tokens, d_head, dtype, len(group_start) - 1, self._gs)
+        self._rT, self._rd, self._bits = _i32arr(rT_grid), _i32arr(rd_grid), _i32arr(bits)
+        self._eps = None
+        if eps2 is not None:
+            e = np.ones(9)
+            for b, v in dict(eps2).items():
+                e[int(b)] = float(v)
+            self._eps = (ctypes.c_double * 9)(*e.tolist())
+        self.params = Params(mode, oversample, power_iters, qcap, self._rT, len(rT_grid), self._rd, len(rd_grid),
+                             self._bits, len(bits), self._eps, float(target_ratio), rot_seed, sketch_seed)
+        self.n_cells = n_seq * (len(group_start) - 1) * 2
+
+    def workspace_bytes(self):
+        n = load().jolt_workspace_bytes(ctypes.byref(self.desc), ctypes.byref(self.params))
+        if n == 0:
+            _check(-1)
+        return n
+
+    def output_bytes(self):
+        n = load().jolt_output_bytes(ctypes.byref(self.desc), ctypes.byref(self.params))
+        if n == 0:
+            _check(-1)
+        return n
+
+    def token_spectrum_len(self):
+        n = load().jolt_token_spectrum_len(ctypes.byref(self.desc), ctypes.byref(self.params))
+        if n <= 0:
+            _check(int(n))
+        return int(n)
+
+
+def _device_of(t):
+    return t.device if t is not None else torch.device("cuda")
+
+
+def workspace(cfg, device="cuda"):
+    return torch.empty(cfg.workspace_bytes(), dtype=torch.uint8, device=device)
+
+
+def compress(K, V, cfg, out=None, ws=None):
+    """Compress K and V (contiguous [n_seq][L][H][T][D] device tensors).
+
+    Returns (blob uint8 tensor, list of pick dicts, lambda)."""
+    lib = load()
+    K, V = K.contiguous(), V.contiguous()
+    if ws is None:
+        ws = workspace(cfg, K.device)
+    if out is None:
+        out = torch.empty(cfg.output_bytes(), dtype=torch.uint8, device=K.device)
+    picks = (Pick * cfg.n_cells)()
+    lam = ctypes.c_double(0.0)
+    _check(lib.jolt_compress(_ptr(K), _ptr(V), ctypes.byref(cfg.desc), ctypes.byref(cfg.params), _ptr(out),
+                             out.numel(), _ptr(ws), ws.numel(), picks, ctypes.byref(lam), _stream()))
+    return out, [_pick_dict(p) for p in picks], lam.value
+
+
+def _pick_dict(p):
+    return {"rT": p.rT, "rd": p.rd, "bits": p.bits, "bytes": p.bytes, "err_pred": p.err_pred, "offset": p.offset,
+            "section_bytes": p.section_bytes}
+
+
+def _picks_array(picks):
+    arr = (Pick * len(picks))()
+    for a, p in zip(arr, picks):
+        a.rT, a.rd, a.bits = int(p["rT"]), int(p["rd"]), int(p["bits"])
+        a.bytes = int(p.get("bytes", 0))
+        a.err_pred = float(p.get("err_pred", 0.0))
+        a.offset = int(p["offset"])
+        a.section_bytes = int(p.get("section_bytes", 0))
+    return arr
+
+
+def reconstruct(blob, cfg, picks, K_out, V_out, ws=None):
+    lib = load()
+    if ws is None:
+        ws = workspace(cfg, blob.device)
+    arr = _picks_array(picks)
+    _check(lib.jolt_reconstruct(_ptr(blob), ctypes.byref(cfg.desc), ctypes.byref(cfg.params), arr, _ptr(K_out),
+                                _ptr(V_out), _ptr(ws), ws.numel(), _stream()))
+
+
+def spectra(K, V, cfg, n_vec=0, ws=None):
+    """Returns (specT [n_cells][nT], specD [n_cells][D], norm2 [n_cells], UT [n_cells][n_vec][T] or None)."""
+    lib = load()
+    dev = K.device
+    nT = cfg.token_spectrum_len()
+    nc, D, T = cfg.n_cells, cfg.desc.d_head, cfg.desc.n_tokens
+    specT = torch.empty(nc, nT, dtype=torch.float64, device=dev)
+    specD = torch.empty(nc, D, dtype=torch.float64, device=dev)
+    norm2 = torch.empty(nc, dtype=torch.float64, device=dev)
+    UT = torch.empty(nc, n_vec, T, dtype=torch.float32, device=dev) if n_vec > 0 else None
+    if ws is None:
+        extra = 0
+        if n_vec > 0:
+            extra = 4 * nc * (n_vec + 8) * (T + 8) * 3 + 8 * nc * (n_vec + 8) * (max(nT, T) + 8) * 6
+        ws = torch.empty(cfg.workspace_bytes() + extra, dtype=torch.uint8, device=dev)
+    _check(lib.jolt_spectra(_ptr(K.contiguous()), _ptr(V.contiguous()), ctypes.byref(cfg.desc),
+                            ctypes.byref(cfg.params), _ptr(specT), _ptr(specD), _ptr(norm2), _ptr(UT), int(n_vec),
+                            _ptr(ws), ws.numel(), _stream()))
+    return specT, specD, norm2, UT
+
+
+def allocate(cell_shapes, elem_bytes, specT_list, specD_list, norm2, rT_grid, rd_grid, bits, budget, eps2=None,
+             device="cuda"):
+    """Lagrangian allocation on given spectra (lists of 1-D float64 arrays, one per cell)."""
+    lib = load()
+    cfg = Config(1, 1, 1, 1, 64, F16, [0, 1], EXACT, rT_grid, rd_grid, bits, 2.0, eps2=eps2)
+    n = len(cell_shapes)
+    shp = (ctypes.c_int32 * (4 * n))(*[int(v) for s in cell_shapes for v in s])
+    offT = np.concatenate([[0], np.cumsum([len(s) for s in specT_list])]).astype(np.int64)
+    offD = np.concatenate([[0], np.cumsum([len(s) for s in specD_list])]).astype(np.int64)
+    dT = torch.from_numpy(np.concatenate(specT_list).astype(np.float64)).to(device)
+    dD = torch.from_numpy(np.concatenate(specD_list).astype(np.float64)).to(device)
+    dn = torch.from_numpy(np.asarray(norm2, dtype=np.float64)).to(device)
+    per = (len(set(bits) | {0})) * len(rT_grid) * len(rd_grid)
+    ws = torch.empty(n * per * 16 + n * (len(rT_grid) + len(rd_grid)) * 8 + n * 64 + (1 << 20), dtype=torch.uint8,
+                     device=device)
+    picks = (Pick * n)()
+    lam = ctypes.c_double(0.0)
+    status = lib.jolt_allocate(n, shp, int(elem_bytes), _ptr(dT), offT.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                               _ptr(dD), offD.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr(dn),
+                               ctypes.byref(cfg.params), float(budget), picks, ctypes.byref(lam), _ptr(ws),
+                               ws.numel(), _stream())
+    return status, [_pick_dict(p) for p in picks], lam.value
+
+
+def encode_residual(X, UT, core, Ud, rT, rd, bits, rot_seed=0):
+    """Residual stage of one cell with given factors (storage dtype = X dtype).
+
+    X [G][H][T][D], UT [T][rT], core [G][H][rT][rd], Ud [D][rd].  Returns (scales, codes)."""
+    lib = load()
+    G, H, T, D = X.shape
+    dtype = DTYPE_OF[X.dtype]
+    scales = torch.empty(G * H * T, dtype=torch.float32, device=X.device)
+    codes = torch.empty(G * H * T, D * bits // 8, dtype=torch.uint8, device=X.device)
+    nws = lib.jolt_encode_residual_workspace_bytes(G, H, T, D, rT, rd)
+    if nws == 0:
+        _check(-1)
+    ws = torch.empty(nws, dtype=torch.uint8, device=X.device)
+    _check(lib.jolt_encode_residual(_ptr(X.contiguous()), G, H, T, D, dtype, _ptr(UT.contiguous()),
+                                    _ptr(core.contiguous()), _ptr(Ud.contiguous()), rT, rd, bits, rot_seed,
+                                    _ptr(scales), _ptr(codes), _ptr(ws), nws, _stream()))
+    return scales, codes
+
+
+def rotation(d_head, seed=0):
+    out = np.zeros((d_head, d_head))
+    _check(load().jolt_rotation(d_head, seed, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+    return out
+
+
+def eps2(d_head):
+    out = np.zeros(9)
+    _check(load().jolt_eps2(d_head, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
+    return out

@@ -293,7 +293,7 @@ def cell_table(sh, c, specT, specD, norm2, rT_grid, rd_grid, bits, eps2):
     for b in bits:
         for rT in rT_grid:
             for rd in rd_grid:
-                tau = (tT[rT] + tD[rd]) / norm2
+                tau = (tT[rT] + tD[rd]) / norm2 if norm2 > 0 else 0.0
                 e = eps2[b] * tau
                 rows.append((b, rT, rd, e, cell_bytes(sh, c, rT, rd, b)))
     b_, rT_, rd_, e_, s_ = map(np.array, zip(*rows))
