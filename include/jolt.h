@@ -179,6 +179,14 @@ size_t jolt_encode_residual_workspace_bytes(int32_t G, int32_t H, int32_t T, int
 int jolt_rotation(int32_t d_head, uint64_t seed, double *h_Q /* [d_head][d_head] */);
 int jolt_eps2(int32_t d_head, double *h_eps2 /* [9], indexed by b */);
 
+/* Stage timing for measurement: when enabled, every stage of the calls that follow records a
+ * pair of HIP events on the caller's stream.  jolt_profile_read() waits for the recorded
+ * events, writes the stage names ('\n'-separated) to h_names, the summed milliseconds to
+ * h_ms and the number of occurrences to h_count, clears the records and returns the number
+ * of distinct stages (or a negative status). */
+int jolt_profile(int32_t enable);
+int32_t jolt_profile_read(char *h_names, int32_t names_bytes, double *h_ms, int32_t *h_count, int32_t max_stages);
+
 /* Thread-local message of the last failing call ("" if none). */
 const char *jolt_last_error(void);
 

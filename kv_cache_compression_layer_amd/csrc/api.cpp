@@ -29,6 +29,34 @@ static thread_local std::string g_err;
 void set_error(const std::string &msg) { g_err = msg; }
 const char *get_error() { return g_err.c_str(); }
 
+// ------------------------------------------------------------------------------------ profiler
+// Optional per-stage timing with HIP events recorded on the caller's stream (off by default).
+struct StageRec {
+  const char *name;
+  hipEvent_t a, b;
+};
+static std::vector<StageRec> g_recs;
+static bool g_prof = false;
+
+struct Stage {
+  hipStream_t st;
+  StageRec rec;
+  bool on;
+  Stage(const char *name, hipStream_t s) : st(s), on(g_prof) {
+    if (!on) return;
+    rec.name = name;
+    HIP_TRY(hipEventCreate(&rec.a));
+    HIP_TRY(hipEventCreate(&rec.b));
+    HIP_TRY(hipEventRecord(rec.a, st));
+  }
+  void end() {
+    if (!on) return;
+    on = false;
+    if (hipEventRecord(rec.b, st) == hipSuccess) g_recs.push_back(rec);
+  }
+  ~Stage() { end(); }
+};
+
 namespace {
 
 constexpr int BIG = 1 << 30;
@@ -350,6 +378,7 @@ void apply_f32(const float *A, long long lda, long long abs_, const float *a_ama
 
 // --------------------------------------------------------------------------- spectra stage
 void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
+  Stage prof("feature_gram", st);
   const int nkv = pl.n_cells / 2, D = pl.D;
   const long long Kdim = (long long)pl.GH * pl.T;
   int ns = nsplit_for(Kdim, 1, pl.n_cells, 8192);
@@ -384,6 +413,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
 
   // Y^T = A X_(T)^T with A = Omega^T (16-bit / fp32) or Z^T (fp32)
   auto sketch = [&](const void *A, int a_src, long long a_bs, const float *a_amax, float *out, float *c_amax) {
+    Stage prof("sketch_gemm", st);
     for_kv(K, V, [&](int t, const void *X) {
       GemmArgs g = ga();
       g.A = (const char *)A + (a_bs ? t * a_bs * (a_src == SRC_F32 ? 4 : 2) : 0);
@@ -400,6 +430,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   };
   // P^T = Q^T X_(T)  (ell x M), Q^T fp32 rows of length T
   auto project = [&](const float *Qt, const float *q_amax, float *out, float *c_amax) {
+    Stage prof("project_gemm", st);
     for_kv(K, V, [&](int t, const void *X) {
       GemmArgs g = ga();
       g.A = Qt + t * ell * Tld; g.M = (int)ell; g.N = (int)Mf; g.K = pl.T;
@@ -413,6 +444,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   };
   // rows of Y^T (ell x T) -> orthonormal rows by Cholesky QR (passes times)
   auto cholqr = [&](float *Y, float *Yam, float *tmp, float *tmp_am, int passes) -> float * {
+    Stage prof("cholqr_tall", st);
     for (int p = 0; p < passes; ++p) {
       gram_f32(pl, b, Y, Tld, ell * Tld, (int)ell, pl.T, Yam, b.G64, ell * ell, (int)ell, nb, st);
       chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, 2 * ell * ell, b.RinvT, ell * ld, (int)ld, amR, st);
@@ -436,6 +468,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     fill_f32(amP, nb, 0.f, st);
     project(Q, Qam, b.Pt, amP);
     // Z = orth(P): Cholesky QR on the rows of P^T (length M)
+    Stage prof_z("cholqr_z", st);
     gram_f32(pl, b, b.Pt, Mf, ell * Mf, (int)ell, (int)Mf, amP, b.G64, ell * ell, (int)ell, nb, st);
     chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, 2 * ell * ell, b.RinvT, ell * ld, (int)ld, amR, st);
     fill_f32(amZ, nb, 0.f, st);
@@ -461,14 +494,21 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   float *amP1 = b.amax + 5 * nb;
   fill_f32(amP1, nb, 0.f, st);
   project(Q, Qam, b.Pt, amP1);
-  gram64(b.Pt, ell * Mf, (int)Mf, (int)ell, (int)Mf, b.G64, ell * ell, (int)ell, nb, st);
-  sym_eigvals(b.G64, ell * ell, (int)ell, (int)ell, nb, b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, true, st);
+  {
+    Stage prof("gram64", st);
+    gram64(b.Pt, ell * Mf, (int)Mf, (int)ell, (int)Mf, b.G64, ell * ell, (int)ell, nb, st);
+  }
+  {
+    Stage prof("eigvals_B", st);
+    sym_eigvals(b.G64, ell * ell, (int)ell, (int)ell, nb, b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, true, st);
+  }
   flash_spec(b.evT, ell, pl.q, b.norm2, b.specT, pl.nT, nb, st);
   // the fit reads Q^T from b.bufA
   if (Q != b.bufA) std::swap(b.bufA, b.bufB);
 }
 
 void stage_exact(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
+  Stage prof("token_gram_eig", st);
   const int nb = pl.n_cells, nkv = nb / 2;
   const long long T = pl.T, Tld = pl.T_ld, Mf = pl.M;
   int ns = nsplit_for(Mf, tiles_of(T, T), nb, 1024);
@@ -621,6 +661,7 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
   const float *Qtf = (const float *)(b.params + rot_offs[1]);
 
   float *amYp = b.amax + 6 * nb, *amCr = b.amax + 7 * nb;
+  Stage prof_vec("fit_token_factor", st);
   float *UTt = b.bufB;  // [nb][kmax][Tld]
   float *Yp = b.Zt;     // [nb][kmax][Mf]
   fill_f32(amYp, nb, 0.f, st);
@@ -659,8 +700,10 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
       gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), false, g, nkv, 1, st);
     });
   }
+  prof_vec.end();
   // ---- projected feature Gram -> U_d
   {
+    Stage prof("fit_feature_factor", st);
     const long long Kd = kmax * GH;
     int ns = nsplit_for(Kd, 1, nb, 1024);
     GemmArgs g = ga();
@@ -680,6 +723,7 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
   }
   // ---- core: Cp[(r, j)][kk] = Y_p[r][j][:] . U_d[:, kk]
   {
+    Stage prof("fit_core", st);
     GemmArgs g = ga();
     g.A = Yp; g.a_ld = D; g.a_bs = kmax * Mf; g.a_amax = amYp; g.ab_amax_bs = 1;
     g.B = b.Udrows; g.b_ld = D; g.b_bs = kmd * D;
@@ -688,11 +732,13 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
   }
   // ---- factors into the blob (rounded) + rounded copies for the residual
+  Stage prof_put("put_factors", st);
   fill_f32(b.Udr, (long long)nb * kmd * D, 0.f, st);
   fill_f32(b.Cr, (long long)nb * GH * kmax * kmd, 0.f, st);
   put_ut(pl.dtype, d_fc, nb, UTt, kmax * Tld, (int)Tld, pl.T, (int)kmax, st);
   put_small(pl.dtype, d_fc, nb, b.Udrows, kmd * D, b.Cp, kmax * GH * kmd, (int)kmax, (int)kmd, D, GH, b.Udr, b.Cr, st);
   write_headers(d_fc, nb, st);
+  prof_put.end();
 
   // ---- residual: Bcat = [Q^T | -(D_j Q)^T] per (cell, j), then the fused encode
   bool any = false;
@@ -700,6 +746,7 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
   if (!any) return;
   {
     // Vt[n][kk] = sum_d Q[d][n] Udr[kk][d]
+    Stage prof("residual_operand", st);
     GemmArgs g = ga();
     g.A = Qtf; g.a_ld = D; g.a_bs = 0; g.a_amax_c = 1.f;
     g.B = b.Udr; g.b_ld = D; g.b_bs = kmd * D; g.b_amax_c = 1.f;
@@ -741,7 +788,10 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
   JOLT_REQUIRE(rup((long long)u.host.size(), 256) + (long long)u2.host.size() <= (long long)b.params_bytes,
                JOLT_EWORKSPACE, "parameter area too small");
   HIP_TRY(hipMemcpyAsync(dst, u2.host.data(), u2.host.size(), hipMemcpyHostToDevice, st));
-  encode_cells(pl.dtype, (const EncCell *)(dst + o_ec), (int)ec.size(), pl.T, D, GH, st);
+  {
+    Stage prof("residual_encode", st);
+    encode_cells(pl.dtype, (const EncCell *)(dst + o_ec), (int)ec.size(), pl.T, D, GH, st);
+  }
 }
 
 // ----------------------------------------------------------------------------- entry helpers
@@ -777,6 +827,48 @@ using namespace jolt;
 extern "C" {
 
 const char *jolt_last_error(void) { return get_error(); }
+
+int jolt_profile(int32_t enable) {
+  return guarded([&]() {
+    g_prof = enable != 0;
+    return 0;
+  });
+}
+
+int32_t jolt_profile_read(char *h_names, int32_t names_bytes, double *h_ms, int32_t *h_count, int32_t max_stages) {
+  return guarded([&]() {
+    std::vector<std::string> names;
+    std::vector<double> ms;
+    std::vector<int> cnt;
+    for (auto &r : g_recs) {
+      HIP_TRY(hipEventSynchronize(r.b));
+      float t = 0.f;
+      HIP_TRY(hipEventElapsedTime(&t, r.a, r.b));
+      size_t i = 0;
+      while (i < names.size() && names[i] != r.name) ++i;
+      if (i == names.size()) {
+        names.push_back(r.name);
+        ms.push_back(0.0);
+        cnt.push_back(0);
+      }
+      ms[i] += t;
+      cnt[i] += 1;
+      hipEventDestroy(r.a);
+      hipEventDestroy(r.b);
+    }
+    g_recs.clear();
+    std::string joined;
+    int n = 0;
+    for (size_t i = 0; i < names.size() && (int)i < max_stages; ++i, ++n) {
+      joined += names[i] + "\n";
+      h_ms[i] = ms[i];
+      h_count[i] = cnt[i];
+    }
+    JOLT_REQUIRE((int)joined.size() < names_bytes, JOLT_EBUFFER, "profile: name buffer too small");
+    memcpy(h_names, joined.c_str(), joined.size() + 1);
+    return n;
+  });
+}
 
 size_t jolt_workspace_bytes(const jolt_cache_desc *desc, const jolt_params *params) {
   size_t out = 0;
@@ -995,8 +1087,11 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
     AllocDev ad = bind_alloc(b.params, o);
     const long long dense = (long long)nb * pl.cell_elems() * pl.c;
     const double budget = (double)dense / pl.C;
-    run_allocation(nb, ad, pl.c, b.specT, b.specD, b.norm2, (int)pl.rT.size(), (int)pl.rd.size(), (int)pl.bits.size(),
-                   budget, b, st);
+    {
+      Stage prof("allocate", st);
+      run_allocation(nb, ad, pl.c, b.specT, b.specD, b.norm2, (int)pl.rT.size(), (int)pl.rd.size(),
+                     (int)pl.bits.size(), budget, b, st);
+    }
     std::vector<int> pick(nb);
     std::vector<double> n2(nb);
     AllocOut ao;
@@ -1128,6 +1223,7 @@ int jolt_reconstruct(const void *d_blob, const jolt_cache_desc *desc, const jolt
     g.C = Dm; g.c_ld = Kd; g.c_bs = (long long)GH * D * Kd; g.c_bs2 = (long long)D * Kd;
     gemm(MF_F16, SRC_F32, false, SRC_F32, true, g, nb * GH, 1, st);
     amax_cells(Dm, (long long)GH * D * Kd, (long long)GH * D * Kd, nb, am, st);
+    Stage prof("residual_decode", st);
     decode_cells(pl.dtype, (const DecCell *)(params_area + o_dc), nb, pl.T, D, GH, st);
     return 0;
   });

@@ -22,7 +22,8 @@ TORCH_DTYPE = {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}
 DTYPE_OF = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 EXPORTS = ["jolt_workspace_bytes", "jolt_output_bytes", "jolt_allocate", "jolt_compress", "jolt_reconstruct",
            "jolt_spectra", "jolt_token_spectrum_len", "jolt_encode_residual",
-           "jolt_encode_residual_workspace_bytes", "jolt_rotation", "jolt_eps2", "jolt_last_error"]
+           "jolt_encode_residual_workspace_bytes", "jolt_rotation", "jolt_eps2", "jolt_last_error", "jolt_profile",
+           "jolt_profile_read"]
 
 
 class JoltError(RuntimeError):
@@ -83,6 +84,8 @@ def load():
         "jolt_rotation": (ctypes.c_int, [i32, ctypes.c_uint64, ctypes.POINTER(dbl)]),
         "jolt_eps2": (ctypes.c_int, [i32, ctypes.POINTER(dbl)]),
         "jolt_last_error": (ctypes.c_char_p, []),
+        "jolt_profile": (ctypes.c_int, [i32]),
+        "jolt_profile_read": (i32, [ctypes.c_char_p, i32, ctypes.POINTER(dbl), ctypes.POINTER(i32), i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -272,3 +275,21 @@ def eps2(d_head):
     out = np.zeros(9)
     _check(load().jolt_eps2(d_head, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
     return out
+
+
+def profile(enable=True):
+    """Turn the library's per-stage HIP-event timing on or off."""
+    _check(load().jolt_profile(1 if enable else 0))
+
+
+def profile_read():
+    """{stage: (total ms, occurrences)} since the last read (waits for the recorded events)."""
+    n_max = 64
+    names = ctypes.create_string_buffer(8192)
+    ms = (ctypes.c_double * n_max)()
+    cnt = (ctypes.c_int32 * n_max)()
+    n = load().jolt_profile_read(names, 8192, ms, cnt, n_max)
+    if n < 0:
+        _check(n)
+    keys = names.value.decode().split("\n")[:n]
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(keys)}

@@ -357,13 +357,13 @@ def fit_cell(X, UT_r, rd):
     projected tensor, then the core.  Returns (U_T, U_d, core, projected spectrum)."""
     G, H, T, D = X.shape
     UT = _sign_normalise(np.asarray(UT_r, dtype=np.float64))
-    Y = np.einsum("tr,ghtd->ghrd", UT, X)               # token-projected tensor
+    Y = np.einsum("tr,ghtd->ghrd", UT, X, optimize=True)               # token-projected tensor
     Yr = Y.reshape(-1, D)
     w, V = np.linalg.eigh(Yr.T @ Yr)
     order = np.argsort(w)[::-1]
     w, V = w[order], V[:, order]
     Ud = _sign_normalise(V[:, :rd])
-    core = np.einsum("ghrd,dk->ghrk", Y, Ud)
+    core = np.einsum("ghrd,dk->ghrk", Y, Ud, optimize=True)
     return UT, Ud, core, np.maximum(w, 0.0)
 
 
@@ -373,7 +373,7 @@ def encode_cell(X, UT, Ud, core, b, Qrot, dtype):
     UTr = round_to_dtype(UT, dtype)
     Udr = round_to_dtype(Ud, dtype)
     Cr = round_to_dtype(core, dtype)
-    Xt = np.einsum("tr,ghrk,dk->ghtd", UTr, Cr, Udr)
+    Xt = np.einsum("tr,ghrk,dk->ghtd", UTr, Cr, Udr, optimize=True)
     out = {"UT": UTr, "Ud": Udr, "core": Cr, "backbone": Xt, "b": b}
     if b > 0:
         D = X.shape[-1]
@@ -385,7 +385,7 @@ def encode_cell(X, UT, Ud, core, b, Qrot, dtype):
 
 def decode_cell(UT, Ud, core, b, u, scales, Qrot, shape):
     """Backbone plus the de-rotated, dequantised residual (float64)."""
-    Xt = np.einsum("tr,ghrk,dk->ghtd", UT, core, Ud)
+    Xt = np.einsum("tr,ghrk,dk->ghtd", UT, core, Ud, optimize=True)
     if b > 0:
         D = shape[-1]
         Erot = dequantize_rows(u, scales, b).astype(np.float64)
