@@ -49,8 +49,8 @@ def kernel_models(T, L, H, D, G, ell, picks, dtype_bytes):
     m["sketch_gemm"] = {"flops": 2.0 * T * M * ell * cells_per_launch, "launches_per_call": 2,
                         "bytes": (T * M * dtype_bytes + 4.0 * ell * T) * cells_per_launch}
     # P^T = Q^T X: same contraction
-    m["project_gemm"] = {"flops": 2.0 * T * M * ell * cells_per_launch, "launches_per_call": 2,
-                         "bytes": (T * M * dtype_bytes + 4.0 * ell * T) * cells_per_launch}
+    m["project_gemm"] = {"flops": 2.0 * T * M * ell * n_cells, "launches_per_call": 1,
+                         "bytes": (T * M * dtype_bytes + 4.0 * ell * T) * n_cells}
     # fused residual encode: one launch over the cells with b > 0
     flops = 0.0
     byts = 0.0
@@ -62,8 +62,10 @@ def kernel_models(T, L, H, D, G, ell, picks, dtype_bytes):
         byts += R * D * dtype_bytes + T * p["rT"] * dtype_bytes + R * D * p["bits"] / 8.0 + 4.0 * R
     m["residual_encode"] = {"flops": flops, "bytes": byts, "launches_per_call": 1}
     # feature Gram: 2 R D^2 per cell, X read once
-    m["feature_gram"] = {"flops": 2.0 * GH * T * D * D * cells_per_launch, "launches_per_call": 2,
-                         "bytes": GH * T * D * dtype_bytes * cells_per_launch}
+    m["feature_gram"] = {"flops": 2.0 * GH * T * D * D * n_cells, "launches_per_call": 1,
+                         "bytes": GH * T * D * dtype_bytes * n_cells}
+    # per-(l,h) transpose of the cache: read + write once
+    m["transpose_x"] = {"flops": 0.0, "launches_per_call": 2, "bytes": 2.0 * GH * T * D * dtype_bytes * cells_per_launch}
     return m
 
 

@@ -201,6 +201,8 @@ struct Bufs {
   long long *tab_s;
   int *pick;
   AllocOut *aout;
+  // per-(l,h) transposed cache [cell][j][d][T_ld]
+  void *Xt;
   // device parameter area
   char *params;
   size_t params_bytes;
@@ -251,6 +253,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
   const int nb = pl.n_cells, D = pl.D;
   const long long ell = pl.ell, ld = pl.ell_ld;
   b.part = ar.take<float>(sz.part_elems);
+  b.Xt = ar.take<char>((long long)nb * pl.GH * D * pl.T_ld * pl.c);
   b.Gd64 = ar.take<double>((long long)nb * D * D);
   b.dD = ar.take<double>((long long)nb * D);
   b.eD = ar.take<double>((long long)nb * D);
@@ -379,23 +382,23 @@ void apply_f32(const float *A, long long lda, long long abs_, const float *a_ama
 // --------------------------------------------------------------------------- spectra stage
 void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
   Stage prof("feature_gram", st);
-  const int nkv = pl.n_cells / 2, D = pl.D;
-  const long long Kdim = (long long)pl.GH * pl.T;
+  const int D = pl.D;
+  const long long Kdim = (long long)pl.GH * pl.T_ld;  // zero padding of Xt contributes nothing
   int ns = nsplit_for(Kdim, 1, pl.n_cells, 8192);
   GemmArgs g = ga();
   g.M = D; g.N = D; g.K = (int)Kdim;
   g.k_chunk = (int)rup((Kdim + ns - 1) / ns, 32);
   ns = (int)((Kdim + g.k_chunk - 1) / g.k_chunk);
-  g.a_ld = D; g.b_ld = D;
-  g.a_bs = g.b_bs = pl.cell_elems();
-  g.c_ld = D; g.c_split = (long long)D * D; g.c_bs = 2LL * ns * D * D;
+  // A(m = d, k = (j, t)) = B(k, n = d) = Xt[j][d][t]
+  g.A = b.Xt; g.B = b.Xt;
+  g.a_ld = pl.T_ld; g.a_blk = pl.T_ld; g.a_blk_stride = (long long)D * pl.T_ld;
+  g.b_ld = pl.T_ld; g.b_blk = pl.T_ld; g.b_blk_stride = (long long)D * pl.T_ld;
+  g.a_bs = g.b_bs = (long long)pl.GH * D * pl.T_ld;
+  g.C = b.part; g.c_ld = D; g.c_split = (long long)D * D; g.c_bs = (long long)ns * D * D;
   JOLT_REQUIRE((long long)pl.n_cells * ns * D * D <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
-  for_kv(K, V, [&](int t, const void *X) {
-    GemmArgs h = g;
-    h.A = X; h.B = X;
-    h.C = b.part + (long long)t * ns * D * D;
-    gemm(pl.xmf(), pl.xsrc(), false, pl.xsrc(), false, h, nkv, ns, st);
-  });
+  gemm(pl.xmf(), pl.xsrc(), true, pl.xsrc(), true, g, pl.n_cells, ns, st);
+  (void)K;
+  (void)V;
   reduce_splits(b.part, (long long)ns * D * D, (long long)D * D, ns, 0, D, D, D, b.Gd64, true, (long long)D * D, D,
                 pl.n_cells, st);
   trace_f64(b.Gd64, (long long)D * D, D, pl.n_cells, b.norm2, st);
@@ -431,16 +434,15 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   // P^T = Q^T X_(T)  (ell x M), Q^T fp32 rows of length T
   auto project = [&](const float *Qt, const float *q_amax, float *out, float *c_amax) {
     Stage prof("project_gemm", st);
-    for_kv(K, V, [&](int t, const void *X) {
-      GemmArgs g = ga();
-      g.A = Qt + t * ell * Tld; g.M = (int)ell; g.N = (int)Mf; g.K = pl.T;
-      g.a_ld = Tld; g.a_bs = 2 * ell * Tld; g.a_amax = q_amax + t; g.ab_amax_bs = 2;
-      g.B = X; g.b_ld = pl.D; g.b_blk = pl.D; g.b_blk_stride = (long long)pl.T * pl.D; g.b_bs = cellX;
-      g.C = out + t * ell * Mf; g.c_ld = Mf; g.c_bs = 2 * ell * Mf;
-      g.c_amax = c_amax ? c_amax + t : nullptr; g.c_amax_bs = 2;
-      g.m_fastest = 1;
-      gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), false, g, nkv, 1, st);
-    });
+    // B(k = t, n = (j, d)) = Xt[j][d][t]
+    GemmArgs g = ga();
+    g.A = Qt; g.M = (int)ell; g.N = (int)Mf; g.K = pl.T;
+    g.a_ld = Tld; g.a_bs = ell * Tld; g.a_amax = q_amax;
+    g.B = b.Xt; g.b_ld = Tld; g.b_bs = Mf * Tld;
+    g.C = out; g.c_ld = Mf; g.c_bs = ell * Mf;
+    g.c_amax = c_amax;
+    g.m_fastest = 1;
+    gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, 1, st);
   };
   // rows of Y^T (ell x T) -> orthonormal rows by Cholesky QR (passes times)
   auto cholqr = [&](float *Y, float *Yam, float *tmp, float *tmp_am, int passes) -> float * {
@@ -690,15 +692,13 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     fill_f32(UTt, (long long)nb * kmax * Tld, 0.f, st);
     sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, T, b.specT, pl.nT, (int)T, d_rT, (int)kmax, nb, b.Zw, kmax * T, b.work,
                 (long long)invit_work_doubles((int)T, (int)kmax), nullptr, UTt, kmax * Tld, (int)Tld, st);
-    for_kv(K, V, [&](int t, const void *X) {
-      GemmArgs g = ga();
-      g.A = UTt + t * kmax * Tld; g.a_ld = Tld; g.a_bs = 2 * kmax * Tld; g.a_amax_c = 1.f;
-      g.B = X; g.b_ld = D; g.b_blk = D; g.b_blk_stride = T * D; g.b_bs = cellX;
-      g.M = (int)kmax; g.N = (int)Mf; g.K = (int)T;
-      g.C = Yp + t * kmax * Mf; g.c_ld = Mf; g.c_bs = 2 * kmax * Mf;
-      g.c_amax = amYp + t; g.c_amax_bs = 2; g.m_fastest = 1;
-      gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), false, g, nkv, 1, st);
-    });
+    GemmArgs g = ga();
+    g.A = UTt; g.a_ld = Tld; g.a_bs = kmax * Tld; g.a_amax_c = 1.f;
+    g.B = b.Xt; g.b_ld = Tld; g.b_bs = Mf * Tld;
+    g.M = (int)kmax; g.N = (int)Mf; g.K = (int)T;
+    g.C = Yp; g.c_ld = Mf; g.c_bs = kmax * Mf;
+    g.c_amax = amYp; g.m_fastest = 1;
+    gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, 1, st);
   }
   prof_vec.end();
   // ---- projected feature Gram -> U_d
@@ -814,6 +814,14 @@ Sizes sizes_worst(const Plan &pl) { return sizes_for(pl, pl.rT.back(), pl.rd.bac
 
 void spectra_all(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
   JOLT_REQUIRE(K && V, JOLT_EINVAL, "null cache pointer");
+  {
+    Stage prof("transpose_x", st);
+    const long long cellX = pl.cell_elems(), cellXt = (long long)pl.GH * pl.D * pl.T_ld;
+    for_kv(K, V, [&](int t, const void *X) {
+      transpose_x(X, (char *)b.Xt + (long long)t * cellXt * pl.c, pl.c, pl.T, pl.T_ld, pl.D, pl.GH, pl.n_cells / 2,
+                  cellX, 2 * cellXt, st);
+    });
+  }
   stage_feature(pl, b, K, V, st);
   if (pl.mode == JOLT_FLASH) stage_flash(pl, b, K, V, st);
   else stage_exact(pl, b, K, V, st);

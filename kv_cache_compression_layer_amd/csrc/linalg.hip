@@ -395,59 +395,171 @@ __global__ void __launch_bounds__(256) backtransform_kernel(const double *Zin, l
 }
 
 // ---------------------------------------------------------------------------------------------
-// Cholesky G = R^T R (R upper, fp64) and RinvT = (R^{-1})^T written as fp32 [n][ld_out]
-// (row c' holds column c' of R^{-1}); amax of RinvT for the fp16 split.  Non-positive pivots
-// are replaced by a tiny multiple of the largest diagonal (documented regularisation).
+// Cholesky G = R^T R (R upper, fp64), right-looking in 32-column panels, and the triangular
+// inverse by block rows from the bottom.  Writes RinvT = (R^{-1})^T as fp32 [n][ld_out] and its
+// max |entry| (for the fp16 split of the apply GEMM).  Non-positive pivots are replaced by a tiny
+// multiple of the largest diagonal entry (documented regularisation).
+// LDS: a 32 x 32 diagonal block and a 32 x (n - k0) panel (n <= 544 keeps the panel in LDS).
 // ---------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(LT) chol_inv_kernel(const double *G, long long g_bs, int ldg, int n, double *Rw,
+constexpr int CNB = 32;
+constexpr int CHOL_MAXN_LDS = 544;
+constexpr int CT = 256;  // threads: keeps the 32-wide register panels out of scratch
+
+__global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long g_bs, int ldg, int n, double *Rw,
                                                       long long r_bs, float *RinvT, long long o_bs, int ld_out,
                                                       float *amax) {
-  __shared__ double red[LT / 64];
-  __shared__ double piv_s;
+  extern __shared__ double sm[];
+  double *Dk = sm;               // [32][33] diagonal block / its inverse
+  double *P = sm + CNB * 33;     // [32][n] panel
+  __shared__ float fred[CT / 64];
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const double *Gb = G + b * g_bs;
-  double *R = Rw + b * r_bs;  // [n][n] upper, row-major; also holds R^{-1} later in lower? no: separate
-  double *Ri = R + (long long)n * n;  // R^{-1} upper [n][n]
+  double *A = Rw + b * r_bs;          // working copy, becomes R (upper)
+  double *X = A + (long long)n * n;   // R^{-1} (upper)
   double dmax = 0.0;
   for (int i = 0; i < n; ++i) dmax = fmax(dmax, Gb[(long long)i * ldg + i]);
   const double floor_piv = fmax(dmax * 1e-28, 1e-300);
-  // left-looking: row j of R from G[j][j..] minus contributions of rows < j
-  for (int j = 0; j < n; ++j) {
-    if (tid == 0) {
-      double s = Gb[(long long)j * ldg + j];
-      for (int kk = 0; kk < j; ++kk) s -= R[(long long)kk * n + j] * R[(long long)kk * n + j];
-      piv_s = sqrt(fmax(s, floor_piv));
-      R[(long long)j * n + j] = piv_s;
+  for (long long idx = tid; idx < (long long)n * n; idx += nt) {
+    int i = (int)(idx / n), j = (int)(idx % n);
+    A[idx] = (j >= i) ? Gb[(long long)i * ldg + j] : 0.0;
+  }
+  __syncthreads();
+  for (int k0 = 0; k0 < n; k0 += CNB) {
+    const int kb = min(CNB, n - k0), rem = n - k0 - kb;
+    // (1) diagonal block
+    for (int idx = tid; idx < kb * kb; idx += nt) {
+      int i = idx / kb, j = idx % kb;
+      Dk[i * 33 + j] = (j >= i) ? A[(long long)(k0 + i) * n + k0 + j] : 0.0;
     }
     __syncthreads();
-    const double p = piv_s;
-    for (int i = j + 1 + tid; i < n; i += nt) {
-      double s = Gb[(long long)j * ldg + i];
-      for (int kk = 0; kk < j; ++kk) s -= R[(long long)kk * n + j] * R[(long long)kk * n + i];
-      R[(long long)j * n + i] = s / p;
+    for (int j = 0; j < kb; ++j) {
+      if (tid == 0) Dk[j * 33 + j] = sqrt(fmax(Dk[j * 33 + j], floor_piv));
+      __syncthreads();
+      const double piv = Dk[j * 33 + j];
+      for (int c = j + 1 + tid; c < kb; c += nt) Dk[j * 33 + c] /= piv;
+      __syncthreads();
+      for (int idx = tid; idx < kb * kb; idx += nt) {
+        int r = idx / kb, c = idx % kb;
+        if (r > j && c >= r) Dk[r * 33 + c] -= Dk[j * 33 + r] * Dk[j * 33 + c];
+      }
+      __syncthreads();
+    }
+    for (int idx = tid; idx < kb * kb; idx += nt) {
+      int i = idx / kb, j = idx % kb;
+      A[(long long)(k0 + i) * n + k0 + j] = (j >= i) ? Dk[i * 33 + j] : 0.0;
+    }
+    // (2) panel: R[k0.., c] = R_kk^{-T} A[k0.., c]  (forward substitution per column)
+    const bool in_lds = (n <= CHOL_MAXN_LDS);
+    for (int c = tid; c < rem; c += nt) {
+      double x[CNB];
+#pragma unroll
+      for (int i = 0; i < CNB; ++i) {
+        double v = (i < kb) ? A[(long long)(k0 + i) * n + k0 + kb + c] : 0.0;
+#pragma unroll
+        for (int q = 0; q < CNB; ++q)
+          if (q < i) v -= Dk[q * 33 + i] * x[q];
+        x[i] = (i < kb) ? v / Dk[i * 33 + i] : 0.0;
+      }
+#pragma unroll
+      for (int i = 0; i < CNB; ++i)
+        if (i < kb) {
+          A[(long long)(k0 + i) * n + k0 + kb + c] = x[i];
+          if (in_lds) P[i * rem + c] = x[i];
+        }
+    }
+    __syncthreads();
+    // (3) trailing update A22 -= panel^T panel (upper triangle), 4 x 4 register blocks
+    const int nb4 = (rem + 3) / 4;
+    for (int blk = tid; blk < nb4 * nb4; blk += nt) {
+      const int bi = blk / nb4, bj = blk % nb4;
+      if (bj < bi) continue;
+      double acc[4][4] = {};
+      for (int q = 0; q < kb; ++q) {
+        double u[4], v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int ii = bi * 4 + t, jj = bj * 4 + t;
+          u[t] = (ii < rem) ? (in_lds ? P[q * rem + ii] : A[(long long)(k0 + q) * n + k0 + kb + ii]) : 0.0;
+          v[t] = (jj < rem) ? (in_lds ? P[q * rem + jj] : A[(long long)(k0 + q) * n + k0 + kb + jj]) : 0.0;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) acc[t][w] += u[t] * v[w];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int ii = bi * 4 + t, jj = bj * 4 + w;
+          if (ii < rem && jj < rem && jj >= ii) A[(long long)(k0 + kb + ii) * n + k0 + kb + jj] -= acc[t][w];
+        }
     }
     __syncthreads();
   }
-  // R^{-1} (upper): rows from the bottom up, all columns c >= i in parallel
-  for (int i = n - 1; i >= 0; --i) {
-    const double rii = R[(long long)i * n + i];
-    for (int c = i + tid; c < n; c += nt) {
-      double s = (c == i) ? 1.0 : 0.0;
-      for (int kk = i + 1; kk <= c; ++kk) s -= R[(long long)i * n + kk] * Ri[(long long)kk * n + c];
-      Ri[(long long)i * n + c] = s / rii;
+  // ---- X = R^{-1}: block rows from the bottom ----------------------------------------------
+  const int nblk = (n + CNB - 1) / CNB;
+  for (int bi = nblk - 1; bi >= 0; --bi) {
+    const int i0 = bi * CNB, ib = min(CNB, n - i0), rest = n - i0 - ib;
+    // inverse of the diagonal block (upper) into Dk: column c by back substitution
+    for (int idx = tid; idx < CNB * 33; idx += nt) Dk[idx] = 0.0;
+    __syncthreads();
+    for (int c = tid; c < ib; c += nt) {
+      for (int r = c; r >= 0; --r) {
+        double v = (r == c) ? 1.0 : 0.0;
+        for (int q = r + 1; q <= c; ++q) v -= A[(long long)(i0 + r) * n + i0 + q] * Dk[q * 33 + c];
+        Dk[r * 33 + c] = v / A[(long long)(i0 + r) * n + i0 + r];
+      }
+    }
+    // block row of R right of the diagonal block into the panel buffer
+    const bool in_lds = (n <= CHOL_MAXN_LDS);
+    for (int idx = tid; idx < ib * rest && in_lds; idx += nt) {
+      int r = idx / rest, c = idx % rest;
+      P[r * rest + c] = A[(long long)(i0 + r) * n + i0 + ib + c];
+    }
+    __syncthreads();
+    for (int idx = tid; idx < ib * ib; idx += nt) {
+      int r = idx / ib, c = idx % ib;
+      X[(long long)(i0 + r) * n + i0 + c] = Dk[r * 33 + c];
+    }
+    // X[i0.., c] = -Dinv * sum_{k in (i0+ib)..c} R[i0.., k] X[k][c], one thread per column c
+    for (int cc = tid; cc < rest; cc += nt) {
+      const int c = i0 + ib + cc;
+      double sacc[CNB];
+#pragma unroll
+      for (int r = 0; r < CNB; ++r) sacc[r] = 0.0;
+      for (int k = i0 + ib; k <= c; ++k) {
+        const double xk = X[(long long)k * n + c];
+        const int kk = k - i0 - ib;
+        if (in_lds) {
+#pragma unroll
+          for (int r = 0; r < CNB; ++r) sacc[r] += (r < ib ? P[r * rest + kk] : 0.0) * xk;
+        } else {
+#pragma unroll
+          for (int r = 0; r < CNB; ++r) sacc[r] += (r < ib ? A[(long long)(i0 + r) * n + k] : 0.0) * xk;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < CNB; ++r) {
+        double v = 0.0;
+#pragma unroll
+        for (int q = 0; q < CNB; ++q)
+          if (q >= r) v -= Dk[r * 33 + q] * sacc[q];  // Dk is zero beyond ib
+        if (r < ib) X[(long long)(i0 + r) * n + c] = v;
+      }
     }
     __syncthreads();
   }
+  // ---- output (R^{-1})^T as fp32 and its max |entry| -----------------------------------------
   float lmax = 0.f;
   float *O = RinvT + b * o_bs;
   for (long long idx = tid; idx < (long long)n * n; idx += nt) {
     int cp = (int)(idx / n), c = (int)(idx % n);  // RinvT[cp][c] = Rinv[c][cp]
-    float v = (c <= cp) ? (float)Ri[(long long)c * n + cp] : 0.f;
+    float v = (c <= cp) ? (float)X[(long long)c * n + cp] : 0.f;
     O[(long long)cp * ld_out + c] = v;
     lmax = fmaxf(lmax, fabsf(v));
   }
   lmax = warp_max(lmax);
-  __shared__ float fred[LT / 64];
   if ((tid & 63) == 0) fred[tid >> 6] = lmax;
   __syncthreads();
   if (tid == 0) {
@@ -505,6 +617,22 @@ __global__ void __launch_bounds__(256) gram64_kernel(const float *P, long long p
 
 }  // namespace
 
+// allow the large dynamic LDS allocations of the one-workgroup kernels (gfx950: 160 KiB per CU)
+void ensure_lds_attrs() {
+  static bool done = false;
+  if (done) return;
+  int dev = 0, maxsh = 65536;
+  HIP_TRY(hipGetDevice(&dev));
+  if (hipDeviceGetAttribute(&maxsh, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) maxsh = 65536;
+  const int want = maxsh - 2048;  // leave room for the kernels' static LDS
+  // best effort: the runtime may already allow the full amount
+  (void)hipFuncSetAttribute((const void *)chol_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipFuncSetAttribute((const void *)tridiag_values_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipFuncSetAttribute((const void *)backtransform_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipGetLastError();
+  done = true;
+}
+
 size_t tridiag_lds_bytes(int n) { return ((size_t)n * n + 2 * (size_t)n) * sizeof(double); }
 
 void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d, double *e, double *refl,
@@ -515,6 +643,7 @@ void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d
   bool use_lds = lds_full <= lds_cap;
   size_t shm = use_lds ? lds_full : std::max<size_t>(2 * (size_t)n * sizeof(double), 4096);
   JOLT_REQUIRE(shm <= 160 * 1024, JOLT_EINVAL, "eigensolver: n too large for LDS staging");
+  ensure_lds_attrs();
   hipLaunchKernelGGL(tridiag_values_kernel, dim3(batch), dim3(LT), shm, st, A, a_bs, lda, (const int *)nullptr, n,
                      d, e, refl, beta, t_bs, evals, ev_bs, clamp ? 1 : 0, use_lds ? 1 : 0);
   HIP_LAUNCH_CHECK();
@@ -530,6 +659,7 @@ void sym_eigvecs(const double *d, const double *e, const double *refl, const dou
   hipLaunchKernelGGL(invit_kernel, dim3(batch), dim3(LT), 2 * (size_t)n * sizeof(double), st, d, e, t_bs, evals,
                      ev_bs, k_dev, (const int *)nullptr, n, Zw, z_bs, work, w_bs, kmax);
   HIP_LAUNCH_CHECK();
+  ensure_lds_attrs();
   int vb = std::max(1, std::min(32, (int)((60 * 1024) / (n * 8)) - 1));
   size_t shm = ((size_t)vb * n + n + 64) * sizeof(double);
   dim3 grid((kmax + vb - 1) / vb, batch);
@@ -540,7 +670,9 @@ void sym_eigvecs(const double *d, const double *e, const double *refl, const dou
 
 void chol_inv(const double *G, long long g_bs, int ldg, int n, int batch, double *Rw, long long r_bs, float *RinvT,
               long long o_bs, int ld_out, float *amax, hipStream_t st) {
-  hipLaunchKernelGGL(chol_inv_kernel, dim3(batch), dim3(LT), 0, st, G, g_bs, ldg, n, Rw, r_bs, RinvT, o_bs, ld_out,
+  size_t shm = (size_t)(CNB * 33 + (n <= CHOL_MAXN_LDS ? CNB * n : 0)) * sizeof(double);
+  ensure_lds_attrs();
+  hipLaunchKernelGGL(chol_inv_kernel, dim3(batch), dim3(CT), shm, st, G, g_bs, ldg, n, Rw, r_bs, RinvT, o_bs, ld_out,
                      amax);
   HIP_LAUNCH_CHECK();
 }

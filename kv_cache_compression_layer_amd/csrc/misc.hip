@@ -183,6 +183,26 @@ __global__ void amax_kernel(const float *x, long long per, long long bs, float *
   if ((threadIdx.x & 63) == 0) atomicMax((unsigned int *)(out + cell), __float_as_uint(m));
 }
 
+// Xt[b][j][d][t] = X[b][j][t][d] (16- or 32-bit elements), t padded to T_ld with zeros.
+template <typename E>
+__global__ void transpose_x_kernel(const E *X, E *Xt, int T, int T_ld, int D, int GH, long long x_bs, long long xt_bs) {
+  __shared__ E tile[64][65];
+  const int b = blockIdx.z, j = blockIdx.y % GH;
+  const int t0 = blockIdx.x * 64, d0 = (blockIdx.y / GH) * 64;
+  const E *src = X + b * x_bs + (long long)j * T * D;
+  E *dst = Xt + b * xt_bs + (long long)j * D * T_ld;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
+  for (int yy = ty; yy < 64; yy += 4) {
+    int t = t0 + yy, d = d0 + tx;
+    tile[yy][tx] = (t < T && d < D) ? src[(long long)t * D + d] : E(0);
+  }
+  __syncthreads();
+  for (int yy = ty; yy < 64; yy += 4) {
+    int d = d0 + yy, t = t0 + tx;
+    if (d < D && t < T_ld) dst[(long long)d * T_ld + t] = tile[tx][yy];
+  }
+}
+
 int grid_for(long long n) { return (int)std::max<long long>(1, std::min<long long>((n + 255) / 256, 8192)); }
 
 }  // namespace
@@ -190,6 +210,17 @@ int grid_for(long long n) { return (int)std::max<long long>(1, std::min<long lon
 void gen_omega(void *out, int dtype, int M, int ell, uint64_t key, hipStream_t st) {
   long long n = (long long)M * ell;
   hipLaunchKernelGGL(omega_kernel, dim3(grid_for(n)), dim3(256), 0, st, out, dtype, M, ell, key);
+  HIP_LAUNCH_CHECK();
+}
+void transpose_x(const void *X, void *Xt, int elem_bytes, int T, int T_ld, int D, int GH, int batch, long long x_bs,
+                 long long xt_bs, hipStream_t st) {
+  dim3 grid((T_ld + 63) / 64, GH * ((D + 63) / 64), batch);
+  if (elem_bytes == 2)
+    hipLaunchKernelGGL(transpose_x_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)X, (uint16_t *)Xt, T,
+                       T_ld, D, GH, x_bs, xt_bs);
+  else
+    hipLaunchKernelGGL(transpose_x_kernel<float>, grid, dim3(256), 0, st, (const float *)X, (float *)Xt, T, T_ld, D,
+                       GH, x_bs, xt_bs);
   HIP_LAUNCH_CHECK();
 }
 void fill_f32(float *p, long long n, float v, hipStream_t st) {

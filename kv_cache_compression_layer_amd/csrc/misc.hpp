@@ -15,6 +15,9 @@ struct FactorCell {
 };
 
 void gen_omega(void *out, int dtype, int M, int ell, uint64_t key, hipStream_t st);
+// per-(l,h) slice transpose of a cell: Xt[b][j][d][t] = X[b][j][t][d], t zero-padded to T_ld
+void transpose_x(const void *X, void *Xt, int elem_bytes, int T, int T_ld, int D, int GH, int batch, long long x_bs,
+                 long long xt_bs, hipStream_t st);
 void fill_f32(float *p, long long n, float v, hipStream_t st);
 void fill_f64(double *p, long long n, double v, hipStream_t st);
 void trace_f64(const double *G, long long g_bs, int n, int batch, double *out, hipStream_t st);
