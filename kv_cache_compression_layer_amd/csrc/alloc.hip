@@ -92,7 +92,7 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
       best.cost = INFINITY;
       best.s = LLONG_MAX;
       best.b = best.rT = best.rd = INT_MAX;
-      best.idx = -1;
+      best.idx = 0;  // any finite candidate replaces it; keeps the index valid for non-finite tables
       for (int i = lane; i < per; i += 64) {
         const long long w = (long long)c * per + i;
         Best cand;

@@ -170,6 +170,7 @@ Plan make_plan(const jolt_cache_desc *d, const jolt_params *p) {
     pl.power_iters = p->power_iters;
     pl.nT = q + 1;
     JOLT_REQUIRE(pl.rT.back() <= q, JOLT_EINVAL, "rT_grid exceeds q_cap");
+    JOLT_REQUIRE(ell <= 544, JOLT_EINVAL, "q_cap + oversample must not exceed 544");
   } else {
     JOLT_REQUIRE(pl.T <= pl.M, JOLT_EINVAL, "exact mode needs T <= |g| n_h d_h");
     pl.q = pl.T;
@@ -190,7 +191,9 @@ struct Bufs {
   double *specT, *specD, *norm2;
   // flash / exact token stage
   void *omegaT;
-  float *bufA, *bufB, *Pt, *Zt, *RinvT;
+  // tall panels, each in two layouts: rows of length T ([ell][T_ld]) and rows of length ell
+  // ([T][ell_ld]); P / Z likewise ([ell][M] and [M][ell_ld])
+  float *bufA, *bufB, *bufA2, *bufB2, *Pt, *P2, *Zt, *Z2, *RinvT, *YpT;
   double *G64, *Rw, *dT, *eT, *betaT, *evT;
   float *amax;  // [8][n_cells]
   // fit
@@ -273,8 +276,12 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
     b.omegaT = ar.take<char>(ell * pl.M * pl.c);
     b.bufA = ar.take<float>((long long)nb * ell * pl.T_ld);
     b.bufB = ar.take<float>((long long)nb * ell * pl.T_ld);
+    b.bufA2 = ar.take<float>((long long)nb * pl.T * ld);
+    b.bufB2 = ar.take<float>((long long)nb * pl.T * ld);
     b.Pt = ar.take<float>((long long)nb * ell * pl.M);
+    b.P2 = ar.take<float>((long long)nb * pl.M * ld);
     b.Zt = ar.take<float>((long long)nb * ell * pl.M);
+    b.Z2 = ar.take<float>((long long)nb * pl.M * ld);
     b.Rw = ar.take<double>((long long)nb * 2 * ell * ell);
     b.RinvT = ar.take<float>((long long)nb * ell * ld);
     b.Wrows = ar.take<float>((long long)nb * sz.kmax * ld);
@@ -286,6 +293,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
   b.work = ar.take<double>((long long)nb * invit_work_doubles((int)n_tok, sz.kmax));
   b.ZwD = ar.take<double>((long long)nb * sz.kmax_d * D);
   b.workD = ar.take<double>((long long)nb * invit_work_doubles(D, sz.kmax_d));
+  b.YpT = ar.take<float>((long long)nb * pl.M * sz.kmax);
   b.Udrows = ar.take<float>((long long)nb * sz.kmax_d * D);
   b.Cp = ar.take<float>((long long)nb * sz.kmax * pl.GH * sz.kmax_d);
   b.Udr = ar.take<float>((long long)nb * sz.kmax_d * D);
@@ -365,20 +373,6 @@ void gram_f32(const Plan &pl, Bufs &b, const float *X, long long ldx, long long 
   reduce_splits(b.part, g.c_bs, g.c_split, ns, 0, rows, rows, rl, out, true, out_bs, ldo, batch, st);
 }
 
-// C[b] = A[b] B[b]  with A = RinvT-like [M][lda] K-contig fp32 and B N-contig fp32 rows
-void apply_f32(const float *A, long long lda, long long abs_, const float *a_amax, const float *B, long long ldb,
-               long long bbs, const float *b_amax, float *C, long long ldc, long long cbs, float *c_amax, int M, int N,
-               int K, int batch, hipStream_t st) {
-  GemmArgs g = ga();
-  g.A = A; g.B = B; g.C = C;
-  g.M = M; g.N = N; g.K = K;
-  g.a_ld = lda; g.a_bs = abs_; g.a_amax = a_amax;
-  g.b_ld = ldb; g.b_bs = bbs; g.b_amax = b_amax; g.ab_amax_bs = 1;
-  g.c_ld = ldc; g.c_bs = cbs; g.c_amax = c_amax; g.c_amax_bs = 1;
-  g.m_fastest = 1;
-  gemm(MF_F16, SRC_F32, true, SRC_F32, false, g, batch, 1, st);
-}
-
 // --------------------------------------------------------------------------- spectra stage
 void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
   Stage prof("feature_gram", st);
@@ -405,97 +399,108 @@ void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStr
   sym_eigvals(b.Gd64, (long long)D * D, D, D, pl.n_cells, b.dD, b.eD, b.Gd64, b.betaD, D, b.specD, D, true, st);
 }
 
-// X-operand GEMM: C = A * X^T-ish variants share the cell bookkeeping
+// FlashJoLT token spectrum (Sec. 3.1): randomized subspace iteration with Cholesky QR.
+// Every large contraction is K-contiguous on both operands; tall fp32 panels are written in
+// both layouts by the GEMM epilogue so the next consumer never transposes while loading.
 void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
   const int nb = pl.n_cells, nkv = nb / 2;
-  const long long ell = pl.ell, ld = pl.ell_ld, Tld = pl.T_ld, Mf = pl.M;
+  const long long ell = pl.ell, ld = pl.ell_ld, Tld = pl.T_ld, Mf = pl.M, T = pl.T;
   const long long cellX = pl.cell_elems();
   float *amY = b.amax, *amR = b.amax + nb, *amQ = b.amax + 2 * nb, *amP = b.amax + 3 * nb, *amZ = b.amax + 4 * nb;
   gen_omega(b.omegaT, pl.dtype, pl.M, pl.ell, stream_key(pl.sketch_seed, 2), st);
   fill_f32(b.amax, 8LL * nb, 0.f, st);
 
-  // Y^T = A X_(T)^T with A = Omega^T (16-bit / fp32) or Z^T (fp32)
-  auto sketch = [&](const void *A, int a_src, long long a_bs, const float *a_amax, float *out, float *c_amax) {
+  // Y^T = A X_(T)^T with A = Omega^T (cache dtype) or Z^T (fp32); also Y = (Y^T)^T
+  auto sketch = [&](const void *A, int a_src, long long a_bs, const float *a_amax, float *outT, float *outR,
+                    float *c_amax) {
     Stage prof("sketch_gemm", st);
     for_kv(K, V, [&](int t, const void *X) {
       GemmArgs g = ga();
       g.A = (const char *)A + (a_bs ? t * a_bs * (a_src == SRC_F32 ? 4 : 2) : 0);
-      g.B = X; g.M = (int)ell; g.N = pl.T; g.K = (int)Mf;
+      g.B = X; g.M = (int)ell; g.N = (int)T; g.K = (int)Mf;
       g.a_ld = Mf; g.a_bs = 2 * a_bs;
       g.a_amax = a_amax ? a_amax + t : nullptr; g.ab_amax_bs = 2;
-      g.b_ld = pl.D; g.b_blk = pl.D; g.b_blk_stride = (long long)pl.T * pl.D; g.b_bs = cellX;
-      g.C = out + t * ell * Tld; g.c_ld = Tld; g.c_bs = 2 * ell * Tld;
+      g.b_ld = pl.D; g.b_blk = pl.D; g.b_blk_stride = T * pl.D; g.b_bs = cellX;
+      g.C = outT + t * ell * Tld; g.c_ld = Tld; g.c_bs = 2 * ell * Tld;
+      g.C2 = outR + t * T * ld; g.c2_ld = ld; g.c2_bs = 2 * T * ld;
       g.c_amax = c_amax ? c_amax + t : nullptr; g.c_amax_bs = 2;
       g.m_fastest = 1;
-      int mf = pl.xmf();
-      gemm(mf, a_src, true, pl.xsrc(), true, g, nkv, 1, st);
+      gemm(pl.xmf(), a_src, true, pl.xsrc(), true, g, nkv, 1, st);
     });
   };
-  // P^T = Q^T X_(T)  (ell x M), Q^T fp32 rows of length T
-  auto project = [&](const float *Qt, const float *q_amax, float *out, float *c_amax) {
+  // P^T = Q^T X_(T) (ell x M) and P = (P^T)^T, from the rows of Q^T and the transposed cache
+  auto project = [&](const float *Qt, const float *q_amax, float *c_amax) {
     Stage prof("project_gemm", st);
-    // B(k = t, n = (j, d)) = Xt[j][d][t]
     GemmArgs g = ga();
-    g.A = Qt; g.M = (int)ell; g.N = (int)Mf; g.K = pl.T;
+    g.A = Qt; g.M = (int)ell; g.N = (int)Mf; g.K = (int)T;
     g.a_ld = Tld; g.a_bs = ell * Tld; g.a_amax = q_amax;
     g.B = b.Xt; g.b_ld = Tld; g.b_bs = Mf * Tld;
-    g.C = out; g.c_ld = Mf; g.c_bs = ell * Mf;
+    g.C = b.Pt; g.c_ld = Mf; g.c_bs = ell * Mf;
+    g.C2 = b.P2; g.c2_ld = ld; g.c2_bs = Mf * ld;
     g.c_amax = c_amax;
     g.m_fastest = 1;
     gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, 1, st);
   };
-  // rows of Y^T (ell x T) -> orthonormal rows by Cholesky QR (passes times)
-  auto cholqr = [&](float *Y, float *Yam, float *tmp, float *tmp_am, int passes) -> float * {
+  // R from the Gram of the rows of Yt, then Q = Y R^{-1} in both layouts
+  struct Pair {
+    float *T, *R, *am;
+  };
+  Pair pa{b.bufA, b.bufA2, amY}, pb{b.bufB, b.bufB2, amQ};
+  auto cholqr = [&](Pair y, Pair q, int passes) -> Pair {
     Stage prof("cholqr_tall", st);
     for (int p = 0; p < passes; ++p) {
-      gram_f32(pl, b, Y, Tld, ell * Tld, (int)ell, pl.T, Yam, b.G64, ell * ell, (int)ell, nb, st);
+      gram_f32(pl, b, y.T, Tld, ell * Tld, (int)ell, (int)T, y.am, b.G64, ell * ell, (int)ell, nb, st);
       chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, 2 * ell * ell, b.RinvT, ell * ld, (int)ld, amR, st);
-      fill_f32(tmp_am, nb, 0.f, st);
-      apply_f32(b.RinvT, ld, ell * ld, amR, Y, Tld, ell * Tld, Yam, tmp, Tld, ell * Tld, tmp_am, (int)ell, pl.T,
-                (int)ell, nb, st);
-      std::swap(Y, tmp);
-      std::swap(Yam, tmp_am);
+      fill_f32(q.am, nb, 0.f, st);
+      GemmArgs g = ga();
+      g.A = y.R; g.a_ld = ld; g.a_bs = T * ld; g.a_amax = y.am;
+      g.B = b.RinvT; g.b_ld = ld; g.b_bs = ell * ld; g.b_amax = amR;
+      g.M = (int)T; g.N = (int)ell; g.K = (int)ell;
+      g.C = q.R; g.c_ld = ld; g.c_bs = T * ld;
+      g.C2 = q.T; g.c2_ld = Tld; g.c2_bs = ell * Tld;
+      g.c_amax = q.am;
+      g.m_fastest = 0;
+      gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
+      std::swap(y, q);
     }
-    return Y;
+    return y;
   };
 
-  sketch(b.omegaT, pl.xsrc(), 0, nullptr, b.bufA, amY);
-  float *Q = b.bufA, *Qam = amY;
-  {
-    float *other = b.bufB, *other_am = amQ;
-    Q = cholqr(b.bufA, amY, other, other_am, 1);
-    Qam = (Q == b.bufA) ? amY : amQ;
-  }
+  sketch(b.omegaT, pl.xsrc(), 0, nullptr, pa.T, pa.R, pa.am);
+  Pair Q = cholqr(pa, pb, 1);
   for (int it = 0; it < pl.power_iters; ++it) {
     fill_f32(amP, nb, 0.f, st);
-    project(Q, Qam, b.Pt, amP);
-    // Z = orth(P): Cholesky QR on the rows of P^T (length M)
-    Stage prof_z("cholqr_z", st);
-    gram_f32(pl, b, b.Pt, Mf, ell * Mf, (int)ell, (int)Mf, amP, b.G64, ell * ell, (int)ell, nb, st);
-    chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, 2 * ell * ell, b.RinvT, ell * ld, (int)ld, amR, st);
-    fill_f32(amZ, nb, 0.f, st);
-    apply_f32(b.RinvT, ld, ell * ld, amR, b.Pt, Mf, ell * Mf, amP, b.Zt, Mf, ell * Mf, amZ, (int)ell, (int)Mf,
-              (int)ell, nb, st);
-    float *Y = (Q == b.bufA) ? b.bufB : b.bufA;
-    float *Yam = (Q == b.bufA) ? amQ : amY;
-    fill_f32(Yam, nb, 0.f, st);
-    sketch(b.Zt, SRC_F32, ell * Mf, amZ, Y, Yam);
-    float *other = (Y == b.bufA) ? b.bufB : b.bufA;
-    float *other_am = (Y == b.bufA) ? amQ : amY;
+    project(Q.T, Q.am, amP);
+    {
+      // Z = orth(P) by Cholesky QR; Z^T feeds the next sketch
+      Stage prof_z("cholqr_z", st);
+      gram_f32(pl, b, b.Pt, Mf, ell * Mf, (int)ell, (int)Mf, amP, b.G64, ell * ell, (int)ell, nb, st);
+      chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, 2 * ell * ell, b.RinvT, ell * ld, (int)ld, amR, st);
+      fill_f32(amZ, nb, 0.f, st);
+      GemmArgs g = ga();
+      g.A = b.P2; g.a_ld = ld; g.a_bs = Mf * ld; g.a_amax = amP;
+      g.B = b.RinvT; g.b_ld = ld; g.b_bs = ell * ld; g.b_amax = amR;
+      g.M = (int)Mf; g.N = (int)ell; g.K = (int)ell;
+      g.C = b.Z2; g.c_ld = ld; g.c_bs = Mf * ld;
+      g.C2 = b.Zt; g.c2_ld = Mf; g.c2_bs = ell * Mf;
+      g.c_amax = amZ;
+      gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
+    }
+    Pair Y = (Q.T == pa.T) ? pb : pa;
+    Pair other = (Q.T == pa.T) ? pa : pb;
+    fill_f32(Y.am, nb, 0.f, st);
+    sketch(b.Zt, SRC_F32, ell * Mf, amZ, Y.T, Y.R, Y.am);
     const int passes = (it + 1 == pl.power_iters) ? 2 : 1;
-    Q = cholqr(Y, Yam, other, other_am, passes);
-    Qam = (Q == b.bufA) ? amY : amQ;
+    Q = cholqr(Y, other, passes);
   }
   if (pl.power_iters == 0) {  // the final basis is orthonormalised twice
-    float *other = (Q == b.bufA) ? b.bufB : b.bufA;
-    float *other_am = (Q == b.bufA) ? amQ : amY;
-    Q = cholqr(Q, Qam, other, other_am, 1);
-    Qam = (Q == b.bufA) ? amY : amQ;
+    Pair other = (Q.T == pa.T) ? pb : pa;
+    Q = cholqr(Q, other, 1);
   }
   // B = Q^T X_(T) -> H = B B^T (fp64) -> eigenvalues; spectrum = top q + tail entry
   float *amP1 = b.amax + 5 * nb;
   fill_f32(amP1, nb, 0.f, st);
-  project(Q, Qam, b.Pt, amP1);
+  project(Q.T, Q.am, amP1);
   {
     Stage prof("gram64", st);
     gram64(b.Pt, ell * Mf, (int)Mf, (int)ell, (int)Mf, b.G64, ell * ell, (int)ell, nb, st);
@@ -505,8 +510,11 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     sym_eigvals(b.G64, ell * ell, (int)ell, (int)ell, nb, b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, true, st);
   }
   flash_spec(b.evT, ell, pl.q, b.norm2, b.specT, pl.nT, nb, st);
-  // the fit reads Q^T from b.bufA
-  if (Q != b.bufA) std::swap(b.bufA, b.bufB);
+  // the fit reads Q (both layouts) from b.bufA / b.bufA2
+  if (Q.T != b.bufA) {
+    std::swap(b.bufA, b.bufB);
+    std::swap(b.bufA2, b.bufB2);
+  }
 }
 
 void stage_exact(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
@@ -648,6 +656,19 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     uint32_t h[10] = {0x544C4F4Au, 1u, (uint32_t)pl.G, (uint32_t)pl.H, (uint32_t)pl.T, (uint32_t)D,
                       (uint32_t)p.rT, (uint32_t)p.rd, (uint32_t)p.bits, (uint32_t)pl.dtype};
     memcpy(f.hdr, h, sizeof(h));
+    // padding after each part: [start + bytes, next part)
+    const long long R = (long long)GH * pl.T;
+    const long long part_start[5] = {p.sec.off_UT, p.sec.off_Ud, p.sec.off_core, p.sec.off_scales, p.sec.off_codes};
+    const long long part_bytes[5] = {(long long)pl.T * p.rT * pl.c, (long long)D * p.rd * pl.c,
+                                     (long long)GH * p.rT * p.rd * pl.c,
+                                     p.bits > 0 ? R * 4 : 0, p.bits > 0 ? R * D * p.bits / 8 : 0};
+    const long long part_end[5] = {p.sec.off_Ud, p.sec.off_core, p.sec.off_scales,
+                                   p.bits > 0 ? p.sec.off_codes : p.sec.off_scales, p.sec.end};
+    for (int r = 0; r < 5; ++r) {
+      const long long a = part_start[r] + part_bytes[r];
+      f.pad_ptr[r] = out + p.off + a;
+      f.pad_len[r] = (int)std::max<long long>(0, part_end[r] - a);
+    }
   }
   std::vector<size_t> offs;
   size_t o_rT = u.add(rTv.data(), nb * 4), o_rd = u.add(rdv.data(), nb * 4), o_fc = u.add(fc.data(), nb * sizeof(FactorCell));
@@ -675,18 +696,19 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     // U_T^T = W^T Q^T (rows of length T)
     GemmArgs g = ga();
     g.A = b.Wrows; g.a_ld = ld; g.a_bs = kmax * ld; g.a_amax_c = 1.f;
-    g.B = b.bufA; g.b_ld = Tld; g.b_bs = ell * Tld;
-    g.b_amax = nullptr; g.b_amax_c = 1.f;  // Q has orthonormal rows: |entries| <= 1
+    g.B = b.bufA2; g.b_ld = ld; g.b_bs = (long long)pl.T * ld;  // Q [T][ell_ld]
+    g.b_amax = nullptr; g.b_amax_c = 1.f;  // Q has orthonormal columns: |entries| <= 1
     g.M = (int)kmax; g.N = pl.T; g.K = (int)ell;
     g.C = UTt; g.c_ld = Tld; g.c_bs = kmax * Tld; g.m_fastest = 1;
-    gemm(MF_F16, SRC_F32, true, SRC_F32, false, g, nb, 1, st);
+    gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
     // token-projected tensor Y_p = W^T P1^T  (kmax x M)
     GemmArgs h = ga();
     h.A = b.Wrows; h.a_ld = ld; h.a_bs = kmax * ld; h.a_amax_c = 1.f;
-    h.B = b.Pt; h.b_ld = Mf; h.b_bs = ell * Mf; h.b_amax = b.amax + 5 * nb; h.ab_amax_bs = 1;
+    h.B = b.P2; h.b_ld = ld; h.b_bs = Mf * ld; h.b_amax = b.amax + 5 * nb; h.ab_amax_bs = 1;
     h.M = (int)kmax; h.N = (int)Mf; h.K = (int)ell;
     h.C = Yp; h.c_ld = Mf; h.c_bs = kmax * Mf; h.c_amax = amYp; h.c_amax_bs = 1; h.m_fastest = 1;
-    gemm(MF_F16, SRC_F32, true, SRC_F32, false, h, nb, 1, st);
+    h.C2 = b.YpT; h.c2_ld = kmax; h.c2_bs = Mf * kmax;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, true, h, nb, 1, st);
   } else {
     const long long T = pl.T;
     fill_f32(UTt, (long long)nb * kmax * Tld, 0.f, st);
@@ -697,6 +719,7 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     g.B = b.Xt; g.b_ld = Tld; g.b_bs = Mf * Tld;
     g.M = (int)kmax; g.N = (int)Mf; g.K = (int)T;
     g.C = Yp; g.c_ld = Mf; g.c_bs = kmax * Mf;
+    g.C2 = b.YpT; g.c2_ld = kmax; g.c2_bs = Mf * kmax;
     g.c_amax = amYp; g.m_fastest = 1;
     gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, 1, st);
   }
@@ -706,15 +729,18 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     Stage prof("fit_feature_factor", st);
     const long long Kd = kmax * GH;
     int ns = nsplit_for(Kd, 1, nb, 1024);
+    // A(m = d, k = (j, r)) = B(k, n = d) = Y_p^T[(j D + d)][r]
     GemmArgs g = ga();
-    g.A = Yp; g.B = Yp; g.M = D; g.N = D; g.K = (int)Kd;
-    g.a_ld = D; g.b_ld = D; g.a_bs = g.b_bs = kmax * Mf;
+    g.A = b.YpT; g.B = b.YpT; g.M = D; g.N = D; g.K = (int)Kd;
+    g.a_ld = kmax; g.a_blk = (int)kmax; g.a_blk_stride = (long long)D * kmax;
+    g.b_ld = kmax; g.b_blk = (int)kmax; g.b_blk_stride = (long long)D * kmax;
+    g.a_bs = g.b_bs = Mf * kmax;
     g.a_amax = amYp; g.b_amax = amYp; g.ab_amax_bs = 1;
     g.k_chunk = (int)rup((Kd + ns - 1) / ns, 32);
     ns = (int)((Kd + g.k_chunk - 1) / g.k_chunk);
     JOLT_REQUIRE((long long)nb * ns * D * D <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
     g.C = b.part; g.c_ld = D; g.c_split = (long long)D * D; g.c_bs = (long long)ns * D * D;
-    gemm(MF_F16, SRC_F32, false, SRC_F32, false, g, nb, ns, st);
+    gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, ns, st);
     reduce_splits(b.part, g.c_bs, g.c_split, ns, 0, D, D, D, b.Gd64, true, (long long)D * D, D, nb, st);
     sym_eigvals(b.Gd64, (long long)D * D, D, D, nb, b.dD, b.eD, b.Gd64, b.betaD, D, b.evD, D, true, st);
     fill_f32(b.Udrows, (long long)nb * kmd * D, 0.f, st);
@@ -966,10 +992,10 @@ int jolt_spectra(const void *d_K, const void *d_V, const jolt_cache_desc *desc, 
                     (long long)invit_work_doubles((int)ell, (int)kmax), nullptr, b.Wrows, kmax * ld, (int)ld, st);
         GemmArgs g = ga();
         g.A = b.Wrows; g.a_ld = ld; g.a_bs = kmax * ld; g.a_amax_c = 1.f;
-        g.B = b.bufA; g.b_ld = Tld; g.b_bs = ell * Tld; g.b_amax_c = 1.f;
+        g.B = b.bufA2; g.b_ld = ld; g.b_bs = (long long)pl.T * ld; g.b_amax_c = 1.f;
         g.M = n_vec; g.N = pl.T; g.K = (int)ell;
         g.C = b.bufB; g.c_ld = Tld; g.c_bs = kmax * Tld; g.m_fastest = 1;
-        gemm(MF_F16, SRC_F32, true, SRC_F32, false, g, nb, 1, st);
+        gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
       } else {
         sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, pl.T, b.specT, pl.nT, pl.T, dk, (int)kmax, nb, b.Zw, kmax * pl.T,
                     b.work, (long long)invit_work_doubles(pl.T, (int)kmax), nullptr, b.bufB, kmax * Tld, (int)Tld, st);

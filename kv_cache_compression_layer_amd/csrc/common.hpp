@@ -123,6 +123,9 @@ struct GemmArgs {
   long long a_bs2, b_bs2, c_bs2;
   int ab_amax_bs, c_amax_bs;
   float alpha;  // output multiplier
+  // optional second, transposed output: C2[n][m] (row pitch c2_ld, batch stride c2_bs)
+  float *C2;
+  long long c2_ld, c2_bs;
 };
 
 // a_kc: A contiguous along K (else along M); b_kc: B contiguous along K (else along N)

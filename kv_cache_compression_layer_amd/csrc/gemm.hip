@@ -20,12 +20,26 @@ namespace {
 
 using namespace core;
 
+// Store one raw 8-vector (already in registers) into the LDS tile [plane][row][k], splitting into
+// planes.  KC: the 8 values run along k at row r; else along rows r..r+7 at column k.
+template <int S, int MF, int P, bool KC>
+__device__ __forceinline__ void store_raw8(uint16_t *tile, int rows, int r, int k, const Raw8<S> &x, float scale) {
+  if constexpr (KC && S != SRC_F32 && ((S == SRC_F16 && MF == MF_F16) || (S == SRC_BF16 && MF == MF_BF16))) {
+    *(uint4 *)(tile + r * LDK + k) = x.v;  // already in the MFMA format
+  } else {
+    uint16_t pl[8][3];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split_planes<S, MF>(raw_elem<S>(x, i), scale, pl[i]);
+    lds_store8<P, KC>(tile, rows, r, k, pl);
+  }
+}
+
 template <int MF, int SA, bool AKC, int SB, bool BKC>
 __global__ void __launch_bounds__(NT) gemm_kernel(GemmArgs g) {
   constexpr int PA = Planes<SA, MF>::n, PB = Planes<SB, MF>::n;
   constexpr int MAXO = (MF == MF_F16) ? 1 : 2;  // keep cross products with plane order i+j <= MAXO
-  __shared__ __attribute__((aligned(16))) uint16_t As[PA * BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[PB * BN * LDK];
+  constexpr int ASZ = PA * BM * LDK, BSZ = PB * BN * LDK, STG = ASZ + BSZ;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int zb = blockIdx.z, split = blockIdx.y;
@@ -62,7 +76,8 @@ __global__ void __launch_bounds__(NT) gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float ra[2][8], rb[2][8];
+  Raw8<SA> ra[2];
+  Raw8<SB> rb[2];
 
   auto gload = [&](int k0) {
 #pragma unroll
@@ -71,34 +86,32 @@ __global__ void __launch_bounds__(NT) gemm_kernel(GemmArgs g) {
       if constexpr (AKC) {
         int r = v >> 2, kv = (v & 3) * 8;
         int m = m0 + r;
-        load8<SA>(Ab, (long long)m * g.a_ld, k0 + kv, kend, m < g.M, g.a_blk, g.a_blk_stride, ra[it]);
+        load_raw8<SA>(Ab, (long long)m * g.a_ld, k0 + kv, kend, m < g.M, g.a_blk, g.a_blk_stride, ra[it]);
       } else {
         int kr = v >> 4, mv = (v & 15) * 8;
         int k = k0 + kr;
-        load8<SA>(Ab, (long long)k * g.a_ld, m0 + mv, g.M, k < kend, g.a_blk, g.a_blk_stride, ra[it]);
+        load_raw8<SA>(Ab, (long long)k * g.a_ld, m0 + mv, g.M, k < kend, g.a_blk, g.a_blk_stride, ra[it]);
       }
       if constexpr (BKC) {
         int r = v >> 2, kv = (v & 3) * 8;
         int n = n0 + r;
-        load8<SB>(Bb, (long long)n * g.b_ld, k0 + kv, kend, n < g.N, g.b_blk, g.b_blk_stride, rb[it]);
+        load_raw8<SB>(Bb, (long long)n * g.b_ld, k0 + kv, kend, n < g.N, g.b_blk, g.b_blk_stride, rb[it]);
       } else {
         int kr = v >> 4, nv = (v & 15) * 8;
         int k = k0 + kr;
-        load8<SB>(Bb, (long long)k * g.b_ld, n0 + nv, g.N, k < kend, g.b_blk, g.b_blk_stride, rb[it]);
+        load_raw8<SB>(Bb, (long long)k * g.b_ld, n0 + nv, g.N, k < kend, g.b_blk, g.b_blk_stride, rb[it]);
       }
     }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
+    uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       int v = tid + it * NT;
-      uint16_t pa[8][3], pb[8][3];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) { split_planes<SA, MF>(ra[it][i], ascale, pa[i]); split_planes<SB, MF>(rb[it][i], bscale, pb[i]); }
-      if constexpr (AKC) lds_store8<PA, true>(As, BM, v >> 2, (v & 3) * 8, pa);
-      else lds_store8<PA, false>(As, BM, (v & 15) * 8, v >> 4, pa);
-      if constexpr (BKC) lds_store8<PB, true>(Bs, BN, v >> 2, (v & 3) * 8, pb);
-      else lds_store8<PB, false>(Bs, BN, (v & 15) * 8, v >> 4, pb);
+      if constexpr (AKC) store_raw8<SA, MF, PA, true>(As, BM, v >> 2, (v & 3) * 8, ra[it], ascale);
+      else store_raw8<SA, MF, PA, false>(As, BM, (v & 15) * 8, v >> 4, ra[it], ascale);
+      if constexpr (BKC) store_raw8<SB, MF, PB, true>(Bs, BN, v >> 2, (v & 3) * 8, rb[it], bscale);
+      else store_raw8<SB, MF, PB, false>(Bs, BN, (v & 15) * 8, v >> 4, rb[it], bscale);
     }
   };
 
@@ -107,11 +120,13 @@ __global__ void __launch_bounds__(NT) gemm_kernel(GemmArgs g) {
 
   if (kbeg < kend) {
     gload(kbeg);
-    lstore();
+    lstore(0);
     __syncthreads();
+    int buf = 0;
     for (int k0 = kbeg; k0 < kend; k0 += BK) {
       const bool more = k0 + BK < kend;
       if (more) gload(k0 + BK);
+      const uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
       uint4 af[PA][4], bf[PB][4];
 #pragma unroll
       for (int p = 0; p < PA; ++p)
@@ -132,31 +147,42 @@ __global__ void __launch_bounds__(NT) gemm_kernel(GemmArgs g) {
             for (int i = 0; i < 4; ++i)
 #pragma unroll
               for (int j = 0; j < 4; ++j) acc[i][j] = mfma<MF>(af[pa][i], bf[pb][j], acc[i][j]);
+      if (more) lstore(buf ^ 1);
       __syncthreads();
-      if (more) {
-        lstore();
-        __syncthreads();
-      }
+      buf ^= 1;
     }
   }
 
   const float cs = g.alpha / (ascale * bscale);
   float *Cb = g.C + (long long)batch * g.c_bs + (long long)bin * g.c_bs2 + (long long)split * g.c_split;
+  float *C2b = g.C2 ? g.C2 + (long long)batch * g.c2_bs : nullptr;
   float lmax = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
+      const int mb = m0 + wm * 64 + i * 16 + (lane >> 4) * 4;
+      const int n = n0 + wn * 64 + j * 16 + fr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        int m = m0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        int n = n0 + wn * 64 + j * 16 + fr;
+        const int m = mb + r;
         if (m < g.M && n < g.N) {
           float v = acc[i][j][r] * cs;
           Cb[(long long)m * g.c_ld + n] = v;
           lmax = fmaxf(lmax, fabsf(v));
         }
       }
+      if (C2b && n < g.N) {
+        if (mb + 4 <= g.M && ((g.c2_ld & 3) == 0)) {
+          *(float4 *)(C2b + (long long)n * g.c2_ld + mb) =
+              make_float4(acc[i][j][0] * cs, acc[i][j][1] * cs, acc[i][j][2] * cs, acc[i][j][3] * cs);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (mb + r < g.M) C2b[(long long)n * g.c2_ld + mb + r] = acc[i][j][r] * cs;
+        }
+      }
+    }
   if (g.c_amax) {
     lmax = warp_max(lmax);
     if (lane == 0) atomicMax((unsigned int *)(g.c_amax + (long long)batch * g.c_amax_bs), __float_as_uint(lmax));
@@ -205,6 +231,7 @@ void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int b
                    g.a_bs2 % 8 == 0 && g.b_bs2 % 8 == 0 && ((uintptr_t)g.A % 16) == 0 && ((uintptr_t)g.B % 16) == 0,
                JOLT_EINVAL, "gemm: operands must be 16-byte aligned with strides in multiples of 8 elements");
   JOLT_REQUIRE(g.inner >= 1 && batch % g.inner == 0, JOLT_EINVAL, "gemm: bad inner batch");
+  JOLT_REQUIRE(g.C2 == nullptr || ((uintptr_t)g.C2 % 16) == 0, JOLT_EINVAL, "gemm: C2 must be 16-byte aligned");
   GemmArgs h = g;
   if (nsplit == 1) h.k_chunk = ((g.K + BK - 1) / BK) * BK;
   if (mf == MF_F16) {

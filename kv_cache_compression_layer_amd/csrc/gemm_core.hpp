@@ -79,6 +79,66 @@ __device__ __forceinline__ void split_planes(float x, float scale, uint16_t (&p)
   }
 }
 
+// Raw 8-element vector of a source (no conversion): 16-bit -> one uint4, fp32 -> two float4.
+template <int S>
+struct Raw8 {
+  uint4 v;
+};
+template <>
+struct Raw8<SRC_F32> {
+  float4 a, b;
+};
+
+template <int S>
+__device__ __forceinline__ void load_raw8(const void *base, long long off, int c0, int lim, bool row_ok, int blk,
+                                          long long bstride, Raw8<S> &r) {
+  if (row_ok && c0 + 8 <= lim) {
+    long long o = off + blk_idx(c0, blk, bstride);
+    if constexpr (S == SRC_F32) {
+      const float4 *p = (const float4 *)((const float *)base + o);
+      r.a = p[0];
+      r.b = p[1];
+    } else {
+      r.v = *(const uint4 *)((const uint16_t *)base + o);
+    }
+  } else {
+    if constexpr (S == SRC_F32) {
+      float t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int c = c0 + i;
+        t[i] = (row_ok && c < lim) ? ((const float *)base)[off + blk_idx(c, blk, bstride)] : 0.f;
+      }
+      r.a = make_float4(t[0], t[1], t[2], t[3]);
+      r.b = make_float4(t[4], t[5], t[6], t[7]);
+    } else {
+      uint16_t t[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int c = c0 + i;
+        t[i] = (row_ok && c < lim) ? ((const uint16_t *)base)[off + blk_idx(c, blk, bstride)] : (uint16_t)0;
+      }
+      r.v.x = t[0] | ((uint32_t)t[1] << 16);
+      r.v.y = t[2] | ((uint32_t)t[3] << 16);
+      r.v.z = t[4] | ((uint32_t)t[5] << 16);
+      r.v.w = t[6] | ((uint32_t)t[7] << 16);
+    }
+  }
+}
+
+template <int S>
+__device__ __forceinline__ float raw_elem(const Raw8<S> &r, int i) {
+  if constexpr (S == SRC_F32) {
+    const float t[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+    return t[i];
+  } else {
+    const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+    uint16_t h = (uint16_t)((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFF));
+    if constexpr (S == SRC_F16) return f16_to_f32(h);
+    else return bf16_to_f32(h);
+  }
+}
+
 template <int MF>
 __device__ __forceinline__ f32x4 mfma(const uint4 &a, const uint4 &b, f32x4 c) {
   if constexpr (MF == MF_F16)

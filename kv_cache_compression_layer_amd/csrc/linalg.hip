@@ -403,30 +403,34 @@ __global__ void __launch_bounds__(256) backtransform_kernel(const double *Zin, l
 // ---------------------------------------------------------------------------------------------
 constexpr int CNB = 32;
 constexpr int CHOL_MAXN_LDS = 544;
-constexpr int CT = 256;  // threads: keeps the 32-wide register panels out of scratch
+constexpr int CT = 1024;
 
 __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long g_bs, int ldg, int n, double *Rw,
                                                       long long r_bs, float *RinvT, long long o_bs, int ld_out,
                                                       float *amax) {
   extern __shared__ double sm[];
   double *Dk = sm;               // [32][33] diagonal block / its inverse
-  double *P = sm + CNB * 33;     // [32][n] panel
+  double *Rd = sm + CNB * 33;    // [32][33] diagonal block of R (inverse phase)
+  double *P = sm + 2 * CNB * 33; // [32][n] panel (row block of R)
   __shared__ float fred[CT / 64];
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int lane = tid & 63, wave = tid >> 6, nwave = nt >> 6;
   const double *Gb = G + b * g_bs;
   double *A = Rw + b * r_bs;          // working copy, becomes R (upper)
   double *X = A + (long long)n * n;   // R^{-1} (upper)
+  const bool in_lds = (n <= CHOL_MAXN_LDS);
   double dmax = 0.0;
   for (int i = 0; i < n; ++i) dmax = fmax(dmax, Gb[(long long)i * ldg + i]);
   const double floor_piv = fmax(dmax * 1e-28, 1e-300);
   for (long long idx = tid; idx < (long long)n * n; idx += nt) {
     int i = (int)(idx / n), j = (int)(idx % n);
     A[idx] = (j >= i) ? Gb[(long long)i * ldg + j] : 0.0;
+    X[idx] = 0.0;
   }
   __syncthreads();
   for (int k0 = 0; k0 < n; k0 += CNB) {
     const int kb = min(CNB, n - k0), rem = n - k0 - kb;
-    // (1) diagonal block
+    // (1) diagonal block (unblocked right-looking Cholesky in LDS)
     for (int idx = tid; idx < kb * kb; idx += nt) {
       int i = idx / kb, j = idx % kb;
       Dk[i * 33 + j] = (j >= i) ? A[(long long)(k0 + i) * n + k0 + j] : 0.0;
@@ -448,8 +452,7 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
       int i = idx / kb, j = idx % kb;
       A[(long long)(k0 + i) * n + k0 + j] = (j >= i) ? Dk[i * 33 + j] : 0.0;
     }
-    // (2) panel: R[k0.., c] = R_kk^{-T} A[k0.., c]  (forward substitution per column)
-    const bool in_lds = (n <= CHOL_MAXN_LDS);
+    // (2) panel: R[k0.., c] = R_kk^{-T} A[k0.., c], forward substitution per column
     for (int c = tid; c < rem; c += nt) {
       double x[CNB];
 #pragma unroll
@@ -476,11 +479,12 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
       double acc[4][4] = {};
       for (int q = 0; q < kb; ++q) {
         double u[4], v[4];
+        const double *src = in_lds ? P + q * rem : A + (long long)(k0 + q) * n + k0 + kb;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int ii = bi * 4 + t, jj = bj * 4 + t;
-          u[t] = (ii < rem) ? (in_lds ? P[q * rem + ii] : A[(long long)(k0 + q) * n + k0 + kb + ii]) : 0.0;
-          v[t] = (jj < rem) ? (in_lds ? P[q * rem + jj] : A[(long long)(k0 + q) * n + k0 + kb + jj]) : 0.0;
+          u[t] = (ii < rem) ? src[ii] : 0.0;
+          v[t] = (jj < rem) ? src[jj] : 0.0;
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -498,54 +502,57 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
     __syncthreads();
   }
   // ---- X = R^{-1}: block rows from the bottom ----------------------------------------------
+  // X[i0+r][c] = -sum_q Dinv[r][q] S[q][c],  S[q][c] = sum_{k = i0+ib}^{c} R[i0+q][k] X[k][c]
+  // Work split: each wave owns 64 consecutive columns (one per lane) and 8 rows q of S.
   const int nblk = (n + CNB - 1) / CNB;
+  double *S = P;  // reuse the panel buffer for S when it fits, else X's rows are read from global
   for (int bi = nblk - 1; bi >= 0; --bi) {
     const int i0 = bi * CNB, ib = min(CNB, n - i0), rest = n - i0 - ib;
-    // inverse of the diagonal block (upper) into Dk: column c by back substitution
-    for (int idx = tid; idx < CNB * 33; idx += nt) Dk[idx] = 0.0;
+    // inverse of the diagonal block (upper) into Dk, from an LDS copy Rd of the block
+    for (int idx = tid; idx < CNB * 33; idx += nt) {
+      Dk[idx] = 0.0;
+      const int r = idx / 33, c = idx % 33;
+      Rd[idx] = (r < ib && c < ib && c >= r) ? A[(long long)(i0 + r) * n + i0 + c] : 0.0;
+    }
     __syncthreads();
     for (int c = tid; c < ib; c += nt) {
       for (int r = c; r >= 0; --r) {
         double v = (r == c) ? 1.0 : 0.0;
-        for (int q = r + 1; q <= c; ++q) v -= A[(long long)(i0 + r) * n + i0 + q] * Dk[q * 33 + c];
-        Dk[r * 33 + c] = v / A[(long long)(i0 + r) * n + i0 + r];
+        for (int q = r + 1; q <= c; ++q) v -= Rd[r * 33 + q] * Dk[q * 33 + c];
+        Dk[r * 33 + c] = v / Rd[r * 33 + r];
       }
-    }
-    // block row of R right of the diagonal block into the panel buffer
-    const bool in_lds = (n <= CHOL_MAXN_LDS);
-    for (int idx = tid; idx < ib * rest && in_lds; idx += nt) {
-      int r = idx / rest, c = idx % rest;
-      P[r * rest + c] = A[(long long)(i0 + r) * n + i0 + ib + c];
     }
     __syncthreads();
     for (int idx = tid; idx < ib * ib; idx += nt) {
       int r = idx / ib, c = idx % ib;
       X[(long long)(i0 + r) * n + i0 + c] = Dk[r * 33 + c];
     }
-    // X[i0.., c] = -Dinv * sum_{k in (i0+ib)..c} R[i0.., k] X[k][c], one thread per column c
-    for (int cc = tid; cc < rest; cc += nt) {
-      const int c = i0 + ib + cc;
-      double sacc[CNB];
+    if (rest > 0) {
+      const int cgroups = (rest + 63) / 64, ngroups = cgroups * 4;  // (column group, 8-row group)
+      for (int gi = wave; gi < ngroups; gi += nwave) {
+        const int cg = gi >> 2, rg = gi & 3;
+        const int cc = cg * 64 + lane, c = i0 + ib + cc;
+        double acc[8] = {};
+        if (cc < rest) {
+          for (int k = i0 + ib; k <= c; ++k) {
+            const double xk = X[(long long)k * n + c];
 #pragma unroll
-      for (int r = 0; r < CNB; ++r) sacc[r] = 0.0;
-      for (int k = i0 + ib; k <= c; ++k) {
-        const double xk = X[(long long)k * n + c];
-        const int kk = k - i0 - ib;
-        if (in_lds) {
-#pragma unroll
-          for (int r = 0; r < CNB; ++r) sacc[r] += (r < ib ? P[r * rest + kk] : 0.0) * xk;
-        } else {
-#pragma unroll
-          for (int r = 0; r < CNB; ++r) sacc[r] += (r < ib ? A[(long long)(i0 + r) * n + k] : 0.0) * xk;
+            for (int q = 0; q < 8; ++q) {
+              const int r = rg * 8 + q;
+              acc[q] += ((r < ib) ? A[(long long)(i0 + r) * n + k] : 0.0) * xk;
+            }
+          }
         }
+        if (in_lds && cc < rest)
+#pragma unroll
+          for (int q = 0; q < 8; ++q) S[(rg * 8 + q) * rest + cc] = acc[q];
       }
-#pragma unroll
-      for (int r = 0; r < CNB; ++r) {
+      __syncthreads();
+      for (int idx = tid; idx < ib * rest && in_lds; idx += nt) {
+        const int r = idx / rest, cc = idx % rest;
         double v = 0.0;
-#pragma unroll
-        for (int q = 0; q < CNB; ++q)
-          if (q >= r) v -= Dk[r * 33 + q] * sacc[q];  // Dk is zero beyond ib
-        if (r < ib) X[(long long)(i0 + r) * n + c] = v;
+        for (int q = r; q < ib; ++q) v -= Dk[r * 33 + q] * S[q * rest + cc];
+        X[(long long)(i0 + r) * n + i0 + ib + cc] = v;
       }
     }
     __syncthreads();
@@ -670,7 +677,8 @@ void sym_eigvecs(const double *d, const double *e, const double *refl, const dou
 
 void chol_inv(const double *G, long long g_bs, int ldg, int n, int batch, double *Rw, long long r_bs, float *RinvT,
               long long o_bs, int ld_out, float *amax, hipStream_t st) {
-  size_t shm = (size_t)(CNB * 33 + (n <= CHOL_MAXN_LDS ? CNB * n : 0)) * sizeof(double);
+  JOLT_REQUIRE(n >= 1 && n <= CHOL_MAXN_LDS, JOLT_EINVAL, "Cholesky QR: panel width above 544 is not supported");
+  size_t shm = (size_t)(2 * CNB * 33 + CNB * n) * sizeof(double);
   ensure_lds_attrs();
   hipLaunchKernelGGL(chol_inv_kernel, dim3(batch), dim3(CT), shm, st, G, g_bs, ldg, n, Rw, r_bs, RinvT, o_bs, ld_out,
                      amax);

@@ -159,7 +159,7 @@ __global__ void headers_kernel(const FactorCell *cells, int ncells) {
   const FactorCell c = cells[cell];
   if (threadIdx.x < 64) {
     uint32_t *h = (uint32_t *)c.header;
-    h[threadIdx.x] = threadIdx.x < 10 ? c.hdr[threadIdx.x] : 0u;
+    h[threadIdx.x] = threadIdx.x < 10 ? c.hdr[threadIdx.x] : 0u;  // 256-byte header
   }
 }
 
@@ -267,7 +267,7 @@ void get_small(int dtype, const FactorCell *cells, int ncells, int kmax, int kma
   HIP_LAUNCH_CHECK();
 }
 void write_headers(const FactorCell *cells, int ncells, hipStream_t st) {
-  hipLaunchKernelGGL(headers_kernel, dim3(ncells), dim3(64), 0, st, cells, ncells);
+  hipLaunchKernelGGL(headers_kernel, dim3(ncells), dim3(256), 0, st, cells, ncells);
   HIP_LAUNCH_CHECK();
 }
 void bcat_q(float *Bcat, int ncells, int GH, int D, int Kb, const float *Qt, hipStream_t st) {

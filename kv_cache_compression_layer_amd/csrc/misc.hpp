@@ -12,6 +12,8 @@ struct FactorCell {
   void *core;  // [GH][rT][rd]
   int rT, rd, bits, pad;
   uint32_t hdr[10];
+  void *pad_ptr[5];  // alignment padding after U_T, U_d, core, scales, codes (zeroed by the header writer)
+  int pad_len[5];
 };
 
 void gen_omega(void *out, int dtype, int M, int ell, uint64_t key, hipStream_t st);

@@ -1,0 +1,141 @@
+"""GPU checks at the full sizes of the model-shaped workloads, in the launch configuration that
+bench.py times (one jolt_compress over the whole cache).  The oracle recomputes what it can in
+seconds (every cell of the Mistral-7B shape; sampled cells elsewhere); the rest is checked through
+properties that hold at any size (tail identity, budget, grid membership, decode error)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from kv_cache_compression_layer_amd import jolt
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.view(torch.uint16).cpu().numpy() if t.dtype == torch.bfloat16 else t.cpu().numpy()
+
+
+def _run(K, V, cfg, groups):
+    blob, picks, lam = jolt.compress(K, V, cfg)
+    Ko, Vo = torch.empty_like(K), torch.empty_like(V)
+    jolt.reconstruct(blob, cfg, picks, Ko, Vo)
+    torch.cuda.synchronize()
+    return blob, picks, lam, Ko, Vo
+
+
+def _properties(K, V, cfg, picks, rT, rd, bits, C, dt):
+    sT, sD, n2, _ = jolt.spectra(K, V, cfg)
+    torch.cuda.synchronize()
+    sT, n2 = sT.cpu().numpy(), n2.cpu().numpy()
+    if cfg.params.mode == jolt.FLASH:
+        assert np.all(np.abs(sT.sum(axis=1) - n2) <= 1e-9 * n2)      # tail entry restores ||X||^2
+    assert np.all(np.diff(sT[:, :-1], axis=1) <= 1e-9 * n2[:, None])  # descending
+    for p in picks:
+        assert p["rT"] in rT and p["rd"] in rd and p["bits"] in set(bits) | {0}
+    return sT, n2
+
+
+@pytest.mark.parametrize("C", [2.0, 3.0])
+def test_mistral7b_shape_flash_full_size(C):
+    L, H, T, D = 32, 8, 1024, 128
+    K, V = synth.power_law(L=L, H=H, T=T, D=D, dtype="f16", seed=0)
+    groups = list(range(0, L + 1, 4))
+    rT, rd, bits = [8, 16, 24, 32], list(range(8, 129, 8)), [2, 4, 8]
+    eps2 = oracle.eps2_calibrate(D, [0] + bits, rows=1 << 16)
+    p = dict(mode="flash", oversample=10, power_iters=1, qcap=None, rT_grid=rT, rd_grid=rd, bits=bits, eps2=eps2,
+             target_ratio=C)
+    ref = oracle.compress(_np(K), _np(V), groups, "f16", p)
+    cfg = jolt.Config(1, L, H, T, D, jolt.F16, groups, jolt.FLASH, rT, rd, bits, C, eps2=eps2)
+    Kd, Vd = K.cuda(), V.cuda()
+    blob, picks, lam, Ko, Vo = _run(Kd, Vd, cfg, groups)
+    assert [(q["rT"], q["rd"], q["bits"]) for q in picks] == [(x["rT"], x["rd"], x["b"]) for x in ref["cells"]]
+    # the multiplier: the oracle's tables minimised at the GPU's lambda give the same picks
+    eps = p["eps2"]
+    for x, q in zip(ref["cells"], picks):
+        t = oracle.cell_table(oracle.CellShape(4, H, T, D), 2, x["specT"], x["specD"], x["norm2"], rT, rd,
+                              sorted(set(bits) | {0}), eps)
+        i = oracle.argmin_cell(t, lam)
+        assert (int(t["rT"][i]), int(t["rd"][i]), int(t["b"][i])) == (q["rT"], q["rd"], q["bits"])
+    assert sum(q["bytes"] for q in picks) <= ref["budget"]
+    for x in ref["cells"]:
+        src = Ko if x["kv"] == 0 else Vo
+        X = (K if x["kv"] == 0 else V)[0, groups[x["group"]]:groups[x["group"] + 1]].double().numpy()
+        got = src[0, groups[x["group"]]:groups[x["group"] + 1]].double().cpu().numpy()
+        err = np.linalg.norm(got - X) / np.linalg.norm(X)
+        assert abs(err - x["rel_err"]) <= 1e-3 + 0.02 * x["rel_err"] + 3e-4, (err, x["rel_err"])
+    _properties(Kd, Vd, cfg, picks, rT, rd, bits, C, "f16")
+
+
+def _big(dt, n_seq, L, H, T, D, alpha_v, C, seed=0):
+    K, V = synth.power_law(n_seq=n_seq, L=L, H=H, T=T, D=D, dtype=dt, seed=seed, alpha_v=alpha_v, device="cuda")
+    groups = list(range(0, L + 1, 4))
+    q = oracle.qcap_eq5(T, C)
+    rT, rd, bits = list(range(8, q + 1, 8)), list(range(8, D + 1, 8)), [2, 4, 8]
+    eps2 = jolt.eps2(D)
+    cfg = jolt.Config(n_seq, L, H, T, D, {"f16": jolt.F16, "bf16": jolt.BF16}[dt], groups, jolt.FLASH, rT, rd, bits,
+                      C, eps2={b: eps2[b] for b in range(9)})
+    return K, V, groups, cfg, rT, rd, bits
+
+
+def _sampled_oracle(K, groups, sT_gpu, sD_gpu, n2_gpu, dt, flash_omega=None):
+    """The oracle's ||X||^2 and feature spectrum of the first key cell."""
+    X = oracle.to_f64(_np(K[0, groups[0]:groups[1]]), dt)
+    n2 = float(np.sum(X * X))
+    sD = oracle.feature_spectrum(X)
+    assert abs(n2_gpu[0] - n2) <= 1e-6 * n2
+    assert np.abs(sD_gpu[0] - sD).max() <= 1e-5 * n2
+    return X, n2
+
+
+@pytest.mark.parametrize("C", [2.0, 5.0])
+def test_llama31_8b_long_context_full_size(C):
+    K, V, groups, cfg, rT, rd, bits = _big("f16", 1, 32, 8, 65536, 128, 0.5, C)
+    blob, picks, lam, Ko, Vo = _run(K, V, cfg, groups)
+    dense = 2 * 32 * 8 * 65536 * 128 * 2
+    S = sum(p["bytes"] for p in picks)
+    assert S <= dense / C and S >= 0.9 * dense / C
+    sT, sD, n2, _ = jolt.spectra(K, V, cfg)
+    torch.cuda.synchronize()
+    sT, sD, n2 = sT.cpu().numpy(), sD.cpu().numpy(), n2.cpu().numpy()
+    assert np.all(np.abs(sT.sum(axis=1) - n2) <= 1e-9 * n2)
+    _sampled_oracle(K, groups, sT, sD, n2, "f16")
+    # decode error of every cell is small and close to the surrogate's ordering (K vs V harder)
+    for c, p in enumerate(picks):
+        s, g, t = 0, (c // 2), c % 2
+        X = (K if t == 0 else V)[0, groups[g]:groups[g + 1]].float()
+        Xh = (Ko if t == 0 else Vo)[0, groups[g]:groups[g + 1]].float()
+        err = float(torch.linalg.vector_norm(Xh - X) / torch.linalg.vector_norm(X))
+        assert err < 0.2, (c, err)
+
+
+def test_batched_serving_shape_bf16_full_size():
+    K, V, groups, cfg, rT, rd, bits = _big("bf16", 4, 32, 8, 16384, 128, 1.0, 3.0)
+    blob, picks, lam, Ko, Vo = _run(K, V, cfg, groups)
+    assert len(picks) == 64
+    dense = 2 * 4 * 32 * 8 * 16384 * 128 * 2
+    assert sum(p["bytes"] for p in picks) <= dense / 3.0
+    sT, sD, n2, _ = jolt.spectra(K, V, cfg)
+    torch.cuda.synchronize()
+    sT, sD, n2 = sT.cpu().numpy(), sD.cpu().numpy(), n2.cpu().numpy()
+    assert np.all(np.abs(sT.sum(axis=1) - n2) <= 1e-9 * n2)
+    _sampled_oracle(K, groups, sT, sD, n2, "bf16")
+
+
+def test_llama2_13b_shape_flash_full_size_sampled_token_spectrum():
+    L, H, T, D, C = 40, 40, 4096, 128, 3.0
+    K, V, groups, cfg, rT, rd, bits = _big("f16", 1, L, H, T, D, 1.0, C)
+    blob, picks, lam, Ko, Vo = _run(K, V, cfg, groups)
+    assert len(picks) == 20
+    sT, sD, n2, _ = jolt.spectra(K, V, cfg)
+    torch.cuda.synchronize()
+    sT, sD, n2 = sT.cpu().numpy(), sD.cpu().numpy(), n2.cpu().numpy()
+    X, N2 = _sampled_oracle(K, groups, sT, sD, n2, "f16")
+    # the oracle's randomized token spectrum of the first key cell with the same test matrix
+    q = oracle.qcap_eq5(T, C)
+    ell = q + 10
+    Xt = oracle.token_unfolding(X)
+    Om = oracle.sketch_matrix(Xt.shape[1], ell, 0, "f16")
+    _, spec = oracle.token_factors_flash(Xt, Om, q, 1, N2)
+    assert np.abs(sT[0] - spec).max() <= 1e-5 * N2

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bars (stated per test): reconstructions within 1e-3 relative Frobenius; token subspaces via
+projectors within 1e-3 where the oracle's spectral gap makes the subspace well defined; quantised
+codes >= 99.9% identical with the rest off by one; allocations bit-exact on identical spectra.
+Inputs are seeded synthetic caches (synth/), sizes chosen so the oracle runs in seconds while
+spanning several 128-row tiles with ragged tails.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from kv_cache_compression_layer_amd import jolt
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f16": jolt.F16, "bf16": jolt.BF16, "f32": jolt.F32}
+ULP_TOL = {"f16": 1e-3, "bf16": 4e-3, "f32": 1e-5}
+
+
+def _np(t):
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.uint16).cpu().numpy()
+    return t.cpu().numpy()
+
+
+CASES = {
+    # name: (generator kwargs, dtype, mode, n_seq, L, H, T, D, ratio, rT grid, bits)
+    "tiny_f32_exact": ("lowrank", "f32", "exact", 1, 1, 2, 128, 64, 2.0, [8, 16, 32, 64], [2, 3, 4]),
+    "f16_exact_ragged": ("pl", "f16", "exact", 1, 8, 2, 300, 64, 3.0, list(range(8, 297, 8)), [2, 4, 8]),
+    "f16_flash_d128": ("pl", "f16", "flash", 1, 8, 4, 700, 128, 2.0, [8, 16, 24, 32], [2, 4, 8]),
+    "bf16_flash": ("pl", "bf16", "flash", 1, 4, 2, 1000, 64, 4.0, [8, 16, 24, 32], [1, 2, 3, 4]),
+    "f16_flash_two_seqs": ("pl", "f16", "flash", 2, 4, 2, 256, 64, 3.0, [8, 16, 24, 32], [2, 4, 8]),
+}
+_cache = {}
+
+
+def case(name):
+    if name in _cache:
+        return _cache[name]
+    gen, dt, mode, S, L, H, T, D, C, rT, bits = CASES[name]
+    if gen == "lowrank":
+        K, V = synth.per_head_lowrank(L=L, H=H, T=T, D=D, dtype=dt)
+    else:
+        K, V = synth.power_law(n_seq=S, L=L, H=H, T=T, D=D, dtype=dt, seed=11, alpha_v=0.5 if D == 128 else 1.0)
+    G = 4 if L % 4 == 0 else L
+    groups = list(range(0, L + 1, G))
+    rd = [r for r in [8, 16, 24, 32, 40, 48, 56, 64, 80, 96, 112, 128] if r <= D]
+    eps2 = oracle.eps2_calibrate(D, [0] + bits, rows=1 << 15)
+    p = dict(mode=mode, oversample=10, power_iters=1, qcap=None, rT_grid=rT, rd_grid=rd, bits=bits, eps2=eps2,
+             target_ratio=C)
+    ref = oracle.compress(_np(K), _np(V), groups, dt, p, keep=True)
+    assert ref["status"] == 0
+    cfg = jolt.Config(S, L, H, T, D, DT[dt], groups, jolt.FLASH if mode == "flash" else jolt.EXACT, rT, rd, bits, C,
+                      eps2=eps2)
+    out = dict(K=K, V=V, Kd=K.cuda(), Vd=V.cuda(), groups=groups, ref=ref, cfg=cfg, dt=dt, D=D, T=T, p=p, bits=bits,
+               rd=rd, rT=rT, G=G)
+    _cache[name] = out
+    return out
+
+
+def _cell_view(t, c, groups):
+    s, g, kv = c["seq"], c["group"], c["kv"]
+    return t[s, groups[g]:groups[g + 1]]
+
+
+def _round(x, dt):
+    return oracle.round_to_dtype(x, dt)
+
+
+# ------------------------------------------------------------------------------ reconstruct
+@pytest.mark.parametrize("name", list(CASES))
+def test_reconstruct_matches_oracle_on_oracle_blob(name):
+    c = case(name)
+    ref = c["ref"]
+    blob = torch.from_numpy(np.frombuffer(ref["blob"], dtype=np.uint8).copy()).cuda()
+    picks = [{"rT": x["rT"], "rd": x["rd"], "bits": x["b"], "offset": x["offset"]} for x in ref["cells"]]
+    Ko, Vo = torch.empty_like(c["Kd"]), torch.empty_like(c["Vd"])
+    jolt.reconstruct(blob, c["cfg"], picks, Ko, Vo)
+    torch.cuda.synchronize()
+    for x in ref["cells"]:
+        got = _cell_view(Ko if x["kv"] == 0 else Vo, x, c["groups"]).double().cpu().numpy()
+        want = _round(x["Xhat"], c["dt"])
+        rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+        assert rel <= 1e-3, (x["seq"], x["group"], x["kv"], rel)
+        # elementwise: all but a sliver within one rounding step of the dtype
+        close = np.abs(got - want) <= ULP_TOL[c["dt"]] * np.abs(want) + 1e-6 * np.abs(want).max()
+        assert close.mean() >= 0.999, close.mean()
+
+
+# ------------------------------------------------------------------------------ residual codes
+@pytest.mark.parametrize("name", ["tiny_f32_exact", "f16_exact_ragged", "f16_flash_d128", "bf16_flash"])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 8])
+def test_encode_codes_match_oracle_given_oracle_factors(name, b):
+    c = case(name)
+    Q = oracle.rotation(c["D"], 0)
+    for x in c["ref"]["cells"][:2]:
+        X = x["X"]
+        core = np.einsum("tr,ghtd,dk->ghrk", x["UT_fit"], X, x["Ud_fit"], optimize=True)
+        enc = oracle.encode_cell(X, x["UT_fit"], x["Ud_fit"], core, b, Q, c["dt"])
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[c["dt"]]
+        Xd = _cell_view(c["Kd"] if x["kv"] == 0 else c["Vd"], x, c["groups"]).contiguous()
+
+        def dev(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(torch.float64).to(tdt).cuda()
+
+        scales, codes = jolt.encode_residual(Xd, dev(enc["UT"]), dev(enc["core"]), dev(enc["Ud"]),
+                                             enc["UT"].shape[1], enc["Ud"].shape[1], b)
+        torch.cuda.synchronize()
+        u_gpu = oracle.unpack_rows(codes.cpu().numpy(), b, c["D"]).astype(int)
+        u_ref = enc["u"].astype(int)
+        same = np.mean(u_gpu == u_ref)
+        assert same >= 0.999, same
+        assert np.abs(u_gpu - u_ref).max() <= 1
+        s_ref = enc["scales"].astype(np.float64)
+        assert np.abs(scales.cpu().numpy() - s_ref).max() <= 1e-4 * s_ref.max() + 1e-30
+
+
+# ------------------------------------------------------------------------------ allocation
+@pytest.mark.parametrize("name", list(CASES))
+def test_allocation_bit_exact_on_oracle_spectra(name):
+    c = case(name)
+    ref = c["ref"]
+    cells = ref["cells"]
+    G = c["G"]
+    shapes = [(G, c["cfg"].desc.n_heads, c["T"], c["D"])] * len(cells)
+    for C in (c["p"]["target_ratio"], 1.7, 5.5):
+        budget = ref["dense_bytes"] / C
+        tabs = [oracle.cell_table(oracle.CellShape(*s), oracle.DTYPE_BYTES[c["dt"]], x["specT"], x["specD"],
+                                  x["norm2"], c["rT"], c["rd"], sorted(set(c["bits"]) | {0}), c["p"]["eps2"])
+                for s, x in zip(shapes, cells)]
+        want = oracle.allocate(tabs, budget)
+        st, picks, lam = jolt.allocate(shapes, oracle.DTYPE_BYTES[c["dt"]], [x["specT"] for x in cells],
+                                       [x["specD"] for x in cells], [x["norm2"] for x in cells], c["rT"], c["rd"],
+                                       c["bits"], budget, eps2=c["p"]["eps2"])
+        if want["status"] != 0:
+            assert st == -2
+            continue
+        assert st == 0
+        assert lam == want["lam"]
+        for t, i, q in zip(tabs, want["picks"], picks):
+            assert (q["rT"], q["rd"], q["bits"]) == (int(t["rT"][i]), int(t["rd"][i]), int(t["b"][i]))
+            assert q["err_pred"] == float(t["e"][i])
+            assert q["bytes"] == int(t["s"][i])
+
+
+def test_allocation_infeasible_budget_is_reported():
+    c = case("tiny_f32_exact")
+    cells = c["ref"]["cells"]
+    shapes = [(1, 2, 128, 64)] * 2
+    st, _, _ = jolt.allocate(shapes, 4, [x["specT"] for x in cells], [x["specD"] for x in cells],
+                             [x["norm2"] for x in cells], c["rT"], c["rd"], c["bits"], 100.0, eps2=c["p"]["eps2"])
+    assert st == -2
+
+
+# ------------------------------------------------------------------------------ spectra
+@pytest.mark.parametrize("name", list(CASES))
+def test_spectra_and_token_subspaces_match_oracle(name):
+    c = case(name)
+    ref = c["ref"]
+    nvec = min(c["rT"][-1], 32)
+    sT, sD, n2, UT = jolt.spectra(c["Kd"], c["Vd"], c["cfg"], n_vec=nvec)
+    torch.cuda.synchronize()
+    sT, sD, n2, UT = sT.cpu().numpy(), sD.cpu().numpy(), n2.cpu().numpy(), UT.double().cpu().numpy()
+    for i, x in enumerate(ref["cells"]):
+        N2 = x["norm2"]
+        assert abs(n2[i] - N2) <= 1e-6 * N2
+        assert np.abs(sD[i] - x["specD"]).max() <= 1e-5 * N2
+        assert np.abs(sT[i] - x["specT"]).max() <= 1e-5 * N2
+        # spectrum of a flash cell sums to ||X||^2 (tail entry)
+        if c["p"]["mode"] == "flash":
+            assert abs(sT[i].sum() - n2[i]) <= 1e-9 * n2[i]
+        Uo = x["U"]
+        s2 = x["specT"]
+        for r in (8, 16, min(nvec, len(s2) - 2)):
+            gap = (s2[r - 1] - s2[r]) / s2[0]
+            if gap < 1e-3:
+                continue  # subspace not well determined at this rank (reported by the gap)
+            Ug = UT[i, :r].T
+            Pg, Po = Ug @ Ug.T, Uo[:, :r] @ Uo[:, :r].T
+            assert np.linalg.norm(Pg - Po, 2) <= 1e-3, (i, r, gap)
+
+
+# ------------------------------------------------------------------------------ end to end
+@pytest.mark.parametrize("name", list(CASES))
+def test_compress_end_to_end_matches_oracle(name):
+    c = case(name)
+    ref = c["ref"]
+    blob, picks, lam = jolt.compress(c["Kd"], c["Vd"], c["cfg"])
+    Ko, Vo = torch.empty_like(c["Kd"]), torch.empty_like(c["Vd"])
+    jolt.reconstruct(blob, c["cfg"], picks, Ko, Vo)
+    torch.cuda.synchronize()
+    S = sum(p["bytes"] for p in picks)
+    assert S <= ref["budget"]
+    same_picks = [(p["rT"], p["rd"], p["bits"]) for p in picks] == [(x["rT"], x["rd"], x["b"]) for x in ref["cells"]]
+    assert same_picks, ([(p["rT"], p["rd"], p["bits"]) for p in picks], [(x["rT"], x["rd"], x["b"]) for x in ref["cells"]])
+    # lambda is the first bisection midpoint that lands in [0.995 B, B]; spectra that agree to
+    # fp32 rounding can accept a neighbouring midpoint, so check the multiplier's meaning instead:
+    # the oracle's own tables, minimised at the GPU's lambda, give the same picks
+    _check_lambda_consistent(c, lam, picks)
+    for x in ref["cells"]:
+        got = _cell_view(Ko if x["kv"] == 0 else Vo, x, c["groups"]).double().cpu().numpy()
+        X = x["X"]
+        err = np.linalg.norm(got - X) / np.linalg.norm(X)
+        # the dtype rounding of the dense output adds in quadrature
+        floor = {"f16": 3e-4, "bf16": 2.5e-3, "f32": 1e-6}[c["dt"]]
+        assert abs(err - x["rel_err"]) <= 1e-3 + 0.02 * x["rel_err"] + floor, (err, x["rel_err"])
+        want = _round(x["Xhat"], c["dt"])
+        assert np.linalg.norm(got - want) / np.linalg.norm(want) <= 1e-3 + floor
+
+
+def _check_lambda_consistent(c, lam, picks):
+    ref = c["ref"]
+    G = c["G"]
+    for x, q in zip(ref["cells"], picks):
+        sh = oracle.CellShape(G, c["cfg"].desc.n_heads, c["T"], c["D"])
+        t = oracle.cell_table(sh, oracle.DTYPE_BYTES[c["dt"]], x["specT"], x["specD"], x["norm2"], c["rT"], c["rd"],
+                              sorted(set(c["bits"]) | {0}), c["p"]["eps2"])
+        i = oracle.argmin_cell(t, lam)
+        assert (int(t["rT"][i]), int(t["rd"][i]), int(t["b"][i])) == (q["rT"], q["rd"], q["bits"])
+
+
+def test_compress_is_deterministic():
+    c = case("f16_flash_d128")
+    b1, p1, l1 = jolt.compress(c["Kd"], c["Vd"], c["cfg"])
+    b2, p2, l2 = jolt.compress(c["Kd"], c["Vd"], c["cfg"])
+    torch.cuda.synchronize()
+    n = sum(p["section_bytes"] for p in p1)
+    assert p1 == p2 and l1 == l2
+    assert torch.equal(b1[:n], b2[:n])
+
+
+# ------------------------------------------------------------------------------ error paths
+def test_nonfinite_input_is_reported():
+    c = case("f16_flash_two_seqs")
+    K = c["Kd"].clone()
+    K[0, 0, 0, 0, 0] = float("nan")
+    with pytest.raises(jolt.JoltError) as e:
+        jolt.compress(K, c["Vd"], c["cfg"])
+    assert e.value.status == -5
+
+
+def test_small_output_and_workspace_are_reported():
+    c = case("f16_flash_two_seqs")
+    out = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(jolt.JoltError) as e:
+        jolt.compress(c["Kd"], c["Vd"], c["cfg"], out=out)
+    assert e.value.status == -6
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    with pytest.raises(jolt.JoltError) as e:
+        jolt.compress(c["Kd"], c["Vd"], c["cfg"], ws=ws)
+    assert e.value.status == -3
