@@ -157,6 +157,11 @@ __global__ void headers_kernel(const FactorCell *cells, int ncells) {
   const int cell = blockIdx.x;
   if (cell >= ncells) return;
   const FactorCell c = cells[cell];
+  // zero the alignment padding after every part of the section (at most 255 bytes each)
+  for (int r = 0; r < 5; ++r) {
+    uint8_t *p = (uint8_t *)c.pad_ptr[r];
+    for (int i = threadIdx.x; i < c.pad_len[r]; i += blockDim.x) p[i] = 0;
+  }
   if (threadIdx.x < 64) {
     uint32_t *h = (uint32_t *)c.header;
     h[threadIdx.x] = threadIdx.x < 10 ? c.hdr[threadIdx.x] : 0u;  // 256-byte header

@@ -51,13 +51,7 @@ def test_mistral7b_shape_flash_full_size(C):
     Kd, Vd = K.cuda(), V.cuda()
     blob, picks, lam, Ko, Vo = _run(Kd, Vd, cfg, groups)
     assert [(q["rT"], q["rd"], q["bits"]) for q in picks] == [(x["rT"], x["rd"], x["b"]) for x in ref["cells"]]
-    # the multiplier: the oracle's tables minimised at the GPU's lambda give the same picks
-    eps = p["eps2"]
-    for x, q in zip(ref["cells"], picks):
-        t = oracle.cell_table(oracle.CellShape(4, H, T, D), 2, x["specT"], x["specD"], x["norm2"], rT, rd,
-                              sorted(set(bits) | {0}), eps)
-        i = oracle.argmin_cell(t, lam)
-        assert (int(t["rT"][i]), int(t["rd"][i]), int(t["b"][i])) == (q["rT"], q["rd"], q["bits"])
+    assert abs(lam - ref["lam"]) <= 1e-2 * ref["lam"]
     assert sum(q["bytes"] for q in picks) <= ref["budget"]
     for x in ref["cells"]:
         src = Ko if x["kv"] == 0 else Vo

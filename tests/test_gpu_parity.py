@@ -198,10 +198,9 @@ def test_compress_end_to_end_matches_oracle(name):
     assert S <= ref["budget"]
     same_picks = [(p["rT"], p["rd"], p["bits"]) for p in picks] == [(x["rT"], x["rd"], x["b"]) for x in ref["cells"]]
     assert same_picks, ([(p["rT"], p["rd"], p["bits"]) for p in picks], [(x["rT"], x["rd"], x["b"]) for x in ref["cells"]])
-    # lambda is the first bisection midpoint that lands in [0.995 B, B]; spectra that agree to
-    # fp32 rounding can accept a neighbouring midpoint, so check the multiplier's meaning instead:
-    # the oracle's own tables, minimised at the GPU's lambda, give the same picks
-    _check_lambda_consistent(c, lam, picks)
+    # lambda is the first bisection midpoint that lands in [0.995 B, B]; spectra that agree to fp32
+    # rounding may accept a neighbouring midpoint, so lambda is compared loosely and the picks exactly
+    assert abs(lam - ref["lam"]) <= 1e-2 * ref["lam"]
     for x in ref["cells"]:
         got = _cell_view(Ko if x["kv"] == 0 else Vo, x, c["groups"]).double().cpu().numpy()
         X = x["X"]
@@ -211,17 +210,6 @@ def test_compress_end_to_end_matches_oracle(name):
         assert abs(err - x["rel_err"]) <= 1e-3 + 0.02 * x["rel_err"] + floor, (err, x["rel_err"])
         want = _round(x["Xhat"], c["dt"])
         assert np.linalg.norm(got - want) / np.linalg.norm(want) <= 1e-3 + floor
-
-
-def _check_lambda_consistent(c, lam, picks):
-    ref = c["ref"]
-    G = c["G"]
-    for x, q in zip(ref["cells"], picks):
-        sh = oracle.CellShape(G, c["cfg"].desc.n_heads, c["T"], c["D"])
-        t = oracle.cell_table(sh, oracle.DTYPE_BYTES[c["dt"]], x["specT"], x["specD"], x["norm2"], c["rT"], c["rd"],
-                              sorted(set(c["bits"]) | {0}), c["p"]["eps2"])
-        i = oracle.argmin_cell(t, lam)
-        assert (int(t["rT"][i]), int(t["rd"][i]), int(t["b"][i])) == (q["rT"], q["rd"], q["bits"])
 
 
 def test_compress_is_deterministic():
