@@ -19,24 +19,44 @@ namespace {
 
 using namespace core;
 
-template <int MF>
-__device__ __forceinline__ void mma_step(const uint16_t *As, int pa_n, const uint16_t *Bs, int pb_n, int maxo,
-                                         int wm, int wn, int lane, f32x4 (&acc)[4][4]) {
+template <int MF, int PA, int PB, int MAXO>
+__device__ __forceinline__ void mma_step(const uint16_t *As, const uint16_t *Bs, int wm, int wn, int lane,
+                                         f32x4 (&acc)[4][4]) {
   const int fr = lane & 15, fk = (lane >> 4) * 8;
-  uint4 af[3][4], bf[3][4];
-  for (int p = 0; p < pa_n; ++p)
+  uint4 af[PA][4], bf[PB][4];
+#pragma unroll
+  for (int p = 0; p < PA; ++p)
 #pragma unroll
     for (int i = 0; i < 4; ++i) af[p][i] = *(const uint4 *)(As + p * BM * LDK + (wm * 64 + i * 16 + fr) * LDK + fk);
-  for (int p = 0; p < pb_n; ++p)
+#pragma unroll
+  for (int p = 0; p < PB; ++p)
 #pragma unroll
     for (int j = 0; j < 4; ++j) bf[p][j] = *(const uint4 *)(Bs + p * BN * LDK + (wn * 64 + j * 16 + fr) * LDK + fk);
-  for (int pa = pa_n - 1; pa >= 0; --pa)
-    for (int pb = pb_n - 1; pb >= 0; --pb)
-      if (pa + pb <= maxo)
+#pragma unroll
+  for (int pa = PA - 1; pa >= 0; --pa)
+#pragma unroll
+    for (int pb = PB - 1; pb >= 0; --pb)
+      if (pa + pb <= MAXO)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = mfma<MF>(af[pa][i], bf[pb][j], acc[i][j]);
+}
+
+// Store a raw 8-vector into an LDS tile along k (row r, column k), splitting into planes.
+template <int S, int MF, int P, int NB16>
+__device__ __forceinline__ void put8(uint16_t *tile, int rows, int r, int k, const Raw8<S> &x, float scale) {
+  if constexpr (S != SRC_F32 && ((S == SRC_F16 && MF == MF_F16) || (S == SRC_BF16 && MF == MF_BF16))) {
+    *(uint4 *)(tile + r * LDK + k) = x.v;
+  } else {
+    uint16_t pl[8][3];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (S == SRC_F32 && MF == MF_F16 && NB16 == 3) split3_f16(raw_elem<S>(x, i), scale, pl[i]);
+      else split_planes<S, MF>(raw_elem<S>(x, i), scale, pl[i]);
+    }
+    lds_store8<P, true>(tile, rows, r, k, pl);
+  }
 }
 
 // 16-bit plane count of a source under the MFMA type; for fp32 with f16 MFMA the B operand of
@@ -58,10 +78,11 @@ __global__ void __launch_bounds__(NT) encode_kernel(const EncCell *cells, int T,
   constexpr int PA = CPlanes<SX, MF, NB16>::n;
   constexpr int PB = CPlanes<SRC_F32, MF, NB16>::n;
   constexpr int MAXO = (MF == MF_F16) ? (NB16 - 1) : 2;
-  __shared__ __attribute__((aligned(16))) uint16_t As[PA * BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[PB * BN * LDK];
+  constexpr int ASZ = PA * BM * LDK, BSZ = PB * BN * LDK, STG = ASZ + BSZ;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STG];
   __shared__ float smax[2][BM];
-  __shared__ uint8_t ucode[BM * 128];
+  uint8_t *ucode = (uint8_t *)lds;  // [BM][128] codes, reuses the tiles after the main loop
+  static_assert(2 * STG * 2 >= BM * 128, "code staging must fit in the tile buffers");
 
   const EncCell c = cells[blockIdx.z];
   const int j = blockIdx.x / ttiles, tt = blockIdx.x % ttiles;
@@ -80,7 +101,8 @@ __global__ void __launch_bounds__(NT) encode_kernel(const EncCell *cells, int T,
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float ra[2][8], rb[2][8];
+  Raw8<SX> ra[2];
+  Raw8<SRC_F32> rb[2];
   auto gload = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -88,38 +110,32 @@ __global__ void __launch_bounds__(NT) encode_kernel(const EncCell *cells, int T,
       int r = v >> 2, kv = (v & 3) * 8;
       int t = t0 + r;
       int k = k0 + kv;
-      if (k < D) load8<SX>(c.X, xoff + (long long)t * D, k, D, t < T, 1 << 30, 0, ra[it]);
-      else load8<SX>(c.UT, (long long)t * c.rT, k - D, c.rT, t < T, 1 << 30, 0, ra[it]);
-      load8<SRC_F32>(Bj, (long long)r * c.Kb, k0 + kv, K, r < D, 1 << 30, 0, rb[it]);
+      if (k < D) load_raw8<SX>(c.X, xoff + (long long)t * D, k, D, t < T, 1 << 30, 0, ra[it]);
+      else load_raw8<SX>(c.UT, (long long)t * c.rT, k - D, c.rT, t < T, 1 << 30, 0, ra[it]);
+      load_raw8<SRC_F32>(Bj, (long long)r * c.Kb, k0 + kv, K, r < D, 1 << 30, 0, rb[it]);
     }
   };
-  auto lstore = [&](int) {
+  auto lstore = [&](int buf) {
+    uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       int v = tid + it * NT;
-      uint16_t pa[8][3], pb[8][3];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        split_planes<SX, MF>(ra[it][i], 1.f, pa[i]);
-        csplit<SRC_F32, MF, NB16>(rb[it][i], bscale, pb[i]);
-      }
-      lds_store8<PA, true>(As, BM, v >> 2, (v & 3) * 8, pa);
-      lds_store8<PB, true>(Bs, BN, v >> 2, (v & 3) * 8, pb);
+      put8<SX, MF, PA, NB16>(As, BM, v >> 2, (v & 3) * 8, ra[it], 1.f);
+      put8<SRC_F32, MF, PB, NB16>(Bs, BN, v >> 2, (v & 3) * 8, rb[it], bscale);
     }
   };
 
   gload(0);
   lstore(0);
   __syncthreads();
+  int buf = 0;
   for (int k0 = 0; k0 < K; k0 += BK) {
     const bool more = k0 + BK < K;
     if (more) gload(k0 + BK);
-    mma_step<MF>(As, PA, Bs, PB, MAXO, wm, wn, lane, acc);
+    mma_step<MF, PA, PB, MAXO>(lds + buf * STG, lds + buf * STG + ASZ, wm, wn, lane, acc);
+    if (more) lstore(buf ^ 1);
     __syncthreads();
-    if (more) {
-      lstore(k0 + BK);
-      __syncthreads();
-    }
+    buf ^= 1;
   }
 
   // ---- quantisation epilogue -------------------------------------------------------------
@@ -212,10 +228,10 @@ template <int MF, int SX, int NB16>
 __global__ void __launch_bounds__(NT) decode_kernel(const DecCell *cells, int T, int D, int ttiles) {
   constexpr int PA = CPlanes<SX, MF, NB16>::n;  // U_T part; the codes part uses one plane
   constexpr int PB = CPlanes<SRC_F32, MF, NB16>::n;
-  constexpr int MAXO_U = (MF == MF_F16) ? (NB16 - 1) : 2;
-  constexpr int MAXO_C = (MF == MF_F16) ? (NB16 - 1) : 2;
-  __shared__ __attribute__((aligned(16))) uint16_t As[PA * BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[PB * BN * LDK];
+  constexpr int MAXO = (MF == MF_F16) ? (NB16 - 1) : 2;
+  constexpr int ASZ = PA * BM * LDK, BSZ = PB * BN * LDK, STG = ASZ + BSZ;
+  constexpr int SC = (MF == MF_F16) ? SRC_F16 : SRC_BF16;  // small integer codes are exact
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STG];
   __shared__ float srow[BM];
 
   const DecCell c = cells[blockIdx.z];
@@ -236,105 +252,96 @@ __global__ void __launch_bounds__(NT) decode_kernel(const DecCell *cells, int T,
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float ra[2][8], rb[2][8];
   // ---- phase 1: codes Q^T, then scale rows ---------------------------------------------------
   if (b > 0) {
+    float ca[2][8];
+    Raw8<SRC_F32> rb[2];
     auto gload = [&](int k0) {
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         int v = tid + it * NT;
         int r = v >> 2, kv = (v & 3) * 8;
         int t = t0 + r;
-        if (t < T) unpack8(c.codes + ((long long)j * T + t) * rowbytes, k0 + kv, b, ra[it]);
+        if (t < T) unpack8(c.codes + ((long long)j * T + t) * rowbytes, k0 + kv, b, ca[it]);
         else
 #pragma unroll
-          for (int i = 0; i < 8; ++i) ra[it][i] = 0.f;
-        load8<SRC_F32>(c.Q, (long long)r * D, k0 + kv, D, r < D, 1 << 30, 0, rb[it]);
+          for (int i = 0; i < 8; ++i) ca[it][i] = 0.f;
+        load_raw8<SRC_F32>(c.Q, (long long)r * D, k0 + kv, D, r < D, 1 << 30, 0, rb[it]);
       }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int buf) {
+      uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         int v = tid + it * NT;
-        uint16_t pa[8][3], pb[8][3];
+        uint16_t pa[8][3];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          split_planes<(MF == MF_F16 ? SRC_F16 : SRC_BF16), MF>(ra[it][i], 1.f, pa[i]);  // small integers: exact
-          csplit<SRC_F32, MF, NB16>(rb[it][i], qscale, pb[i]);
-        }
+        for (int i = 0; i < 8; ++i) split_planes<SC, MF>(ca[it][i], 1.f, pa[i]);
         lds_store8<1, true>(As, BM, v >> 2, (v & 3) * 8, pa);
-        lds_store8<PB, true>(Bs, BN, v >> 2, (v & 3) * 8, pb);
+        put8<SRC_F32, MF, PB, NB16>(Bs, BN, v >> 2, (v & 3) * 8, rb[it], qscale);
       }
     };
     gload(0);
-    lstore();
+    lstore(0);
     __syncthreads();
+    int buf = 0;
     for (int k0 = 0; k0 < D; k0 += BK) {
       const bool more = k0 + BK < D;
       if (more) gload(k0 + BK);
-      mma_step<MF>(As, 1, Bs, PB, MAXO_C, wm, wn, lane, acc);
+      mma_step<MF, 1, PB, MAXO>(lds + buf * STG, lds + buf * STG + ASZ, wm, wn, lane, acc);
+      if (more) lstore(buf ^ 1);
       __syncthreads();
-      if (more) {
-        lstore();
-        __syncthreads();
-      }
+      buf ^= 1;
     }
     for (int rr = tid; rr < BM; rr += NT) srow[rr] = (t0 + rr < T) ? c.scales[(long long)j * T + t0 + rr] : 0.f;
     __syncthreads();
-    const float inv = 1.f / qscale;
+    // rows scaled by s and moved into the dscale frame of phase 2
+    const float f = dscale / qscale;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float s = srow[wm * 64 + i * 16 + (lane >> 4) * 4 + r] * inv;
+        const float sr = srow[wm * 64 + i * 16 + (lane >> 4) * 4 + r] * f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[i][q][r] *= s;
+        for (int q = 0; q < 4; ++q) acc[i][q][r] *= sr;
       }
   }
   // ---- phase 2: + U_T D_j ------------------------------------------------------------------
   {
-    // rescale the running accumulator into the (dscale-scaled) frame of phase 2
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[i][q] *= dscale;
     const float *Dj = c.Dm + (long long)j * D * c.Kd;
+    Raw8<SX> ra[2];
+    Raw8<SRC_F32> rb[2];
     auto gload = [&](int k0) {
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         int v = tid + it * NT;
         int r = v >> 2, kv = (v & 3) * 8;
         int t = t0 + r;
-        load8<SX>(c.UT, (long long)t * c.rT, k0 + kv, c.rT, t < T, 1 << 30, 0, ra[it]);
-        load8<SRC_F32>(Dj, (long long)r * c.Kd, k0 + kv, c.rT, r < D, 1 << 30, 0, rb[it]);
+        load_raw8<SX>(c.UT, (long long)t * c.rT, k0 + kv, c.rT, t < T, 1 << 30, 0, ra[it]);
+        load_raw8<SRC_F32>(Dj, (long long)r * c.Kd, k0 + kv, c.rT, r < D, 1 << 30, 0, rb[it]);
       }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int buf) {
+      uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         int v = tid + it * NT;
-        uint16_t pa[8][3], pb[8][3];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          split_planes<SX, MF>(ra[it][i], 1.f, pa[i]);
-          csplit<SRC_F32, MF, NB16>(rb[it][i], dscale, pb[i]);
-        }
-        lds_store8<PA, true>(As, BM, v >> 2, (v & 3) * 8, pa);
-        lds_store8<PB, true>(Bs, BN, v >> 2, (v & 3) * 8, pb);
+        put8<SX, MF, PA, NB16>(As, BM, v >> 2, (v & 3) * 8, ra[it], 1.f);
+        put8<SRC_F32, MF, PB, NB16>(Bs, BN, v >> 2, (v & 3) * 8, rb[it], dscale);
       }
     };
-    gload(0);
-    lstore();
     __syncthreads();
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    int buf = 0;
     for (int k0 = 0; k0 < c.rT; k0 += BK) {
       const bool more = k0 + BK < c.rT;
       if (more) gload(k0 + BK);
-      mma_step<MF>(As, PA, Bs, PB, MAXO_U, wm, wn, lane, acc);
+      mma_step<MF, PA, PB, MAXO>(lds + buf * STG, lds + buf * STG + ASZ, wm, wn, lane, acc);
+      if (more) lstore(buf ^ 1);
       __syncthreads();
-      if (more) {
-        lstore();
-        __syncthreads();
-      }
+      buf ^= 1;
     }
   }
   const float inv = 1.f / dscale;

@@ -97,12 +97,20 @@ __global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long
     }
     __syncthreads();
     if (bet == 0.0) continue;
-    // p = beta * A22 v  (A22 symmetric: read column-wise for coalescing)
+    // p = beta * A22 v: one wave per row, lanes along the (contiguous) row
     double *A22 = W + (long long)(k + 1) * ldw + (k + 1);
-    for (int i = tid; i < m; i += nt) {
-      double s = 0.0;
-      for (int j = 0; j < m; ++j) s += A22[(long long)j * ldw + i] * vbuf[j];
-      pbuf[i] = bet * s;
+    const int lane = tid & 63, wv = tid >> 6, nwv = nt >> 6;
+    for (int i = wv; i < m; i += nwv) {
+      const double *ri = A22 + (long long)i * ldw;
+      double s0 = 0.0, s1 = 0.0;
+      int jj = lane;
+      for (; jj + 64 < m; jj += 128) {
+        s0 += ri[jj] * vbuf[jj];
+        s1 += ri[jj + 64] * vbuf[jj + 64];
+      }
+      if (jj < m) s0 += ri[jj] * vbuf[jj];
+      const double sr = warp_sum_d(s0 + s1);
+      if (lane == 0) pbuf[i] = bet * sr;
     }
     __syncthreads();
     part = 0.0;
@@ -111,9 +119,11 @@ __global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long
     const double c = 0.5 * bet * pv;
     for (int i = tid; i < m; i += nt) pbuf[i] -= c * vbuf[i];  // w
     __syncthreads();
-    for (long long idx = tid; idx < (long long)m * m; idx += nt) {
-      int i = (int)(idx / m), j = (int)(idx % m);
-      A22[(long long)i * ldw + j] -= vbuf[i] * pbuf[j] + pbuf[i] * vbuf[j];
+    // A22 -= v w^T + w v^T: one wave per row
+    for (int i = wv; i < m; i += nwv) {
+      double *ri = A22 + (long long)i * ldw;
+      const double vi = vbuf[i], wi = pbuf[i];
+      for (int jj = lane; jj < m; jj += 64) ri[jj] -= vi * pbuf[jj] + wi * vbuf[jj];
     }
     __syncthreads();
   }
@@ -505,7 +515,6 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
   // X[i0+r][c] = -sum_q Dinv[r][q] S[q][c],  S[q][c] = sum_{k = i0+ib}^{c} R[i0+q][k] X[k][c]
   // Work split: each wave owns 64 consecutive columns (one per lane) and 8 rows q of S.
   const int nblk = (n + CNB - 1) / CNB;
-  double *S = P;  // reuse the panel buffer for S when it fits, else X's rows are read from global
   for (int bi = nblk - 1; bi >= 0; --bi) {
     const int i0 = bi * CNB, ib = min(CNB, n - i0), rest = n - i0 - ib;
     // inverse of the diagonal block (upper) into Dk, from an LDS copy Rd of the block
@@ -528,31 +537,72 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
       X[(long long)(i0 + r) * n + i0 + c] = Dk[r * 33 + c];
     }
     if (rest > 0) {
+      // R's block row right of the diagonal block into LDS
+      for (int idx = tid; idx < ib * rest; idx += nt) {
+        const int r = idx / rest, cc = idx % rest;
+        P[r * rest + cc] = A[(long long)(i0 + r) * n + i0 + ib + cc];
+      }
+      __syncthreads();
+      // S[q][c] = sum_k R[i0+q][k] X[k][c] (X upper triangular and zero below, so k runs to the
+      // wave's last column), stored in place in X's rows i0.. (not yet final, not read here)
       const int cgroups = (rest + 63) / 64, ngroups = cgroups * 4;  // (column group, 8-row group)
       for (int gi = wave; gi < ngroups; gi += nwave) {
         const int cg = gi >> 2, rg = gi & 3;
         const int cc = cg * 64 + lane, c = i0 + ib + cc;
+        const int kend = min(n, i0 + ib + cg * 64 + 64);
         double acc[8] = {};
-        if (cc < rest) {
-          for (int k = i0 + ib; k <= c; ++k) {
-            const double xk = X[(long long)k * n + c];
+        const bool live = cc < rest;
+        int k = i0 + ib;
+        for (; k + 4 <= kend; k += 4) {
+          double x0 = live ? X[(long long)k * n + c] : 0.0;
+          double x1 = live ? X[(long long)(k + 1) * n + c] : 0.0;
+          double x2 = live ? X[(long long)(k + 2) * n + c] : 0.0;
+          double x3 = live ? X[(long long)(k + 3) * n + c] : 0.0;
+          const int kk = k - i0 - ib;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              const int r = rg * 8 + q;
-              acc[q] += ((r < ib) ? A[(long long)(i0 + r) * n + k] : 0.0) * xk;
+          for (int q = 0; q < 8; ++q) {
+            const int r = rg * 8 + q;
+            if (r < ib) {
+              const double *pr = P + r * rest + kk;
+              acc[q] += pr[0] * x0 + pr[1] * x1 + pr[2] * x2 + pr[3] * x3;
             }
           }
         }
-        if (in_lds && cc < rest)
+        for (; k < kend; ++k) {
+          const double x0 = live ? X[(long long)k * n + c] : 0.0;
+          const int kk = k - i0 - ib;
 #pragma unroll
-          for (int q = 0; q < 8; ++q) S[(rg * 8 + q) * rest + cc] = acc[q];
+          for (int q = 0; q < 8; ++q) {
+            const int r = rg * 8 + q;
+            if (r < ib) acc[q] += P[r * rest + kk] * x0;
+          }
+        }
+        if (live)
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (rg * 8 + q < ib) X[(long long)(i0 + rg * 8 + q) * n + c] = acc[q];
       }
       __syncthreads();
-      for (int idx = tid; idx < ib * rest && in_lds; idx += nt) {
+      // X[i0+r][c] = -sum_{q >= r} Dinv[r][q] S[q][c]: waves own (64 columns, 8 rows r); the
+      // result goes to the LDS panel (free now), then back over S once every wave has read it
+      for (int gi = wave; gi < ngroups; gi += nwave) {
+        const int cg = gi >> 2, rg = gi & 3;
+        const int cc = cg * 64 + lane, c = i0 + ib + cc;
+        if (rg * 8 >= ib || cc >= rest) continue;
+        double acc[8] = {};
+        for (int q = rg * 8; q < ib; ++q) {
+          const double sq = X[(long long)(i0 + q) * n + c];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[t] -= Dk[(rg * 8 + t) * 33 + q] * sq;  // Dinv upper: 0 for q < r
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (rg * 8 + t < ib) P[(rg * 8 + t) * rest + cc] = acc[t];
+      }
+      __syncthreads();
+      for (int idx = tid; idx < ib * rest; idx += nt) {
         const int r = idx / rest, cc = idx % rest;
-        double v = 0.0;
-        for (int q = r; q < ib; ++q) v -= Dk[r * 33 + q] * S[q * rest + cc];
-        X[(long long)(i0 + r) * n + i0 + ib + cc] = v;
+        X[(long long)(i0 + r) * n + i0 + ib + cc] = P[r * rest + cc];
       }
     }
     __syncthreads();
