@@ -369,6 +369,7 @@ void gram_f32(const Plan &pl, Bufs &b, const float *X, long long ldx, long long 
   JOLT_REQUIRE((long long)batch * ns * rows * rl <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
   g.C = b.part; g.c_ld = rl; g.c_split = (long long)rows * rl; g.c_bs = (long long)ns * rows * rl;
   g.m_fastest = 1;
+  g.tri = 1;  // the Cholesky factorisation reads the upper triangle only
   gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, batch, ns, st);
   reduce_splits(b.part, g.c_bs, g.c_split, ns, 0, rows, rows, rl, out, true, out_bs, ldo, batch, st);
 }
@@ -460,6 +461,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       g.C2 = q.T; g.c2_ld = Tld; g.c2_bs = ell * Tld;
       g.c_amax = q.am;
       g.m_fastest = 0;
+      g.tri = 2;  // R^{-1} is upper triangular
       gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
       std::swap(y, q);
     }
@@ -484,6 +486,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       g.C = b.Z2; g.c_ld = ld; g.c_bs = Mf * ld;
       g.C2 = b.Zt; g.c2_ld = Mf; g.c2_bs = ell * Mf;
       g.c_amax = amZ;
+      g.tri = 2;
       gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
     }
     Pair Y = (Q.T == pa.T) ? pb : pa;
@@ -887,8 +890,8 @@ int32_t jolt_profile_read(char *h_names, int32_t names_bytes, double *h_ms, int3
       }
       ms[i] += t;
       cnt[i] += 1;
-      hipEventDestroy(r.a);
-      hipEventDestroy(r.b);
+      (void)hipEventDestroy(r.a);
+      (void)hipEventDestroy(r.b);
     }
     g_recs.clear();
     std::string joined;

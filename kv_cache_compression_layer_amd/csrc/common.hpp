@@ -126,11 +126,19 @@ struct GemmArgs {
   // optional second, transposed output: C2[n][m] (row pitch c2_ld, batch stride c2_bs)
   float *C2;
   long long c2_ld, c2_bs;
+  // structure flags: 1 = only tiles touching the upper triangle (m < n) are needed; the others
+  // are written as zeros without work; 2 = B(k, n) = 0 for k > n (an upper triangular factor),
+  // so each column tile stops its k loop at its last column (single split only)
+  int tri;
 };
 
 // a_kc: A contiguous along K (else along M); b_kc: B contiguous along K (else along N)
 void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int batch, int nsplit,
           hipStream_t st);
+
+// the same product for operands that are both contiguous along K (larger wave tiles); called by
+// gemm() after validation
+void gemm_kc(int mf, int sa, int sb, const GemmArgs &g, int batch, int nsplit, hipStream_t st);
 
 // sum of split-K partials in fixed order: out[b][i] = sum_s part[b][s][i] (fp64 accumulate)
 void reduce_splits(const float *part, long long part_bs, long long part_ss, int nsplit, long long n,

@@ -232,8 +232,15 @@ void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int b
                JOLT_EINVAL, "gemm: operands must be 16-byte aligned with strides in multiples of 8 elements");
   JOLT_REQUIRE(g.inner >= 1 && batch % g.inner == 0, JOLT_EINVAL, "gemm: bad inner batch");
   JOLT_REQUIRE(g.C2 == nullptr || ((uintptr_t)g.C2 % 16) == 0, JOLT_EINVAL, "gemm: C2 must be 16-byte aligned");
+  JOLT_REQUIRE(g.tri == 0 || (a_kc && b_kc), JOLT_EINVAL, "gemm: structure flags need K-contiguous operands");
+  JOLT_REQUIRE(!(g.tri & 2) || nsplit == 1, JOLT_EINVAL, "gemm: triangular B needs a single split");
+  JOLT_REQUIRE(!(g.tri & 1) || g.M == g.N, JOLT_EINVAL, "gemm: upper-triangle output needs a square product");
   GemmArgs h = g;
   if (nsplit == 1) h.k_chunk = ((g.K + BK - 1) / BK) * BK;
+  if (a_kc && b_kc) {
+    gemm_kc(mf, sa, sb, h, batch, nsplit, st);
+    return;
+  }
   if (mf == MF_F16) {
     if (sa == SRC_F16 && sb == SRC_F16) launch_layout<MF_F16, SRC_F16, SRC_F16>(a_kc, b_kc, h, batch, nsplit, st);
     else if (sa == SRC_F16 && sb == SRC_F32) launch_layout<MF_F16, SRC_F16, SRC_F32>(a_kc, b_kc, h, batch, nsplit, st);
