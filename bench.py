@@ -36,7 +36,24 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dtype", default="f16", choices=["f16", "bf16"])
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy():
+    """Three launches of torch's elementwise copy over 1 GiB: the byte counters of a profiler read
+    on this kernel give the scale between counter units and bytes moved."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
 def kernel_models(T, L, H, D, G, ell, picks, dtype_bytes):
@@ -126,6 +143,9 @@ def cpu_baseline(K, V, groups, cfgd, sample_T):
 
 def main():
     a = parse()
+    if a.calibrate_copy:
+        calibrate_copy()
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path shards by cell "
               f"across GPUs by design, but only the one-GPU kernel is built and measured)", file=sys.stderr)

@@ -9,10 +9,14 @@
 //   * 4 waves (2 x 2) per block; each wave owns TM x TN output subtiles of 16 x 16 (64 x 128 or
 //     128 x 64), so a wave reads 12 fragments from LDS for 32 MFMAs instead of 8 for 16;
 //   * LDS tiles are [row][32] without padding; the four 16-byte chunks of a row are XOR-permuted
-//     by the row index so that the 16 rows read by one fragment load fall in distinct banks,
-//     which keeps two blocks resident per CU even with two fp32 planes;
+//     by the row index so that fragment loads and tile stores are free of bank conflicts, which
+//     keeps two blocks resident per CU even with two fp32 planes;
+//   * the loop is specialised outside the k loop (every subtile live or not; aligned full
+//     stages with pointer-increment addressing or the general bounds-checked path);
 //   * subtiles entirely outside M or N skip their MFMAs (the ragged last tile of a 522-wide
 //     sketch dimension costs its loads, not its matrix-core time).
+#include <type_traits>
+
 #include "common.hpp"
 #include "gemm_core.hpp"
 
@@ -25,9 +29,13 @@ using namespace core;
 constexpr int KBK = 32;   // k per LDS stage (one MFMA depth)
 constexpr int KNT = 256;  // threads per block (4 waves, 2 x 2)
 
-// LDS element offset of chunk `chunk` (8 halves) of row `row` in a [rows][32] tile.
+// LDS element offset of chunk `chunk` (8 halves) of row `row` in a [rows][32] tile.  The chunk
+// permutation depends on row % 8 only (rows 2i and 2i + 1 share a 128-byte bank row, and the
+// four pairs of a fragment's eight rows get the four chunk rotations), which measures free of
+// LDS bank conflicts for both the fragment reads and the tile stores; every 16-row fragment of
+// a wave shares one pattern, so fragment addresses differ by compile-time constants.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * KBK + ((chunk ^ (row >> 1) ^ (row >> 3)) & 3) * 8;
+  return row * KBK + ((chunk ^ (row >> 1)) & 3) * 8;
 }
 
 // Store one raw 8-vector (8 consecutive k of one row) into every plane of an LDS tile.
@@ -51,8 +59,8 @@ __device__ __forceinline__ void put8(uint16_t *tile, int plane_elems, int off, c
   }
 }
 
-template <int MF, int SA, int SB, int TM, int TN>
-__global__ void __launch_bounds__(KNT) __attribute__((amdgpu_waves_per_eu(2, 2))) gemm_kc_kernel(GemmArgs g) {
+template <int MF, int SA, int SB, int TM, int TN, int W>
+__global__ void __launch_bounds__(KNT) __attribute__((amdgpu_waves_per_eu(W, W))) gemm_kc_kernel(GemmArgs g) {
   constexpr int PA = Planes<SA, MF>::n, PB = Planes<SB, MF>::n;
   constexpr int MAXO = (MF == MF_F16) ? 1 : 2;  // keep plane products with order i + j <= MAXO
   constexpr int WM = TM * 16, WN = TN * 16, BM = 2 * WM, BN = 2 * WN;
@@ -61,17 +69,23 @@ __global__ void __launch_bounds__(KNT) __attribute__((amdgpu_waves_per_eu(2, 2))
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int zb = blockIdx.z, split = blockIdx.y;
+  // XCD-aware remap over the whole grid: linear block L is dispatched to XCD L % 8, so give each
+  // XCD one contiguous range of (batch, split, tile) -- whole cells where the grid allows -- and
+  // every operand panel is streamed through one L2 instead of all eight.
+  int t, split, zb;
+  {
+    const long long gx = gridDim.x, gxy = gx * gridDim.y, total = gxy * gridDim.z;
+    long long L = blockIdx.x + gx * blockIdx.y + gxy * blockIdx.z;
+    const long long per = total / 8;
+    if (L < per * 8) L = (L % 8) * per + L / 8;
+    t = (int)(L % gx);
+    split = (int)((L / gx) % gridDim.y);
+    zb = (int)(L / gxy);
+  }
   const int inner = g.inner > 0 ? g.inner : 1;
   const int batch = zb / inner, bin = zb % inner;
-  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-  const int ntiles = tiles_m * tiles_n;
-  // XCD-aware remap: hardware block b runs on XCD b % 8; give each XCD a contiguous range.
-  int t = blockIdx.x;
-  {
-    const int per = ntiles / 8;
-    if (t < per * 8) t = (t % 8) * per + t / 8;
-  }
+  const int tiles_m = (g.M + BM - 1) / BM;
+  const int tiles_n = (g.N + BN - 1) / BN;
   int tm, tn;
   if (g.m_fastest) { tm = t % tiles_m; tn = t / tiles_m; }
   else { tn = t % tiles_n; tm = t / tiles_n; }
@@ -106,19 +120,84 @@ __global__ void __launch_bounds__(KNT) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   Raw8<SA> ra[LA];
   Raw8<SB> rb[LB];
-  auto gload = [&](int k0) {
+  // Load slots: thread v of a stage loads 8 consecutive k of row v / 4 at chunk v % 4.  Row
+  // pointers are fixed for the whole k loop (rows past the edge read row 0 and are zeroed); the
+  // k offset in blocked addressing, (k / blk) * blk_stride + k % blk, is advanced by the stage
+  // depth without divisions.  When blk is a multiple of 32 a stage never straddles a block, so a
+  // full stage needs no per-lane index arithmetic at all.
+  constexpr int ESA = (SA == SRC_F32) ? 4 : 2, ESB = (SB == SRC_F32) ? 4 : 2;
+  // (byte offsets of the rows within the batch fit 32 bits: checked by the host)
+  uint32_t pa[LA], pb[LB];
+  bool oka[LA], okb[LB];
+#pragma unroll
+  for (int it = 0; it < LA; ++it) {
+    const int v = tid + it * KNT, m = m0 + (v >> 2);
+    oka[it] = m < g.M;
+    pa[it] = (uint32_t)(((long long)(oka[it] ? m : 0) * g.a_ld + (v & 3) * 8) * ESA);
+  }
+#pragma unroll
+  for (int it = 0; it < LB; ++it) {
+    const int v = tid + it * KNT, n = n0 + (v >> 2);
+    okb[it] = n < g.N;
+    pb[it] = (uint32_t)(((long long)(okb[it] ? n : 0) * g.b_ld + (v & 3) * 8) * ESB);
+  }
+  const bool afast = (g.a_blk % KBK) == 0, bfast = (g.b_blk % KBK) == 0;
+  const int nsteps = (kend - kbeg + KBK - 1) / KBK;
+  const int nfast = (afast && bfast) ? (kend - kbeg) / KBK : 0;  // leading steps with fast loads
+  // fast path state: scalar base pointers of the current stage and the position inside the block
+  int ar = kbeg % g.a_blk, br = kbeg % g.b_blk;
+  const char *abase = Ab + ((long long)(kbeg / g.a_blk) * g.a_blk_stride + ar) * ESA;
+  const char *bbase = Bb + ((long long)(kbeg / g.b_blk) * g.b_blk_stride + br) * ESB;
+  auto gload_fast = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int it = 0; it < LA; ++it) {
-      const int v = tid + it * KNT, r = v >> 2, m = m0 + r;
+      if constexpr (SA == SRC_F32) {
+        const float4 *q = (const float4 *)(abase + pa[it]);
+        float4 x = q[0], y = q[1];
+        if (!oka[it]) x = y = make_float4(0.f, 0.f, 0.f, 0.f);
+        ra[it].a = x;
+        ra[it].b = y;
+      } else {
+        uint4 x = *(const uint4 *)(abase + pa[it]);
+        if (!oka[it]) x = make_uint4(0u, 0u, 0u, 0u);
+        ra[it].v = x;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < LB; ++it) {
+      if constexpr (SB == SRC_F32) {
+        const float4 *q = (const float4 *)(bbase + pb[it]);
+        float4 x = q[0], y = q[1];
+        if (!okb[it]) x = y = make_float4(0.f, 0.f, 0.f, 0.f);
+        rb[it].a = x;
+        rb[it].b = y;
+      } else {
+        uint4 x = *(const uint4 *)(bbase + pb[it]);
+        if (!okb[it]) x = make_uint4(0u, 0u, 0u, 0u);
+        rb[it].v = x;
+      }
+    }
+    // next stage: a block of blocked addressing ends exactly on a stage boundary
+    ar += KBK;
+    abase += KBK * ESA;
+    if (ar == g.a_blk) { ar = 0; abase += (g.a_blk_stride - g.a_blk) * ESA; }
+    br += KBK;
+    bbase += KBK * ESB;
+    if (br == g.b_blk) { br = 0; bbase += (g.b_blk_stride - g.b_blk) * ESB; }
+  };
+  auto gload_slow = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < LA; ++it) {
+      const int v = tid + it * KNT, m = m0 + (v >> 2);
       load_raw8<SA>(Ab, (long long)m * g.a_ld, k0 + (v & 3) * 8, kend, m < g.M, g.a_blk, g.a_blk_stride, ra[it]);
     }
 #pragma unroll
     for (int it = 0; it < LB; ++it) {
-      const int v = tid + it * KNT, r = v >> 2, n = n0 + r;
+      const int v = tid + it * KNT, n = n0 + (v >> 2);
       load_raw8<SB>(Bb, (long long)n * g.b_ld, k0 + (v & 3) * 8, kend, n < g.N, g.b_blk, g.b_blk_stride, rb[it]);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
     uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
 #pragma unroll
     for (int it = 0; it < LA; ++it) {
@@ -132,52 +211,62 @@ __global__ void __launch_bounds__(KNT) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   };
 
-  int aoff[TM], boff[TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) aoff[i] = swz(wm * WM + i * 16 + fr, fc);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) boff[j] = swz(wn * WN + j * 16 + fr, fc);
+  // fragment i of the wave's A rows sits at aoff + i * 16 rows (same chunk pattern); likewise B
+  const int aoff = swz(wm * WM + fr, fc), boff = swz(wn * WN + fr, fc);
 
-  if (kbeg < kend) {
-    gload(kbeg);
+  // one 32-deep step from LDS buffer `buf`; FULL: every subtile of the wave is inside M x N
+  auto compute = [&](auto FULL, int buf) __attribute__((always_inline)) {
+    const uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
+    uint4 bf[PB][TN];
+#pragma unroll
+    for (int p = 0; p < PB; ++p)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[p][j] = *(const uint4 *)(Bs + p * BN * KBK + j * 16 * KBK + boff);
+#pragma unroll
+    for (int pa_ = PA - 1; pa_ >= 0; --pa_) {
+      uint4 af[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = *(const uint4 *)(As + pa_ * BM * KBK + i * 16 * KBK + aoff);
+#pragma unroll
+      for (int pb_ = PB - 1; pb_ >= 0; --pb_) {
+        if (pa_ + pb_ > MAXO) continue;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            if constexpr (decltype(FULL)::value) acc[i][j] = mfma<MF>(af[i], bf[pb_][j], acc[i][j]);
+            else if (i < mlive && j < nlive) acc[i][j] = mfma<MF>(af[i], bf[pb_][j], acc[i][j]);
+          }
+      }
+    }
+  };
+  auto mainloop = [&](auto FULL) __attribute__((always_inline)) {
+    if (nfast > 0) gload_fast();
+    else gload_slow(kbeg);
     lstore(0);
     __syncthreads();
-    int buf = 0;
-    for (int k0 = kbeg; k0 < kend; k0 += KBK) {
-      const bool more = k0 + KBK < kend;
-      if (more) gload(k0 + KBK);
-      const uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
-      uint4 bf[PB][TN];
-#pragma unroll
-      for (int p = 0; p < PB; ++p)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) bf[p][j] = *(const uint4 *)(Bs + p * BN * KBK + boff[j]);
-#pragma unroll
-      for (int pa = PA - 1; pa >= 0; --pa) {
-        uint4 af[TM];
-#pragma unroll
-        for (int i = 0; i < TM; ++i) af[i] = *(const uint4 *)(As + pa * BM * KBK + aoff[i]);
-#pragma unroll
-        for (int pb = PB - 1; pb >= 0; --pb) {
-          if (pa + pb > MAXO) continue;
-          if (full) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-              for (int j = 0; j < TN; ++j) acc[i][j] = mfma<MF>(af[i], bf[pb][j], acc[i][j]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-              for (int j = 0; j < TN; ++j)
-                if (i < mlive && j < nlive) acc[i][j] = mfma<MF>(af[i], bf[pb][j], acc[i][j]);
-          }
-        }
-      }
+    int buf = 0, s = 0;
+    // steady state: the next step's loads take the fast path
+    for (; s + 1 < nfast; ++s) {
+      gload_fast();
+      compute(FULL, buf);
+      lstore(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+    // remaining steps (the ragged end of K, or every step when blocked addressing is irregular)
+    for (; s < nsteps; ++s) {
+      const bool more = s + 1 < nsteps;
+      if (more) gload_slow(kbeg + (s + 1) * KBK);
+      compute(FULL, buf);
       if (more) lstore(buf ^ 1);
       __syncthreads();
       buf ^= 1;
     }
+  };
+  if (kbeg < kend) {
+    if (full) mainloop(std::integral_constant<bool, true>{});
+    else mainloop(std::integral_constant<bool, false>{});
   }
 
   const float cs = g.alpha / (ascale * bscale);
@@ -216,11 +305,11 @@ __global__ void __launch_bounds__(KNT) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-template <int MF, int SA, int SB, int TM, int TN>
+template <int MF, int SA, int SB, int TM, int TN, int W = 2>
 void launch_kc(const GemmArgs &g, int batch, int nsplit, hipStream_t st) {
   constexpr int BM = 32 * TM, BN = 32 * TN;
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kc_kernel<MF, SA, SB, TM, TN>), dim3(tiles, nsplit, batch), dim3(KNT), 0, st, g);
+  hipLaunchKernelGGL((gemm_kc_kernel<MF, SA, SB, TM, TN, W>), dim3(tiles, nsplit, batch), dim3(KNT), 0, st, g);
 }
 
 template <int MF, int SA, int SB>
@@ -237,6 +326,9 @@ void launch_shape(const GemmArgs &g, int batch, int nsplit, hipStream_t st) {
 
 // Both operands contiguous along K; arguments validated by gemm().
 void gemm_kc(int mf, int sa, int sb, const GemmArgs &g, int batch, int nsplit, hipStream_t st) {
+  const long long esa = sa == SRC_F32 ? 4 : 2, esb = sb == SRC_F32 ? 4 : 2;
+  JOLT_REQUIRE(((long long)g.M * g.a_ld + 32) * esa < (1LL << 32) && ((long long)g.N * g.b_ld + 32) * esb < (1LL << 32),
+               JOLT_EINVAL, "gemm: row offsets exceed 32 bits");
   if (mf == MF_F16) {
     if (sa == SRC_F16 && sb == SRC_F16) launch_shape<MF_F16, SRC_F16, SRC_F16>(g, batch, nsplit, st);
     else if (sa == SRC_F16 && sb == SRC_F32) launch_shape<MF_F16, SRC_F16, SRC_F32>(g, batch, nsplit, st);
