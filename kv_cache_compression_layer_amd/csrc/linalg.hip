@@ -30,6 +30,51 @@ __device__ double block_sum(double v, double *red) {
   return s;
 }
 
+// All eigenvalues of the symmetric tridiagonal (d, e) by Sturm-sequence bisection (one thread
+// per eigenvalue, descending order into ev; d and e^2 staged in LDS scratch of 2n doubles).
+__device__ void bisect_all(int n, const double *d, const double *e, double *smem, double *ev, int clamp) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  double *sd = smem, *se2 = smem + n;
+  for (int i = tid; i < n; i += nt) {
+    sd[i] = d[i];
+    se2[i] = (i + 1 < n) ? e[i] * e[i] : 0.0;
+  }
+  __syncthreads();
+  double lo0 = 1e300, hi0 = -1e300, tn = 0.0;
+  for (int i = 0; i < n; ++i) {
+    double r = (i > 0 ? sqrt(se2[i - 1]) : 0.0) + (i + 1 < n ? sqrt(se2[i]) : 0.0);
+    lo0 = fmin(lo0, sd[i] - r);
+    hi0 = fmax(hi0, sd[i] + r);
+  }
+  tn = fmax(fabs(lo0), fabs(hi0));
+  const double pivmin = fmax(1e-300, 1e-300 * tn * tn);
+  lo0 -= 2.2e-16 * tn * 4 + pivmin;
+  hi0 += 2.2e-16 * tn * 4 + pivmin;
+  for (int j = tid; j < n; j += nt) {
+    const int s = n - 1 - j;  // j-th largest == s-th smallest (0-based)
+    double lo = lo0, hi = hi0;
+    for (int it = 0; it < 200; ++it) {
+      double mid = 0.5 * (lo + hi);
+      if (mid <= lo || mid >= hi) break;
+      if (hi - lo <= 2.2e-16 * fmax(fabs(lo), fabs(hi)) * 2 + pivmin) break;
+      int cnt = 0;
+      double q = sd[0] - mid;
+      if (fabs(q) < pivmin) q = -pivmin;
+      cnt += (q < 0.0);
+      for (int i = 1; i < n; ++i) {
+        q = (sd[i] - mid) - se2[i - 1] / q;
+        if (fabs(q) < pivmin) q = -pivmin;
+        cnt += (q < 0.0);
+      }
+      if (cnt <= s) lo = mid;
+      else hi = mid;
+    }
+    double v = 0.5 * (lo + hi);
+    if (clamp && v < 0.0) v = 0.0;
+    ev[j] = v;
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Householder tridiagonalisation + all eigenvalues by bisection.
 // A: [batch][n][lda] fp64 symmetric (overwritten).  Output per batch: d[n], e[n] (e[n-1]=0),
@@ -141,47 +186,252 @@ __global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long
   }
   __syncthreads();
 
-  // ---- bisection (Sturm counts) for every eigenvalue; d, e^2 staged in LDS ------------------
-  double *sd = smem, *se2 = smem + n;  // reuse LDS (working copy no longer needed)
-  for (int i = tid; i < n; i += nt) {
-    sd[i] = d[i];
-    se2[i] = (i + 1 < n) ? e[i] * e[i] : 0.0;
+  bisect_all(n, d, e, smem, evals + b * ev_bs, clamp);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The same reduction for matrices kept in global memory (too large for LDS), arranged so that the
+// trailing matrix is swept once per step.  Step k (reflector v_k from row k, p_k = beta_k A v_k,
+// w_k = p_k - (beta_k / 2)(p_k . v_k) v_k, A <- A - v_k w_k^T - w_k v_k^T on rows/cols > k):
+//   1. wave 0 applies the update to row k+1 and forms reflector k+1 from it (one-step look-ahead);
+//   2. every wave applies the update to its rows i > k+1 and, in the same pass over the row,
+//      accumulates p_{k+1}[i] = beta_{k+1} sum_j A[i][j] v_{k+1}[j].
+// Column k+1 of rows i > k+1 is never read again (its content is row k+1 by symmetry) and is not
+// updated.  v and p live in LDS with absolute indices, two buffers each alternating by step, so a
+// step needs two workgroup barriers.  Same formulas as tridiag_values_kernel; sums run in a fixed
+// order, so results are deterministic.  LDS: 4n doubles.
+// ---------------------------------------------------------------------------------------------
+constexpr int TCH = 9;  // 64-wide row chunks a wave keeps in registers (one pass covers 576 columns)
+constexpr int TRB = 2;  // rows a wave sweeps together (TRB * TCH loads in flight)
+
+// Wave-level: Householder reflector from row r (x = W[r][r+1..n)), written to v (LDS, absolute
+// columns), the reflector row R[r][..] and d/e/beta[r]; returns beta on every lane.  General
+// width (re-reads the row); the fused kernel uses the register version below when it fits.
+__device__ __forceinline__ double wave_reflector(double *W, int ldw, int n, int r, double *v, double *R, long long r_ld, double *d,
+                                 double *e, double *be) {
+  const int lane = threadIdx.x & 63;
+  const double *x = W + (long long)r * ldw;
+  double part = 0.0, alpha = 0.0;
+  for (int j = r + 1 + lane; j < n; j += 64) {
+    const double xj = x[j];
+    if (j == r + 1) alpha = xj;
+    else part += xj * xj;
+  }
+  const double sigma = warp_sum_d(part);
+  alpha = __shfl(alpha, 0, 64);  // column r+1 is lane 0's first element
+  double bet, v0, mu;
+  if (sigma == 0.0) {
+    bet = 0.0;
+    v0 = 1.0;
+    mu = alpha;
+  } else {
+    mu = sqrt(alpha * alpha + sigma);
+    v0 = (alpha <= 0.0) ? (alpha - mu) : (-sigma / (alpha + mu));
+    bet = 2.0 * v0 * v0 / (sigma + v0 * v0);
+  }
+  const double dr = x[r];
+  for (int j = r + 1 + lane; j < n; j += 64) {
+    const double vj = (j == r + 1) ? 1.0 : x[j] / v0;
+    v[j] = vj;
+    R[(long long)r * r_ld + j] = vj;  // may alias row r of W: each element is read before it is written
+  }
+  if (lane == 0) {
+    d[r] = dr;
+    e[r] = (sigma == 0.0) ? alpha : mu;
+    be[r] = bet;
+  }
+  return bet;
+}
+
+// Row r (columns r..n-1, n - r <= 64 * TCH) held in registers x[t] = row[r + lane + 64 t]:
+// the same reflector, one read of the row.
+__device__ __forceinline__ double wave_reflector_regs(const double (&x)[TCH], int n, int r, double *v, double *R, long long r_ld,
+                                      double *d, double *e, double *be) {
+  const int lane = threadIdx.x & 63;
+  double part = 0.0;
+#pragma unroll
+  for (int t = 0; t < TCH; ++t) {
+    const int j = r + lane + 64 * t;
+    if (j >= r + 2 && j < n) part += x[t] * x[t];
+  }
+  const double sigma = warp_sum_d(part);
+  const double alpha = __shfl(x[0], 1, 64), dr = __shfl(x[0], 0, 64);
+  double bet, v0, mu;
+  if (sigma == 0.0) {
+    bet = 0.0;
+    v0 = 1.0;
+    mu = alpha;
+  } else {
+    mu = sqrt(alpha * alpha + sigma);
+    v0 = (alpha <= 0.0) ? (alpha - mu) : (-sigma / (alpha + mu));
+    bet = 2.0 * v0 * v0 / (sigma + v0 * v0);
+  }
+#pragma unroll
+  for (int t = 0; t < TCH; ++t) {
+    const int j = r + lane + 64 * t;
+    if (j >= r + 1 && j < n) {
+      const double vj = (j == r + 1) ? 1.0 : x[t] / v0;
+      v[j] = vj;
+      R[(long long)r * r_ld + j] = vj;
+    }
+  }
+  if (lane == 0) {
+    d[r] = dr;
+    e[r] = (sigma == 0.0) ? alpha : mu;
+    be[r] = bet;
+  }
+  return bet;
+}
+
+__global__ void __launch_bounds__(LT) tridiag_fused_kernel(double *A, long long a_bs, int lda, int n,
+                                                           double *d_out, double *e_out, double *refl, double *beta,
+                                                           long long t_bs, double *evals, long long ev_bs, int clamp) {
+  extern __shared__ double smem[];
+  __shared__ double sbeta[2];
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwave = blockDim.x >> 6;
+  double *W = A + b * a_bs;
+  const int ldw = lda;
+  double *d = d_out + b * t_bs, *e = e_out + b * t_bs, *R = refl + b * t_bs * (long long)n, *be = beta + b * t_bs;
+  // v_k at smem + (k % 2) n, p_k at smem + (2 + k % 2) n (pointers derived arithmetically from the
+  // LDS array so that every access compiles to an LDS instruction)
+
+  if (n >= 3) {
+    // prologue: reflector 0 and p_0 = beta_0 A[1.., 1..] v_0
+    if (wave == 0) {
+      const double bt = wave_reflector(W, ldw, n, 0, smem, R, n, d, e, be);
+      if (lane == 0) sbeta[0] = bt;
+    }
+    __syncthreads();
+    {
+      const double b0 = sbeta[0];
+      for (int i = 1 + wave; i < n; i += nwave) {
+        const double *ri = W + (long long)i * ldw;
+        double s = 0.0;
+        for (int j = 1 + lane; j < n; j += 64) s += ri[j] * smem[j];
+        s = warp_sum_d(s);
+        if (lane == 0) smem[2 * n + i] = b0 * s;
+      }
+    }
+    __syncthreads();
+    for (int k = 0; k + 2 < n; ++k) {
+      const int cur = k & 1, nxt = cur ^ 1, r = k + 1;
+      const double *vk = smem + cur * n, *pk = smem + (2 + cur) * n;
+      double *vnx = smem + nxt * n;
+      // c = (beta_k / 2) p_k . v_k, computed by every wave in the same order
+      double part = 0.0;
+      for (int j = r + lane; j < n; j += 64) part += pk[j] * vk[j];
+      const double c = 0.5 * sbeta[cur] * warp_sum_d(part);
+      const bool last = (r == n - 2);
+      if (wave == 0) {
+        // update row r (columns r..n-1), then the next reflector from it
+        double *rr = W + (long long)r * ldw;
+        const double wr = pk[r] - c * vk[r], vr = vk[r];
+        if (n - r <= 64 * TCH) {
+          double x[TCH];
+#pragma unroll
+          for (int t = 0; t < TCH; ++t) {
+            const int j = r + lane + 64 * t;
+            x[t] = (j < n) ? rr[j] : 0.0;
+          }
+#pragma unroll
+          for (int t = 0; t < TCH; ++t) {
+            const int j = r + lane + 64 * t;
+            if (j < n) {
+              x[t] -= vr * (pk[j] - c * vk[j]) + wr * vk[j];
+              rr[j] = x[t];  // (columns > r are overwritten by the reflector when it aliases the row)
+            }
+          }
+          if (!last) {
+            const double bt = wave_reflector_regs(x, n, r, vnx, R, n, d, e, be);
+            if (lane == 0) sbeta[nxt] = bt;
+          } else {
+            const double e2 = __shfl(x[0], 1, 64);  // column n-1 of row n-2
+            if (lane == 0) {
+              d[n - 2] = x[0];
+              e[n - 2] = e2;
+              be[n - 2] = 0.0;
+            }
+          }
+        } else {
+          for (int j = r + lane; j < n; j += 64) rr[j] -= vr * (pk[j] - c * vk[j]) + wr * vk[j];
+          if (!last) {
+            const double bt = wave_reflector(W, ldw, n, r, vnx, R, n, d, e, be);
+            if (lane == 0) sbeta[nxt] = bt;
+          } else if (lane == 0) {
+            d[n - 2] = rr[n - 2];
+            e[n - 2] = rr[n - 1];
+            be[n - 2] = 0.0;
+          }
+        }
+      }
+      __syncthreads();
+      // rows r+1..n-1: update columns r+1..n-1 and accumulate the next matvec in the same pass;
+      // a wave sweeps TRB rows at once with every load of a chunk group issued before any use
+      const double bn = last ? 0.0 : sbeta[nxt];
+      const double *vn = vnx;
+      double *pn = smem + (2 + nxt) * n;
+      for (int i0 = r + 1 + wave * TRB; i0 < n; i0 += nwave * TRB) {
+        double s[TRB], wi[TRB], vi[TRB];
+#pragma unroll
+        for (int q = 0; q < TRB; ++q) {
+          const int i = min(i0 + q, n - 1);
+          s[q] = 0.0;
+          wi[q] = pk[i] - c * vk[i];
+          vi[q] = vk[i];
+        }
+        for (int j0 = r + 1; j0 < n; j0 += 64 * TCH) {
+          double a[TRB][TCH];
+#pragma unroll
+          for (int q = 0; q < TRB; ++q)
+#pragma unroll
+            for (int t = 0; t < TCH; ++t) {
+              const int j = j0 + lane + 64 * t;
+              a[q][t] = (i0 + q < n && j < n) ? W[(long long)(i0 + q) * ldw + j] : 0.0;
+            }
+#pragma unroll
+          for (int t = 0; t < TCH; ++t) {
+            const int j = j0 + lane + 64 * t;
+            if (j < n) {
+              const double pj = pk[j] - c * vk[j], vj = vk[j], vnj = last ? 0.0 : vn[j];
+#pragma unroll
+              for (int q = 0; q < TRB; ++q) {
+                if (i0 + q < n) {
+                  const double u = a[q][t] - (vi[q] * pj + wi[q] * vj);
+                  W[(long long)(i0 + q) * ldw + j] = u;
+                  s[q] += u * vnj;
+                }
+              }
+            }
+          }
+        }
+        if (!last) {
+#pragma unroll
+          for (int q = 0; q < TRB; ++q) {
+            const double sq = warp_sum_d(s[q]);
+            if (lane == 0 && i0 + q < n) pn[i0 + q] = bn * sq;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    if (tid == 0) {
+      d[n - 1] = W[(long long)(n - 1) * ldw + (n - 1)];
+      e[n - 1] = 0.0;
+      be[n - 1] = 0.0;
+    }
+  } else if (tid == 0) {
+    d[0] = W[0];
+    if (n == 2) {
+      d[1] = W[(long long)ldw + 1];
+      e[0] = W[1];
+    }
+    e[n - 1] = 0.0;
+    be[0] = 0.0;
+    be[n - 1] = 0.0;
   }
   __syncthreads();
-  double lo0 = 1e300, hi0 = -1e300, tn = 0.0;
-  for (int i = 0; i < n; ++i) {
-    double r = (i > 0 ? sqrt(se2[i - 1]) : 0.0) + (i + 1 < n ? sqrt(se2[i]) : 0.0);
-    lo0 = fmin(lo0, sd[i] - r);
-    hi0 = fmax(hi0, sd[i] + r);
-  }
-  tn = fmax(fabs(lo0), fabs(hi0));
-  const double pivmin = fmax(1e-300, 1e-300 * tn * tn);
-  lo0 -= 2.2e-16 * tn * 4 + pivmin;
-  hi0 += 2.2e-16 * tn * 4 + pivmin;
-  double *ev = evals + b * ev_bs;
-  for (int j = tid; j < n; j += nt) {
-    const int s = n - 1 - j;  // j-th largest == s-th smallest (0-based)
-    double lo = lo0, hi = hi0;
-    for (int it = 0; it < 200; ++it) {
-      double mid = 0.5 * (lo + hi);
-      if (mid <= lo || mid >= hi) break;
-      if (hi - lo <= 2.2e-16 * fmax(fabs(lo), fabs(hi)) * 2 + pivmin) break;
-      int cnt = 0;
-      double q = sd[0] - mid;
-      if (fabs(q) < pivmin) q = -pivmin;
-      cnt += (q < 0.0);
-      for (int i = 1; i < n; ++i) {
-        q = (sd[i] - mid) - se2[i - 1] / q;
-        if (fabs(q) < pivmin) q = -pivmin;
-        cnt += (q < 0.0);
-      }
-      if (cnt <= s) lo = mid;
-      else hi = mid;
-    }
-    double v = 0.5 * (lo + hi);
-    if (clamp && v < 0.0) v = 0.0;
-    ev[j] = v;
-  }
+  bisect_all(n, d, e, smem, evals + b * ev_bs, clamp);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -685,6 +935,7 @@ void ensure_lds_attrs() {
   // best effort: the runtime may already allow the full amount
   (void)hipFuncSetAttribute((const void *)chol_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_values_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)backtransform_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipGetLastError();
   done = true;
@@ -695,14 +946,19 @@ size_t tridiag_lds_bytes(int n) { return ((size_t)n * n + 2 * (size_t)n) * sizeo
 void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d, double *e, double *refl,
                  double *beta, long long t_bs, double *evals, long long ev_bs, bool clamp, hipStream_t st) {
   JOLT_REQUIRE(n >= 1 && n <= 8192, JOLT_EINVAL, "eigensolver: unsupported size");
+  JOLT_REQUIRE(t_bs == n, JOLT_EINVAL, "eigensolver: tridiagonal stride must equal n");
   size_t lds_full = tridiag_lds_bytes(n);
   const size_t lds_cap = 150 * 1024;
-  bool use_lds = lds_full <= lds_cap;
-  size_t shm = use_lds ? lds_full : std::max<size_t>(2 * (size_t)n * sizeof(double), 4096);
-  JOLT_REQUIRE(shm <= 160 * 1024, JOLT_EINVAL, "eigensolver: n too large for LDS staging");
   ensure_lds_attrs();
-  hipLaunchKernelGGL(tridiag_values_kernel, dim3(batch), dim3(LT), shm, st, A, a_bs, lda, (const int *)nullptr, n,
-                     d, e, refl, beta, t_bs, evals, ev_bs, clamp ? 1 : 0, use_lds ? 1 : 0);
+  if (lds_full <= lds_cap) {
+    hipLaunchKernelGGL(tridiag_values_kernel, dim3(batch), dim3(LT), lds_full, st, A, a_bs, lda, (const int *)nullptr,
+                       n, d, e, refl, beta, t_bs, evals, ev_bs, clamp ? 1 : 0, 1);
+  } else {
+    const size_t shm = 4 * (size_t)n * sizeof(double);
+    JOLT_REQUIRE(shm <= 150 * 1024, JOLT_EINVAL, "eigensolver: n too large for LDS staging");
+    hipLaunchKernelGGL(tridiag_fused_kernel, dim3(batch), dim3(LT), shm, st, A, a_bs, lda, n, d, e, refl, beta, t_bs,
+                       evals, ev_bs, clamp ? 1 : 0);
+  }
   HIP_LAUNCH_CHECK();
 }
 
