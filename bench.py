@@ -38,7 +38,93 @@ def parse():
     ap.add_argument("--dtype", default="f16", choices=["f16", "bf16"])
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="print a per-kernel summary of a rocprofv3 --kernel-trace --output-format csv directory")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc csv directories (FETCH_SIZE / WRITE_SIZE of this bench and of "
+                         "--calibrate-copy): write profiles/traffic.json for the dominant kernel and print a summary")
     return ap.parse_args()
+
+
+# the dominant kernel of the workload: the projection P^T = Q^T X (fp32 Q in two fp16 planes
+# times the fp16 cache), one launch over the 16 cells
+TRAFFIC_KERNEL = {"stage": "project_gemm", "name": "gemm_kc_kernel<0, 2, 0, 4, 8, 2>",
+                  "sources": ["kv_cache_compression_layer_amd/csrc/gemm_kc.hip",
+                              "kv_cache_compression_layer_amd/csrc/gemm_core.hpp",
+                              "kv_cache_compression_layer_amd/csrc/common.hpp"]}
+
+
+def project_grid(T=65536, L=32, H=8, D=128, G=4, ell=522):
+    """Work-items of the projection launch as the profiler reports them (128 x 256 tiles)."""
+    tiles = -(-ell // 128) * -(-(G * H * D) // 256)
+    return tiles * 256 * (2 * L // G)
+
+
+def _rows(d, fname):
+    import csv
+    with open(os.path.join(d, fname)) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profile(d):
+    """Per (kernel, grid) call count and durations from a kernel-trace csv directory."""
+    import collections
+    rows = _rows(d, "run_kernel_trace.csv")
+    agg = collections.defaultdict(list)
+    other = [0.0, 0]
+    for r in rows:
+        ms = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+        if "jolt::" not in r["Kernel_Name"]:  # input generation and torch glue outside the library
+            other[0] += ms
+            other[1] += 1
+            continue
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        agg[(r["Kernel_Name"], grid)].append(ms)
+    tot = sum(sum(v) for v in agg.values())
+    out = ["library kernels: %.2f ms over %d dispatches (other kernels of the process: %.2f ms over %d)"
+           % (tot, sum(len(v) for v in agg.values()), other[0], other[1]),
+           "%9s %6s %10s %10s %12s  %s" % ("total_ms", "calls", "avg_ms", "share", "grid_items", "kernel")]
+    for (name, grid), v in sorted(agg.items(), key=lambda kv: -sum(kv[1]))[:30]:
+        nm = name.replace("jolt::(anonymous namespace)::", "")
+        nm = nm if len(nm) <= 90 else nm[:87] + "..."
+        out.append("%9.3f %6d %10.4f %9.1f%% %12d  %s" % (sum(v), len(v), sum(v) / len(v), 100 * sum(v) / tot, grid, nm))
+    return "\n".join(out)
+
+
+def traffic_from(fetch, write, cfetch, cwrite):
+    """HBM bytes per launch of the dominant kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for a plain copy of known size."""
+    def counter(d, pick):
+        vals = [float(r["Counter_Value"]) for r in _rows(d, "run_counter_collection.csv") if pick(r)]
+        return sum(vals) / len(vals), len(vals)
+    grid = project_grid()
+    is_k = lambda r: TRAFFIC_KERNEL["name"] in r["Kernel_Name"] and int(r["Grid_Size"]) == grid
+    is_copy = lambda r: "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower()
+    f_kib, nf = counter(fetch, is_k)
+    w_kib, nw = counter(write, is_k)
+    cf_kib, _ = counter(cfetch, is_copy)
+    cw_kib, _ = counter(cwrite, is_copy)
+    fscale = COPY_BYTES / (cf_kib * 1024.0)
+    wscale = COPY_BYTES / (cw_kib * 1024.0)
+    bytes_per_launch = f_kib * 1024.0 * fscale + w_kib * 1024.0 * wscale
+    ent = {"kernel": TRAFFIC_KERNEL["name"], "grid_items": grid, "sources": TRAFFIC_KERNEL["sources"],
+           "source_hash": source_hash(TRAFFIC_KERNEL["sources"]), "fetch_kib": f_kib, "write_kib": w_kib,
+           "fetch_scale": fscale, "write_scale": wscale, "bytes_per_launch": bytes_per_launch,
+           "dispatches": [nf, nw]}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    t = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            t = json.load(f)
+    t[TRAFFIC_KERNEL["stage"]] = ent
+    with open(path, "w") as f:
+        json.dump(t, f, indent=1)
+    return ("kernel %s (grid %d work-items), %d/%d dispatches\n"
+            "FETCH_SIZE %.0f KiB/dispatch x scale %.4f (copy of %d bytes read %.0f KiB)\n"
+            "WRITE_SIZE %.0f KiB/dispatch x scale %.4f (copy of %d bytes wrote %.0f KiB)\n"
+            "HBM bytes per launch: %.4g (read %.4g, write %.4g)"
+            % (ent["kernel"], grid, nf, nw, f_kib, fscale, COPY_BYTES, cf_kib, w_kib, wscale, COPY_BYTES, cw_kib,
+               bytes_per_launch, f_kib * 1024 * fscale, w_kib * 1024 * wscale))
 
 
 COPY_BYTES = 1 << 30
@@ -65,9 +151,9 @@ def kernel_models(T, L, H, D, G, ell, picks, dtype_bytes):
     # Y^T = Omega^T X^T and Y^T = Z^T X^T: 2 T M ell flops per cell, X read once
     m["sketch_gemm"] = {"flops": 2.0 * T * M * ell * cells_per_launch, "launches_per_call": 2,
                         "bytes": (T * M * dtype_bytes + 4.0 * ell * T) * cells_per_launch}
-    # P^T = Q^T X: same contraction
+    # P^T = Q^T X: same contraction; reads X and fp32 Q once, writes P in both layouts
     m["project_gemm"] = {"flops": 2.0 * T * M * ell * n_cells, "launches_per_call": 1,
-                         "bytes": (T * M * dtype_bytes + 4.0 * ell * T) * n_cells}
+                         "bytes": (T * M * dtype_bytes + 4.0 * ell * T + 2 * 4.0 * ell * M) * n_cells}
     # fused residual encode: one launch over the cells with b > 0
     flops = 0.0
     byts = 0.0
@@ -145,6 +231,12 @@ def main():
     a = parse()
     if a.calibrate_copy:
         calibrate_copy()
+        return
+    if a.summarize_profile:
+        print(summarize_profile(a.summarize_profile))
+        return
+    if a.traffic_from:
+        print(traffic_from(*a.traffic_from))
         return
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path shards by cell "
