@@ -1,4 +1,6 @@
-// C ABI of libjolt: argument validation, workspace carving and stage sequencing on one stream.
+// C ABI of libjolt: argument validation, workspace carving and stage sequencing.  Work is ordered on
+// the caller's stream; the spectra stages of disjoint cell ranges fork onto library-owned side
+// streams (default priority) and join back before the allocation reads them.
 //
 // Pipeline of jolt_compress (Krishnan & Schulz, "A JoLT for the KV Cache", Sec. 3 and 3.1):
 //   spectra   feature Gram -> ||X||^2, unprojected feature spectrum;
@@ -13,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -195,7 +198,8 @@ struct Bufs {
   // ([T][ell_ld]); P / Z likewise ([ell][M] and [M][ell_ld])
   float *bufA, *bufB, *bufA2, *bufB2, *Pt, *P2, *Zt, *Z2, *RinvT, *YpT;
   double *G64, *Rw, *dT, *eT, *betaT, *evT;
-  float *amax;  // [8][n_cells]
+  float *amax;  // [8][n_cells]: slot k of cell c at amax[k * am_ld + c]
+  int am_ld;
   // fit
   float *Wrows, *Udrows, *Cp, *Udr, *Cr, *Vt, *Bcat, *bamax, *Qf, *Qtf;
   double *Zw, *work, *ZwD, *workD;
@@ -220,17 +224,25 @@ int nsplit_for(long long K, long long tiles, int batch, long long min_chunk) {
 
 long long tiles_of(long long M, long long N) { return ((M + 127) / 128) * ((N + 127) / 128); }
 
+// The spectra of the cells can run as kViews independent chains of consecutive cells on their own
+// streams, each with its own split-K scratch.  Measured on the 8B shape, two chains were slower
+// than one (the one-workgroup fp64 stages lose their CUs to the concurrent matrix-core launches
+// and the final eigensolve of each chain cannot overlap anything), so one chain is used.
+constexpr int kViews = 1;
+
+int n_views(const Plan &pl) {
+  int v = kViews;
+  while (v > 1 && (pl.n_cells % (2 * v) != 0)) --v;  // views hold whole (group, K|V) pairs
+  return v;
+}
+
 struct Sizes {
   int kmax, kmax_d, Kb;
-  long long part_elems;
+  long long part_elems;    // whole split-K scratch
+  long long part_view;     // per spectra view (the first n_views of them are disjoint slices)
 };
 
-Sizes sizes_for(const Plan &pl, int kmax, int kmax_d) {
-  Sizes s;
-  s.kmax = kmax;
-  s.kmax_d = kmax_d;
-  s.Kb = (int)rup(pl.D + kmax, 8);
-  const int nb = pl.n_cells;
+long long part_elems_for(const Plan &pl, int kmax, int nb) {
   long long pe = 0;
   {  // feature Gram partials
     int ns = nsplit_for((long long)pl.GH * pl.T, 1, nb, 8192);
@@ -239,7 +251,7 @@ Sizes sizes_for(const Plan &pl, int kmax, int kmax_d) {
     pe = std::max(pe, (long long)nb * ns2 * pl.D * pl.D);
   }
   if (pl.mode == JOLT_FLASH) {
-    int ns = nsplit_for(pl.T, tiles_of(pl.ell, pl.ell), nb, 2048);
+    int ns = nsplit_for(pl.T, tiles_of(pl.ell, pl.ell), nb, 1024);
     pe = std::max(pe, (long long)nb * ns * pl.ell * pl.ell_ld);
     int ns2 = nsplit_for(pl.M, tiles_of(pl.ell, pl.ell), nb, 1024);
     pe = std::max(pe, (long long)nb * ns2 * pl.ell * pl.ell_ld);
@@ -247,7 +259,17 @@ Sizes sizes_for(const Plan &pl, int kmax, int kmax_d) {
     int ns = nsplit_for(pl.M, tiles_of(pl.T, pl.T), nb, 1024);
     pe = std::max(pe, (long long)nb * ns * pl.T * pl.T_ld);
   }
-  s.part_elems = pe;
+  return rup(pe, 64);
+}
+
+Sizes sizes_for(const Plan &pl, int kmax, int kmax_d) {
+  Sizes s;
+  s.kmax = kmax;
+  s.kmax_d = kmax_d;
+  s.Kb = (int)rup(pl.D + kmax, 8);
+  const int nv = n_views(pl);
+  s.part_view = part_elems_for(pl, kmax, pl.n_cells / nv);
+  s.part_elems = std::max(part_elems_for(pl, kmax, pl.n_cells), nv * s.part_view);
   return s;
 }
 
@@ -266,6 +288,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
   b.specD = ar.take<double>((long long)nb * D);
   b.norm2 = ar.take<double>(nb);
   b.amax = ar.take<float>(8LL * nb);
+  b.am_ld = nb;
   const long long n_tok = pl.mode == JOLT_FLASH ? ell : pl.T;  // size of the token-side eigenproblem
   b.G64 = ar.take<double>((long long)nb * n_tok * n_tok);
   b.dT = ar.take<double>((long long)nb * n_tok);
@@ -403,13 +426,15 @@ void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStr
 // FlashJoLT token spectrum (Sec. 3.1): randomized subspace iteration with Cholesky QR.
 // Every large contraction is K-contiguous on both operands; tall fp32 panels are written in
 // both layouts by the GEMM epilogue so the next consumer never transposes while loading.
-void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
+// mark (optional) is recorded on st once the first orthonormal basis Q_0 exists; the next spectra
+// chain waits for it, which puts the chains out of phase.
+void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st, hipEvent_t mark = nullptr) {
   const int nb = pl.n_cells, nkv = nb / 2;
   const long long ell = pl.ell, ld = pl.ell_ld, Tld = pl.T_ld, Mf = pl.M, T = pl.T;
   const long long cellX = pl.cell_elems();
-  float *amY = b.amax, *amR = b.amax + nb, *amQ = b.amax + 2 * nb, *amP = b.amax + 3 * nb, *amZ = b.amax + 4 * nb;
-  gen_omega(b.omegaT, pl.dtype, pl.M, pl.ell, stream_key(pl.sketch_seed, 2), st);
-  fill_f32(b.amax, 8LL * nb, 0.f, st);
+  const int am = b.am_ld;
+  float *amY = b.amax, *amR = b.amax + am, *amQ = b.amax + 2 * am, *amP = b.amax + 3 * am, *amZ = b.amax + 4 * am;
+  // (Omega is generated and the amax slots are cleared once for all cells by spectra_all)
 
   // Y^T = A X_(T)^T with A = Omega^T (cache dtype) or Z^T (fp32); also Y = (Y^T)^T
   auto sketch = [&](const void *A, int a_src, long long a_bs, const float *a_amax, float *outT, float *outR,
@@ -470,6 +495,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
 
   sketch(b.omegaT, pl.xsrc(), 0, nullptr, pa.T, pa.R, pa.am);
   Pair Q = cholqr(pa, pb, 1);
+  if (mark) HIP_TRY(hipEventRecord(mark, st));
   for (int it = 0; it < pl.power_iters; ++it) {
     fill_f32(amP, nb, 0.f, st);
     project(Q.T, Q.am, amP);
@@ -501,7 +527,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     Q = cholqr(Q, other, 1);
   }
   // B = Q^T X_(T) -> H = B B^T (fp64) -> eigenvalues; spectrum = top q + tail entry
-  float *amP1 = b.amax + 5 * nb;
+  float *amP1 = b.amax + 5 * am;
   fill_f32(amP1, nb, 0.f, st);
   project(Q.T, Q.am, amP1);
   {
@@ -513,7 +539,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     sym_eigvals(b.G64, ell * ell, (int)ell, (int)ell, nb, b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, true, st);
   }
   flash_spec(b.evT, ell, pl.q, b.norm2, b.specT, pl.nT, nb, st);
-  // the fit reads Q (both layouts) from b.bufA / b.bufA2
+  // the fit reads Q (both layouts) from bufA / bufA2: report it by swapping this view's pointers
   if (Q.T != b.bufA) {
     std::swap(b.bufA, b.bufB);
     std::swap(b.bufA2, b.bufB2);
@@ -686,7 +712,7 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
   const float *Qf = (const float *)(b.params + rot_offs[0]);
   const float *Qtf = (const float *)(b.params + rot_offs[1]);
 
-  float *amYp = b.amax + 6 * nb, *amCr = b.amax + 7 * nb;
+  float *amYp = b.amax + 6 * b.am_ld, *amCr = b.amax + 7 * b.am_ld;
   Stage prof_vec("fit_token_factor", st);
   float *UTt = b.bufB;  // [nb][kmax][Tld]
   float *Yp = b.Zt;     // [nb][kmax][Mf]
@@ -707,7 +733,7 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     // token-projected tensor Y_p = W^T P1^T  (kmax x M)
     GemmArgs h = ga();
     h.A = b.Wrows; h.a_ld = ld; h.a_bs = kmax * ld; h.a_amax_c = 1.f;
-    h.B = b.P2; h.b_ld = ld; h.b_bs = Mf * ld; h.b_amax = b.amax + 5 * nb; h.ab_amax_bs = 1;
+    h.B = b.P2; h.b_ld = ld; h.b_bs = Mf * ld; h.b_amax = b.amax + 5 * b.am_ld; h.ab_amax_bs = 1;
     h.M = (int)kmax; h.N = (int)Mf; h.K = (int)ell;
     h.C = Yp; h.c_ld = Mf; h.c_bs = kmax * Mf; h.c_amax = amYp; h.c_amax_bs = 1; h.m_fastest = 1;
     h.C2 = b.YpT; h.c2_ld = kmax; h.c2_bs = Mf * kmax;
@@ -841,7 +867,63 @@ int guarded(F f) {
 
 Sizes sizes_worst(const Plan &pl) { return sizes_for(pl, pl.rT.back(), pl.rd.back()); }
 
-void spectra_all(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
+// Side streams (default priority) for the spectra views, created once per device.
+hipStream_t side_stream(int i) {
+  static std::mutex mu;
+  static std::vector<std::vector<hipStream_t>> per_dev;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)per_dev.size() <= dev) per_dev.resize(dev + 1);
+  auto &v = per_dev[dev];
+  while ((int)v.size() <= i) {
+    hipStream_t s = nullptr;
+    HIP_TRY(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+    v.push_back(s);
+  }
+  return v[i];
+}
+
+// Buffers of cells [c0, c0 + nc) for the spectra stages: every per-cell buffer offset to the first
+// cell (same per-cell strides as carve), the split-K scratch slice `slot`, amax slots with the full
+// stride.  Only the buffers the spectra stages touch are offset.
+Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot) {
+  Bufs v = b;
+  const long long D = pl.D, ell = pl.ell, ld = pl.ell_ld, Tld = pl.T_ld, T = pl.T, M = pl.M;
+  const long long n_tok = pl.mode == JOLT_FLASH ? ell : T;
+  v.part = b.part + (long long)slot * sz.part_view;
+  v.part_elems = sz.part_view;
+  v.Xt = (char *)b.Xt + (long long)c0 * pl.GH * D * Tld * pl.c;
+  v.Gd64 = b.Gd64 + c0 * D * D;
+  v.dD = b.dD + c0 * D;
+  v.eD = b.eD + c0 * D;
+  v.betaD = b.betaD + c0 * D;
+  v.evD = b.evD + c0 * D;
+  v.specT = b.specT + (long long)c0 * pl.nT;
+  v.specD = b.specD + c0 * D;
+  v.norm2 = b.norm2 + c0;
+  v.amax = b.amax + c0;
+  v.G64 = b.G64 + c0 * n_tok * n_tok;
+  v.dT = b.dT + c0 * n_tok;
+  v.eT = b.eT + c0 * n_tok;
+  v.betaT = b.betaT + c0 * n_tok;
+  v.evT = b.evT + c0 * n_tok;
+  if (pl.mode == JOLT_FLASH) {
+    v.bufA = b.bufA + c0 * ell * Tld;
+    v.bufB = b.bufB + c0 * ell * Tld;
+    v.bufA2 = b.bufA2 + c0 * T * ld;
+    v.bufB2 = b.bufB2 + c0 * T * ld;
+    v.Pt = b.Pt + c0 * ell * M;
+    v.P2 = b.P2 + c0 * M * ld;
+    v.Zt = b.Zt + c0 * ell * M;
+    v.Z2 = b.Z2 + c0 * M * ld;
+    v.Rw = b.Rw + c0 * 2 * ell * ell;
+    v.RinvT = b.RinvT + c0 * ell * ld;
+  }
+  return v;
+}
+
+void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const void *V, hipStream_t st) {
   JOLT_REQUIRE(K && V, JOLT_EINVAL, "null cache pointer");
   {
     Stage prof("transpose_x", st);
@@ -851,9 +933,59 @@ void spectra_all(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
                   cellX, 2 * cellXt, st);
     });
   }
-  stage_feature(pl, b, K, V, st);
-  if (pl.mode == JOLT_FLASH) stage_flash(pl, b, K, V, st);
-  else stage_exact(pl, b, K, V, st);
+  if (pl.mode == JOLT_FLASH) {
+    gen_omega(b.omegaT, pl.dtype, pl.M, pl.ell, stream_key(pl.sketch_seed, 2), st);
+    fill_f32(b.amax, 8LL * b.am_ld, 0.f, st);
+  }
+  const int nv = n_views(pl), nc = pl.n_cells / nv;
+  Plan pv = pl;
+  pv.n_cells = nc;
+  // fork: every view starts after the common prologue; view i > 0 also waits until view i - 1 has
+  // formed its first basis
+  std::vector<hipEvent_t> evs;
+  auto new_event = [&]() {
+    hipEvent_t e;
+    HIP_TRY(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+    evs.push_back(e);
+    return e;
+  };
+  hipEvent_t fork = new_event();
+  HIP_TRY(hipEventRecord(fork, st));
+  hipEvent_t prev_mark = nullptr;
+  std::vector<hipStream_t> streams(nv);
+  bool swapped = false;
+  for (int v = 0; v < nv; ++v) {
+    hipStream_t sv = v == 0 ? st : side_stream(v - 1);
+    streams[v] = sv;
+    if (v > 0) HIP_TRY(hipStreamWaitEvent(sv, fork, 0));
+    if (prev_mark) HIP_TRY(hipStreamWaitEvent(sv, prev_mark, 0));
+    const int c0 = v * nc;
+    Bufs bv = cell_view(b, pl, sz, c0, v);
+    const long long xoff = (long long)(c0 / 2) * pl.cell_elems() * pl.c;
+    const void *Kv = (const char *)K + xoff, *Vv = (const char *)V + xoff;
+    stage_feature(pv, bv, Kv, Vv, sv);
+    hipEvent_t mark = (pl.mode == JOLT_FLASH && v + 1 < nv) ? new_event() : nullptr;
+    if (pl.mode == JOLT_FLASH) {
+      float *bufA0 = bv.bufA;
+      stage_flash(pv, bv, Kv, Vv, sv, mark);
+      swapped = bv.bufA != bufA0;
+    } else {
+      stage_exact(pv, bv, Kv, Vv, sv);
+    }
+    prev_mark = mark;
+  }
+  // join
+  for (int v = 1; v < nv; ++v) {
+    hipEvent_t j = new_event();
+    HIP_TRY(hipEventRecord(j, streams[v]));
+    HIP_TRY(hipStreamWaitEvent(st, j, 0));
+  }
+  for (hipEvent_t e : evs) (void)hipEventDestroy(e);  // released once the recorded work completes
+  // the fit reads Q (both layouts) from b.bufA / b.bufA2
+  if (swapped) {
+    std::swap(b.bufA, b.bufB);
+    std::swap(b.bufA2, b.bufB2);
+  }
 }
 
 }  // namespace
@@ -976,7 +1108,7 @@ int jolt_spectra(const void *d_K, const void *d_V, const jolt_cache_desc *desc, 
     Sizes sz = sizes_worst(pl);
     if (d_UT) sz = sizes_for(pl, std::max(pl.rT.back(), (int)rup(n_vec, 8)), pl.rd.back());
     Bufs b = carve(ar, pl, sz);
-    spectra_all(pl, b, d_K, d_V, st);
+    spectra_all(pl, b, sz, d_K, d_V, st);
     const int nb = pl.n_cells;
     HIP_TRY(hipMemcpyAsync(d_specT, b.specT, (size_t)nb * pl.nT * 8, hipMemcpyDeviceToDevice, st));
     HIP_TRY(hipMemcpyAsync(d_specD, b.specD, (size_t)nb * pl.D * 8, hipMemcpyDeviceToDevice, st));
@@ -1106,7 +1238,7 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
     Sizes sz = sizes_worst(pl);
     Bufs b = carve(ar, pl, sz);
     const int nb = pl.n_cells;
-    spectra_all(pl, b, d_K, d_V, st);
+    spectra_all(pl, b, sz, d_K, d_V, st);
     // ---- allocation
     std::vector<int> shape(4 * nb);
     std::vector<long long> offT(nb + 1), offD(nb + 1);

@@ -79,7 +79,8 @@ __device__ void bisect_all(int n, const double *d, const double *e, double *smem
 // Householder tridiagonalisation + all eigenvalues by bisection.
 // A: [batch][n][lda] fp64 symmetric (overwritten).  Output per batch: d[n], e[n] (e[n-1]=0),
 // reflectors refl[n][n] (row k holds v_k for rows k+1.., v_k[0] = 1), beta[n],
-// evals[n] descending (clamped at >= 0 when clamp != 0).
+// evals[n] descending (clamped at >= 0 when clamp != 0).  The working copy lives in LDS
+// (n^2 + 2n doubles), so this kernel serves n <= 136.
 // ---------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long a_bs, int lda, const int *n_of,
                                                             int n_fixed, double *d_out, double *e_out,
@@ -94,22 +95,12 @@ __global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long
   double *Ag = A + b * a_bs;
   double *d = d_out + b * t_bs, *e = e_out + b * t_bs, *R = refl + b * t_bs * (long long)n_fixed,
          *be = beta + b * t_bs;
-  // working copy: LDS if it fits, else in place in global memory
-  double *W;
-  int ldw;
-  double *vbuf, *pbuf;
-  if (use_lds) {
-    W = smem;
-    ldw = n;
-    vbuf = smem + (long long)n * n;
-    pbuf = vbuf + n;
-    for (int i = tid; i < n * n; i += nt) W[i] = Ag[(long long)(i / n) * lda + (i % n)];
-  } else {
-    W = Ag;
-    ldw = lda;
-    vbuf = smem;
-    pbuf = smem + n;
-  }
+  // working copy in LDS (matrices that do not fit take tridiag_fused_kernel)
+  (void)use_lds;
+  double *W = smem;
+  const int ldw = n;
+  double *vbuf = smem + (long long)n * n, *pbuf = vbuf + n;
+  for (int i = tid; i < n * n; i += nt) W[i] = Ag[(long long)(i / n) * lda + (i % n)];
   __syncthreads();
 
   for (int k = 0; k + 2 < n; ++k) {
@@ -690,28 +681,37 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
   __syncthreads();
   for (int k0 = 0; k0 < n; k0 += CNB) {
     const int kb = min(CNB, n - k0), rem = n - k0 - kb;
-    // (1) diagonal block (unblocked right-looking Cholesky in LDS)
-    for (int idx = tid; idx < kb * kb; idx += nt) {
-      int i = idx / kb, j = idx % kb;
-      Dk[i * 33 + j] = (j >= i) ? A[(long long)(k0 + i) * n + k0 + j] : 0.0;
+    // (1) diagonal block: unblocked right-looking Cholesky by wave 0 alone, lane c holding column
+    //     c of the block in registers; row j of the factor reaches the other lanes by shuffles,
+    //     so the 32 sequential steps need no workgroup barrier
+    if (wave == 0) {
+      const int c = lane;
+      double a[CNB];
+#pragma unroll
+      for (int r = 0; r < CNB; ++r) a[r] = (c < kb && r <= c && r < kb) ? A[(long long)(k0 + r) * n + k0 + c] : 0.0;
+#pragma unroll
+      for (int j = 0; j < CNB; ++j) {
+        if (j < kb) {
+          const double piv = sqrt(fmax(__shfl(a[j], j, 64), floor_piv));
+          if (c == j) a[j] = piv;
+          else if (c > j) a[j] /= piv;  // row j of R, column c
+#pragma unroll
+          for (int r = j + 1; r < CNB; ++r) {
+            const double rjr = __shfl(a[j], r, 64);  // R[j][r], held by lane r
+            if (r <= c) a[r] -= rjr * a[j];
+          }
+        }
+      }
+      if (c < CNB) {
+#pragma unroll
+        for (int r = 0; r < CNB; ++r) {
+          const double v = (r <= c) ? a[r] : 0.0;
+          Dk[r * 33 + c] = v;
+          if (c < kb && r < kb) A[(long long)(k0 + r) * n + k0 + c] = v;
+        }
+      }
     }
     __syncthreads();
-    for (int j = 0; j < kb; ++j) {
-      if (tid == 0) Dk[j * 33 + j] = sqrt(fmax(Dk[j * 33 + j], floor_piv));
-      __syncthreads();
-      const double piv = Dk[j * 33 + j];
-      for (int c = j + 1 + tid; c < kb; c += nt) Dk[j * 33 + c] /= piv;
-      __syncthreads();
-      for (int idx = tid; idx < kb * kb; idx += nt) {
-        int r = idx / kb, c = idx % kb;
-        if (r > j && c >= r) Dk[r * 33 + c] -= Dk[j * 33 + r] * Dk[j * 33 + c];
-      }
-      __syncthreads();
-    }
-    for (int idx = tid; idx < kb * kb; idx += nt) {
-      int i = idx / kb, j = idx % kb;
-      A[(long long)(k0 + i) * n + k0 + j] = (j >= i) ? Dk[i * 33 + j] : 0.0;
-    }
     // (2) panel: R[k0.., c] = R_kk^{-T} A[k0.., c], forward substitution per column
     for (int c = tid; c < rem; c += nt) {
       double x[CNB];
@@ -731,34 +731,40 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
         }
     }
     __syncthreads();
-    // (3) trailing update A22 -= panel^T panel (upper triangle), 4 x 4 register blocks
+    // (3) trailing update A22 -= panel^T panel (upper triangle), 4 x 4 register blocks; the panel
+    //     is read from LDS or from global memory by separate loops (a pointer that may be either
+    //     would compile to flat loads)
     const int nb4 = (rem + 3) / 4;
-    for (int blk = tid; blk < nb4 * nb4; blk += nt) {
-      const int bi = blk / nb4, bj = blk % nb4;
-      if (bj < bi) continue;
-      double acc[4][4] = {};
-      for (int q = 0; q < kb; ++q) {
-        double u[4], v[4];
-        const double *src = in_lds ? P + q * rem : A + (long long)(k0 + q) * n + k0 + kb;
+    auto trailing = [&](const double *pan, long long pan_ld) __attribute__((always_inline)) {
+      for (int blk = tid; blk < nb4 * nb4; blk += nt) {
+        const int bi = blk / nb4, bj = blk % nb4;
+        if (bj < bi) continue;
+        double acc[4][4] = {};
+        for (int q = 0; q < kb; ++q) {
+          double u[4], v[4];
+          const double *src = pan + q * pan_ld;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int ii = bi * 4 + t, jj = bj * 4 + t;
-          u[t] = (ii < rem) ? src[ii] : 0.0;
-          v[t] = (jj < rem) ? src[jj] : 0.0;
+          for (int t = 0; t < 4; ++t) {
+            const int ii = bi * 4 + t, jj = bj * 4 + t;
+            u[t] = (ii < rem) ? src[ii] : 0.0;
+            v[t] = (jj < rem) ? src[jj] : 0.0;
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) acc[t][w] += u[t] * v[w];
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
-          for (int w = 0; w < 4; ++w) acc[t][w] += u[t] * v[w];
+          for (int w = 0; w < 4; ++w) {
+            const int ii = bi * 4 + t, jj = bj * 4 + w;
+            if (ii < rem && jj < rem && jj >= ii) A[(long long)(k0 + kb + ii) * n + k0 + kb + jj] -= acc[t][w];
+          }
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int ii = bi * 4 + t, jj = bj * 4 + w;
-          if (ii < rem && jj < rem && jj >= ii) A[(long long)(k0 + kb + ii) * n + k0 + kb + jj] -= acc[t][w];
-        }
-    }
+    };
+    if (in_lds) trailing(P, rem);
+    else trailing(A + (long long)k0 * n + k0 + kb, n);
     __syncthreads();
   }
   // ---- X = R^{-1}: block rows from the bottom ----------------------------------------------
