@@ -703,9 +703,6 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
   size_t o_rT = u.add(rTv.data(), nb * 4), o_rd = u.add(rdv.data(), nb * 4), o_fc = u.add(fc.data(), nb * sizeof(FactorCell));
   std::vector<size_t> rot_offs;
   upload_rotation(pl, b, u, rot_offs);
-  // encode cells (b > 0)
-  std::vector<EncCell> enc;
-  std::vector<EncCell> encv;
   upload(b, u, st);
   int *d_rT = (int *)(b.params + o_rT), *d_rd = (int *)(b.params + o_rd);
   FactorCell *d_fc = (FactorCell *)(b.params + o_fc);
@@ -825,14 +822,14 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     const CellPick &p = picks[c];
     if (p.bits == 0) continue;
     const int s = c / (2 * pl.n_groups), g = (c / 2) % pl.n_groups, t = c % 2;
-    const char *Xb = (const char *)(t == 0 ? K : V);
     EncCell e;
-    e.X = Xb + ((long long)s * pl.n_groups + g) * cellX * pl.c;
-    e.UT = out + p.off + p.sec.off_UT;
-    e.Bcat = b.Bcat + (long long)c * GH * D * sz.Kb;
-    e.b_amax = b.bamax + c;
-    e.scales = (float *)(out + p.off + p.sec.off_scales);
-    e.codes = (uint8_t *)(out + p.off + p.sec.off_codes);
+    e.x_off = ((long long)s * pl.n_groups + g) * cellX * pl.c;
+    e.kv = t;
+    e.ut_off = p.off + p.sec.off_UT;
+    e.sc_off = p.off + p.sec.off_scales;
+    e.cd_off = p.off + p.sec.off_codes;
+    e.bcat_off = (long long)c * GH * D * sz.Kb * 4;
+    e.am_idx = c;
     e.GH = GH; e.rT = p.rT; e.bits = p.bits; e.Kb = sz.Kb;
     ec.push_back(e);
   }
@@ -845,7 +842,10 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
   HIP_TRY(hipMemcpyAsync(dst, u2.host.data(), u2.host.size(), hipMemcpyHostToDevice, st));
   {
     Stage prof("residual_encode", st);
-    encode_cells(pl.dtype, (const EncCell *)(dst + o_ec), (int)ec.size(), pl.T, D, GH, st);
+    EncArgs ea;
+    ea.xk = (const char *)K; ea.xv = (const char *)V; ea.utb = out; ea.scb = out; ea.cdb = out;
+    ea.bcat = (const char *)b.Bcat; ea.bamax = b.bamax; ea.cells = (const EncCell *)(dst + o_ec);
+    encode_cells(pl.dtype, ea, (int)ec.size(), pl.T, D, GH, st);
   }
 }
 
@@ -1417,6 +1417,9 @@ int jolt_encode_residual(const void *d_X, int32_t G, int32_t H, int32_t T, int32
     JOLT_REQUIRE(dtype == JOLT_F16 || dtype == JOLT_BF16 || dtype == JOLT_F32, JOLT_EINVAL, "bad dtype");
     JOLT_REQUIRE(rT >= 8 && rT % 8 == 0 && rT <= T && rd >= 8 && rd % 8 == 0 && rd <= D, JOLT_EINVAL, "bad ranks");
     JOLT_REQUIRE(bits >= 1 && bits <= 8, JOLT_EINVAL, "bits must lie in 1..8");
+    JOLT_REQUIRE(((uintptr_t)d_X % 16) == 0 && ((uintptr_t)d_UT % 16) == 0 && ((uintptr_t)d_scales % 4) == 0 &&
+                     ((uintptr_t)d_codes % 4) == 0,
+                 JOLT_EINVAL, "X and U_T must be 16-byte aligned, scales and codes 4-byte aligned");
     JOLT_REQUIRE(d_ws != nullptr && ws_bytes >= jolt_encode_residual_workspace_bytes(G, H, T, D, rT, rd),
                  JOLT_EWORKSPACE, "workspace too small");
     hipStream_t st = S(stream);
@@ -1442,7 +1445,7 @@ int jolt_encode_residual(const void *d_X, int32_t G, int32_t H, int32_t T, int32
       for (int j = 0; j < D; ++j) qt[(size_t)j * D + i] = (float)Q[(size_t)i * D + j];
     size_t o_qt = u.add(qt.data(), qt.size() * 4);
     EncCell e;
-    e.X = d_X; e.UT = d_UT; e.Bcat = Bcat; e.b_amax = am; e.scales = d_scales; e.codes = d_codes;
+    memset(&e, 0, sizeof(e));
     e.GH = GH; e.rT = rT; e.bits = bits; e.Kb = Kb;
     size_t o_ec = u.add(&e, sizeof(e));
     HIP_TRY(hipMemcpyAsync(pa, u.host.data(), u.host.size(), hipMemcpyHostToDevice, st));
@@ -1465,7 +1468,10 @@ int jolt_encode_residual(const void *d_X, int32_t G, int32_t H, int32_t T, int32
     h.alpha = -1.f;
     gemm(MF_F16, SRC_F32, true, SRC_F32, true, h, GH, 1, st);
     amax_cells(Bcat, (long long)GH * D * Kb, 0, 1, am, st);
-    encode_cells(dtype, (const EncCell *)(pa + o_ec), 1, T, D, GH, st);
+    EncArgs ea;
+    ea.xk = ea.xv = (const char *)d_X; ea.utb = (const char *)d_UT; ea.scb = (char *)d_scales;
+    ea.cdb = (char *)d_codes; ea.bcat = (const char *)Bcat; ea.bamax = am; ea.cells = (const EncCell *)(pa + o_ec);
+    encode_cells(dtype, ea, 1, T, D, GH, st);
     return 0;
   });
 }

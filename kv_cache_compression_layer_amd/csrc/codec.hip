@@ -1,6 +1,6 @@
 // Residual codec of the method (Sec. 3, "Rotated low-bit residual"): fused encode and decode.
 //
-// Encode, per cell, per head-slice j = (l, h) and 128-token tile:
+// Encode, per cell, per head-slice j = (l, h) and 256-token tile:
 //   E_rot = (X_j - U_T D_j) Q = [X_j | U_T] [Q ; -D_j Q]     (one MFMA pass, K = d_h + r_T)
 //   per row: absmax (wavefront + cross-wave reduction), s = absmax / q_max (fp32),
 //   code = clamp(rint(e / s)), packed b bits per element LSB-first, one fp32 scale per row.
@@ -73,134 +73,242 @@ __device__ __forceinline__ void csplit(float x, float scale, uint16_t (&p)[3]) {
 }
 
 // ------------------------------------------------------------------------------------------ encode
-template <int MF, int SX, int NB16>
-__global__ void __launch_bounds__(NT) encode_kernel(const EncCell *cells, int T, int D, int ttiles) {
-  constexpr int PA = CPlanes<SX, MF, NB16>::n;
-  constexpr int PB = CPlanes<SRC_F32, MF, NB16>::n;
-  constexpr int MAXO = (MF == MF_F16) ? (NB16 - 1) : 2;
-  constexpr int ASZ = PA * BM * LDK, BSZ = PB * BN * LDK, STG = ASZ + BSZ;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STG];
-  __shared__ float smax[2][BM];
-  uint8_t *ucode = (uint8_t *)lds;  // [BM][128] codes, reuses the tiles after the main loop
-  static_assert(2 * STG * 2 >= BM * 128, "code staging must fit in the tile buffers");
+// Tile: 256 rows (4 waves x 64 rows, each wave holding whole rows) x all D columns; the k loop runs
+// over [X_j | U_T] (D + r_T).  LDS tiles are [row][32] with the 16-byte chunks XOR-permuted by
+// (row / 2) % 4 (free of bank conflicts for fragment loads and tile stores); row pointers are fixed
+// for the k loop, full stages load without index arithmetic, the ragged last stage is bounds-checked.
+constexpr int EBM = 256, EKB = 32, ENT = 256;
 
-  const EncCell c = cells[blockIdx.z];
-  const int j = blockIdx.x / ttiles, tt = blockIdx.x % ttiles;
+__device__ __forceinline__ int eswz(int row, int chunk) { return row * EKB + ((chunk ^ (row >> 1)) & 3) * 8; }
+
+template <int S, int MF, int P>
+__device__ __forceinline__ void eput8(uint16_t *tile, int plane_elems, int off, const Raw8<S> &x, float scale) {
+  if constexpr (S != SRC_F32 && ((S == SRC_F16 && MF == MF_F16) || (S == SRC_BF16 && MF == MF_BF16))) {
+    *(uint4 *)(tile + off) = x.v;
+  } else {
+    uint16_t pl[8][3];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) split_planes<S, MF>(raw_elem<S>(x, i), scale, pl[i]);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      uint4 w;
+      w.x = pl[0][p] | ((uint32_t)pl[1][p] << 16);
+      w.y = pl[2][p] | ((uint32_t)pl[3][p] << 16);
+      w.z = pl[4][p] | ((uint32_t)pl[5][p] << 16);
+      w.w = pl[6][p] | ((uint32_t)pl[7][p] << 16);
+      *(uint4 *)(tile + p * plane_elems + off) = w;
+    }
+  }
+}
+
+template <int S>
+__device__ __forceinline__ void eload8(const char *p, bool ok, Raw8<S> &r) {
+  if constexpr (S == SRC_F32) {
+    const float4 *q = (const float4 *)p;
+    float4 x = q[0], y = q[1];
+    if (!ok) x = y = make_float4(0.f, 0.f, 0.f, 0.f);
+    r.a = x;
+    r.b = y;
+  } else {
+    uint4 x = *(const uint4 *)p;
+    if (!ok) x = make_uint4(0u, 0u, 0u, 0u);
+    r.v = x;
+  }
+}
+
+// W waves per SIMD: 2 for 16-bit caches; fp32 caches carry three planes per operand and run at 1
+template <int MF, int SX, int TN, int W = (SX == SRC_F32 ? 1 : 2)>
+__global__ void __launch_bounds__(ENT) __attribute__((amdgpu_waves_per_eu(W, W)))
+encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
+  constexpr int D = TN * 16;
+  constexpr int PA = Planes<SX, MF>::n, PB = Planes<SRC_F32, MF>::n;
+  constexpr int MAXO = (MF == MF_F16) ? 1 : 2;
+  constexpr int ASZ = PA * EBM * EKB, BSZ = PB * D * EKB, STG = ASZ + BSZ;
+  constexpr int LA = EBM * 4 / ENT, LB = D * 4 / ENT;
+  constexpr int ESX = (SX == SRC_F32) ? 4 : 2;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // 2 * STG halves
+  __shared__ float srow[EBM];
+  uint8_t *ucode = (uint8_t *)lds;  // [EBM][D] codes, reuses the tiles after the main loop
+  static_assert(2 * STG * 2 >= EBM * D, "code staging must fit in the tile buffers");
+
+  // XCD-aware order over the whole grid: consecutive (cell, slice, tile) on one XCD, so the
+  // tiles of one slice share its Bcat panel in that XCD's L2
+  int tt, j, cz;
+  {
+    const long long gx = gridDim.x, total = gx * gridDim.z;
+    long long L = blockIdx.x + gx * blockIdx.z;
+    const long long per = total / 8;
+    if (L < per * 8) L = (L % 8) * per + L / 8;
+    cz = (int)(L / gx);
+    const int x = (int)(L % gx);
+    j = x / ttiles;
+    tt = x % ttiles;
+  }
+  const EncCell c = ea.cells[cz];
   if (j >= c.GH) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int t0 = tt * BM;
-  const int K = D + c.rT;
-  const long long xoff = (long long)j * T * D;
-  const float *Bj = c.Bcat + (long long)j * D * c.Kb;
-  const float bscale = (MF == MF_F16) ? f16_split_scale(*c.b_amax) : 1.f;
+  const int tid = threadIdx.x, lane = tid & 63, wm = tid >> 6;
+  const int fr = lane & 15, fc = lane >> 4;
+  const int t0 = tt * EBM;
+  const int rT = c.rT, K = D + rT;
+  const char *xbase = (c.kv ? ea.xv : ea.xk) + c.x_off + (long long)j * T * D * ESX;
+  const char *utbase = ea.utb + c.ut_off;
+  const char *bj = ea.bcat + c.bcat_off + (long long)j * D * c.Kb * 4;
+  const float bscale = (MF == MF_F16) ? f16_split_scale(ea.bamax[c.am_idx]) : 1.f;
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][TN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < TN; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  Raw8<SX> ra[2];
-  Raw8<SRC_F32> rb[2];
-  auto gload = [&](int k0) {
+  // load slots: A rows t0 + v / 4 (X then U_T), B rows n = v / 4 of Bcat_j, chunk v % 4
+  Raw8<SX> ra[LA];
+  Raw8<SRC_F32> rb[LB];
+  long long xo[LA], uo[LA];
+  bool oka[LA];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      int v = tid + it * NT;
-      int r = v >> 2, kv = (v & 3) * 8;
-      int t = t0 + r;
-      int k = k0 + kv;
-      if (k < D) load_raw8<SX>(c.X, xoff + (long long)t * D, k, D, t < T, 1 << 30, 0, ra[it]);
-      else load_raw8<SX>(c.UT, (long long)t * c.rT, k - D, c.rT, t < T, 1 << 30, 0, ra[it]);
-      load_raw8<SRC_F32>(Bj, (long long)r * c.Kb, k0 + kv, K, r < D, 1 << 30, 0, rb[it]);
+  for (int it = 0; it < LA; ++it) {
+    const int v = tid + it * ENT, t = t0 + (v >> 2);
+    oka[it] = t < T;
+    const long long tr = oka[it] ? t : 0;
+    xo[it] = (tr * D + (v & 3) * 8) * ESX;
+    uo[it] = (tr * rT + (v & 3) * 8) * ESX;
+  }
+  auto gload_fast = [&](int k0) __attribute__((always_inline)) {
+    if (k0 < D) {
+#pragma unroll
+      for (int it = 0; it < LA; ++it) eload8<SX>(xbase + xo[it] + (long long)k0 * ESX, oka[it], ra[it]);
+    } else {
+#pragma unroll
+      for (int it = 0; it < LA; ++it) eload8<SX>(utbase + uo[it] + (long long)(k0 - D) * ESX, oka[it], ra[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < LB; ++it) {
+      const int v = tid + it * ENT;
+      eload8<SRC_F32>(bj + ((long long)(v >> 2) * c.Kb + (v & 3) * 8 + k0) * 4, true, rb[it]);
     }
   };
-  auto lstore = [&](int buf) {
+  auto gload_slow = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < LA; ++it) {
+      const int v = tid + it * ENT, t = t0 + (v >> 2), k = k0 + (v & 3) * 8;
+      if (k < D) load_raw8<SX>(xbase, (long long)t * D, k, D, t < T, 1 << 30, 0, ra[it]);
+      else load_raw8<SX>(utbase, (long long)t * rT, k - D, rT, t < T, 1 << 30, 0, ra[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < LB; ++it) {
+      const int v = tid + it * ENT;
+      load_raw8<SRC_F32>(bj, (long long)(v >> 2) * c.Kb, k0 + (v & 3) * 8, K, true, 1 << 30, 0, rb[it]);
+    }
+  };
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
     uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      int v = tid + it * NT;
-      put8<SX, MF, PA, NB16>(As, BM, v >> 2, (v & 3) * 8, ra[it], 1.f);
-      put8<SRC_F32, MF, PB, NB16>(Bs, BN, v >> 2, (v & 3) * 8, rb[it], bscale);
+    for (int it = 0; it < LA; ++it) {
+      const int v = tid + it * ENT;
+      eput8<SX, MF, PA>(As, EBM * EKB, eswz(v >> 2, v & 3), ra[it], 1.f);
+    }
+#pragma unroll
+    for (int it = 0; it < LB; ++it) {
+      const int v = tid + it * ENT;
+      eput8<SRC_F32, MF, PB>(Bs, D * EKB, eswz(v >> 2, v & 3), rb[it], bscale);
+    }
+  };
+  const int aoff = eswz(wm * 64 + fr, fc), boff = eswz(fr, fc);
+  // plane products in the order (pa, pb) descending, as in the GEMM kernels; B fragments are
+  // loaded per plane so only one plane is live
+  auto compute = [&](int buf) __attribute__((always_inline)) {
+    const uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
+#pragma unroll
+    for (int pa = PA - 1; pa >= 0; --pa) {
+      uint4 af[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *(const uint4 *)(As + pa * EBM * EKB + i * 16 * EKB + aoff);
+#pragma unroll
+      for (int pb = PB - 1; pb >= 0; --pb) {
+        if (pa + pb > MAXO) continue;
+        uint4 bf[TN];
+#pragma unroll
+        for (int q = 0; q < TN; ++q) bf[q] = *(const uint4 *)(Bs + pb * D * EKB + q * 16 * EKB + boff);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < TN; ++q) acc[i][q] = mfma<MF>(af[i], bf[q], acc[i][q]);
+      }
     }
   };
 
-  gload(0);
+  const int nsteps = (K + EKB - 1) / EKB, nfull = K / EKB;
+  if (nfull > 0) gload_fast(0);
+  else gload_slow(0);
   lstore(0);
   __syncthreads();
-  int buf = 0;
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    const bool more = k0 + BK < K;
-    if (more) gload(k0 + BK);
-    mma_step<MF, PA, PB, MAXO>(lds + buf * STG, lds + buf * STG + ASZ, wm, wn, lane, acc);
+  int buf = 0, s = 0;
+  for (; s + 1 < nfull; ++s) {
+    gload_fast((s + 1) * EKB);
+    compute(buf);
+    lstore(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  for (; s < nsteps; ++s) {
+    const bool more = s + 1 < nsteps;
+    if (more) gload_slow((s + 1) * EKB);
+    compute(buf);
     if (more) lstore(buf ^ 1);
     __syncthreads();
     buf ^= 1;
   }
 
-  // ---- quantisation epilogue -------------------------------------------------------------
+  // ---- quantisation: rows are whole inside a wave -------------------------------------------
   const float inv = 1.f / bscale;
   const int b = c.bits;
   const int qm = (b >= 2) ? ((1 << (b - 1)) - 1) : 1;
-  const int fr = lane & 15;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float m = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int n = wn * 64 + q * 16 + fr;
-        float v = acc[i][q][r] * inv;
+      for (int q = 0; q < TN; ++q) {
+        const float v = acc[i][q][r] * inv;
         acc[i][q][r] = v;
-        if (n < D) m = fmaxf(m, fabsf(v));
+        m = fmaxf(m, fabsf(v));
       }
       m = fmaxf(m, __shfl_xor(m, 1, 64));
       m = fmaxf(m, __shfl_xor(m, 2, 64));
       m = fmaxf(m, __shfl_xor(m, 4, 64));
       m = fmaxf(m, __shfl_xor(m, 8, 64));
-      if (fr == 0) smax[wn][wm * 64 + i * 16 + (lane >> 4) * 4 + r] = m;
-    }
-  __syncthreads();
+      const int row = wm * 64 + i * 16 + fc * 4 + r;
+      const float sc = (b == 1) ? m : m / (float)qm;
+      if (fr == 0) srow[row] = sc;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-      const float amax = fmaxf(smax[0][row], smax[1][row]);
-      const float s = (b == 1) ? amax : amax / (float)qm;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        int n = wn * 64 + q * 16 + fr;
-        if (n < D) {
-          float v = acc[i][q][r];
-          int u;
-          if (b == 1) u = (v >= 0.f) ? 1 : 0;
-          else if (s > 0.f) {
-            float qv = rintf(v / s);
-            qv = fminf(fmaxf(qv, (float)-qm), (float)qm);
-            u = (int)qv + qm;
-          } else u = qm;
-          ucode[row * 128 + n] = (uint8_t)u;
-        }
+      for (int q = 0; q < TN; ++q) {
+        const float v = acc[i][q][r];
+        int u;
+        if (b == 1) u = (v >= 0.f) ? 1 : 0;
+        else if (sc > 0.f) {
+          float qv = rintf(v / sc);
+          qv = fminf(fmaxf(qv, (float)-qm), (float)qm);
+          u = (int)qv + qm;
+        } else u = qm;
+        ucode[row * D + q * 16 + fr] = (uint8_t)u;
       }
     }
   __syncthreads();
   const long long row0 = (long long)j * T + t0;
-  const int nrows = min(BM, T - t0);
-  for (int rr = tid; rr < nrows; rr += NT) {
-    float amax = fmaxf(smax[0][rr], smax[1][rr]);
-    c.scales[row0 + rr] = (b == 1) ? amax : amax / (float)qm;
-  }
+  const int nrows = min(EBM, T - t0);
+  float *scales = (float *)(ea.scb + c.sc_off);
+  for (int rr = tid; rr < nrows; rr += ENT) scales[row0 + rr] = srow[rr];
   const int wpr = D * b / 32;  // 32-bit words per row (D in {64,128}: integral)
-  uint32_t *out = (uint32_t *)(c.codes + row0 * (D * b / 8));
-  for (int w = tid; w < nrows * wpr; w += NT) {
+  uint32_t *out = (uint32_t *)(ea.cdb + c.cd_off + row0 * (D * b / 8));
+  for (int w = tid; w < nrows * wpr; w += ENT) {
     const int rr = w / wpr, wi = w % wpr;
     const int bit0 = wi * 32;
     const int e0 = bit0 / b, e1 = min(D - 1, (bit0 + 31) / b);
     uint32_t word = 0;
     for (int e = e0; e <= e1; ++e) {
-      uint32_t u = ucode[rr * 128 + e];
+      uint32_t u = ucode[rr * D + e];
       int pos = e * b - bit0;
       if (pos >= 0) word |= (pos < 32) ? (u << pos) : 0u;
       else word |= u >> (-pos);
@@ -360,10 +468,20 @@ __global__ void __launch_bounds__(NT) decode_kernel(const DecCell *cells, int T,
     }
 }
 
-template <int MF, int SX, int NB16>
-void launch_enc(const EncCell *cells, int ncells, int T, int D, int GHmax, hipStream_t st) {
-  int tt = (T + BM - 1) / BM;
-  hipLaunchKernelGGL((encode_kernel<MF, SX, NB16>), dim3(tt * GHmax, 1, ncells), dim3(NT), 0, st, cells, T, D, tt);
+template <int MF, int SX, int TN>
+void launch_enc(const EncArgs &a, int ncells, int T, int GHmax, hipStream_t st) {
+  constexpr int D = TN * 16;
+  constexpr int PA = Planes<SX, MF>::n, PB = Planes<SRC_F32, MF>::n;
+  constexpr size_t shm = 2 * (size_t)(PA * EBM * EKB + PB * D * EKB) * 2;
+  static bool attr = false;  // allow the dynamic LDS size once
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void *)encode_kernel<MF, SX, TN>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)shm);
+    (void)hipGetLastError();
+    attr = true;
+  }
+  const int tt = (T + EBM - 1) / EBM;
+  hipLaunchKernelGGL((encode_kernel<MF, SX, TN>), dim3(tt * GHmax, 1, ncells), dim3(ENT), shm, st, a, T, tt, GHmax);
 }
 template <int MF, int SX, int NB16>
 void launch_dec(const DecCell *cells, int ncells, int T, int D, int GHmax, hipStream_t st) {
@@ -373,11 +491,18 @@ void launch_dec(const DecCell *cells, int ncells, int T, int D, int GHmax, hipSt
 
 }  // namespace
 
-void encode_cells(int dtype, const EncCell *d_cells, int ncells, int T, int D, int GHmax, hipStream_t st) {
+void encode_cells(int dtype, const EncArgs &a, int ncells, int T, int D, int GHmax, hipStream_t st) {
   JOLT_REQUIRE(D == 64 || D == 128, JOLT_EINVAL, "codec: d_head must be 64 or 128");
-  if (dtype == JOLT_F16) launch_enc<MF_F16, SRC_F16, 2>(d_cells, ncells, T, D, GHmax, st);
-  else if (dtype == JOLT_BF16) launch_enc<MF_BF16, SRC_BF16, 2>(d_cells, ncells, T, D, GHmax, st);
-  else launch_enc<MF_BF16, SRC_F32, 2>(d_cells, ncells, T, D, GHmax, st);
+  if (ncells <= 0) return;
+  if (D == 128) {
+    if (dtype == JOLT_F16) launch_enc<MF_F16, SRC_F16, 8>(a, ncells, T, GHmax, st);
+    else if (dtype == JOLT_BF16) launch_enc<MF_BF16, SRC_BF16, 8>(a, ncells, T, GHmax, st);
+    else launch_enc<MF_BF16, SRC_F32, 8>(a, ncells, T, GHmax, st);
+  } else {
+    if (dtype == JOLT_F16) launch_enc<MF_F16, SRC_F16, 4>(a, ncells, T, GHmax, st);
+    else if (dtype == JOLT_BF16) launch_enc<MF_BF16, SRC_BF16, 4>(a, ncells, T, GHmax, st);
+    else launch_enc<MF_BF16, SRC_F32, 4>(a, ncells, T, GHmax, st);
+  }
   HIP_LAUNCH_CHECK();
 }
 

@@ -4,16 +4,25 @@
 
 namespace jolt {
 
-// One cell of the encode pass.  Bcat[j][n][k] (fp32, row pitch Kb): k < D -> Q[k][n];
-// D <= k < D + rT -> -(D_j Q)[k - D][n].  b_amax: device max |Bcat| (fp16 split scale).
+// One cell of the encode pass, as byte offsets from the bases in EncArgs (so that every address
+// the kernel forms derives from a kernel argument and compiles to global memory instructions).
+// Bcat[j][n][k] (fp32, row pitch Kb): k < D -> Q[k][n]; D <= k < D + rT -> -(D_j Q)[k - D][n].
 struct EncCell {
-  const void *X;      // [GH][T][D] cache dtype
-  const void *UT;     // [T][rT] storage dtype
-  const float *Bcat;  // [GH][D][Kb]
-  const float *b_amax;
-  float *scales;      // [GH*T]
-  uint8_t *codes;     // [GH*T][D*bits/8]
+  long long x_off;     // cache slice [GH][T][D] (cache dtype) in xk (kv == 0) or xv (kv == 1)
+  long long ut_off;    // U_T [T][rT] (cache dtype) in utb
+  long long sc_off;    // fp32 scales [GH*T] in scb
+  long long cd_off;    // codes [GH*T][D*bits/8] in cdb
+  long long bcat_off;  // Bcat [GH][D][Kb] in bcat (bytes)
+  int kv, am_idx;      // cache selector; index of max |Bcat| in bamax (fp16 split scale)
   int GH, rT, bits, Kb;
+};
+
+struct EncArgs {
+  const char *xk, *xv, *utb;
+  char *scb, *cdb;
+  const char *bcat;
+  const float *bamax;
+  const EncCell *cells;
 };
 
 // One cell of the decode pass.  Dm[j][n][r] = D_j[r][n] (fp32, row pitch Kd); Q row-major.
@@ -28,7 +37,7 @@ struct DecCell {
   int GH, rT, bits, Kd;
 };
 
-void encode_cells(int dtype, const EncCell *d_cells, int ncells, int T, int D, int GHmax, hipStream_t st);
+void encode_cells(int dtype, const EncArgs &a, int ncells, int T, int D, int GHmax, hipStream_t st);
 void decode_cells(int dtype, const DecCell *d_cells, int ncells, int T, int D, int GHmax, hipStream_t st);
 
 }  // namespace jolt
