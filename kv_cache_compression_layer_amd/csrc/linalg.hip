@@ -30,48 +30,76 @@ __device__ double block_sum(double v, double *red) {
   return s;
 }
 
-// All eigenvalues of the symmetric tridiagonal (d, e) by Sturm-sequence bisection (one thread
-// per eigenvalue, descending order into ev; d and e^2 staged in LDS scratch of 2n doubles).
-__device__ void bisect_all(int n, const double *d, const double *e, double *smem, double *ev, int clamp) {
-  const int tid = threadIdx.x, nt = blockDim.x;
+// All eigenvalues of `batch` symmetric tridiagonals (d, e), descending, by multisection: a group
+// of BL lanes brackets one eigenvalue and evaluates BL Sturm counts per iteration (BL - 1 interior
+// shifts spaced evenly inside the bracket), narrowing the bracket (BL + 1)-fold per iteration.
+// Sturm recurrence with a pivot guard, Gershgorin starting interval, stop at a relative width of
+// about 2 ulp (Golub & Van Loan, Sec. 8.4).
+constexpr int BL = 16;
+
+__global__ void __launch_bounds__(256) bisect_kernel(const double *d_in, const double *e_in, long long t_bs, int n,
+                                                     double *evals, long long ev_bs, int clamp) {
+  extern __shared__ double smem[];
+  __shared__ double red[3][4];
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const double *d = d_in + b * t_bs, *e = e_in + b * t_bs;
   double *sd = smem, *se2 = smem + n;
-  for (int i = tid; i < n; i += nt) {
-    sd[i] = d[i];
-    se2[i] = (i + 1 < n) ? e[i] * e[i] : 0.0;
+  double lo0 = 1e300, hi0 = -1e300;
+  for (int i = tid; i < n; i += 256) {
+    const double di = d[i], ei = (i + 1 < n) ? e[i] : 0.0, ep = (i > 0) ? e[i - 1] : 0.0;
+    sd[i] = di;
+    se2[i] = ei * ei;
+    const double r = fabs(ep) + fabs(ei);
+    lo0 = fmin(lo0, di - r);
+    hi0 = fmax(hi0, di + r);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    lo0 = fmin(lo0, __shfl_xor(lo0, o, 64));
+    hi0 = fmax(hi0, __shfl_xor(hi0, o, 64));
+  }
+  if (lane == 0) {
+    red[0][wave] = lo0;
+    red[1][wave] = hi0;
   }
   __syncthreads();
-  double lo0 = 1e300, hi0 = -1e300, tn = 0.0;
-  for (int i = 0; i < n; ++i) {
-    double r = (i > 0 ? sqrt(se2[i - 1]) : 0.0) + (i + 1 < n ? sqrt(se2[i]) : 0.0);
-    lo0 = fmin(lo0, sd[i] - r);
-    hi0 = fmax(hi0, sd[i] + r);
-  }
-  tn = fmax(fabs(lo0), fabs(hi0));
+  lo0 = fmin(fmin(red[0][0], red[0][1]), fmin(red[0][2], red[0][3]));
+  hi0 = fmax(fmax(red[1][0], red[1][1]), fmax(red[1][2], red[1][3]));
+  const double tn = fmax(fabs(lo0), fabs(hi0));
   const double pivmin = fmax(1e-300, 1e-300 * tn * tn);
   lo0 -= 2.2e-16 * tn * 4 + pivmin;
   hi0 += 2.2e-16 * tn * 4 + pivmin;
-  for (int j = tid; j < n; j += nt) {
-    const int s = n - 1 - j;  // j-th largest == s-th smallest (0-based)
-    double lo = lo0, hi = hi0;
-    for (int it = 0; it < 200; ++it) {
-      double mid = 0.5 * (lo + hi);
-      if (mid <= lo || mid >= hi) break;
-      if (hi - lo <= 2.2e-16 * fmax(fabs(lo), fabs(hi)) * 2 + pivmin) break;
-      int cnt = 0;
-      double q = sd[0] - mid;
+  const int g = lane / BL, l = lane % BL;
+  const int j = (blockIdx.x * 256 + tid) / BL;  // eigenvalue index (descending)
+  if (j >= n) return;
+  const int s = n - 1 - j;                     // j-th largest == s-th smallest
+  double lo = lo0, hi = hi0;
+  for (int it = 0; it < 200; ++it) {
+    if (hi - lo <= 2.2e-16 * fmax(fabs(lo), fabs(hi)) * 2 + pivmin) break;
+    const double x = lo + (hi - lo) * (double)(l + 1) / (double)(BL + 1);
+    int cnt = 0;
+    double q = sd[0] - x;
+    if (fabs(q) < pivmin) q = -pivmin;
+    cnt += (q < 0.0);
+    for (int i = 1; i < n; ++i) {
+      q = (sd[i] - x) - se2[i - 1] / q;
       if (fabs(q) < pivmin) q = -pivmin;
       cnt += (q < 0.0);
-      for (int i = 1; i < n; ++i) {
-        q = (sd[i] - mid) - se2[i - 1] / q;
-        if (fabs(q) < pivmin) q = -pivmin;
-        cnt += (q < 0.0);
-      }
-      if (cnt <= s) lo = mid;
-      else hi = mid;
     }
+    // first lane of the group whose count exceeds s: the eigenvalue lies in (x_{P-1}, x_P]
+    const unsigned long long over = __ballot(cnt > s);
+    const unsigned grp = (unsigned)((over >> (g * BL)) & ((1ull << BL) - 1ull));
+    const int P = grp ? __builtin_ctz(grp) : BL;
+    const double w = hi - lo;
+    const double nlo = (P > 0) ? lo + w * (double)P / (double)(BL + 1) : lo;
+    const double nhi = (P < BL) ? lo + w * (double)(P + 1) / (double)(BL + 1) : hi;
+    if (!(nlo > lo || nhi < hi)) break;  // no progress at this precision
+    lo = nlo;
+    hi = nhi;
+  }
+  if (l == 0) {
     double v = 0.5 * (lo + hi);
     if (clamp && v < 0.0) v = 0.0;
-    ev[j] = v;
+    evals[b * ev_bs + j] = v;
   }
 }
 
@@ -175,9 +203,9 @@ __global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long
     e[n - 1] = 0.0;
     be[n - 1] = 0.0;
   }
-  __syncthreads();
-
-  bisect_all(n, d, e, smem, evals + b * ev_bs, clamp);
+  (void)evals;
+  (void)ev_bs;
+  (void)clamp;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -421,8 +449,9 @@ __global__ void __launch_bounds__(LT) tridiag_fused_kernel(double *A, long long 
     be[0] = 0.0;
     be[n - 1] = 0.0;
   }
-  __syncthreads();
-  bisect_all(n, d, e, smem, evals + b * ev_bs, clamp);
+  (void)evals;
+  (void)ev_bs;
+  (void)clamp;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -436,7 +465,6 @@ __global__ void __launch_bounds__(LT) invit_kernel(const double *d_in, const dou
                                                    double *work, long long w_bs, int kmax) {
   extern __shared__ double smem[];
   __shared__ double red[LT / 64];
-  __shared__ int cl_start[2];
   const int b = blockIdx.x;
   const int n = n_of ? n_of[b] : n_fixed;
   const int k = min(k_of[b], n);
@@ -544,13 +572,11 @@ __global__ void __launch_bounds__(LT) invit_kernel(const double *d_in, const dou
   // cluster re-orthogonalisation (sequential over vectors, parallel over entries)
   const double ctol = 1e-7 * fmax(tn, 1e-300);
   for (int j = 1; j < k; ++j) {
-    if (tid == 0) {
-      int s = j;
-      while (s > 0 && fabs(ev[s - 1] - ev[s]) <= ctol) --s;
-      cl_start[0] = s;
-    }
-    __syncthreads();
-    const int s = cl_start[0];
+    // start of j's cluster, found by every thread (uniform); vectors outside a cluster are final
+    // already and need no barrier
+    if (fabs(ev[j - 1] - ev[j]) > ctol) continue;
+    int s = j;
+    while (s > 0 && fabs(ev[s - 1] - ev[s]) <= ctol) --s;
     if (s < j) {
       double *zj = Zb + (long long)j * n;
       for (int pass = 0; pass < 2; ++pass) {
@@ -942,6 +968,7 @@ void ensure_lds_attrs() {
   (void)hipFuncSetAttribute((const void *)chol_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_values_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipFuncSetAttribute((const void *)bisect_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)backtransform_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipGetLastError();
   done = true;
@@ -965,6 +992,12 @@ void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d
     hipLaunchKernelGGL(tridiag_fused_kernel, dim3(batch), dim3(LT), shm, st, A, a_bs, lda, n, d, e, refl, beta, t_bs,
                        evals, ev_bs, clamp ? 1 : 0);
   }
+  HIP_LAUNCH_CHECK();
+  // eigenvalues of the tridiagonals: BL lanes per eigenvalue, 256 / BL eigenvalues per block
+  const size_t bshm = 2 * (size_t)n * sizeof(double);
+  JOLT_REQUIRE(bshm <= 150 * 1024, JOLT_EINVAL, "eigensolver: n too large for the bisection");
+  dim3 bgrid((unsigned)(((long long)n * BL + 255) / 256), batch);
+  hipLaunchKernelGGL(bisect_kernel, bgrid, dim3(256), bshm, st, d, e, t_bs, n, evals, ev_bs, clamp ? 1 : 0);
   HIP_LAUNCH_CHECK();
 }
 
