@@ -459,7 +459,9 @@ __global__ void __launch_bounds__(LT) tridiag_fused_kernel(double *A, long long 
 // eigenvector, rows of Z [k][n] (fp64).  Work arrays interleaved [i][j] for coalescing.
 // Then clusters (relative gap <= 1e-7 ||T||) are re-orthogonalised by two passes of Gram-Schmidt.
 // ---------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(LT) invit_kernel(const double *d_in, const double *e_in, long long t_bs,
+constexpr int IT = 512;  // threads of the inverse-iteration kernel (one eigenvector each)
+
+__global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const double *e_in, long long t_bs,
                                                    const double *evals_all, long long ev_bs, const int *k_of,
                                                    const int *n_of, int n_fixed, double *Z, long long z_bs,
                                                    double *work, long long w_bs, int kmax) {
@@ -481,9 +483,11 @@ __global__ void __launch_bounds__(LT) invit_kernel(const double *d_in, const dou
   const double tiny = fmax(tn * 1e-15, 1e-300);
   double *Zb = Z + b * z_bs;
   double *wb = work + b * w_bs;
-  // work layout: u0,u1,u2 (upper bands) and x, each [n][kmax]
+  // work layout: u0, u1, u2 (upper bands), multipliers, two iterate buffers, each [n][kmax];
+  // then the pivot flags
   double *U0 = wb, *U1 = wb + (long long)n * kmax, *U2 = wb + 2LL * n * kmax, *Xv = wb + 3LL * n * kmax;
-  unsigned char *piv = (unsigned char *)(wb + 4LL * n * kmax);
+  double *Za = wb + 4LL * n * kmax, *Zb2 = wb + 5LL * n * kmax;
+  unsigned char *piv = (unsigned char *)(wb + 6LL * n * kmax);
   for (int j = tid; j < k; j += nt) {
     const double lam = ev[j];
     // factor P (T - lam I) = L U with partial pivoting; L multipliers applied on the fly, so
@@ -525,47 +529,115 @@ __global__ void __launch_bounds__(LT) invit_kernel(const double *d_in, const dou
     U0[(long long)(n - 1) * kmax + j] = (a == 0.0) ? tiny : a;
     U1[(long long)(n - 1) * kmax + j] = 0.0;
     U2[(long long)(n - 1) * kmax + j] = 0.0;
-    // multipliers live in Xv; keep them in Z row temporarily (Z row j is the output vector)
-    double *z = Zb + (long long)j * n;
+    // iterate on vectors stored interleaved ([i][kmax], coalesced across threads), alternating
+    // between two buffers so that loads never wait on this thread's own stores
+    double *__restrict__ za = Za;
+    double *__restrict__ zb = Zb2;
     // start vector: deterministic pseudo-random, entries in (0.5, 1.5)
     for (int i = 0; i < n; ++i) {
       uint64_t h = (uint64_t)(i + 1) * 0x9E3779B97F4A7C15ull ^ (uint64_t)(j + 7) * 0xBF58476D1CE4E5B9ull;
       h ^= h >> 31;
       h *= 0x94D049BB133111EBull;
       h ^= h >> 29;
-      z[i] = 0.5 + (double)(h >> 11) * (1.0 / 9007199254740992.0);
+      za[(long long)i * kmax + j] = 0.5 + (double)(h >> 11) * (1.0 / 9007199254740992.0);
     }
     for (int iter = 0; iter < 3; ++iter) {
-      // apply L^{-1} P
-      for (int i = 0; i < n - 1; ++i) {
-        double l = Xv[(long long)i * kmax + j];
-        if (piv[(long long)i * kmax + j]) {
-          double t = z[i];
-          z[i] = z[i + 1];
-          z[i + 1] = t - l * z[i];
-        } else {
-          z[i + 1] -= l * z[i];
+      // apply L^{-1} P: za -> zb (the running entry stays in a register); the operands of the
+      // next IP steps are loaded while the current ones are used
+      constexpr int IP = 4;
+      double cur = za[j];
+      {
+        double cl[IP], cn[IP], nl[IP], nn[IP];
+        unsigned char cp[IP], np[IP];
+        auto fetch = [&](int i0, double (&l)[IP], double (&x)[IP], unsigned char (&pv)[IP]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int t = 0; t < IP; ++t) {
+            const int i = i0 + t;
+            const bool ok = i < n - 1;
+            l[t] = ok ? Xv[(long long)i * kmax + j] : 0.0;
+            x[t] = ok ? za[(long long)(i + 1) * kmax + j] : 0.0;
+            pv[t] = ok ? piv[(long long)i * kmax + j] : (unsigned char)0;
+          }
+        };
+        fetch(0, cl, cn, cp);
+        for (int i0 = 0; i0 < n - 1; i0 += IP) {
+          fetch(i0 + IP, nl, nn, np);
+#pragma unroll
+          for (int t = 0; t < IP; ++t) {
+            const int i = i0 + t;
+            if (i < n - 1) {
+              if (cp[t]) {
+                zb[(long long)i * kmax + j] = cn[t];
+                cur = cur - cl[t] * cn[t];
+              } else {
+                zb[(long long)i * kmax + j] = cur;
+                cur = cn[t] - cl[t] * cur;
+              }
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < IP; ++t) {
+            cl[t] = nl[t];
+            cn[t] = nn[t];
+            cp[t] = np[t];
+          }
         }
       }
-      // back substitution with U (bands u0, u1, u2)
-      double scale = 0.0;
-      for (int i = n - 1; i >= 0; --i) {
-        double s = z[i];
-        if (i + 1 < n) s -= U1[(long long)i * kmax + j] * z[i + 1];
-        if (i + 2 < n) s -= U2[(long long)i * kmax + j] * z[i + 2];
-        z[i] = s / U0[(long long)i * kmax + j];
-        scale = fmax(scale, fabs(z[i]));
+      zb[(long long)(n - 1) * kmax + j] = cur;
+      // back substitution with U (bands u0, u1, u2): zb -> za, same prefetching
+      double scale = 0.0, z1 = 0.0, z2 = 0.0;  // z[i + 1], z[i + 2]
+      {
+        double c0[IP], c1[IP], c2[IP], cz[IP], n0[IP], n1[IP], n2[IP], nz[IP];
+        auto fetch = [&](int i0, double (&u0)[IP], double (&u1)[IP], double (&u2)[IP], double (&x)[IP]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int t = 0; t < IP; ++t) {
+            const int i = i0 - t;
+            const bool ok = i >= 0;
+            u0[t] = ok ? U0[(long long)i * kmax + j] : 1.0;
+            u1[t] = ok ? U1[(long long)i * kmax + j] : 0.0;
+            u2[t] = ok ? U2[(long long)i * kmax + j] : 0.0;
+            x[t] = ok ? zb[(long long)i * kmax + j] : 0.0;
+          }
+        };
+        fetch(n - 1, c0, c1, c2, cz);
+        for (int i0 = n - 1; i0 >= 0; i0 -= IP) {
+          fetch(i0 - IP, n0, n1, n2, nz);
+#pragma unroll
+          for (int t = 0; t < IP; ++t) {
+            const int i = i0 - t;
+            if (i >= 0) {
+              double sv = cz[t];
+              if (i + 1 < n) sv -= c1[t] * z1;
+              if (i + 2 < n) sv -= c2[t] * z2;
+              const double zi = sv / c0[t];
+              za[(long long)i * kmax + j] = zi;
+              scale = fmax(scale, fabs(zi));
+              z2 = z1;
+              z1 = zi;
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < IP; ++t) {
+            c0[t] = n0[t];
+            c1[t] = n1[t];
+            c2[t] = n2[t];
+            cz[t] = nz[t];
+          }
+        }
       }
       // normalise to unit 2-norm (rescale by max first to avoid overflow)
       double inv = (scale > 0.0) ? 1.0 / scale : 1.0;
       double nrm = 0.0;
       for (int i = 0; i < n; ++i) {
-        z[i] *= inv;
-        nrm += z[i] * z[i];
+        const double zi = za[(long long)i * kmax + j] * inv;
+        za[(long long)i * kmax + j] = zi;
+        nrm += zi * zi;
       }
       nrm = 1.0 / sqrt(nrm);
-      for (int i = 0; i < n; ++i) z[i] *= nrm;
+      for (int i = 0; i < n; ++i) za[(long long)i * kmax + j] *= nrm;
     }
+    double *z = Zb + (long long)j * n;  // output row j
+    for (int i = 0; i < n; ++i) z[i] = za[(long long)i * kmax + j];
   }
   __syncthreads();
   __threadfence_block();
@@ -1001,14 +1073,14 @@ void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d
   HIP_LAUNCH_CHECK();
 }
 
-size_t invit_work_doubles(int n, int kmax) { return 4ull * n * kmax + ((size_t)n * kmax + 7) / 8 + 8; }
+size_t invit_work_doubles(int n, int kmax) { return 6ull * n * kmax + ((size_t)n * kmax + 7) / 8 + 8; }
 
 void sym_eigvecs(const double *d, const double *e, const double *refl, const double *beta, long long t_bs,
                  const double *evals, long long ev_bs, int n, const int *k_dev, int kmax, int batch, double *Zw,
                  long long z_bs, double *work, long long w_bs, double *out64, float *out32, long long out_bs,
                  int out_ld, hipStream_t st) {
   if (kmax <= 0) return;
-  hipLaunchKernelGGL(invit_kernel, dim3(batch), dim3(LT), 2 * (size_t)n * sizeof(double), st, d, e, t_bs, evals,
+  hipLaunchKernelGGL(invit_kernel, dim3(batch), dim3(IT), 2 * (size_t)n * sizeof(double), st, d, e, t_bs, evals,
                      ev_bs, k_dev, (const int *)nullptr, n, Zw, z_bs, work, w_bs, kmax);
   HIP_LAUNCH_CHECK();
   ensure_lds_attrs();
