@@ -305,7 +305,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
     b.P2 = ar.take<float>((long long)nb * pl.M * ld);
     b.Zt = ar.take<float>((long long)nb * ell * pl.M);
     b.Z2 = ar.take<float>((long long)nb * pl.M * ld);
-    b.Rw = ar.take<double>((long long)nb * 2 * ell * ell);
+    b.Rw = ar.take<double>((long long)nb * chol_scratch_doubles((int)ell));
     b.RinvT = ar.take<float>((long long)nb * ell * ld);
     b.Wrows = ar.take<float>((long long)nb * sz.kmax * ld);
   } else {
@@ -476,7 +476,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     Stage prof("cholqr_tall", st);
     for (int p = 0; p < passes; ++p) {
       gram_f32(pl, b, y.T, Tld, ell * Tld, (int)ell, (int)T, y.am, b.G64, ell * ell, (int)ell, nb, st);
-      chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, 2 * ell * ell, b.RinvT, ell * ld, (int)ld, amR, st);
+      chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, chol_scratch_doubles((int)ell), b.RinvT, ell * ld, (int)ld, amR, st);
       fill_f32(q.am, nb, 0.f, st);
       GemmArgs g = ga();
       g.A = y.R; g.a_ld = ld; g.a_bs = T * ld; g.a_amax = y.am;
@@ -503,7 +503,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       // Z = orth(P) by Cholesky QR; Z^T feeds the next sketch
       Stage prof_z("cholqr_z", st);
       gram_f32(pl, b, b.Pt, Mf, ell * Mf, (int)ell, (int)Mf, amP, b.G64, ell * ell, (int)ell, nb, st);
-      chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, 2 * ell * ell, b.RinvT, ell * ld, (int)ld, amR, st);
+      chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, chol_scratch_doubles((int)ell), b.RinvT, ell * ld, (int)ld, amR, st);
       fill_f32(amZ, nb, 0.f, st);
       GemmArgs g = ga();
       g.A = b.P2; g.a_ld = ld; g.a_bs = Mf * ld; g.a_amax = amP;
@@ -917,7 +917,7 @@ Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot)
     v.P2 = b.P2 + c0 * M * ld;
     v.Zt = b.Zt + c0 * ell * M;
     v.Z2 = b.Z2 + c0 * M * ld;
-    v.Rw = b.Rw + c0 * 2 * ell * ell;
+    v.Rw = b.Rw + c0 * chol_scratch_doubles((int)ell);
     v.RinvT = b.RinvT + c0 * ell * ld;
   }
   return v;

@@ -744,9 +744,9 @@ __global__ void __launch_bounds__(256) backtransform_kernel(const double *Zin, l
 }
 
 // ---------------------------------------------------------------------------------------------
-// Cholesky G = R^T R (R upper, fp64), right-looking in 32-column panels, and the triangular
-// inverse by block rows from the bottom.  Writes RinvT = (R^{-1})^T as fp32 [n][ld_out] and its
-// max |entry| (for the fp16 split of the apply GEMM).  Non-positive pivots are replaced by a tiny
+// Cholesky G = R^T R (R upper, fp64), right-looking in 32-column panels, one workgroup per
+// matrix; the inverse R^{-1} follows in diag_inv_kernel and tri_inv_kernel, which write
+// RinvT = (R^{-1})^T as fp32 [n][ld_out] and its max |entry| (for the fp16 split of the apply GEMM).  Non-positive pivots are replaced by a tiny
 // multiple of the largest diagonal entry (documented regularisation).
 // LDS: a 32 x 32 diagonal block and a 32 x (n - k0) panel (n <= 544 keeps the panel in LDS).
 // ---------------------------------------------------------------------------------------------
@@ -758,15 +758,13 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
                                                       long long r_bs, float *RinvT, long long o_bs, int ld_out,
                                                       float *amax) {
   extern __shared__ double sm[];
-  double *Dk = sm;               // [32][33] diagonal block / its inverse
-  double *Rd = sm + CNB * 33;    // [32][33] diagonal block of R (inverse phase)
+  double *Dk = sm;               // [32][33] diagonal block of R
   double *P = sm + 2 * CNB * 33; // [32][n] panel (row block of R)
   __shared__ float fred[CT / 64];
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int lane = tid & 63, wave = tid >> 6, nwave = nt >> 6;
   const double *Gb = G + b * g_bs;
   double *A = Rw + b * r_bs;          // working copy, becomes R (upper)
-  double *X = A + (long long)n * n;   // R^{-1} (upper)
   const bool in_lds = (n <= CHOL_MAXN_LDS);
   double dmax = 0.0;
   for (int i = 0; i < n; ++i) dmax = fmax(dmax, Gb[(long long)i * ldg + i]);
@@ -774,8 +772,8 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
   for (long long idx = tid; idx < (long long)n * n; idx += nt) {
     int i = (int)(idx / n), j = (int)(idx % n);
     A[idx] = (j >= i) ? Gb[(long long)i * ldg + j] : 0.0;
-    X[idx] = 0.0;
   }
+  if (tid == 0) amax[b] = 0.f;  // max |R^{-1}| is accumulated by tri_inv_kernel
   __syncthreads();
   for (int k0 = 0; k0 < n; k0 += CNB) {
     const int kb = min(CNB, n - k0), rem = n - k0 - kb;
@@ -865,109 +863,94 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
     else trailing(A + (long long)k0 * n + k0 + kb, n);
     __syncthreads();
   }
-  // ---- X = R^{-1}: block rows from the bottom ----------------------------------------------
-  // X[i0+r][c] = -sum_q Dinv[r][q] S[q][c],  S[q][c] = sum_{k = i0+ib}^{c} R[i0+q][k] X[k][c]
-  // Work split: each wave owns 64 consecutive columns (one per lane) and 8 rows q of S.
-  const int nblk = (n + CNB - 1) / CNB;
-  for (int bi = nblk - 1; bi >= 0; --bi) {
-    const int i0 = bi * CNB, ib = min(CNB, n - i0), rest = n - i0 - ib;
-    // inverse of the diagonal block (upper) into Dk, from an LDS copy Rd of the block
-    for (int idx = tid; idx < CNB * 33; idx += nt) {
-      Dk[idx] = 0.0;
-      const int r = idx / 33, c = idx % 33;
-      Rd[idx] = (r < ib && c < ib && c >= r) ? A[(long long)(i0 + r) * n + i0 + c] : 0.0;
+  // the triangular inverse and the fp32 output run in diag_inv_kernel / tri_inv_kernel
+  (void)RinvT;
+  (void)o_bs;
+  (void)ld_out;
+  (void)fred;
+}
+
+// Inverses of the 32 x 32 diagonal blocks of R (upper), one wave per block: lane c solves
+// R_ii x = e_c by back substitution with column q of R_ii held by lane q (shuffled), and writes
+// column c of the inverse to Dinv block i (row-major 32 x 32, zeros outside the block) in the
+// second half of the Cholesky scratch.
+__global__ void __launch_bounds__(64) diag_inv_kernel(double *Rw, long long r_bs, int n) {
+  const int bi = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+  const int i0 = bi * CNB, ib = min(CNB, n - i0);
+  const double *R = Rw + b * r_bs;
+  double *Dv = Rw + b * r_bs + (long long)n * n + (long long)bi * CNB * CNB;
+  double a[CNB];  // a[r] = R[i0 + r][i0 + c]
+#pragma unroll
+  for (int r = 0; r < CNB; ++r) a[r] = (c < ib && r <= c) ? R[(long long)(i0 + r) * n + i0 + c] : (r == c ? 1.0 : 0.0);
+  double x[CNB];
+#pragma unroll
+  for (int r = CNB - 1; r >= 0; --r) {
+    double v = (r == c) ? 1.0 : 0.0;
+#pragma unroll
+    for (int q = r + 1; q < CNB; ++q) {
+      const double rq = __shfl(a[r], q, 64);  // R[r][q]
+      if (q <= c) v -= rq * x[q];
     }
+    const double rr = __shfl(a[r], r, 64);
+    x[r] = (r <= c) ? v / rr : 0.0;
+  }
+  if (c < CNB) {
+#pragma unroll
+    for (int r = 0; r < CNB; ++r) Dv[r * CNB + c] = (c < ib && r < ib) ? x[r] : 0.0;
+  }
+}
+
+// X = R^{-1} by independent back substitutions over 16-column slabs: workgroup (cb, b) holds
+// X[:, 16 cb .. 16 cb + 15] in LDS, starts from the diagonal-block inverse and walks the block
+// rows upwards, X_i = -Dinv_i (R[i, >i] X[>i, slab]).  Writes (R^{-1})^T rows as fp32 and folds
+// max |entry| into amax[b] (zeroed by the Cholesky kernel).
+constexpr int SW = 16;  // slab width
+__global__ void __launch_bounds__(512) tri_inv_kernel(const double *Rw, long long r_bs, int n, float *RinvT,
+                                                      long long o_bs, int ld_out, float *amax) {
+  extern __shared__ double sm[];
+  __shared__ double Ts[CNB][SW];
+  __shared__ float fred[8];
+  const int cb = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int c0 = cb * SW, cw = min(SW, n - c0);
+  const int rd = c0 / CNB, rows = (rd + 1) * CNB;  // slab rows 0 .. rows-1 (zero past n)
+  const double *R = Rw + b * r_bs;
+  const double *Dinv = R + (long long)n * n;
+  double *Xs = sm;  // [rows][SW]
+  for (int idx = tid; idx < rows * SW; idx += 512) {
+    const int r = idx / SW, c = idx % SW;
+    double v = 0.0;
+    if (r >= rd * CNB && c < cw) v = Dinv[(long long)rd * CNB * CNB + (r - rd * CNB) * CNB + (c0 - rd * CNB) + c];
+    Xs[idx] = v;
+  }
+  __syncthreads();
+  const int q = tid / SW, c = tid % SW;  // 32 x 16 threads
+  for (int i = rd - 1; i >= 0; --i) {
+    const int i0 = i * CNB, kbeg = i0 + CNB, kend = min(rows, n);
+    const double *Rrow = R + (long long)(i0 + q) * n;
+    double t0 = 0.0, t1 = 0.0, t2 = 0.0, t3 = 0.0;
+    int k = kbeg;
+    for (; k + 4 <= kend; k += 4) {
+      t0 += Rrow[k] * Xs[k * SW + c];
+      t1 += Rrow[k + 1] * Xs[(k + 1) * SW + c];
+      t2 += Rrow[k + 2] * Xs[(k + 2) * SW + c];
+      t3 += Rrow[k + 3] * Xs[(k + 3) * SW + c];
+    }
+    for (; k < kend; ++k) t0 += Rrow[k] * Xs[k * SW + c];
+    Ts[q][c] = (t0 + t1) + (t2 + t3);
     __syncthreads();
-    for (int c = tid; c < ib; c += nt) {
-      for (int r = c; r >= 0; --r) {
-        double v = (r == c) ? 1.0 : 0.0;
-        for (int q = r + 1; q <= c; ++q) v -= Rd[r * 33 + q] * Dk[q * 33 + c];
-        Dk[r * 33 + c] = v / Rd[r * 33 + r];
-      }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < ib * ib; idx += nt) {
-      int r = idx / ib, c = idx % ib;
-      X[(long long)(i0 + r) * n + i0 + c] = Dk[r * 33 + c];
-    }
-    if (rest > 0) {
-      // R's block row right of the diagonal block into LDS
-      for (int idx = tid; idx < ib * rest; idx += nt) {
-        const int r = idx / rest, cc = idx % rest;
-        P[r * rest + cc] = A[(long long)(i0 + r) * n + i0 + ib + cc];
-      }
-      __syncthreads();
-      // S[q][c] = sum_k R[i0+q][k] X[k][c] (X upper triangular and zero below, so k runs to the
-      // wave's last column), stored in place in X's rows i0.. (not yet final, not read here)
-      const int cgroups = (rest + 63) / 64, ngroups = cgroups * 4;  // (column group, 8-row group)
-      for (int gi = wave; gi < ngroups; gi += nwave) {
-        const int cg = gi >> 2, rg = gi & 3;
-        const int cc = cg * 64 + lane, c = i0 + ib + cc;
-        const int kend = min(n, i0 + ib + cg * 64 + 64);
-        double acc[8] = {};
-        const bool live = cc < rest;
-        int k = i0 + ib;
-        for (; k + 4 <= kend; k += 4) {
-          double x0 = live ? X[(long long)k * n + c] : 0.0;
-          double x1 = live ? X[(long long)(k + 1) * n + c] : 0.0;
-          double x2 = live ? X[(long long)(k + 2) * n + c] : 0.0;
-          double x3 = live ? X[(long long)(k + 3) * n + c] : 0.0;
-          const int kk = k - i0 - ib;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int r = rg * 8 + q;
-            if (r < ib) {
-              const double *pr = P + r * rest + kk;
-              acc[q] += pr[0] * x0 + pr[1] * x1 + pr[2] * x2 + pr[3] * x3;
-            }
-          }
-        }
-        for (; k < kend; ++k) {
-          const double x0 = live ? X[(long long)k * n + c] : 0.0;
-          const int kk = k - i0 - ib;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            const int r = rg * 8 + q;
-            if (r < ib) acc[q] += P[r * rest + kk] * x0;
-          }
-        }
-        if (live)
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            if (rg * 8 + q < ib) X[(long long)(i0 + rg * 8 + q) * n + c] = acc[q];
-      }
-      __syncthreads();
-      // X[i0+r][c] = -sum_{q >= r} Dinv[r][q] S[q][c]: waves own (64 columns, 8 rows r); the
-      // result goes to the LDS panel (free now), then back over S once every wave has read it
-      for (int gi = wave; gi < ngroups; gi += nwave) {
-        const int cg = gi >> 2, rg = gi & 3;
-        const int cc = cg * 64 + lane, c = i0 + ib + cc;
-        if (rg * 8 >= ib || cc >= rest) continue;
-        double acc[8] = {};
-        for (int q = rg * 8; q < ib; ++q) {
-          const double sq = X[(long long)(i0 + q) * n + c];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) acc[t] -= Dk[(rg * 8 + t) * 33 + q] * sq;  // Dinv upper: 0 for q < r
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          if (rg * 8 + t < ib) P[(rg * 8 + t) * rest + cc] = acc[t];
-      }
-      __syncthreads();
-      for (int idx = tid; idx < ib * rest; idx += nt) {
-        const int r = idx / rest, cc = idx % rest;
-        X[(long long)(i0 + r) * n + i0 + ib + cc] = P[r * rest + cc];
-      }
-    }
+    const double *Di = Dinv + (long long)i * CNB * CNB + q * CNB;  // row q of Dinv_i
+    double v = 0.0;
+    for (int p = q; p < CNB; ++p) v -= Di[p] * Ts[p][c];
+    Xs[(i0 + q) * SW + c] = v;
     __syncthreads();
   }
-  // ---- output (R^{-1})^T as fp32 and its max |entry| -----------------------------------------
+  // output rows c0 .. c0+cw-1 of (R^{-1})^T: RinvT[c0 + c][r] = X[r][c0 + c] (zero below row c0 + c)
   float lmax = 0.f;
   float *O = RinvT + b * o_bs;
-  for (long long idx = tid; idx < (long long)n * n; idx += nt) {
-    int cp = (int)(idx / n), c = (int)(idx % n);  // RinvT[cp][c] = Rinv[c][cp]
-    float v = (c <= cp) ? (float)X[(long long)c * n + cp] : 0.f;
-    O[(long long)cp * ld_out + c] = v;
+  for (int idx = tid; idx < cw * n; idx += 512) {
+    const int cc = idx / n, r = idx % n;
+    const float v = (r <= c0 + cc) ? (float)Xs[r * SW + cc] : 0.f;
+    O[(long long)(c0 + cc) * ld_out + r] = v;
     lmax = fmaxf(lmax, fabsf(v));
   }
   lmax = warp_max(lmax);
@@ -975,8 +958,8 @@ __global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long
   __syncthreads();
   if (tid == 0) {
     float m = 0.f;
-    for (int i = 0; i < nt / 64; ++i) m = fmaxf(m, fred[i]);
-    amax[b] = m;
+    for (int w = 0; w < 8; ++w) m = fmaxf(m, fred[w]);
+    atomicMax((unsigned int *)(amax + b), __float_as_uint(m));
   }
 }
 
@@ -1038,6 +1021,7 @@ void ensure_lds_attrs() {
   const int want = maxsh - 2048;  // leave room for the kernels' static LDS
   // best effort: the runtime may already allow the full amount
   (void)hipFuncSetAttribute((const void *)chol_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipFuncSetAttribute((const void *)tri_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_values_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)bisect_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
@@ -1092,13 +1076,23 @@ void sym_eigvecs(const double *d, const double *e, const double *refl, const dou
   HIP_LAUNCH_CHECK();
 }
 
+long long chol_scratch_doubles(int n) { return (long long)n * n + (long long)((n + CNB - 1) / CNB) * CNB * CNB; }
+
 void chol_inv(const double *G, long long g_bs, int ldg, int n, int batch, double *Rw, long long r_bs, float *RinvT,
               long long o_bs, int ld_out, float *amax, hipStream_t st) {
   JOLT_REQUIRE(n >= 1 && n <= CHOL_MAXN_LDS, JOLT_EINVAL, "Cholesky QR: panel width above 544 is not supported");
+  JOLT_REQUIRE(r_bs >= chol_scratch_doubles(n), JOLT_EINVAL, "Cholesky QR: scratch too small per matrix");
   size_t shm = (size_t)(2 * CNB * 33 + CNB * n) * sizeof(double);
   ensure_lds_attrs();
   hipLaunchKernelGGL(chol_inv_kernel, dim3(batch), dim3(CT), shm, st, G, g_bs, ldg, n, Rw, r_bs, RinvT, o_bs, ld_out,
                      amax);
+  HIP_LAUNCH_CHECK();
+  const int nblk = (n + CNB - 1) / CNB;
+  hipLaunchKernelGGL(diag_inv_kernel, dim3(nblk, batch), dim3(64), 0, st, Rw, r_bs, n);
+  HIP_LAUNCH_CHECK();
+  const int ncb = (n + SW - 1) / SW;
+  const size_t tshm = (size_t)nblk * CNB * SW * sizeof(double);
+  hipLaunchKernelGGL(tri_inv_kernel, dim3(ncb, batch), dim3(512), tshm, st, Rw, r_bs, n, RinvT, o_bs, ld_out, amax);
   HIP_LAUNCH_CHECK();
 }
 

@@ -19,7 +19,9 @@ void sym_eigvecs(const double *d, const double *e, const double *refl, const dou
                  int out_ld, hipStream_t st);
 
 // G[b] (fp64, n x n SPD) = R^T R; writes (R^{-1})^T as fp32 [n][ld_out] and its max |entry|.
-// Rw: [batch][2 n n] fp64 scratch.
+// Rw: [batch][chol_scratch_doubles(n)] fp64 scratch (R, then the inverses of its 32 x 32
+// diagonal blocks).
+long long chol_scratch_doubles(int n);
 void chol_inv(const double *G, long long g_bs, int ldg, int n, int batch, double *Rw, long long r_bs, float *RinvT,
               long long o_bs, int ld_out, float *amax, hipStream_t st);
 
