@@ -48,20 +48,21 @@ def parse():
 
 # the dominant kernel of the workload: the projection P^T = Q^T X (fp32 Q in two fp16 planes
 # times the fp16 cache), one launch over the 16 cells
-# (one launch covers all 16 cells; the launch shape is set by the library's sequencing, hence
-# api.cpp among the sources whose change invalidates the counters)
+# (one launch covers all 16 cells, split 16-fold along K = T; the launch shape is set by the
+# library's sequencing, hence api.cpp among the sources whose change invalidates the counters)
 TRAFFIC_KERNEL = {"stage": "project_gemm", "name": "gemm_kc_kernel<0, 2, 0, 4, 8, 2>", "cells_per_launch": 16,
+                  "splits": 16,
                   "sources": ["kv_cache_compression_layer_amd/csrc/gemm_kc.hip",
                               "kv_cache_compression_layer_amd/csrc/gemm_core.hpp",
                               "kv_cache_compression_layer_amd/csrc/common.hpp",
                               "kv_cache_compression_layer_amd/csrc/api.cpp"]}
 
 
-def project_grid(cells, ell=522, M=4096):
+def project_grid(cells, splits=1, ell=522, M=4096):
     """Work-items of a projection launch over `cells` cells as the profiler reports them
-    (128 x 256 tiles of 256 threads)."""
+    (128 x 256 tiles of 256 threads, one block per tile, K split and cell)."""
     tiles = -(-ell // 128) * -(-M // 256)
-    return tiles * 256 * cells
+    return tiles * 256 * cells * splits
 
 
 def _rows(d, fname):
@@ -101,7 +102,7 @@ def traffic_from(fetch, write, cfetch, cwrite):
     def counter(d, pick):
         vals = [float(r["Counter_Value"]) for r in _rows(d, "run_counter_collection.csv") if pick(r)]
         return sum(vals) / len(vals), len(vals)
-    grid = project_grid(TRAFFIC_KERNEL["cells_per_launch"])
+    grid = project_grid(TRAFFIC_KERNEL["cells_per_launch"], TRAFFIC_KERNEL["splits"])
     is_k = lambda r: TRAFFIC_KERNEL["name"] in r["Kernel_Name"] and int(r["Grid_Size"]) == grid
     is_copy = lambda r: "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower()
     f_kib, nf = counter(fetch, is_k)

@@ -242,6 +242,9 @@ struct Sizes {
   long long part_view;     // per spectra view (the first n_views of them are disjoint slices)
 };
 
+// K splits of the FlashJoLT projection: one per 4096 tokens, at most 16 (K = T is the long side)
+int project_splits(const Plan &pl) { return (int)std::min<long long>(16, std::max<long long>(1, pl.T / 4096)); }
+
 long long part_elems_for(const Plan &pl, int kmax, int nb) {
   long long pe = 0;
   {  // feature Gram partials
@@ -251,6 +254,8 @@ long long part_elems_for(const Plan &pl, int kmax, int nb) {
     pe = std::max(pe, (long long)nb * ns2 * pl.D * pl.D);
   }
   if (pl.mode == JOLT_FLASH) {
+    const int ps = project_splits(pl);
+    if (ps > 1) pe = std::max(pe, (long long)nb * ps * pl.ell * pl.M);
     int ns = nsplit_for(pl.T, tiles_of(pl.ell, pl.ell), nb, 1024);
     pe = std::max(pe, (long long)nb * ns * pl.ell * pl.ell_ld);
     int ns2 = nsplit_for(pl.M, tiles_of(pl.ell, pl.ell), nb, 1024);
@@ -455,17 +460,33 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     });
   };
   // P^T = Q^T X_(T) (ell x M) and P = (P^T)^T, from the rows of Q^T and the transposed cache
+  // P^T = Q^T X_(T) (ell x M) and P = (P^T)^T.  K = T is long: the product is split along K
+  // (more, shorter blocks fill the last wave of the grid) and the partials are summed in fixed
+  // order by the reduction, which writes both layouts and max |P|.
+  const int pns = project_splits(pl);
   auto project = [&](const float *Qt, const float *q_amax, float *c_amax) {
     Stage prof("project_gemm", st);
     GemmArgs g = ga();
     g.A = Qt; g.M = (int)ell; g.N = (int)Mf; g.K = (int)T;
     g.a_ld = Tld; g.a_bs = ell * Tld; g.a_amax = q_amax;
     g.B = b.Xt; g.b_ld = Tld; g.b_bs = Mf * Tld;
-    g.C = b.Pt; g.c_ld = Mf; g.c_bs = ell * Mf;
-    g.C2 = b.P2; g.c2_ld = ld; g.c2_bs = Mf * ld;
-    g.c_amax = c_amax;
     g.m_fastest = 1;
-    gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, 1, st);
+    if (pns <= 1) {
+      g.C = b.Pt; g.c_ld = Mf; g.c_bs = ell * Mf;
+      g.C2 = b.P2; g.c2_ld = ld; g.c2_bs = Mf * ld;
+      g.c_amax = c_amax;
+      gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, 1, st);
+      return;
+    }
+    g.k_chunk = (int)rup((T + pns - 1) / pns, 32);
+    const int ns = (int)((T + g.k_chunk - 1) / g.k_chunk);
+    JOLT_REQUIRE((long long)nb * ns * ell * Mf <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
+    g.C = b.part; g.c_ld = Mf; g.c_split = ell * Mf; g.c_bs = (long long)ns * ell * Mf;
+    gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, ns, st);
+    prof.end();
+    Stage prof_r("project_reduce", st);
+    reduce_splits_dual(b.part, g.c_bs, g.c_split, ns, (int)ell, (int)Mf, Mf, b.Pt, ell * Mf, Mf, b.P2, Mf * ld, ld,
+                       c_amax, nb, st);
   };
   // R from the Gram of the rows of Yt, then Q = Y R^{-1} in both layouts
   struct Pair {

@@ -140,6 +140,12 @@ void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int b
 // gemm() after validation
 void gemm_kc(int mf, int sa, int sb, const GemmArgs &g, int batch, int nsplit, hipStream_t st);
 
+// split-K partials summed in fixed order (fp64) into C [rows][cols] (row pitch c_ld) and its
+// transpose C2 [cols][rows] (row pitch c2_ld); optional per-batch max |C| into amax (atomic max)
+void reduce_splits_dual(const float *part, long long part_bs, long long part_ss, int nsplit, int rows, int cols,
+                        long long ld_in, float *C, long long c_bs, long long c_ld, float *C2, long long c2_bs,
+                        long long c2_ld, float *amax, int batch, hipStream_t st);
+
 // sum of split-K partials in fixed order: out[b][i] = sum_s part[b][s][i] (fp64 accumulate)
 void reduce_splits(const float *part, long long part_bs, long long part_ss, int nsplit, long long n,
                    int rows, int cols, long long ld_in, void *out, bool out_f64, long long out_bs,

@@ -219,6 +219,49 @@ __global__ void reduce_splits_kernel(const float *part, long long part_bs, long 
   }
 }
 
+// Split-K partials summed in fixed order (fp64) and written in two layouts, C[r][c] and
+// C2[c][r], through a 32 x 32 LDS tile so both stores are coalesced; max |C| per batch is folded
+// into amax (float bits, atomic max; the caller clears it).
+__global__ void __launch_bounds__(256) reduce_splits_dual_kernel(const float *part, long long part_bs,
+                                                                 long long part_ss, int nsplit, int rows, int cols,
+                                                                 long long ld_in, float *C, long long c_bs,
+                                                                 long long c_ld, float *C2, long long c2_bs,
+                                                                 long long c2_ld, float *amax) {
+  __shared__ float tile[32][33];
+  __shared__ float wmax[4];
+  const int b = blockIdx.z, tid = threadIdx.x, tx = tid & 31, ty = tid >> 5;  // 32 x 8 threads
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const float *pb = part + b * part_bs;
+  float lmax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = r0 + ty + 8 * k, c = c0 + tx;
+    float v = 0.f;
+    if (r < rows && c < cols) {
+      const float *p = pb + (long long)r * ld_in + c;
+      double s = 0.0;
+      for (int q = 0; q < nsplit; ++q) s += (double)p[q * part_ss];
+      v = (float)s;
+      C[b * c_bs + (long long)r * c_ld + c] = v;
+    }
+    tile[ty + 8 * k][tx] = v;
+    lmax = fmaxf(lmax, fabsf(v));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = c0 + ty + 8 * k, r = r0 + tx;
+    if (r < rows && c < cols) C2[b * c2_bs + (long long)c * c2_ld + r] = tile[tx][ty + 8 * k];
+  }
+  if (amax) {
+    lmax = warp_max(lmax);
+    if ((tid & 63) == 0) wmax[tid >> 6] = lmax;
+    __syncthreads();
+    if (tid == 0)
+      atomicMax((unsigned int *)(amax + b), __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
+  }
+}
+
 }  // namespace
 
 void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int batch, int nsplit,
@@ -265,6 +308,15 @@ void reduce_splits(const float *part, long long part_bs, long long part_ss, int 
   int blocks = (int)std::min<long long>((tot + 255) / 256, 4096);
   hipLaunchKernelGGL(reduce_splits_kernel, dim3(blocks, batch), dim3(256), 0, st, part, part_bs, part_ss, nsplit,
                      rows, cols, ld_in, out, out_f64 ? 1 : 0, out_bs, ld_out);
+  HIP_LAUNCH_CHECK();
+}
+
+void reduce_splits_dual(const float *part, long long part_bs, long long part_ss, int nsplit, int rows, int cols,
+                        long long ld_in, float *C, long long c_bs, long long c_ld, float *C2, long long c2_bs,
+                        long long c2_ld, float *amax, int batch, hipStream_t st) {
+  dim3 grid((cols + 31) / 32, (rows + 31) / 32, batch);
+  hipLaunchKernelGGL(reduce_splits_dual_kernel, grid, dim3(256), 0, st, part, part_bs, part_ss, nsplit, rows, cols,
+                     ld_in, C, c_bs, c_ld, C2, c2_bs, c2_ld, amax);
   HIP_LAUNCH_CHECK();
 }
 
