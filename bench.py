@@ -154,10 +154,10 @@ def kernel_models(T, L, H, D, G, ell, picks, dtype_bytes):
     n_cells = 2 * cells_per_launch
     m = {}
     # Y^T = Omega^T X^T and Y^T = Z^T X^T: 2 T M ell flops per cell, X read once
-    m["sketch_gemm"] = {"flops": 2.0 * T * M * ell * cells_per_launch, "launches_per_call": 2,
+    m["sketch_gemm"] = {"flops": 2.0 * T * M * ell * cells_per_launch, "launches_per_record": 2,
                         "bytes": (T * M * dtype_bytes + 4.0 * ell * T) * cells_per_launch}
     # P^T = Q^T X: same contraction; reads X and fp32 Q once, writes P in both layouts
-    m["project_gemm"] = {"flops": 2.0 * T * M * ell * n_cells, "launches_per_call": 1,
+    m["project_gemm"] = {"flops": 2.0 * T * M * ell * n_cells, "launches_per_record": 1,
                          "bytes": (T * M * dtype_bytes + 4.0 * ell * T + 2 * 4.0 * ell * M) * n_cells}
     # fused residual encode: one launch over the cells with b > 0
     flops = 0.0
@@ -168,12 +168,12 @@ def kernel_models(T, L, H, D, G, ell, picks, dtype_bytes):
         R = GH * T
         flops += 2.0 * R * (D + p["rT"]) * D
         byts += R * D * dtype_bytes + T * p["rT"] * dtype_bytes + R * D * p["bits"] / 8.0 + 4.0 * R
-    m["residual_encode"] = {"flops": flops, "bytes": byts, "launches_per_call": 1}
+    m["residual_encode"] = {"flops": flops, "bytes": byts, "launches_per_record": 1}
     # feature Gram: 2 R D^2 per cell, X read once
-    m["feature_gram"] = {"flops": 2.0 * GH * T * D * D * n_cells, "launches_per_call": 1,
+    m["feature_gram"] = {"flops": 2.0 * GH * T * D * D * n_cells, "launches_per_record": 1,
                          "bytes": GH * T * D * dtype_bytes * n_cells}
     # per-(l,h) transpose of the cache: read + write once
-    m["transpose_x"] = {"flops": 0.0, "launches_per_call": 2, "bytes": 2.0 * GH * T * D * dtype_bytes * cells_per_launch}
+    m["transpose_x"] = {"flops": 0.0, "launches_per_record": 2, "bytes": 2.0 * GH * T * D * dtype_bytes * cells_per_launch}
     return m
 
 
@@ -292,9 +292,8 @@ def main():
     jolt.profile(False)
     ell = min(512 + 10, T)
     models = kernel_models(T, L, H, D, G, ell, picks, 2)
-    # The profiled call is one compress call.  The library may split a stage's cells over several
-    # concurrent launches, so rates use the whole call's algorithmic work over the stage's summed
-    # launch time; the per-launch duration is that sum over the launch count.
+    # The profiled call is one compress call; rates use the stage's algorithmic work over its summed
+    # launch time, the per-launch duration is that sum over the number of launches.
     best = None
     for name, (ms, cnt) in stages.items():
         if name in models and cnt > 0:
@@ -304,11 +303,12 @@ def main():
     if best:
         name, ms, cnt = best
         mdl = models[name]
-        call_flops = mdl["flops"] * mdl["launches_per_call"]
-        call_bytes = mdl["bytes"] * mdl["launches_per_call"]
-        flop_rate = call_flops / (ms / 1e3) / 1e12
-        byte_rate = call_bytes / (ms / 1e3) / 1e9
-        pl_ms = ms / cnt
+        # the stage was recorded cnt times, each record covering launches_per_record launches of
+        # the modelled work over the whole cell batch
+        nl = cnt * mdl["launches_per_record"]
+        flop_rate = mdl["flops"] * nl / (ms / 1e3) / 1e12
+        byte_rate = mdl["bytes"] * nl / (ms / 1e3) / 1e9
+        pl_ms = ms / nl
         ai = mdl["flops"] / max(mdl["bytes"], 1.0)
         ridge = MFMA_PEAK_TFLOPS[a.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
         if ai >= ridge:
@@ -320,7 +320,7 @@ def main():
         roof["traffic"] = traffic_for(name)
         roof["kernel"] = name
         roof["launch_ms"] = round(pl_ms, 4)
-        roof["launches"] = cnt
+        roof["launches"] = nl
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(K, V, groups, {"eps2": [float(x) for x in eps2], "rT": rT, "rd": rd, "bits": bits,
