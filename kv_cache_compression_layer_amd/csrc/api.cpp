@@ -248,7 +248,7 @@ int project_splits(const Plan &pl) { return (int)std::min<long long>(16, std::ma
 long long part_elems_for(const Plan &pl, int kmax, int nb) {
   long long pe = 0;
   {  // feature Gram partials
-    int ns = nsplit_for((long long)pl.GH * pl.T, 1, nb, 8192);
+    int ns = nsplit_for((long long)pl.GH * pl.T_ld, 1, nb, 8192);  // K of the feature Gram, padding included
     pe = std::max(pe, (long long)nb * ns * pl.D * pl.D);
     int ns2 = nsplit_for((long long)kmax * pl.GH, 1, nb, 1024);
     pe = std::max(pe, (long long)nb * ns2 * pl.D * pl.D);

@@ -188,7 +188,53 @@ __global__ void amax_kernel(const float *x, long long per, long long bs, float *
   if ((threadIdx.x & 63) == 0) atomicMax((unsigned int *)(out + cell), __float_as_uint(m));
 }
 
-// Xt[b][j][d][t] = X[b][j][t][d] (16- or 32-bit elements), t padded to T_ld with zeros.
+// Xt[b][j][d][t] = X[b][j][t][d] with 16-byte global accesses on both sides: a 128-token x
+// 64-dim tile is read row by row into LDS (rows padded by one 32-bit word, so the column reads of
+// the second phase spread over the banks) and written back column by column.  Needs D % 64 == 0,
+// T_ld % 8 == 0 and 16-byte aligned rows; tokens T..T_ld-1 are written as zeros.
+template <typename E>
+__global__ void __launch_bounds__(256) transpose_x_vec_kernel(const E *X, E *Xt, int T, int T_ld, int D, int GH,
+                                                             long long x_bs, long long xt_bs) {
+  constexpr int VEC = 16 / sizeof(E);              // elements per 16-byte access
+  constexpr int TT = 128, TD = 64;                 // tokens x dims of the tile
+  constexpr int PW = TD * (int)sizeof(E) / 4 + 1;  // 32-bit words per LDS row
+  constexpr int CPR = TD / VEC, RPP = 256 / CPR;   // load phase: chunks per token row, rows per pass
+  constexpr int CPO = TT / VEC, RPO = 256 / CPO;   // store phase: chunks per dim row, rows per pass
+  __shared__ uint32_t tile[TT * PW];
+  const int b = blockIdx.z, j = blockIdx.y % GH;
+  const int t0 = blockIdx.x * TT, d0 = (blockIdx.y / GH) * TD;
+  const E *src = X + b * x_bs + (long long)j * T * D + d0;
+  E *dst = Xt + b * xt_bs + (long long)j * D * T_ld + (long long)d0 * T_ld;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < TT / RPP; ++p) {
+    const int r = p * RPP + tid / CPR, c = tid % CPR, t = t0 + r;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (t < T) v = *(const uint4 *)(src + (long long)t * D + c * VEC);
+    uint32_t *w = tile + r * PW + c * 4;
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < TD / RPO; ++p) {
+    const int d = p * RPO + tid / CPO, c = tid % CPO, t = t0 + c * VEC;
+    if (t >= T_ld) continue;
+    uint32_t o[4];
+    if constexpr (sizeof(E) == 2) {
+      const uint16_t *h = (const uint16_t *)tile;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = (uint32_t)h[(c * VEC + 2 * q) * 2 * PW + d] | ((uint32_t)h[(c * VEC + 2 * q + 1) * 2 * PW + d] << 16);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = tile[(c * VEC + q) * PW + d];
+    }
+    *(uint4 *)(dst + (long long)d * T_ld + t) = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
+// Xt[b][j][d][t] = X[b][j][t][d] (16- or 32-bit elements), t padded to T_ld with zeros; any
+// alignment (used when the cache rows are not 16-byte aligned).
 template <typename E>
 __global__ void transpose_x_kernel(const E *X, E *Xt, int T, int T_ld, int D, int GH, long long x_bs, long long xt_bs) {
   __shared__ E tile[64][65];
@@ -219,6 +265,18 @@ void gen_omega(void *out, int dtype, int M, int ell, uint64_t key, hipStream_t s
 }
 void transpose_x(const void *X, void *Xt, int elem_bytes, int T, int T_ld, int D, int GH, int batch, long long x_bs,
                  long long xt_bs, hipStream_t st) {
+  const bool vec = D % 64 == 0 && T_ld % 8 == 0 && ((uintptr_t)X & 15) == 0 && ((uintptr_t)Xt & 15) == 0;
+  if (vec) {
+    dim3 grid((T_ld + 127) / 128, GH * (D / 64), batch);
+    if (elem_bytes == 2)
+      hipLaunchKernelGGL(transpose_x_vec_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)X, (uint16_t *)Xt,
+                         T, T_ld, D, GH, x_bs, xt_bs);
+    else
+      hipLaunchKernelGGL(transpose_x_vec_kernel<float>, grid, dim3(256), 0, st, (const float *)X, (float *)Xt, T, T_ld,
+                         D, GH, x_bs, xt_bs);
+    HIP_LAUNCH_CHECK();
+    return;
+  }
   dim3 grid((T_ld + 63) / 64, GH * ((D + 63) / 64), batch);
   if (elem_bytes == 2)
     hipLaunchKernelGGL(transpose_x_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)X, (uint16_t *)Xt, T,
