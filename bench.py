@@ -50,9 +50,9 @@ def parse():
 # times the fp16 cache), one launch over the 16 cells
 # (one launch covers all 16 cells, split 16-fold along K = T; the launch shape is set by the
 # library's sequencing, hence api.cpp among the sources whose change invalidates the counters)
-TRAFFIC_KERNEL = {"stage": "project_gemm", "name": "gemm_kc_kernel<0, 2, 0, 4, 8, 2>", "cells_per_launch": 16,
+TRAFFIC_KERNEL = {"stage": "project_gemm", "name": "gemm_dma_kernel<0, 2, 1, 3, 8, 3, 4, 2>", "cells_per_launch": 16,
                   "splits": 16,
-                  "sources": ["kv_cache_compression_layer_amd/csrc/gemm_kc.hip",
+                  "sources": ["kv_cache_compression_layer_amd/csrc/gemm_dma.hip",
                               "kv_cache_compression_layer_amd/csrc/gemm_core.hpp",
                               "kv_cache_compression_layer_amd/csrc/common.hpp",
                               "kv_cache_compression_layer_amd/csrc/api.cpp"]}
@@ -60,9 +60,9 @@ TRAFFIC_KERNEL = {"stage": "project_gemm", "name": "gemm_kc_kernel<0, 2, 0, 4, 8
 
 def project_grid(cells, splits=1, ell=522, M=4096):
     """Work-items of a projection launch over `cells` cells as the profiler reports them
-    (128 x 256 tiles of 256 threads, one block per tile, K split and cell)."""
-    tiles = -(-ell // 128) * -(-M // 256)
-    return tiles * 256 * cells * splits
+    (192 x 256 tiles of 512 threads, one block per tile, K split and cell)."""
+    tiles = -(-ell // 192) * -(-M // 256)
+    return tiles * 512 * cells * splits
 
 
 def _rows(d, fname):

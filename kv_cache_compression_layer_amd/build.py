@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libjolt.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["gemm.hip", "gemm_kc.hip", "linalg.hip", "codec.hip", "alloc.hip", "misc.hip", "setup.cpp", "api.cpp"]
+SOURCES = ["gemm.hip", "gemm_kc.hip", "gemm_dma.hip", "linalg.hip", "codec.hip", "alloc.hip", "misc.hip", "setup.cpp", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

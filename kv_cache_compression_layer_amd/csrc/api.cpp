@@ -94,6 +94,8 @@ struct Plan {
   uint64_t rot_seed, sketch_seed;
   long long cell_elems() const { return (long long)GH * T * D; }
   int xmf() const { return dtype == JOLT_F16 ? MF_F16 : MF_BF16; }
+  int fp32_planes() const { return xmf() == MF_F16 ? 2 : 3; }  // planes of an fp32 operand
+  long long pln_cell() const { return (long long)fp32_planes() * ell * std::max<long long>(T_ld, M); }
   int xsrc() const { return dtype == JOLT_F16 ? SRC_F16 : (dtype == JOLT_BF16 ? SRC_BF16 : SRC_F32); }
 };
 
@@ -210,6 +212,9 @@ struct Bufs {
   AllocOut *aout;
   // per-(l,h) transposed cache [cell][j][d][T_ld]
   void *Xt;
+  // 16-bit planes of an fp32 operand of the plane GEMM: Q^T for the projection, Z^T for the
+  // power-iteration sketch (used one after the other), [cell][plane][ell][max(T_ld, M)]
+  uint16_t *pln;
   // device parameter area
   char *params;
   size_t params_bytes;
@@ -313,6 +318,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
     b.Rw = ar.take<double>((long long)nb * chol_scratch_doubles((int)ell));
     b.RinvT = ar.take<float>((long long)nb * ell * ld);
     b.Wrows = ar.take<float>((long long)nb * sz.kmax * ld);
+    b.pln = pl.xsrc() == SRC_F32 ? nullptr : ar.take<uint16_t>((long long)nb * pl.pln_cell());
   } else {
     b.bufB = ar.take<float>((long long)nb * sz.kmax * pl.T_ld);  // token factor rows
     b.Zt = ar.take<float>((long long)nb * sz.kmax * pl.M);       // token-projected tensor
@@ -441,9 +447,18 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   float *amY = b.amax, *amR = b.amax + am, *amQ = b.amax + 2 * am, *amP = b.amax + 3 * am, *amZ = b.amax + 4 * am;
   // (Omega is generated and the amax slots are cleared once for all cells by spectra_all)
 
-  // Y^T = A X_(T)^T with A = Omega^T (cache dtype) or Z^T (fp32); also Y = (Y^T)^T
+  // Y^T = A X_(T)^T with A = Omega^T (cache dtype) or Z^T (fp32); also Y = (Y^T)^T.  On the plane
+  // path an fp32 A is first split into its 16-bit planes (the split the GEMM would make on the fly).
+  const int P32 = pl.fp32_planes();
+  const bool dma_ok = b.pln != nullptr;
   auto sketch = [&](const void *A, int a_src, long long a_bs, const float *a_amax, float *outT, float *outR,
                     float *c_amax) {
+    bool planes = dma_ok && a_src == SRC_F32 && Mf % 32 == 0;
+    if (planes) {
+      Stage prof_s("split_planes", st);
+      split_planes(pl.xmf(), (const float *)A, ell * Mf, Mf, (int)ell, (int)Mf, (int)Mf, b.pln, P32 * ell * Mf,
+                   ell * Mf, Mf, a_amax, 1, nb, st);
+    }
     Stage prof("sketch_gemm", st);
     for_kv(K, V, [&](int t, const void *X) {
       GemmArgs g = ga();
@@ -456,15 +471,30 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       g.C2 = outR + t * T * ld; g.c2_ld = ld; g.c2_bs = 2 * T * ld;
       g.c_amax = c_amax ? c_amax + t : nullptr; g.c_amax_bs = 2;
       g.m_fastest = 1;
+      if (planes) {
+        GemmArgs h = g;
+        h.A = b.pln + t * P32 * ell * Mf;
+        h.a_bs = 2 * P32 * ell * Mf;
+        h.a_ps = ell * Mf;
+        if (gemm_dma(pl.xmf(), P32, 1, h, nkv, 1, st)) return;
+      } else if (dma_ok && a_src != SRC_F32) {
+        if (gemm_dma(pl.xmf(), 1, 1, g, nkv, 1, st)) return;
+      }
       gemm(pl.xmf(), a_src, true, pl.xsrc(), true, g, nkv, 1, st);
     });
   };
-  // P^T = Q^T X_(T) (ell x M) and P = (P^T)^T, from the rows of Q^T and the transposed cache
   // P^T = Q^T X_(T) (ell x M) and P = (P^T)^T.  K = T is long: the product is split along K
   // (more, shorter blocks fill the last wave of the grid) and the partials are summed in fixed
-  // order by the reduction, which writes both layouts and max |P|.
+  // order by the reduction, which writes both layouts and max |P|.  On the plane path Q^T is
+  // first split into its 16-bit planes.
   const int pns = project_splits(pl);
   auto project = [&](const float *Qt, const float *q_amax, float *c_amax) {
+    const bool planes = dma_ok && pns > 1 && T % 32 == 0;
+    if (planes) {
+      Stage prof_s("split_planes", st);
+      split_planes(pl.xmf(), Qt, ell * Tld, Tld, (int)ell, (int)T, (int)T, b.pln, P32 * ell * Tld, ell * Tld, Tld,
+                   q_amax, 1, nb, st);
+    }
     Stage prof("project_gemm", st);
     GemmArgs g = ga();
     g.A = Qt; g.M = (int)ell; g.N = (int)Mf; g.K = (int)T;
@@ -482,7 +512,13 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     const int ns = (int)((T + g.k_chunk - 1) / g.k_chunk);
     JOLT_REQUIRE((long long)nb * ns * ell * Mf <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
     g.C = b.part; g.c_ld = Mf; g.c_split = ell * Mf; g.c_bs = (long long)ns * ell * Mf;
-    gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, ns, st);
+    bool done = false;
+    if (planes) {
+      GemmArgs h = g;
+      h.A = b.pln; h.a_bs = P32 * ell * Tld; h.a_ps = ell * Tld;
+      done = gemm_dma(pl.xmf(), P32, 1, h, nb, ns, st);
+    }
+    if (!done) gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, ns, st);
     prof.end();
     Stage prof_r("project_reduce", st);
     reduce_splits_dual(b.part, g.c_bs, g.c_split, ns, (int)ell, (int)Mf, Mf, b.Pt, ell * Mf, Mf, b.P2, Mf * ld, ld,
@@ -940,6 +976,7 @@ Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot)
     v.Z2 = b.Z2 + c0 * M * ld;
     v.Rw = b.Rw + c0 * chol_scratch_doubles((int)ell);
     v.RinvT = b.RinvT + c0 * ell * ld;
+    if (b.pln) v.pln = b.pln + c0 * pl.pln_cell();
   }
   return v;
 }

@@ -130,6 +130,8 @@ struct GemmArgs {
   // are written as zeros without work; 2 = B(k, n) = 0 for k > n (an upper triangular factor),
   // so each column tile stops its k loop at its last column (single split only)
   int tri;
+  // operands stored as 16-bit planes (plane-GEMM path): element stride between planes
+  long long a_ps, b_ps;
 };
 
 // a_kc: A contiguous along K (else along M); b_kc: B contiguous along K (else along N)
@@ -139,6 +141,14 @@ void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int b
 // the same product for operands that are both contiguous along K (larger wave tiles); called by
 // gemm() after validation
 void gemm_kc(int mf, int sa, int sb, const GemmArgs &g, int batch, int nsplit, hipStream_t st);
+// Products of operands stored as 16-bit planes (pa planes of A at stride a_ps, pb of B), both
+// contiguous along K, fed through LDS by DMA; false (nothing launched) when the shape does not fit.
+bool gemm_dma(int mf, int pa, int pb, const GemmArgs &g, int batch, int nsplit, hipStream_t st);
+// fp32 rows [batch][rows][s_ld] -> planes [batch][plane][rows][d_ld] (2 fp16 planes after the
+// power-of-two scale of amax[b * amax_bs], or 3 bf16 planes); columns [cols, cols_pad) zeroed.
+void split_planes(int mf, const float *src, long long s_bs, long long s_ld, int rows, int cols, int cols_pad,
+                  uint16_t *dst, long long d_bs, long long d_ps, long long d_ld, const float *amax, int amax_bs,
+                  int batch, hipStream_t st);
 
 // split-K partials summed in fixed order (fp64) into C [rows][cols] (row pitch c_ld) and its
 // transpose C2 [cols][rows] (row pitch c2_ld); optional per-batch max |C| into amax (atomic max)
