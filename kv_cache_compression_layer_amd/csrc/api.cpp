@@ -204,6 +204,7 @@ struct Bufs {
   int am_ld;
   // fit
   float *Wrows, *Udrows, *Cp, *Udr, *Cr, *Vt, *Bcat, *bamax, *Qf, *Qtf;
+  uint16_t *Bpl;  // 16-bit planes of Bcat, [cell][plane][GH][D][Kb]
   double *Zw, *work, *ZwD, *workD;
   // alloc
   double *tailT, *tailD, *tab_e;
@@ -334,6 +335,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
   b.Cr = ar.take<float>((long long)nb * pl.GH * sz.kmax * sz.kmax_d);
   b.Vt = ar.take<float>((long long)nb * D * sz.kmax_d);
   b.Bcat = ar.take<float>((long long)nb * pl.GH * D * sz.Kb);
+  b.Bpl = ar.take<uint16_t>((long long)nb * pl.fp32_planes() * pl.GH * D * sz.Kb);
   b.bamax = ar.take<float>(nb);
   b.Qf = ar.take<float>((long long)D * D);
   b.Qtf = ar.take<float>((long long)D * D);
@@ -873,6 +875,9 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     h.alpha = -1.f;
     gemm(MF_F16, SRC_F32, true, SRC_F32, true, h, nb * GH, 1, st);
     amax_cells(b.Bcat, (long long)GH * D * sz.Kb, (long long)GH * D * sz.Kb, nb, b.bamax, st);
+    const long long per = (long long)GH * D * sz.Kb;
+    split_planes(pl.xmf(), b.Bcat, per, sz.Kb, (int)(GH * D), sz.Kb, sz.Kb, b.Bpl, pl.fp32_planes() * per, per,
+                 sz.Kb, b.bamax, 1, nb, st);
   }
   std::vector<EncCell> ec;
   for (int c = 0; c < nb; ++c) {
@@ -885,7 +890,7 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     e.ut_off = p.off + p.sec.off_UT;
     e.sc_off = p.off + p.sec.off_scales;
     e.cd_off = p.off + p.sec.off_codes;
-    e.bcat_off = (long long)c * GH * D * sz.Kb * 4;
+    e.bcat_off = (long long)c * pl.fp32_planes() * GH * D * sz.Kb * 2;
     e.am_idx = c;
     e.GH = GH; e.rT = p.rT; e.bits = p.bits; e.Kb = sz.Kb;
     ec.push_back(e);
@@ -901,7 +906,8 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     Stage prof("residual_encode", st);
     EncArgs ea;
     ea.xk = (const char *)K; ea.xv = (const char *)V; ea.utb = out; ea.scb = out; ea.cdb = out;
-    ea.bcat = (const char *)b.Bcat; ea.bamax = b.bamax; ea.cells = (const EncCell *)(dst + o_ec);
+    ea.bcat = (const char *)b.Bpl; ea.b_ps = (long long)GH * D * sz.Kb;
+    ea.bamax = b.bamax; ea.cells = (const EncCell *)(dst + o_ec);
     encode_cells(pl.dtype, ea, (int)ec.size(), pl.T, D, GH, st);
   }
 }
@@ -1461,7 +1467,8 @@ size_t jolt_encode_residual_workspace_bytes(int32_t G, int32_t H, int32_t T, int
   const long long GH = (long long)G * H, Kb = rup(D + rT, 8);
   long long bytes = 0;
   auto add = [&](long long n) { bytes += rup(std::max<long long>(n, 1), 256); };
-  add(rd * D * 4LL); add(GH * rT * rd * 4LL); add(D * rd * 4LL); add(GH * D * Kb * 4LL); add(16);
+  add(rd * D * 4LL); add(GH * rT * rd * 4LL); add(D * rd * 4LL); add(GH * D * Kb * 4LL); add(3 * GH * D * Kb * 2LL);
+  add(16);
   add(64 * 1024 + 2LL * D * D * 4);
   return (size_t)bytes + 4096;
 }
@@ -1490,6 +1497,8 @@ int jolt_encode_residual(const void *d_X, int32_t G, int32_t H, int32_t T, int32
     float *Cr = ar.take<float>((long long)GH * rT * rd);
     float *Vt = ar.take<float>((long long)D * rd);
     float *Bcat = ar.take<float>((long long)GH * D * Kb);
+    const int P = dtype == JOLT_F16 ? 2 : 3;  // 16-bit planes of Bcat
+    uint16_t *Bpl = ar.take<uint16_t>((long long)P * GH * D * Kb);
     float *am = ar.take<float>(4);
     char *pa = ar.take<char>(64 * 1024 + 2LL * D * D * 4);
     Upload u;
@@ -1526,9 +1535,12 @@ int jolt_encode_residual(const void *d_X, int32_t G, int32_t H, int32_t T, int32
     h.alpha = -1.f;
     gemm(MF_F16, SRC_F32, true, SRC_F32, true, h, GH, 1, st);
     amax_cells(Bcat, (long long)GH * D * Kb, 0, 1, am, st);
+    split_planes(dtype == JOLT_F16 ? MF_F16 : MF_BF16, Bcat, 0, Kb, GH * D, Kb, Kb, Bpl, 0, (long long)GH * D * Kb,
+                 Kb, am, 0, 1, st);
     EncArgs ea;
     ea.xk = ea.xv = (const char *)d_X; ea.utb = (const char *)d_UT; ea.scb = (char *)d_scales;
-    ea.cdb = (char *)d_codes; ea.bcat = (const char *)Bcat; ea.bamax = am; ea.cells = (const EncCell *)(pa + o_ec);
+    ea.cdb = (char *)d_codes; ea.bcat = (const char *)Bpl; ea.b_ps = (long long)GH * D * Kb;
+    ea.bamax = am; ea.cells = (const EncCell *)(pa + o_ec);
     encode_cells(dtype, ea, 1, T, D, GH, st);
     return 0;
   });

@@ -116,7 +116,10 @@ __device__ __forceinline__ void eload8(const char *p, bool ok, Raw8<S> &r) {
   }
 }
 
-// W waves per SIMD: 2 for 16-bit caches; fp32 caches carry three planes per operand and run at 1
+// W waves per SIMD: 2 for 16-bit caches; fp32 caches carry three planes per operand and run at 1.
+// B = [Q ; -D_j Q] arrives as 16-bit planes (split once per cell by the host sequence).  The MFMA
+// takes B as its first operand, so lane l holds output columns 4 (l / 16) + r (r = 0..3) of token
+// row l % 16 in every 16 x 16 subtile: four consecutive codes of one row per lane.
 template <int MF, int SX, int TN, int W = (SX == SRC_F32 ? 1 : 2)>
 __global__ void __launch_bounds__(ENT) __attribute__((amdgpu_waves_per_eu(W, W)))
 encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
@@ -124,15 +127,15 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
   constexpr int PA = Planes<SX, MF>::n, PB = Planes<SRC_F32, MF>::n;
   constexpr int MAXO = (MF == MF_F16) ? 1 : 2;
   constexpr int ASZ = PA * EBM * EKB, BSZ = PB * D * EKB, STG = ASZ + BSZ;
-  constexpr int LA = EBM * 4 / ENT, LB = D * 4 / ENT;
+  constexpr int LA = EBM * 4 / ENT, LB = D * 4 / ENT;  // 8-element chunks per thread per stage (B: per plane)
   constexpr int ESX = (SX == SRC_F32) ? 4 : 2;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // 2 * STG halves
   __shared__ float srow[EBM];
-  uint8_t *ucode = (uint8_t *)lds;  // [EBM][D] codes, reuses the tiles after the main loop
-  static_assert(2 * STG * 2 >= EBM * D, "code staging must fit in the tile buffers");
+  uint32_t *rowbits = (uint32_t *)lds;  // [EBM][D * bits / 32] packed codes, reuses the tiles
+  static_assert(2 * STG * 2 >= EBM * D, "packed codes must fit in the tile buffers");
 
   // XCD-aware order over the whole grid: consecutive (cell, slice, tile) on one XCD, so the
-  // tiles of one slice share its Bcat panel in that XCD's L2
+  // tiles of one slice share its B panel in that XCD's L2
   int tt, j, cz;
   {
     const long long gx = gridDim.x, total = gx * gridDim.z;
@@ -152,7 +155,7 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
   const int rT = c.rT, K = D + rT;
   const char *xbase = (c.kv ? ea.xv : ea.xk) + c.x_off + (long long)j * T * D * ESX;
   const char *utbase = ea.utb + c.ut_off;
-  const char *bj = ea.bcat + c.bcat_off + (long long)j * D * c.Kb * 4;
+  const char *bj = ea.bcat + c.bcat_off + (long long)j * D * c.Kb * 2;  // plane 0 of slice j
   const float bscale = (MF == MF_F16) ? f16_split_scale(ea.bamax[c.am_idx]) : 1.f;
 
   f32x4 acc[4][TN];
@@ -161,9 +164,9 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
 #pragma unroll
     for (int q = 0; q < TN; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // load slots: A rows t0 + v / 4 (X then U_T), B rows n = v / 4 of Bcat_j, chunk v % 4
+  // load slots: A rows t0 + v / 4 (X then U_T), B rows n = v / 4 of each plane of B_j, chunk v % 4
   Raw8<SX> ra[LA];
-  Raw8<SRC_F32> rb[LB];
+  uint4 rb[PB][LB];
   long long xo[LA], uo[LA];
   bool oka[LA];
 #pragma unroll
@@ -174,6 +177,17 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
     xo[it] = (tr * D + (v & 3) * 8) * ESX;
     uo[it] = (tr * rT + (v & 3) * 8) * ESX;
   }
+  auto bload = [&](int k0, bool check) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < PB; ++p)
+#pragma unroll
+      for (int it = 0; it < LB; ++it) {
+        const int v = tid + it * ENT, k = k0 + (v & 3) * 8;
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (!check || k < K) x = *(const uint4 *)(bj + (p * ea.b_ps + (long long)(v >> 2) * c.Kb + k) * 2);
+        rb[p][it] = x;
+      }
+  };
   auto gload_fast = [&](int k0) __attribute__((always_inline)) {
     if (k0 < D) {
 #pragma unroll
@@ -182,11 +196,7 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
 #pragma unroll
       for (int it = 0; it < LA; ++it) eload8<SX>(utbase + uo[it] + (long long)(k0 - D) * ESX, oka[it], ra[it]);
     }
-#pragma unroll
-    for (int it = 0; it < LB; ++it) {
-      const int v = tid + it * ENT;
-      eload8<SRC_F32>(bj + ((long long)(v >> 2) * c.Kb + (v & 3) * 8 + k0) * 4, true, rb[it]);
-    }
+    bload(k0, false);
   };
   auto gload_slow = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
@@ -195,11 +205,7 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
       if (k < D) load_raw8<SX>(xbase, (long long)t * D, k, D, t < T, 1 << 30, 0, ra[it]);
       else load_raw8<SX>(utbase, (long long)t * rT, k - D, rT, t < T, 1 << 30, 0, ra[it]);
     }
-#pragma unroll
-    for (int it = 0; it < LB; ++it) {
-      const int v = tid + it * ENT;
-      load_raw8<SRC_F32>(bj, (long long)(v >> 2) * c.Kb, k0 + (v & 3) * 8, K, true, 1 << 30, 0, rb[it]);
-    }
+    bload(k0, true);
   };
   auto lstore = [&](int buf) __attribute__((always_inline)) {
     uint16_t *As = lds + buf * STG, *Bs = As + ASZ;
@@ -209,10 +215,12 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
       eput8<SX, MF, PA>(As, EBM * EKB, eswz(v >> 2, v & 3), ra[it], 1.f);
     }
 #pragma unroll
-    for (int it = 0; it < LB; ++it) {
-      const int v = tid + it * ENT;
-      eput8<SRC_F32, MF, PB>(Bs, D * EKB, eswz(v >> 2, v & 3), rb[it], bscale);
-    }
+    for (int p = 0; p < PB; ++p)
+#pragma unroll
+      for (int it = 0; it < LB; ++it) {
+        const int v = tid + it * ENT;
+        *(uint4 *)(Bs + p * D * EKB + eswz(v >> 2, v & 3)) = rb[p][it];
+      }
   };
   const int aoff = eswz(wm * 64 + fr, fc), boff = eswz(fr, fc);
   // plane products in the order (pa, pb) descending, as in the GEMM kernels; B fragments are
@@ -233,7 +241,7 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int q = 0; q < TN; ++q) acc[i][q] = mfma<MF>(af[i], bf[q], acc[i][q]);
+          for (int q = 0; q < TN; ++q) acc[i][q] = mfma<MF>(bf[q], af[i], acc[i][q]);
       }
     }
   };
@@ -260,61 +268,65 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
     buf ^= 1;
   }
 
-  // ---- quantisation: rows are whole inside a wave -------------------------------------------
-  const float inv = 1.f / bscale;
+  // ---- quantisation and packing ---------------------------------------------------------------
+  // Row m = wm * 64 + 16 i + fr of the tile lives in the four lanes fr + 16 fc, each holding its
+  // columns 16 q + 4 fc + r.  The code of e is rint(e / s) in fp32 (IEEE quotient); it is formed
+  // from e * (1 / s), whose distance from the quotient (< 2e-5 for |e / s| <= 127) only matters
+  // within 1e-4 of a rounding boundary, where the quotient itself is taken.  Each lane ORs the
+  // 4 b bits of its four codes into the row's words in LDS (LSB-first), then the tile's rows are
+  // copied out whole.
+  const float inv = 1.f / bscale;  // a power of two
   const int b = c.bits;
   const int qm = (b >= 2) ? ((1 << (b - 1)) - 1) : 1;
+  const int wpr = D * b / 32;  // 32-bit words per row (D in {64, 128}: integral)
+  for (int w = tid; w < EBM * wpr; w += ENT) rowbits[w] = 0u;
+  __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    float m = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float m = 0.f;
+    for (int q = 0; q < TN; ++q)
 #pragma unroll
-      for (int q = 0; q < TN; ++q) {
+      for (int r = 0; r < 4; ++r) {
         const float v = acc[i][q][r] * inv;
         acc[i][q][r] = v;
         m = fmaxf(m, fabsf(v));
       }
-      m = fmaxf(m, __shfl_xor(m, 1, 64));
-      m = fmaxf(m, __shfl_xor(m, 2, 64));
-      m = fmaxf(m, __shfl_xor(m, 4, 64));
-      m = fmaxf(m, __shfl_xor(m, 8, 64));
-      const int row = wm * 64 + i * 16 + fc * 4 + r;
-      const float sc = (b == 1) ? m : m / (float)qm;
-      if (fr == 0) srow[row] = sc;
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    const int row = wm * 64 + i * 16 + fr;
+    const float sc = (b == 1) ? m : m / (float)qm;
+    if (fc == 0) srow[row] = sc;
+    const float rinv = sc > 0.f ? 1.f / sc : 0.f;
 #pragma unroll
-      for (int q = 0; q < TN; ++q) {
+    for (int q = 0; q < TN; ++q) {
+      uint32_t chunk = 0u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
         const float v = acc[i][q][r];
-        int u;
-        if (b == 1) u = (v >= 0.f) ? 1 : 0;
+        uint32_t u;
+        if (b == 1) u = (v >= 0.f) ? 1u : 0u;
         else if (sc > 0.f) {
-          float qv = rintf(v / sc);
+          const float t = v * rinv;
+          float qv = rintf(t);
+          if (__builtin_expect(fabsf(fabsf(t - qv) - 0.5f) < 1e-4f, 0)) qv = rintf(v / sc);
           qv = fminf(fmaxf(qv, (float)-qm), (float)qm);
-          u = (int)qv + qm;
-        } else u = qm;
-        ucode[row * D + q * 16 + fr] = (uint8_t)u;
+          u = (uint32_t)((int)qv + qm);
+        } else u = (uint32_t)qm;
+        chunk |= u << (r * b);
       }
+      const int bit = (q * 16 + fc * 4) * b, wd = bit >> 5, sh = bit & 31;
+      atomicOr(&rowbits[row * wpr + wd], chunk << sh);
+      if (sh + 4 * b > 32) atomicOr(&rowbits[row * wpr + wd + 1], chunk >> (32 - sh));
     }
+  }
   __syncthreads();
   const long long row0 = (long long)j * T + t0;
   const int nrows = min(EBM, T - t0);
   float *scales = (float *)(ea.scb + c.sc_off);
   for (int rr = tid; rr < nrows; rr += ENT) scales[row0 + rr] = srow[rr];
-  const int wpr = D * b / 32;  // 32-bit words per row (D in {64,128}: integral)
   uint32_t *out = (uint32_t *)(ea.cdb + c.cd_off + row0 * (D * b / 8));
-  for (int w = tid; w < nrows * wpr; w += ENT) {
-    const int rr = w / wpr, wi = w % wpr;
-    const int bit0 = wi * 32;
-    const int e0 = bit0 / b, e1 = min(D - 1, (bit0 + 31) / b);
-    uint32_t word = 0;
-    for (int e = e0; e <= e1; ++e) {
-      uint32_t u = ucode[rr * D + e];
-      int pos = e * b - bit0;
-      if (pos >= 0) word |= (pos < 32) ? (u << pos) : 0u;
-      else word |= u >> (-pos);
-    }
-    out[w] = word;
-  }
+  for (int w = tid; w < nrows * wpr; w += ENT) out[w] = rowbits[w];
 }
 
 // ------------------------------------------------------------------------------------------ decode

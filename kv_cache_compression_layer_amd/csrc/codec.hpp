@@ -12,7 +12,7 @@ struct EncCell {
   long long ut_off;    // U_T [T][rT] (cache dtype) in utb
   long long sc_off;    // fp32 scales [GH*T] in scb
   long long cd_off;    // codes [GH*T][D*bits/8] in cdb
-  long long bcat_off;  // Bcat [GH][D][Kb] in bcat (bytes)
+  long long bcat_off;  // B = [Q ; -D_j Q] as 16-bit planes [plane][GH][D][Kb] in bcat (bytes)
   int kv, am_idx;      // cache selector; index of max |Bcat| in bamax (fp16 split scale)
   int GH, rT, bits, Kb;
 };
@@ -20,7 +20,8 @@ struct EncCell {
 struct EncArgs {
   const char *xk, *xv, *utb;
   char *scb, *cdb;
-  const char *bcat;
+  const char *bcat;   // 16-bit planes of B, plane stride b_ps elements
+  long long b_ps;
   const float *bamax;
   const EncCell *cells;
 };
