@@ -302,6 +302,12 @@ __device__ __forceinline__ double wave_reflector_regs(const double (&x)[TCH], in
   return bet;
 }
 
+// UP (n <= 64 TCH): the sweep touches only the upper triangle of the trailing block (j >= i),
+// read and written once; element (i, j), j > i, adds u v'_j to the row sum of i and u v'_i to the
+// column sum of j, kept per lane for the lane's absolute columns lane + 64 t; the column sums of
+// the waves are added to the row sums in LDS in wave order (deterministic), which takes a third
+// barrier per step.  Half the traffic of the full sweep.  LDS: 5n + 64 TCH nwave doubles.
+template <bool UP>
 __global__ void __launch_bounds__(LT) tridiag_fused_kernel(double *A, long long a_bs, int lda, int n,
                                                            double *d_out, double *e_out, double *refl, double *beta,
                                                            long long t_bs, double *evals, long long ev_bs, int clamp) {
@@ -390,49 +396,114 @@ __global__ void __launch_bounds__(LT) tridiag_fused_kernel(double *A, long long 
       const double bn = last ? 0.0 : sbeta[nxt];
       const double *vn = vnx;
       double *pn = smem + (2 + nxt) * n;
-      for (int i0 = r + 1 + wave * TRB; i0 < n; i0 += nwave * TRB) {
-        double s[TRB], wi[TRB], vi[TRB];
+      if constexpr (UP) {
+        double *prow = smem + 4 * n, *pcol = smem + 5 * n;  // row sums [n]; column sums [nwave][64 TCH]
+        double cacc[TCH];
 #pragma unroll
-        for (int q = 0; q < TRB; ++q) {
-          const int i = min(i0 + q, n - 1);
-          s[q] = 0.0;
-          wi[q] = pk[i] - c * vk[i];
-          vi[q] = vk[i];
-        }
-        for (int j0 = r + 1; j0 < n; j0 += 64 * TCH) {
+        for (int t = 0; t < TCH; ++t) cacc[t] = 0.0;
+        for (int i0 = r + 1 + wave * TRB; i0 < n; i0 += nwave * TRB) {
+          double s[TRB], wi[TRB], vi[TRB], vni[TRB];
+#pragma unroll
+          for (int q = 0; q < TRB; ++q) {
+            const int i = min(i0 + q, n - 1);
+            s[q] = 0.0;
+            wi[q] = pk[i] - c * vk[i];
+            vi[q] = vk[i];
+            vni[q] = last ? 0.0 : vn[i];
+          }
+          const int tstart = i0 >> 6;  // first 64-column chunk holding column i0 (uniform)
           double a[TRB][TCH];
 #pragma unroll
-          for (int q = 0; q < TRB; ++q)
+          for (int t = 0; t < TCH; ++t)
+            if (t >= tstart) {
+              const int j = lane + 64 * t;
 #pragma unroll
-            for (int t = 0; t < TCH; ++t) {
-              const int j = j0 + lane + 64 * t;
-              a[q][t] = (i0 + q < n && j < n) ? W[(long long)(i0 + q) * ldw + j] : 0.0;
+              for (int q = 0; q < TRB; ++q)
+                a[q][t] = (i0 + q < n && j >= i0 + q && j < n) ? W[(long long)(i0 + q) * ldw + j] : 0.0;
             }
 #pragma unroll
-          for (int t = 0; t < TCH; ++t) {
-            const int j = j0 + lane + 64 * t;
-            if (j < n) {
-              const double pj = pk[j] - c * vk[j], vj = vk[j], vnj = last ? 0.0 : vn[j];
+          for (int t = 0; t < TCH; ++t)
+            if (t >= tstart) {
+              const int j = lane + 64 * t;
+              if (j >= i0 && j < n) {
+                const double pj = pk[j] - c * vk[j], vj = vk[j], vnj = last ? 0.0 : vn[j];
 #pragma unroll
-              for (int q = 0; q < TRB; ++q) {
-                if (i0 + q < n) {
-                  const double u = a[q][t] - (vi[q] * pj + wi[q] * vj);
-                  W[(long long)(i0 + q) * ldw + j] = u;
-                  s[q] += u * vnj;
+                for (int q = 0; q < TRB; ++q) {
+                  if (i0 + q < n && j >= i0 + q) {
+                    const double u = a[q][t] - (vi[q] * pj + wi[q] * vj);
+                    W[(long long)(i0 + q) * ldw + j] = u;
+                    s[q] += u * vnj;
+                    if (j > i0 + q) cacc[t] += u * vni[q];
+                  }
                 }
               }
+            }
+          if (!last) {
+#pragma unroll
+            for (int q = 0; q < TRB; ++q) {
+              const double sq = warp_sum_d(s[q]);
+              if (lane == 0 && i0 + q < n) prow[i0 + q] = sq;
             }
           }
         }
         if (!last) {
 #pragma unroll
-          for (int q = 0; q < TRB; ++q) {
-            const double sq = warp_sum_d(s[q]);
-            if (lane == 0 && i0 + q < n) pn[i0 + q] = bn * sq;
+          for (int t = 0; t < TCH; ++t) pcol[wave * 64 * TCH + lane + 64 * t] = cacc[t];
+        }
+        __syncthreads();
+        if (!last) {
+          for (int j = r + 1 + tid; j < n; j += blockDim.x) {
+            double sum = prow[j];
+            for (int w = 0; w < nwave; ++w) sum += pcol[w * 64 * TCH + j];
+            pn[j] = bn * sum;
           }
         }
+        __syncthreads();
+      } else {
+        for (int i0 = r + 1 + wave * TRB; i0 < n; i0 += nwave * TRB) {
+          double s[TRB], wi[TRB], vi[TRB];
+#pragma unroll
+          for (int q = 0; q < TRB; ++q) {
+            const int i = min(i0 + q, n - 1);
+            s[q] = 0.0;
+            wi[q] = pk[i] - c * vk[i];
+            vi[q] = vk[i];
+          }
+          for (int j0 = r + 1; j0 < n; j0 += 64 * TCH) {
+            double a[TRB][TCH];
+#pragma unroll
+            for (int q = 0; q < TRB; ++q)
+#pragma unroll
+              for (int t = 0; t < TCH; ++t) {
+                const int j = j0 + lane + 64 * t;
+                a[q][t] = (i0 + q < n && j < n) ? W[(long long)(i0 + q) * ldw + j] : 0.0;
+              }
+#pragma unroll
+            for (int t = 0; t < TCH; ++t) {
+              const int j = j0 + lane + 64 * t;
+              if (j < n) {
+                const double pj = pk[j] - c * vk[j], vj = vk[j], vnj = last ? 0.0 : vn[j];
+#pragma unroll
+                for (int q = 0; q < TRB; ++q) {
+                  if (i0 + q < n) {
+                    const double u = a[q][t] - (vi[q] * pj + wi[q] * vj);
+                    W[(long long)(i0 + q) * ldw + j] = u;
+                    s[q] += u * vnj;
+                  }
+                }
+              }
+            }
+          }
+          if (!last) {
+#pragma unroll
+            for (int q = 0; q < TRB; ++q) {
+              const double sq = warp_sum_d(s[q]);
+              if (lane == 0 && i0 + q < n) pn[i0 + q] = bn * sq;
+            }
+          }
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
     if (tid == 0) {
       d[n - 1] = W[(long long)(n - 1) * ldw + (n - 1)];
@@ -1023,7 +1094,8 @@ void ensure_lds_attrs() {
   (void)hipFuncSetAttribute((const void *)chol_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tri_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_values_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
-  (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)bisect_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)backtransform_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipGetLastError();
@@ -1043,10 +1115,16 @@ void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d
     hipLaunchKernelGGL(tridiag_values_kernel, dim3(batch), dim3(LT), lds_full, st, A, a_bs, lda, (const int *)nullptr,
                        n, d, e, refl, beta, t_bs, evals, ev_bs, clamp ? 1 : 0, 1);
   } else {
-    const size_t shm = 4 * (size_t)n * sizeof(double);
-    JOLT_REQUIRE(shm <= 150 * 1024, JOLT_EINVAL, "eigensolver: n too large for LDS staging");
-    hipLaunchKernelGGL(tridiag_fused_kernel, dim3(batch), dim3(LT), shm, st, A, a_bs, lda, n, d, e, refl, beta, t_bs,
-                       evals, ev_bs, clamp ? 1 : 0);
+    const size_t shm_up = (5 * (size_t)n + 64 * TCH * (LT / 64)) * sizeof(double);
+    if (n <= 64 * TCH && shm_up <= 150 * 1024) {
+      hipLaunchKernelGGL(tridiag_fused_kernel<true>, dim3(batch), dim3(LT), shm_up, st, A, a_bs, lda, n, d, e, refl,
+                         beta, t_bs, evals, ev_bs, clamp ? 1 : 0);
+    } else {
+      const size_t shm = 4 * (size_t)n * sizeof(double);
+      JOLT_REQUIRE(shm <= 150 * 1024, JOLT_EINVAL, "eigensolver: n too large for LDS staging");
+      hipLaunchKernelGGL(tridiag_fused_kernel<false>, dim3(batch), dim3(LT), shm, st, A, a_bs, lda, n, d, e, refl,
+                         beta, t_bs, evals, ev_bs, clamp ? 1 : 0);
+    }
   }
   HIP_LAUNCH_CHECK();
   // eigenvalues of the tridiagonals: BL lanes per eigenvalue, 256 / BL eigenvalues per block
