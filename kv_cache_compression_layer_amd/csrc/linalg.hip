@@ -821,124 +821,145 @@ __global__ void __launch_bounds__(256) backtransform_kernel(const double *Zin, l
 // multiple of the largest diagonal entry (documented regularisation).
 // LDS: a 32 x 32 diagonal block and a 32 x (n - k0) panel (n <= 544 keeps the panel in LDS).
 // ---------------------------------------------------------------------------------------------
+// value of a double held by lane l (l uniform, typically a compile-time constant): two scalar
+// lane reads instead of an LDS permute, so the factorisation steps of one wave stay in registers
+__device__ __forceinline__ double lane_d(double v, int l) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+  return __hiloint2double(hi, lo);
+}
+
 constexpr int CNB = 32;
 constexpr int CHOL_MAXN_LDS = 544;
 constexpr int CT = 1024;
 
-__global__ void __launch_bounds__(CT) chol_inv_kernel(const double *G, long long g_bs, int ldg, int n, double *Rw,
-                                                      long long r_bs, float *RinvT, long long o_bs, int ld_out,
-                                                      float *amax) {
-  extern __shared__ double sm[];
-  double *Dk = sm;               // [32][33] diagonal block of R
-  double *P = sm + 2 * CNB * 33; // [32][n] panel (row block of R)
-  __shared__ float fred[CT / 64];
-  const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
-  const int lane = tid & 63, wave = tid >> 6, nwave = nt >> 6;
+// The Cholesky factorisation G = R^T R split into launches so that the trailing updates, which
+// carry almost all of the n^3 / 3 flops, spread over the whole GPU.  Per matrix the scratch holds
+// R (n^2, the result), the 32 x 32 diagonal-block inverses used by the triangular inverse, a
+// working copy W of the trailing matrix (n^2), the inverse of the current diagonal block and the
+// pivot floor.  chol_init copies the upper triangle of G into W and clears R; per 32-column
+// panel, chol_diag (one wave per matrix) factors the diagonal block of W into R and inverts it,
+// then chol_update (one workgroup per 32 x 32 upper tile of the trailing block of each matrix)
+// solves the two panel tiles it needs with that inverse, writes the solved tile of R's row block
+// (diagonal tiles only) and subtracts panel^T panel from its tile of W.
+__device__ __forceinline__ long long chol_w_off(int n) { return (long long)n * n + (long long)((n + CNB - 1) / CNB) * CNB * CNB; }
+
+__global__ void __launch_bounds__(256) chol_init_kernel(const double *G, long long g_bs, int ldg, int n, double *Rw,
+                                                        long long r_bs, float *amax) {
+  const int b = blockIdx.y;
   const double *Gb = G + b * g_bs;
-  double *A = Rw + b * r_bs;          // working copy, becomes R (upper)
-  const bool in_lds = (n <= CHOL_MAXN_LDS);
-  double dmax = 0.0;
-  for (int i = 0; i < n; ++i) dmax = fmax(dmax, Gb[(long long)i * ldg + i]);
-  const double floor_piv = fmax(dmax * 1e-28, 1e-300);
-  for (long long idx = tid; idx < (long long)n * n; idx += nt) {
-    int i = (int)(idx / n), j = (int)(idx % n);
-    A[idx] = (j >= i) ? Gb[(long long)i * ldg + j] : 0.0;
+  double *R = Rw + b * r_bs, *W = R + chol_w_off(n);
+  for (long long idx = blockIdx.x * 256LL + threadIdx.x; idx < (long long)n * n; idx += (long long)gridDim.x * 256) {
+    const int i = (int)(idx / n), j = (int)(idx % n);
+    W[idx] = (j >= i) ? Gb[(long long)i * ldg + j] : 0.0;
+    R[idx] = 0.0;
   }
-  if (tid == 0) amax[b] = 0.f;  // max |R^{-1}| is accumulated by tri_inv_kernel
+  if (blockIdx.x == 0 && threadIdx.x < 64) {
+    // pivot floor from the diagonal of G
+    double dmax = 0.0;
+    for (int i = threadIdx.x; i < n; i += 64) dmax = fmax(dmax, Gb[(long long)i * ldg + i]);
+    for (int o = 32; o > 0; o >>= 1) dmax = fmax(dmax, __shfl_xor(dmax, o, 64));
+    if (threadIdx.x == 0) {
+      W[(long long)n * n + CNB * 33] = fmax(dmax * 1e-28, 1e-300);
+      amax[b] = 0.f;  // max |R^{-1}| is accumulated by tri_inv_kernel
+    }
+  }
+}
+
+__global__ void __launch_bounds__(64) chol_diag_kernel(int n, double *Rw, long long r_bs, int k0) {
+  __shared__ double Dk[CNB * 33];
+  const int b = blockIdx.x, c = threadIdx.x;
+  double *R = Rw + b * r_bs, *W = R + chol_w_off(n), *Dvg = W + (long long)n * n;
+  const double floor_piv = Dvg[CNB * 33];
+  const int kb = min(CNB, n - k0);
+  // right-looking Cholesky of the diagonal block: lane c holds column c (a[r] = W[r][c], r <= c);
+  // row j of the factor is published in LDS and read back by every lane (one wave: LDS order is
+  // program order, no barrier)
+  double a[CNB];
+#pragma unroll
+  for (int r = 0; r < CNB; ++r) a[r] = (c < kb && r <= c && r < kb) ? W[(long long)(k0 + r) * n + k0 + c] : 0.0;
+#pragma unroll
+  for (int jj = 0; jj < CNB; ++jj) {
+    if (jj < kb) {
+      const double piv = sqrt(fmax(lane_d(a[jj], jj), floor_piv));
+      if (c == jj) a[jj] = piv;
+      else if (c > jj) a[jj] /= piv;  // R[jj][c]
+      if (c < CNB) Dk[jj * 33 + c] = (c >= jj) ? a[jj] : 0.0;
+#pragma unroll
+      for (int r = jj + 1; r < CNB; ++r) {
+        const double rjr = Dk[jj * 33 + r];  // R[jj][r]
+        if (r <= c) a[r] -= rjr * a[jj];
+      }
+    }
+  }
+  if (c < kb) {
+#pragma unroll
+    for (int r = 0; r < CNB; ++r)
+      if (r < kb && r <= c) R[(long long)(k0 + r) * n + k0 + c] = a[r];
+  }
+  // inverse of the diagonal block: lane c solves R_kk x = e_c by back substitution
+  double x[CNB];
+#pragma unroll
+  for (int r = CNB - 1; r >= 0; --r) {
+    double v = (r == c) ? 1.0 : 0.0;
+#pragma unroll
+    for (int q = r + 1; q < CNB; ++q)
+      if (q <= c) v -= Dk[r * 33 + q] * x[q];
+    x[r] = (r <= c && r < kb && c < kb) ? v / Dk[r * 33 + r] : 0.0;
+  }
+  if (c < CNB) {
+#pragma unroll
+    for (int r = 0; r < CNB; ++r) Dvg[r * 33 + c] = x[r];  // (R_kk^{-1})[r][c]
+  }
+}
+
+// grid (nt * nt, batch), nt = ceil(rem / 32): tile (ti, tj), tj >= ti, of the trailing upper block
+__global__ void __launch_bounds__(256) chol_update_kernel(double *Rw, long long r_bs, int n, int k0) {
+  __shared__ double Dv[CNB * 33];
+  __shared__ double Pi[CNB][33], Pj[CNB][33], Ai[CNB][33], Aj[CNB][33];
+  const int kb = min(CNB, n - k0), base = k0 + kb, rem = n - base;
+  const int ntl = (rem + 31) / 32;
+  const int ti = blockIdx.x / ntl, tj = blockIdx.x % ntl, b = blockIdx.y;
+  if (tj < ti) return;
+  double *R = Rw + b * r_bs, *W = R + chol_w_off(n);
+  const double *Dvg = W + (long long)n * n;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < CNB * 33; e += 256) Dv[e] = Dvg[e];
+  for (int e = tid; e < CNB * 32; e += 256) {
+    const int q = e / 32, x = e % 32;
+    const int ci = ti * 32 + x, cj = tj * 32 + x;
+    Ai[q][x] = (q < kb && ci < rem) ? W[(long long)(k0 + q) * n + base + ci] : 0.0;
+    Aj[q][x] = (q < kb && cj < rem) ? W[(long long)(k0 + q) * n + base + cj] : 0.0;
+  }
   __syncthreads();
-  for (int k0 = 0; k0 < n; k0 += CNB) {
-    const int kb = min(CNB, n - k0), rem = n - k0 - kb;
-    // (1) diagonal block: unblocked right-looking Cholesky by wave 0 alone, lane c holding column
-    //     c of the block in registers; row j of the factor reaches the other lanes by shuffles,
-    //     so the 32 sequential steps need no workgroup barrier
-    if (wave == 0) {
-      const int c = lane;
-      double a[CNB];
-#pragma unroll
-      for (int r = 0; r < CNB; ++r) a[r] = (c < kb && r <= c && r < kb) ? A[(long long)(k0 + r) * n + k0 + c] : 0.0;
-#pragma unroll
-      for (int j = 0; j < CNB; ++j) {
-        if (j < kb) {
-          const double piv = sqrt(fmax(__shfl(a[j], j, 64), floor_piv));
-          if (c == j) a[j] = piv;
-          else if (c > j) a[j] /= piv;  // row j of R, column c
-#pragma unroll
-          for (int r = j + 1; r < CNB; ++r) {
-            const double rjr = __shfl(a[j], r, 64);  // R[j][r], held by lane r
-            if (r <= c) a[r] -= rjr * a[j];
-          }
-        }
-      }
-      if (c < CNB) {
-#pragma unroll
-        for (int r = 0; r < CNB; ++r) {
-          const double v = (r <= c) ? a[r] : 0.0;
-          Dk[r * 33 + c] = v;
-          if (c < kb && r < kb) A[(long long)(k0 + r) * n + k0 + c] = v;
-        }
-      }
+  // solved panel tiles: P[i][x] = sum_{q <= i} (R_kk^{-1})[q][i] A[q][x]
+  for (int e = tid; e < CNB * 32; e += 256) {
+    const int i = e / 32, x = e % 32;
+    double vi = 0.0, vj = 0.0;
+    for (int q = 0; q <= i; ++q) {
+      const double d = Dv[q * 33 + i];
+      vi += d * Ai[q][x];
+      vj += d * Aj[q][x];
     }
-    __syncthreads();
-    // (2) panel: R[k0.., c] = R_kk^{-T} A[k0.., c], forward substitution per column
-    for (int c = tid; c < rem; c += nt) {
-      double x[CNB];
-#pragma unroll
-      for (int i = 0; i < CNB; ++i) {
-        double v = (i < kb) ? A[(long long)(k0 + i) * n + k0 + kb + c] : 0.0;
-#pragma unroll
-        for (int q = 0; q < CNB; ++q)
-          if (q < i) v -= Dk[q * 33 + i] * x[q];
-        x[i] = (i < kb) ? v / Dk[i * 33 + i] : 0.0;
-      }
-#pragma unroll
-      for (int i = 0; i < CNB; ++i)
-        if (i < kb) {
-          A[(long long)(k0 + i) * n + k0 + kb + c] = x[i];
-          if (in_lds) P[i * rem + c] = x[i];
-        }
-    }
-    __syncthreads();
-    // (3) trailing update A22 -= panel^T panel (upper triangle), 4 x 4 register blocks; the panel
-    //     is read from LDS or from global memory by separate loops (a pointer that may be either
-    //     would compile to flat loads)
-    const int nb4 = (rem + 3) / 4;
-    auto trailing = [&](const double *pan, long long pan_ld) __attribute__((always_inline)) {
-      for (int blk = tid; blk < nb4 * nb4; blk += nt) {
-        const int bi = blk / nb4, bj = blk % nb4;
-        if (bj < bi) continue;
-        double acc[4][4] = {};
-        for (int q = 0; q < kb; ++q) {
-          double u[4], v[4];
-          const double *src = pan + q * pan_ld;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int ii = bi * 4 + t, jj = bj * 4 + t;
-            u[t] = (ii < rem) ? src[ii] : 0.0;
-            v[t] = (jj < rem) ? src[jj] : 0.0;
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) acc[t][w] += u[t] * v[w];
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int ii = bi * 4 + t, jj = bj * 4 + w;
-            if (ii < rem && jj < rem && jj >= ii) A[(long long)(k0 + kb + ii) * n + k0 + kb + jj] -= acc[t][w];
-          }
-      }
-    };
-    if (in_lds) trailing(P, rem);
-    else trailing(A + (long long)k0 * n + k0 + kb, n);
-    __syncthreads();
+    Pi[i][x] = vi;
+    Pj[i][x] = vj;
+    const int cj = tj * 32 + x;
+    if (ti == tj && i < kb && cj < rem) R[(long long)(k0 + i) * n + base + cj] = vj;
   }
-  // the triangular inverse and the fp32 output run in diag_inv_kernel / tri_inv_kernel
-  (void)RinvT;
-  (void)o_bs;
-  (void)ld_out;
-  (void)fred;
+  __syncthreads();
+  const int r = tid >> 3, c0 = (tid & 7) * 4;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int q = 0; q < kb; ++q) {
+    const double u = Pi[q][r];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc[w] += u * Pj[q][c0 + w];
+  }
+  const int ii = ti * 32 + r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int jj = tj * 32 + c0 + w;
+    if (ii < rem && jj < rem && jj >= ii) W[(long long)(base + ii) * n + base + jj] -= acc[w];
+  }
 }
 
 // Inverses of the 32 x 32 diagonal blocks of R (upper), one wave per block: lane c solves
@@ -959,10 +980,10 @@ __global__ void __launch_bounds__(64) diag_inv_kernel(double *Rw, long long r_bs
     double v = (r == c) ? 1.0 : 0.0;
 #pragma unroll
     for (int q = r + 1; q < CNB; ++q) {
-      const double rq = __shfl(a[r], q, 64);  // R[r][q]
+      const double rq = lane_d(a[r], q);  // R[r][q]
       if (q <= c) v -= rq * x[q];
     }
-    const double rr = __shfl(a[r], r, 64);
+    const double rr = lane_d(a[r], r);
     x[r] = (r <= c) ? v / rr : 0.0;
   }
   if (c < CNB) {
@@ -1091,7 +1112,6 @@ void ensure_lds_attrs() {
   if (hipDeviceGetAttribute(&maxsh, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) maxsh = 65536;
   const int want = maxsh - 2048;  // leave room for the kernels' static LDS
   // best effort: the runtime may already allow the full amount
-  (void)hipFuncSetAttribute((const void *)chol_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tri_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_values_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
@@ -1154,17 +1174,30 @@ void sym_eigvecs(const double *d, const double *e, const double *refl, const dou
   HIP_LAUNCH_CHECK();
 }
 
-long long chol_scratch_doubles(int n) { return (long long)n * n + (long long)((n + CNB - 1) / CNB) * CNB * CNB; }
+long long chol_scratch_doubles(int n) {
+  return 2LL * n * n + (long long)((n + CNB - 1) / CNB) * CNB * CNB + CNB * 33 + 8;
+}
 
 void chol_inv(const double *G, long long g_bs, int ldg, int n, int batch, double *Rw, long long r_bs, float *RinvT,
               long long o_bs, int ld_out, float *amax, hipStream_t st) {
   JOLT_REQUIRE(n >= 1 && n <= CHOL_MAXN_LDS, JOLT_EINVAL, "Cholesky QR: panel width above 544 is not supported");
   JOLT_REQUIRE(r_bs >= chol_scratch_doubles(n), JOLT_EINVAL, "Cholesky QR: scratch too small per matrix");
-  size_t shm = (size_t)(2 * CNB * 33 + CNB * n) * sizeof(double);
   ensure_lds_attrs();
-  hipLaunchKernelGGL(chol_inv_kernel, dim3(batch), dim3(CT), shm, st, G, g_bs, ldg, n, Rw, r_bs, RinvT, o_bs, ld_out,
-                     amax);
-  HIP_LAUNCH_CHECK();
+  {
+    const long long nn = (long long)n * n;
+    hipLaunchKernelGGL(chol_init_kernel, dim3((unsigned)std::min<long long>((nn + 255) / 256, 1024), batch), dim3(256),
+                       0, st, G, g_bs, ldg, n, Rw, r_bs, amax);
+    HIP_LAUNCH_CHECK();
+    for (int k0 = 0; k0 < n; k0 += CNB) {
+      hipLaunchKernelGGL(chol_diag_kernel, dim3(batch), dim3(64), 0, st, n, Rw, r_bs, k0);
+      HIP_LAUNCH_CHECK();
+      const int rem = n - k0 - std::min(CNB, n - k0);
+      if (rem <= 0) break;
+      const int ntl = (rem + 31) / 32;
+      hipLaunchKernelGGL(chol_update_kernel, dim3(ntl * ntl, batch), dim3(256), 0, st, Rw, r_bs, n, k0);
+      HIP_LAUNCH_CHECK();
+    }
+  }
   const int nblk = (n + CNB - 1) / CNB;
   hipLaunchKernelGGL(diag_inv_kernel, dim3(nblk, batch), dim3(64), 0, st, Rw, r_bs, n);
   HIP_LAUNCH_CHECK();
