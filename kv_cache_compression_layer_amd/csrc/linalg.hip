@@ -1055,50 +1055,62 @@ __global__ void __launch_bounds__(512) tri_inv_kernel(const double *Rw, long lon
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// H[b][c][c'] = sum_m P[b][c][m] P[b][c'][m] in fp64 from fp32 rows (64 x 64 tiles, symmetric).
-// ---------------------------------------------------------------------------------------------
+// H[b] (fp64) = P[b] P[b]^T for fp32 rows P[b] [rows][ldp] (K columns): products of fp32 values
+// are exact in fp64, accumulated by the fp64 matrix cores.  One block per 64 x 64 lower tile
+// (mirrored into the upper one); each wave owns a 32 x 32 quadrant as 2 x 2 blocks of
+// v_mfma_f64_16x16x4 (lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and receives
+// C[4 v + l / 16][l % 16] in its v-th value).  32-deep slices of both row blocks are staged in LDS.
+typedef double d4 __attribute__((ext_vector_type(4)));
 __global__ void __launch_bounds__(256) gram64_kernel(const float *P, long long p_bs, int ldp, int rows, int K,
                                                      double *H, long long h_bs, int ldh) {
-  __shared__ double As[16][65], Bs[16][65];
+  constexpr int KT = 32;
+  __shared__ float As[64][KT + 1], Bs[64][KT + 1];
   const int b = blockIdx.z;
   const int ti = blockIdx.y, tj = blockIdx.x;
   if (tj > ti) return;
   const int r0 = ti * 64, c0 = tj * 64;
   const float *Pb = P + b * p_bs;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-  double acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int idx = threadIdx.x; idx < 16 * 64; idx += 256) {
-      int kk = idx & 15, r = idx >> 4;
-      int k = k0 + kk;
-      As[kk][r] = (r0 + r < rows && k < K) ? (double)Pb[(long long)(r0 + r) * ldp + k] : 0.0;
-      Bs[kk][r] = (c0 + r < rows && k < K) ? (double)Pb[(long long)(c0 + r) * ldp + k] : 0.0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1, rr = lane & 15, kq = lane >> 4;
+  d4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
+  for (int k0 = 0; k0 < K; k0 += KT) {
+    for (int e = tid; e < 64 * KT; e += 256) {
+      const int r = e / KT, k = e % KT, kk = k0 + k;
+      As[r][k] = (r0 + r < rows && kk < K) ? Pb[(long long)(r0 + r) * ldp + kk] : 0.f;
+      Bs[r][k] = (c0 + r < rows && kk < K) ? Pb[(long long)(c0 + r) * ldp + kk] : 0.f;
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      double a[4], bb[4];
+    for (int ks = 0; ks < KT; ks += 4) {
+      double a[2], bb[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = As[kk][ty * 4 + i]; bb[i] = Bs[kk][tx * 4 + i]; }
+      for (int i = 0; i < 2; ++i) a[i] = (double)As[wr * 32 + i * 16 + rr][ks + kq];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 2; ++j) bb[j] = (double)Bs[wc * 32 + j * 16 + rr][ks + kq];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * bb[j];
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
     }
     __syncthreads();
   }
   double *Hb = H + b * h_bs;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int r = r0 + ty * 4 + i, c = c0 + tx * 4 + j;
-      if (r < rows && c < rows) {
-        Hb[(long long)r * ldh + c] = acc[i][j];
-        Hb[(long long)c * ldh + r] = acc[i][j];
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = r0 + wr * 32 + i * 16 + 4 * v + kq, c = c0 + wc * 32 + j * 16 + rr;
+        if (r < rows && c < rows && c <= r) {
+          Hb[(long long)r * ldh + c] = acc[i][j][v];
+          Hb[(long long)c * ldh + r] = acc[i][j][v];
+        }
       }
-    }
 }
 
 }  // namespace
