@@ -17,27 +17,24 @@ namespace {
 
 constexpr int AT = 1024;
 
+// The grids are strictly ascending (bits, r_T and r_d are validated so on entry), so the
+// tie-break order (b, r_T, r_d) is the order of the table index (b slowest, r_d fastest).
 struct Best {
   double cost;
   long long s;
-  int b, rT, rd, idx;
+  int idx;
 };
 
 __device__ __forceinline__ bool less_than(const Best &x, const Best &y) {
   if (x.cost != y.cost) return x.cost < y.cost;
   if (x.s != y.s) return x.s < y.s;
-  if (x.b != y.b) return x.b < y.b;
-  if (x.rT != y.rT) return x.rT < y.rT;
-  return x.rd < y.rd;
+  return x.idx < y.idx;
 }
 
 __device__ Best shfl_best(const Best &v, int o) {
   Best r;
   r.cost = __shfl_xor(v.cost, o, 64);
   r.s = __shfl_xor(v.s, o, 64);
-  r.b = __shfl_xor(v.b, o, 64);
-  r.rT = __shfl_xor(v.rT, o, 64);
-  r.rd = __shfl_xor(v.rd, o, 64);
   r.idx = __shfl_xor(v.idx, o, 64);
   return r;
 }
@@ -85,24 +82,37 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
   }
   __syncthreads();
 
-  // (3) evaluation of the per-cell minimisers at lambda: one wave per cell
+  // (3) evaluation of the per-cell minimisers at lambda: one wave per cell; a lane visits its
+  // candidates in ascending index order (so an equal cost and size never replaces its best) and
+  // reads them in batches of 8 so that their loads are in flight together
+  constexpr int EB = 8;
   auto evaluate = [&](double lam) {
     for (int c = wave; c < nc; c += nw) {
       Best best;
       best.cost = INFINITY;
       best.s = LLONG_MAX;
-      best.b = best.rT = best.rd = INT_MAX;
       best.idx = 0;  // any finite candidate replaces it; keeps the index valid for non-finite tables
-      for (int i = lane; i < per; i += 64) {
-        const long long w = (long long)c * per + i;
-        Best cand;
-        cand.s = a.s[w];
-        cand.cost = __dadd_rn(a.e[w], __dmul_rn(lam, (double)cand.s));
-        cand.b = a.bits[i / (nT * nD)];
-        cand.rT = a.rT_grid[(i / nD) % nT];
-        cand.rd = a.rd_grid[i % nD];
-        cand.idx = i;
-        if (less_than(cand, best)) best = cand;
+      const double *ec = a.e + (long long)c * per;
+      const long long *sc = a.s + (long long)c * per;
+      for (int i0 = lane; i0 < per; i0 += 64 * EB) {
+        double ev[EB];
+        long long sv[EB];
+#pragma unroll
+        for (int u = 0; u < EB; ++u) {
+          const int i = min(i0 + 64 * u, per - 1);
+          ev[u] = ec[i];
+          sv[u] = sc[i];
+        }
+#pragma unroll
+        for (int u = 0; u < EB; ++u) {
+          const int i = i0 + 64 * u;
+          const double cost = __dadd_rn(ev[u], __dmul_rn(lam, (double)sv[u]));
+          if (i < per && (cost < best.cost || (cost == best.cost && sv[u] < best.s))) {
+            best.cost = cost;
+            best.s = sv[u];
+            best.idx = i;
+          }
+        }
       }
       for (int o = 32; o > 0; o >>= 1) {
         Best oth = shfl_best(best, o);
