@@ -48,10 +48,10 @@ def parse():
 
 # the dominant kernel of the workload: the projection P^T = Q^T X (fp32 Q in two fp16 planes
 # times the fp16 cache), one launch over the 16 cells
-# (one launch covers all 16 cells, split 16-fold along K = T; the launch shape is set by the
+# (one launch covers all 16 cells, split 4-fold along K = T; the launch shape is set by the
 # library's sequencing, hence api.cpp among the sources whose change invalidates the counters)
 TRAFFIC_KERNEL = {"stage": "project_gemm", "name": "gemm_dma_kernel<0, 2, 1, 3, 8, 3, 4, 2>", "cells_per_launch": 16,
-                  "splits": 16,
+                  "splits": 4,
                   "sources": ["kv_cache_compression_layer_amd/csrc/gemm_dma.hip",
                               "kv_cache_compression_layer_amd/csrc/gemm_core.hpp",
                               "kv_cache_compression_layer_amd/csrc/common.hpp",

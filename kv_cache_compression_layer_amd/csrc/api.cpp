@@ -248,8 +248,10 @@ struct Sizes {
   long long part_view;     // per spectra view (the first n_views of them are disjoint slices)
 };
 
-// K splits of the FlashJoLT projection: one per 4096 tokens, at most 16 (K = T is the long side)
-int project_splits(const Plan &pl) { return (int)std::min<long long>(16, std::max<long long>(1, pl.T / 4096)); }
+// K splits of the FlashJoLT projection: one per 16384 tokens, at most 4 (K = T is the long side).
+// Measured on the 8B shape (3 x 16 output tiles per cell): 4 splits beat 8 and 16, whose extra
+// partial sums cost more write and reduction traffic than the shorter blocks gain.
+int project_splits(const Plan &pl) { return (int)std::min<long long>(4, std::max<long long>(1, pl.T / 16384)); }
 
 long long part_elems_for(const Plan &pl, int kmax, int nb) {
   long long pe = 0;
@@ -491,7 +493,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   // first split into its 16-bit planes.
   const int pns = project_splits(pl);
   auto project = [&](const float *Qt, const float *q_amax, float *c_amax) {
-    const bool planes = dma_ok && pns > 1 && T % 32 == 0;
+    const bool planes = dma_ok && T % 32 == 0;
     if (planes) {
       Stage prof_s("split_planes", st);
       split_planes(pl.xmf(), Qt, ell * Tld, Tld, (int)ell, (int)T, (int)T, b.pln, P32 * ell * Tld, ell * Tld, Tld,
@@ -507,6 +509,11 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       g.C = b.Pt; g.c_ld = Mf; g.c_bs = ell * Mf;
       g.C2 = b.P2; g.c2_ld = ld; g.c2_bs = Mf * ld;
       g.c_amax = c_amax;
+      if (planes) {
+        GemmArgs h = g;
+        h.A = b.pln; h.a_bs = P32 * ell * Tld; h.a_ps = ell * Tld;
+        if (gemm_dma(pl.xmf(), P32, 1, h, nb, 1, st)) return;
+      }
       gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, 1, st);
       return;
     }

@@ -6,15 +6,16 @@
 // plane products taken in the same order inside each 32-deep k step, so every output element
 // sees the same sequence of fp32 accumulations as there.  What differs is how the matrix cores
 // are fed:
-//   * one wave per SIMD, each owning TM x TN 16 x 16 subtiles (up to 128 x 128) with its
-//     accumulators in AGPRs, four waves per block (2 x 2): half the LDS reads per MFMA of two
-//     64 x 128 waves;
+//   * eight waves per block (4 x 2), two per SIMD, each owning TM x TN 16 x 16 subtiles (48 x 128
+//     for the fp32-plane products: 192 x 256 blocks) with the accumulators in registers;
 //   * operand tiles go from global memory straight into LDS (no staging registers, no VALU):
 //     lane l of a DMA instruction writes bytes [16 l, 16 l + 16) of a 1 KB run, i.e. chunk l % 4
 //     of row l / 4 of a 16-row group, so the lane loads whichever logical chunk the row's XOR
 //     permutation puts there and the fragment reads stay free of bank conflicts;
-//   * three LDS stages: stage s + 2 is requested before stage s is multiplied, so global latency
-//     is covered by two stages of matrix-core work.
+//   * NS LDS stages: stage s + NS - 1 is requested before stage s is multiplied, so global
+//     latency is covered by NS - 1 stages of matrix-core work;
+//   * fragment reads are issued in the order the MFMAs consume them (pinned by scheduling
+//     barriers), so a wave's first MFMAs start after two reads instead of after the whole stage.
 // Operands are zero-padded along K to a multiple of 32 in memory; rows past M (N) read a valid
 // row and their results are dropped.
 #include <type_traits>
@@ -125,11 +126,15 @@ template <class C, int PA, int PB, int TM, int TN>
 __device__ __forceinline__ void read_frags(const lds16 *__restrict__ src, int aoff, int boff,
                                            Frags<C, PA, PB, TM, TN> &f) {
   constexpr int PB0 = (PB - 1 < C::MAXO - (PA - 1)) ? PB - 1 : (C::MAXO - (PA - 1) > 0 ? C::MAXO - (PA - 1) : 0);
+  // (a scheduling barrier after each read pins the issue order, which the scheduler would otherwise
+  // regroup by address so that the first MFMA waits for nearly every read of the stage)
   auto ra = [&](int p, int i) __attribute__((always_inline)) {
     f.a[p][i] = *(const lds_u32x4 *)(src + p * C::BM * DK + i * 16 * DK + aoff);
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto rb = [&](int p, int j) __attribute__((always_inline)) {
     f.b[p][j] = *(const lds_u32x4 *)(src + C::ASZ + p * C::BN * DK + j * 16 * DK + boff);
+    __builtin_amdgcn_sched_barrier(0);
   };
   ra(PA - 1, 0);
 #pragma unroll
