@@ -183,9 +183,15 @@ __global__ void __launch_bounds__(NT) gemm_kernel(GemmArgs g) {
         }
       }
     }
-  if (g.c_amax) {
+  if (g.c_amax) {  // one atomic per workgroup
+    __shared__ float wred[NT / 64];
     lmax = warp_max(lmax);
-    if (lane == 0) atomicMax((unsigned int *)(g.c_amax + (long long)batch * g.c_amax_bs), __float_as_uint(lmax));
+    if (lane == 0) wred[threadIdx.x >> 6] = lmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 1; w < NT / 64; ++w) lmax = fmaxf(lmax, wred[w]);
+      atomicMax((unsigned int *)(g.c_amax + (long long)batch * g.c_amax_bs), __float_as_uint(lmax));
+    }
   }
 }
 

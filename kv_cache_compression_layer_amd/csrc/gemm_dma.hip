@@ -344,6 +344,8 @@ gemm_dma_kernel(GemmArgs g) {
       }
     }
   if (g.c_amax) {
+    // one atomic per wave: a second LDS object here would cost the main loop its alias-free
+    // LDS accesses (the compiler then waits for every DMA before each fragment read)
     lmax = warp_max(lmax);
     if (lane == 0) atomicMax((unsigned int *)(g.c_amax + (long long)batch * g.c_amax_bs), __float_as_uint(lmax));
   }

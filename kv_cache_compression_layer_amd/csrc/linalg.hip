@@ -81,7 +81,11 @@ __global__ void __launch_bounds__(256) bisect_kernel(const double *d_in, const d
     if (fabs(q) < pivmin) q = -pivmin;
     cnt += (q < 0.0);
     for (int i = 1; i < n; ++i) {
-      q = (sd[i] - x) - se2[i - 1] / q;
+      // e_{i-1}^2 / q by the hardware reciprocal and one Newton step (within an ulp or two of the
+      // rounded quotient: the count keeps the backward stability of the recurrence)
+      double y = __builtin_amdgcn_rcp(q);
+      y = fma(y, fma(-q, y, 1.0), y);
+      q = (sd[i] - x) - se2[i - 1] * y;
       if (fabs(q) < pivmin) q = -pivmin;
       cnt += (q < 0.0);
     }
@@ -814,6 +818,94 @@ __global__ void __launch_bounds__(256) backtransform_kernel(const double *Zin, l
   }
 }
 
+// Register variant for n <= 64 NC: each wave owns VPW eigenvector rows, lane l holding entries
+// l + 64 t, and walks all reflectors on its own (no workgroup barriers): per reflector one dot
+// product per row (lane partials, wave sum) and the rank-one update, with the next reflector's
+// entries loaded while the current one is applied.
+template <int NC, int VPW>
+__global__ void __launch_bounds__(256) backtransform_regs_kernel(const double *Zin, long long z_bs, const double *refl,
+                                                                 const double *beta, long long t_bs, int n,
+                                                                 const int *k_of, double *out64, float *out32,
+                                                                 long long out_bs, int out_ld) {
+  const int b = blockIdx.y, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k = min(k_of[b], n);
+  const int q0 = (blockIdx.x * (blockDim.x >> 6) + wave) * VPW;
+  if (q0 >= k) return;
+  const double *Zb = Zin + b * z_bs;
+  const double *Rb = refl + b * t_bs * (long long)n;
+  const double *bb = beta + b * t_bs;
+  double z[VPW][NC];
+#pragma unroll
+  for (int q = 0; q < VPW; ++q)
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      const int p = lane + 64 * t;
+      z[q][t] = (q0 + q < k && p < n) ? Zb[(long long)(q0 + q) * n + p] : 0.0;
+    }
+  // reflector kk holds v at absolute columns kk + 1 .. n - 1 of row kk
+  auto load_v = [&](int kk, double (&v)[NC]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      const int p = lane + 64 * t;
+      v[t] = (kk >= 0 && p > kk && p < n) ? Rb[(long long)kk * n + p] : 0.0;
+    }
+  };
+  double v[NC], vn[NC];
+  load_v(n - 3, v);
+  for (int kk = n - 3; kk >= 0; --kk) {
+    load_v(kk - 1, vn);
+    const double bt = bb[kk];
+    if (bt != 0.0) {
+#pragma unroll
+      for (int q = 0; q < VPW; ++q) {
+        double s = 0.0;
+#pragma unroll
+        for (int t = 0; t < NC; ++t) s += v[t] * z[q][t];
+        const double c = bt * warp_sum_d(s);
+#pragma unroll
+        for (int t = 0; t < NC; ++t) z[q][t] -= c * v[t];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NC; ++t) v[t] = vn[t];
+  }
+  // sign normalisation (largest-magnitude entry positive, first index on ties) and output
+#pragma unroll
+  for (int q = 0; q < VPW; ++q) {
+    if (q0 + q >= k) break;
+    double best = -1.0;
+    int bi = 0;
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      const int p = lane + 64 * t;
+      const double a = fabs(z[q][t]);
+      if (p < n && a > best) { best = a; bi = p; }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ob = __shfl_xor(best, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    }
+    double val = 0.0;
+#pragma unroll
+    for (int t = 0; t < NC; ++t)
+      if (lane + 64 * t == bi) val = z[q][t];
+    val = __shfl(val, bi & 63, 64);
+    const double sg = (val < 0.0) ? -1.0 : 1.0;
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      const int p = lane + 64 * t;
+      if (p < n) {
+        const double x = sg * z[q][t];
+        const long long o = b * out_bs + (long long)(q0 + q) * out_ld + p;
+        if (out64) out64[o] = x;
+        if (out32) out32[o] = (float)x;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Cholesky G = R^T R (R upper, fp64), right-looking in 32-column panels, one workgroup per
 // matrix; the inverse R^{-1} follows in diag_inv_kernel and tri_inv_kernel, which write
@@ -1177,6 +1269,22 @@ void sym_eigvecs(const double *d, const double *e, const double *refl, const dou
   hipLaunchKernelGGL(invit_kernel, dim3(batch), dim3(IT), 2 * (size_t)n * sizeof(double), st, d, e, t_bs, evals,
                      ev_bs, k_dev, (const int *)nullptr, n, Zw, z_bs, work, w_bs, kmax);
   HIP_LAUNCH_CHECK();
+  if (n <= 64 * 9) {
+    // register variant: 4 rows per wave, 4 waves per workgroup
+    constexpr int VPW = 4;
+    dim3 g2((kmax + 4 * VPW - 1) / (4 * VPW), batch);
+    if (n <= 128)
+      hipLaunchKernelGGL((backtransform_regs_kernel<2, VPW>), g2, dim3(256), 0, st, Zw, z_bs, refl, beta, t_bs, n, k_dev,
+                         out64, out32, out_bs, out_ld);
+    else if (n <= 256)
+      hipLaunchKernelGGL((backtransform_regs_kernel<4, VPW>), g2, dim3(256), 0, st, Zw, z_bs, refl, beta, t_bs, n, k_dev,
+                         out64, out32, out_bs, out_ld);
+    else
+      hipLaunchKernelGGL((backtransform_regs_kernel<9, VPW>), g2, dim3(256), 0, st, Zw, z_bs, refl, beta, t_bs, n, k_dev,
+                         out64, out32, out_bs, out_ld);
+    HIP_LAUNCH_CHECK();
+    return;
+  }
   ensure_lds_attrs();
   int vb = std::max(1, std::min(32, (int)((60 * 1024) / (n * 8)) - 1));
   size_t shm = ((size_t)vb * n + n + 64) * sizeof(double);

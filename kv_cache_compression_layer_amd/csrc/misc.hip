@@ -178,14 +178,30 @@ __global__ void bcat_q_kernel(float *Bcat, int ncells, int GH, int D, int Kb, co
   }
 }
 
-__global__ void amax_kernel(const float *x, long long per, long long bs, float *out) {
+// max |x| of each cell: 16-byte loads where the cell is aligned, one atomic per workgroup (the
+// per-wave atomics of a wide grid all hit the same word and serialise in L2)
+__global__ void __launch_bounds__(256) amax_kernel(const float *x, long long per, long long bs, float *out) {
+  __shared__ float red[4];
   const int cell = blockIdx.y;
   const float *p = x + cell * bs;
+  const long long stride = (long long)gridDim.x * 256, i0 = blockIdx.x * 256LL + threadIdx.x;
   float m = 0.f;
-  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < per; i += (long long)gridDim.x * blockDim.x)
-    m = fmaxf(m, fabsf(p[i]));
+  long long tail = 0;
+  if ((((uintptr_t)p) & 15) == 0) {
+    const long long n4 = per / 4;
+    const float4 *p4 = (const float4 *)p;
+    for (long long i = i0; i < n4; i += stride) {
+      const float4 v = p4[i];
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    tail = n4 * 4;
+  }
+  for (long long i = tail + i0; i < per; i += stride) m = fmaxf(m, fabsf(p[i]));
   m = warp_max(m);
-  if ((threadIdx.x & 63) == 0) atomicMax((unsigned int *)(out + cell), __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax((unsigned int *)(out + cell), __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 // Xt[b][j][d][t] = X[b][j][t][d] with 16-byte global accesses on both sides: a 128-token x
@@ -340,7 +356,7 @@ void bcat_q(float *Bcat, int ncells, int GH, int D, int Kb, const float *Qt, hip
 }
 void amax_cells(const float *x, long long per, long long bs, int ncells, float *out, hipStream_t st) {
   fill_f32(out, ncells, 0.f, st);
-  int g = (int)std::min<long long>((per + 255) / 256, 1024);
+  int g = (int)std::min<long long>((per + 4095) / 4096, 128);  // about 16 elements per thread, at most 128 groups per cell
   hipLaunchKernelGGL(amax_kernel, dim3(std::max(g, 1), ncells), dim3(256), 0, st, x, per, bs, out);
   HIP_LAUNCH_CHECK();
 }
