@@ -192,6 +192,8 @@ Plan make_plan(const jolt_cache_desc *d, const jolt_params *p) {
 struct Bufs {
   // common
   float *part;
+  float *fpart;  // feature Gram partials (own region: that stage may run beside the token stages)
+  long long fpart_elems;
   double *Gd64, *dD, *eD, *betaD, *evD;
   double *specT, *specD, *norm2;
   // flash / exact token stage
@@ -253,6 +255,12 @@ struct Sizes {
 // partial sums cost more write and reduction traffic than the shorter blocks gain.
 int project_splits(const Plan &pl) { return (int)std::min<long long>(4, std::max<long long>(1, pl.T / 16384)); }
 
+// split-K partials of the unprojected feature Gram (K = GH T_ld, padding included)
+long long feature_part_elems(const Plan &pl, int nb) {
+  const int ns = nsplit_for((long long)pl.GH * pl.T_ld, 1, nb, 8192);
+  return rup((long long)nb * ns * pl.D * pl.D, 64);
+}
+
 long long part_elems_for(const Plan &pl, int kmax, int nb) {
   long long pe = 0;
   {  // feature Gram partials
@@ -291,6 +299,13 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
   const int nb = pl.n_cells, D = pl.D;
   const long long ell = pl.ell, ld = pl.ell_ld;
   b.part = ar.take<float>(sz.part_elems);
+  {
+    const int nv = n_views(pl);
+    Plan pv = pl;
+    pv.n_cells = nb / nv;
+    b.fpart_elems = std::max(feature_part_elems(pl, nb), nv * feature_part_elems(pv, pv.n_cells));
+    b.fpart = ar.take<float>(b.fpart_elems);
+  }
   b.Xt = ar.take<char>((long long)nb * pl.GH * D * pl.T_ld * pl.c);
   b.Gd64 = ar.take<double>((long long)nb * D * D);
   b.dD = ar.take<double>((long long)nb * D);
@@ -427,12 +442,12 @@ void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStr
   g.a_ld = pl.T_ld; g.a_blk = pl.T_ld; g.a_blk_stride = (long long)D * pl.T_ld;
   g.b_ld = pl.T_ld; g.b_blk = pl.T_ld; g.b_blk_stride = (long long)D * pl.T_ld;
   g.a_bs = g.b_bs = (long long)pl.GH * D * pl.T_ld;
-  g.C = b.part; g.c_ld = D; g.c_split = (long long)D * D; g.c_bs = (long long)ns * D * D;
-  JOLT_REQUIRE((long long)pl.n_cells * ns * D * D <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
+  g.C = b.fpart; g.c_ld = D; g.c_split = (long long)D * D; g.c_bs = (long long)ns * D * D;
+  JOLT_REQUIRE((long long)pl.n_cells * ns * D * D <= b.fpart_elems, JOLT_EWORKSPACE, "split-K buffer too small");
   gemm(pl.xmf(), pl.xsrc(), true, pl.xsrc(), true, g, pl.n_cells, ns, st);
   (void)K;
   (void)V;
-  reduce_splits(b.part, (long long)ns * D * D, (long long)D * D, ns, 0, D, D, D, b.Gd64, true, (long long)D * D, D,
+  reduce_splits(b.fpart, (long long)ns * D * D, (long long)D * D, ns, 0, D, D, D, b.Gd64, true, (long long)D * D, D,
                 pl.n_cells, st);
   trace_f64(b.Gd64, (long long)D * D, D, pl.n_cells, b.norm2, st);
   sym_eigvals(b.Gd64, (long long)D * D, D, D, pl.n_cells, b.dD, b.eD, b.Gd64, b.betaD, D, b.specD, D, true, st);
@@ -443,7 +458,10 @@ void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStr
 // both layouts by the GEMM epilogue so the next consumer never transposes while loading.
 // mark (optional) is recorded on st once the first orthonormal basis Q_0 exists; the next spectra
 // chain waits for it, which puts the chains out of phase.
-void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st, hipEvent_t mark = nullptr) {
+// xready (optional): the transposed cache and the feature-stage outputs (||X||^2) are produced on
+// another stream; st waits for it before the first projection, which is their first reader.
+void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st, hipEvent_t mark = nullptr,
+                 hipEvent_t xready = nullptr) {
   const int nb = pl.n_cells, nkv = nb / 2;
   const long long ell = pl.ell, ld = pl.ell_ld, Tld = pl.T_ld, Mf = pl.M, T = pl.T;
   const long long cellX = pl.cell_elems();
@@ -493,6 +511,10 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   // first split into its 16-bit planes.
   const int pns = project_splits(pl);
   auto project = [&](const float *Qt, const float *q_amax, float *c_amax) {
+    if (xready) {
+      HIP_TRY(hipStreamWaitEvent(st, xready, 0));
+      xready = nullptr;
+    }
     const bool planes = dma_ok && T % 32 == 0;
     if (planes) {
       Stage prof_s("split_planes", st);
@@ -963,6 +985,12 @@ Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot)
   const long long n_tok = pl.mode == JOLT_FLASH ? ell : T;
   v.part = b.part + (long long)slot * sz.part_view;
   v.part_elems = sz.part_view;
+  {
+    Plan pv = pl;
+    pv.n_cells = pl.n_cells / n_views(pl);
+    v.fpart_elems = feature_part_elems(pv, pv.n_cells);
+    v.fpart = b.fpart + (long long)slot * v.fpart_elems;
+  }
   v.Xt = (char *)b.Xt + (long long)c0 * pl.GH * D * Tld * pl.c;
   v.Gd64 = b.Gd64 + c0 * D * D;
   v.dD = b.dD + c0 * D;
@@ -996,23 +1024,7 @@ Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot)
 
 void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const void *V, hipStream_t st) {
   JOLT_REQUIRE(K && V, JOLT_EINVAL, "null cache pointer");
-  {
-    Stage prof("transpose_x", st);
-    const long long cellX = pl.cell_elems(), cellXt = (long long)pl.GH * pl.D * pl.T_ld;
-    for_kv(K, V, [&](int t, const void *X) {
-      transpose_x(X, (char *)b.Xt + (long long)t * cellXt * pl.c, pl.c, pl.T, pl.T_ld, pl.D, pl.GH, pl.n_cells / 2,
-                  cellX, 2 * cellXt, st);
-    });
-  }
-  if (pl.mode == JOLT_FLASH) {
-    gen_omega(b.omegaT, pl.dtype, pl.M, pl.ell, stream_key(pl.sketch_seed, 2), st);
-    fill_f32(b.amax, 8LL * b.am_ld, 0.f, st);
-  }
   const int nv = n_views(pl), nc = pl.n_cells / nv;
-  Plan pv = pl;
-  pv.n_cells = nc;
-  // fork: every view starts after the common prologue; view i > 0 also waits until view i - 1 has
-  // formed its first basis
   std::vector<hipEvent_t> evs;
   auto new_event = [&]() {
     hipEvent_t e;
@@ -1020,6 +1032,40 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
     evs.push_back(e);
     return e;
   };
+  // FlashJoLT with one spectra chain: the transpose of the cache and the feature stage (both
+  // bandwidth-heavy) run on a side stream beside the Gaussian sketch and the first Cholesky QR
+  // (matrix-core work on the untransposed cache); the token chain waits for them before its first
+  // projection.
+  const bool side = pl.mode == JOLT_FLASH && nv == 1;
+  hipStream_t sx = st;
+  hipEvent_t xready = nullptr;
+  if (side) {
+    hipEvent_t start = new_event();
+    HIP_TRY(hipEventRecord(start, st));
+    sx = side_stream(0);
+    HIP_TRY(hipStreamWaitEvent(sx, start, 0));
+  }
+  {
+    Stage prof("transpose_x", sx);
+    const long long cellX = pl.cell_elems(), cellXt = (long long)pl.GH * pl.D * pl.T_ld;
+    for_kv(K, V, [&](int t, const void *X) {
+      transpose_x(X, (char *)b.Xt + (long long)t * cellXt * pl.c, pl.c, pl.T, pl.T_ld, pl.D, pl.GH, pl.n_cells / 2,
+                  cellX, 2 * cellXt, sx);
+    });
+  }
+  if (side) {
+    stage_feature(pl, b, K, V, sx);
+    xready = new_event();
+    HIP_TRY(hipEventRecord(xready, sx));
+  }
+  if (pl.mode == JOLT_FLASH) {
+    gen_omega(b.omegaT, pl.dtype, pl.M, pl.ell, stream_key(pl.sketch_seed, 2), st);
+    fill_f32(b.amax, 8LL * b.am_ld, 0.f, st);
+  }
+  Plan pv = pl;
+  pv.n_cells = nc;
+  // fork: every view starts after the common prologue; view i > 0 also waits until view i - 1 has
+  // formed its first basis
   hipEvent_t fork = new_event();
   HIP_TRY(hipEventRecord(fork, st));
   hipEvent_t prev_mark = nullptr;
@@ -1034,11 +1080,11 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
     Bufs bv = cell_view(b, pl, sz, c0, v);
     const long long xoff = (long long)(c0 / 2) * pl.cell_elems() * pl.c;
     const void *Kv = (const char *)K + xoff, *Vv = (const char *)V + xoff;
-    stage_feature(pv, bv, Kv, Vv, sv);
+    if (!side) stage_feature(pv, bv, Kv, Vv, sv);
     hipEvent_t mark = (pl.mode == JOLT_FLASH && v + 1 < nv) ? new_event() : nullptr;
     if (pl.mode == JOLT_FLASH) {
       float *bufA0 = bv.bufA;
-      stage_flash(pv, bv, Kv, Vv, sv, mark);
+      stage_flash(pv, bv, Kv, Vv, sv, mark, xready);
       swapped = bv.bufA != bufA0;
     } else {
       stage_exact(pv, bv, Kv, Vv, sv);
@@ -1046,6 +1092,7 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
     prev_mark = mark;
   }
   // join
+  if (xready) HIP_TRY(hipStreamWaitEvent(st, xready, 0));  // (already waited for by the first projection)
   for (int v = 1; v < nv; ++v) {
     hipEvent_t j = new_event();
     HIP_TRY(hipEventRecord(j, streams[v]));

@@ -536,13 +536,13 @@ __global__ void __launch_bounds__(LT) tridiag_fused_kernel(double *A, long long 
 // ---------------------------------------------------------------------------------------------
 constexpr int IT = 512;  // threads of the inverse-iteration kernel (one eigenvector each)
 
-__global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const double *e_in, long long t_bs,
+// grid (ceil(kmax / 64), batch) of one wave each: thread j of matrix b iterates eigenvector j.
+__global__ void __launch_bounds__(64) invit_kernel(const double *d_in, const double *e_in, long long t_bs,
                                                    const double *evals_all, long long ev_bs, const int *k_of,
                                                    const int *n_of, int n_fixed, double *Z, long long z_bs,
                                                    double *work, long long w_bs, int kmax) {
   extern __shared__ double smem[];
-  __shared__ double red[LT / 64];
-  const int b = blockIdx.x;
+  const int b = blockIdx.y;
   const int n = n_of ? n_of[b] : n_fixed;
   const int k = min(k_of[b], n);
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -563,7 +563,7 @@ __global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const dou
   double *U0 = wb, *U1 = wb + (long long)n * kmax, *U2 = wb + 2LL * n * kmax, *Xv = wb + 3LL * n * kmax;
   double *Za = wb + 4LL * n * kmax, *Zb2 = wb + 5LL * n * kmax;
   unsigned char *piv = (unsigned char *)(wb + 6LL * n * kmax);
-  for (int j = tid; j < k; j += nt) {
+  for (int j = blockIdx.x * nt + tid; j < k; j += gridDim.x * nt) {
     const double lam = ev[j];
     // factor P (T - lam I) = L U with partial pivoting; L multipliers applied on the fly, so
     // they are stored in U2's slot of the row below only through piv/U arrays.
@@ -578,7 +578,7 @@ __global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const dou
         // no swap
         double aa = (a == 0.0) ? tiny : a;
         double l = sub / aa;
-        U0[(long long)i * kmax + j] = aa;
+        U0[(long long)i * kmax + j] = 1.0 / aa;  // reciprocal pivot (the solves multiply)
         U1[(long long)i * kmax + j] = bb;
         U2[(long long)i * kmax + j] = cc;
         piv[(long long)i * kmax + j] = 0;
@@ -589,7 +589,7 @@ __global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const dou
       } else {
         // swap rows i and i+1
         double l = a / sub;
-        U0[(long long)i * kmax + j] = sub;
+        U0[(long long)i * kmax + j] = 1.0 / sub;
         U1[(long long)i * kmax + j] = nd;
         U2[(long long)i * kmax + j] = ne;
         piv[(long long)i * kmax + j] = 1;
@@ -601,7 +601,7 @@ __global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const dou
         cc = 0.0;
       }
     }
-    U0[(long long)(n - 1) * kmax + j] = (a == 0.0) ? tiny : a;
+    U0[(long long)(n - 1) * kmax + j] = 1.0 / ((a == 0.0) ? tiny : a);
     U1[(long long)(n - 1) * kmax + j] = 0.0;
     U2[(long long)(n - 1) * kmax + j] = 0.0;
     // iterate on vectors stored interleaved ([i][kmax], coalesced across threads), alternating
@@ -616,11 +616,16 @@ __global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const dou
       h ^= h >> 29;
       za[(long long)i * kmax + j] = 0.5 + (double)(h >> 11) * (1.0 / 9007199254740992.0);
     }
+    // the iterate is rescaled by 1 / max|z| between iterations through the factor sc applied as
+    // it is read (no extra pass over it); the unit 2-norm is taken once, on output
+    double sc = 1.0;
+    double scale = 0.0;
     for (int iter = 0; iter < 3; ++iter) {
       // apply L^{-1} P: za -> zb (the running entry stays in a register); the operands of the
-      // next IP steps are loaded while the current ones are used
-      constexpr int IP = 4;
-      double cur = za[j];
+      // next IP steps are loaded while the current ones are used (deep enough to cover a memory
+      // round trip: the whole chain is one thread's)
+      constexpr int IP = 8;
+      double cur = za[j] * sc;
       {
         double cl[IP], cn[IP], nl[IP], nn[IP];
         unsigned char cp[IP], np[IP];
@@ -630,7 +635,7 @@ __global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const dou
             const int i = i0 + t;
             const bool ok = i < n - 1;
             l[t] = ok ? Xv[(long long)i * kmax + j] : 0.0;
-            x[t] = ok ? za[(long long)(i + 1) * kmax + j] : 0.0;
+            x[t] = ok ? za[(long long)(i + 1) * kmax + j] * sc : 0.0;
             pv[t] = ok ? piv[(long long)i * kmax + j] : (unsigned char)0;
           }
         };
@@ -660,8 +665,10 @@ __global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const dou
       }
       zb[(long long)(n - 1) * kmax + j] = cur;
       // back substitution with U (bands u0, u1, u2): zb -> za, same prefetching
-      double scale = 0.0, z1 = 0.0, z2 = 0.0;  // z[i + 1], z[i + 2]
+      double z1 = 0.0, z2 = 0.0;  // z[i + 1], z[i + 2]
+      scale = 0.0;
       {
+        constexpr int IP = 8;
         double c0[IP], c1[IP], c2[IP], cz[IP], n0[IP], n1[IP], n2[IP], nz[IP];
         auto fetch = [&](int i0, double (&u0)[IP], double (&u1)[IP], double (&u2)[IP], double (&x)[IP]) __attribute__((always_inline)) {
 #pragma unroll
@@ -684,7 +691,7 @@ __global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const dou
               double sv = cz[t];
               if (i + 1 < n) sv -= c1[t] * z1;
               if (i + 2 < n) sv -= c2[t] * z2;
-              const double zi = sv / c0[t];
+              const double zi = sv * c0[t];
               za[(long long)i * kmax + j] = zi;
               scale = fmax(scale, fabs(zi));
               z2 = z1;
@@ -700,23 +707,52 @@ __global__ void __launch_bounds__(IT) invit_kernel(const double *d_in, const dou
           }
         }
       }
-      // normalise to unit 2-norm (rescale by max first to avoid overflow)
-      double inv = (scale > 0.0) ? 1.0 / scale : 1.0;
-      double nrm = 0.0;
-      for (int i = 0; i < n; ++i) {
-        const double zi = za[(long long)i * kmax + j] * inv;
-        za[(long long)i * kmax + j] = zi;
-        nrm += zi * zi;
-      }
-      nrm = 1.0 / sqrt(nrm);
-      for (int i = 0; i < n; ++i) za[(long long)i * kmax + j] *= nrm;
+      sc = (scale > 0.0) ? 1.0 / scale : 1.0;
     }
+    // unit 2-norm of sc * z (entries read in groups of 8, all loads of a group in flight)
+    constexpr int OG = 8;
+    double nrm = 0.0;
+    for (int i0 = 0; i0 < n; i0 += OG) {
+      double x[OG];
+#pragma unroll
+      for (int t = 0; t < OG; ++t) x[t] = (i0 + t < n) ? za[(long long)(i0 + t) * kmax + j] * sc : 0.0;
+#pragma unroll
+      for (int t = 0; t < OG; ++t) nrm += x[t] * x[t];
+    }
+    const double f = sc / sqrt(nrm);
     double *z = Zb + (long long)j * n;  // output row j
-    for (int i = 0; i < n; ++i) z[i] = za[(long long)i * kmax + j];
+    for (int i0 = 0; i0 < n; i0 += OG) {
+      double x[OG];
+#pragma unroll
+      for (int t = 0; t < OG; ++t) x[t] = (i0 + t < n) ? za[(long long)(i0 + t) * kmax + j] : 0.0;
+#pragma unroll
+      for (int t = 0; t < OG; ++t)
+        if (i0 + t < n) z[i0 + t] = x[t] * f;
+    }
   }
+}
+
+// Cluster re-orthogonalisation of the inverse-iteration vectors (one workgroup per matrix,
+// sequential over vectors, parallel over entries): eigenvalues closer than 1e-7 ||T|| form a
+// cluster, whose vectors are orthogonalised in order by two passes of Gram-Schmidt.
+__global__ void __launch_bounds__(IT) invit_cluster_kernel(const double *d_in, const double *e_in, long long t_bs,
+                                                           const double *evals_all, long long ev_bs, const int *k_of,
+                                                           const int *n_of, int n_fixed, double *Z, long long z_bs) {
+  __shared__ double red[IT / 64];
+  const int b = blockIdx.x;
+  const int n = n_of ? n_of[b] : n_fixed;
+  const int k = min(k_of[b], n);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const double *d = d_in + b * t_bs, *e = e_in + b * t_bs, *ev = evals_all + b * ev_bs;
+  double *Zb = Z + b * z_bs;
+  double tn = 0.0;
+  for (int i = tid; i < n; i += nt) tn = fmax(tn, fabs(d[i]) + (i + 1 < n ? fabs(e[i]) : 0.0) + (i ? fabs(e[i - 1]) : 0.0));
+  for (int o = 32; o > 0; o >>= 1) tn = fmax(tn, __shfl_xor(tn, o, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = tn;
   __syncthreads();
-  __threadfence_block();
-  // cluster re-orthogonalisation (sequential over vectors, parallel over entries)
+  tn = 0.0;
+  for (int w = 0; w < nt / 64; ++w) tn = fmax(tn, red[w]);
+  __syncthreads();
   const double ctol = 1e-7 * fmax(tn, 1e-300);
   for (int j = 1; j < k; ++j) {
     // start of j's cluster, found by every thread (uniform); vectors outside a cluster are final
@@ -1266,8 +1302,11 @@ void sym_eigvecs(const double *d, const double *e, const double *refl, const dou
                  long long z_bs, double *work, long long w_bs, double *out64, float *out32, long long out_bs,
                  int out_ld, hipStream_t st) {
   if (kmax <= 0) return;
-  hipLaunchKernelGGL(invit_kernel, dim3(batch), dim3(IT), 2 * (size_t)n * sizeof(double), st, d, e, t_bs, evals,
-                     ev_bs, k_dev, (const int *)nullptr, n, Zw, z_bs, work, w_bs, kmax);
+  hipLaunchKernelGGL(invit_kernel, dim3((kmax + 63) / 64, batch), dim3(64), 2 * (size_t)n * sizeof(double), st, d, e,
+                     t_bs, evals, ev_bs, k_dev, (const int *)nullptr, n, Zw, z_bs, work, w_bs, kmax);
+  HIP_LAUNCH_CHECK();
+  hipLaunchKernelGGL(invit_cluster_kernel, dim3(batch), dim3(IT), 0, st, d, e, t_bs, evals, ev_bs, k_dev,
+                     (const int *)nullptr, n, Zw, z_bs);
   HIP_LAUNCH_CHECK();
   if (n <= 64 * 9) {
     // register variant: 4 rows per wave, 4 waves per workgroup
