@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -458,10 +459,13 @@ void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStr
 // both layouts by the GEMM epilogue so the next consumer never transposes while loading.
 // mark (optional) is recorded on st once the first orthonormal basis Q_0 exists; the next spectra
 // chain waits for it, which puts the chains out of phase.
-// xready (optional): the transposed cache and the feature-stage outputs (||X||^2) are produced on
-// another stream; st waits for it before the first projection, which is their first reader.
+// side_work (optional): enqueues the transpose of the cache and the feature stage on another
+// stream and returns the event that marks their end; it is called once the Gaussian sketch (which
+// reads the untransposed cache) is queued, and st waits for the event before the first
+// projection, the first reader of their outputs.
 void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st, hipEvent_t mark = nullptr,
-                 hipEvent_t xready = nullptr) {
+                 const std::function<hipEvent_t()> &side_work = {}) {
+  hipEvent_t xready = nullptr;
   const int nb = pl.n_cells, nkv = nb / 2;
   const long long ell = pl.ell, ld = pl.ell_ld, Tld = pl.T_ld, Mf = pl.M, T = pl.T;
   const long long cellX = pl.cell_elems();
@@ -582,6 +586,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   };
 
   sketch(b.omegaT, pl.xsrc(), 0, nullptr, pa.T, pa.R, pa.am);
+  if (side_work) xready = side_work();
   Pair Q = cholqr(pa, pb, 1);
   if (mark) HIP_TRY(hipEventRecord(mark, st));
   for (int it = 0; it < pl.power_iters; ++it) {
@@ -1033,30 +1038,34 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
     return e;
   };
   // FlashJoLT with one spectra chain: the transpose of the cache and the feature stage (both
-  // bandwidth-heavy) run on a side stream beside the Gaussian sketch and the first Cholesky QR
-  // (matrix-core work on the untransposed cache); the token chain waits for them before its first
-  // projection.
+  // bandwidth-heavy) run on a side stream beside the first Cholesky QR of the token chain (whose
+  // factorisation and triangular-inverse launches leave most of the GPU idle); the token chain
+  // waits for them before its first projection.
   const bool side = pl.mode == JOLT_FLASH && nv == 1;
-  hipStream_t sx = st;
-  hipEvent_t xready = nullptr;
-  if (side) {
-    hipEvent_t start = new_event();
-    HIP_TRY(hipEventRecord(start, st));
-    sx = side_stream(0);
-    HIP_TRY(hipStreamWaitEvent(sx, start, 0));
-  }
-  {
-    Stage prof("transpose_x", sx);
+  auto transpose_all = [&](hipStream_t on) {
+    Stage prof("transpose_x", on);
     const long long cellX = pl.cell_elems(), cellXt = (long long)pl.GH * pl.D * pl.T_ld;
     for_kv(K, V, [&](int t, const void *X) {
       transpose_x(X, (char *)b.Xt + (long long)t * cellXt * pl.c, pl.c, pl.T, pl.T_ld, pl.D, pl.GH, pl.n_cells / 2,
-                  cellX, 2 * cellXt, sx);
+                  cellX, 2 * cellXt, on);
     });
-  }
+  };
+  hipEvent_t xready = nullptr;
+  std::function<hipEvent_t()> side_work;
   if (side) {
-    stage_feature(pl, b, K, V, sx);
-    xready = new_event();
-    HIP_TRY(hipEventRecord(xready, sx));
+    side_work = [&]() -> hipEvent_t {
+      hipEvent_t start = new_event();
+      HIP_TRY(hipEventRecord(start, st));
+      hipStream_t sx = side_stream(0);
+      HIP_TRY(hipStreamWaitEvent(sx, start, 0));
+      transpose_all(sx);
+      stage_feature(pl, b, K, V, sx);
+      xready = new_event();
+      HIP_TRY(hipEventRecord(xready, sx));
+      return xready;
+    };
+  } else {
+    transpose_all(st);
   }
   if (pl.mode == JOLT_FLASH) {
     gen_omega(b.omegaT, pl.dtype, pl.M, pl.ell, stream_key(pl.sketch_seed, 2), st);
@@ -1084,7 +1093,7 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
     hipEvent_t mark = (pl.mode == JOLT_FLASH && v + 1 < nv) ? new_event() : nullptr;
     if (pl.mode == JOLT_FLASH) {
       float *bufA0 = bv.bufA;
-      stage_flash(pv, bv, Kv, Vv, sv, mark, xready);
+      stage_flash(pv, bv, Kv, Vv, sv, mark, side_work);
       swapped = bv.bufA != bufA0;
     } else {
       stage_exact(pv, bv, Kv, Vv, sv);
