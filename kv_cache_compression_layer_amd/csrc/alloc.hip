@@ -41,6 +41,8 @@ __device__ Best shfl_best(const Best &v, int o) {
 
 __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
   __shared__ int pick[AllocArgs::kMaxCells];
+  __shared__ long long pick_s[AllocArgs::kMaxCells];  // bytes and distortion of each cell's pick
+  __shared__ double pick_e[AllocArgs::kMaxCells];
   __shared__ double lam_s;
   __shared__ int done_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = AT / 64;
@@ -59,9 +61,23 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
     int gi = ng - 1;
     // ranks beyond the spectrum length discard nothing
     while (gi >= 0 && grid[gi] >= len) outp[gi--] = 0.0;
-    for (int i = len - 1; i >= 0 && gi >= 0; --i) {
-      acc = __dadd_rn(acc, sp[i]);
-      while (gi >= 0 && grid[gi] == i) outp[gi--] = acc;
+    int gv = gi >= 0 ? grid[gi] : -1;  // the next grid rank to emit
+    // the spectrum is read 8 entries at a time (independent loads in flight), summed one by one
+    for (int i0 = len - 1; i0 >= 0 && gi >= 0; i0 -= 8) {
+      double x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = (i0 - u >= 0) ? sp[i0 - u] : 0.0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 - u;
+        if (i >= 0 && gi >= 0) {
+          acc = __dadd_rn(acc, x[u]);
+          while (gi >= 0 && gv == i) {
+            outp[gi--] = acc;
+            gv = gi >= 0 ? grid[gi] : -1;
+          }
+        }
+      }
     }
     while (gi >= 0) outp[gi--] = acc;
   }
@@ -84,8 +100,8 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
 
   // (3) evaluation of the per-cell minimisers at lambda: one wave per cell; a lane visits its
   // candidates in ascending index order (so an equal cost and size never replaces its best) and
-  // reads them in batches of 8 so that their loads are in flight together
-  constexpr int EB = 8;
+  // reads them in batches of 16 so that their loads are in flight together
+  constexpr int EB = 16;
   auto evaluate = [&](double lam) {
     for (int c = wave; c < nc; c += nw) {
       Best best;
@@ -118,17 +134,22 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
         Best oth = shfl_best(best, o);
         if (less_than(oth, best)) best = oth;
       }
-      if (lane == 0) pick[c] = best.idx;
+      if (lane == 0) {
+        pick[c] = best.idx;
+        pick_s[c] = sc[best.idx];
+        pick_e[c] = ec[best.idx];
+      }
     }
     __syncthreads();
   };
+  // totals of the current picks, summed over the cells in order (read from LDS: one global
+  // round trip per cell in this sequential loop would dominate the bisection)
   auto totals = [&](long long &S, double &E) {
     S = 0;
     E = 0.0;
     for (int c = 0; c < nc; ++c) {
-      const long long w = (long long)c * per + pick[c];
-      S += a.s[w];
-      E = __dadd_rn(E, a.e[w]);
+      S += pick_s[c];
+      E = __dadd_rn(E, pick_e[c]);
     }
   };
   auto store = [&](int status, double lam, int iters) {
@@ -198,7 +219,12 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
     __syncthreads();
   }
   // no accept: the feasible end
-  for (int c = tid; c < nc; c += AT) pick[c] = a.out_pick[c];
+  for (int c = tid; c < nc; c += AT) {
+    const int i = a.out_pick[c];
+    pick[c] = i;
+    pick_s[c] = a.s[(long long)c * per + i];
+    pick_e[c] = a.e[(long long)c * per + i];
+  }
   __syncthreads();
   store(0, hi_lam, 50);
 }
