@@ -163,7 +163,10 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
       a.out->E = E;
       a.out->iters = iters;
     }
-    for (int c = tid; c < nc; c += AT) a.out_pick[c] = pick[c];
+    for (int c = tid; c < nc; c += AT) {
+      a.out_pick[c] = pick[c];
+      if (a.out_err) a.out_err[c] = pick_e[c];
+    }
     __syncthreads();
   };
 

@@ -35,6 +35,7 @@ struct AllocArgs {
   double *e;                  // scratch [n_cells][n_bits*n_rT*n_rd]
   long long *s;               // scratch, same shape
   int *out_pick;              // [n_cells] grid index (b-major, then r_T, then r_d)
+  double *out_err;            // [n_cells] table distortion e of each pick (may be null)
   AllocOut *out;
 };
 

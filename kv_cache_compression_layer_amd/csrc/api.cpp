@@ -194,6 +194,7 @@ struct Bufs {
   // common
   float *part;
   float *fpart;  // feature Gram partials (own region: that stage may run beside the token stages)
+  double *perr;  // [n_cells] table distortion of each pick (read back with the picks)
   long long fpart_elems;
   double *Gd64, *dD, *eD, *betaD, *evD;
   double *specT, *specD, *norm2;
@@ -363,6 +364,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
   b.tab_e = ar.take<double>(nb * per);
   b.tab_s = ar.take<long long>(nb * per);
   b.pick = ar.take<int>(nb);
+  b.perr = ar.take<double>(nb);
   b.aout = ar.take<AllocOut>(1);
   b.params_bytes = (size_t)rup(64 * 1024 + 2LL * D * D * 4 +
                                    (long long)nb * (sizeof(EncCell) + sizeof(DecCell) + sizeof(FactorCell) + 64) +
@@ -685,7 +687,7 @@ void run_allocation(int nc, const AllocDev &ad, int elem_bytes, const double *sp
   a.eps2 = ad.eps2;
   a.budget = budget;
   a.tailT = b.tailT; a.tailD = b.tailD; a.e = b.tab_e; a.s = b.tab_s;
-  a.out_pick = b.pick; a.out = b.aout;
+  a.out_pick = b.pick; a.out_err = b.perr; a.out = b.aout;
   run_alloc(a, st);
 }
 
@@ -1309,6 +1311,7 @@ int jolt_allocate(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_byt
     b.tab_e = ar.take<double>(n_cells * per);
     b.tab_s = ar.take<long long>(n_cells * per);
     b.pick = ar.take<int>(n_cells);
+    b.perr = ar.take<double>(n_cells);
     b.aout = ar.take<AllocOut>(1);
     b.params_bytes = (size_t)rup(4096 + (long long)n_cells * 40 + (pl.rT.size() + pl.rd.size()) * 4, 256);
     b.params = ar.take<char>((long long)b.params_bytes);
@@ -1322,8 +1325,10 @@ int jolt_allocate(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_byt
     run_allocation(n_cells, ad, elem_bytes, d_specT, d_specD, d_norm2, (int)pl.rT.size(), (int)pl.rd.size(),
                    (int)pl.bits.size(), budget_bytes, b, st);
     std::vector<int> pick(n_cells);
+    std::vector<double> perr(n_cells);
     AllocOut ao;
     HIP_TRY(hipMemcpyAsync(pick.data(), b.pick, n_cells * 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipMemcpyAsync(perr.data(), b.perr, n_cells * 8, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipMemcpyAsync(&ao, b.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
     HIP_TRY(hipStreamSynchronize(st));
     const int nT = (int)pl.rT.size(), nD = (int)pl.rd.size();
@@ -1335,7 +1340,7 @@ int jolt_allocate(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_byt
       jolt_pick &p = h_picks[c];
       p.rT = pl.rT[ti]; p.rd = pl.rd[di]; p.bits = pl.bits[bi]; p.pad = 0;
       p.bytes = eq1_bytes(s[0], s[1], s[2], s[3], elem_bytes, p.rT, p.rd, p.bits);
-      HIP_TRY(hipMemcpy(&p.err_pred, b.tab_e + (long long)c * per + i, 8, hipMemcpyDeviceToHost));
+      p.err_pred = perr[c];
       Section sec = layout(s[0], s[1], s[2], s[3], elem_bytes, p.rT, p.rd, p.bits);
       p.offset = off;
       p.section_bytes = sec.end;
@@ -1394,9 +1399,8 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
     HIP_TRY(hipMemcpyAsync(pick.data(), b.pick, nb * 4, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipMemcpyAsync(n2.data(), b.norm2, nb * 8, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipMemcpyAsync(&ao, b.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
-    const long long per = (long long)pl.bits.size() * pl.rT.size() * pl.rd.size();
-    std::vector<double> tab_e((size_t)nb * per);
-    HIP_TRY(hipMemcpyAsync(tab_e.data(), b.tab_e, tab_e.size() * 8, hipMemcpyDeviceToHost, st));
+    std::vector<double> perr(nb);
+    HIP_TRY(hipMemcpyAsync(perr.data(), b.perr, nb * 8, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipStreamSynchronize(st));
     for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(n2[c]), JOLT_ENONFINITE, "non-finite ||X||^2 in a cell");
     if (h_lambda) *h_lambda = ao.lambda;
@@ -1419,7 +1423,7 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
       jolt_pick &h = h_picks[c];
       h.rT = p.rT; h.rd = p.rd; h.bits = p.bits; h.pad = 0;
       h.bytes = eq1_bytes(pl.G, pl.H, pl.T, pl.D, pl.c, p.rT, p.rd, p.bits);
-      h.err_pred = tab_e[(size_t)c * per + i];
+      h.err_pred = perr[c];
       h.offset = p.off;
       h.section_bytes = p.sec.end;
     }
