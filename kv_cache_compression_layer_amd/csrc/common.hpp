@@ -87,9 +87,26 @@ __device__ __forceinline__ float warp_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
+// Sum over the 64 lanes of a wave, returned to every lane (every lane must be active): pairs and
+// quads by DPP quad permutes, half rows and rows by the mirror permutes, then rows 1 and 3 take
+// row 0's and row 2's sums (row_bcast15) and rows 2 and 3 take row 1's (row_bcast31), so lane 63
+// ends with the total, which is broadcast.  Registers only (no LDS permutes), fixed order.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWMASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWMASK, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
 __device__ __forceinline__ double warp_sum_d(double v) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f64<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141, 0xF>(v);  // row_half_mirror
+  v += dpp_f64<0x140, 0xF>(v);  // row_mirror
+  v += dpp_f64<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  v += dpp_f64<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), 63);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), 63);
+  return __hiloint2double(hi, lo);
 }
 
 // ---------------------------------------------------------------------------------------------
