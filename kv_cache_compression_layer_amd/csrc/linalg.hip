@@ -266,6 +266,13 @@ __device__ __forceinline__ double wave_reflector(double *W, int ldw, int n, int 
   return bet;
 }
 
+// value of a double held by lane l (l a compile-time constant), by scalar lane reads
+__device__ __forceinline__ double lane_bcast_d(double v, int l) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+  return __hiloint2double(hi, lo);
+}
+
 // Row r (columns r..n-1, n - r <= 64 * TCH) held in registers x[t] = row[r + lane + 64 t]:
 // the same reflector, one read of the row.
 __device__ __forceinline__ double wave_reflector_regs(const double (&x)[TCH], int n, int r, double *v, double *R, long long r_ld,
@@ -278,7 +285,7 @@ __device__ __forceinline__ double wave_reflector_regs(const double (&x)[TCH], in
     if (j >= r + 2 && j < n) part += x[t] * x[t];
   }
   const double sigma = warp_sum_d(part);
-  const double alpha = __shfl(x[0], 1, 64), dr = __shfl(x[0], 0, 64);
+  const double alpha = lane_bcast_d(x[0], 1), dr = lane_bcast_d(x[0], 0);
   double bet, v0, mu;
   if (sigma == 0.0) {
     bet = 0.0;
@@ -949,14 +956,6 @@ __global__ void __launch_bounds__(256) backtransform_regs_kernel(const double *Z
 // multiple of the largest diagonal entry (documented regularisation).
 // LDS: a 32 x 32 diagonal block and a 32 x (n - k0) panel (n <= 544 keeps the panel in LDS).
 // ---------------------------------------------------------------------------------------------
-// value of a double held by lane l (l uniform, typically a compile-time constant): two scalar
-// lane reads instead of an LDS permute, so the factorisation steps of one wave stay in registers
-__device__ __forceinline__ double lane_d(double v, int l) {
-  const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
-  const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
-  return __hiloint2double(hi, lo);
-}
-
 constexpr int CNB = 32;
 constexpr int CHOL_MAXN_LDS = 544;
 constexpr int CT = 1024;
@@ -1009,7 +1008,7 @@ __global__ void __launch_bounds__(64) chol_diag_kernel(int n, double *Rw, long l
 #pragma unroll
   for (int jj = 0; jj < CNB; ++jj) {
     if (jj < kb) {
-      const double piv = sqrt(fmax(lane_d(a[jj], jj), floor_piv));
+      const double piv = sqrt(fmax(lane_bcast_d(a[jj], jj), floor_piv));
       if (c == jj) a[jj] = piv;
       else if (c > jj) a[jj] /= piv;  // R[jj][c]
       if (c < CNB) Dk[jj * 33 + c] = (c >= jj) ? a[jj] : 0.0;
@@ -1108,10 +1107,10 @@ __global__ void __launch_bounds__(64) diag_inv_kernel(double *Rw, long long r_bs
     double v = (r == c) ? 1.0 : 0.0;
 #pragma unroll
     for (int q = r + 1; q < CNB; ++q) {
-      const double rq = lane_d(a[r], q);  // R[r][q]
+      const double rq = lane_bcast_d(a[r], q);  // R[r][q]
       if (q <= c) v -= rq * x[q];
     }
-    const double rr = lane_d(a[r], r);
+    const double rr = lane_bcast_d(a[r], r);
     x[r] = (r <= c) ? v / rr : 0.0;
   }
   if (c < CNB) {
@@ -1149,6 +1148,19 @@ __global__ void __launch_bounds__(512) tri_inv_kernel(const double *Rw, long lon
     const double *Rrow = R + (long long)(i0 + q) * n;
     double t0 = 0.0, t1 = 0.0, t2 = 0.0, t3 = 0.0;
     int k = kbeg;
+    // 16 entries of the row are loaded before any is used (one memory round trip per 16)
+    for (; k + 16 <= kend; k += 16) {
+      double rv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) rv[u] = Rrow[k + u];
+#pragma unroll
+      for (int u = 0; u < 16; u += 4) {
+        t0 += rv[u] * Xs[(k + u) * SW + c];
+        t1 += rv[u + 1] * Xs[(k + u + 1) * SW + c];
+        t2 += rv[u + 2] * Xs[(k + u + 2) * SW + c];
+        t3 += rv[u + 3] * Xs[(k + u + 3) * SW + c];
+      }
+    }
     for (; k + 4 <= kend; k += 4) {
       t0 += Rrow[k] * Xs[k * SW + c];
       t1 += Rrow[k + 1] * Xs[(k + 1) * SW + c];
