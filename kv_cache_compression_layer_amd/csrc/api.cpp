@@ -566,21 +566,28 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     float *T, *R, *am;
   };
   Pair pa{b.bufA, b.bufA2, amY}, pb{b.bufB, b.bufB2, amQ};
-  auto cholqr = [&](Pair y, Pair q, int passes) -> Pair {
+  // Q is computed transposed, Q^T = R^{-T} Y^T (A = R^{-T} is lower triangular: each row tile
+  // stops its k loop at its last row), so the main output [ell][T_ld] has long rows; Q itself
+  // ([T][ell_ld]) is the epilogue's transposed output.  t_only: the last pass writes Q^T alone,
+  // for a basis that only the next projection reads.
+  auto cholqr = [&](Pair y, Pair q, int passes, bool t_only = false) -> Pair {
     Stage prof("cholqr_tall", st);
     for (int p = 0; p < passes; ++p) {
       gram_f32(pl, b, y.T, Tld, ell * Tld, (int)ell, (int)T, y.am, b.G64, ell * ell, (int)ell, nb, st);
       chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, chol_scratch_doubles((int)ell), b.RinvT, ell * ld, (int)ld, amR, st);
       fill_f32(q.am, nb, 0.f, st);
       GemmArgs g = ga();
-      g.A = y.R; g.a_ld = ld; g.a_bs = T * ld; g.a_amax = y.am;
-      g.B = b.RinvT; g.b_ld = ld; g.b_bs = ell * ld; g.b_amax = amR;
-      g.M = (int)T; g.N = (int)ell; g.K = (int)ell;
-      g.C = q.R; g.c_ld = ld; g.c_bs = T * ld;
-      g.C2 = q.T; g.c2_ld = Tld; g.c2_bs = ell * Tld;
+      g.A = b.RinvT; g.a_ld = ld; g.a_bs = ell * ld; g.a_amax = amR;
+      g.B = y.R; g.b_ld = ld; g.b_bs = T * ld; g.b_amax = y.am;
+      g.ab_amax_bs = 1;
+      g.M = (int)ell; g.N = (int)T; g.K = (int)ell;
+      g.C = q.T; g.c_ld = Tld; g.c_bs = ell * Tld;
+      if (!(t_only && p + 1 == passes)) {
+        g.C2 = q.R; g.c2_ld = ld; g.c2_bs = T * ld;
+      }
       g.c_amax = q.am;
-      g.m_fastest = 0;
-      g.tri = 2;  // R^{-1} is upper triangular
+      g.m_fastest = 1;
+      g.tri = 4;
       gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
       std::swap(y, q);
     }
@@ -589,7 +596,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
 
   sketch(b.omegaT, pl.xsrc(), 0, nullptr, pa.T, pa.R, pa.am);
   if (side_work) xready = side_work();
-  Pair Q = cholqr(pa, pb, 1);
+  Pair Q = cholqr(pa, pb, 1, pl.power_iters > 0);
   if (mark) HIP_TRY(hipEventRecord(mark, st));
   for (int it = 0; it < pl.power_iters; ++it) {
     fill_f32(amP, nb, 0.f, st);

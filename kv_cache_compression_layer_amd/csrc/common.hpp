@@ -145,7 +145,9 @@ struct GemmArgs {
   long long c2_ld, c2_bs;
   // structure flags: 1 = only tiles touching the upper triangle (m < n) are needed; the others
   // are written as zeros without work; 2 = B(k, n) = 0 for k > n (an upper triangular factor),
-  // so each column tile stops its k loop at its last column (single split only)
+  // so each column tile stops its k loop at its last column (single split only); 4 = A(m, k) = 0
+  // for k > m (a lower triangular factor), so each row tile stops its k loop at its last row
+  // (single split, K-contiguous kernel only)
   int tri;
   // operands stored as 16-bit planes (plane-GEMM path): element stride between planes
   long long a_ps, b_ps;

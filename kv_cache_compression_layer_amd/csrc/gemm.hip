@@ -282,7 +282,7 @@ void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int b
   JOLT_REQUIRE(g.inner >= 1 && batch % g.inner == 0, JOLT_EINVAL, "gemm: bad inner batch");
   JOLT_REQUIRE(g.C2 == nullptr || ((uintptr_t)g.C2 % 16) == 0, JOLT_EINVAL, "gemm: C2 must be 16-byte aligned");
   JOLT_REQUIRE(g.tri == 0 || (a_kc && b_kc), JOLT_EINVAL, "gemm: structure flags need K-contiguous operands");
-  JOLT_REQUIRE(!(g.tri & 2) || nsplit == 1, JOLT_EINVAL, "gemm: triangular B needs a single split");
+  JOLT_REQUIRE(!(g.tri & 6) || nsplit == 1, JOLT_EINVAL, "gemm: triangular operands need a single split");
   JOLT_REQUIRE(!(g.tri & 1) || g.M == g.N, JOLT_EINVAL, "gemm: upper-triangle output needs a square product");
   GemmArgs h = g;
   if (nsplit == 1) h.k_chunk = ((g.K + BK - 1) / BK) * BK;

@@ -95,6 +95,7 @@ __global__ void __launch_bounds__(KNT) __attribute__((amdgpu_waves_per_eu(W, W))
   int kend = min(g.K, kbeg + g.k_chunk);
   if (kbeg >= kend && split > 0) return;
   if (g.tri & 2) kend = min(kend, n0 + BN);
+  if (g.tri & 4) kend = min(kend, m0 + BM);
   if ((g.tri & 1) && m0 >= n0 + BN) kend = kbeg;  // strictly below the diagonal: zeros
 
   const char *Ab = (const char *)g.A + ((long long)batch * g.a_bs + (long long)bin * g.a_bs2) * (SA == SRC_F32 ? 4 : 2);
