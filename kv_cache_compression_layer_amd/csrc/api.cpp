@@ -201,8 +201,8 @@ struct Bufs {
   // flash / exact token stage
   void *omegaT;
   // tall panels, each in two layouts: rows of length T ([ell][T_ld]) and rows of length ell
-  // ([T][ell_ld]); P / Z likewise ([ell][M] and [M][ell_ld])
-  float *bufA, *bufB, *bufA2, *bufB2, *Pt, *P2, *Zt, *Z2, *RinvT, *YpT;
+  // ([T][ell_ld]); P likewise ([ell][M] and [M][ell_ld]); Z only as Z^T ([ell][M])
+  float *bufA, *bufB, *bufA2, *bufB2, *Pt, *P2, *Zt, *RinvT, *YpT;
   double *G64, *Rw, *dT, *eT, *betaT, *evT;
   float *amax;  // [8][n_cells]: slot k of cell c at amax[k * am_ld + c]
   int am_ld;
@@ -334,7 +334,6 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
     b.Pt = ar.take<float>((long long)nb * ell * pl.M);
     b.P2 = ar.take<float>((long long)nb * pl.M * ld);
     b.Zt = ar.take<float>((long long)nb * ell * pl.M);
-    b.Z2 = ar.take<float>((long long)nb * pl.M * ld);
     b.Rw = ar.take<double>((long long)nb * chol_scratch_doubles((int)ell));
     b.RinvT = ar.take<float>((long long)nb * ell * ld);
     b.Wrows = ar.take<float>((long long)nb * sz.kmax * ld);
@@ -607,22 +606,24 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       gram_f32(pl, b, b.Pt, Mf, ell * Mf, (int)ell, (int)Mf, amP, b.G64, ell * ell, (int)ell, nb, st);
       chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, chol_scratch_doubles((int)ell), b.RinvT, ell * ld, (int)ld, amR, st);
       fill_f32(amZ, nb, 0.f, st);
+      // Z^T = R^{-T} P^T (the sketch reads only Z^T)
       GemmArgs g = ga();
-      g.A = b.P2; g.a_ld = ld; g.a_bs = Mf * ld; g.a_amax = amP;
-      g.B = b.RinvT; g.b_ld = ld; g.b_bs = ell * ld; g.b_amax = amR;
-      g.M = (int)Mf; g.N = (int)ell; g.K = (int)ell;
-      g.C = b.Z2; g.c_ld = ld; g.c_bs = Mf * ld;
-      g.C2 = b.Zt; g.c2_ld = Mf; g.c2_bs = ell * Mf;
+      g.A = b.RinvT; g.a_ld = ld; g.a_bs = ell * ld; g.a_amax = amR;
+      g.B = b.P2; g.b_ld = ld; g.b_bs = Mf * ld; g.b_amax = amP;
+      g.ab_amax_bs = 1;
+      g.M = (int)ell; g.N = (int)Mf; g.K = (int)ell;
+      g.C = b.Zt; g.c_ld = Mf; g.c_bs = ell * Mf;
       g.c_amax = amZ;
-      g.tri = 2;
+      g.m_fastest = 1;
+      g.tri = 4;
       gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
     }
     Pair Y = (Q.T == pa.T) ? pb : pa;
     Pair other = (Q.T == pa.T) ? pa : pb;
     fill_f32(Y.am, nb, 0.f, st);
     sketch(b.Zt, SRC_F32, ell * Mf, amZ, Y.T, Y.R, Y.am);
-    const int passes = (it + 1 == pl.power_iters) ? 2 : 1;
-    Q = cholqr(Y, other, passes);
+    const bool final_basis = it + 1 == pl.power_iters;
+    Q = cholqr(Y, other, final_basis ? 2 : 1, !final_basis);
   }
   if (pl.power_iters == 0) {  // the final basis is orthonormalised twice
     Pair other = (Q.T == pa.T) ? pb : pa;
@@ -1028,7 +1029,6 @@ Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot)
     v.Pt = b.Pt + c0 * ell * M;
     v.P2 = b.P2 + c0 * M * ld;
     v.Zt = b.Zt + c0 * ell * M;
-    v.Z2 = b.Z2 + c0 * M * ld;
     v.Rw = b.Rw + c0 * chol_scratch_doubles((int)ell);
     v.RinvT = b.RinvT + c0 * ell * ld;
     if (b.pln) v.pln = b.pln + c0 * pl.pln_cell();
