@@ -204,6 +204,7 @@ struct Bufs {
   // ([T][ell_ld]); P likewise ([ell][M] and [M][ell_ld]); Z only as Z^T ([ell][M])
   float *bufA, *bufB, *bufA2, *bufB2, *Pt, *P2, *Zt, *RinvT, *YpT;
   double *G64, *Rw, *dT, *eT, *betaT, *evT;
+  double *mwg;  // exchange scratch of the multi-workgroup tridiagonalisation (FlashJoLT B B^T)
   float *amax;  // [8][n_cells]: slot k of cell c at amax[k * am_ld + c]
   int am_ld;
   // fit
@@ -335,6 +336,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
     b.P2 = ar.take<float>((long long)nb * pl.M * ld);
     b.Zt = ar.take<float>((long long)nb * ell * pl.M);
     b.Rw = ar.take<double>((long long)nb * chol_scratch_doubles((int)ell));
+    b.mwg = ar.take<double>((long long)(tridiag_mwg_bytes((int)ell, nb) / sizeof(double)));
     b.RinvT = ar.take<float>((long long)nb * ell * ld);
     b.Wrows = ar.take<float>((long long)nb * sz.kmax * ld);
     b.pln = pl.xsrc() == SRC_F32 ? nullptr : ar.take<uint16_t>((long long)nb * pl.pln_cell());
@@ -639,7 +641,8 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   }
   {
     Stage prof("eigvals_B", st);
-    sym_eigvals(b.G64, ell * ell, (int)ell, (int)ell, nb, b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, true, st);
+    sym_eigvals(b.G64, ell * ell, (int)ell, (int)ell, nb, b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, true, st,
+                b.mwg);
   }
   flash_spec(b.evT, ell, pl.q, b.norm2, b.specT, pl.nT, nb, st);
   // the fit reads Q (both layouts) from bufA / bufA2: report it by swapping this view's pointers
@@ -1030,6 +1033,7 @@ Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot)
     v.P2 = b.P2 + c0 * M * ld;
     v.Zt = b.Zt + c0 * ell * M;
     v.Rw = b.Rw + c0 * chol_scratch_doubles((int)ell);
+    v.mwg = b.mwg + c0 * (long long)(tridiag_mwg_bytes((int)ell, 1) / sizeof(double));
     v.RinvT = b.RinvT + c0 * ell * ld;
     if (b.pln) v.pln = b.pln + c0 * pl.pln_cell();
   }
@@ -1410,6 +1414,7 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
     HIP_TRY(hipMemcpyAsync(perr.data(), b.perr, nb * 8, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipStreamSynchronize(st));
     for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(n2[c]), JOLT_ENONFINITE, "non-finite ||X||^2 in a cell");
+    for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(perr[c]), JOLT_ENONFINITE, "non-finite spectrum in a cell");
     if (h_lambda) *h_lambda = ao.lambda;
     JOLT_REQUIRE(ao.status == 0, JOLT_EINFEASIBLE, "allocation infeasible: the smallest picks exceed the budget");
     const int nT = (int)pl.rT.size(), nD = (int)pl.rd.size();

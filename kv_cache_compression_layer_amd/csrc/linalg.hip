@@ -38,10 +38,16 @@ __device__ double block_sum(double v, double *red) {
 constexpr int BL = 16;
 
 __global__ void __launch_bounds__(256) bisect_kernel(const double *d_in, const double *e_in, long long t_bs, int n,
-                                                     double *evals, long long ev_bs, int clamp) {
+                                                     double *evals, long long ev_bs, int clamp, const unsigned *err,
+                                                     long long err_bs) {
   extern __shared__ double smem[];
   __shared__ double red[3][4];
   const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (err && err[b * err_bs]) {  // the reduction reported a failed exchange: no eigenvalues
+    const int j = (blockIdx.x * 256 + tid) / BL;
+    if (j < n && (tid % BL) == 0) evals[b * ev_bs + j] = __longlong_as_double(0x7ff8000000000000LL);
+    return;
+  }
   const double *d = d_in + b * t_bs, *e = e_in + b * t_bs;
   double *sd = smem, *se2 = smem + n;
   double lo0 = 1e300, hi0 = -1e300;
@@ -274,7 +280,8 @@ __device__ __forceinline__ double lane_bcast_d(double v, int l) {
 }
 
 // Row r (columns r..n-1, n - r <= 64 * TCH) held in registers x[t] = row[r + lane + 64 t]:
-// the same reflector, one read of the row.
+// the same reflector, one read of the row.  A null R skips the reflector row, a null d the
+// d/e/beta entries (v and the returned beta are always formed).
 __device__ __forceinline__ double wave_reflector_regs(const double (&x)[TCH], int n, int r, double *v, double *R, long long r_ld,
                                       double *d, double *e, double *be) {
   const int lane = threadIdx.x & 63;
@@ -302,10 +309,10 @@ __device__ __forceinline__ double wave_reflector_regs(const double (&x)[TCH], in
     if (j >= r + 1 && j < n) {
       const double vj = (j == r + 1) ? 1.0 : x[t] / v0;
       v[j] = vj;
-      R[(long long)r * r_ld + j] = vj;
+      if (R) R[(long long)r * r_ld + j] = vj;
     }
   }
-  if (lane == 0) {
+  if (lane == 0 && d) {
     d[r] = dr;
     e[r] = (sigma == 0.0) ? alpha : mu;
     be[r] = bet;
@@ -534,6 +541,234 @@ __global__ void __launch_bounds__(LT) tridiag_fused_kernel(double *A, long long 
   (void)evals;
   (void)ev_bs;
   (void)clamp;
+}
+
+// ---------------------------------------------------------------------------------------------
+// The same reduction spread over P workgroups per matrix, for matrices whose rows fit in their
+// combined LDS: workgroup w keeps the full rows i = w, w + P, w + 2P, ... (fp64) in LDS for the
+// whole reduction, and only vectors cross workgroups.  Every workgroup forms each reflector itself
+// from the published row, so a step takes one exchange.  Step j (reflector j from row j):
+//   1. read p_{j-1} and row j (after update j-2) from the exchange slot of step j-1, form c_{j-1},
+//      apply update j-1 to row j and form v_j, beta_j from it (wave 0 of every workgroup, the same
+//      arithmetic everywhere; the owner of row j writes d, e, beta and the reflector row);
+//   2. apply update j-1 to the own rows i > j (columns > j) and form p_j[i] = beta_j (A v_j)_i in
+//      the same pass (a wave takes up to MR rows at once and reads the vectors once for them);
+//   3. publish p_j of the own rows and, from the owner of row j+1, that row; wait for all P.
+// Same formulas as tridiag_fused_kernel<false>; every sum runs in a fixed order (deterministic).
+// Exchange: the published values are agent-coherent (write-through) stores and are read with
+// agent-coherent loads; the publishing wave waits for its stores to complete before it bumps the
+// per-matrix step counter, which each workgroup's first thread polls (then an acquire fence), so no
+// L2 write-back is needed per step.  Every wait is bounded: one that runs out sets the matrix's
+// error word (the bisection then reports NaN eigenvalues) and stops waiting.  The reflector row 0
+// is written after the first exchange, when every workgroup has read row 0 of A (refl may alias A).
+// Scratch per matrix: a 256-byte header (step counter, error word) and two slots of p and row
+// (mwg_ldx(n) doubles each).  LDS: (ceil(n / P) + 3) n + ceil(n / P) doubles.
+// ---------------------------------------------------------------------------------------------
+constexpr int MWG_HDR = 32;  // header doubles per matrix
+constexpr int MR = 3;        // rows a wave sweeps together
+__host__ __device__ inline long long mwg_ldx(int n) { return ((long long)n + 63) / 64 * 64; }
+__host__ __device__ inline long long mwg_doubles(int n) { return MWG_HDR + 4 * mwg_ldx(n); }
+
+__global__ void mwg_reset_kernel(double *x, long long stride, int batch) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) {
+    unsigned *h = (unsigned *)(x + b * stride);
+    h[0] = 0u;
+    h[1] = 0u;
+  }
+}
+
+__device__ __forceinline__ void xstore(double *p, double v) {
+  __hip_atomic_store((unsigned long long *)p, (unsigned long long)__double_as_longlong(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double xload(const double *p) {
+  return __longlong_as_double(
+      (long long)__hip_atomic_load((unsigned long long *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+__global__ void __launch_bounds__(LT) tridiag_mwg_kernel(const double *A, long long a_bs, int lda, int n, int P,
+                                                         double *d_out, double *e_out, double *refl, double *beta,
+                                                         long long t_bs, double *xch, unsigned spin_limit) {
+  extern __shared__ double smem[];
+  __shared__ double sbeta[2];
+  __shared__ int sfail;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwave = LT / 64;
+  // block -> (matrix, member): with the usual round-robin placement of blocks on the 8 XCDs, the
+  // members of a matrix share one XCD (and its L2) when the grid is a multiple of 8
+  const int nblk = gridDim.x;
+  const int L = (nblk & 7) == 0 ? (int)(blockIdx.x & 7) * (nblk >> 3) + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+  const int b = L / P, w = L % P;
+  const int nr = (n - w + P - 1) / P, nrmax = (n + P - 1) / P;
+  double *rows = smem;                       // [nrmax][n]: local row li is row w + P li
+  double *sv = rows + (long long)nrmax * n;  // v_j at sv + (j & 1) n (absolute columns)
+  double *sp = sv + 2 * n;                   // p_{j-1}
+  double *pout = sp + n;                     // p_j of the own rows, by local index
+  const double *Ab = A + b * a_bs;
+  double *d = d_out + b * t_bs, *e = e_out + b * t_bs, *R = refl + b * t_bs * (long long)n, *be = beta + b * t_bs;
+  double *X = xch + b * mwg_doubles(n);
+  unsigned *cnt = (unsigned *)X;  // [0] exchanges completed (P per step), [1] error word
+  const long long ldx = mwg_ldx(n);
+  double *XS = X + MWG_HDR;  // slot s: p at XS + 2 s ldx, row at XS + (2 s + 1) ldx
+  auto own_first = [&](int i0) { return i0 <= w ? 0 : (i0 - w + P - 1) / P; };
+
+  if (tid == 0) sfail = 0;
+  for (long long q = tid; q < (long long)nr * n; q += LT) {
+    const int li = (int)(q / n), c = (int)(q % n);
+    rows[q] = Ab[(long long)(w + P * li) * lda + c];
+  }
+  // step 0: reflector 0 from row 0 of A (every workgroup; d/e/beta by the owner of row 0)
+  if (wave == 0) {
+    double x[TCH];
+#pragma unroll
+    for (int t = 0; t < TCH; ++t) {
+      const int c = lane + 64 * t;
+      x[t] = c < n ? Ab[c] : 0.0;
+    }
+    const double bt = wave_reflector_regs(x, n, 0, sv, nullptr, n, w == 0 ? d : nullptr, e, be);
+    if (lane == 0) sbeta[0] = bt;
+  }
+  __syncthreads();
+
+  // update j-1 on the own rows i > j (columns > j) and p_j of those rows
+  auto sweep = [&](int j, double cprev) {
+    const double *vp = sv + ((j + 1) & 1) * n;  // v_{j-1}
+    const double *vj = sv + (j & 1) * n;
+    const double bj = sbeta[j & 1];
+    const int tstart = (j + 1) >> 6;
+    for (int l0 = own_first(j + 1) + wave; l0 < nr; l0 += nwave * MR) {
+      double vi[MR], wi[MR], s[MR];
+#pragma unroll
+      for (int q = 0; q < MR; ++q) {
+        const int li = min(l0 + q * nwave, nr - 1), i = w + P * li;
+        vi[q] = j >= 1 ? vp[i] : 0.0;
+        wi[q] = j >= 1 ? sp[i] - cprev * vp[i] : 0.0;
+        s[q] = 0.0;
+      }
+#pragma unroll
+      for (int t = 0; t < TCH; ++t)
+        if (t >= tstart) {
+          const int c = lane + 64 * t;
+          if (c > j && c < n) {
+            const double vc = j >= 1 ? vp[c] : 0.0, wc = j >= 1 ? sp[c] - cprev * vc : 0.0, xc = vj[c];
+            double a[MR];
+#pragma unroll
+            for (int q = 0; q < MR; ++q)
+              if (l0 + q * nwave < nr) a[q] = rows[(long long)(l0 + q * nwave) * n + c];
+#pragma unroll
+            for (int q = 0; q < MR; ++q)
+              if (l0 + q * nwave < nr) {
+                double u = a[q];
+                if (j >= 1) {
+                  u = a[q] - (vi[q] * wc + wi[q] * vc);
+                  rows[(long long)(l0 + q * nwave) * n + c] = u;
+                }
+                s[q] += u * xc;
+              }
+          }
+        }
+#pragma unroll
+      for (int q = 0; q < MR; ++q)
+        if (l0 + q * nwave < nr) {
+          const double sq = warp_sum_d(s[q]);
+          if (lane == 0) pout[l0 + q * nwave] = bj * sq;
+        }
+    }
+  };
+  // p_j of the own rows and (from its owner) row j+1 into slot j & 1; once those stores have
+  // completed, count the step
+  auto publish = [&](int j) {
+    if (wave == 0) {
+      double *xp = XS + 2 * (j & 1) * ldx, *xr = xp + ldx;
+      for (int li = own_first(j + 1) + lane; li < nr; li += 64) xstore(xp + w + P * li, pout[li]);
+      if ((j + 1) % P == w) {
+        const double *rr = rows + (long long)((j + 1) / P) * n;
+        for (int c = j + 1 + lane; c < n; c += 64) xstore(xr + c, rr[c]);
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (lane == 0) __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  auto wait_all = [&](unsigned target) {
+    if (tid == 0 && !sfail) {
+      unsigned it = 0;
+      while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        if (++it > spin_limit) {
+          sfail = 1;
+          __hip_atomic_fetch_or(cnt + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+  };
+
+  sweep(0, 0.0);
+  __syncthreads();
+  publish(0);
+  for (int j = 1; j <= n - 2; ++j) {
+    wait_all((unsigned)P * (unsigned)j);
+    const double *xp = XS + 2 * ((j - 1) & 1) * ldx, *xr = xp + ldx;
+    double x[TCH];
+    if (wave == 0) {  // row j, loaded beside p_{j-1}
+#pragma unroll
+      for (int t = 0; t < TCH; ++t) {
+        const int c = j + lane + 64 * t;
+        x[t] = c < n ? xload(xr + c) : 0.0;
+      }
+    }
+    for (int c = j + tid; c < n; c += LT) sp[c] = xload(xp + c);
+    if (j == 1 && w == 0)  // every workgroup has read row 0 of A
+      for (int c = 1 + tid; c < n; c += LT) R[c] = sv[c];
+    __syncthreads();
+    // c_{j-1} = (beta_{j-1} / 2) p_{j-1} . v_{j-1}, the same in every wave
+    const double *vp = sv + ((j - 1) & 1) * n;
+    double part = 0.0;
+#pragma unroll
+    for (int t = 0; t < TCH; ++t) {
+      const int c = j + lane + 64 * t;
+      if (c < n) part += sp[c] * vp[c];
+    }
+    const double cprev = 0.5 * sbeta[(j - 1) & 1] * warp_sum_d(part);
+    const bool last = (j == n - 2);
+    if (wave == 0) {
+      const double vr = vp[j], wr = sp[j] - cprev * vp[j];
+#pragma unroll
+      for (int t = 0; t < TCH; ++t) {
+        const int c = j + lane + 64 * t;
+        if (c < n) x[t] -= vr * (sp[c] - cprev * vp[c]) + wr * vp[c];
+      }
+      const bool own = (j % P) == w;
+      if (!last) {
+        const double bt = wave_reflector_regs(x, n, j, sv + (j & 1) * n, own ? R : nullptr, n, own ? d : nullptr, e, be);
+        if (lane == 0) sbeta[j & 1] = bt;
+      } else if (own) {
+        const double e2 = lane_bcast_d(x[0], 1);  // column n-1 of row n-2
+        if (lane == 0) {
+          d[n - 2] = x[0];
+          e[n - 2] = e2;
+          be[n - 2] = 0.0;
+        }
+      }
+    }
+    __syncthreads();
+    if (!last) {
+      sweep(j, cprev);
+      __syncthreads();
+      publish(j);
+    } else if (tid == 0 && (n - 1) % P == w) {
+      // row n-1: update n-3 on its diagonal entry
+      const int i = n - 1;
+      const double vi = vp[i], wi = sp[i] - cprev * vp[i];
+      d[i] = rows[(long long)(i / P) * n + i] - (vi * wi + wi * vi);
+      e[i] = 0.0;
+      be[i] = 0.0;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1268,6 +1503,7 @@ void ensure_lds_attrs() {
   (void)hipFuncSetAttribute((const void *)tridiag_values_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipFuncSetAttribute((const void *)tridiag_mwg_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)bisect_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)backtransform_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipGetLastError();
@@ -1276,16 +1512,67 @@ void ensure_lds_attrs() {
 
 size_t tridiag_lds_bytes(int n) { return ((size_t)n * n + 2 * (size_t)n) * sizeof(double); }
 
+size_t tridiag_mwg_bytes(int n, int batch) { return (size_t)batch * (size_t)mwg_doubles(n) * sizeof(double); }
+
+namespace {
+
+// Members per matrix for tridiag_mwg_kernel (the fewest whose rows fit in LDS) and the matrices
+// per launch, so that every workgroup of a launch can be resident at once (its waits need that).
+bool mwg_plan(int n, int batch, int &P, int &chunk, size_t &shm) {
+  if (n > 64 * TCH) return false;
+  int dev = 0, cus = 0, maxsh = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipDeviceGetAttribute(&maxsh, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  for (int p = 2; p <= 32; p *= 2) {
+    const long long nrm = (n + p - 1) / p;
+    const size_t bytes = (size_t)((nrm + 3) * n + nrm) * sizeof(double);
+    if (bytes + 2048 > (size_t)maxsh) continue;
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, (const void *)tridiag_mwg_kernel, LT, bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      return false;
+    }
+    const long long cap = (long long)cus * occ;
+    if (occ < 1 || cap < p) return false;
+    P = p;
+    chunk = (int)std::min<long long>(batch, cap / p);
+    shm = bytes;
+    return true;
+  }
+  return false;
+}
+
+}  // namespace
+
 void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d, double *e, double *refl,
-                 double *beta, long long t_bs, double *evals, long long ev_bs, bool clamp, hipStream_t st) {
+                 double *beta, long long t_bs, double *evals, long long ev_bs, bool clamp, hipStream_t st,
+                 double *mwg) {
   JOLT_REQUIRE(n >= 1 && n <= 8192, JOLT_EINVAL, "eigensolver: unsupported size");
   JOLT_REQUIRE(t_bs == n, JOLT_EINVAL, "eigensolver: tridiagonal stride must equal n");
   size_t lds_full = tridiag_lds_bytes(n);
   const size_t lds_cap = 150 * 1024;
   ensure_lds_attrs();
+  int P = 0, chunk = 0;
+  size_t shm_m = 0;
+  const bool multi = lds_full > lds_cap && mwg != nullptr && mwg_plan(n, batch, P, chunk, shm_m);
   if (lds_full <= lds_cap) {
     hipLaunchKernelGGL(tridiag_values_kernel, dim3(batch), dim3(LT), lds_full, st, A, a_bs, lda, (const int *)nullptr,
                        n, d, e, refl, beta, t_bs, evals, ev_bs, clamp ? 1 : 0, 1);
+  } else if (multi) {
+    const long long ms = mwg_doubles(n);
+    hipLaunchKernelGGL(mwg_reset_kernel, dim3((batch + 255) / 256), dim3(256), 0, st, mwg, ms, batch);
+    HIP_LAUNCH_CHECK();
+    for (int b0 = 0; b0 < batch; b0 += chunk) {
+      const int nm = std::min(chunk, batch - b0);
+      hipLaunchKernelGGL(tridiag_mwg_kernel, dim3(nm * P), dim3(LT), shm_m, st, A + b0 * a_bs, a_bs, lda, n, P,
+                         d + b0 * t_bs, e + b0 * t_bs, refl + b0 * t_bs * (long long)n, beta + b0 * t_bs, t_bs,
+                         mwg + b0 * ms, 1u << 21);
+      HIP_LAUNCH_CHECK();
+    }
   } else {
     const size_t shm_up = (5 * (size_t)n + 64 * TCH * (LT / 64)) * sizeof(double);
     if (n <= 64 * TCH && shm_up <= 150 * 1024) {
@@ -1303,7 +1590,8 @@ void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d
   const size_t bshm = 2 * (size_t)n * sizeof(double);
   JOLT_REQUIRE(bshm <= 150 * 1024, JOLT_EINVAL, "eigensolver: n too large for the bisection");
   dim3 bgrid((unsigned)(((long long)n * BL + 255) / 256), batch);
-  hipLaunchKernelGGL(bisect_kernel, bgrid, dim3(256), bshm, st, d, e, t_bs, n, evals, ev_bs, clamp ? 1 : 0);
+  hipLaunchKernelGGL(bisect_kernel, bgrid, dim3(256), bshm, st, d, e, t_bs, n, evals, ev_bs, clamp ? 1 : 0,
+                     multi ? (const unsigned *)mwg + 1 : nullptr, multi ? 2 * mwg_doubles(n) : 0LL);
   HIP_LAUNCH_CHECK();
 }
 

@@ -5,9 +5,13 @@
 namespace jolt {
 
 // Eigenvalues (descending) of `batch` symmetric n x n fp64 matrices A[b] (overwritten).
-// d, e, beta: [batch][n]; refl: [batch][n][n]; t_bs must equal n.
+// d, e, beta: [batch][n]; refl: [batch][n][n]; t_bs must equal n.  mwg (optional, 8-byte
+// aligned, tridiag_mwg_bytes(n, batch) bytes) lets matrices too large for one workgroup's LDS be
+// reduced by several workgroups each, their rows spread over those workgroups' LDS.
+size_t tridiag_mwg_bytes(int n, int batch);
 void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d, double *e, double *refl,
-                 double *beta, long long t_bs, double *evals, long long ev_bs, bool clamp, hipStream_t st);
+                 double *beta, long long t_bs, double *evals, long long ev_bs, bool clamp, hipStream_t st,
+                 double *mwg = nullptr);
 
 // Eigenvectors of the k_dev[b] largest eigenvalues (after sym_eigvals), as rows
 // out[b][j][0..n) (fp64 and/or fp32; out_ld >= n).  Zw: [batch][kmax][n] scratch,
