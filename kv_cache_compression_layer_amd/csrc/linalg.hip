@@ -1186,7 +1186,8 @@ __global__ void __launch_bounds__(256) backtransform_regs_kernel(const double *Z
 
 // ---------------------------------------------------------------------------------------------
 // Cholesky G = R^T R (R upper, fp64), right-looking in 32-column panels, one workgroup per
-// matrix; the inverse R^{-1} follows in diag_inv_kernel and tri_inv_kernel, which write
+// matrix; the inverse R^{-1} follows in tri_inv_kernel (from the diagonal-block inverses that
+// chol_diag_kernel leaves), which writes
 // RinvT = (R^{-1})^T as fp32 [n][ld_out] and its max |entry| (for the fp16 split of the apply GEMM).  Non-positive pivots are replaced by a tiny
 // multiple of the largest diagonal entry (documented regularisation).
 // LDS: a 32 x 32 diagonal block and a 32 x (n - k0) panel (n <= 544 keeps the panel in LDS).
@@ -1230,22 +1231,30 @@ __global__ void __launch_bounds__(256) chol_init_kernel(const double *G, long lo
 
 __global__ void __launch_bounds__(64) chol_diag_kernel(int n, double *Rw, long long r_bs, int k0) {
   __shared__ double Dk[CNB * 33];
+  __shared__ double Dr[CNB];  // reciprocals of the diagonal of R_kk
   const int b = blockIdx.x, c = threadIdx.x;
   double *R = Rw + b * r_bs, *W = R + chol_w_off(n), *Dvg = W + (long long)n * n;
   const double floor_piv = Dvg[CNB * 33];
   const int kb = min(CNB, n - k0);
   // right-looking Cholesky of the diagonal block: lane c holds column c (a[r] = W[r][c], r <= c);
   // row j of the factor is published in LDS and read back by every lane (one wave: LDS order is
-  // program order, no barrier)
+  // program order, no barrier).  The pivot chain uses 1/sqrt by the hardware estimate and two
+  // Newton steps (each doubles the correct bits; the last leaves an error of an ulp or two), so a
+  // column costs a multiply instead of a square root and a division.
   double a[CNB];
 #pragma unroll
   for (int r = 0; r < CNB; ++r) a[r] = (c < kb && r <= c && r < kb) ? W[(long long)(k0 + r) * n + k0 + c] : 0.0;
 #pragma unroll
   for (int jj = 0; jj < CNB; ++jj) {
     if (jj < kb) {
-      const double piv = sqrt(fmax(lane_bcast_d(a[jj], jj), floor_piv));
-      if (c == jj) a[jj] = piv;
-      else if (c > jj) a[jj] /= piv;  // R[jj][c]
+      const double dj = fmax(lane_bcast_d(a[jj], jj), floor_piv);
+      double y = __builtin_amdgcn_rsq(dj);
+      const double hd = 0.5 * dj;
+      y = y * fma(-hd * y, y, 1.5);
+      y = y * fma(-hd * y, y, 1.5);
+      if (c == jj) a[jj] = dj * y;
+      else if (c > jj) a[jj] *= y;  // R[jj][c]
+      if (c == 0) Dr[jj] = y;
       if (c < CNB) Dk[jj * 33 + c] = (c >= jj) ? a[jj] : 0.0;
 #pragma unroll
       for (int r = jj + 1; r < CNB; ++r) {
@@ -1259,7 +1268,8 @@ __global__ void __launch_bounds__(64) chol_diag_kernel(int n, double *Rw, long l
     for (int r = 0; r < CNB; ++r)
       if (r < kb && r <= c) R[(long long)(k0 + r) * n + k0 + c] = a[r];
   }
-  // inverse of the diagonal block: lane c solves R_kk x = e_c by back substitution
+  // inverse of the diagonal block: lane c solves R_kk x = e_c by back substitution; written for
+  // the trailing update (stride 33) and as diagonal block k0 / 32 of the triangular inverse
   double x[CNB];
 #pragma unroll
   for (int r = CNB - 1; r >= 0; --r) {
@@ -1267,11 +1277,15 @@ __global__ void __launch_bounds__(64) chol_diag_kernel(int n, double *Rw, long l
 #pragma unroll
     for (int q = r + 1; q < CNB; ++q)
       if (q <= c) v -= Dk[r * 33 + q] * x[q];
-    x[r] = (r <= c && r < kb && c < kb) ? v / Dk[r * 33 + r] : 0.0;
+    x[r] = (r <= c && r < kb && c < kb) ? v * Dr[r] : 0.0;
   }
   if (c < CNB) {
+    double *Dv = R + (long long)n * n + (long long)(k0 / CNB) * CNB * CNB;
 #pragma unroll
-    for (int r = 0; r < CNB; ++r) Dvg[r * 33 + c] = x[r];  // (R_kk^{-1})[r][c]
+    for (int r = 0; r < CNB; ++r) {
+      Dvg[r * 33 + c] = x[r];  // (R_kk^{-1})[r][c]
+      Dv[r * CNB + c] = x[r];
+    }
   }
 }
 
@@ -1324,36 +1338,6 @@ __global__ void __launch_bounds__(256) chol_update_kernel(double *Rw, long long 
   }
 }
 
-// Inverses of the 32 x 32 diagonal blocks of R (upper), one wave per block: lane c solves
-// R_ii x = e_c by back substitution with column q of R_ii held by lane q (shuffled), and writes
-// column c of the inverse to Dinv block i (row-major 32 x 32, zeros outside the block) in the
-// second half of the Cholesky scratch.
-__global__ void __launch_bounds__(64) diag_inv_kernel(double *Rw, long long r_bs, int n) {
-  const int bi = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  const int i0 = bi * CNB, ib = min(CNB, n - i0);
-  const double *R = Rw + b * r_bs;
-  double *Dv = Rw + b * r_bs + (long long)n * n + (long long)bi * CNB * CNB;
-  double a[CNB];  // a[r] = R[i0 + r][i0 + c]
-#pragma unroll
-  for (int r = 0; r < CNB; ++r) a[r] = (c < ib && r <= c) ? R[(long long)(i0 + r) * n + i0 + c] : (r == c ? 1.0 : 0.0);
-  double x[CNB];
-#pragma unroll
-  for (int r = CNB - 1; r >= 0; --r) {
-    double v = (r == c) ? 1.0 : 0.0;
-#pragma unroll
-    for (int q = r + 1; q < CNB; ++q) {
-      const double rq = lane_bcast_d(a[r], q);  // R[r][q]
-      if (q <= c) v -= rq * x[q];
-    }
-    const double rr = lane_bcast_d(a[r], r);
-    x[r] = (r <= c) ? v / rr : 0.0;
-  }
-  if (c < CNB) {
-#pragma unroll
-    for (int r = 0; r < CNB; ++r) Dv[r * CNB + c] = (c < ib && r < ib) ? x[r] : 0.0;
-  }
-}
-
 // X = R^{-1} by independent back substitutions over 16-column slabs: workgroup (cb, b) holds
 // X[:, 16 cb .. 16 cb + 15] in LDS, starts from the diagonal-block inverse and walks the block
 // rows upwards, X_i = -Dinv_i (R[i, >i] X[>i, slab]).  Writes (R^{-1})^T rows as fp32 and folds
@@ -1381,6 +1365,11 @@ __global__ void __launch_bounds__(512) tri_inv_kernel(const double *Rw, long lon
   for (int i = rd - 1; i >= 0; --i) {
     const int i0 = i * CNB, kbeg = i0 + CNB, kend = min(rows, n);
     const double *Rrow = R + (long long)(i0 + q) * n;
+    // row q of Dinv_i (upper triangular), loaded now for use after the barrier
+    const double *Di = Dinv + (long long)i * CNB * CNB + q * CNB;
+    double dv[CNB];
+#pragma unroll
+    for (int p = 0; p < CNB; ++p) dv[p] = Di[p];
     double t0 = 0.0, t1 = 0.0, t2 = 0.0, t3 = 0.0;
     int k = kbeg;
     // 16 entries of the row are loaded before any is used (one memory round trip per 16)
@@ -1405,9 +1394,10 @@ __global__ void __launch_bounds__(512) tri_inv_kernel(const double *Rw, long lon
     for (; k < kend; ++k) t0 += Rrow[k] * Xs[k * SW + c];
     Ts[q][c] = (t0 + t1) + (t2 + t3);
     __syncthreads();
-    const double *Di = Dinv + (long long)i * CNB * CNB + q * CNB;  // row q of Dinv_i
     double v = 0.0;
-    for (int p = q; p < CNB; ++p) v -= Di[p] * Ts[p][c];
+#pragma unroll
+    for (int p = 0; p < CNB; ++p)
+      if (p >= q) v -= dv[p] * Ts[p][c];
     Xs[(i0 + q) * SW + c] = v;
     __syncthreads();
   }
@@ -1657,9 +1647,7 @@ void chol_inv(const double *G, long long g_bs, int ldg, int n, int batch, double
       HIP_LAUNCH_CHECK();
     }
   }
-  const int nblk = (n + CNB - 1) / CNB;
-  hipLaunchKernelGGL(diag_inv_kernel, dim3(nblk, batch), dim3(64), 0, st, Rw, r_bs, n);
-  HIP_LAUNCH_CHECK();
+  const int nblk = (n + CNB - 1) / CNB;  // the diagonal-block inverses were written by chol_diag_kernel
   const int ncb = (n + SW - 1) / SW;
   const size_t tshm = (size_t)nblk * CNB * SW * sizeof(double);
   hipLaunchKernelGGL(tri_inv_kernel, dim3(ncb, batch), dim3(512), tshm, st, Rw, r_bs, n, RinvT, o_bs, ld_out, amax);
