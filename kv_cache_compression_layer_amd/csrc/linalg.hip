@@ -1229,12 +1229,18 @@ __global__ void __launch_bounds__(256) chol_init_kernel(const double *G, long lo
   }
 }
 
-__global__ void __launch_bounds__(64) chol_diag_kernel(int n, double *Rw, long long r_bs, int k0) {
-  __shared__ double Dk[CNB * 33];
-  __shared__ double Dr[CNB];  // reciprocals of the diagonal of R_kk
-  const int b = blockIdx.x, c = threadIdx.x;
-  double *R = Rw + b * r_bs, *W = R + chol_w_off(n), *Dvg = W + (long long)n * n;
-  const double floor_piv = Dvg[CNB * 33];
+// inverse of the diagonal block of panel k0 for the trailing update, alternating between two
+// slots by panel so that a launch can write the next panel's while its blocks read the current one
+__device__ __forceinline__ double *chol_dvg(double *W, int n, int k0) {
+  return W + (long long)n * n + (((k0 / CNB) & 1) ? CNB * 33 + 8 : 0);
+}
+
+// Factor the (updated) diagonal block of panel k0 of W into R and invert it; one wave (lane c
+// of the calling wave), Dk [CNB * 33] and Dr [CNB] in the caller's LDS.
+__device__ __forceinline__ void chol_diag_block(int n, double *R, double *W, int k0, double *Dk, double *Dr) {
+  const int c = threadIdx.x & 63;
+  const double floor_piv = W[(long long)n * n + CNB * 33];
+  double *Dvg = chol_dvg(W, n, k0);
   const int kb = min(CNB, n - k0);
   // right-looking Cholesky of the diagonal block: lane c holds column c (a[r] = W[r][c], r <= c);
   // row j of the factor is published in LDS and read back by every lane (one wave: LDS order is
@@ -1289,6 +1295,14 @@ __global__ void __launch_bounds__(64) chol_diag_kernel(int n, double *Rw, long l
   }
 }
 
+// the first panel's diagonal block (later ones are factored by the update of the panel before)
+__global__ void __launch_bounds__(64) chol_diag_kernel(int n, double *Rw, long long r_bs, int k0) {
+  __shared__ double Dk[CNB * 33];
+  __shared__ double Dr[CNB];
+  double *R = Rw + blockIdx.x * r_bs;
+  chol_diag_block(n, R, R + chol_w_off(n), k0, Dk, Dr);
+}
+
 // grid (nt * nt, batch), nt = ceil(rem / 32): tile (ti, tj), tj >= ti, of the trailing upper block
 __global__ void __launch_bounds__(256) chol_update_kernel(double *Rw, long long r_bs, int n, int k0) {
   __shared__ double Dv[CNB * 33];
@@ -1298,7 +1312,7 @@ __global__ void __launch_bounds__(256) chol_update_kernel(double *Rw, long long 
   const int ti = blockIdx.x / ntl, tj = blockIdx.x % ntl, b = blockIdx.y;
   if (tj < ti) return;
   double *R = Rw + b * r_bs, *W = R + chol_w_off(n);
-  const double *Dvg = W + (long long)n * n;
+  const double *Dvg = chol_dvg(W, n, k0);
   const int tid = threadIdx.x;
   for (int e = tid; e < CNB * 33; e += 256) Dv[e] = Dvg[e];
   for (int e = tid; e < CNB * 32; e += 256) {
@@ -1335,6 +1349,11 @@ __global__ void __launch_bounds__(256) chol_update_kernel(double *Rw, long long 
   for (int w = 0; w < 4; ++w) {
     const int jj = tj * 32 + c0 + w;
     if (ii < rem && jj < rem && jj >= ii) W[(long long)(base + ii) * n + base + jj] -= acc[w];
+  }
+  // the first trailing tile is the next panel's diagonal block, complete now: factor it here
+  if (blockIdx.x == 0) {
+    __syncthreads();
+    if (tid < 64) chol_diag_block(n, R, W, base, &Ai[0][0], &Pi[0][0]);
   }
 }
 
@@ -1624,7 +1643,7 @@ void sym_eigvecs(const double *d, const double *e, const double *refl, const dou
 }
 
 long long chol_scratch_doubles(int n) {
-  return 2LL * n * n + (long long)((n + CNB - 1) / CNB) * CNB * CNB + CNB * 33 + 8;
+  return 2LL * n * n + (long long)((n + CNB - 1) / CNB) * CNB * CNB + 2 * CNB * 33 + 8;
 }
 
 void chol_inv(const double *G, long long g_bs, int ldg, int n, int batch, double *Rw, long long r_bs, float *RinvT,
@@ -1637,9 +1656,9 @@ void chol_inv(const double *G, long long g_bs, int ldg, int n, int batch, double
     hipLaunchKernelGGL(chol_init_kernel, dim3((unsigned)std::min<long long>((nn + 255) / 256, 1024), batch), dim3(256),
                        0, st, G, g_bs, ldg, n, Rw, r_bs, amax);
     HIP_LAUNCH_CHECK();
+    hipLaunchKernelGGL(chol_diag_kernel, dim3(batch), dim3(64), 0, st, n, Rw, r_bs, 0);
+    HIP_LAUNCH_CHECK();
     for (int k0 = 0; k0 < n; k0 += CNB) {
-      hipLaunchKernelGGL(chol_diag_kernel, dim3(batch), dim3(64), 0, st, n, Rw, r_bs, k0);
-      HIP_LAUNCH_CHECK();
       const int rem = n - k0 - std::min(CNB, n - k0);
       if (rem <= 0) break;
       const int ntl = (rem + 31) / 32;
