@@ -35,7 +35,7 @@ __device__ double block_sum(double v, double *red) {
 // shifts spaced evenly inside the bracket), narrowing the bracket (BL + 1)-fold per iteration.
 // Sturm recurrence with a pivot guard, Gershgorin starting interval, stop at a relative width of
 // about 2 ulp (Golub & Van Loan, Sec. 8.4).
-constexpr int BL = 16;
+constexpr int BL = 4;
 
 __global__ void __launch_bounds__(256) bisect_kernel(const double *d_in, const double *e_in, long long t_bs, int n,
                                                      double *evals, long long ev_bs, int clamp, const unsigned *err,
