@@ -236,9 +236,9 @@ int nsplit_for(long long K, long long tiles, int batch, long long min_chunk) {
 long long tiles_of(long long M, long long N) { return ((M + 127) / 128) * ((N + 127) / 128); }
 
 // The spectra of the cells can run as kViews independent chains of consecutive cells on their own
-// streams, each with its own split-K scratch.  Measured on the 8B shape, two chains were slower
-// than one (the one-workgroup fp64 stages lose their CUs to the concurrent matrix-core launches
-// and the final eigensolve of each chain cannot overlap anything), so one chain is used.
+// streams, each with its own split-K scratch.  Measured on the 8B shape, two chains gained nothing
+// over one (the matrix-core launches of one chain already fill the GPU, and the fp64 stages of a
+// chain lose their CUs to the other's), so one chain is used.
 constexpr int kViews = 1;
 
 int n_views(const Plan &pl) {

@@ -35,8 +35,10 @@ __device__ double block_sum(double v, double *red) {
 // shifts spaced evenly inside the bracket), narrowing the bracket (BL + 1)-fold per iteration.
 // Sturm recurrence with a pivot guard, Gershgorin starting interval, stop at a relative width of
 // about 2 ulp (Golub & Van Loan, Sec. 8.4).
-constexpr int BL = 4;
+// BL: 16 lanes for small problems (enough threads to fill the GPU), 4 where the problem is large
+// enough to fill it anyway (fewer Sturm sweeps in total)
 
+template <int BL>
 __global__ void __launch_bounds__(256) bisect_kernel(const double *d_in, const double *e_in, long long t_bs, int n,
                                                      double *evals, long long ev_bs, int clamp, const unsigned *err,
                                                      long long err_bs) {
@@ -1513,7 +1515,8 @@ void ensure_lds_attrs() {
   (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_fused_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)tridiag_mwg_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
-  (void)hipFuncSetAttribute((const void *)bisect_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipFuncSetAttribute((const void *)bisect_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  (void)hipFuncSetAttribute((const void *)bisect_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)backtransform_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipGetLastError();
   done = true;
@@ -1598,9 +1601,17 @@ void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d
   // eigenvalues of the tridiagonals: BL lanes per eigenvalue, 256 / BL eigenvalues per block
   const size_t bshm = 2 * (size_t)n * sizeof(double);
   JOLT_REQUIRE(bshm <= 150 * 1024, JOLT_EINVAL, "eigensolver: n too large for the bisection");
-  dim3 bgrid((unsigned)(((long long)n * BL + 255) / 256), batch);
-  hipLaunchKernelGGL(bisect_kernel, bgrid, dim3(256), bshm, st, d, e, t_bs, n, evals, ev_bs, clamp ? 1 : 0,
-                     multi ? (const unsigned *)mwg + 1 : nullptr, multi ? 2 * mwg_doubles(n) : 0LL);
+  const unsigned *errw = multi ? (const unsigned *)mwg + 1 : nullptr;
+  const long long err_bs = multi ? 2 * mwg_doubles(n) : 0LL;
+  if ((long long)n * batch >= 4096) {
+    dim3 bgrid((unsigned)(((long long)n * 4 + 255) / 256), batch);
+    hipLaunchKernelGGL(bisect_kernel<4>, bgrid, dim3(256), bshm, st, d, e, t_bs, n, evals, ev_bs, clamp ? 1 : 0, errw,
+                       err_bs);
+  } else {
+    dim3 bgrid((unsigned)(((long long)n * 16 + 255) / 256), batch);
+    hipLaunchKernelGGL(bisect_kernel<16>, bgrid, dim3(256), bshm, st, d, e, t_bs, n, evals, ev_bs, clamp ? 1 : 0, errw,
+                       err_bs);
+  }
   HIP_LAUNCH_CHECK();
 }
 
