@@ -133,3 +133,27 @@ def test_llama2_13b_shape_flash_full_size_sampled_token_spectrum():
     Om = oracle.sketch_matrix(Xt.shape[1], ell, 0, "f16")
     _, spec = oracle.token_factors_flash(Xt, Om, q, 1, N2)
     assert np.abs(sT[0] - spec).max() <= 1e-5 * N2
+
+
+@pytest.mark.parametrize("T,C,H,D", [(8192, 2.0, 2, 64), (32768, 5.0, 4, 128)])
+def test_flash_token_spectrum_multiworkgroup_eigensolver(T, C, H, D):
+    """The B B^T eigenproblem at widths that several workgroups per matrix reduce together
+    (ell = 266: 4 per matrix; ell = 522: 16 per matrix; the unfolding is wider than ell in both):
+    the token spectrum of the first key cell against the oracle's with the same test matrix, and
+    bitwise repeatability (the workgroups' exchange keeps every sum in a fixed order)."""
+    L = 8
+    assert 4 * H * D > oracle.qcap_eq5(T, C) + 10
+    K, V, groups, cfg, rT, rd, bits = _big("f16", 1, L, H, T, D, 1.0, C)
+    s1 = jolt.spectra(K, V, cfg)
+    torch.cuda.synchronize()
+    s2 = jolt.spectra(K, V, cfg)
+    torch.cuda.synchronize()
+    sT1, sT2 = s1[0].cpu().numpy(), s2[0].cpu().numpy()
+    assert np.array_equal(sT1, sT2)
+    X = oracle.to_f64(_np(K[0, groups[0]:groups[1]]), "f16")
+    N2 = float(np.sum(X * X))
+    q = oracle.qcap_eq5(T, C)
+    Xt = oracle.token_unfolding(X)
+    Om = oracle.sketch_matrix(Xt.shape[1], q + 10, 0, "f16")
+    _, spec = oracle.token_factors_flash(Xt, Om, q, 1, N2)
+    assert np.abs(sT1[0] - spec).max() <= 1e-5 * N2
