@@ -26,7 +26,13 @@
  *   - Every entry point returns a jolt_status; on failure jolt_last_error()
  *     returns a thread-local message.  Nothing is thrown across the ABI.
  *   - Calls that share one workspace must not overlap; distinct workspaces
- *     may be used concurrently.
+ *     may be used concurrently.  Concurrent calls on one device contend for its
+ *     compute units: the FlashJoLT eigensolver (jolt_compress, jolt_spectra)
+ *     reduces each B B^T matrix with several workgroups that wait for one
+ *     another and so must all be resident at once.  Those waits are bounded:
+ *     if the workgroups cannot all be scheduled in time the affected cells get
+ *     NaN spectra (jolt_compress then fails with JOLT_ENONFINITE) rather than
+ *     the call hanging.  One call per device at a time never meets this.
  */
 #ifndef JOLT_H
 #define JOLT_H
