@@ -167,15 +167,13 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
   // load slots: A rows t0 + v / 4 (X then U_T), B rows n = v / 4 of each plane of B_j, chunk v % 4
   Raw8<SX> ra[LA];
   uint4 rb[PB][LB];
-  long long xo[LA], uo[LA];
+  int trow[LA];  // token row of each load slot (row 0 past the end; zeroed on load)
   bool oka[LA];
 #pragma unroll
   for (int it = 0; it < LA; ++it) {
     const int v = tid + it * ENT, t = t0 + (v >> 2);
     oka[it] = t < T;
-    const long long tr = oka[it] ? t : 0;
-    xo[it] = (tr * D + (v & 3) * 8) * ESX;
-    uo[it] = (tr * rT + (v & 3) * 8) * ESX;
+    trow[it] = oka[it] ? t : 0;
   }
   auto bload = [&](int k0, bool check) __attribute__((always_inline)) {
 #pragma unroll
@@ -189,12 +187,19 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
       }
   };
   auto gload_fast = [&](int k0) __attribute__((always_inline)) {
+    // (row offsets formed per stage: 64-bit offsets held per slot would cost registers)
     if (k0 < D) {
 #pragma unroll
-      for (int it = 0; it < LA; ++it) eload8<SX>(xbase + xo[it] + (long long)k0 * ESX, oka[it], ra[it]);
+      for (int it = 0; it < LA; ++it) {
+        const int c = ((tid + it * ENT) & 3) * 8 + k0;
+        eload8<SX>(xbase + ((long long)trow[it] * D + c) * ESX, oka[it], ra[it]);
+      }
     } else {
 #pragma unroll
-      for (int it = 0; it < LA; ++it) eload8<SX>(utbase + uo[it] + (long long)(k0 - D) * ESX, oka[it], ra[it]);
+      for (int it = 0; it < LA; ++it) {
+        const int c = ((tid + it * ENT) & 3) * 8 + (k0 - D);
+        eload8<SX>(utbase + ((long long)trow[it] * rT + c) * ESX, oka[it], ra[it]);
+      }
     }
     bload(k0, false);
   };
@@ -235,13 +240,17 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
 #pragma unroll
       for (int pb = PB - 1; pb >= 0; --pb) {
         if (pa + pb > MAXO) continue;
-        uint4 bf[TN];
+        // B fragments in two halves of the columns (fewer live registers)
 #pragma unroll
-        for (int q = 0; q < TN; ++q) bf[q] = *(const uint4 *)(Bs + pb * D * EKB + q * 16 * EKB + boff);
+        for (int h = 0; h < 2; ++h) {
+          uint4 bf[TN / 2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+          for (int q = 0; q < TN / 2; ++q) bf[q] = *(const uint4 *)(Bs + pb * D * EKB + (h * TN / 2 + q) * 16 * EKB + boff);
 #pragma unroll
-          for (int q = 0; q < TN; ++q) acc[i][q] = mfma<MF>(bf[q], af[i], acc[i][q]);
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int q = 0; q < TN / 2; ++q) acc[i][h * TN / 2 + q] = mfma<MF>(bf[q], af[i], acc[i][h * TN / 2 + q]);
+        }
       }
     }
   };
