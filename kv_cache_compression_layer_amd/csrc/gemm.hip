@@ -268,6 +268,80 @@ __global__ void __launch_bounds__(256) reduce_splits_dual_kernel(const float *pa
   }
 }
 
+// The same reduction on 64 x 64 tiles with 16-byte accesses on every side (rows, columns and
+// leading dimensions multiples of 4 floats): a thread sums four consecutive columns of four rows
+// (all split loads in flight together) and stores four consecutive rows of four columns of C2.
+// The splits are summed in the same fixed order, so the results equal the scalar kernel's.
+__global__ void __launch_bounds__(256) reduce_splits_dual_vec_kernel(const float *part, long long part_bs,
+                                                                     long long part_ss, int nsplit, int rows, int cols,
+                                                                     long long ld_in, float *C, long long c_bs,
+                                                                     long long c_ld, float *C2, long long c2_bs,
+                                                                     long long c2_ld, float *amax) {
+  __shared__ float tile[64][65];
+  __shared__ float wmax[4];
+  const int b = blockIdx.z, tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;  // 16 x 16 threads
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const float *pb = part + b * part_bs;
+  float lmax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = r0 + ty + 16 * k, c = c0 + 4 * tx;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < rows && c < cols) {  // cols % 4 == 0: the four columns are all inside
+      const float *p = pb + (long long)r * ld_in + c;
+      double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+      int q = 0;
+      for (; q + 4 <= nsplit; q += 4) {
+        float4 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = *(const float4 *)(p + (q + u) * part_ss);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          s0 += (double)x[u].x;
+          s1 += (double)x[u].y;
+          s2 += (double)x[u].z;
+          s3 += (double)x[u].w;
+        }
+      }
+      for (; q < nsplit; ++q) {
+        const float4 x = *(const float4 *)(p + q * part_ss);
+        s0 += (double)x.x;
+        s1 += (double)x.y;
+        s2 += (double)x.z;
+        s3 += (double)x.w;
+      }
+      v = make_float4((float)s0, (float)s1, (float)s2, (float)s3);
+      *(float4 *)(C + b * c_bs + (long long)r * c_ld + c) = v;
+    }
+    const int rr = ty + 16 * k;
+    tile[rr][4 * tx] = v.x;
+    tile[rr][4 * tx + 1] = v.y;
+    tile[rr][4 * tx + 2] = v.z;
+    tile[rr][4 * tx + 3] = v.w;
+    lmax = fmaxf(lmax, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int cc = ty + 16 * k, c = c0 + cc, r = r0 + 4 * tx;
+    if (c < cols && r < rows) {
+      if (r + 4 <= rows) {
+        *(float4 *)(C2 + b * c2_bs + (long long)c * c2_ld + r) =
+            make_float4(tile[4 * tx][cc], tile[4 * tx + 1][cc], tile[4 * tx + 2][cc], tile[4 * tx + 3][cc]);
+      } else {
+        for (int u = 0; r + u < rows; ++u) C2[b * c2_bs + (long long)c * c2_ld + r + u] = tile[4 * tx + u][cc];
+      }
+    }
+  }
+  if (amax) {
+    lmax = warp_max(lmax);
+    if ((tid & 63) == 0) wmax[tid >> 6] = lmax;
+    __syncthreads();
+    if (tid == 0)
+      atomicMax((unsigned int *)(amax + b), __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
+  }
+}
+
 }  // namespace
 
 void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int batch, int nsplit,
@@ -320,9 +394,18 @@ void reduce_splits(const float *part, long long part_bs, long long part_ss, int 
 void reduce_splits_dual(const float *part, long long part_bs, long long part_ss, int nsplit, int rows, int cols,
                         long long ld_in, float *C, long long c_bs, long long c_ld, float *C2, long long c2_bs,
                         long long c2_ld, float *amax, int batch, hipStream_t st) {
-  dim3 grid((cols + 31) / 32, (rows + 31) / 32, batch);
-  hipLaunchKernelGGL(reduce_splits_dual_kernel, grid, dim3(256), 0, st, part, part_bs, part_ss, nsplit, rows, cols,
-                     ld_in, C, c_bs, c_ld, C2, c2_bs, c2_ld, amax);
+  const bool vec = cols % 4 == 0 && ld_in % 4 == 0 && part_ss % 4 == 0 && part_bs % 4 == 0 && c_ld % 4 == 0 &&
+                   c_bs % 4 == 0 && c2_ld % 4 == 0 && c2_bs % 4 == 0 && ((uintptr_t)part & 15) == 0 &&
+                   ((uintptr_t)C & 15) == 0 && ((uintptr_t)C2 & 15) == 0;
+  if (vec) {
+    dim3 grid((cols + 63) / 64, (rows + 63) / 64, batch);
+    hipLaunchKernelGGL(reduce_splits_dual_vec_kernel, grid, dim3(256), 0, st, part, part_bs, part_ss, nsplit, rows,
+                       cols, ld_in, C, c_bs, c_ld, C2, c2_bs, c2_ld, amax);
+  } else {
+    dim3 grid((cols + 31) / 32, (rows + 31) / 32, batch);
+    hipLaunchKernelGGL(reduce_splits_dual_kernel, grid, dim3(256), 0, st, part, part_bs, part_ss, nsplit, rows, cols,
+                       ld_in, C, c_bs, c_ld, C2, c2_bs, c2_ld, amax);
+  }
   HIP_LAUNCH_CHECK();
 }
 
