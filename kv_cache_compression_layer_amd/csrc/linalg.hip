@@ -128,7 +128,6 @@ __global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long
                                                             double *evals, long long ev_bs, int clamp,
                                                             int use_lds) {
   extern __shared__ double smem[];
-  __shared__ double red[LT / 64];
   const int b = blockIdx.x;
   const int n = n_of ? n_of[b] : n_fixed;
   const int tid = threadIdx.x, nt = blockDim.x;
@@ -143,14 +142,16 @@ __global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long
   for (int i = tid; i < n * n; i += nt) W[i] = Ag[(long long)(i / n) * lda + (i % n)];
   __syncthreads();
 
+  const int lane = tid & 63, wv = tid >> 6, nwv = nt >> 6;
+  // three barriers per step: the two reductions are formed by every wave on its own (same order
+  // in every wave, so the values agree) and w = p - c v is formed inside the update
   for (int k = 0; k + 2 < n; ++k) {
     const int m = n - k - 1;  // trailing size
-    double *row = W + (long long)k * ldw + (k + 1);  // x = A[k][k+1..] (= column k by symmetry)
+    const double *row = W + (long long)k * ldw + (k + 1);  // x = A[k][k+1..] (= column k by symmetry)
     double part = 0.0;
-    for (int i = 1 + tid; i < m; i += nt) part += row[i] * row[i];
-    double sigma = block_sum(part, red);
-    double alpha = row[0];
-    __syncthreads();  // row k is overwritten by the reflector below (in place when not staged in LDS)
+    for (int i = 1 + lane; i < m; i += 64) part += row[i] * row[i];
+    const double sigma = warp_sum_d(part);
+    const double alpha = row[0];
     double bet, v0, mu;
     if (sigma == 0.0) {
       bet = 0.0;
@@ -175,7 +176,6 @@ __global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long
     if (bet == 0.0) continue;
     // p = beta * A22 v: one wave per row, lanes along the (contiguous) row
     double *A22 = W + (long long)(k + 1) * ldw + (k + 1);
-    const int lane = tid & 63, wv = tid >> 6, nwv = nt >> 6;
     for (int i = wv; i < m; i += nwv) {
       const double *ri = A22 + (long long)i * ldw;
       double s0 = 0.0, s1 = 0.0;
@@ -190,16 +190,13 @@ __global__ void __launch_bounds__(LT) tridiag_values_kernel(double *A, long long
     }
     __syncthreads();
     part = 0.0;
-    for (int i = tid; i < m; i += nt) part += pbuf[i] * vbuf[i];
-    double pv = block_sum(part, red);
-    const double c = 0.5 * bet * pv;
-    for (int i = tid; i < m; i += nt) pbuf[i] -= c * vbuf[i];  // w
-    __syncthreads();
-    // A22 -= v w^T + w v^T: one wave per row
+    for (int i = lane; i < m; i += 64) part += pbuf[i] * vbuf[i];
+    const double c = 0.5 * bet * warp_sum_d(part);
+    // A22 -= v w^T + w v^T with w = p - c v: one wave per row
     for (int i = wv; i < m; i += nwv) {
       double *ri = A22 + (long long)i * ldw;
-      const double vi = vbuf[i], wi = pbuf[i];
-      for (int jj = lane; jj < m; jj += 64) ri[jj] -= vi * pbuf[jj] + wi * vbuf[jj];
+      const double vi = vbuf[i], wi = pbuf[i] - c * vbuf[i];
+      for (int jj = lane; jj < m; jj += 64) ri[jj] -= vi * (pbuf[jj] - c * vbuf[jj]) + wi * vbuf[jj];
     }
     __syncthreads();
   }
