@@ -1460,13 +1460,45 @@ __global__ void __launch_bounds__(256) gram64_kernel(const float *P, long long p
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = d4{0.0, 0.0, 0.0, 0.0};
-  for (int k0 = 0; k0 < K; k0 += KT) {
-    for (int e = tid; e < 64 * KT; e += 256) {
-      const int r = e / KT, k = e % KT, kk = k0 + k;
-      As[r][k] = (r0 + r < rows && kk < K) ? Pb[(long long)(r0 + r) * ldp + kk] : 0.f;
-      Bs[r][k] = (c0 + r < rows && kk < K) ? Pb[(long long)(c0 + r) * ldp + kk] : 0.f;
+  // the next 32-deep slice is loaded into registers (16-byte loads when rows are 16-byte
+  // aligned) while the current one is multiplied
+  const bool vec = (ldp % 4 == 0) && (K % 4 == 0) && (((uintptr_t)P & 15) == 0);
+  float4 ra[2], rb[2];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u, r = e >> 3, k = k0 + 4 * (e & 7);
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = x;
+      if (vec) {
+        if (r0 + r < rows && k < K) x = *(const float4 *)(Pb + (long long)(r0 + r) * ldp + k);
+        if (c0 + r < rows && k < K) y = *(const float4 *)(Pb + (long long)(c0 + r) * ldp + k);
+      } else {
+        float xa[4], ya[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          xa[j] = (r0 + r < rows && k + j < K) ? Pb[(long long)(r0 + r) * ldp + k + j] : 0.f;
+          ya[j] = (c0 + r < rows && k + j < K) ? Pb[(long long)(c0 + r) * ldp + k + j] : 0.f;
+        }
+        x = make_float4(xa[0], xa[1], xa[2], xa[3]);
+        y = make_float4(ya[0], ya[1], ya[2], ya[3]);
+      }
+      ra[u] = x;
+      rb[u] = y;
     }
+  };
+  auto lstore = [&]() {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = tid + 256 * u, r = e >> 3, k = 4 * (e & 7);
+      As[r][k] = ra[u].x; As[r][k + 1] = ra[u].y; As[r][k + 2] = ra[u].z; As[r][k + 3] = ra[u].w;
+      Bs[r][k] = rb[u].x; Bs[r][k + 1] = rb[u].y; Bs[r][k + 2] = rb[u].z; Bs[r][k + 3] = rb[u].w;
+    }
+  };
+  gload(0);
+  for (int k0 = 0; k0 < K; k0 += KT) {
+    lstore();
     __syncthreads();
+    if (k0 + KT < K) gload(k0 + KT);
 #pragma unroll
     for (int ks = 0; ks < KT; ks += 4) {
       double a[2], bb[2];
