@@ -82,19 +82,23 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
     while (gi >= 0) outp[gi--] = acc;
   }
   __syncthreads();
-  // (2) table
-  for (long long w = tid; w < (long long)nc * per; w += AT) {
-    const int c = (int)(w / per), rem = (int)(w % per);
-    const int bi = rem / (nT * nD), ti = (rem / nD) % nT, di = rem % nD;
+  // (2) table, cell by cell (per-cell values hoisted; 32-bit index arithmetic within a cell)
+  for (int c = 0; c < nc; ++c) {
     const double n2 = a.norm2[c];
-    const double tsum = __dadd_rn(a.tailT[(long long)c * nT + ti], a.tailD[(long long)c * nD + di]);
-    const double tau = (n2 > 0.0) ? __ddiv_rn(tsum, n2) : 0.0;
-    a.e[w] = __dmul_rn(a.eps2[a.bits[bi]], tau);
     const long long G = a.shape[4 * c], H = a.shape[4 * c + 1], T = a.shape[4 * c + 2], D = a.shape[4 * c + 3];
-    const long long rT = a.rT_grid[ti], rd = a.rd_grid[di], b = a.bits[bi];
-    long long s = (G * H * rT * rd + T * rT + D * rd) * a.elem_bytes;
-    if (b > 0) s += G * H * T * (b * D / 8 + 4);
-    a.s[w] = s;
+    const double *tT = a.tailT + (long long)c * nT, *tD = a.tailD + (long long)c * nD;
+    double *ec = a.e + (long long)c * per;
+    long long *sc = a.s + (long long)c * per;
+    for (int rem = tid; rem < per; rem += AT) {
+      const int bi = rem / (nT * nD), ti = (rem / nD) % nT, di = rem % nD;
+      const double tsum = __dadd_rn(tT[ti], tD[di]);
+      const double tau = (n2 > 0.0) ? __ddiv_rn(tsum, n2) : 0.0;
+      ec[rem] = __dmul_rn(a.eps2[a.bits[bi]], tau);
+      const long long rT = a.rT_grid[ti], rd = a.rd_grid[di], b = a.bits[bi];
+      long long s = (G * H * rT * rd + T * rT + D * rd) * a.elem_bytes;
+      if (b > 0) s += G * H * T * (b * D / 8 + 4);
+      sc[rem] = s;
+    }
   }
   __syncthreads();
 
