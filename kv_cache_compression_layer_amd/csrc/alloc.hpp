@@ -10,7 +10,14 @@ struct AllocOut {
   double lambda;
   long long S;
   double E;
+  unsigned sync;  // step counter of the one-workgroup-per-cell kernel (cleared before it runs)
+  unsigned err;   // set when one of its bounded waits ran out
 };
+
+// status of an allocation whose workgroups could not all be scheduled together
+constexpr int kAllocEsync = -100;
+constexpr const char *kAllocEsyncMsg =
+    "allocation: its workgroups could not all be scheduled together (other work on the device)";
 
 struct AllocArgs {
   static constexpr int kMaxCells = 4096;

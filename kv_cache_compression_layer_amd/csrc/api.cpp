@@ -1358,6 +1358,7 @@ int jolt_allocate(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_byt
       off += sec.end;
     }
     if (h_lambda) *h_lambda = ao.lambda;
+    JOLT_REQUIRE(ao.status != kAllocEsync, JOLT_EHIP, kAllocEsyncMsg);
     if (ao.status != 0) {
       set_error("allocation infeasible: the smallest picks exceed the budget");
       return (int)ao.status;
@@ -1416,6 +1417,7 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
     for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(n2[c]), JOLT_ENONFINITE, "non-finite ||X||^2 in a cell");
     for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(perr[c]), JOLT_ENONFINITE, "non-finite spectrum in a cell");
     if (h_lambda) *h_lambda = ao.lambda;
+    JOLT_REQUIRE(ao.status != kAllocEsync, JOLT_EHIP, kAllocEsyncMsg);
     JOLT_REQUIRE(ao.status == 0, JOLT_EINFEASIBLE, "allocation infeasible: the smallest picks exceed the budget");
     const int nT = (int)pl.rT.size(), nD = (int)pl.rd.size();
     std::vector<CellPick> cp(nb);
