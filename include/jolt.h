@@ -29,10 +29,13 @@
  *     may be used concurrently.  Concurrent calls on one device contend for its
  *     compute units: the FlashJoLT eigensolver (jolt_compress, jolt_spectra)
  *     reduces each B B^T matrix with several workgroups that wait for one
- *     another and so must all be resident at once.  Those waits are bounded:
- *     if the workgroups cannot all be scheduled in time the affected cells get
- *     NaN spectra (jolt_compress then fails with JOLT_ENONFINITE) rather than
- *     the call hanging.  One call per device at a time never meets this.
+ *     another, and the allocation (jolt_compress, jolt_allocate) runs one
+ *     workgroup per cell that exchange their picks, so each must have all its
+ *     workgroups resident at once.  Those waits are bounded: if the workgroups
+ *     cannot all be scheduled in time, the affected cells get NaN spectra
+ *     (jolt_compress then fails with JOLT_ENONFINITE) or the allocation fails
+ *     with JOLT_EHIP, rather than the call hanging.  One call per device at a
+ *     time never meets this.
  */
 #ifndef JOLT_H
 #define JOLT_H
