@@ -184,6 +184,22 @@ int jolt_encode_residual(const void *d_X, int32_t G, int32_t H, int32_t T, int32
 /* Workspace (device bytes) needed by jolt_encode_residual; 0 on invalid arguments. */
 size_t jolt_encode_residual_workspace_bytes(int32_t G, int32_t H, int32_t T, int32_t D, int32_t rT, int32_t rd);
 
+/* FlashJoLT Gaussian test matrix (Sec. 3.1, randomized range finder), as jolt_compress draws it:
+ * element (m, c) of Omega (M x ell) is Gaussian number m*ell + c of the sketch stream of
+ * sketch_seed (SplitMix64 + Box-Muller), rounded once to dtype.  Written transposed, as
+ * d_omegaT[c][m] (device, ell*M elements of dtype; caller-owned).  JOLT_EINVAL on bad sizes or
+ * dtype.  Fully asynchronous.  Stage entry point for checking the sketch. */
+int jolt_sketch_matrix(int32_t M, int32_t ell, int32_t dtype, uint64_t sketch_seed, void *d_omegaT,
+                       void *stream);
+
+/* Testing hook for the bounded cross-workgroup waits (per-cell allocation, multi-workgroup
+ * tridiagonalisation).  spin_limit sets the polls each wait may take (0 restores the default);
+ * unreachable != 0 raises every wait's target so that it is never met, so each wait lapses after
+ * spin_limit polls while every kernel still runs to its end: the calls that follow must then fail
+ * with JOLT_EHIP (allocation) or JOLT_ENONFINITE (spectra).  Process-wide; not for production
+ * use.  Always JOLT_OK. */
+int jolt_test_wait_policy(uint32_t spin_limit, int32_t unreachable);
+
 /* Host set-up values (computed once per process and cached; Sec. 3). */
 int jolt_rotation(int32_t d_head, uint64_t seed, double *h_Q /* [d_head][d_head] */);
 int jolt_eps2(int32_t d_head, double *h_eps2 /* [9], indexed by b */);

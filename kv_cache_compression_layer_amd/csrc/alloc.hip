@@ -250,7 +250,7 @@ __device__ __forceinline__ unsigned long long x64load(const void *p) {
   return __hip_atomic_load((unsigned long long *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__global__ void __launch_bounds__(AT) alloc_mwg_kernel(AllocArgs a, unsigned spin_limit) {
+__global__ void __launch_bounds__(AT) alloc_mwg_kernel(AllocArgs a, unsigned spin_limit, unsigned target_extra) {
   constexpr int kSpec = 4096;  // spectrum entries staged in LDS for the sequential suffix sums
   __shared__ double wcost[AT / 64];
   __shared__ long long ws[AT / 64];
@@ -374,7 +374,7 @@ __global__ void __launch_bounds__(AT) alloc_mwg_kernel(AllocArgs a, unsigned spi
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (!fail_s) {
-        const unsigned target = (unsigned)nc * (unsigned)(step + 1);
+        const unsigned target = (unsigned)nc * (unsigned)(step + 1) + target_extra;
         unsigned it = 0;
         while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
           if (++it > spin_limit) {
@@ -492,10 +492,12 @@ void run_alloc(const AllocArgs &a, hipStream_t st) {
             (long long)cus * occ >= a.n_cells;
     (void)hipGetLastError();
   }
+  // the step counter and the lapse word start at zero for either kernel (the host reads err after both)
+  hipLaunchKernelGGL(alloc_sync_reset_kernel, dim3(1), dim3(1), 0, st, a.out);
+  HIP_LAUNCH_CHECK();
   if (multi) {
-    hipLaunchKernelGGL(alloc_sync_reset_kernel, dim3(1), dim3(1), 0, st, a.out);
-    HIP_LAUNCH_CHECK();
-    hipLaunchKernelGGL(alloc_mwg_kernel, dim3(a.n_cells), dim3(AT), 0, st, a, 1u << 21);
+    const WaitPolicy wp = wait_policy();
+    hipLaunchKernelGGL(alloc_mwg_kernel, dim3(a.n_cells), dim3(AT), 0, st, a, wp.spin_limit, wp.target_extra);
   } else {
     hipLaunchKernelGGL(alloc_kernel, dim3(1), dim3(AT), 0, st, a);
   }

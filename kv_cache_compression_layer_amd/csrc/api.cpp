@@ -15,6 +15,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <functional>
 #include <mutex>
 #include <string>
@@ -32,6 +33,12 @@ namespace jolt {
 static thread_local std::string g_err;
 void set_error(const std::string &msg) { g_err = msg; }
 const char *get_error() { return g_err.c_str(); }
+
+// Spin limit of the bounded cross-workgroup waits (about 2M polls of s_sleep 1: well beyond any
+// wait of co-resident workgroups) and the test-only target offset.
+static std::atomic<unsigned> g_spin_limit{1u << 21};
+static std::atomic<unsigned> g_target_extra{0u};
+WaitPolicy wait_policy() { return WaitPolicy{g_spin_limit.load(), g_target_extra.load()}; }
 
 // ------------------------------------------------------------------------------------ profiler
 // Optional per-stage timing with HIP events recorded on the caller's stream (off by default).
@@ -1128,6 +1135,104 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
   }
 }
 
+// Buffers of an allocation alone (jolt_allocate): the per-cell tables, the
+// picks and the parameter area.
+Bufs carve_alloc(Arena &ar, const Plan &pl, int n_cells) {
+  const long long per = (long long)pl.bits.size() * pl.rT.size() * pl.rd.size();
+  Bufs b{};
+  b.tailT = ar.take<double>((long long)n_cells * pl.rT.size());
+  b.tailD = ar.take<double>((long long)n_cells * pl.rd.size());
+  b.tab_e = ar.take<double>(n_cells * per);
+  b.tab_s = ar.take<long long>(n_cells * per);
+  b.pick = ar.take<int>(n_cells);
+  b.perr = ar.take<double>(n_cells);
+  b.aout = ar.take<AllocOut>(1);
+  b.params_bytes = (size_t)rup(4096 + (long long)n_cells * 40 + (pl.rT.size() + pl.rd.size()) * 4, 256);
+  b.params = ar.take<char>((long long)b.params_bytes);
+  return b;
+}
+
+// Lagrangian allocation on given spectra with the workspace d_ws (ws_bytes; ws_what names it in errors).
+int allocate_on(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_bytes, const double *d_specT,
+                const int64_t *h_specT_off, const double *d_specD, const int64_t *h_specD_off, const double *d_norm2,
+                const jolt_params *params, double budget_bytes, jolt_pick *h_picks, double *h_lambda, void *d_ws,
+                size_t ws_bytes, const char *ws_what, void *stream) {
+    JOLT_REQUIRE(n_cells >= 1 && n_cells <= AllocArgs::kMaxCells, JOLT_EINVAL, "n_cells out of range");
+    JOLT_REQUIRE(h_cell_shape && d_specT && h_specT_off && d_specD && h_specD_off && d_norm2 && params && h_picks,
+                 JOLT_EINVAL, "null argument");
+    JOLT_REQUIRE(elem_bytes == 2 || elem_bytes == 4, JOLT_EINVAL, "elem_bytes must be 2 or 4");
+    JOLT_REQUIRE(budget_bytes > 0 && isfinite(budget_bytes), JOLT_EINVAL, "budget must be positive");
+    hipStream_t st = S(stream);
+    Plan pl;
+    check_grid(params->rT_grid, params->n_rT, "rT_grid", pl.rT);
+    check_grid(params->rd_grid, params->n_rd, "rd_grid", pl.rd);
+    int Dmax = 0;
+    for (int c = 0; c < n_cells; ++c) {
+      const int32_t *s = h_cell_shape + 4 * c;
+      JOLT_REQUIRE(s[0] > 0 && s[1] > 0 && s[2] > 0 && s[3] > 0 && (s[3] * 1) % 8 == 0, JOLT_EINVAL, "bad cell shape");
+      JOLT_REQUIRE(h_specT_off[c + 1] > h_specT_off[c] && h_specD_off[c + 1] - h_specD_off[c] == s[3], JOLT_EINVAL,
+                   "bad spectrum offsets");
+      JOLT_REQUIRE(pl.rT.back() <= h_specT_off[c + 1] - h_specT_off[c], JOLT_EINVAL, "rT_grid exceeds a token spectrum");
+      JOLT_REQUIRE(pl.rd.back() <= s[3], JOLT_EINVAL, "rd_grid exceeds d_head");
+      Dmax = std::max(Dmax, (int)s[3]);
+    }
+    fill_bits_eps(params, Dmax, pl);
+    pl.n_cells = n_cells;
+    // workspace: tables + parameter area (sized first, so that a fixed scratch can refuse cleanly)
+    {
+      Arena dry;
+      carve_alloc(dry, pl, n_cells);
+      JOLT_REQUIRE(dry.off <= ws_bytes, JOLT_EWORKSPACE,
+                   std::string(ws_what) + " too small: the allocation needs " + std::to_string(dry.off) +
+                       " bytes, " + std::to_string(ws_bytes) + " available");
+    }
+    Arena ar;
+    ar.dry = false;
+    ar.base = (char *)d_ws;
+    ar.cap = ws_bytes;
+    JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
+    Bufs b = carve_alloc(ar, pl, n_cells);
+    std::vector<int> shape(h_cell_shape, h_cell_shape + 4 * n_cells);
+    std::vector<long long> offT(h_specT_off, h_specT_off + n_cells + 1), offD(h_specD_off, h_specD_off + n_cells + 1);
+    Upload u;
+    std::vector<size_t> o;
+    upload_alloc_tables(u, pl, shape, offT, offD, o);
+    upload(b, u, st);
+    AllocDev ad = bind_alloc(b.params, o);
+    run_allocation(n_cells, ad, elem_bytes, d_specT, d_specD, d_norm2, (int)pl.rT.size(), (int)pl.rd.size(),
+                   (int)pl.bits.size(), budget_bytes, b, st);
+    std::vector<int> pick(n_cells);
+    std::vector<double> perr(n_cells);
+    AllocOut ao;
+    HIP_TRY(hipMemcpyAsync(pick.data(), b.pick, n_cells * 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipMemcpyAsync(perr.data(), b.perr, n_cells * 8, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipMemcpyAsync(&ao, b.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    const int nT = (int)pl.rT.size(), nD = (int)pl.rd.size();
+    long long off = 0;
+    for (int c = 0; c < n_cells; ++c) {
+      const int i = pick[c];
+      const int bi = i / (nT * nD), ti = (i / nD) % nT, di = i % nD;
+      const int32_t *s = h_cell_shape + 4 * c;
+      jolt_pick &p = h_picks[c];
+      p.rT = pl.rT[ti]; p.rd = pl.rd[di]; p.bits = pl.bits[bi]; p.pad = 0;
+      p.bytes = eq1_bytes(s[0], s[1], s[2], s[3], elem_bytes, p.rT, p.rd, p.bits);
+      p.err_pred = perr[c];
+      Section sec = layout(s[0], s[1], s[2], s[3], elem_bytes, p.rT, p.rd, p.bits);
+      p.offset = off;
+      p.section_bytes = sec.end;
+      off += sec.end;
+    }
+    if (h_lambda) *h_lambda = ao.lambda;
+    // a lapsed wait in any workgroup (not only the one that writes the status) voids the picks
+    JOLT_REQUIRE(ao.status != kAllocEsync && ao.err == 0u, JOLT_EHIP, kAllocEsyncMsg);
+    if (ao.status != 0) {
+      set_error("allocation infeasible: the smallest picks exceed the budget");
+      return (int)ao.status;
+    }
+    return 0;
+}
+
 }  // namespace
 }  // namespace jolt
 
@@ -1233,6 +1338,24 @@ int jolt_eps2(int32_t d_head, double *h_eps2) {
   });
 }
 
+int jolt_test_wait_policy(uint32_t spin_limit, int32_t unreachable) {
+  return guarded([&]() {
+    g_spin_limit.store(spin_limit == 0 ? (1u << 21) : spin_limit);
+    g_target_extra.store(unreachable ? 1u : 0u);
+    return 0;
+  });
+}
+
+int jolt_sketch_matrix(int32_t M, int32_t ell, int32_t dtype, uint64_t sketch_seed, void *d_omegaT, void *stream) {
+  return guarded([&]() {
+    JOLT_REQUIRE(M >= 1 && ell >= 1 && (long long)M * ell <= (1LL << 31), JOLT_EINVAL, "bad sketch shape");
+    JOLT_REQUIRE(dtype == JOLT_F16 || dtype == JOLT_BF16 || dtype == JOLT_F32, JOLT_EINVAL, "bad dtype");
+    JOLT_REQUIRE(d_omegaT != nullptr, JOLT_EINVAL, "null output");
+    gen_omega(d_omegaT, dtype, M, ell, stream_key(sketch_seed, 2), S(stream));
+    return 0;
+  });
+}
+
 int jolt_spectra(const void *d_K, const void *d_V, const jolt_cache_desc *desc, const jolt_params *params,
                  double *d_specT, double *d_specD, double *d_norm2, float *d_UT, int32_t n_vec, void *d_ws,
                  size_t ws_bytes, void *stream) {
@@ -1288,82 +1411,8 @@ int jolt_allocate(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_byt
                   const double *d_norm2, const jolt_params *params, double budget_bytes, jolt_pick *h_picks,
                   double *h_lambda, void *d_ws, size_t ws_bytes, void *stream) {
   return guarded([&]() {
-    JOLT_REQUIRE(n_cells >= 1 && n_cells <= AllocArgs::kMaxCells, JOLT_EINVAL, "n_cells out of range");
-    JOLT_REQUIRE(h_cell_shape && d_specT && h_specT_off && d_specD && h_specD_off && d_norm2 && params && h_picks,
-                 JOLT_EINVAL, "null argument");
-    JOLT_REQUIRE(elem_bytes == 2 || elem_bytes == 4, JOLT_EINVAL, "elem_bytes must be 2 or 4");
-    JOLT_REQUIRE(budget_bytes > 0 && isfinite(budget_bytes), JOLT_EINVAL, "budget must be positive");
-    hipStream_t st = S(stream);
-    Plan pl;
-    check_grid(params->rT_grid, params->n_rT, "rT_grid", pl.rT);
-    check_grid(params->rd_grid, params->n_rd, "rd_grid", pl.rd);
-    int Dmax = 0;
-    for (int c = 0; c < n_cells; ++c) {
-      const int32_t *s = h_cell_shape + 4 * c;
-      JOLT_REQUIRE(s[0] > 0 && s[1] > 0 && s[2] > 0 && s[3] > 0 && (s[3] * 1) % 8 == 0, JOLT_EINVAL, "bad cell shape");
-      JOLT_REQUIRE(h_specT_off[c + 1] > h_specT_off[c] && h_specD_off[c + 1] - h_specD_off[c] == s[3], JOLT_EINVAL,
-                   "bad spectrum offsets");
-      JOLT_REQUIRE(pl.rT.back() <= h_specT_off[c + 1] - h_specT_off[c], JOLT_EINVAL, "rT_grid exceeds a token spectrum");
-      JOLT_REQUIRE(pl.rd.back() <= s[3], JOLT_EINVAL, "rd_grid exceeds d_head");
-      Dmax = std::max(Dmax, (int)s[3]);
-    }
-    fill_bits_eps(params, Dmax, pl);
-    pl.n_cells = n_cells;
-    // workspace: tables + parameter area
-    Arena ar;
-    ar.dry = false;
-    ar.base = (char *)d_ws;
-    ar.cap = ws_bytes;
-    JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
-    const long long per = (long long)pl.bits.size() * pl.rT.size() * pl.rd.size();
-    Bufs b{};
-    b.tailT = ar.take<double>((long long)n_cells * pl.rT.size());
-    b.tailD = ar.take<double>((long long)n_cells * pl.rd.size());
-    b.tab_e = ar.take<double>(n_cells * per);
-    b.tab_s = ar.take<long long>(n_cells * per);
-    b.pick = ar.take<int>(n_cells);
-    b.perr = ar.take<double>(n_cells);
-    b.aout = ar.take<AllocOut>(1);
-    b.params_bytes = (size_t)rup(4096 + (long long)n_cells * 40 + (pl.rT.size() + pl.rd.size()) * 4, 256);
-    b.params = ar.take<char>((long long)b.params_bytes);
-    std::vector<int> shape(h_cell_shape, h_cell_shape + 4 * n_cells);
-    std::vector<long long> offT(h_specT_off, h_specT_off + n_cells + 1), offD(h_specD_off, h_specD_off + n_cells + 1);
-    Upload u;
-    std::vector<size_t> o;
-    upload_alloc_tables(u, pl, shape, offT, offD, o);
-    upload(b, u, st);
-    AllocDev ad = bind_alloc(b.params, o);
-    run_allocation(n_cells, ad, elem_bytes, d_specT, d_specD, d_norm2, (int)pl.rT.size(), (int)pl.rd.size(),
-                   (int)pl.bits.size(), budget_bytes, b, st);
-    std::vector<int> pick(n_cells);
-    std::vector<double> perr(n_cells);
-    AllocOut ao;
-    HIP_TRY(hipMemcpyAsync(pick.data(), b.pick, n_cells * 4, hipMemcpyDeviceToHost, st));
-    HIP_TRY(hipMemcpyAsync(perr.data(), b.perr, n_cells * 8, hipMemcpyDeviceToHost, st));
-    HIP_TRY(hipMemcpyAsync(&ao, b.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
-    HIP_TRY(hipStreamSynchronize(st));
-    const int nT = (int)pl.rT.size(), nD = (int)pl.rd.size();
-    long long off = 0;
-    for (int c = 0; c < n_cells; ++c) {
-      const int i = pick[c];
-      const int bi = i / (nT * nD), ti = (i / nD) % nT, di = i % nD;
-      const int32_t *s = h_cell_shape + 4 * c;
-      jolt_pick &p = h_picks[c];
-      p.rT = pl.rT[ti]; p.rd = pl.rd[di]; p.bits = pl.bits[bi]; p.pad = 0;
-      p.bytes = eq1_bytes(s[0], s[1], s[2], s[3], elem_bytes, p.rT, p.rd, p.bits);
-      p.err_pred = perr[c];
-      Section sec = layout(s[0], s[1], s[2], s[3], elem_bytes, p.rT, p.rd, p.bits);
-      p.offset = off;
-      p.section_bytes = sec.end;
-      off += sec.end;
-    }
-    if (h_lambda) *h_lambda = ao.lambda;
-    JOLT_REQUIRE(ao.status != kAllocEsync, JOLT_EHIP, kAllocEsyncMsg);
-    if (ao.status != 0) {
-      set_error("allocation infeasible: the smallest picks exceed the budget");
-      return (int)ao.status;
-    }
-    return 0;
+    return allocate_on(n_cells, h_cell_shape, elem_bytes, d_specT, h_specT_off, d_specD, h_specD_off, d_norm2, params,
+                       budget_bytes, h_picks, h_lambda, d_ws, ws_bytes, "workspace", stream);
   });
 }
 
@@ -1417,7 +1466,7 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
     for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(n2[c]), JOLT_ENONFINITE, "non-finite ||X||^2 in a cell");
     for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(perr[c]), JOLT_ENONFINITE, "non-finite spectrum in a cell");
     if (h_lambda) *h_lambda = ao.lambda;
-    JOLT_REQUIRE(ao.status != kAllocEsync, JOLT_EHIP, kAllocEsyncMsg);
+    JOLT_REQUIRE(ao.status != kAllocEsync && ao.err == 0u, JOLT_EHIP, kAllocEsyncMsg);
     JOLT_REQUIRE(ao.status == 0, JOLT_EINFEASIBLE, "allocation infeasible: the smallest picks exceed the budget");
     const int nT = (int)pl.rT.size(), nD = (int)pl.rd.size();
     std::vector<CellPick> cp(nb);

@@ -47,6 +47,16 @@ struct Fail {
 
 #define HIP_LAUNCH_CHECK() HIP_TRY(hipGetLastError())
 
+// Bounded cross-workgroup waits (the per-cell allocation and the multi-workgroup
+// tridiagonalisation): each wait polls a step counter at most spin_limit times, for a target count
+// raised by target_extra.  target_extra is 0 except under jolt_test_wait_policy(), where it makes
+// every wait lapse so that the lapse reporting can be exercised while every kernel still ends.
+struct WaitPolicy {
+  unsigned spin_limit;
+  unsigned target_extra;
+};
+WaitPolicy wait_policy();
+
 // ---------------------------------------------------------------------------------------------
 // device helpers
 // ---------------------------------------------------------------------------------------------

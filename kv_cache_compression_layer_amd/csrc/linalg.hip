@@ -588,7 +588,8 @@ __device__ __forceinline__ double xload(const double *p) {
 
 __global__ void __launch_bounds__(LT) tridiag_mwg_kernel(const double *A, long long a_bs, int lda, int n, int P,
                                                          double *d_out, double *e_out, double *refl, double *beta,
-                                                         long long t_bs, double *xch, unsigned spin_limit) {
+                                                         long long t_bs, double *xch, unsigned spin_limit,
+                                                         unsigned target_extra) {
   extern __shared__ double smem[];
   __shared__ double sbeta[2];
   __shared__ int sfail;
@@ -691,6 +692,7 @@ __global__ void __launch_bounds__(LT) tridiag_mwg_kernel(const double *A, long l
     }
   };
   auto wait_all = [&](unsigned target) {
+    target += target_extra;
     if (tid == 0 && !sfail) {
       unsigned it = 0;
       while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -1605,13 +1607,14 @@ void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d
                        n, d, e, refl, beta, t_bs, evals, ev_bs, clamp ? 1 : 0, 1);
   } else if (multi) {
     const long long ms = mwg_doubles(n);
+    const WaitPolicy wp = wait_policy();
     hipLaunchKernelGGL(mwg_reset_kernel, dim3((batch + 255) / 256), dim3(256), 0, st, mwg, ms, batch);
     HIP_LAUNCH_CHECK();
     for (int b0 = 0; b0 < batch; b0 += chunk) {
       const int nm = std::min(chunk, batch - b0);
       hipLaunchKernelGGL(tridiag_mwg_kernel, dim3(nm * P), dim3(LT), shm_m, st, A + b0 * a_bs, a_bs, lda, n, P,
                          d + b0 * t_bs, e + b0 * t_bs, refl + b0 * t_bs * (long long)n, beta + b0 * t_bs, t_bs,
-                         mwg + b0 * ms, 1u << 21);
+                         mwg + b0 * ms, wp.spin_limit, wp.target_extra);
       HIP_LAUNCH_CHECK();
     }
   } else {

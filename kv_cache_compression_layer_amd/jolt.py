@@ -23,7 +23,7 @@ DTYPE_OF = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 EXPORTS = ["jolt_workspace_bytes", "jolt_output_bytes", "jolt_allocate", "jolt_compress", "jolt_reconstruct",
            "jolt_spectra", "jolt_token_spectrum_len", "jolt_encode_residual",
            "jolt_encode_residual_workspace_bytes", "jolt_rotation", "jolt_eps2", "jolt_last_error", "jolt_profile",
-           "jolt_profile_read"]
+           "jolt_profile_read", "jolt_sketch_matrix", "jolt_test_wait_policy"]
 
 
 class JoltError(RuntimeError):
@@ -85,6 +85,8 @@ def load():
         "jolt_eps2": (ctypes.c_int, [i32, ctypes.POINTER(dbl)]),
         "jolt_last_error": (ctypes.c_char_p, []),
         "jolt_profile": (ctypes.c_int, [i32]),
+        "jolt_sketch_matrix": (ctypes.c_int, [i32, i32, i32, ctypes.c_uint64, P, P]),
+        "jolt_test_wait_policy": (ctypes.c_int, [ctypes.c_uint32, i32]),
         "jolt_profile_read": (i32, [ctypes.c_char_p, i32, ctypes.POINTER(dbl), ctypes.POINTER(i32), i32]),
     }
     for name, (res, args) in sig.items():
@@ -234,11 +236,11 @@ def allocate(cell_shapes, elem_bytes, specT_list, specD_list, norm2, rT_grid, rd
     dT = torch.from_numpy(np.concatenate(specT_list).astype(np.float64)).to(device)
     dD = torch.from_numpy(np.concatenate(specD_list).astype(np.float64)).to(device)
     dn = torch.from_numpy(np.asarray(norm2, dtype=np.float64)).to(device)
+    picks = (Pick * n)()
+    lam = ctypes.c_double(0.0)
     per = (len(set(bits) | {0})) * len(rT_grid) * len(rd_grid)
     ws = torch.empty(n * per * 16 + n * (len(rT_grid) + len(rd_grid)) * 8 + n * 64 + (1 << 20), dtype=torch.uint8,
                      device=device)
-    picks = (Pick * n)()
-    lam = ctypes.c_double(0.0)
     status = lib.jolt_allocate(n, shp, int(elem_bytes), _ptr(dT), offT.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                _ptr(dD), offD.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr(dn),
                                ctypes.byref(cfg.params), float(budget), picks, ctypes.byref(lam), _ptr(ws),
@@ -275,6 +277,18 @@ def eps2(d_head):
     out = np.zeros(9)
     _check(load().jolt_eps2(d_head, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
     return out
+
+
+def sketch_matrix(M, ell, dtype, seed=0, device="cuda"):
+    """Omega^T (ell x M) in the cache dtype, as jolt_compress draws it (bf16 returned as torch.bfloat16)."""
+    out = torch.empty(ell, M, dtype=TORCH_DTYPE[dtype], device=device)
+    _check(load().jolt_sketch_matrix(int(M), int(ell), int(dtype), int(seed), _ptr(out), _stream()))
+    return out
+
+
+def test_wait_policy(spin_limit=0, unreachable=False):
+    """Testing hook: spin limit of the bounded cross-workgroup waits; unreachable=True makes every wait lapse."""
+    _check(load().jolt_test_wait_policy(int(spin_limit), 1 if unreachable else 0))
 
 
 def profile(enable=True):

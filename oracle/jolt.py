@@ -38,7 +38,7 @@ __all__ = [
     "pack_rows", "unpack_rows", "rotation", "sketch_matrix", "eps2_calibrate", "qcap_eq5",
     "cell_bytes", "token_unfolding", "feature_spectrum", "token_factors_exact",
     "token_factors_flash", "suffix_sums", "cell_table", "argmin_cell", "allocate",
-    "fit_cell", "encode_cell", "decode_cell", "cells_of_cache", "section_layout",
+    "fit_cell", "rotated_residual", "encode_cell", "decode_cell", "cells_of_cache", "section_layout",
     "write_blob", "read_blob_cell", "compress", "reconstruct", "CellShape",
 ]
 
@@ -367,18 +367,24 @@ def fit_cell(X, UT_r, rd):
     return UT, Ud, core, np.maximum(w, 0.0)
 
 
+def rotated_residual(X, UTr, Udr, Cr, Qrot):
+    """Backbone U_T core U_d^T from the stored (rounded) factors, and the residual rows
+    (X - backbone) rotated along features, E Q (rows in (layer, head, token) order)."""
+    Xt = np.einsum("tr,ghrk,dk->ghtd", UTr, Cr, Udr, optimize=True)
+    D = X.shape[-1]
+    return Xt, (X - Xt).reshape(-1, D) @ Qrot
+
+
 def encode_cell(X, UT, Ud, core, b, Qrot, dtype):
     """Round factors to the storage dtype, rebuild the backbone from the rounded
     factors, take the residual, rotate it along features and quantise it per row."""
     UTr = round_to_dtype(UT, dtype)
     Udr = round_to_dtype(Ud, dtype)
     Cr = round_to_dtype(core, dtype)
-    Xt = np.einsum("tr,ghrk,dk->ghtd", UTr, Cr, Udr, optimize=True)
+    Xt, Erot = rotated_residual(X, UTr, Udr, Cr, Qrot)
     out = {"UT": UTr, "Ud": Udr, "core": Cr, "backbone": Xt, "b": b}
     if b > 0:
-        D = X.shape[-1]
-        E = (X - Xt).reshape(-1, D)
-        u, s = quantize_rows(E @ Qrot, b)
+        u, s = quantize_rows(Erot, b)
         out["u"], out["scales"] = u, s
     return out
 

@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import synth
+from _checks import lambda_consistency
 from kv_cache_compression_layer_amd import jolt
 
 pytestmark = pytest.mark.gpu
@@ -169,8 +170,9 @@ def test_spectra_and_token_subspaces_match_oracle(name):
     for i, x in enumerate(ref["cells"]):
         N2 = x["norm2"]
         assert abs(n2[i] - N2) <= 1e-6 * N2
-        assert np.abs(sD[i] - x["specD"]).max() <= 1e-5 * N2
-        assert np.abs(sT[i] - x["specT"]).max() <= 1e-5 * N2
+        # per entry: relative 1e-4 plus a floor of 1e-7 ||X||^2 (the fp32-accumulated Gram partials)
+        assert np.all(np.abs(sD[i] - x["specD"]) <= 1e-4 * x["specD"] + 1e-7 * N2), np.abs(sD[i] - x["specD"]).max() / N2
+        assert np.all(np.abs(sT[i] - x["specT"]) <= 1e-4 * x["specT"] + 1e-7 * N2), np.abs(sT[i] - x["specT"]).max() / N2
         # spectrum of a flash cell sums to ||X||^2 (tail entry)
         if c["p"]["mode"] == "flash":
             assert abs(sT[i].sum() - n2[i]) <= 1e-9 * n2[i]
@@ -199,8 +201,16 @@ def test_compress_end_to_end_matches_oracle(name):
     same_picks = [(p["rT"], p["rd"], p["bits"]) for p in picks] == [(x["rT"], x["rd"], x["b"]) for x in ref["cells"]]
     assert same_picks, ([(p["rT"], p["rd"], p["bits"]) for p in picks], [(x["rT"], x["rd"], x["b"]) for x in ref["cells"]])
     # lambda is the first bisection midpoint that lands in [0.995 B, B]; spectra that agree to fp32
-    # rounding may accept a neighbouring midpoint, so lambda is compared loosely and the picks exactly
+    # rounding may accept a neighbouring midpoint, so lambda is compared loosely, and the picks are
+    # checked to be the exact argmin at the GPU's lambda (its own spectra; the oracle's up to near-ties)
     assert abs(lam - ref["lam"]) <= 1e-2 * ref["lam"]
+    sT, sD, n2, _ = jolt.spectra(c["Kd"], c["Vd"], c["cfg"])
+    torch.cuda.synchronize()
+    ties = lambda_consistency(picks, lam, (sT.cpu().numpy(), sD.cpu().numpy(), n2.cpu().numpy()), ref["cells"],
+                              oracle.CellShape(c["G"], c["cfg"].desc.n_heads, c["T"], c["D"]),
+                              oracle.DTYPE_BYTES[c["dt"]], c["rT"], c["rd"], c["bits"], c["p"]["eps2"])
+    if ties:
+        print("near-tie cells (oracle argmin differs within the spectra difference):", ties)
     for x in ref["cells"]:
         got = _cell_view(Ko if x["kv"] == 0 else Vo, x, c["groups"]).double().cpu().numpy()
         X = x["X"]
