@@ -125,6 +125,20 @@ int jolt_allocate(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_byt
                   jolt_pick *h_picks, double *h_lambda, void *d_ws, size_t ws_bytes,
                   void *stream);
 
+/* jolt_allocate without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * results and errors as jolt_allocate, minus d_ws / ws_bytes: the tables, exchange slots and parameter
+ * area live in a 16 MiB scratch array of the library, one per device, held until the process ends.
+ * Calls whose tables need more (about n_cells * n_bits * n_rT * n_rd * 16 bytes plus a few KB) fail
+ * with JOLT_EWORKSPACE before any work is enqueued.  The call allocates nothing; every call on a
+ * device shares that device's scratch, so calls that overlap on one device race (the caller
+ * serialises them; one call ends with its stream synchronisation). */
+int jolt_allocate_static(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_bytes,
+                         const double *d_specT, const int64_t *h_specT_off,
+                         const double *d_specD, const int64_t *h_specD_off,
+                         const double *d_norm2, const jolt_params *params, double budget_bytes,
+                         jolt_pick *h_picks, double *h_lambda, void *stream);
+
 /* Whole compression of K and V (Sec. 3 and Sec. 3.1): spectra, allocation under one budget,
  * ST-HOSVD fit, rotated b-bit residual.  Writes the blob (layout below) to d_out.
  *   h_picks   host jolt_pick[n_seq*n_groups*2]; h_lambda host double (may be NULL).

@@ -1135,7 +1135,7 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
   }
 }
 
-// Buffers of an allocation alone (jolt_allocate): the per-cell tables, the
+// Buffers of an allocation alone (jolt_allocate, jolt_allocate_static): the per-cell tables, the
 // picks and the parameter area.
 Bufs carve_alloc(Arena &ar, const Plan &pl, int n_cells) {
   const long long per = (long long)pl.bits.size() * pl.rT.size() * pl.rd.size();
@@ -1237,6 +1237,33 @@ int allocate_on(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_bytes
 }  // namespace jolt
 
 using namespace jolt;
+
+// Device scratch of jolt_allocate_static, for callers that cannot allocate device memory: the
+// allocation's tables, exchange slots and parameter area.  Every device the library runs on holds its
+// own copy for the life of the process; its address is looked up once per device (host code never
+// passes the array's name itself to a kernel or copy: on the host that name is only a stand-in).
+constexpr size_t kStaticScratchBytes = 16u << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+// Device address of this device's scratch (hipGetSymbolAddress on the first call per device, with that
+// device current).
+char *static_scratch() {
+  static std::mutex mu;
+  static std::vector<char *> per_dev;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(mu);
+  if ((int)per_dev.size() <= dev) per_dev.resize(dev + 1, nullptr);
+  if (per_dev[dev] == nullptr) {
+    void *ptr = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    JOLT_REQUIRE(ptr != nullptr && ((uintptr_t)ptr % 256) == 0, JOLT_EHIP, "static scratch: bad device address");
+    per_dev[dev] = (char *)ptr;
+  }
+  return per_dev[dev];
+}
+}  // namespace
 
 extern "C" {
 
@@ -1413,6 +1440,17 @@ int jolt_allocate(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_byt
   return guarded([&]() {
     return allocate_on(n_cells, h_cell_shape, elem_bytes, d_specT, h_specT_off, d_specD, h_specD_off, d_norm2, params,
                        budget_bytes, h_picks, h_lambda, d_ws, ws_bytes, "workspace", stream);
+  });
+}
+
+int jolt_allocate_static(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_bytes, const double *d_specT,
+                         const int64_t *h_specT_off, const double *d_specD, const int64_t *h_specD_off,
+                         const double *d_norm2, const jolt_params *params, double budget_bytes, jolt_pick *h_picks,
+                         double *h_lambda, void *stream) {
+  return guarded([&]() {
+    char *ws = static_scratch();
+    return allocate_on(n_cells, h_cell_shape, elem_bytes, d_specT, h_specT_off, d_specD, h_specD_off, d_norm2, params,
+                       budget_bytes, h_picks, h_lambda, ws, kStaticScratchBytes, "static scratch (16 MiB)", stream);
   });
 }
 

@@ -23,7 +23,7 @@ DTYPE_OF = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 EXPORTS = ["jolt_workspace_bytes", "jolt_output_bytes", "jolt_allocate", "jolt_compress", "jolt_reconstruct",
            "jolt_spectra", "jolt_token_spectrum_len", "jolt_encode_residual",
            "jolt_encode_residual_workspace_bytes", "jolt_rotation", "jolt_eps2", "jolt_last_error", "jolt_profile",
-           "jolt_profile_read", "jolt_sketch_matrix", "jolt_test_wait_policy"]
+           "jolt_profile_read", "jolt_sketch_matrix", "jolt_test_wait_policy", "jolt_allocate_static"]
 
 
 class JoltError(RuntimeError):
@@ -75,6 +75,9 @@ def load():
         "jolt_allocate": (ctypes.c_int, [i32, ctypes.POINTER(i32), i32, P, ctypes.POINTER(i64), P,
                                          ctypes.POINTER(i64), P, pp, dbl, ctypes.POINTER(Pick),
                                          ctypes.POINTER(dbl), P, sz, P]),
+        "jolt_allocate_static": (ctypes.c_int, [i32, ctypes.POINTER(i32), i32, P, ctypes.POINTER(i64), P,
+                                                ctypes.POINTER(i64), P, pp, dbl, ctypes.POINTER(Pick),
+                                                ctypes.POINTER(dbl), P]),
         "jolt_compress": (ctypes.c_int, [P, P, pd, pp, P, sz, P, sz, ctypes.POINTER(Pick), ctypes.POINTER(dbl), P]),
         "jolt_reconstruct": (ctypes.c_int, [P, pd, pp, ctypes.POINTER(Pick), P, P, P, sz, P]),
         "jolt_spectra": (ctypes.c_int, [P, P, pd, pp, P, P, P, P, i32, P, sz, P]),
@@ -225,8 +228,10 @@ def spectra(K, V, cfg, n_vec=0, ws=None):
 
 
 def allocate(cell_shapes, elem_bytes, specT_list, specD_list, norm2, rT_grid, rd_grid, bits, budget, eps2=None,
-             device="cuda"):
-    """Lagrangian allocation on given spectra (lists of 1-D float64 arrays, one per cell)."""
+             device="cuda", static_scratch=False):
+    """Lagrangian allocation on given spectra (lists of 1-D float64 arrays, one per cell).
+
+    static_scratch=True calls jolt_allocate_static (no workspace: the library's fixed device scratch)."""
     lib = load()
     cfg = Config(1, 1, 1, 1, 64, F16, [0, 1], EXACT, rT_grid, rd_grid, bits, 2.0, eps2=eps2)
     n = len(cell_shapes)
@@ -238,6 +243,13 @@ def allocate(cell_shapes, elem_bytes, specT_list, specD_list, norm2, rT_grid, rd
     dn = torch.from_numpy(np.asarray(norm2, dtype=np.float64)).to(device)
     picks = (Pick * n)()
     lam = ctypes.c_double(0.0)
+    if static_scratch:
+        status = lib.jolt_allocate_static(n, shp, int(elem_bytes), _ptr(dT),
+                                          offT.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr(dD),
+                                          offD.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr(dn),
+                                          ctypes.byref(cfg.params), float(budget), picks, ctypes.byref(lam),
+                                          _stream())
+        return status, [_pick_dict(p) for p in picks], lam.value
     per = (len(set(bits) | {0})) * len(rT_grid) * len(rd_grid)
     ws = torch.empty(n * per * 16 + n * (len(rT_grid) + len(rd_grid)) * 8 + n * 64 + (1 << 20), dtype=torch.uint8,
                      device=device)
