@@ -212,8 +212,14 @@ struct Bufs {
   float *bufA, *bufB, *bufA2, *bufB2, *Pt, *P2, *Zt, *RinvT, *YpT;
   double *G64, *Rw, *dT, *eT, *betaT, *evT;
   double *mwg;  // exchange scratch of the multi-workgroup tridiagonalisation (FlashJoLT B B^T)
-  float *amax;  // [8][n_cells]: slot k of cell c at amax[k * am_ld + c]
+  float *amax;  // [9][n_cells]: slot k of cell c at amax[k * am_ld + c]
   int am_ld;
+  // FlashJoLT with power iterations: the final basis is kept implicit (Q = Y R^{-1} is never formed).
+  // The fit then reads Y ([T][ell_ld], bufA2) with its |max| basis_am, R^{-T} (RinvT) and P' = Y^T X
+  // (P2); Wt holds W~ = R^{-1} W as rows.  basis_implicit = 0: bufA2 holds an orthonormal Q.
+  int basis_implicit;
+  float *basis_am;
+  float *Wt;
   // fit
   float *Wrows, *Udrows, *Cp, *Udr, *Cr, *Vt, *Bcat, *bamax, *Qf, *Qtf;
   uint16_t *Bpl;  // 16-bit planes of Bcat, [cell][plane][GH][D][Kb]
@@ -325,7 +331,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
   b.specT = ar.take<double>((long long)nb * pl.nT);
   b.specD = ar.take<double>((long long)nb * D);
   b.norm2 = ar.take<double>(nb);
-  b.amax = ar.take<float>(8LL * nb);
+  b.amax = ar.take<float>(9LL * nb);
   b.am_ld = nb;
   const long long n_tok = pl.mode == JOLT_FLASH ? ell : pl.T;  // size of the token-side eigenproblem
   b.G64 = ar.take<double>((long long)nb * n_tok * n_tok);
@@ -346,6 +352,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
     b.mwg = ar.take<double>((long long)(tridiag_mwg_bytes((int)ell, nb) / sizeof(double)));
     b.RinvT = ar.take<float>((long long)nb * ell * ld);
     b.Wrows = ar.take<float>((long long)nb * sz.kmax * ld);
+    b.Wt = ar.take<float>((long long)nb * sz.kmax * ld);
     b.pln = pl.xsrc() == SRC_F32 ? nullptr : ar.take<uint16_t>((long long)nb * pl.pln_cell());
   } else {
     b.bufB = ar.take<float>((long long)nb * sz.kmax * pl.T_ld);  // token factor rows
@@ -602,6 +609,16 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     return y;
   };
 
+  // R alone from the Gram of the rows of Yt (the final basis of a power iteration stays implicit)
+  auto chol_only = [&](Pair y) {
+    Stage prof("cholqr_tall", st);
+    gram_f32(pl, b, y.T, Tld, ell * Tld, (int)ell, (int)T, y.am, b.G64, ell * ell, (int)ell, nb, st);
+    chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, chol_scratch_doubles((int)ell), b.RinvT, ell * ld, (int)ld,
+             amR, st);
+  };
+  b.basis_implicit = 0;
+  b.basis_am = nullptr;
+
   sketch(b.omegaT, pl.xsrc(), 0, nullptr, pa.T, pa.R, pa.am);
   if (side_work) xready = side_work();
   Pair Q = cholqr(pa, pb, 1, pl.power_iters > 0);
@@ -631,10 +648,20 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     Pair other = (Q.T == pa.T) ? pa : pb;
     fill_f32(Y.am, nb, 0.f, st);
     sketch(b.Zt, SRC_F32, ell * Mf, amZ, Y.T, Y.R, Y.am);
-    const bool final_basis = it + 1 == pl.power_iters;
-    Q = cholqr(Y, other, final_basis ? 2 : 1, !final_basis);
+    if (it + 1 == pl.power_iters) {
+      // The final basis Q = Y R^{-1} (one Cholesky-QR pass in exact arithmetic) is not formed: its
+      // Gram gives R, the projection runs on Y (P' = Y^T X) and B = Q^T X = R^{-T} P'.  The products
+      // that would read Q read Y and R^{-1} instead (U_T = Y (R^{-1} W), Y_p = (R^{-1} W)^T P'), so no
+      // second pass is needed for orthogonality: the basis is only ever used through R.
+      chol_only(Y);
+      Q = Y;
+      b.basis_implicit = 1;
+      b.basis_am = Y.am;
+    } else {
+      Q = cholqr(Y, other, 1, true);
+    }
   }
-  if (pl.power_iters == 0) {  // the final basis is orthonormalised twice
+  if (pl.power_iters == 0) {  // the final basis (the raw sketch) is orthonormalised twice, explicitly
     Pair other = (Q.T == pa.T) ? pb : pa;
     Q = cholqr(Q, other, 1);
   }
@@ -642,9 +669,24 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   float *amP1 = b.amax + 5 * am;
   fill_f32(amP1, nb, 0.f, st);
   project(Q.T, Q.am, amP1);
+  const float *Bp = b.Pt;
+  if (b.basis_implicit) {
+    // B = R^{-T} P' ([ell][M]; R^{-T} is lower triangular), into the free Z^T buffer
+    Stage prof("basis_apply", st);
+    GemmArgs g = ga();
+    g.A = b.RinvT; g.a_ld = ld; g.a_bs = ell * ld; g.a_amax = amR;
+    g.B = b.P2; g.b_ld = ld; g.b_bs = Mf * ld; g.b_amax = amP1;
+    g.ab_amax_bs = 1;
+    g.M = (int)ell; g.N = (int)Mf; g.K = (int)ell;
+    g.C = b.Zt; g.c_ld = Mf; g.c_bs = ell * Mf;
+    g.m_fastest = 1;
+    g.tri = 4;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
+    Bp = b.Zt;
+  }
   {
     Stage prof("gram64", st);
-    gram64(b.Pt, ell * Mf, (int)Mf, (int)ell, (int)Mf, b.G64, ell * ell, (int)ell, nb, st);
+    gram64(Bp, ell * Mf, (int)Mf, (int)ell, (int)Mf, b.G64, ell * ell, (int)ell, nb, st);
   }
   {
     Stage prof("eigvals_B", st);
@@ -652,7 +694,8 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
                 b.mwg);
   }
   flash_spec(b.evT, ell, pl.q, b.norm2, b.specT, pl.nT, nb, st);
-  // the fit reads Q (both layouts) from bufA / bufA2: report it by swapping this view's pointers
+  // the fit reads the final basis (Q, or Y when implicit; both layouts) from bufA / bufA2: report it by
+  // swapping this view's pointers
   if (Q.T != b.bufA) {
     std::swap(b.bufA, b.bufB);
     std::swap(b.bufA2, b.bufB2);
@@ -776,6 +819,45 @@ struct CellPick {
   Section sec;
 };
 
+// Token factor columns 0..kmax-1 of every FlashJoLT cell as rows of length T (U_T^T, [nb][kmax][Tld],
+// the first m rows computed) from the eigenvector rows W of B B^T (b.Wrows): U_T = Q W, or
+// U_T = Y (R^{-1} W) when the final basis is implicit.  Returns the rows applied to the basis (W, or
+// R^{-1} W in b.Wt) and their |max| slot (null: |entries| <= 1), which the token projection reuses.
+struct FactorRows {
+  const float *rows;
+  const float *amax;
+};
+FactorRows flash_factor_rows(const Plan &pl, Bufs &b, long long kmax, int m, float *UTt, hipStream_t st) {
+  const int nb = pl.n_cells;
+  const long long ell = pl.ell, ld = pl.ell_ld, Tld = pl.T_ld;
+  FactorRows fr{b.Wrows, nullptr};
+  if (b.basis_implicit) {
+    // W~ rows = W rows R^{-T}: W~[r][k] = sum_j W[r][j] RinvT[j][k] (B contiguous along N)
+    float *amW = b.amax + 8 * b.am_ld;
+    fill_f32(amW, nb, 0.f, st);
+    fill_f32(b.Wt, (long long)nb * kmax * ld, 0.f, st);
+    GemmArgs w = ga();
+    w.A = b.Wrows; w.a_ld = ld; w.a_bs = kmax * ld; w.a_amax_c = 1.f;
+    w.B = b.RinvT; w.b_ld = ld; w.b_bs = ell * ld; w.b_amax = b.amax + b.am_ld;
+    w.ab_amax_bs = 1;
+    w.M = (int)kmax; w.N = (int)ell; w.K = (int)ell;
+    w.C = b.Wt; w.c_ld = ld; w.c_bs = kmax * ld; w.c_amax = amW; w.c_amax_bs = 1; w.m_fastest = 1;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, false, w, nb, 1, st);
+    fr = FactorRows{b.Wt, amW};
+  }
+  // U_T^T = rows^T basis^T (rows of length T); the basis is [T][ell_ld] in bufA2
+  GemmArgs g = ga();
+  g.A = fr.rows; g.a_ld = ld; g.a_bs = kmax * ld; g.a_amax = fr.amax; g.a_amax_c = 1.f;
+  g.B = b.bufA2; g.b_ld = ld; g.b_bs = (long long)pl.T * ld;
+  g.b_amax = b.basis_implicit ? b.basis_am : nullptr;  // an orthonormal Q has |entries| <= 1
+  g.b_amax_c = 1.f;
+  g.ab_amax_bs = 1;
+  g.M = m; g.N = pl.T; g.K = (int)ell;
+  g.C = UTt; g.c_ld = Tld; g.c_bs = kmax * Tld; g.m_fastest = 1;
+  gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
+  return fr;
+}
+
 void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const void *V, char *out,
                const std::vector<CellPick> &picks, hipStream_t st) {
   const int nb = pl.n_cells, nkv = nb / 2, D = pl.D, GH = pl.GH;
@@ -832,17 +914,11 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     fill_f32(b.Wrows, (long long)nb * kmax * ld, 0.f, st);
     sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, (int)ell, d_rT, (int)kmax, nb, b.Zw, kmax * ell, b.work,
                 (long long)invit_work_doubles((int)ell, (int)kmax), nullptr, b.Wrows, kmax * ld, (int)ld, st);
-    // U_T^T = W^T Q^T (rows of length T)
-    GemmArgs g = ga();
-    g.A = b.Wrows; g.a_ld = ld; g.a_bs = kmax * ld; g.a_amax_c = 1.f;
-    g.B = b.bufA2; g.b_ld = ld; g.b_bs = (long long)pl.T * ld;  // Q [T][ell_ld]
-    g.b_amax = nullptr; g.b_amax_c = 1.f;  // Q has orthonormal columns: |entries| <= 1
-    g.M = (int)kmax; g.N = pl.T; g.K = (int)ell;
-    g.C = UTt; g.c_ld = Tld; g.c_bs = kmax * Tld; g.m_fastest = 1;
-    gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
-    // token-projected tensor Y_p = W^T P1^T  (kmax x M)
+    const FactorRows fr = flash_factor_rows(pl, b, kmax, (int)kmax, UTt, st);
+    // token-projected tensor Y_p = W^T B = rows^T P2^T (kmax x M): P2 holds P = Q^T X, or P' = Y^T X
+    // when the basis is implicit (then rows = R^{-1} W)
     GemmArgs h = ga();
-    h.A = b.Wrows; h.a_ld = ld; h.a_bs = kmax * ld; h.a_amax_c = 1.f;
+    h.A = fr.rows; h.a_ld = ld; h.a_bs = kmax * ld; h.a_amax = fr.amax; h.a_amax_c = 1.f;
     h.B = b.P2; h.b_ld = ld; h.b_bs = Mf * ld; h.b_amax = b.amax + 5 * b.am_ld; h.ab_amax_bs = 1;
     h.M = (int)kmax; h.N = (int)Mf; h.K = (int)ell;
     h.C = Yp; h.c_ld = Mf; h.c_bs = kmax * Mf; h.c_amax = amYp; h.c_amax_bs = 1; h.m_fastest = 1;
@@ -1089,7 +1165,7 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
   }
   if (pl.mode == JOLT_FLASH) {
     gen_omega(b.omegaT, pl.dtype, pl.M, pl.ell, stream_key(pl.sketch_seed, 2), st);
-    fill_f32(b.amax, 8LL * b.am_ld, 0.f, st);
+    fill_f32(b.amax, 9LL * b.am_ld, 0.f, st);
   }
   Plan pv = pl;
   pv.n_cells = nc;
@@ -1115,6 +1191,10 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
       float *bufA0 = bv.bufA;
       stage_flash(pv, bv, Kv, Vv, sv, mark, side_work);
       swapped = bv.bufA != bufA0;
+      if (v == 0) {  // every view takes the same path; the amax slot pointers of view 0 span all cells
+        b.basis_implicit = bv.basis_implicit;
+        b.basis_am = bv.basis_am;
+      }
     } else {
       stage_exact(pv, bv, Kv, Vv, sv);
     }
@@ -1415,12 +1495,7 @@ int jolt_spectra(const void *d_K, const void *d_V, const jolt_cache_desc *desc, 
         fill_f32(b.Wrows, (long long)nb * kmax * ld, 0.f, st);
         sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, (int)ell, dk, (int)kmax, nb, b.Zw, kmax * ell, b.work,
                     (long long)invit_work_doubles((int)ell, (int)kmax), nullptr, b.Wrows, kmax * ld, (int)ld, st);
-        GemmArgs g = ga();
-        g.A = b.Wrows; g.a_ld = ld; g.a_bs = kmax * ld; g.a_amax_c = 1.f;
-        g.B = b.bufA2; g.b_ld = ld; g.b_bs = (long long)pl.T * ld; g.b_amax_c = 1.f;
-        g.M = n_vec; g.N = pl.T; g.K = (int)ell;
-        g.C = b.bufB; g.c_ld = Tld; g.c_bs = kmax * Tld; g.m_fastest = 1;
-        gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
+        flash_factor_rows(pl, b, kmax, n_vec, b.bufB, st);
       } else {
         sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, pl.T, b.specT, pl.nT, pl.T, dk, (int)kmax, nb, b.Zw, kmax * pl.T,
                     b.work, (long long)invit_work_doubles(pl.T, (int)kmax), nullptr, b.bufB, kmax * Tld, (int)Tld, st);
