@@ -303,7 +303,7 @@ Sizes sizes_for(const Plan &pl, int kmax, int kmax_d) {
   Sizes s;
   s.kmax = kmax;
   s.kmax_d = kmax_d;
-  s.Kb = (int)rup(pl.D + kmax, 8);
+  s.Kb = (int)rup(pl.D + kmax, 32);  // the encode's 32-deep stages read whole rows of B (zero padded)
   const int nv = n_views(pl);
   s.part_view = part_elems_for(pl, kmax, pl.n_cells / nv);
   s.part_elems = std::max(part_elems_for(pl, kmax, pl.n_cells), nv * s.part_view);
@@ -995,6 +995,7 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     g.C = b.Vt; g.c_ld = kmd; g.c_bs = D * kmd;
     gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
     amax_cells(b.Cr, GH * kmax * kmd, GH * kmax * kmd, nb, amCr, st);
+    fill_f32(b.Bcat, (long long)nb * GH * D * sz.Kb, 0.f, st);  // columns past D + r_T stay zero
     bcat_q(b.Bcat, nb, GH, D, sz.Kb, Qtf, st);
     GemmArgs h = ga();
     h.A = b.Vt; h.a_ld = kmd; h.a_bs = D * kmd; h.a_bs2 = 0; h.a_amax_c = 1.f;
@@ -1707,7 +1708,7 @@ int jolt_reconstruct(const void *d_blob, const jolt_cache_desc *desc, const jolt
 
 size_t jolt_encode_residual_workspace_bytes(int32_t G, int32_t H, int32_t T, int32_t D, int32_t rT, int32_t rd) {
   if (G <= 0 || H <= 0 || T <= 0 || (D != 64 && D != 128) || rT < 8 || rd < 8) return 0;
-  const long long GH = (long long)G * H, Kb = rup(D + rT, 8);
+  const long long GH = (long long)G * H, Kb = rup(D + rT, 32);
   long long bytes = 0;
   auto add = [&](long long n) { bytes += rup(std::max<long long>(n, 1), 256); };
   add(rd * D * 4LL); add(GH * rT * rd * 4LL); add(D * rd * 4LL); add(GH * D * Kb * 4LL); add(3 * GH * D * Kb * 2LL);
@@ -1731,7 +1732,7 @@ int jolt_encode_residual(const void *d_X, int32_t G, int32_t H, int32_t T, int32
     JOLT_REQUIRE(d_ws != nullptr && ws_bytes >= jolt_encode_residual_workspace_bytes(G, H, T, D, rT, rd),
                  JOLT_EWORKSPACE, "workspace too small");
     hipStream_t st = S(stream);
-    const int GH = G * H, Kb = (int)rup(D + rT, 8);
+    const int GH = G * H, Kb = (int)rup(D + rT, 32);
     Arena ar;
     ar.dry = false;
     ar.base = (char *)d_ws;
@@ -1768,6 +1769,7 @@ int jolt_encode_residual(const void *d_X, int32_t G, int32_t H, int32_t T, int32
     g.C = Vt; g.c_ld = rd;
     gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, 1, 1, st);
     amax_cells(Cr, (long long)GH * rT * rd, 0, 1, am + 1, st);
+    fill_f32(Bcat, (long long)GH * D * Kb, 0.f, st);  // columns past D + r_T stay zero
     bcat_q(Bcat, 1, GH, D, Kb, Qtf, st);
     GemmArgs h = ga();
     h.A = Vt; h.a_ld = rd; h.a_amax_c = 1.f;

@@ -11,6 +11,7 @@
 // codes are exact in 16 bits.
 #include "common.hpp"
 #include "gemm_core.hpp"
+#include "dma.hpp"
 #include "codec.hpp"
 
 namespace jolt {
@@ -338,6 +339,318 @@ encode_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
   for (int w = tid; w < nrows * wpr; w += ENT) out[w] = rowbits[w];
 }
 
+
+// ------------------------------------------------------------------------------- encode (DMA-fed)
+// 16-bit caches.  One block of 2 NWR waves takes 128 NWR token rows of one (cell, slice) and all D
+// output columns; wave (wr, wc) owns rows 128 wr .. 128 wr + 127 and columns (D / 2) wc .. (D / 2) wc +
+// D / 2 - 1 (the wave tile that needs the fewest fragment reads per MFMA with B in PB planes).
+// Operand tiles go global -> LDS by DMA with NS stages in flight: A = [X_j | U_T] rows (X_j for k < D,
+// U_T after; the buffer descriptors bound each source, so rows past T and the U_T columns past r_T in
+// the last 32-deep stage read zero), B = the PB 16-bit planes of [Q ; -D_j Q] (rows past D + r_T are
+// zero).  Each stage multiplies in the order of encode_kernel (B plane descending), so every
+// accumulator sees the same fp32 sequence and the codes are the same.  The block's LDS (at most 80 KB)
+// leaves room for a second block per CU, whose main loop covers this one's prologue and epilogue.
+// Row |max| is combined across the two column halves through LDS; codes are ORed into LDS row words
+// (row pitch padded by four words against bank conflicts) and copied out with 16-byte stores.
+// Block order: 8 slices x 8 token tiles of a cell run as one group on one XCD, so each U_T tile and
+// each slice's B planes are fetched from HBM once per group and reused from that XCD's L2.
+
+__device__ __forceinline__ long long uniform64(long long v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (long long)(((uint64_t)hi << 32) | lo);
+}
+
+template <int MF, int TN, int NS, int NWR>
+struct XCfg {
+  static constexpr int D = TN * 16, NW = 2 * NWR, NT = 64 * NW, ROWS = 128 * NWR;
+  static constexpr int PB = (MF == MF_F16) ? 2 : 3;     // planes of B
+  static constexpr int MAXO = (MF == MF_F16) ? 1 : 2;   // plane products kept: pb <= MAXO (A has one plane)
+  static constexpr int WR = 128, WC = D / 2, TI = WR / 16, TQ = WC / 16;
+  static constexpr int ASZ = ROWS * dma::DK, BSZ = PB * D * dma::DK, STG = ASZ + BSZ;  // halves per stage
+  // DMA slots per wave and stage: NA of A (16-row groups w, w + NW, ...) and NBS of B (B group w + NW i;
+  // a wave past the last B group repeats group w % NGB: the same bytes to the same place as the wave
+  // that owns it)
+  static constexpr int NGA = ROWS / 16, NGB = PB * D / 16, NA = NGA / NW, NBS = (NGB + NW - 1) / NW;
+  static constexpr int ND = NA + NBS;
+  static constexpr int RP = D * 8 / 32 + 4;  // LDS row pitch of the packed codes (words; b <= 8)
+  static_assert(NGA % NW == 0, "A groups split evenly over the waves");
+  static_assert(NS * STG * 2 <= 80 * 1024, "two blocks per CU");
+  static_assert((ROWS * RP + 3 * ROWS) * 4 <= NS * STG * 2, "epilogue fits in the stage buffers");
+  static_assert((NS - 2) * ND < 64, "vmcnt range");
+};
+
+// one stage of DMA requests of this wave into stage buffer dst: A from X_j (k < D) or U_T, then B
+template <int D, int NW, int NA, int NBS>
+__device__ __forceinline__ void enc_issue(dma::lds16 *__restrict__ dst, int k, dma::i32x4 rsx, dma::i32x4 rsu,
+                                          dma::i32x4 rsb, const uint32_t (&gx)[NA], const uint32_t (&gu)[NA],
+                                          const uint32_t (&gb)[NBS], int wave, const int (&bslot)[NBS]) {
+  using namespace dma;
+  if (k < D) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      raw_buffer_load_lds(rsx, (__attribute__((address_space(3))) uint32_t *)(dst + (i * NW + wave) * 16 * DK), 16,
+                          (int)gx[i], k * 2, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NA; ++i)
+      raw_buffer_load_lds(rsu, (__attribute__((address_space(3))) uint32_t *)(dst + (i * NW + wave) * 16 * DK), 16,
+                          (int)gu[i], (k - D) * 2, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NBS; ++i)
+    raw_buffer_load_lds(rsb, (__attribute__((address_space(3))) uint32_t *)(dst + bslot[i] * 16 * DK), 16, (int)gb[i],
+                        k * 2, 0, 0);
+}
+
+// (slice, tile) of block index `rem` of a cell with GH slices and tt tiles: groups of SG slices x TG
+// tiles, tile-major inside a group (consecutive blocks share the U_T tile)
+__device__ __forceinline__ void enc_order(int rem, int GH, int tt, int &j, int &tile) {
+  constexpr int SG = 8, TG = 8;
+  const int sg = rem / (SG * tt), ns = min(SG, GH - sg * SG);
+  const int rem2 = rem - sg * SG * tt;
+  const int tg = rem2 / (ns * TG);
+  const int rem3 = rem2 - tg * ns * TG;
+  j = sg * SG + rem3 % ns;
+  tile = tg * TG + rem3 / ns;
+}
+
+template <int MF, int TN, int NS, int NWR>
+__global__ void __launch_bounds__(128 * NWR) __attribute__((amdgpu_waves_per_eu(2, 2)))
+encode_dma_kernel(EncArgs ea, int T, int ttiles, int GHmax) {
+  using C = XCfg<MF, TN, NS, NWR>;
+  using namespace dma;
+  constexpr int D = C::D, PB = C::PB, TI = C::TI, TQ = C::TQ, ND = C::ND, NGA = C::NGA, NW = C::NW, NT = C::NT;
+  constexpr int ROWS = C::ROWS, RP = C::RP;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[NS * C::STG];
+  lds16 *const L0 = (lds16 *)lds_raw, *const Llast = L0 + (NS - 1) * C::STG;
+
+  // XCD-aware order: consecutive blocks of the remapped index run on one XCD; inside a cell, groups of
+  // slices x tiles (enc_order)
+  int tt, j, cz;
+  {
+    const long long gx = gridDim.x, total = gx * gridDim.z;
+    long long L = blockIdx.x + gx * blockIdx.z;
+    const long long per = total / 8;
+    if (L < per * 8) L = (L % 8) * per + L / 8;
+    cz = (int)(L / gx);
+    const int x = (int)(L % gx);
+    if (x >= GHmax * ttiles) return;
+    enc_order(x, GHmax, ttiles, j, tt);
+  }
+  // the cell record is read with vector loads (the compiler cannot prove it invariant); its fields are
+  // block-uniform, so they are moved to scalar registers: buffer descriptors built from vector
+  // registers would make every DMA request a serialising waterfall loop
+  EncCell c = ea.cells[cz];
+  c.x_off = uniform64(c.x_off);
+  c.ut_off = uniform64(c.ut_off);
+  c.sc_off = uniform64(c.sc_off);
+  c.cd_off = uniform64(c.cd_off);
+  c.bcat_off = uniform64(c.bcat_off);
+  c.kv = __builtin_amdgcn_readfirstlane(c.kv);
+  c.am_idx = __builtin_amdgcn_readfirstlane(c.am_idx);
+  c.GH = __builtin_amdgcn_readfirstlane(c.GH);
+  c.rT = __builtin_amdgcn_readfirstlane(c.rT);
+  c.bits = __builtin_amdgcn_readfirstlane(c.bits);
+  c.Kb = __builtin_amdgcn_readfirstlane(c.Kb);
+  if (j >= c.GH) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int fr = lane & 15, fc = lane >> 4;
+  const int t0 = tt * ROWS;
+  const int rT = c.rT, K = D + rT, Kb = c.Kb;
+  const int nsteps = (K + DK - 1) / DK;
+
+  // sources: X_j [T][D], U_T [T][rT] (cache dtype), B planes [plane][n][Kb] of slice j
+  const char *xj = (c.kv ? ea.xv : ea.xk) + c.x_off + (long long)j * T * D * 2;
+  const char *ut = ea.utb + c.ut_off;
+  const char *bj = ea.bcat + c.bcat_off + (long long)j * D * Kb * 2;
+  const i32x4 rsx = make_rsrc(xj, (uint32_t)((long long)T * D * 2));
+  const i32x4 rsu = make_rsrc(ut, (uint32_t)((long long)T * rT * 2));
+  const i32x4 rsb = make_rsrc(bj, 0xFFFFFFFFu);
+  const float bscale = (MF == MF_F16) ? f16_split_scale(ea.bamax[c.am_idx]) : 1.f;
+
+  // DMA slots of this wave: lane -> row lane / 4 of a 16-row group, logical chunk
+  // (lane % 4) ^ ((row / 2) % 4) (the tile's XOR permutation)
+  constexpr int NA = C::NA, NBS = C::NBS;
+  uint32_t gx_[NA], gu_[NA], gb_[NBS];
+  int bslot[NBS];
+  {
+    const int r = lane >> 2, p = lane & 3;
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int row = (i * NW + wave) * 16 + r, ch = (p ^ (row >> 1)) & 3;
+      const long long t = (long long)t0 + row;  // past T: out of the descriptor's range, reads zero
+      gx_[i] = (uint32_t)min((t * D + ch * 8) * 2, 0xFFFFFFF0LL);
+      gu_[i] = (uint32_t)min((t * rT + ch * 8) * 2, 0xFFFFFFF0LL);
+    }
+#pragma unroll
+    for (int i = 0; i < NBS; ++i) {
+      int Gb = i * NW + wave;
+      if (Gb >= C::NGB) Gb = wave % C::NGB;
+      bslot[i] = NGA + Gb;
+      const int plane = Gb / (D / 16), row = (Gb % (D / 16)) * 16 + r, ch = (p ^ (row >> 1)) & 3;
+      gb_[i] = (uint32_t)((plane * ea.b_ps + (long long)row * Kb + ch * 8) * 2);
+    }
+  }
+
+  const int aoff = dswz(wr * C::WR + fr, fc), boff = C::ASZ + dswz(wc * C::WC + fr, fc);
+  f32x4 acc[TI][TQ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int q = 0; q < TQ; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  {
+    lds16 *far = L0;
+#pragma unroll
+    for (int q = 0; q < NS - 1; ++q)
+      if (q < nsteps) {
+        enc_issue<D, NW, NA, NBS>(far, q * DK, rsx, rsu, rsb, gx_, gu_, gb_, wave, bslot);
+        far += C::STG;
+      }
+    lds16 *cur = L0;
+    for (int s = 0; s < nsteps; ++s) {
+      const int later = min(NS - 2, nsteps - 1 - s);
+      wait_stages<ND, NS - 2>(later);
+      wait_lgkm0();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (s + NS - 1 < nsteps)
+        enc_issue<D, NW, NA, NBS>(far, (s + NS - 1) * DK, rsx, rsu, rsb, gx_, gu_, gb_, wave, bslot);
+      u32x4 af[TI];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        af[i] = *(const lds_u32x4 *)(cur + aoff + i * 16 * DK);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int pb = PB - 1; pb >= 0; --pb) {
+        if (pb > C::MAXO) continue;
+        u32x4 bf[TQ];
+#pragma unroll
+        for (int q = 0; q < TQ; ++q) {
+          bf[q] = *(const lds_u32x4 *)(cur + boff + pb * D * DK + q * 16 * DK);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int q = 0; q < TQ; ++q) acc[i][q] = mfma16<MF>(bf[q], af[i], acc[i][q]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      cur = cur == Llast ? L0 : cur + C::STG;
+      far = far == Llast ? L0 : far + C::STG;
+    }
+  }
+  __syncthreads();  // every wave is done with the stage buffers: the epilogue reuses them
+
+  // ---- quantisation and packing (the rules of encode_kernel) -------------------------------------
+  // lane (fr, fc) of wave (wr, wc) holds, per 16-row group i and column group q, the columns
+  // D/2 wc + 16 q + 4 fc + r (r = 0..3) of token row 128 wr + 16 i + fr.  The accumulators carry the
+  // power-of-two split scale of B: e = acc / bscale exactly, so |max| and the code decisions are taken
+  // on acc with the scale folded into their factors (the same fp32 values as on e).
+  const int b = c.bits;
+  const int qm = (b >= 2) ? ((1 << (b - 1)) - 1) : 1;
+  uint32_t *rowbits = (uint32_t *)lds_raw;            // [ROWS][RP]
+  float *rmax = (float *)(rowbits + ROWS * RP);       // [2][ROWS]
+  float *srow = rmax + 2 * ROWS;                      // [ROWS]
+  const float inv = 1.f / bscale;  // a power of two
+  for (int w = tid; w < ROWS * RP; w += NT) rowbits[w] = 0u;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    float m = 0.f;
+#pragma unroll
+    for (int q = 0; q < TQ; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(acc[i][q][r]));
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (fc == 0) rmax[wc * ROWS + wr * C::WR + i * 16 + fr] = m * inv;
+  }
+  __syncthreads();
+  auto put = [&](int row, int q, uint32_t chunk) __attribute__((always_inline)) {
+    const int bit = (wc * C::WC + q * 16 + fc * 4) * b, wd = bit >> 5, sh = bit & 31;
+    atomicOr(&rowbits[row * RP + wd], chunk << sh);
+    if (sh + 4 * b > 32) atomicOr(&rowbits[row * RP + wd + 1], chunk >> (32 - sh));
+  };
+  if (b == 1) {  // sign code, scale = |max|
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = wr * C::WR + i * 16 + fr;
+      if (wc == 0 && fc == 0) srow[row] = fmaxf(rmax[row], rmax[ROWS + row]);
+#pragma unroll
+      for (int q = 0; q < TQ; ++q) {
+        uint32_t chunk = 0u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) chunk |= (acc[i][q][r] >= 0.f ? 1u : 0u) << r;
+        put(row, q, chunk);
+      }
+    }
+  } else {
+    const float qmf = (float)qm;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = wr * C::WR + i * 16 + fr;
+      const float m = fmaxf(rmax[row], rmax[ROWS + row]);
+      const float sc = m / qmf;  // IEEE quotient, as the scale is defined
+      if (wc == 0 && fc == 0) srow[row] = sc;
+      // code = rint(e / sc): formed from e * (1 / sc), which differs from the IEEE quotient by far less
+      // than 1e-4 for |e / sc| <= 127, so only values within 1e-4 of a rounding boundary can round
+      // differently; if any of the lane's values is that close, the lane takes the quotient for all of them
+      const float rs = sc > 0.f ? __builtin_amdgcn_rcpf(sc) * inv : 0.f;  // zero row: every code is q_max (0)
+      uint32_t chunk[TQ];
+      bool near = false;
+#pragma unroll
+      for (int q = 0; q < TQ; ++q) {
+        chunk[q] = 0u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float t = acc[i][q][r] * rs;
+          const float qv = rintf(t);
+          near |= fabsf(fabsf(t - qv) - 0.5f) < 1e-4f;
+          const float cq = __builtin_amdgcn_fmed3f(qv, -qmf, qmf) + qmf;
+          chunk[q] |= (uint32_t)cq << (r * b);
+        }
+      }
+      if (near) {
+#pragma unroll
+        for (int q = 0; q < TQ; ++q) {
+          chunk[q] = 0u;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float qv = rintf((acc[i][q][r] * inv) / sc);
+            chunk[q] |= (uint32_t)(__builtin_amdgcn_fmed3f(qv, -qmf, qmf) + qmf) << (r * b);
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < TQ; ++q) put(row, q, chunk[q]);
+    }
+  }
+  __syncthreads();
+  const int wpr = D * b / 32;
+  const long long row0 = (long long)j * T + t0;
+  const int nrows = min(ROWS, T - t0);
+  float *scales = (float *)(ea.scb + c.sc_off);
+  for (int rr = tid; rr < nrows; rr += NT) scales[row0 + rr] = srow[rr];
+  // codes: wpr words per row (D b / 8 bytes, a multiple of 8); 16-byte stores when aligned
+  char *outb = ea.cdb + c.cd_off + row0 * (D * b / 8);
+  if ((((uintptr_t)outb) & 15) == 0 && (wpr & 3) == 0) {
+    const int q4 = wpr / 4;
+    for (int w = tid; w < nrows * q4; w += NT) {
+      const int rr = w / q4, k4 = w - rr * q4;
+      *(uint4 *)(outb + ((long long)rr * wpr + 4 * k4) * 4) = *(const uint4 *)(rowbits + rr * RP + 4 * k4);
+    }
+  } else {
+    for (int w = tid; w < nrows * wpr; w += NT) {
+      const int rr = w / wpr, k = w - rr * wpr;
+      ((uint32_t *)outb)[(long long)rr * wpr + k] = rowbits[rr * RP + k];
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------ decode
 // unpack 8 codes (elements k0..k0+7 of row) to their signed values
 __device__ __forceinline__ void unpack8(const uint8_t *rowp, int k0, int b, float (&v)[8]) {
@@ -504,6 +817,14 @@ void launch_enc(const EncArgs &a, int ncells, int T, int GHmax, hipStream_t st) 
   const int tt = (T + EBM - 1) / EBM;
   hipLaunchKernelGGL((encode_kernel<MF, SX, TN>), dim3(tt * GHmax, 1, ncells), dim3(ENT), shm, st, a, T, tt, GHmax);
 }
+template <int MF, int TN, int NS>
+void launch_enc_dma(const EncArgs &a, int ncells, int T, int GHmax, hipStream_t st) {
+  using C = XCfg<MF, TN, NS, 2>;
+  const int tt = (T + C::ROWS - 1) / C::ROWS;
+  hipLaunchKernelGGL((encode_dma_kernel<MF, TN, NS, 2>), dim3(tt * GHmax, 1, ncells), dim3(C::NT), 0, st, a, T, tt,
+                     GHmax);
+}
+
 template <int MF, int SX, int NB16>
 void launch_dec(const DecCell *cells, int ncells, int T, int D, int GHmax, hipStream_t st) {
   int tt = (T + BM - 1) / BM;
@@ -515,13 +836,15 @@ void launch_dec(const DecCell *cells, int ncells, int T, int D, int GHmax, hipSt
 void encode_cells(int dtype, const EncArgs &a, int ncells, int T, int D, int GHmax, hipStream_t st) {
   JOLT_REQUIRE(D == 64 || D == 128, JOLT_EINVAL, "codec: d_head must be 64 or 128");
   if (ncells <= 0) return;
+  // 16-bit caches: the DMA-fed kernel (B rows padded with zeros to a multiple of 32); fp32 caches carry
+  // A in three planes split while loading and keep the register-staged kernel
   if (D == 128) {
-    if (dtype == JOLT_F16) launch_enc<MF_F16, SRC_F16, 8>(a, ncells, T, GHmax, st);
-    else if (dtype == JOLT_BF16) launch_enc<MF_BF16, SRC_BF16, 8>(a, ncells, T, GHmax, st);
+    if (dtype == JOLT_F16) launch_enc_dma<MF_F16, 8, 2>(a, ncells, T, GHmax, st);
+    else if (dtype == JOLT_BF16) launch_enc_dma<MF_BF16, 8, 2>(a, ncells, T, GHmax, st);
     else launch_enc<MF_BF16, SRC_F32, 8>(a, ncells, T, GHmax, st);
   } else {
-    if (dtype == JOLT_F16) launch_enc<MF_F16, SRC_F16, 4>(a, ncells, T, GHmax, st);
-    else if (dtype == JOLT_BF16) launch_enc<MF_BF16, SRC_BF16, 4>(a, ncells, T, GHmax, st);
+    if (dtype == JOLT_F16) launch_enc_dma<MF_F16, 4, 3>(a, ncells, T, GHmax, st);
+    else if (dtype == JOLT_BF16) launch_enc_dma<MF_BF16, 4, 2>(a, ncells, T, GHmax, st);
     else launch_enc<MF_BF16, SRC_F32, 4>(a, ncells, T, GHmax, st);
   }
   HIP_LAUNCH_CHECK();

@@ -6,7 +6,8 @@ namespace jolt {
 
 // One cell of the encode pass, as byte offsets from the bases in EncArgs (so that every address
 // the kernel forms derives from a kernel argument and compiles to global memory instructions).
-// Bcat[j][n][k] (fp32, row pitch Kb): k < D -> Q[k][n]; D <= k < D + rT -> -(D_j Q)[k - D][n].
+// Bcat[j][n][k] (fp32, row pitch Kb, a multiple of 32): k < D -> Q[k][n]; D <= k < D + rT ->
+// -(D_j Q)[k - D][n]; k >= D + rT -> 0.
 struct EncCell {
   long long x_off;     // cache slice [GH][T][D] (cache dtype) in xk (kv == 0) or xv (kv == 1)
   long long ut_off;    // U_T [T][rT] (cache dtype) in utb
