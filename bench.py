@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dtype", default="f16", choices=["f16", "bf16"])
+    ap.add_argument("--compare-modes", action="store_true",
+                    help="report FlashJoLT against exact JoLT on the Mistral-7B-shaped cache (T = 1024): "
+                         "compression time and relative reconstruction error of K and V at 2x and 3x")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -45,6 +48,9 @@ def parse():
                          "--calibrate-copy): write profiles/traffic.json for the dominant kernel and print a summary")
     return ap.parse_args()
 
+
+# HIP-event records per stage cover this many kernel launches (K and V cells in separate launches)
+LAUNCHES_PER_RECORD = {"sketch_gemm": 2, "transpose_x": 2}
 
 # the dominant kernel of the workload: the projection P^T = Q^T X (fp32 Q in two fp16 planes
 # times the fp16 cache), one launch over the 16 cells
@@ -147,34 +153,75 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
-def kernel_models(T, L, H, D, G, ell, picks, dtype_bytes):
-    """Algorithmic flops / bytes per launch of the measured stages (see the design notes)."""
-    GH, M = G * H, G * H * D
-    cells_per_launch = (L // G)            # K cells or V cells of one launch
-    n_cells = 2 * cells_per_launch
+FP64_PEAK_TFLOPS = 78.6
+
+
+def stage_models(T, L, H, D, G, ell, picks, c):
+    """Algorithmic flops and HBM bytes of every stage of one compress call over the whole cache
+    (each operand read once, each output written once; split-precision planes and padding not
+    counted), with the peak of the units the stage runs on: 'mfma' (fp16/bf16 matrix cores: the
+    products of the sketch, projection, Gram and fit), 'fp64' (fp64 Gram, eigensolvers, Cholesky)."""
+    GH, M, R = G * H, G * H * D, G * H * T
+    n = 2 * (L // G)                        # cells
+    kmax = max(p["rT"] for p in picks)      # the fit products run every cell at the largest pick
+    kd = max(p["rd"] for p in picks)
+    f4 = 4.0
     m = {}
-    # Y^T = Omega^T X^T and Y^T = Z^T X^T: 2 T M ell flops per cell, X read once
-    m["sketch_gemm"] = {"flops": 2.0 * T * M * ell * cells_per_launch, "launches_per_record": 2,
-                        "bytes": (T * M * dtype_bytes + 4.0 * ell * T) * cells_per_launch}
-    # P^T = Q^T X: same contraction; reads X and fp32 Q once, writes P in both layouts
-    m["project_gemm"] = {"flops": 2.0 * T * M * ell * n_cells, "launches_per_record": 1,
-                         "bytes": (T * M * dtype_bytes + 4.0 * ell * T + 2 * 4.0 * ell * M) * n_cells}
-    # fused residual encode: one launch over the cells with b > 0
-    flops = 0.0
-    byts = 0.0
-    for p in picks:
-        if p["bits"] == 0:
-            continue
-        R = GH * T
-        flops += 2.0 * R * (D + p["rT"]) * D
-        byts += R * D * dtype_bytes + T * p["rT"] * dtype_bytes + R * D * p["bits"] / 8.0 + 4.0 * R
-    m["residual_encode"] = {"flops": flops, "bytes": byts, "launches_per_record": 1}
-    # feature Gram: 2 R D^2 per cell, X read once
-    m["feature_gram"] = {"flops": 2.0 * GH * T * D * D * n_cells, "launches_per_record": 1,
-                         "bytes": GH * T * D * dtype_bytes * n_cells}
-    # per-(l,h) transpose of the cache: read + write once
-    m["transpose_x"] = {"flops": 0.0, "launches_per_record": 2, "bytes": 2.0 * GH * T * D * dtype_bytes * cells_per_launch}
+
+    def add(name, flops, byts, unit):
+        m[name] = {"flops": float(flops), "bytes": float(byts), "unit": unit}
+
+    add("transpose_x", 0.0, 2.0 * T * M * c * n, "mfma")
+    add("feature_gram", 2.0 * R * D * D * n, T * M * c * n, "mfma")
+    # two sketches: Y = X Omega, Y = X Z (fp32 Y written in two layouts)
+    add("sketch_gemm", 2 * 2.0 * T * M * ell * n, 2 * (T * M * c + 2 * f4 * T * ell + f4 * M * ell) * n, "mfma")
+    # 16-bit planes of Q_0^T, Z^T and Y^T (fp32 read, two fp16 planes written)
+    add("split_planes", 0.0, (2 * T * ell + M * ell) * 8.0 * n, "mfma")
+    # two projections (P^T = Q_0^T X, P'^T = Y^T X; K split 4-fold, partials written)
+    add("project_gemm", 2 * 2.0 * T * M * ell * n, 2 * (T * M * c + f4 * T * ell + 4 * f4 * ell * M) * n, "mfma")
+    add("project_reduce", 0.0, 2 * (4 * f4 * ell * M + 2 * f4 * ell * M) * n, "mfma")
+    # two tall Grams (T ell^2 each, symmetric), one apply Q_0^T = R^-T Y^T (T ell^2, triangular),
+    # two Cholesky factorisations and triangular inverses (2 ell^3 / 3 each)
+    add("cholqr_tall", (3.0 * T * ell * ell + 4.0 * ell ** 3 / 3) * n, (3 * f4 * T * ell + f4 * T * ell) * n, "mfma")
+    add("cholqr_z", (2.0 * M * ell * ell + 2.0 * ell ** 3 / 3) * n, 3 * f4 * M * ell * n, "mfma")
+    add("basis_apply", 1.0 * M * ell * ell * n, 2 * f4 * M * ell * n, "mfma")
+    add("gram64", 1.0 * ell * ell * M * n, f4 * ell * M * n, "fp64")
+    add("eigvals_B", (4.0 * ell ** 3 / 3) * n, 8.0 * ell * ell * n, "fp64")
+    add("allocate", 0.0, 0.0, "fp64")
+    # fit: eigenvectors, W~ = W R^-T, U_T^T = W~^T Y^T, Y_p = W~^T P'^T
+    add("fit_token_factor", (2.0 * kmax * ell * ell + 2.0 * T * ell * kmax + 2.0 * kmax * ell * M) * n,
+        (f4 * T * ell + f4 * kmax * T + f4 * ell * M + 2 * f4 * kmax * M) * n, "mfma")
+    add("fit_feature_factor", 2.0 * kmax * GH * D * D * n, 2 * f4 * kmax * M * n, "mfma")
+    add("fit_core", 2.0 * kmax * GH * D * kd * n, (f4 * kmax * M + f4 * GH * kmax * kd) * n, "mfma")
+    add("put_factors", 0.0, sum((T * p["rT"] + D * p["rd"] + GH * p["rT"] * p["rd"]) * (f4 + c) for p in picks), "mfma")
+    add("residual_operand", sum(2.0 * GH * D * p["rT"] * p["rd"] for p in picks), sum(8.0 * GH * D * (D + p["rT"]) for p in picks),
+        "mfma")
+    enc_f = sum(2.0 * R * (D + p["rT"]) * D for p in picks if p["bits"] > 0)
+    enc_b = sum(R * D * c + T * p["rT"] * c + R * D * p["bits"] / 8.0 + f4 * R for p in picks if p["bits"] > 0)
+    add("residual_encode", enc_f, enc_b, "mfma")
     return m
+
+
+def stage_table(stages, models, dtype):
+    """Per stage: time, algorithmic work, achieved rates and both roofline fractions; the binding
+    roof is the one the stage's arithmetic intensity points to."""
+    out = {}
+    for name, (ms, cnt) in stages.items():
+        mdl = models.get(name)
+        if mdl is None:
+            out[name] = {"ms": round(ms, 3), "records": cnt}
+            continue
+        s = ms / 1e3
+        peak = MFMA_PEAK_TFLOPS[dtype] if mdl["unit"] == "mfma" else FP64_PEAK_TFLOPS
+        tf = mdl["flops"] / s / 1e12 if s > 0 else 0.0
+        gb = mdl["bytes"] / s / 1e9 if s > 0 else 0.0
+        ridge = peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+        ai = mdl["flops"] / mdl["bytes"] if mdl["bytes"] > 0 else float("inf")
+        out[name] = {"ms": round(ms, 3), "gflop": round(mdl["flops"] / 1e9, 2), "gbyte": round(mdl["bytes"] / 1e9, 3),
+                     "tflops": round(tf, 2), "gbs": round(gb, 1), "flop_frac": round(tf / peak, 4),
+                     "hbm_frac": round(gb / HBM_PEAK_GBS, 4), "peak_unit": mdl["unit"],
+                     "bound": ("mfma" if mdl["unit"] == "mfma" else "fp64") if ai >= ridge else "hbm"}
+    return out
 
 
 def source_hash(paths):
@@ -199,6 +246,28 @@ def traffic_for(stage):
         return ent["bytes_per_launch"]
     except Exception:
         return None
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_info():
+    try:
+        from threadpoolctl import threadpool_info
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return f"{i.get('internal_api')} {i.get('version')} ({i.get('num_threads')} threads)"
+    except Exception:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def cpu_baseline(K, V, groups, cfgd, sample_T):
@@ -226,14 +295,69 @@ def cpu_baseline(K, V, groups, cfgd, sample_T):
     dt = time.time() - t0
     n_groups = len(groups) - 1
     value = sample_T / (dt * n_groups)
-    return {"value": value, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    host = {"nproc": os.cpu_count(), "cpu_model": _cpu_model(), "blas": _blas_info()}
+    return {"value": value, "unit": "tokens/s", "cores": int(threads), "kind": "oracle", "host": host,
             "sample": f"oracle compress of layer group 0 (K and V cells) on the first {sample_T} tokens "
                       f"({dt:.1f} s); scaled as {sample_T} tokens / ({dt:.1f} s x {n_groups} groups); "
                       f"status {r['status']}"}
 
 
+def compare_modes():
+    """FlashJoLT against exact JoLT on one cache (the pages compare them at 1024-token context): per
+    budget and mode, the time of one jolt_compress (median of 5 after a warm-up, HIP events) and the
+    relative Frobenius error of the whole K and V caches after jolt_reconstruct."""
+    import torch
+    import synth
+    from kv_cache_compression_layer_amd import jolt
+    torch.cuda.set_device(0)
+    L, H, T, D, G = 32, 8, 1024, 128, 4
+    groups = list(range(0, L + 1, G))
+    K, V = synth.power_law(n_seq=1, L=L, H=H, T=T, D=D, group=G, alpha_k=1.0, alpha_v=1.0, noise_var=0.02,
+                           n_outliers=4, dtype="f16", seed=0, device="cuda")
+    e = jolt.eps2(D)
+    eps2 = {b: float(e[b]) for b in range(9)}
+    rows = {}
+    for C in (2.0, 3.0):
+        for mode, name in ((jolt.EXACT, "exact"), (jolt.FLASH, "flash")):
+            q = 32 if C <= 4 else 64
+            rT = list(range(8, (T if mode == jolt.EXACT else q) + 1, 8))
+            cfg = jolt.Config(1, L, H, T, D, jolt.F16, groups, mode, rT, list(range(8, D + 1, 8)), [2, 4, 8], C,
+                              eps2=eps2)
+            ws = torch.empty(cfg.workspace_bytes(), dtype=torch.uint8, device="cuda")
+            out = torch.empty(cfg.output_bytes(), dtype=torch.uint8, device="cuda")
+            jolt.compress(K, V, cfg, out=out, ws=ws)
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                blob, picks, lam = jolt.compress(K, V, cfg, out=out, ws=ws)
+                e1.record()
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            Ko, Vo = torch.empty_like(K), torch.empty_like(V)
+            jolt.reconstruct(blob, cfg, picks, Ko, Vo, ws=ws)
+            torch.cuda.synchronize()
+            err = [float(torch.linalg.vector_norm((O.float() - X.float())) / torch.linalg.vector_norm(X.float()))
+                   for O, X in ((Ko, K), (Vo, V))]
+            rows[f"{name}_{C:g}x"] = {"ms": round(sorted(times)[2], 3), "err_K": round(err[0], 5),
+                                      "err_V": round(err[1], 5),
+                                      "token_ranks_K": [p["rT"] for p in picks[0::2]],
+                                      "token_ranks_V": [p["rT"] for p in picks[1::2]]}
+            del ws, out, Ko, Vo
+    for C in ("2x", "3x"):
+        ex, fl = rows[f"exact_{C}"], rows[f"flash_{C}"]
+        rows[f"gap_{C}"] = {"dK": round(fl["err_K"] - ex["err_K"], 5), "dV": round(fl["err_V"] - ex["err_V"], 5),
+                            "time_ratio_exact_over_flash": round(ex["ms"] / fl["ms"], 3)}
+    print(json.dumps({"workload": "Mistral-7B-shaped KV cache, 32 layers (groups of 4) x 8 KV heads x T=1024 x "
+                                  "d_head 128, f16, synthetic (power law, exponent 1)", "modes": rows}), flush=True)
+
+
 def main():
     a = parse()
+    if a.compare_modes:
+        compare_modes()
+        return
     if a.calibrate_copy:
         calibrate_copy()
         return
@@ -291,36 +415,40 @@ def main():
     stages = jolt.profile_read()
     jolt.profile(False)
     ell = min(512 + 10, T)
-    models = kernel_models(T, L, H, D, G, ell, picks, 2)
-    # The profiled call is one compress call; rates use the stage's algorithmic work over its summed
-    # launch time, the per-launch duration is that sum over the number of launches.
-    best = None
-    for name, (ms, cnt) in stages.items():
-        if name in models and cnt > 0:
-            if best is None or ms > best[1]:
-                best = (name, ms, cnt)
-    roof = None
-    if best:
-        name, ms, cnt = best
-        mdl = models[name]
-        # the stage was recorded cnt times, each record covering launches_per_record launches of
-        # the modelled work over the whole cell batch
-        nl = cnt * mdl["launches_per_record"]
-        flop_rate = mdl["flops"] * nl / (ms / 1e3) / 1e12
-        byte_rate = mdl["bytes"] * nl / (ms / 1e3) / 1e9
-        pl_ms = ms / nl
-        ai = mdl["flops"] / max(mdl["bytes"], 1.0)
-        ridge = MFMA_PEAK_TFLOPS[a.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
-        if ai >= ridge:
-            roof = {"bound": "mfma", "achieved": round(flop_rate, 2), "peak": MFMA_PEAK_TFLOPS[a.dtype],
-                    "unit": "TFLOP/s", "frac": round(flop_rate / MFMA_PEAK_TFLOPS[a.dtype], 4)}
-        else:
-            roof = {"bound": "hbm", "achieved": round(byte_rate, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(byte_rate / HBM_PEAK_GBS, 4)}
-        roof["traffic"] = traffic_for(name)
-        roof["kernel"] = name
-        roof["launch_ms"] = round(pl_ms, 4)
-        roof["launches"] = nl
+    models = stage_models(T, L, H, D, G, ell, picks, 2)
+    table = stage_table(stages, models, a.dtype)
+    # The dominant kernel: the stage with the largest time.  Its rate is its algorithmic work over its
+    # summed launch time (HIP events on the library's stream); per-launch time = that sum / launches.
+    name = max((k for k in table if "gflop" in table[k]), key=lambda k: table[k]["ms"])
+    ent, mdl = table[name], models[name]
+    launches = stages[name][1] * LAUNCHES_PER_RECORD.get(name, 1)
+    if ent["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": ent["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ent["hbm_frac"]}
+    else:
+        pk = MFMA_PEAK_TFLOPS[a.dtype] if mdl["unit"] == "mfma" else FP64_PEAK_TFLOPS
+        roof = {"bound": "mfma", "achieved": ent["tflops"], "peak": pk, "unit": "TFLOP/s", "frac": ent["flop_frac"]}
+    roof["traffic"] = traffic_for(name)
+    roof["kernel"] = name
+    roof["launch_ms"] = round(stages[name][0] / launches, 4)
+    roof["launches"] = launches
+
+    # dense reconstruction of the whole cache from the blob (jolt_reconstruct, asynchronous on torch's
+    # stream): the blob is read once and the cache written once
+    Ko, Vo = torch.empty_like(K), torch.empty_like(V)
+    jolt.reconstruct(blob, cfg, picks, Ko, Vo, ws=ws)
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    r0.record(st)
+    for _ in range(3):
+        jolt.reconstruct(blob, cfg, picks, Ko, Vo, ws=ws)
+    r1.record(st)
+    torch.cuda.synchronize()
+    rec_ms = r0.elapsed_time(r1) / 3
+    rec_bytes = float(sum(p["bytes"] for p in picks)) + 2.0 * L * H * T * D * 2
+    reconstruct = {"ms": round(rec_ms, 3), "gbyte": round(rec_bytes / 1e9, 3),
+                   "gbs": round(rec_bytes / (rec_ms / 1e3) / 1e9, 1),
+                   "hbm_frac": round(rec_bytes / (rec_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del Ko, Vo
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(K, V, groups, {"eps2": [float(x) for x in eps2], "rT": rT, "rd": rd, "bits": bits,
@@ -348,7 +476,8 @@ def main():
                    "picks": [[p["rT"], p["rd"], p["bits"]] for p in picks]},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "stages_ms": {k: round(v[0], 3) for k, v in stages.items()},
+        "stages": table,
+        "reconstruct": reconstruct,
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(gen_s, 2),
     }

@@ -166,3 +166,69 @@ def test_flash_token_spectrum_multiworkgroup_eigensolver(T, C, H, D):
     _, spec = oracle.token_factors_flash(Xt, Om, q, 1, N2)
     assert np.all(np.abs(sT1[0][:-1] - spec[:-1]) <= 1e-5 * spec[:-1] + 1e-7 * N2)
     assert abs(sT1[0][-1] - spec[-1]) <= 1e-5 * N2
+
+
+def test_mistral7b_shape_exact_full_size():
+    """Exact JoLT at the Mistral-7B shape (16 cells of 4 x 8 x 1024 x 128 fp16, token Gram 1024 x 1024,
+    token rank grid 8..1024): the oracle's exact spectra (SVD of every cell's token unfolding) against
+    the GPU's (relative 1e-4 above 1e-7 ||X||^2), the GPU's picks as the exact argmin of the tables at
+    its lambda, and on two sampled cells the token projector at the picked rank (gap reported) and
+    the oracle's fit, encode and decode on the GPU's factor and picks against the GPU reconstruction."""
+    from test_gpu_parity_ranks import xhat_tolerance
+    L, H, T, D, C = 32, 8, 1024, 128, 2.0
+    K, V = synth.power_law(L=L, H=H, T=T, D=D, dtype="f16", seed=0)
+    groups = list(range(0, L + 1, 4))
+    rT, rd, bits = list(range(8, T + 1, 8)), list(range(8, 129, 8)), [2, 4, 8]
+    e = jolt.eps2(D)
+    eps2 = {b: float(e[b]) for b in range(9)}
+    cfg = jolt.Config(1, L, H, T, D, jolt.F16, groups, jolt.EXACT, rT, rd, bits, C, eps2=eps2)
+    Kd, Vd = K.cuda(), V.cuda()
+    blob, picks, lam, Ko, Vo = _run(Kd, Vd, cfg, groups)
+    n_vec = max(p["rT"] for p in picks[:2])
+    sT, sD, n2, UT = jolt.spectra(Kd, Vd, cfg, n_vec=n_vec)
+    torch.cuda.synchronize()
+    sT, sD, n2, UT = sT.cpu().numpy(), sD.cpu().numpy(), n2.cpu().numpy(), UT[:2].double().cpu().numpy()
+    shape = oracle.CellShape(4, H, T, D)
+    cells = []
+    for c, (s, g, t, Xs) in enumerate(oracle.cells_of_cache(K.numpy(), V.numpy(), groups)):
+        X = oracle.to_f64(Xs, "f16")
+        N2 = float(np.sum(X * X))
+        Xt = oracle.token_unfolding(X)
+        if c < 2:
+            U, spec = oracle.token_factors_exact(Xt)
+        else:
+            U, spec = None, np.linalg.svd(Xt, compute_uv=False) ** 2
+        # the exact route eigendecomposes the token Gram accumulated in fp32, so an eigenvalue's error is
+        # relative plus a floor proportional to ||X||^2 (the Gram's largest entries); the bar of the
+        # small-case spectra test
+        d = np.abs(sT[c] - spec)
+        if c < 2:
+            big = spec > 1e-5 * N2
+            print(f"cell {c}: token spectrum max |d| {d.max() / N2:.2e} ||X||^2, max rel above 1e-5 ||X||^2 "
+                  f"{(d[big] / spec[big]).max():.2e}")
+        assert np.all(d <= 1e-4 * spec + 1e-7 * N2), (c, float(np.max(d - 1e-4 * spec) / N2))
+        assert abs(n2[c] - N2) <= 1e-6 * N2
+        cells.append({"X": X if c < 2 else None, "U": U, "specT": spec, "specD": oracle.feature_spectrum(X),
+                      "norm2": N2})
+    ties = lambda_consistency(picks, lam, (sT, sD, n2), cells, shape, 2, rT, rd, bits, eps2)
+    print("near-tie cells:", ties, "picks:", [(p["rT"], p["rd"], p["bits"]) for p in picks])
+    Qrot = oracle.rotation(D, 0)
+    for c in range(2):
+        x, p = cells[c], picks[c]
+        r = p["rT"]
+        gap = (x["specT"][r - 1] - x["specT"][r]) / x["specT"][0]
+        Ug = UT[c][:r].T
+        sin = np.linalg.norm(Ug @ (Ug.T @ x["U"][:, :r]) - x["U"][:, :r], 2)
+        UTf, Udf, core, _ = oracle.fit_cell(x["X"], Ug, p["rd"])
+        enc = oracle.encode_cell(x["X"], UTf, Udf, core, p["bits"], Qrot, "f16")
+        Xh = oracle.decode_cell(enc["UT"], enc["Ud"], enc["core"], p["bits"], enc.get("u"), enc.get("scales"), Qrot,
+                                x["X"].shape)
+        got = (Ko if c % 2 == 0 else Vo)[0, groups[c // 2]:groups[c // 2 + 1]].double().cpu().numpy()
+        want = oracle.round_to_dtype(Xh, "f16")
+        relx = np.linalg.norm(got - want) / np.linalg.norm(want)
+        tol = xhat_tolerance(enc.get("scales"), D, np.linalg.norm(want), p["bits"]) + 3e-4
+        print(f"cell {c}: pick {r, p['rd'], p['bits']}, projector sine {sin:.2e} at gap {gap:.2e}, "
+              f"|Xhat - Xhat_oracle| / |Xhat_oracle| {relx:.2e} (bar {tol:.2e})")
+        if gap >= 1e-3:
+            assert sin <= 1e-3
+        assert relx <= tol
