@@ -37,7 +37,7 @@ __all__ = [
     "DTYPE_BYTES", "to_f64", "round_to_dtype", "qmax", "quantize_rows", "dequantize_rows",
     "pack_rows", "unpack_rows", "rotation", "sketch_matrix", "eps2_calibrate", "qcap_eq5",
     "cell_bytes", "token_unfolding", "feature_spectrum", "token_factors_exact",
-    "token_factors_flash", "suffix_sums", "cell_table", "argmin_cell", "allocate",
+    "token_factors_flash", "layer_token_basis", "alignment_scores", "group_layers", "suffix_sums", "cell_table", "argmin_cell", "allocate",
     "fit_cell", "rotated_residual", "encode_cell", "decode_cell", "cells_of_cache", "section_layout",
     "write_blob", "read_blob_cell", "compress", "reconstruct", "CellShape",
 ]
@@ -397,6 +397,48 @@ def decode_cell(UT, Ud, core, b, u, scales, Qrot, shape):
         Erot = dequantize_rows(u, scales, b).astype(np.float64)
         Xt = Xt + (Erot @ Qrot.T).reshape(shape)
     return Xt
+
+
+# ----------------------------------------------------------------------------
+# layer grouping by token-subspace alignment (Sec. 3, "Method", and its footnote on size bounds)
+# ----------------------------------------------------------------------------
+def layer_token_basis(Xl, k=8):
+    """Top-k token-mode left singular vectors of one layer's key cache (n_h x T x d_h): the columns of
+    U of the SVD of the T x (n_h d_h) unfolding, as a T x k array with orthonormal columns."""
+    H, T, D = Xl.shape
+    A = Xl.transpose(1, 0, 2).reshape(T, H * D)
+    U, _, _ = np.linalg.svd(A, full_matrices=False)
+    return U[:, :k]
+
+
+def alignment_scores(K, k=8):
+    """Score of each pair of consecutive layers (l, l+1) of a key cache (L x n_h x T x d_h): the mean
+    squared cosine between their token bases, read as the mean of the squared cosines of the k
+    principal angles between the two k-dimensional subspaces, ||U_l^T U_{l+1}||_F^2 / k (independent
+    of the choice of basis inside each subspace).  Returns L-1 scores."""
+    K = np.asarray(K, dtype=np.float64)
+    U = [layer_token_basis(K[l], k) for l in range(K.shape[0])]
+    return np.array([float(np.sum((U[l].T @ U[l + 1]) ** 2)) / k for l in range(len(U) - 1)])
+
+
+def group_layers(scores, min_size=2, max_size=8):
+    """Contiguous layer groups from the L-1 consecutive-layer scores: a new group starts where the
+    score falls below the median of all scores, but only once the current group holds min_size
+    layers; a group is closed at max_size layers whatever the score; a trailing group of one layer
+    joins its predecessor.  Returns the start offsets (n_groups + 1 entries, last = L)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    L = len(scores) + 1
+    med = float(np.median(scores)) if len(scores) else 0.0
+    sizes = [1]
+    for l in range(1, L):
+        if sizes[-1] >= max_size or (scores[l - 1] < med and sizes[-1] >= min_size):
+            sizes.append(1)
+        else:
+            sizes[-1] += 1
+    if len(sizes) > 1 and sizes[-1] == 1:
+        last = sizes.pop()
+        sizes[-1] += last
+    return [int(v) for v in np.concatenate([[0], np.cumsum(sizes)])]
 
 
 # ----------------------------------------------------------------------------
