@@ -198,6 +198,24 @@ int jolt_encode_residual(const void *d_X, int32_t G, int32_t H, int32_t T, int32
 /* Workspace (device bytes) needed by jolt_encode_residual; 0 on invalid arguments. */
 size_t jolt_encode_residual_workspace_bytes(int32_t G, int32_t H, int32_t T, int32_t D, int32_t rT, int32_t rd);
 
+/* Layer grouping by token-subspace alignment (Sec. 3 "Method", with its footnote on group sizes).
+ * For every layer, the top 8 token-mode singular vectors of its key cache (the T x n_h d_h unfolding;
+ * randomized subspace iteration with 24 extra vectors and 3 power iterations, Gaussian test matrix
+ * drawn from sketch_seed); each pair of consecutive layers is scored by the mean squared cosine of
+ * the principal angles between their bases, ||U_l^T U_{l+1}||_F^2 / 8 (averaged over the n_seq
+ * sequences); a new group starts where a score falls below the median of all scores, once the current
+ * group holds two layers; a group closes at eight layers; a trailing single layer joins its predecessor.
+ *   d_K             device key cache [n_seq][n_layers][n_heads][n_tokens][d_head] (desc->n_groups and
+ *                   desc->group_start are ignored).
+ *   h_group_start   host int32[n_layers + 1]: the group start offsets (first 0, last n_layers).
+ *   h_n_groups      host int32: number of groups.
+ *   h_scores        host double[n_layers - 1], or NULL: the scores.
+ * Workspace: jolt_layer_groups_workspace_bytes(desc).  Synchronises the stream once.  The result can
+ * be passed to jolt_compress as desc->group_start (groups of unequal size). */
+size_t jolt_layer_groups_workspace_bytes(const jolt_cache_desc *desc);
+int jolt_layer_groups(const void *d_K, const jolt_cache_desc *desc, uint64_t sketch_seed, int32_t *h_group_start,
+                      int32_t *h_n_groups, double *h_scores, void *d_ws, size_t ws_bytes, void *stream);
+
 /* FlashJoLT Gaussian test matrix (Sec. 3.1, randomized range finder), as jolt_compress draws it:
  * element (m, c) of Omega (M x ell) is Gaussian number m*ell + c of the sketch stream of
  * sketch_seed (SplitMix64 + Box-Muller), rounded once to dtype.  Written transposed, as

@@ -155,7 +155,7 @@ Plan make_plan(const jolt_cache_desc *d, const jolt_params *p) {
   for (int g = 0; g < pl.n_groups; ++g) {
     JOLT_REQUIRE(d->group_start[g + 1] > d->group_start[g], JOLT_EINVAL, "group_start must be increasing");
     JOLT_REQUIRE(d->group_start[g + 1] - d->group_start[g] == pl.G, JOLT_EINVAL,
-                 "layer groups must all have the same size");
+                 "this entry point needs layer groups of one size (jolt_compress and jolt_reconstruct take any)");
   }
   pl.GH = pl.G * pl.H;
   pl.M = pl.GH * pl.D;
@@ -724,6 +724,68 @@ void stage_exact(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   reduce_splits(b.part, (long long)ns * T * Tld, T * Tld, ns, 0, (int)T, (int)T, Tld, b.G64, true, T * T, (int)T, nb,
                 st);
   sym_eigvals(b.G64, T * T, (int)T, (int)T, nb, b.dT, b.eT, b.G64, b.betaT, T, b.specT, pl.nT, true, st);
+}
+
+// ----------------------------------------------------------------------------- layer grouping
+// Per layer, the top kGroupVecs token-mode singular vectors of the key cache, by the FlashJoLT
+// pipeline with one layer per cell (oversampling and power iterations enough to converge the leading
+// subspace well below the scores' resolution); value cells ride along (the pipeline pairs K and V)
+// and are not used.
+constexpr int kGroupVecs = 8, kGroupOversample = 24, kGroupPowerIters = 3;
+
+struct LayerSetup {
+  std::vector<int32_t> starts;
+  int32_t grid[1] = {kGroupVecs};
+  double eps2[9] = {1, 1, 1, 1, 1, 1, 1, 1, 1};
+  jolt_cache_desc d1;
+  jolt_params p1;
+};
+
+void layer_setup(const jolt_cache_desc *desc, uint64_t seed, LayerSetup &ls) {
+  JOLT_REQUIRE(desc != nullptr && desc->n_layers >= 1, JOLT_EINVAL, "layer grouping: bad cache descriptor");
+  ls.d1 = *desc;
+  ls.starts.resize(desc->n_layers + 1);
+  for (int l = 0; l <= desc->n_layers; ++l) ls.starts[l] = l;
+  ls.d1.n_groups = desc->n_layers;
+  ls.d1.group_start = ls.starts.data();
+  memset(&ls.p1, 0, sizeof(ls.p1));
+  ls.p1.mode = JOLT_FLASH;
+  ls.p1.oversample = kGroupOversample;
+  ls.p1.power_iters = kGroupPowerIters;
+  ls.p1.qcap = kGroupVecs;
+  ls.p1.rT_grid = ls.grid; ls.p1.n_rT = 1;
+  ls.p1.rd_grid = ls.grid; ls.p1.n_rd = 1;
+  ls.p1.bits = nullptr; ls.p1.n_bits = 0;
+  ls.p1.eps2 = ls.eps2;
+  ls.p1.target_ratio = 2.0;
+  ls.p1.sketch_seed = seed;
+}
+
+// numpy's median: the middle value, or the mean of the two middle values of an even count
+double median_of(std::vector<double> v) {
+  if (v.empty()) return 0.0;
+  std::sort(v.begin(), v.end());
+  const size_t n = v.size();
+  return (n % 2) ? v[n / 2] : 0.5 * (v[n / 2 - 1] + v[n / 2]);
+}
+
+// Sec. 3 "Method": a new group where the score of consecutive layers falls below the median of all
+// scores; size bounds first: a group opens only once the current one has two layers, closes at
+// eight, and a trailing single layer joins its predecessor
+std::vector<int32_t> groups_from_scores(const std::vector<double> &sc, int L) {
+  const double med = median_of(sc);
+  std::vector<int> sizes{1};
+  for (int l = 1; l < L; ++l) {
+    if (sizes.back() >= 8 || (sc[l - 1] < med && sizes.back() >= 2)) sizes.push_back(1);
+    else ++sizes.back();
+  }
+  if (sizes.size() > 1 && sizes.back() == 1) {
+    sizes.pop_back();
+    ++sizes.back();
+  }
+  std::vector<int32_t> starts{0};
+  for (int v : sizes) starts.push_back(starts.back() + v);
+  return starts;
 }
 
 // ----------------------------------------------------------------------------- allocation
@@ -1314,6 +1376,292 @@ int allocate_on(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_bytes
     return 0;
 }
 
+// ----------------------------------------------------------------------------- unequal layer groups
+// A cache whose layer groups differ in size is compressed partition by partition: the groups of one
+// size, staged contiguously, form a cache with equal groups that the batched stages take as it is;
+// the allocation runs once over all cells.  Parts are ordered by first appearance of their size.
+struct Part {
+  int G = 0;
+  std::vector<int> groups;      // indices of the original groups, ascending
+  std::vector<int32_t> starts;  // 0, G, 2G, ... of the staged cache
+  jolt_cache_desc d;
+};
+
+std::vector<Part> split_parts(const jolt_cache_desc *d) {
+  JOLT_REQUIRE(d && d->n_groups >= 1 && d->group_start && d->n_seq >= 1 && d->n_layers >= 1, JOLT_EINVAL,
+               "bad cache descriptor");
+  JOLT_REQUIRE(d->group_start[0] == 0 && d->group_start[d->n_groups] == d->n_layers, JOLT_EINVAL,
+               "group_start must run from 0 to n_layers");
+  std::vector<Part> parts;
+  for (int g = 0; g < d->n_groups; ++g) {
+    const int G = d->group_start[g + 1] - d->group_start[g];
+    JOLT_REQUIRE(G >= 1, JOLT_EINVAL, "group_start must be increasing");
+    size_t i = 0;
+    while (i < parts.size() && parts[i].G != G) ++i;
+    if (i == parts.size()) {
+      parts.emplace_back();
+      parts.back().G = G;
+    }
+    parts[i].groups.push_back(g);
+  }
+  for (Part &p : parts) {
+    p.starts.resize(p.groups.size() + 1);
+    for (size_t i = 0; i <= p.groups.size(); ++i) p.starts[i] = (int32_t)(i * p.G);
+    p.d = *d;
+    p.d.n_layers = (int32_t)(p.G * p.groups.size());
+    p.d.n_groups = (int32_t)p.groups.size();
+    p.d.group_start = p.starts.data();
+  }
+  return parts;
+}
+
+bool equal_groups(const jolt_cache_desc *d) { return split_parts(d).size() == 1; }
+
+// Dense reconstruction of the given cells (all of one group size, as pl describes them)
+struct RecCell {
+  const jolt_pick *p;
+  char *out;  // [G][H][T][D] in the cache dtype
+};
+
+void reconstruct_cells(const Plan &pl, const std::vector<RecCell> &cells, const char *blob, Arena &ar, hipStream_t st) {
+  const int nb = (int)cells.size(), D = pl.D, GH = pl.GH;
+  int kmax = 8, kmd = 8;
+  for (const RecCell &rc : cells) {
+    const jolt_pick &p = *rc.p;
+    JOLT_REQUIRE(p.rT >= 8 && p.rT % 8 == 0 && p.rT <= pl.T && p.rd >= 8 && p.rd % 8 == 0 && p.rd <= D &&
+                     p.bits >= 0 && p.bits <= 8 && p.offset >= 0 && p.offset % 256 == 0,
+                 JOLT_EINVAL, "bad pick");
+    kmax = std::max(kmax, p.rT);
+    kmd = std::max(kmd, p.rd);
+  }
+  const int Kd = (int)rup(kmax, 8);
+  float *Udr = ar.take<float>((long long)nb * kmd * D);
+  float *Cr = ar.take<float>((long long)nb * GH * kmax * kmd);
+  float *Dm = ar.take<float>((long long)nb * GH * D * Kd);
+  float *am = ar.take<float>(2LL * nb);
+  char *params_area = ar.take<char>(64 * 1024 + (long long)nb * (sizeof(FactorCell) + sizeof(DecCell)) + 2LL * D * D * 4);
+  Upload u;
+  std::vector<FactorCell> fc(nb);
+  std::vector<DecCell> dc(nb);
+  std::vector<size_t> rot_offs;
+  {
+    const std::vector<double> &Q = rotation(D, pl.rot_seed);
+    std::vector<float> qf(Q.size());
+    for (size_t i = 0; i < Q.size(); ++i) qf[i] = (float)Q[i];
+    rot_offs.push_back(u.add(qf.data(), qf.size() * 4));
+  }
+  for (int c = 0; c < nb; ++c) {
+    const jolt_pick &p = *cells[c].p;
+    Section sec = layout(pl.G, pl.H, pl.T, D, pl.c, p.rT, p.rd, p.bits);
+    FactorCell &f = fc[c];
+    memset(&f, 0, sizeof(f));
+    f.UT = (void *)(blob + p.offset + sec.off_UT);
+    f.Ud = (void *)(blob + p.offset + sec.off_Ud);
+    f.core = (void *)(blob + p.offset + sec.off_core);
+    f.rT = p.rT; f.rd = p.rd; f.bits = p.bits;
+    DecCell &d = dc[c];
+    d.UT = f.UT;
+    d.Dm = Dm + (long long)c * GH * D * Kd;
+    d.Q = nullptr;  // bound after upload
+    d.d_amax = nullptr;
+    d.scales = (const float *)(blob + p.offset + sec.off_scales);
+    d.codes = (const uint8_t *)(blob + p.offset + sec.off_codes);
+    d.out = cells[c].out;
+    d.GH = GH; d.rT = p.rT; d.bits = p.bits; d.Kd = Kd;
+  }
+  size_t o_fc = u.add(fc.data(), nb * sizeof(FactorCell));
+  const float *Qdev = (const float *)(params_area + rot_offs[0]);
+  for (int c = 0; c < nb; ++c) {
+    dc[c].Q = Qdev;
+    dc[c].d_amax = am + c;
+  }
+  size_t o_dc = u.add(dc.data(), nb * sizeof(DecCell));
+  HIP_TRY(hipMemcpyAsync(params_area, u.host.data(), u.host.size(), hipMemcpyHostToDevice, st));
+  FactorCell *d_fc = (FactorCell *)(params_area + o_fc);
+  fill_f32(Udr, (long long)nb * kmd * D, 0.f, st);
+  fill_f32(Cr, (long long)nb * GH * kmax * kmd, 0.f, st);
+  get_small(pl.dtype, d_fc, nb, kmax, kmd, D, GH, Udr, Cr, st);
+  amax_cells(Cr, (long long)GH * kmax * kmd, (long long)GH * kmax * kmd, nb, am + nb, st);
+  // Dm[cell][j][n][r] = sum_kk Udr[kk][n] Cr[j][r][kk]
+  GemmArgs g = ga();
+  g.A = Udr; g.a_ld = D; g.a_bs = (long long)kmd * D; g.a_bs2 = 0; g.a_amax_c = 1.f;
+  g.B = Cr; g.b_ld = kmd; g.b_bs = (long long)GH * kmax * kmd; g.b_bs2 = (long long)kmax * kmd;
+  g.b_amax = am + nb; g.ab_amax_bs = 1;
+  g.inner = GH;
+  g.M = D; g.N = kmax; g.K = kmd;
+  g.C = Dm; g.c_ld = Kd; g.c_bs = (long long)GH * D * Kd; g.c_bs2 = (long long)D * Kd;
+  gemm(MF_F16, SRC_F32, false, SRC_F32, true, g, nb * GH, 1, st);
+  amax_cells(Dm, (long long)GH * D * Kd, (long long)GH * D * Kd, nb, am, st);
+  Stage prof("residual_decode", st);
+  decode_cells(pl.dtype, (const DecCell *)(params_area + o_dc), nb, pl.T, D, GH, st);
+}
+
+// Buffers of a compress call over unequal groups: per part the staged K and V and the part's own
+// carving; then the spectra of all cells packed in cell order and the allocation's buffers.
+struct PartBufs {
+  char *K, *V;
+  Bufs b;
+  Sizes sz;
+};
+struct PartsLayout {
+  std::vector<Plan> pl;
+  std::vector<PartBufs> pb;
+  double *specT, *specD, *norm2;
+  Bufs ab;
+  long long nT_total;
+};
+
+PartsLayout carve_parts(Arena &ar, const std::vector<Part> &parts, const jolt_params *params) {
+  PartsLayout L;
+  long long nT_total = 0;
+  int nc = 0;
+  for (const Part &pt : parts) {
+    Plan pl = make_plan(&pt.d, params);
+    PartBufs pb;
+    const long long bytes = (long long)pl.n_seq * pl.L * pl.H * pl.T * pl.D * pl.c;
+    pb.K = ar.take<char>(bytes);
+    pb.V = ar.take<char>(bytes);
+    pb.sz = sizes_worst(pl);
+    pb.b = carve(ar, pl, pb.sz);
+    nT_total += (long long)pl.n_cells * pl.nT;
+    nc += pl.n_cells;
+    L.pl.push_back(pl);
+    L.pb.push_back(pb);
+  }
+  const int D = L.pl[0].D;
+  L.specT = ar.take<double>(nT_total);
+  L.specD = ar.take<double>((long long)nc * D);
+  L.norm2 = ar.take<double>(nc);
+  Plan all = L.pl[0];
+  all.n_cells = nc;
+  L.ab = carve_alloc(ar, all, nc);
+  L.nT_total = nT_total;
+  return L;
+}
+
+int compress_parts(const void *d_K, const void *d_V, const jolt_cache_desc *desc, const jolt_params *params,
+                   void *d_out, size_t out_bytes, void *d_ws, size_t ws_bytes, jolt_pick *h_picks, double *h_lambda,
+                   hipStream_t st) {
+  const std::vector<Part> parts = split_parts(desc);
+  Arena ar;
+  ar.dry = false;
+  ar.base = (char *)d_ws;
+  ar.cap = ws_bytes;
+  PartsLayout L = carve_parts(ar, parts, params);
+  const int n_groups = desc->n_groups, nc = 2 * desc->n_seq * n_groups;
+  const Plan &p0 = L.pl[0];
+  const int H = p0.H, T = p0.T, D = p0.D, c = p0.c;
+  const long long layer = (long long)H * T * D * c;  // bytes of one layer of one sequence
+  // global cell c = 2 (s n_groups + g) + t: its part, and its cell index inside the part
+  std::vector<int> part_of(nc), local_of(nc);
+  std::vector<long long> offT(nc + 1, 0), offD(nc + 1, 0);
+  std::vector<int> shape(4 * nc);
+  for (size_t q = 0; q < parts.size(); ++q)
+    for (int s = 0; s < desc->n_seq; ++s)
+      for (size_t gl = 0; gl < parts[q].groups.size(); ++gl)
+        for (int t = 0; t < 2; ++t) {
+          const int cg = 2 * (s * n_groups + parts[q].groups[gl]) + t;
+          part_of[cg] = (int)q;
+          local_of[cg] = 2 * (s * (int)parts[q].groups.size() + (int)gl) + t;
+        }
+  for (int cg = 0; cg < nc; ++cg) {
+    const Plan &pl = L.pl[part_of[cg]];
+    offT[cg + 1] = offT[cg] + pl.nT;
+    offD[cg + 1] = offD[cg] + D;
+    shape[4 * cg] = pl.G; shape[4 * cg + 1] = H; shape[4 * cg + 2] = T; shape[4 * cg + 3] = D;
+  }
+  // stage each part's layers contiguously
+  for (size_t q = 0; q < parts.size(); ++q) {
+    const Part &pt = parts[q];
+    for (int s = 0; s < desc->n_seq; ++s)
+      for (size_t gl = 0; gl < pt.groups.size(); ++gl) {
+        const long long src = ((long long)s * desc->n_layers + desc->group_start[pt.groups[gl]]) * layer;
+        const long long dst = ((long long)s * pt.d.n_layers + (long long)gl * pt.G) * layer;
+        HIP_TRY(hipMemcpyAsync(L.pb[q].K + dst, (const char *)d_K + src, pt.G * layer, hipMemcpyDeviceToDevice, st));
+        HIP_TRY(hipMemcpyAsync(L.pb[q].V + dst, (const char *)d_V + src, pt.G * layer, hipMemcpyDeviceToDevice, st));
+      }
+  }
+  // spectra per part, packed in cell order
+  for (size_t q = 0; q < parts.size(); ++q) {
+    spectra_all(L.pl[q], L.pb[q].b, L.pb[q].sz, L.pb[q].K, L.pb[q].V, st);
+    const Bufs &b = L.pb[q].b;
+    const int nT = L.pl[q].nT;
+    for (int cg = 0; cg < nc; ++cg) {
+      if (part_of[cg] != (int)q) continue;
+      const int cl = local_of[cg];
+      HIP_TRY(hipMemcpyAsync(L.specT + offT[cg], b.specT + (long long)cl * nT, nT * 8, hipMemcpyDeviceToDevice, st));
+      HIP_TRY(hipMemcpyAsync(L.specD + offD[cg], b.specD + (long long)cl * D, D * 8, hipMemcpyDeviceToDevice, st));
+      HIP_TRY(hipMemcpyAsync(L.norm2 + cg, b.norm2 + cl, 8, hipMemcpyDeviceToDevice, st));
+    }
+  }
+  // one allocation over all cells
+  Upload u;
+  std::vector<size_t> o;
+  upload_alloc_tables(u, p0, shape, offT, offD, o);
+  upload(L.ab, u, st);
+  AllocDev ad = bind_alloc(L.ab.params, o);
+  long long dense = 0;
+  for (int cg = 0; cg < nc; ++cg) dense += (long long)shape[4 * cg] * H * T * D * c;
+  const double budget = (double)dense / p0.C;
+  {
+    Stage prof("allocate", st);
+    run_allocation(nc, ad, c, L.specT, L.specD, L.norm2, (int)p0.rT.size(), (int)p0.rd.size(), (int)p0.bits.size(),
+                   budget, L.ab, st);
+  }
+  std::vector<int> pick(nc);
+  std::vector<double> n2(nc), perr(nc);
+  AllocOut ao;
+  HIP_TRY(hipMemcpyAsync(pick.data(), L.ab.pick, nc * 4, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipMemcpyAsync(n2.data(), L.norm2, nc * 8, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipMemcpyAsync(&ao, L.ab.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipMemcpyAsync(perr.data(), L.ab.perr, nc * 8, hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  for (int cg = 0; cg < nc; ++cg) JOLT_REQUIRE(isfinite(n2[cg]), JOLT_ENONFINITE, "non-finite ||X||^2 in a cell");
+  for (int cg = 0; cg < nc; ++cg) JOLT_REQUIRE(isfinite(perr[cg]), JOLT_ENONFINITE, "non-finite spectrum in a cell");
+  if (h_lambda) *h_lambda = ao.lambda;
+  JOLT_REQUIRE(ao.status != kAllocEsync && ao.err == 0u, JOLT_EHIP, kAllocEsyncMsg);
+  JOLT_REQUIRE(ao.status == 0, JOLT_EINFEASIBLE, "allocation infeasible: the smallest picks exceed the budget");
+  const int nTg = (int)p0.rT.size(), nDg = (int)p0.rd.size();
+  std::vector<CellPick> cp(nc);
+  long long off = 0;
+  for (int cg = 0; cg < nc; ++cg) {
+    const int i = pick[cg], G = shape[4 * cg];
+    CellPick &p = cp[cg];
+    p.bits = p0.bits[i / (nTg * nDg)];
+    p.rT = p0.rT[(i / nDg) % nTg];
+    p.rd = p0.rd[i % nDg];
+    p.sec = layout(G, H, T, D, c, p.rT, p.rd, p.bits);
+    p.off = off;
+    off += p.sec.end;
+    jolt_pick &h = h_picks[cg];
+    h.rT = p.rT; h.rd = p.rd; h.bits = p.bits; h.pad = 0;
+    h.bytes = eq1_bytes(G, H, T, D, c, p.rT, p.rd, p.bits);
+    h.err_pred = perr[cg];
+    h.offset = p.off;
+    h.section_bytes = p.sec.end;
+  }
+  JOLT_REQUIRE((size_t)off <= out_bytes, JOLT_EBUFFER, "output buffer too small for the blob");
+  // fit and residual per part (blob offsets are the global ones)
+  for (size_t q = 0; q < parts.size(); ++q) {
+    const Plan &pl = L.pl[q];
+    std::vector<CellPick> cpl(pl.n_cells);
+    int kmax = 8, kmax_d = 8;
+    for (int cg = 0; cg < nc; ++cg) {
+      if (part_of[cg] != (int)q) continue;
+      cpl[local_of[cg]] = cp[cg];
+      kmax = std::max(kmax, cp[cg].rT);
+      kmax_d = std::max(kmax_d, cp[cg].rd);
+    }
+    Sizes fsz = sizes_for(pl, kmax, kmax_d);
+    Sizes use = L.pb[q].sz;
+    use.kmax = fsz.kmax;
+    use.kmax_d = fsz.kmax_d;
+    use.Kb = fsz.Kb;
+    stage_fit(pl, L.pb[q].b, use, L.pb[q].K, L.pb[q].V, (char *)d_out, cpl, st);
+  }
+  return 0;
+}
+
 }  // namespace
 }  // namespace jolt
 
@@ -1395,10 +1743,14 @@ int32_t jolt_profile_read(char *h_names, int32_t names_bytes, double *h_ms, int3
 size_t jolt_workspace_bytes(const jolt_cache_desc *desc, const jolt_params *params) {
   size_t out = 0;
   int st = guarded([&]() {
-    Plan pl = make_plan(desc, params);
     Arena ar;
-    Sizes sz = sizes_worst(pl);
-    carve(ar, pl, sz);
+    if (equal_groups(desc)) {
+      Plan pl = make_plan(desc, params);
+      Sizes sz = sizes_worst(pl);
+      carve(ar, pl, sz);
+    } else {
+      carve_parts(ar, split_parts(desc), params);
+    }
     out = ar.off + 4096;
     return 0;
   });
@@ -1408,11 +1760,18 @@ size_t jolt_workspace_bytes(const jolt_cache_desc *desc, const jolt_params *para
 size_t jolt_output_bytes(const jolt_cache_desc *desc, const jolt_params *params) {
   size_t out = 0;
   int st = guarded([&]() {
-    Plan pl = make_plan(desc, params);
-    long long dense = (long long)pl.n_cells * pl.cell_elems() * pl.c;
-    double B = (double)dense / pl.C;
+    const std::vector<Part> parts = split_parts(desc);
+    long long dense = 0, n_cells = 0;
+    double C = 0.0;
+    for (const Part &pt : parts) {
+      Plan pl = make_plan(&pt.d, params);
+      dense += (long long)pl.n_cells * pl.cell_elems() * pl.c;
+      n_cells += pl.n_cells;
+      C = pl.C;
+    }
+    double B = (double)dense / C;
     // every section: header + up to 5 parts padded to 256 bytes
-    out = (size_t)ceil(B) + (size_t)pl.n_cells * (256 + 5 * 256) + 256;
+    out = (size_t)ceil(B) + (size_t)n_cells * (256 + 5 * 256) + 256;
     return 0;
   });
   return st == 0 ? out : 0;
@@ -1460,6 +1819,75 @@ int jolt_sketch_matrix(int32_t M, int32_t ell, int32_t dtype, uint64_t sketch_se
     JOLT_REQUIRE(dtype == JOLT_F16 || dtype == JOLT_BF16 || dtype == JOLT_F32, JOLT_EINVAL, "bad dtype");
     JOLT_REQUIRE(d_omegaT != nullptr, JOLT_EINVAL, "null output");
     gen_omega(d_omegaT, dtype, M, ell, stream_key(sketch_seed, 2), S(stream));
+    return 0;
+  });
+}
+
+size_t jolt_layer_groups_workspace_bytes(const jolt_cache_desc *desc) {
+  size_t out = 0;
+  int st = guarded([&]() {
+    LayerSetup ls;
+    layer_setup(desc, 0, ls);
+    Plan pl = make_plan(&ls.d1, &ls.p1);
+    Arena ar;
+    carve(ar, pl, sizes_for(pl, kGroupVecs, kGroupVecs));
+    ar.take<double>((long long)pl.n_seq * std::max(pl.L - 1, 1) * kGroupVecs * kGroupVecs);
+    out = ar.off + 4096;
+    return 0;
+  });
+  return st == 0 ? out : 0;
+}
+
+int jolt_layer_groups(const void *d_K, const jolt_cache_desc *desc, uint64_t sketch_seed, int32_t *h_group_start,
+                      int32_t *h_n_groups, double *h_scores, void *d_ws, size_t ws_bytes, void *stream) {
+  return guarded([&]() {
+    JOLT_REQUIRE(d_K && h_group_start && h_n_groups, JOLT_EINVAL, "null argument");
+    JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
+    LayerSetup ls;
+    layer_setup(desc, sketch_seed, ls);
+    Plan pl = make_plan(&ls.d1, &ls.p1);
+    hipStream_t st = S(stream);
+    Arena ar;
+    ar.dry = false;
+    ar.base = (char *)d_ws;
+    ar.cap = ws_bytes;
+    const int k = kGroupVecs, L = pl.L, nb = pl.n_cells;
+    Sizes sz = sizes_for(pl, k, k);
+    Bufs b = carve(ar, pl, sz);
+    double *S = ar.take<double>((long long)pl.n_seq * std::max(L - 1, 1) * k * k);
+    spectra_all(pl, b, sz, d_K, d_K, st);
+    std::vector<int> kv(nb, k);
+    Upload u;
+    const size_t ok = u.add(kv.data(), nb * 4);
+    upload(b, u, st);
+    const long long ell = pl.ell, ld = pl.ell_ld;
+    fill_f32(b.Wrows, (long long)nb * sz.kmax * ld, 0.f, st);
+    sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, (int)ell, (const int *)(b.params + ok), sz.kmax, nb, b.Zw,
+                (long long)sz.kmax * ell, b.work, (long long)invit_work_doubles((int)ell, sz.kmax), nullptr, b.Wrows,
+                (long long)sz.kmax * ld, (int)ld, st);
+    flash_factor_rows(pl, b, sz.kmax, k, b.bufB, st);
+    std::vector<double> hS((size_t)pl.n_seq * std::max(L - 1, 1) * k * k, 0.0);
+    if (L >= 2) {
+      pair_cross(b.bufB, (long long)sz.kmax * pl.T_ld, pl.T_ld, pl.T, k, L, pl.n_seq, S, st);
+      HIP_TRY(hipMemcpyAsync(hS.data(), S, hS.size() * sizeof(double), hipMemcpyDeviceToHost, st));
+    }
+    HIP_TRY(hipStreamSynchronize(st));
+    std::vector<double> sc(std::max(L - 1, 0), 0.0);
+    for (int l = 0; l + 1 < L; ++l) {
+      double acc = 0.0;
+      for (int q = 0; q < pl.n_seq; ++q) {
+        const double *m = hS.data() + ((size_t)q * (L - 1) + l) * k * k;
+        double f = 0.0;
+        for (int i = 0; i < k * k; ++i) f += m[i] * m[i];
+        acc += f / k;
+      }
+      sc[l] = acc / pl.n_seq;
+      JOLT_REQUIRE(isfinite(sc[l]), JOLT_ENONFINITE, "layer grouping: non-finite alignment score");
+    }
+    const std::vector<int32_t> g = groups_from_scores(sc, L);
+    *h_n_groups = (int32_t)g.size() - 1;
+    memcpy(h_group_start, g.data(), g.size() * sizeof(int32_t));
+    if (h_scores) memcpy(h_scores, sc.data(), sc.size() * sizeof(double));
     return 0;
   });
 }
@@ -1534,10 +1962,13 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
                   void *d_out, size_t out_bytes, void *d_ws, size_t ws_bytes, jolt_pick *h_picks, double *h_lambda,
                   void *stream) {
   return guarded([&]() {
-    Plan pl = make_plan(desc, params);
     hipStream_t st = S(stream);
     JOLT_REQUIRE(d_out && h_picks, JOLT_EINVAL, "null output");
     JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
+    JOLT_REQUIRE(d_K && d_V, JOLT_EINVAL, "null cache pointer");
+    if (!equal_groups(desc))
+      return compress_parts(d_K, d_V, desc, params, d_out, out_bytes, d_ws, ws_bytes, h_picks, h_lambda, st);
+    Plan pl = make_plan(desc, params);
     Arena ar;
     ar.dry = false;
     ar.base = (char *)d_ws;
@@ -1620,88 +2051,28 @@ int jolt_reconstruct(const void *d_blob, const jolt_cache_desc *desc, const jolt
                      const jolt_pick *h_picks, void *d_K_out, void *d_V_out, void *d_ws, size_t ws_bytes,
                      void *stream) {
   return guarded([&]() {
-    Plan pl = make_plan(desc, params);
-    hipStream_t st = S(stream);
-    JOLT_REQUIRE(d_blob && h_picks && d_K_out && d_V_out, JOLT_EINVAL, "null argument");
+    JOLT_REQUIRE(d_blob && h_picks && d_K_out && d_V_out && desc, JOLT_EINVAL, "null argument");
     JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
-    const int nb = pl.n_cells, D = pl.D, GH = pl.GH;
-    int kmax = 8, kmd = 8;
-    for (int c = 0; c < nb; ++c) {
-      const jolt_pick &p = h_picks[c];
-      JOLT_REQUIRE(p.rT >= 8 && p.rT % 8 == 0 && p.rT <= pl.T && p.rd >= 8 && p.rd % 8 == 0 && p.rd <= D &&
-                       p.bits >= 0 && p.bits <= 8 && p.offset >= 0 && p.offset % 256 == 0,
-                   JOLT_EINVAL, "bad pick");
-      kmax = std::max(kmax, p.rT);
-      kmd = std::max(kmd, p.rd);
+    hipStream_t st = S(stream);
+    const std::vector<Part> parts = split_parts(desc);
+    for (const Part &pt : parts) {
+      Plan pl = make_plan(&pt.d, params);
+      const int c_bytes = pl.c;
+      std::vector<RecCell> cells;
+      for (int s = 0; s < desc->n_seq; ++s)
+        for (int g : pt.groups)
+          for (int t = 0; t < 2; ++t) {
+            const int c = 2 * (s * desc->n_groups + g) + t;
+            char *ob = (char *)(t == 0 ? d_K_out : d_V_out);
+            const long long lay = (long long)s * desc->n_layers + desc->group_start[g];
+            cells.push_back(RecCell{&h_picks[c], ob + lay * (long long)pl.H * pl.T * pl.D * c_bytes});
+          }
+      Arena ar;
+      ar.dry = false;
+      ar.base = (char *)d_ws;
+      ar.cap = ws_bytes;
+      reconstruct_cells(pl, cells, (const char *)d_blob, ar, st);  // parts run in stream order: scratch reused
     }
-    Arena ar;
-    ar.dry = false;
-    ar.base = (char *)d_ws;
-    ar.cap = ws_bytes;
-    const int Kd = (int)rup(kmax, 8);
-    float *Udr = ar.take<float>((long long)nb * kmd * D);
-    float *Cr = ar.take<float>((long long)nb * GH * kmax * kmd);
-    float *Dm = ar.take<float>((long long)nb * GH * D * Kd);
-    float *am = ar.take<float>(2LL * nb);
-    char *params_area = ar.take<char>(64 * 1024 + (long long)nb * (sizeof(FactorCell) + sizeof(DecCell)) + 2LL * D * D * 4);
-    Upload u;
-    std::vector<FactorCell> fc(nb);
-    std::vector<DecCell> dc(nb);
-    const long long cellX = pl.cell_elems();
-    const char *blob = (const char *)d_blob;
-    std::vector<size_t> rot_offs;
-    {
-      const std::vector<double> &Q = rotation(D, pl.rot_seed);
-      std::vector<float> qf(Q.size());
-      for (size_t i = 0; i < Q.size(); ++i) qf[i] = (float)Q[i];
-      rot_offs.push_back(u.add(qf.data(), qf.size() * 4));
-    }
-    for (int c = 0; c < nb; ++c) {
-      const jolt_pick &p = h_picks[c];
-      Section sec = layout(pl.G, pl.H, pl.T, D, pl.c, p.rT, p.rd, p.bits);
-      FactorCell &f = fc[c];
-      memset(&f, 0, sizeof(f));
-      f.UT = (void *)(blob + p.offset + sec.off_UT);
-      f.Ud = (void *)(blob + p.offset + sec.off_Ud);
-      f.core = (void *)(blob + p.offset + sec.off_core);
-      f.rT = p.rT; f.rd = p.rd; f.bits = p.bits;
-      const int s = c / (2 * pl.n_groups), g = (c / 2) % pl.n_groups, t = c % 2;
-      char *ob = (char *)(t == 0 ? d_K_out : d_V_out);
-      DecCell &d = dc[c];
-      d.UT = f.UT;
-      d.Dm = Dm + (long long)c * GH * D * Kd;
-      d.Q = nullptr;  // bound after upload
-      d.d_amax = nullptr;
-      d.scales = (const float *)(blob + p.offset + sec.off_scales);
-      d.codes = (const uint8_t *)(blob + p.offset + sec.off_codes);
-      d.out = ob + ((long long)s * pl.n_groups + g) * cellX * pl.c;
-      d.GH = GH; d.rT = p.rT; d.bits = p.bits; d.Kd = Kd;
-    }
-    size_t o_fc = u.add(fc.data(), nb * sizeof(FactorCell));
-    const float *Qdev = (const float *)(params_area + rot_offs[0]);
-    for (int c = 0; c < nb; ++c) {
-      dc[c].Q = Qdev;
-      dc[c].d_amax = am + c;
-    }
-    size_t o_dc = u.add(dc.data(), nb * sizeof(DecCell));
-    HIP_TRY(hipMemcpyAsync(params_area, u.host.data(), u.host.size(), hipMemcpyHostToDevice, st));
-    FactorCell *d_fc = (FactorCell *)(params_area + o_fc);
-    fill_f32(Udr, (long long)nb * kmd * D, 0.f, st);
-    fill_f32(Cr, (long long)nb * GH * kmax * kmd, 0.f, st);
-    get_small(pl.dtype, d_fc, nb, kmax, kmd, D, GH, Udr, Cr, st);
-    amax_cells(Cr, (long long)GH * kmax * kmd, (long long)GH * kmax * kmd, nb, am + nb, st);
-    // Dm[cell][j][n][r] = sum_kk Udr[kk][n] Cr[j][r][kk]
-    GemmArgs g = ga();
-    g.A = Udr; g.a_ld = D; g.a_bs = (long long)kmd * D; g.a_bs2 = 0; g.a_amax_c = 1.f;
-    g.B = Cr; g.b_ld = kmd; g.b_bs = (long long)GH * kmax * kmd; g.b_bs2 = (long long)kmax * kmd;
-    g.b_amax = am + nb; g.ab_amax_bs = 1;
-    g.inner = GH;
-    g.M = D; g.N = kmax; g.K = kmd;
-    g.C = Dm; g.c_ld = Kd; g.c_bs = (long long)GH * D * Kd; g.c_bs2 = (long long)D * Kd;
-    gemm(MF_F16, SRC_F32, false, SRC_F32, true, g, nb * GH, 1, st);
-    amax_cells(Dm, (long long)GH * D * Kd, (long long)GH * D * Kd, nb, am, st);
-    Stage prof("residual_decode", st);
-    decode_cells(pl.dtype, (const DecCell *)(params_area + o_dc), nb, pl.T, D, GH, st);
     return 0;
   });
 }

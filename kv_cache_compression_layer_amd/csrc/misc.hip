@@ -47,6 +47,40 @@ __global__ void omega_kernel(void *out, int dtype, int M, int ell, uint64_t key)
   }
 }
 
+// Cross products of the token bases of consecutive layers: block (l, s) forms the k x k matrix
+// S = U_l U_{l+1}^T of sequence s, U_l the first k rows of length T of layer l's key cell (cells
+// ordered (sequence, layer, K|V), rows at stride ld, cell stride cs); products summed in fp64.
+template <int K>
+__global__ void __launch_bounds__(256) pair_cross_kernel(const float *U, long long cs, int ld, int T, int L, double *S) {
+  __shared__ double red[4][K * K];
+  const int l = blockIdx.x, sq = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float *a = U + (long long)(2 * (sq * L + l)) * cs;
+  const float *b = a + 2 * cs;
+  double acc[K * K];
+#pragma unroll
+  for (int i = 0; i < K * K; ++i) acc[i] = 0.0;
+  for (int t = tid; t < T; t += 256) {
+    double x[K], y[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      x[i] = a[(long long)i * ld + t];
+      y[i] = b[(long long)i * ld + t];
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+#pragma unroll
+      for (int j = 0; j < K; ++j) acc[i * K + j] += x[i] * y[j];
+  }
+#pragma unroll
+  for (int i = 0; i < K * K; ++i) {
+    double v = acc[i];
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (lane == 0) red[w][i] = v;
+  }
+  __syncthreads();
+  if (tid < K * K) S[((long long)sq * (L - 1) + l) * K * K + tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+}
+
 __global__ void fill_f32_kernel(float *p, long long n, float v) {
   for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n; i += (long long)gridDim.x * blockDim.x) p[i] = v;
 }
@@ -302,6 +336,14 @@ void transpose_x(const void *X, void *Xt, int elem_bytes, int T, int T_ld, int D
                        GH, x_bs, xt_bs);
   HIP_LAUNCH_CHECK();
 }
+void pair_cross(const float *U, long long cell_stride, int ld, int T, int k, int L, int n_seq, double *S,
+                hipStream_t st) {
+  JOLT_REQUIRE(k == 8, JOLT_EINVAL, "layer grouping: 8 token vectors per layer");
+  if (L < 2) return;
+  hipLaunchKernelGGL((pair_cross_kernel<8>), dim3(L - 1, n_seq), dim3(256), 0, st, U, cell_stride, ld, T, L, S);
+  HIP_LAUNCH_CHECK();
+}
+
 void fill_f32(float *p, long long n, float v, hipStream_t st) {
   if (n <= 0) return;
   hipLaunchKernelGGL(fill_f32_kernel, dim3(grid_for(n)), dim3(256), 0, st, p, n, v);

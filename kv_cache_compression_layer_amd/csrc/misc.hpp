@@ -21,6 +21,10 @@ void gen_omega(void *out, int dtype, int M, int ell, uint64_t key, hipStream_t s
 void transpose_x(const void *X, void *Xt, int elem_bytes, int T, int T_ld, int D, int GH, int batch, long long x_bs,
                  long long xt_bs, hipStream_t st);
 void fill_f32(float *p, long long n, float v, hipStream_t st);
+// S[s][l] = U_l U_{l+1}^T (k x k, fp64) for consecutive layers of each sequence; U holds k rows of
+// length T (pitch ld) per cell, cells (sequence, layer, K|V) at stride cell_stride
+void pair_cross(const float *U, long long cell_stride, int ld, int T, int k, int L, int n_seq, double *S,
+                hipStream_t st);
 void fill_f64(double *p, long long n, double v, hipStream_t st);
 void trace_f64(const double *G, long long g_bs, int n, int batch, double *out, hipStream_t st);
 void flash_spec(const double *evals, long long ev_bs, int q, const double *norm2, double *specT, long long sp_bs,

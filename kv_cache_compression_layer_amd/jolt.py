@@ -23,7 +23,8 @@ DTYPE_OF = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 EXPORTS = ["jolt_workspace_bytes", "jolt_output_bytes", "jolt_allocate", "jolt_compress", "jolt_reconstruct",
            "jolt_spectra", "jolt_token_spectrum_len", "jolt_encode_residual",
            "jolt_encode_residual_workspace_bytes", "jolt_rotation", "jolt_eps2", "jolt_last_error", "jolt_profile",
-           "jolt_profile_read", "jolt_sketch_matrix", "jolt_test_wait_policy", "jolt_allocate_static"]
+           "jolt_profile_read", "jolt_sketch_matrix", "jolt_test_wait_policy", "jolt_allocate_static", "jolt_layer_groups",
+           "jolt_layer_groups_workspace_bytes"]
 
 
 class JoltError(RuntimeError):
@@ -89,6 +90,9 @@ def load():
         "jolt_last_error": (ctypes.c_char_p, []),
         "jolt_profile": (ctypes.c_int, [i32]),
         "jolt_sketch_matrix": (ctypes.c_int, [i32, i32, i32, ctypes.c_uint64, P, P]),
+        "jolt_layer_groups_workspace_bytes": (sz, [pd]),
+        "jolt_layer_groups": (ctypes.c_int, [P, pd, ctypes.c_uint64, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                             ctypes.POINTER(dbl), P, sz, P]),
         "jolt_test_wait_policy": (ctypes.c_int, [ctypes.c_uint32, i32]),
         "jolt_profile_read": (i32, [ctypes.c_char_p, i32, ctypes.POINTER(dbl), ctypes.POINTER(i32), i32]),
     }
@@ -289,6 +293,26 @@ def eps2(d_head):
     out = np.zeros(9)
     _check(load().jolt_eps2(d_head, out.ctypes.data_as(ctypes.POINTER(ctypes.c_double))))
     return out
+
+
+def layer_groups(K, sketch_seed=0):
+    """Layer groups of a key cache [n_seq][L][H][T][D] by token-subspace alignment.
+
+    Returns (group_start list, scores array of the L-1 consecutive-layer pairs)."""
+    lib = load()
+    n_seq, L, H, T, D = K.shape
+    cfg = Config(n_seq, L, H, T, D, DTYPE_OF[K.dtype], list(range(L + 1)), FLASH, [8], [8], [2], 2.0)
+    nws = lib.jolt_layer_groups_workspace_bytes(ctypes.byref(cfg.desc))
+    if nws == 0:
+        _check(-1)
+    ws = torch.empty(nws, dtype=torch.uint8, device=K.device)
+    starts = (ctypes.c_int32 * (L + 1))()
+    ng = ctypes.c_int32(0)
+    sc = np.zeros(max(L - 1, 0))
+    _check(lib.jolt_layer_groups(_ptr(K.contiguous()), ctypes.byref(cfg.desc), int(sketch_seed), starts,
+                                 ctypes.byref(ng), sc.ctypes.data_as(ctypes.POINTER(ctypes.c_double)), _ptr(ws),
+                                 nws, _stream()))
+    return [int(starts[i]) for i in range(ng.value + 1)], sc
 
 
 def sketch_matrix(M, ell, dtype, seed=0, device="cuda"):

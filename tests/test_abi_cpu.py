@@ -69,7 +69,7 @@ def test_exact_spectrum_length_is_min_T_M():
 @pytest.mark.parametrize("bad", [
     dict(d_head=96),
     dict(dtype=7),
-    dict(group_start=[0, 3, 8]),           # non-uniform groups
+    dict(group_start=[0, 0, 8]),           # an empty group
     dict(group_start=[0, 4, 9]),           # does not end at n_layers
     dict(rd_grid=[8, 16, 128]),            # rank above d_head
     dict(rd_grid=[16, 8]),                 # not ascending
@@ -87,6 +87,21 @@ def test_invalid_configurations_are_rejected(bad):
     with pytest.raises(jolt.JoltError) as e:
         cfg.workspace_bytes()
     assert e.value.status == -1
+
+
+def test_unequal_groups_are_sized_per_part():
+    """Groups of different sizes (Sec. 3's alignment grouping yields 2..9 layers): the workspace covers
+    each size's own carving plus the staged layers, the output bound the dense bytes of all cells."""
+    eq = _cfg(group_start=[0, 4, 8])
+    uneq = _cfg(group_start=[0, 3, 8])
+    lib = jolt.load()
+    ws_eq = lib.jolt_workspace_bytes(ctypes.byref(eq.desc), ctypes.byref(eq.params))
+    ws_un = lib.jolt_workspace_bytes(ctypes.byref(uneq.desc), ctypes.byref(uneq.params))
+    assert ws_eq > 0 and ws_un > ws_eq
+    assert lib.jolt_output_bytes(ctypes.byref(uneq.desc), ctypes.byref(uneq.params)) == \
+        lib.jolt_output_bytes(ctypes.byref(eq.desc), ctypes.byref(eq.params))
+    # the stage entry points still take one group size
+    assert lib.jolt_token_spectrum_len(ctypes.byref(uneq.desc), ctypes.byref(uneq.params)) < 0
 
 
 def test_eps2_argument_validation():
