@@ -38,6 +38,7 @@ __all__ = [
     "pack_rows", "unpack_rows", "rotation", "sketch_matrix", "eps2_calibrate", "qcap_eq5",
     "cell_bytes", "token_unfolding", "feature_spectrum", "token_factors_exact",
     "token_factors_flash", "layer_token_basis", "alignment_scores", "group_layers", "suffix_sums", "cell_table", "argmin_cell", "allocate",
+    "argmin_cell_greedy", "allocate_with", "allocate_greedy", "allocate_kv_decoupled", "allocate_uniform_ranks",
     "fit_cell", "rotated_residual", "encode_cell", "decode_cell", "cells_of_cache", "section_layout",
     "write_blob", "read_blob_cell", "compress", "reconstruct", "CellShape",
 ]
@@ -340,6 +341,122 @@ def allocate(tables, budget):
         else:
             hi, idx_hi, S_hi, E_hi = mid, idx, S, E
     return {"status": 0, "lam": hi, "picks": idx_hi, "S": S_hi, "E": E_hi, "iters": MAX_BISECT}
+
+
+# ----------------------------------------------------------------------------
+# allocator variants (Sec. 3 "Solving the allocation" greedy search; Sec. 4.4 ablations)
+# ----------------------------------------------------------------------------
+def argmin_cell_greedy(tab, lam, n_rT, n_rd):
+    """The pages' per-cell search at fixed lambda: for each bit-width, start at the smallest token and
+    feature grid ranks and take one rank step at a time, in the mode whose next grid step removes the
+    most error per added byte, as long as that step lowers e + lambda s (its error reduction exceeds
+    lambda times its byte increment); stop when neither mode can step.  The cell keeps the bit-width
+    with the smallest e + lambda s (ties: smaller bytes, then smaller b).  On equal descent rates the
+    token mode steps first.  Table index: b-major, then r_T, then r_d."""
+    e, sz = tab["e"], tab["s"].astype(np.float64)
+    n_b = len(e) // (n_rT * n_rd)
+    best = None
+    for bi in range(n_b):
+        iT, iD = 0, 0
+        while True:
+            here = (bi * n_rT + iT) * n_rd + iD
+            moves = []
+            if iT + 1 < n_rT:
+                nxt = (bi * n_rT + iT + 1) * n_rd + iD
+                de, ds = e[here] - e[nxt], sz[nxt] - sz[here]
+                if de > lam * ds:
+                    moves.append((de / ds, 0, nxt))
+            if iD + 1 < n_rd:
+                nxt = (bi * n_rT + iT) * n_rd + iD + 1
+                de, ds = e[here] - e[nxt], sz[nxt] - sz[here]
+                if de > lam * ds:
+                    moves.append((de / ds, 1, nxt))
+            if not moves:
+                break
+            rate, mode, nxt = max(moves, key=lambda m: (m[0], -m[1]))
+            if mode == 0:
+                iT += 1
+            else:
+                iD += 1
+        i = (bi * n_rT + iT) * n_rd + iD
+        key = (e[i] + lam * sz[i], sz[i], bi)
+        if best is None or key < best[0]:
+            best = (key, i)
+    return int(best[1])
+
+
+def allocate_with(tables, budget, argmin):
+    """Geometric bisection on lambda (as allocate) with a given per-cell minimiser argmin(table, lam)."""
+    def evaluate(lam):
+        idx = [argmin(t, lam) for t in tables]
+        return idx, int(sum(int(t["s"][i]) for t, i in zip(tables, idx))), \
+            float(sum(float(t["e"][i]) for t, i in zip(tables, idx)))
+
+    lo, hi = LAMBDA_LO, LAMBDA_HI
+    idx, S, E = evaluate(lo)
+    if S <= budget:
+        return {"status": 0, "lam": lo, "picks": idx, "S": S, "E": E, "iters": 0}
+    idx_hi, S_hi, E_hi = evaluate(hi)
+    if S_hi > budget:
+        return {"status": -2, "lam": hi, "picks": idx_hi, "S": S_hi, "E": E_hi, "iters": 0}
+    for it in range(MAX_BISECT):
+        mid = math.sqrt(lo * hi)
+        idx, S, E = evaluate(mid)
+        if 0.995 * budget <= S <= budget:
+            return {"status": 0, "lam": mid, "picks": idx, "S": S, "E": E, "iters": it + 1}
+        if S > budget:
+            lo = mid
+        else:
+            hi, idx_hi, S_hi, E_hi = mid, idx, S, E
+    return {"status": 0, "lam": hi, "picks": idx_hi, "S": S_hi, "E": E_hi, "iters": MAX_BISECT}
+
+
+def allocate_greedy(tables, budget, n_rT, n_rd):
+    """The Lagrangian allocation with the pages' greedy per-cell search instead of the exact argmin."""
+    return allocate_with(tables, budget, lambda t, lam: argmin_cell_greedy(t, lam, n_rT, n_rd))
+
+
+def allocate_kv_decoupled(tables, budget, dense_bytes):
+    """Keys and values under budgets of their own (Sec. 4.4 "Allocation strategy"): cells alternate K, V
+    (cell order (sequence, group, K|V)); each kind gets the budget in proportion to its dense bytes.
+    Returns the two allocations' picks merged in cell order, both lambdas and the worse status."""
+    out = {"picks": [0] * len(tables), "lam": [], "status": 0, "S": 0, "E": 0.0}
+    for kind in (0, 1):
+        cells = [c for c in range(len(tables)) if c % 2 == kind]
+        share = sum(dense_bytes[c] for c in cells) / float(sum(dense_bytes))
+        r = allocate([tables[c] for c in cells], budget * share)
+        out["lam"].append(r["lam"])
+        out["status"] = min(out["status"], r["status"])
+        out["S"] += r["S"]
+        out["E"] += r["E"]
+        for c, i in zip(cells, r["picks"]):
+            out["picks"][c] = i
+    return out
+
+
+def allocate_uniform_ranks(tables, budget, n_rT, n_rd):
+    """One (r_T, r_d) for every cell, bit-widths still allocated per cell by the Lagrangian (Sec. 4.4
+    "Per-group ranks"): for every grid pair, the bisection over the cells' bit-widths at that pair; the
+    pair whose feasible allocation has the smallest total error wins (ties: smaller total bytes, then
+    the earlier pair).  Returns the allocation with picks as full-table indices and the pair."""
+    best = None
+    for iT in range(n_rT):
+        for iD in range(n_rd):
+            sub = []
+            for t in tables:
+                n_b = len(t["e"]) // (n_rT * n_rd)
+                ix = np.array([(bi * n_rT + iT) * n_rd + iD for bi in range(n_b)])
+                sub.append({k: v[ix] for k, v in t.items()} | {"_ix": ix})
+            r = allocate(sub, budget)
+            if r["status"] != 0:
+                continue
+            key = (r["E"], r["S"], iT, iD)
+            if best is None or key < best[0]:
+                picks = [int(t["_ix"][i]) for t, i in zip(sub, r["picks"])]
+                best = (key, dict(r, picks=picks, pair=(iT, iD)))
+    if best is None:
+        return {"status": -2, "picks": None}
+    return best[1]
 
 
 # ----------------------------------------------------------------------------
