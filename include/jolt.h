@@ -82,7 +82,33 @@ typedef struct {
   double target_ratio;  /* C > 1: budget B = (dense bytes of all cells) / C */
   uint64_t rot_seed;    /* seed of the feature rotation */
   uint64_t sketch_seed; /* seed of the FlashJoLT Gaussian test matrix */
+  int32_t alloc_variant; /* jolt_alloc_variant flags; 0 = joint allocation, exact per-cell argmin */
 } jolt_params;
+
+/* Allocator variants (jolt_params.alloc_variant), all on the same distortion/byte table:
+ *   JOLT_ALLOC_GREEDY        the per-cell minimiser is the pages' greedy rank search (Sec. 3, "Solving
+ *                            the allocation"): per bit-width, start at the smallest grid ranks and step
+ *                            the mode whose next grid step removes the most error per added byte while
+ *                            that step lowers e + lambda s; keep the bit-width of smallest e + lambda s
+ *                            (equal rates: the token mode steps first).
+ *   JOLT_ALLOC_KV_DECOUPLED  keys and values are allocated separately (Sec. 4.4, "Allocation strategy"):
+ *                            the K cells (even cell indices) and the V cells (odd) each run their own
+ *                            bisection, under the budget's share of their dense bytes |g| n_h T d_h c;
+ *                            combinable with JOLT_ALLOC_GREEDY; needs at least two cells.
+ *   JOLT_ALLOC_UNIFORM_RANKS every cell takes the same (r_T, r_d) (Sec. 4.4, "Per-group ranks"); the
+ *                            bit-widths are still allocated per cell: for every grid pair a bisection over
+ *                            the cells' bit-widths; the feasible pair of smallest total error wins (ties:
+ *                            fewer bytes, then the earlier pair).  Not combinable with the others.
+ * Unknown flags, or uniform ranks with another flag: JOLT_EINVAL.  The multiplier of a uniform-rank
+ * allocation is that of the winning pair's bisection.
+ * Rank-only compression (bits = {0}) and a token-rank cap (the token grid cut at the cap, Appendix A)
+ * are restrictions of the grids. */
+typedef enum {
+  JOLT_ALLOC_JOINT = 0,
+  JOLT_ALLOC_GREEDY = 1,
+  JOLT_ALLOC_KV_DECOUPLED = 2,
+  JOLT_ALLOC_UNIFORM_RANKS = 4
+} jolt_alloc_variant;
 
 /* Allocation of one cell, and where its section sits in the blob. */
 typedef struct {
@@ -113,7 +139,8 @@ size_t jolt_output_bytes(const jolt_cache_desc *desc, const jolt_params *params)
  *   budget_bytes   B.
  *   h_picks        host jolt_pick[n_cells] (offset/section_bytes are set as if the cells were
  *                  written back to back in order).
- *   h_lambda       host double: the multiplier returned.
+ *   h_lambda       host double: the multiplier returned (may be NULL); with JOLT_ALLOC_KV_DECOUPLED
+ *                  host double[2]: the keys' multiplier, then the values'.
  * Every grid rank must satisfy r_T <= (length of the cell's token spectrum) and r_d <= d_h,
  * else JOLT_EINVAL (for a FlashJoLT spectrum, whose last entry is the tail, the caller keeps
  * r_T <= q_cap).  JOLT_EINFEASIBLE if even the smallest picks exceed B.
@@ -141,7 +168,8 @@ int jolt_allocate_static(int32_t n_cells, const int32_t *h_cell_shape, int32_t e
 
 /* Whole compression of K and V (Sec. 3 and Sec. 3.1): spectra, allocation under one budget,
  * ST-HOSVD fit, rotated b-bit residual.  Writes the blob (layout below) to d_out.
- *   h_picks   host jolt_pick[n_seq*n_groups*2]; h_lambda host double (may be NULL).
+ *   h_picks   host jolt_pick[n_seq*n_groups*2]; h_lambda host double (may be NULL; two doubles, keys'
+ *             then values', with JOLT_ALLOC_KV_DECOUPLED).
  * Synchronises the stream once (to read the picks); the blob is complete when the stream
  * reaches the end of the enqueued work.
  *

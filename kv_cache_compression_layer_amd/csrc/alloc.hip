@@ -25,6 +25,9 @@ struct Best {
   int idx;
 };
 
+// index, in the caller's arrays, of cell k of this run
+__device__ __forceinline__ int gcell(const AllocArgs &a, int k) { return a.cell_first + k * a.cell_step; }
+
 __device__ __forceinline__ bool less_than(const Best &x, const Best &y) {
   if (x.cost != y.cost) return x.cost < y.cost;
   if (x.s != y.s) return x.s < y.s;
@@ -39,6 +42,45 @@ __device__ Best shfl_best(const Best &v, int o) {
   return r;
 }
 
+// The greedy per-cell search for bit-width index bi (Sec. 3, "Solving the allocation"): from the
+// smallest grid ranks, step the mode whose next grid step removes the most error per added byte while
+// that step lowers e + lambda s, until neither can; equal rates step the token mode.  Same fp64
+// operations and roundings as the exact search.
+__device__ Best greedy_walk(const double *ec, const long long *sc, int bi, int nT, int nD, double lam) {
+  int iT = 0, iD = 0;
+  for (int step = 0; step < nT + nD; ++step) {
+    const int here = (bi * nT + iT) * nD + iD;
+    const double eh = ec[here], sh = (double)sc[here];
+    bool okT = false, okD = false;
+    double rt = 0.0, rd = 0.0;
+    if (iT + 1 < nT) {
+      const int nx = here + nD;
+      const double de = __dsub_rn(eh, ec[nx]), ds = __dsub_rn((double)sc[nx], sh);
+      if (de > __dmul_rn(lam, ds)) {
+        okT = true;
+        rt = __ddiv_rn(de, ds);
+      }
+    }
+    if (iD + 1 < nD) {
+      const int nx = here + 1;
+      const double de = __dsub_rn(eh, ec[nx]), ds = __dsub_rn((double)sc[nx], sh);
+      if (de > __dmul_rn(lam, ds)) {
+        okD = true;
+        rd = __ddiv_rn(de, ds);
+      }
+    }
+    if (!okT && !okD) break;
+    if (okT && (!okD || rt >= rd)) ++iT;
+    else ++iD;
+  }
+  const int i = (bi * nT + iT) * nD + iD;
+  Best b;
+  b.cost = __dadd_rn(ec[i], __dmul_rn(lam, (double)sc[i]));
+  b.s = sc[i];
+  b.idx = i;
+  return b;
+}
+
 __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
   __shared__ int pick[AllocArgs::kMaxCells];
   __shared__ long long pick_s[AllocArgs::kMaxCells];  // bytes and distortion of each cell's pick
@@ -51,9 +93,9 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
 
   // (1) suffix sums at the grid ranks (one thread per cell and mode; sequential order)
   for (int w = tid; w < 2 * nc; w += AT) {
-    const int c = w >> 1, mode = w & 1;
-    const double *sp = mode == 0 ? a.specT + a.specT_off[c] : a.specD + a.specD_off[c];
-    const int len = mode == 0 ? (int)(a.specT_off[c + 1] - a.specT_off[c]) : (int)(a.specD_off[c + 1] - a.specD_off[c]);
+    const int c = w >> 1, mode = w & 1, g = gcell(a, c);
+    const double *sp = mode == 0 ? a.specT + a.specT_off[g] : a.specD + a.specD_off[g];
+    const int len = mode == 0 ? (int)(a.specT_off[g + 1] - a.specT_off[g]) : (int)(a.specD_off[g + 1] - a.specD_off[g]);
     const int *grid = mode == 0 ? a.rT_grid : a.rd_grid;
     const int ng = mode == 0 ? nT : nD;
     double *outp = mode == 0 ? a.tailT + (long long)c * nT : a.tailD + (long long)c * nD;
@@ -84,8 +126,9 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
   __syncthreads();
   // (2) table, cell by cell (per-cell values hoisted; 32-bit index arithmetic within a cell)
   for (int c = 0; c < nc; ++c) {
-    const double n2 = a.norm2[c];
-    const long long G = a.shape[4 * c], H = a.shape[4 * c + 1], T = a.shape[4 * c + 2], D = a.shape[4 * c + 3];
+    const int g = gcell(a, c);
+    const double n2 = a.norm2[g];
+    const long long G = a.shape[4 * g], H = a.shape[4 * g + 1], T = a.shape[4 * g + 2], D = a.shape[4 * g + 3];
     const double *tT = a.tailT + (long long)c * nT, *tD = a.tailD + (long long)c * nD;
     double *ec = a.e + (long long)c * per;
     long long *sc = a.s + (long long)c * per;
@@ -114,6 +157,9 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
       best.idx = 0;  // any finite candidate replaces it; keeps the index valid for non-finite tables
       const double *ec = a.e + (long long)c * per;
       const long long *sc = a.s + (long long)c * per;
+      if (a.greedy) {  // lane b walks bit-width b
+        if (lane < nb) best = greedy_walk(ec, sc, lane, nT, nD, lam);
+      } else
       for (int i0 = lane; i0 < per; i0 += 64 * EB) {
         double ev[EB];
         long long sv[EB];
@@ -168,8 +214,8 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
       a.out->iters = iters;
     }
     for (int c = tid; c < nc; c += AT) {
-      a.out_pick[c] = pick[c];
-      if (a.out_err) a.out_err[c] = pick_e[c];
+      a.out_pick[gcell(a, c)] = pick[c];
+      if (a.out_err) a.out_err[gcell(a, c)] = pick_e[c];
     }
     __syncthreads();
   };
@@ -199,7 +245,7 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
     return;
   }
   // keep the feasible end's picks in out_pick while bisecting
-  for (int c = tid; c < nc; c += AT) a.out_pick[c] = pick[c];
+  for (int c = tid; c < nc; c += AT) a.out_pick[gcell(a, c)] = pick[c];
   __syncthreads();
   double hi_lam = hi;
   for (int it = 0; it < 50; ++it) {
@@ -221,13 +267,13 @@ __global__ void __launch_bounds__(AT) alloc_kernel(AllocArgs a) {
     else {
       hi = lam_s;
       hi_lam = hi;
-      for (int c = tid; c < nc; c += AT) a.out_pick[c] = pick[c];
+      for (int c = tid; c < nc; c += AT) a.out_pick[gcell(a, c)] = pick[c];
     }
     __syncthreads();
   }
   // no accept: the feasible end
   for (int c = tid; c < nc; c += AT) {
-    const int i = a.out_pick[c];
+    const int i = a.out_pick[gcell(a, c)];
     pick[c] = i;
     pick_s[c] = a.s[(long long)c * per + i];
     pick_e[c] = a.e[(long long)c * per + i];
@@ -268,18 +314,19 @@ __global__ void __launch_bounds__(AT) alloc_mwg_kernel(AllocArgs a, unsigned spi
 
   // (1) suffix sums of this cell (thread 0: token mode, thread 1: feature mode; sequential order),
   // from LDS copies of the two spectra when they fit
-  const int lenT = (int)(a.specT_off[c + 1] - a.specT_off[c]), lenD = (int)(a.specD_off[c + 1] - a.specD_off[c]);
+  const int g = gcell(a, c);
+  const int lenT = (int)(a.specT_off[g + 1] - a.specT_off[g]), lenD = (int)(a.specD_off[g + 1] - a.specD_off[g]);
   const bool staged = lenT + lenD <= kSpec;
   if (staged) {
-    for (int i = tid; i < lenT; i += AT) spec_l[i] = a.specT[a.specT_off[c] + i];
-    for (int i = tid; i < lenD; i += AT) spec_l[lenT + i] = a.specD[a.specD_off[c] + i];
+    for (int i = tid; i < lenT; i += AT) spec_l[i] = a.specT[a.specT_off[g] + i];
+    for (int i = tid; i < lenD; i += AT) spec_l[lenT + i] = a.specD[a.specD_off[g] + i];
   }
   __syncthreads();
   if (tid < 2) {
     const int mode = tid;
     const double *sp = staged ? (mode == 0 ? spec_l : spec_l + lenT)
-                              : (mode == 0 ? a.specT + a.specT_off[c] : a.specD + a.specD_off[c]);
-    const int len = mode == 0 ? (int)(a.specT_off[c + 1] - a.specT_off[c]) : (int)(a.specD_off[c + 1] - a.specD_off[c]);
+                              : (mode == 0 ? a.specT + a.specT_off[g] : a.specD + a.specD_off[g]);
+    const int len = mode == 0 ? lenT : lenD;
     const int *grid = mode == 0 ? a.rT_grid : a.rd_grid;
     const int ng = mode == 0 ? nT : nD;
     double *outp = mode == 0 ? a.tailT + (long long)c * nT : a.tailD + (long long)c * nD;
@@ -309,8 +356,8 @@ __global__ void __launch_bounds__(AT) alloc_mwg_kernel(AllocArgs a, unsigned spi
   __syncthreads();
   // (2) this cell's table
   {
-    const double n2 = a.norm2[c];
-    const long long G = a.shape[4 * c], H = a.shape[4 * c + 1], T = a.shape[4 * c + 2], D = a.shape[4 * c + 3];
+    const double n2 = a.norm2[g];
+    const long long G = a.shape[4 * g], H = a.shape[4 * g + 1], T = a.shape[4 * g + 2], D = a.shape[4 * g + 3];
     const double *tT = a.tailT + (long long)c * nT, *tD = a.tailD + (long long)c * nD;
     for (int rem = tid; rem < per; rem += AT) {
       const int bi = rem / (nT * nD), ti = (rem / nD) % nT, di = rem % nD;
@@ -336,13 +383,17 @@ __global__ void __launch_bounds__(AT) alloc_mwg_kernel(AllocArgs a, unsigned spi
     best.cost = INFINITY;
     best.s = LLONG_MAX;
     best.idx = 0;
-    for (int i = tid; i < per; i += AT) {
-      const long long sv = sc[i];
-      const double cost = __dadd_rn(ec[i], __dmul_rn(lam, (double)sv));
-      if (cost < best.cost || (cost == best.cost && sv < best.s)) {
-        best.cost = cost;
-        best.s = sv;
-        best.idx = i;
+    if (a.greedy) {  // thread b walks bit-width b
+      if (tid < nb) best = greedy_walk(ec, sc, tid, nT, nD, lam);
+    } else {
+      for (int i = tid; i < per; i += AT) {
+        const long long sv = sc[i];
+        const double cost = __dadd_rn(ec[i], __dmul_rn(lam, (double)sv));
+        if (cost < best.cost || (cost == best.cost && sv < best.s)) {
+          best.cost = cost;
+          best.s = sv;
+          best.idx = i;
+        }
       }
     }
     for (int o = 32; o > 0; o >>= 1) {
@@ -412,8 +463,8 @@ __global__ void __launch_bounds__(AT) alloc_mwg_kernel(AllocArgs a, unsigned spi
   };
   auto finish = [&](int status, double lam, int iters, int pick) {
     if (tid == 0) {
-      a.out_pick[c] = pick;
-      if (a.out_err) a.out_err[c] = ec[pick];
+      a.out_pick[g] = pick;
+      if (a.out_err) a.out_err[g] = ec[pick];
       if (c == 0) {
         a.out->status = fail_s ? kAllocEsync : status;
         a.out->lambda = lam;

@@ -37,6 +37,9 @@ struct AllocArgs {
   int n_bits;
   const double *eps2;         // device [9]
   double budget;
+  int greedy;                 // per-cell minimiser: 0 exact argmin over the grid, 1 the greedy rank search
+  int cell_first, cell_step;  // cell k of this run is cell cell_first + k * cell_step of shape, the
+                              // spectra, norm2, out_pick and out_err (scratch is indexed by k)
   double *tailT;              // scratch [n_cells][n_rT]
   double *tailD;              // scratch [n_cells][n_rd]
   double *e;                  // scratch [n_cells][n_bits*n_rT*n_rd]

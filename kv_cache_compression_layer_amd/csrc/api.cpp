@@ -135,6 +135,13 @@ void fill_bits_eps(const jolt_params *p, int D, Plan &pl) {
   }
 }
 
+// jolt_alloc_variant flags: known ones only, uniform ranks alone
+void check_variant(int v) {
+  JOLT_REQUIRE(v >= 0 && (v & ~(JOLT_ALLOC_GREEDY | JOLT_ALLOC_KV_DECOUPLED | JOLT_ALLOC_UNIFORM_RANKS)) == 0 &&
+                   (!(v & JOLT_ALLOC_UNIFORM_RANKS) || v == JOLT_ALLOC_UNIFORM_RANKS),
+               JOLT_EINVAL, "alloc_variant: unknown flags, or uniform ranks combined with another variant");
+}
+
 Plan make_plan(const jolt_cache_desc *d, const jolt_params *p) {
   JOLT_REQUIRE(d && p, JOLT_EINVAL, "null descriptor or params");
   Plan pl;
@@ -164,6 +171,7 @@ Plan make_plan(const jolt_cache_desc *d, const jolt_params *p) {
   pl.c = dtype_bytes(pl.dtype);
   pl.mode = p->mode;
   JOLT_REQUIRE(pl.mode == JOLT_EXACT || pl.mode == JOLT_FLASH, JOLT_EINVAL, "bad mode");
+  check_variant(p->alloc_variant);
   JOLT_REQUIRE(p->target_ratio > 1.0 && isfinite(p->target_ratio), JOLT_EINVAL, "target_ratio must exceed 1");
   pl.C = p->target_ratio;
   check_grid(p->rT_grid, p->n_rT, "rT_grid", pl.rT);
@@ -795,10 +803,12 @@ struct AllocDev {
   double *eps2;
 };
 
-void run_allocation(int nc, const AllocDev &ad, int elem_bytes, const double *specT, const double *specD,
-                    const double *norm2, int n_rT, int n_rd, int n_bits, double budget, Bufs &b, hipStream_t st) {
+// One bisection run over n cells (cell k is cell first + k * step of the tables; its pick lands there).
+void run_allocation(int n, int first, int step, int greedy, const AllocDev &ad, int n_rT, int n_rd, int n_bits,
+                    int elem_bytes, const double *specT, const double *specD, const double *norm2, double budget,
+                    Bufs &b, hipStream_t st) {
   AllocArgs a;
-  a.n_cells = nc;
+  a.n_cells = n;
   a.shape = ad.shape;
   a.elem_bytes = elem_bytes;
   a.specT = specT; a.specT_off = ad.offT;
@@ -809,9 +819,105 @@ void run_allocation(int nc, const AllocDev &ad, int elem_bytes, const double *sp
   a.bits = ad.bits; a.n_bits = n_bits;
   a.eps2 = ad.eps2;
   a.budget = budget;
+  a.greedy = greedy;
+  a.cell_first = first;
+  a.cell_step = step;
   a.tailT = b.tailT; a.tailD = b.tailD; a.e = b.tab_e; a.s = b.tab_s;
   a.out_pick = b.pick; a.out_err = b.perr; a.out = b.aout;
   run_alloc(a, st);
+}
+
+// An allocation read back: per cell the full-table index (b-major, then r_T, then r_d) and its
+// distortion e, the multiplier(s) and the status.
+struct AllocHost {
+  std::vector<int> pick;
+  std::vector<double> perr;
+  double lambda[2] = {0.0, 0.0};  // K/V-decoupled: the keys' and the values' multipliers
+  int status = 0;                  // 0 or JOLT_EINFEASIBLE
+};
+
+// The allocation variant v (jolt_alloc_variant flags) over the nc cells whose spectra, norms and
+// shapes (shape: host copy of the device table) are given, read back to the host.  Joint and greedy:
+// one bisection.  K/V-decoupled: one bisection over the even (key) cells and one over the odd (value)
+// cells, each under the budget's share of their dense bytes |g| n_h T d_h c.  Uniform ranks: one
+// bisection over the bit-widths per (r_T, r_d) grid pair (every cell at that pair); the feasible pair of
+// smallest total error wins, ties to fewer bytes, then the earlier pair.
+AllocHost allocate_cells(int v, int nc, const AllocDev &ad, const std::vector<int> &shape, int n_rT, int n_rd,
+                         int n_bits, int elem_bytes, const double *specT, const double *specD, const double *norm2,
+                         double budget, Bufs &b, hipStream_t st) {
+  check_variant(v);
+  const int greedy = (v & JOLT_ALLOC_GREEDY) ? 1 : 0;
+  AllocHost r;
+  r.pick.resize(nc);
+  r.perr.resize(nc);
+  auto read_out = [&](AllocOut &ao) {
+    HIP_TRY(hipMemcpyAsync(&ao, b.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    // a lapsed wait in any workgroup (not only the one that writes the status) voids the picks
+    JOLT_REQUIRE(ao.status != kAllocEsync && ao.err == 0u, JOLT_EHIP, kAllocEsyncMsg);
+  };
+  auto read_picks = [&]() {
+    HIP_TRY(hipMemcpyAsync(r.pick.data(), b.pick, (size_t)nc * 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipMemcpyAsync(r.perr.data(), b.perr, (size_t)nc * 8, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+  };
+  if (v & JOLT_ALLOC_UNIFORM_RANKS) {
+    bool found = false;
+    double bestE = 0.0;
+    long long bestS = 0;
+    r.status = JOLT_EINFEASIBLE;
+    for (int iT = 0; iT < n_rT; ++iT)
+      for (int iD = 0; iD < n_rd; ++iD) {
+        AllocDev one = ad;
+        one.rT += iT;
+        one.rd += iD;
+        run_allocation(nc, 0, 1, 0, one, 1, 1, n_bits, elem_bytes, specT, specD, norm2, budget, b, st);
+        AllocOut ao;
+        read_out(ao);
+        if (ao.status != 0) continue;
+        if (found && !(ao.E < bestE || (ao.E == bestE && ao.S < bestS))) continue;
+        found = true;
+        bestE = ao.E;
+        bestS = ao.S;
+        r.lambda[0] = r.lambda[1] = ao.lambda;
+        r.status = 0;
+        read_picks();
+        for (int c = 0; c < nc; ++c) r.pick[c] = (r.pick[c] * n_rT + iT) * n_rd + iD;  // bit index -> table
+      }
+    return r;
+  }
+  if (v & JOLT_ALLOC_KV_DECOUPLED) {
+    JOLT_REQUIRE(nc >= 2, JOLT_EINVAL, "alloc_variant: K/V-decoupled allocation needs a key and a value cell");
+    long long dense[2] = {0, 0};
+    for (int c = 0; c < nc; ++c)
+      dense[c & 1] += (long long)shape[4 * c] * shape[4 * c + 1] * shape[4 * c + 2] * shape[4 * c + 3] * elem_bytes;
+    const double total = (double)(dense[0] + dense[1]);
+    for (int kind = 0; kind < 2; ++kind) {
+      const int n = (nc - kind + 1) / 2;
+      run_allocation(n, kind, 2, greedy, ad, n_rT, n_rd, n_bits, elem_bytes, specT, specD, norm2,
+                     budget * ((double)dense[kind] / total), b, st);
+      AllocOut ao;
+      read_out(ao);
+      r.lambda[kind] = ao.lambda;
+      if (ao.status != 0) r.status = ao.status;
+    }
+    read_picks();
+    return r;
+  }
+  run_allocation(nc, 0, 1, greedy, ad, n_rT, n_rd, n_bits, elem_bytes, specT, specD, norm2, budget, b, st);
+  AllocOut ao;
+  read_out(ao);
+  r.lambda[0] = r.lambda[1] = ao.lambda;
+  r.status = ao.status;
+  read_picks();
+  return r;
+}
+
+// The multiplier(s) to the caller: one double, two (keys', values') for a K/V-decoupled allocation.
+void put_lambda(double *h_lambda, int variant, const AllocHost &r) {
+  if (!h_lambda) return;
+  h_lambda[0] = r.lambda[0];
+  if (variant & JOLT_ALLOC_KV_DECOUPLED) h_lambda[1] = r.lambda[1];
 }
 
 struct Section {
@@ -1305,6 +1411,7 @@ int allocate_on(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_bytes
                  JOLT_EINVAL, "null argument");
     JOLT_REQUIRE(elem_bytes == 2 || elem_bytes == 4, JOLT_EINVAL, "elem_bytes must be 2 or 4");
     JOLT_REQUIRE(budget_bytes > 0 && isfinite(budget_bytes), JOLT_EINVAL, "budget must be positive");
+    check_variant(params->alloc_variant);
     hipStream_t st = S(stream);
     Plan pl;
     check_grid(params->rT_grid, params->n_rT, "rT_grid", pl.rT);
@@ -1342,15 +1449,10 @@ int allocate_on(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_bytes
     upload_alloc_tables(u, pl, shape, offT, offD, o);
     upload(b, u, st);
     AllocDev ad = bind_alloc(b.params, o);
-    run_allocation(n_cells, ad, elem_bytes, d_specT, d_specD, d_norm2, (int)pl.rT.size(), (int)pl.rd.size(),
-                   (int)pl.bits.size(), budget_bytes, b, st);
-    std::vector<int> pick(n_cells);
-    std::vector<double> perr(n_cells);
-    AllocOut ao;
-    HIP_TRY(hipMemcpyAsync(pick.data(), b.pick, n_cells * 4, hipMemcpyDeviceToHost, st));
-    HIP_TRY(hipMemcpyAsync(perr.data(), b.perr, n_cells * 8, hipMemcpyDeviceToHost, st));
-    HIP_TRY(hipMemcpyAsync(&ao, b.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
-    HIP_TRY(hipStreamSynchronize(st));
+    AllocHost r = allocate_cells(params->alloc_variant, n_cells, ad, shape, (int)pl.rT.size(), (int)pl.rd.size(),
+                                 (int)pl.bits.size(), elem_bytes, d_specT, d_specD, d_norm2, budget_bytes, b, st);
+    const std::vector<int> &pick = r.pick;
+    const std::vector<double> &perr = r.perr;
     const int nT = (int)pl.rT.size(), nD = (int)pl.rd.size();
     long long off = 0;
     for (int c = 0; c < n_cells; ++c) {
@@ -1366,12 +1468,10 @@ int allocate_on(int32_t n_cells, const int32_t *h_cell_shape, int32_t elem_bytes
       p.section_bytes = sec.end;
       off += sec.end;
     }
-    if (h_lambda) *h_lambda = ao.lambda;
-    // a lapsed wait in any workgroup (not only the one that writes the status) voids the picks
-    JOLT_REQUIRE(ao.status != kAllocEsync && ao.err == 0u, JOLT_EHIP, kAllocEsyncMsg);
-    if (ao.status != 0) {
+    put_lambda(h_lambda, params->alloc_variant, r);
+    if (r.status != 0) {
       set_error("allocation infeasible: the smallest picks exceed the budget");
-      return (int)ao.status;
+      return r.status;
     }
     return 0;
 }
@@ -1603,24 +1703,20 @@ int compress_parts(const void *d_K, const void *d_V, const jolt_cache_desc *desc
   long long dense = 0;
   for (int cg = 0; cg < nc; ++cg) dense += (long long)shape[4 * cg] * H * T * D * c;
   const double budget = (double)dense / p0.C;
+  AllocHost r;
   {
     Stage prof("allocate", st);
-    run_allocation(nc, ad, c, L.specT, L.specD, L.norm2, (int)p0.rT.size(), (int)p0.rd.size(), (int)p0.bits.size(),
-                   budget, L.ab, st);
+    r = allocate_cells(params->alloc_variant, nc, ad, shape, (int)p0.rT.size(), (int)p0.rd.size(), (int)p0.bits.size(), c,
+                       L.specT, L.specD, L.norm2, budget, L.ab, st);
   }
-  std::vector<int> pick(nc);
-  std::vector<double> n2(nc), perr(nc);
-  AllocOut ao;
-  HIP_TRY(hipMemcpyAsync(pick.data(), L.ab.pick, nc * 4, hipMemcpyDeviceToHost, st));
+  const std::vector<int> &pick = r.pick;
+  std::vector<double> n2(nc);
   HIP_TRY(hipMemcpyAsync(n2.data(), L.norm2, nc * 8, hipMemcpyDeviceToHost, st));
-  HIP_TRY(hipMemcpyAsync(&ao, L.ab.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
-  HIP_TRY(hipMemcpyAsync(perr.data(), L.ab.perr, nc * 8, hipMemcpyDeviceToHost, st));
   HIP_TRY(hipStreamSynchronize(st));
   for (int cg = 0; cg < nc; ++cg) JOLT_REQUIRE(isfinite(n2[cg]), JOLT_ENONFINITE, "non-finite ||X||^2 in a cell");
-  for (int cg = 0; cg < nc; ++cg) JOLT_REQUIRE(isfinite(perr[cg]), JOLT_ENONFINITE, "non-finite spectrum in a cell");
-  if (h_lambda) *h_lambda = ao.lambda;
-  JOLT_REQUIRE(ao.status != kAllocEsync && ao.err == 0u, JOLT_EHIP, kAllocEsyncMsg);
-  JOLT_REQUIRE(ao.status == 0, JOLT_EINFEASIBLE, "allocation infeasible: the smallest picks exceed the budget");
+  for (int cg = 0; cg < nc; ++cg) JOLT_REQUIRE(isfinite(r.perr[cg]), JOLT_ENONFINITE, "non-finite spectrum in a cell");
+  put_lambda(h_lambda, params->alloc_variant, r);
+  JOLT_REQUIRE(r.status == 0, JOLT_EINFEASIBLE, "allocation infeasible: the smallest picks exceed the budget");
   const int nTg = (int)p0.rT.size(), nDg = (int)p0.rd.size();
   std::vector<CellPick> cp(nc);
   long long off = 0;
@@ -1636,7 +1732,7 @@ int compress_parts(const void *d_K, const void *d_V, const jolt_cache_desc *desc
     jolt_pick &h = h_picks[cg];
     h.rT = p.rT; h.rd = p.rd; h.bits = p.bits; h.pad = 0;
     h.bytes = eq1_bytes(G, H, T, D, c, p.rT, p.rd, p.bits);
-    h.err_pred = perr[cg];
+    h.err_pred = r.perr[cg];
     h.offset = p.off;
     h.section_bytes = p.sec.end;
   }
@@ -1994,25 +2090,20 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
     AllocDev ad = bind_alloc(b.params, o);
     const long long dense = (long long)nb * pl.cell_elems() * pl.c;
     const double budget = (double)dense / pl.C;
+    AllocHost r;
     {
       Stage prof("allocate", st);
-      run_allocation(nb, ad, pl.c, b.specT, b.specD, b.norm2, (int)pl.rT.size(), (int)pl.rd.size(),
-                     (int)pl.bits.size(), budget, b, st);
+      r = allocate_cells(params->alloc_variant, nb, ad, shape, (int)pl.rT.size(), (int)pl.rd.size(),
+                         (int)pl.bits.size(), pl.c, b.specT, b.specD, b.norm2, budget, b, st);
     }
-    std::vector<int> pick(nb);
+    const std::vector<int> &pick = r.pick;
     std::vector<double> n2(nb);
-    AllocOut ao;
-    HIP_TRY(hipMemcpyAsync(pick.data(), b.pick, nb * 4, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipMemcpyAsync(n2.data(), b.norm2, nb * 8, hipMemcpyDeviceToHost, st));
-    HIP_TRY(hipMemcpyAsync(&ao, b.aout, sizeof(ao), hipMemcpyDeviceToHost, st));
-    std::vector<double> perr(nb);
-    HIP_TRY(hipMemcpyAsync(perr.data(), b.perr, nb * 8, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipStreamSynchronize(st));
     for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(n2[c]), JOLT_ENONFINITE, "non-finite ||X||^2 in a cell");
-    for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(perr[c]), JOLT_ENONFINITE, "non-finite spectrum in a cell");
-    if (h_lambda) *h_lambda = ao.lambda;
-    JOLT_REQUIRE(ao.status != kAllocEsync && ao.err == 0u, JOLT_EHIP, kAllocEsyncMsg);
-    JOLT_REQUIRE(ao.status == 0, JOLT_EINFEASIBLE, "allocation infeasible: the smallest picks exceed the budget");
+    for (int c = 0; c < nb; ++c) JOLT_REQUIRE(isfinite(r.perr[c]), JOLT_ENONFINITE, "non-finite spectrum in a cell");
+    put_lambda(h_lambda, params->alloc_variant, r);
+    JOLT_REQUIRE(r.status == 0, JOLT_EINFEASIBLE, "allocation infeasible: the smallest picks exceed the budget");
     const int nT = (int)pl.rT.size(), nD = (int)pl.rd.size();
     std::vector<CellPick> cp(nb);
     long long off = 0;
@@ -2031,7 +2122,7 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
       jolt_pick &h = h_picks[c];
       h.rT = p.rT; h.rd = p.rd; h.bits = p.bits; h.pad = 0;
       h.bytes = eq1_bytes(pl.G, pl.H, pl.T, pl.D, pl.c, p.rT, p.rd, p.bits);
-      h.err_pred = perr[c];
+      h.err_pred = r.perr[c];
       h.offset = p.off;
       h.section_bytes = p.sec.end;
     }

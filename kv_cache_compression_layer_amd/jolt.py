@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libjolt.so")
 
 F16, BF16, F32 = 0, 1, 2
 EXACT, FLASH = 0, 1
+ALLOC_JOINT, ALLOC_GREEDY, ALLOC_KV_DECOUPLED, ALLOC_UNIFORM_RANKS = 0, 1, 2, 4
 STATUS = {0: "JOLT_OK", -1: "JOLT_EINVAL", -2: "JOLT_EINFEASIBLE", -3: "JOLT_EWORKSPACE", -4: "JOLT_EHIP",
           -5: "JOLT_ENONFINITE", -6: "JOLT_EBUFFER"}
 TORCH_DTYPE = {F16: torch.float16, BF16: torch.bfloat16, F32: torch.float32}
@@ -46,7 +47,7 @@ class Params(ctypes.Structure):
                 ("rd_grid", ctypes.POINTER(ctypes.c_int32)), ("n_rd", ctypes.c_int32),
                 ("bits", ctypes.POINTER(ctypes.c_int32)), ("n_bits", ctypes.c_int32),
                 ("eps2", ctypes.POINTER(ctypes.c_double)), ("target_ratio", ctypes.c_double),
-                ("rot_seed", ctypes.c_uint64), ("sketch_seed", ctypes.c_uint64)]
+                ("rot_seed", ctypes.c_uint64), ("sketch_seed", ctypes.c_uint64), ("alloc_variant", ctypes.c_int32)]
 
 
 class Pick(ctypes.Structure):
@@ -127,7 +128,8 @@ class Config:
     """Cache descriptor + parameters, holding the ctypes arrays alive."""
 
     def __init__(self, n_seq, n_layers, n_heads, n_tokens, d_head, dtype, group_start, mode, rT_grid, rd_grid,
-                 bits, target_ratio, oversample=10, power_iters=1, qcap=0, eps2=None, rot_seed=0, sketch_seed=0):
+                 bits, target_ratio, oversample=10, power_iters=1, qcap=0, eps2=None, rot_seed=0, sketch_seed=0,
+                 alloc_variant=0):
         self._gs = _i32arr(group_start)
         self.desc = CacheDesc(n_seq, n_layers, n_heads, n_tokens, d_head, dtype, len(group_start) - 1, self._gs)
         self._rT, self._rd, self._bits = _i32arr(rT_grid), _i32arr(rd_grid), _i32arr(bits)
@@ -138,7 +140,8 @@ class Config:
                 e[int(b)] = float(v)
             self._eps = (ctypes.c_double * 9)(*e.tolist())
         self.params = Params(mode, oversample, power_iters, qcap, self._rT, len(rT_grid), self._rd, len(rd_grid),
-                             self._bits, len(bits), self._eps, float(target_ratio), rot_seed, sketch_seed)
+                             self._bits, len(bits), self._eps, float(target_ratio), rot_seed, sketch_seed,
+                             int(alloc_variant))
         self.n_cells = n_seq * (len(group_start) - 1) * 2
 
     def workspace_bytes(self):
@@ -179,10 +182,10 @@ def compress(K, V, cfg, out=None, ws=None):
     if out is None:
         out = torch.empty(cfg.output_bytes(), dtype=torch.uint8, device=K.device)
     picks = (Pick * cfg.n_cells)()
-    lam = ctypes.c_double(0.0)
+    lam = (ctypes.c_double * 2)(0.0, 0.0)  # K/V-decoupled allocations return two multipliers
     _check(lib.jolt_compress(_ptr(K), _ptr(V), ctypes.byref(cfg.desc), ctypes.byref(cfg.params), _ptr(out),
-                             out.numel(), _ptr(ws), ws.numel(), picks, ctypes.byref(lam), _stream()))
-    return out, [_pick_dict(p) for p in picks], lam.value
+                             out.numel(), _ptr(ws), ws.numel(), picks, lam, _stream()))
+    return out, [_pick_dict(p) for p in picks], _lam(lam, cfg.params.alloc_variant)
 
 
 def _pick_dict(p):
@@ -231,13 +234,18 @@ def spectra(K, V, cfg, n_vec=0, ws=None):
     return specT, specD, norm2, UT
 
 
+def _lam(lam, variant):
+    return (lam[0], lam[1]) if variant & ALLOC_KV_DECOUPLED else lam[0]
+
+
 def allocate(cell_shapes, elem_bytes, specT_list, specD_list, norm2, rT_grid, rd_grid, bits, budget, eps2=None,
-             device="cuda", static_scratch=False):
+             device="cuda", static_scratch=False, alloc_variant=0):
     """Lagrangian allocation on given spectra (lists of 1-D float64 arrays, one per cell).
 
     static_scratch=True calls jolt_allocate_static (no workspace: the library's fixed device scratch)."""
     lib = load()
-    cfg = Config(1, 1, 1, 1, 64, F16, [0, 1], EXACT, rT_grid, rd_grid, bits, 2.0, eps2=eps2)
+    cfg = Config(1, 1, 1, 1, 64, F16, [0, 1], EXACT, rT_grid, rd_grid, bits, 2.0, eps2=eps2,
+                 alloc_variant=alloc_variant)
     n = len(cell_shapes)
     shp = (ctypes.c_int32 * (4 * n))(*[int(v) for s in cell_shapes for v in s])
     offT = np.concatenate([[0], np.cumsum([len(s) for s in specT_list])]).astype(np.int64)
@@ -246,22 +254,22 @@ def allocate(cell_shapes, elem_bytes, specT_list, specD_list, norm2, rT_grid, rd
     dD = torch.from_numpy(np.concatenate(specD_list).astype(np.float64)).to(device)
     dn = torch.from_numpy(np.asarray(norm2, dtype=np.float64)).to(device)
     picks = (Pick * n)()
-    lam = ctypes.c_double(0.0)
+    lam = (ctypes.c_double * 2)(0.0, 0.0)  # K/V-decoupled allocations return two multipliers
     if static_scratch:
         status = lib.jolt_allocate_static(n, shp, int(elem_bytes), _ptr(dT),
                                           offT.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr(dD),
                                           offD.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr(dn),
-                                          ctypes.byref(cfg.params), float(budget), picks, ctypes.byref(lam),
+                                          ctypes.byref(cfg.params), float(budget), picks, lam,
                                           _stream())
-        return status, [_pick_dict(p) for p in picks], lam.value
+        return status, [_pick_dict(p) for p in picks], _lam(lam, cfg.params.alloc_variant)
     per = (len(set(bits) | {0})) * len(rT_grid) * len(rd_grid)
     ws = torch.empty(n * per * 16 + n * (len(rT_grid) + len(rd_grid)) * 8 + n * 64 + (1 << 20), dtype=torch.uint8,
                      device=device)
     status = lib.jolt_allocate(n, shp, int(elem_bytes), _ptr(dT), offT.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                _ptr(dD), offD.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _ptr(dn),
-                               ctypes.byref(cfg.params), float(budget), picks, ctypes.byref(lam), _ptr(ws),
+                               ctypes.byref(cfg.params), float(budget), picks, lam, _ptr(ws),
                                ws.numel(), _stream())
-    return status, [_pick_dict(p) for p in picks], lam.value
+    return status, [_pick_dict(p) for p in picks], _lam(lam, cfg.params.alloc_variant)
 
 
 def encode_residual(X, UT, core, Ud, rT, rd, bits, rot_seed=0):

@@ -655,7 +655,8 @@ def compress(K, V, group_start, dtype, params, keep=False):
 
     K, V: arrays (n_seq, L, H, T, D) in the storage dtype (bf16 as raw uint16).
     params: dict(mode 'exact'|'flash', oversample, power_iters, qcap (None -> Eq. 5),
-            rT_grid, rd_grid, bits, eps2 {b: value}, target_ratio, rot_seed, sketch_seed).
+            rT_grid, rd_grid, bits, eps2 {b: value}, target_ratio, rot_seed, sketch_seed,
+            alloc 'joint' (default) | 'greedy' | 'kv_decoupled' | 'uniform').
     """
     c = DTYPE_BYTES[dtype]
     n_seq, L, H, T, D = K.shape
@@ -691,9 +692,18 @@ def compress(K, V, group_start, dtype, params, keep=False):
                       "specD": specD, "U": U, "X": X if keep else None})
     dense = sum(sh.R * sh.D * c for sh in shapes)
     budget = dense / C
-    al = allocate(tables, budget)
-    result = {"status": al["status"], "lam": al["lam"], "budget": budget, "dense_bytes": dense,
-              "S": al["S"], "E_pred": al["E"], "iters": al["iters"], "cells": []}
+    variant = params.get("alloc", "joint")
+    nR, nD = len(params["rT_grid"]), len(params["rd_grid"])
+    if variant == "greedy":
+        al = allocate_greedy(tables, budget, nR, nD)
+    elif variant == "kv_decoupled":
+        al = allocate_kv_decoupled(tables, budget, [sh.R * sh.D * c for sh in shapes])
+    elif variant == "uniform":
+        al = allocate_uniform_ranks(tables, budget, nR, nD)
+    else:
+        al = allocate(tables, budget)
+    result = {"status": al["status"], "lam": al.get("lam"), "budget": budget, "dense_bytes": dense,
+              "S": al.get("S"), "E_pred": al.get("E"), "iters": al.get("iters"), "cells": []}
     if al["status"] != 0:
         return result
     encs = []
