@@ -222,9 +222,9 @@ struct Bufs {
   double *mwg;  // exchange scratch of the multi-workgroup tridiagonalisation (FlashJoLT B B^T)
   float *amax;  // [9][n_cells]: slot k of cell c at amax[k * am_ld + c]
   int am_ld;
-  // FlashJoLT with power iterations: the final basis is kept implicit (Q = Y R^{-1} is never formed).
-  // The fit then reads Y ([T][ell_ld], bufA2) with its |max| basis_am, R^{-T} (RinvT) and P' = Y^T X
-  // (P2); Wt holds W~ = R^{-1} W as rows.  basis_implicit = 0: bufA2 holds an orthonormal Q.
+  // FlashJoLT keeps the final basis implicit (Q = Y R^{-1} is never formed).  The fit then reads Y
+  // ([T][ell_ld], bufA2) with its |max| basis_am, R^{-T} (RinvT) and P' = Y^T X (P2); Wt holds
+  // W~ = R^{-1} W as rows.  basis_implicit = 0: bufA2 holds an orthonormal Q.
   int basis_implicit;
   float *basis_am;
   float *Wt;
@@ -255,6 +255,13 @@ int nsplit_for(long long K, long long tiles, int batch, long long min_chunk) {
 }
 
 long long tiles_of(long long M, long long N) { return ((M + 127) / 128) * ((N + 127) / 128); }
+
+// K splits of a Gram of `rows` rows on the DMA plane kernel (192 x 192 tiles, the upper triangle's
+// tiles working): about 2048 working blocks, K chunks of at least 1024
+int gram_plane_splits(long long rows, long long K, int batch) {
+  const long long t = (rows + 191) / 192;
+  return nsplit_for(K, t * (t + 1) / 2, batch, 1024);
+}
 
 // The spectra of the cells can run as kViews independent chains of consecutive cells on their own
 // streams, each with its own split-K scratch.  Measured on the 8B shape, two chains gained nothing
@@ -300,6 +307,8 @@ long long part_elems_for(const Plan &pl, int kmax, int nb) {
     pe = std::max(pe, (long long)nb * ns * pl.ell * pl.ell_ld);
     int ns2 = nsplit_for(pl.M, tiles_of(pl.ell, pl.ell), nb, 1024);
     pe = std::max(pe, (long long)nb * ns2 * pl.ell * pl.ell_ld);
+    int ns3 = gram_plane_splits(pl.ell, pl.T, nb);
+    pe = std::max(pe, (long long)nb * ns3 * pl.ell * rup(pl.ell, 16));
   } else {
     int ns = nsplit_for(pl.M, tiles_of(pl.T, pl.T), nb, 1024);
     pe = std::max(pe, (long long)nb * ns * pl.T * pl.T_ld);
@@ -453,6 +462,30 @@ void gram_f32(const Plan &pl, Bufs &b, const float *X, long long ldx, long long 
   reduce_splits(b.part, g.c_bs, g.c_split, ns, 0, rows, rows, rl, out, true, out_bs, ldo, batch, st);
 }
 
+// gram_f32 on rows already split into their 16-bit planes (P planes [rows][ld] at plane stride ps, batch
+// stride bs, split with the scale of amax): the same products on the DMA plane kernel.  False (nothing
+// launched) when that kernel does not take the shape.
+bool gram_planes(const Plan &pl, Bufs &b, const uint16_t *P, long long ld, long long ps, long long bs, int rows, int K,
+                 const float *amax, double *out, long long out_bs, int ldo, int batch, hipStream_t st) {
+  const int np = pl.fp32_planes();
+  GemmArgs g = ga();
+  g.A = P; g.B = P;
+  g.M = rows; g.N = rows; g.K = K;
+  g.a_ld = g.b_ld = ld; g.a_ps = g.b_ps = ps; g.a_bs = g.b_bs = bs;
+  g.a_amax = amax; g.b_amax = amax; g.ab_amax_bs = 1;
+  int ns = gram_plane_splits(rows, K, batch);
+  g.k_chunk = (int)rup((K + ns - 1) / ns, 32);
+  ns = (int)((K + g.k_chunk - 1) / g.k_chunk);
+  const long long rl = rup(rows, 16);
+  JOLT_REQUIRE((long long)batch * ns * rows * rl <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
+  g.C = b.part; g.c_ld = rl; g.c_split = (long long)rows * rl; g.c_bs = (long long)ns * rows * rl;
+  g.m_fastest = 1;
+  g.tri = 1;
+  if (!gemm_dma(pl.xmf(), np, np, g, batch, ns, st)) return false;
+  reduce_splits(b.part, g.c_bs, g.c_split, ns, 0, rows, rows, rl, out, true, out_bs, ldo, batch, st);
+  return true;
+}
+
 // --------------------------------------------------------------------------- spectra stage
 void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
   Stage prof("feature_gram", st);
@@ -534,22 +567,24 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       gemm(pl.xmf(), a_src, true, pl.xsrc(), true, g, nkv, 1, st);
     });
   };
-  // P^T = Q^T X_(T) (ell x M) and P = (P^T)^T.  K = T is long: the product is split along K
-  // (more, shorter blocks fill the last wave of the grid) and the partials are summed in fixed
-  // order by the reduction, which writes both layouts and max |P|.  On the plane path Q^T is
-  // first split into its 16-bit planes.
+  // The 16-bit planes of a basis Y^T (fp32 [ell][T_ld]), read by its Gram and its projection.
+  const bool tplanes = dma_ok && T % 32 == 0;
+  auto split_basis = [&](const float *Yt, const float *am) {
+    if (!tplanes) return;
+    Stage prof_s("split_planes", st);
+    split_planes(pl.xmf(), Yt, ell * Tld, Tld, (int)ell, (int)T, (int)T, b.pln, P32 * ell * Tld, ell * Tld, Tld, am, 1,
+                 nb, st);
+  };
+  // P'^T = Y^T X_(T) (ell x M) and P' = (P'^T)^T, from the planes of Y^T when they are in b.pln.  K = T
+  // is long: the product is split along K (more, shorter blocks fill the last wave of the grid) and
+  // the partials are summed in fixed order by the reduction, which writes both layouts and max |P'|.
   const int pns = project_splits(pl);
   auto project = [&](const float *Qt, const float *q_amax, float *c_amax) {
     if (xready) {
       HIP_TRY(hipStreamWaitEvent(st, xready, 0));
       xready = nullptr;
     }
-    const bool planes = dma_ok && T % 32 == 0;
-    if (planes) {
-      Stage prof_s("split_planes", st);
-      split_planes(pl.xmf(), Qt, ell * Tld, Tld, (int)ell, (int)T, (int)T, b.pln, P32 * ell * Tld, ell * Tld, Tld,
-                   q_amax, 1, nb, st);
-    }
+    const bool planes = tplanes;
     Stage prof("project_gemm", st);
     GemmArgs g = ga();
     g.A = Qt; g.M = (int)ell; g.N = (int)Mf; g.K = (int)T;
@@ -584,54 +619,55 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     reduce_splits_dual(b.part, g.c_bs, g.c_split, ns, (int)ell, (int)Mf, Mf, b.Pt, ell * Mf, Mf, b.P2, Mf * ld, ld,
                        c_amax, nb, st);
   };
-  // R from the Gram of the rows of Yt, then Q = Y R^{-1} in both layouts
   struct Pair {
     float *T, *R, *am;
   };
   Pair pa{b.bufA, b.bufA2, amY}, pb{b.bufB, b.bufB2, amQ};
-  // Q is computed transposed, Q^T = R^{-T} Y^T (A = R^{-T} is lower triangular: each row tile
-  // stops its k loop at its last row), so the main output [ell][T_ld] has long rows; Q itself
-  // ([T][ell_ld]) is the epilogue's transposed output.  t_only: the last pass writes Q^T alone,
-  // for a basis that only the next projection reads.
-  auto cholqr = [&](Pair y, Pair q, int passes, bool t_only = false) -> Pair {
-    Stage prof("cholqr_tall", st);
-    for (int p = 0; p < passes; ++p) {
-      gram_f32(pl, b, y.T, Tld, ell * Tld, (int)ell, (int)T, y.am, b.G64, ell * ell, (int)ell, nb, st);
-      chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, chol_scratch_doubles((int)ell), b.RinvT, ell * ld, (int)ld, amR, st);
-      fill_f32(q.am, nb, 0.f, st);
-      GemmArgs g = ga();
-      g.A = b.RinvT; g.a_ld = ld; g.a_bs = ell * ld; g.a_amax = amR;
-      g.B = y.R; g.b_ld = ld; g.b_bs = T * ld; g.b_amax = y.am;
-      g.ab_amax_bs = 1;
-      g.M = (int)ell; g.N = (int)T; g.K = (int)ell;
-      g.C = q.T; g.c_ld = Tld; g.c_bs = ell * Tld;
-      if (!(t_only && p + 1 == passes)) {
-        g.C2 = q.R; g.c2_ld = ld; g.c2_bs = T * ld;
-      }
-      g.c_amax = q.am;
-      g.m_fastest = 1;
-      g.tri = 4;
-      gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
-      std::swap(y, q);
-    }
-    return y;
-  };
-
-  // R alone from the Gram of the rows of Yt (the final basis of a power iteration stays implicit)
+  // R^{-T} and max |R^{-T}| (b.RinvT, amR) from the Gram of the rows of Y^T (on its planes when split)
   auto chol_only = [&](Pair y) {
     Stage prof("cholqr_tall", st);
-    gram_f32(pl, b, y.T, Tld, ell * Tld, (int)ell, (int)T, y.am, b.G64, ell * ell, (int)ell, nb, st);
+    if (!(tplanes && gram_planes(pl, b, b.pln, Tld, ell * Tld, P32 * ell * Tld, (int)ell, (int)T, y.am, b.G64,
+                                 ell * ell, (int)ell, nb, st)))
+      gram_f32(pl, b, y.T, Tld, ell * Tld, (int)ell, (int)T, y.am, b.G64, ell * ell, (int)ell, nb, st);
     chol_inv(b.G64, ell * ell, (int)ell, (int)ell, nb, b.Rw, chol_scratch_doubles((int)ell), b.RinvT, ell * ld, (int)ld,
              amR, st);
   };
-  b.basis_implicit = 0;
-  b.basis_am = nullptr;
-
+  // An intermediate basis is orthonormalised explicitly, Q^T = R^{-T} Y^T (one Cholesky-QR pass; A =
+  // R^{-T} is lower triangular: each row tile stops its k loop at its last row), and only Q^T is
+  // written unless `rows` asks for Q = (Q^T)^T too: the next projection reads nothing else.
+  // (Projecting Y and applying R^{-1} afterwards would save this product but amplifies the
+  // projection's rounding by the condition of Y.)
+  auto orthonormalise = [&](Pair y, Pair q, bool rows) {
+    chol_only(y);
+    Stage prof("cholqr_tall", st);
+    fill_f32(q.am, nb, 0.f, st);
+    GemmArgs g = ga();
+    g.A = b.RinvT; g.a_ld = ld; g.a_bs = ell * ld; g.a_amax = amR;
+    g.B = y.R; g.b_ld = ld; g.b_bs = T * ld; g.b_amax = y.am;
+    g.ab_amax_bs = 1;
+    g.M = (int)ell; g.N = (int)T; g.K = (int)ell;
+    g.C = q.T; g.c_ld = Tld; g.c_bs = ell * Tld;
+    if (rows) {
+      g.C2 = q.R; g.c2_ld = ld; g.c2_bs = T * ld;
+    }
+    g.c_amax = q.am;
+    g.m_fastest = 1;
+    g.tri = 4;
+    gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
+  };
+  // The final basis stays implicit: Q = Y R^{-1} is never formed.  Its Gram gives R, the projection
+  // runs on Y (P' = Y^T X_(T)), B = Q^T X_(T) = R^{-T} P'^T, and the fit reads Y and R^{-1} instead of
+  // Q (U_T = Y (R^{-1} W), Y_p = (R^{-1} W)^T P'), so no second pass is needed for orthogonality.
+  b.basis_implicit = 1;
   sketch(b.omegaT, pl.xsrc(), 0, nullptr, pa.T, pa.R, pa.am);
   if (side_work) xready = side_work();
-  Pair Q = cholqr(pa, pb, 1, pl.power_iters > 0);
-  if (mark) HIP_TRY(hipEventRecord(mark, st));
+  Pair Y = pa;
+  split_basis(Y.T, Y.am);
   for (int it = 0; it < pl.power_iters; ++it) {
+    Pair Q = (Y.T == pa.T) ? pb : pa;
+    orthonormalise(Y, Q, false);
+    if (it == 0 && mark) HIP_TRY(hipEventRecord(mark, st));
+    split_basis(Q.T, Q.am);
     fill_f32(amP, nb, 0.f, st);
     project(Q.T, Q.am, amP);
     {
@@ -652,34 +688,29 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       g.tri = 4;
       gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
     }
-    Pair Y = (Q.T == pa.T) ? pb : pa;
-    Pair other = (Q.T == pa.T) ? pa : pb;
+    // the next sketch overwrites Y's pair (Q's is read no more)
     fill_f32(Y.am, nb, 0.f, st);
     sketch(b.Zt, SRC_F32, ell * Mf, amZ, Y.T, Y.R, Y.am);
-    if (it + 1 == pl.power_iters) {
-      // The final basis Q = Y R^{-1} (one Cholesky-QR pass in exact arithmetic) is not formed: its
-      // Gram gives R, the projection runs on Y (P' = Y^T X) and B = Q^T X = R^{-T} P'.  The products
-      // that would read Q read Y and R^{-1} instead (U_T = Y (R^{-1} W), Y_p = (R^{-1} W)^T P'), so no
-      // second pass is needed for orthogonality: the basis is only ever used through R.
-      chol_only(Y);
-      Q = Y;
-      b.basis_implicit = 1;
-      b.basis_am = Y.am;
-    } else {
-      Q = cholqr(Y, other, 1, true);
-    }
+    split_basis(Y.T, Y.am);
   }
-  if (pl.power_iters == 0) {  // the final basis (the raw sketch) is orthonormalised twice, explicitly
-    Pair other = (Q.T == pa.T) ? pb : pa;
-    Q = cholqr(Q, other, 1);
+  if (pl.power_iters == 0) {
+    // the raw sketch is orthonormalised once explicitly before it becomes the implicit final basis (a
+    // second Cholesky-QR pass, R close to the identity), as its condition is not reduced by an iteration
+    Pair Q = pb;
+    orthonormalise(Y, Q, true);
+    if (mark) HIP_TRY(hipEventRecord(mark, st));
+    Y = Q;
+    split_basis(Y.T, Y.am);
   }
-  // B = Q^T X_(T) -> H = B B^T (fp64) -> eigenvalues; spectrum = top q + tail entry
+  chol_only(Y);
+  b.basis_am = Y.am;
+  // B = Q^T X_(T) = R^{-T} P'^T -> H = B B^T (fp64) -> eigenvalues; spectrum = top q + tail entry
   float *amP1 = b.amax + 5 * am;
   fill_f32(amP1, nb, 0.f, st);
-  project(Q.T, Q.am, amP1);
-  const float *Bp = b.Pt;
-  if (b.basis_implicit) {
-    // B = R^{-T} P' ([ell][M]; R^{-T} is lower triangular), into the free Z^T buffer
+  project(Y.T, Y.am, amP1);
+  const float *Bp = b.Zt;
+  {
+    // B = R^{-T} P'^T ([ell][M]; R^{-T} is lower triangular), into the free Z^T buffer
     Stage prof("basis_apply", st);
     GemmArgs g = ga();
     g.A = b.RinvT; g.a_ld = ld; g.a_bs = ell * ld; g.a_amax = amR;
@@ -690,7 +721,6 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     g.m_fastest = 1;
     g.tri = 4;
     gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
-    Bp = b.Zt;
   }
   {
     Stage prof("gram64", st);
@@ -702,9 +732,9 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
                 b.mwg);
   }
   flash_spec(b.evT, ell, pl.q, b.norm2, b.specT, pl.nT, nb, st);
-  // the fit reads the final basis (Q, or Y when implicit; both layouts) from bufA / bufA2: report it by
-  // swapping this view's pointers
-  if (Q.T != b.bufA) {
+  // the fit reads the final basis Y (both layouts) from bufA / bufA2: report it by swapping this
+  // view's pointers
+  if (Y.T != b.bufA) {
     std::swap(b.bufA, b.bufB);
     std::swap(b.bufA2, b.bufB2);
   }

@@ -308,38 +308,50 @@ void launch_dma(const GemmArgs &g, int batch, int nsplit, hipStream_t st) {
 
 // fp32 rows -> P 16-bit planes with the split of the fp32 GEMM operands (power-of-two scale from
 // the batch's |x| bound for fp16; three bf16 planes otherwise); columns [cols, cols_pad) become 0.
-// Thread: 8 consecutive columns of one row.
+// Thread: SPT runs of 8 consecutive columns of one row, 2048 columns apart (the block's loads of one
+// run are contiguous); the loads of all runs are issued before the first split.
+constexpr int kSplitRuns = 4;
 template <int MF, int P>
 __global__ void __launch_bounds__(256) split_planes_kernel(const float *src, long long s_bs, long long s_ld, int rows,
                                                            int cols, int cols_pad, uint16_t *dst, long long d_bs,
                                                            long long d_ps, long long d_ld, const float *amax,
                                                            int amax_bs) {
   const int b = blockIdx.z, row = blockIdx.y;
-  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (row >= rows || c0 >= cols_pad) return;
+  if (row >= rows) return;
   float scale = 1.f;
   if constexpr (MF == MF_F16) scale = f16_split_scale(amax ? amax[(long long)b * amax_bs] : 1.f);
-  const float *x = src + b * s_bs + row * s_ld + c0;
-  float v[8];
-  if (c0 + 8 <= cols) {
-    const float4 p = *(const float4 *)x, q = *(const float4 *)(x + 4);
-    v[0] = p.x; v[1] = p.y; v[2] = p.z; v[3] = p.w; v[4] = q.x; v[5] = q.y; v[6] = q.z; v[7] = q.w;
-  } else {
+  const float *xr = src + b * s_bs + row * s_ld;
+  uint16_t *dr = dst + b * d_bs + row * d_ld;
+  float v[kSplitRuns][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = c0 + i < cols ? x[i] : 0.f;
+  for (int u = 0; u < kSplitRuns; ++u) {
+    const int c0 = ((blockIdx.x * kSplitRuns + u) * 256 + threadIdx.x) * 8;
+    const float *x = xr + c0;
+    if (c0 + 8 <= cols) {
+      const float4 p = *(const float4 *)x, q = *(const float4 *)(x + 4);
+      v[u][0] = p.x; v[u][1] = p.y; v[u][2] = p.z; v[u][3] = p.w;
+      v[u][4] = q.x; v[u][5] = q.y; v[u][6] = q.z; v[u][7] = q.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = c0 + i < cols ? x[i] : 0.f;
+    }
   }
-  uint16_t pl[8][3];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) split_planes<SRC_F32, MF>(v[i], scale, pl[i]);
-  uint16_t *d = dst + b * d_bs + row * d_ld + c0;
+  for (int u = 0; u < kSplitRuns; ++u) {
+    const int c0 = ((blockIdx.x * kSplitRuns + u) * 256 + threadIdx.x) * 8;
+    if (c0 >= cols_pad) continue;
+    uint16_t pl[8][3];
 #pragma unroll
-  for (int p = 0; p < P; ++p) {
-    uint4 w;
-    w.x = pl[0][p] | ((uint32_t)pl[1][p] << 16);
-    w.y = pl[2][p] | ((uint32_t)pl[3][p] << 16);
-    w.z = pl[4][p] | ((uint32_t)pl[5][p] << 16);
-    w.w = pl[6][p] | ((uint32_t)pl[7][p] << 16);
-    *(uint4 *)(d + p * d_ps) = w;
+    for (int i = 0; i < 8; ++i) split_planes<SRC_F32, MF>(v[u][i], scale, pl[i]);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      uint4 w;
+      w.x = pl[0][p] | ((uint32_t)pl[1][p] << 16);
+      w.y = pl[2][p] | ((uint32_t)pl[3][p] << 16);
+      w.z = pl[4][p] | ((uint32_t)pl[5][p] << 16);
+      w.w = pl[6][p] | ((uint32_t)pl[7][p] << 16);
+      *(uint4 *)(dr + c0 + p * d_ps) = w;
+    }
   }
 }
 
@@ -352,7 +364,7 @@ void split_planes(int mf, const float *src, long long s_bs, long long s_ld, int 
                    ((uintptr_t)src & 15) == 0 && ((uintptr_t)dst & 15) == 0,
                JOLT_EINVAL, "split_planes: misaligned operand");
   if (rows <= 0 || cols_pad <= 0 || batch <= 0) return;
-  dim3 grid((cols_pad / 8 + 255) / 256, rows, batch);
+  dim3 grid((cols_pad / 8 + 256 * kSplitRuns - 1) / (256 * kSplitRuns), rows, batch);
   if (mf == MF_F16)
     hipLaunchKernelGGL((split_planes_kernel<MF_F16, 2>), grid, dim3(256), 0, st, src, s_bs, s_ld, rows, cols,
                        cols_pad, dst, d_bs, d_ps, d_ld, amax, amax_bs);
@@ -370,7 +382,7 @@ bool gemm_dma(int mf, int pa, int pb, const GemmArgs &g0, int batch, int nsplit,
   if (nsplit == 1) g.k_chunk = g.K;  // one split covers K (callers leave k_chunk unset then)
   if (g.M <= 0 || g.N <= 0 || batch <= 0 || nsplit <= 0) return true;
   if (g.K % DK != 0 || g.k_chunk <= 0 || g.k_chunk % DK != 0 || (long long)g.k_chunk * nsplit < g.K) return false;
-  if (g.inner > 1 || (g.tri & 1)) return false;
+  if (g.inner > 1 || (g.tri & 4)) return false;
   if (g.a_blk % DK != 0 || g.b_blk % DK != 0) return false;
   if ((g.a_ld * 2) % 16 != 0 || (g.b_ld * 2) % 16 != 0 || (g.a_ps * 2) % 16 != 0 || (g.b_ps * 2) % 16 != 0) return false;
   auto extent = [](long long rows, long long ld, long long planes, long long ps, long long K, int blk,
@@ -382,8 +394,11 @@ bool gemm_dma(int mf, int pa, int pb, const GemmArgs &g0, int batch, int nsplit,
       extent(g.N, g.b_ld, pb, g.b_ps, g.K, g.b_blk, g.b_blk_stride) >= (1LL << 32))
     return false;
   if (((uintptr_t)g.A & 15) || ((uintptr_t)g.B & 15)) return false;
-  // 8 waves (4 x 2) of 48 x 128 output each: 192 x 256 blocks
+  // 8 waves (4 x 2) of 48 x 128 output each: 192 x 256 blocks; Grams of fp32 rows (both operands
+  // in planes) on 48 x 96 wave tiles: 192 x 192 blocks, which tile a 522-row Gram with less padding
   if (mf == MF_F16 && pa == 2 && pb == 1) launch_dma<MF_F16, 2, 1, 3, 8, 3, 4, 2>(g, batch, nsplit, st);
+  else if (mf == MF_F16 && pa == 2 && pb == 2) launch_dma<MF_F16, 2, 2, 3, 6, 3, 4, 2>(g, batch, nsplit, st);
+  else if (mf == MF_BF16 && pa == 3 && pb == 3) launch_dma<MF_BF16, 3, 3, 3, 6, 2, 4, 2>(g, batch, nsplit, st);
   else if (mf == MF_F16 && pa == 1 && pb == 1) launch_dma<MF_F16, 1, 1, 3, 8, 4, 4, 2>(g, batch, nsplit, st);
   else if (mf == MF_BF16 && pa == 3 && pb == 1) launch_dma<MF_BF16, 3, 1, 3, 8, 3, 4, 2>(g, batch, nsplit, st);
   else if (mf == MF_BF16 && pa == 1 && pb == 1) launch_dma<MF_BF16, 1, 1, 3, 8, 4, 4, 2>(g, batch, nsplit, st);
