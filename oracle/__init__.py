@@ -16,3 +16,4 @@ published SplitMix64 outputs).  Nothing here is "parity unpinned".
 """
 from . import rng  # noqa: F401
 from .jolt import *  # noqa: F401,F403
+from . import decode  # noqa: F401,E402
