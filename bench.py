@@ -13,6 +13,7 @@ The JSON line also carries the roofline of the dominant kernel, measured live wi
 HIP-event stage profiler on its own stream, and the CPU oracle timed on a bounded sample.
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -353,6 +354,91 @@ def compare_modes():
                                   "d_head 128, f16, synthetic (power law, exponent 1)", "modes": rows}), flush=True)
 
 
+def decode_measure(jolt, torch, blob, cfg, picks, T, L, H, D, G, dt, reps=20):
+    """One decode step of one layer (32 query heads over 8 KV heads, RoPE base 500000): the fused
+    attention over the compressed cells (jolt_decode_attention on a prepared layer state; also with
+    the per-layer preparation in every call) against reconstruct-then-attend (jolt_reconstruct of the layer's group, its share per
+    layer, then RoPE on the dense keys and scaled dot-product attention in torch).  Memory: the layer's
+    compressed bytes plus the fused path's workspace against the dense K and V the other path holds."""
+    import math
+    st = torch.cuda.current_stream()
+    tdt = torch.float16 if dt == "f16" else torch.bfloat16
+    nq = 4 * H
+    rope = jolt.rope_table(D, 500000.0, T)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    q = torch.randn(nq, D, device="cuda", generator=g) * 0.5
+    out = torch.empty(nq, D, device="cuda")
+    res = {}
+    for layer in (0, L - 1):
+        gi = layer // G
+        gp = [picks[2 * gi], picks[2 * gi + 1]]
+        nb = jolt.load().jolt_decode_attention_workspace_bytes(ctypes.byref(cfg.desc), jolt._picks_array(picks), 0,
+                                                               layer, nq)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        jolt.decode_attention(blob, cfg, picks, 0, layer, q, rope=rope, out=out, ws=ws)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(st)
+        for _ in range(reps):
+            jolt.decode_attention(blob, cfg, picks, 0, layer, q, rope=rope, out=out, ws=ws)
+        e1.record(st)
+        for _ in range(reps):
+            jolt.decode_attention(blob, cfg, picks, 0, layer, q, rope=rope, out=out, ws=ws, reuse_prepared=True)
+        e2.record(st)
+        torch.cuda.synchronize()
+        fused_prep = e0.elapsed_time(e1) / reps
+        fused = e1.elapsed_time(e2) / reps
+        # reconstruct-then-attend: the group's cells decoded densely, then one layer attended
+        gcfg = jolt.Config(1, G, H, T, D, cfg.desc.dtype, [0, G], jolt.FLASH, [8], [8], [2], 2.0)
+        Kg = torch.empty(1, G, H, T, D, dtype=tdt, device="cuda")
+        Vg = torch.empty_like(Kg)
+        gws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")  # the two cells' backbone slices
+        jolt.reconstruct(blob, gcfg, gp, Kg, Vg, ws=gws)
+        # position-only RoPE factors in the cache dtype (a serving loop keeps them): k cos + rot(k) sin
+        cos2 = torch.cat([rope[..., 0], rope[..., 0]], dim=-1).to(tdt)
+        sin2 = torch.cat([-rope[..., 1], rope[..., 1]], dim=-1).to(tdt)
+        qt = q.to(tdt).view(H, nq // H, D).transpose(1, 2).contiguous()  # [H][D][G]
+        scale = 1.0 / math.sqrt(D)
+
+        def attend():
+            # decode attention on the dense layer: RoPE on the keys, scores by batched products over the
+            # KV heads (grouped queries side by side), softmax over tokens in fp32, weighted values
+            Kl, Vl = Kg[0, layer - gi * G], Vg[0, layer - gi * G]
+            Kr = torch.addcmul(Kl * cos2, Kl.roll(D // 2, dims=-1), sin2)
+            s = torch.bmm(Kr, qt)                                            # [H][T][G]
+            p = torch.softmax(s.float() * scale, dim=1).to(tdt).transpose(1, 2).contiguous()
+            return torch.bmm(p, Vl)                                          # [H][G][D]
+        attend()
+        torch.cuda.synchronize()
+        r0, r1, r2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        r0.record(st)
+        for _ in range(reps):
+            jolt.reconstruct(blob, gcfg, gp, Kg, Vg, ws=gws)
+        r1.record(st)
+        for _ in range(reps):
+            attend()
+        r2.record(st)
+        torch.cuda.synchronize()
+        rec_g = r0.elapsed_time(r1) / reps
+        att = r1.elapsed_time(r2) / reps
+        dense_layer = 2 * H * T * D * 2
+        comp_layer = (gp[0]["bytes"] + gp[1]["bytes"]) / G
+        res[f"layer{layer}"] = {
+            "picks_kv": [[p["rT"], p["rd"], p["bits"]] for p in gp],
+            "fused_ms": round(fused, 4),
+            "fused_with_prepare_ms": round(fused_prep, 4),
+            "reconstruct_group_ms": round(rec_g, 4),
+            "reconstruct_then_attend_ms": round(rec_g / G + att, 4),
+            "attend_dense_ms": round(att, 4),
+            "fused_vs_reconstruct_then_attend": round(fused / (rec_g / G + att), 3),
+            "kv_bytes_dense": dense_layer,
+            "kv_bytes_fused": int(comp_layer + nb),
+            "memory_ratio": round(dense_layer / (comp_layer + nb), 3),
+        }
+        del Kg, Vg, gws, ws
+    return res
+
+
 def main():
     a = parse()
     if a.compare_modes:
@@ -449,6 +535,7 @@ def main():
                    "gbs": round(rec_bytes / (rec_ms / 1e3) / 1e9, 1),
                    "hbm_frac": round(rec_bytes / (rec_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
     del Ko, Vo
+    decode = decode_measure(jolt, torch, blob, cfg, picks, T, L, H, D, G, a.dtype)
     cpu = None
     if not a.no_cpu_baseline:
         cpu = cpu_baseline(K, V, groups, {"eps2": [float(x) for x in eps2], "rT": rT, "rd": rd, "bits": bits,
@@ -478,6 +565,7 @@ def main():
         "cpu_baseline": cpu,
         "stages": table,
         "reconstruct": reconstruct,
+        "decode_attention": decode,
         "wall_s_timed": round(wall, 3),
         "input_gen_s": round(gen_s, 2),
     }

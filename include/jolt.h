@@ -197,6 +197,47 @@ int jolt_reconstruct(const void *d_blob, const jolt_cache_desc *desc, const jolt
                      const jolt_pick *h_picks, void *d_K_out, void *d_V_out, void *d_ws,
                      size_t ws_bytes, void *stream);
 
+/* RoPE cosine / sine table for jolt_decode_attention (rotate-half pairs: dimension i turns with
+ * i + d_h/2).  d_table: device float[n_pos][d_head/2][2] = {cos a, sin a} with a the fp32 product of
+ * fp32(p) and fp32(base^(-2i/d_head)) (the product rounded to fp32, as the usual fp32 RoPE does),
+ * p < n_pos, i < d_head/2.  The table depends on positions only: one table serves every layer and
+ * head.  d_head even, at most 128; base > 1.  Asynchronous on the stream. */
+int jolt_rope_table(int32_t d_head, double base, int32_t n_pos, float *d_table, void *stream);
+
+/* Workspace bytes of jolt_decode_attention for this layer (0 on invalid arguments). */
+size_t jolt_decode_attention_workspace_bytes(const jolt_cache_desc *desc, const jolt_pick *h_picks,
+                                             int32_t seq, int32_t layer, int32_t n_q_heads);
+
+/* One decode step of one layer, evaluated over the compressed cells (Sec. 4.5, "Fused decode
+ * kernel"): no dense K or V of the layer is written to memory.  Keys are rebuilt per 128-token tile
+ * on chip from U_T, the core and U_d plus the de-rotated residual, rotated by RoPE at their
+ * positions and scored; values are accumulated in rank space against the value token factor and
+ * in the rotated frame against the value codes, and expanded once per head.  Equal, up to rounding,
+ * to softmax attention over the reconstruction jolt_reconstruct gives, with keys rotated by RoPE.
+ *   d_blob, desc, params, h_picks   as written by jolt_compress (params: rot_seed is used).
+ *   seq, layer     the sequence and the layer (any layer group size).
+ *   d_q            device float[n_q_heads][d_h]: the step's queries, already rotated at their own
+ *                  position; query head j reads KV head j / (n_q_heads / n_h) (grouped-query
+ *                  attention; 1 to 8 query heads per KV head).
+ *   d_k_tail, d_v_tail  device, cache dtype, [n_h][n_tail][d_h]: tokens newer than the compressed
+ *                  ones (keys before RoPE, positions T .. T + n_tail - 1); NULL when n_tail == 0;
+ *                  n_tail <= 1024.
+ *   d_rope, n_rope_pos  a table from jolt_rope_table covering positions 0 .. T + n_tail - 1.
+ *   d_out          device float[n_q_heads][d_h].
+ *   d_ws, ws_bytes at least jolt_decode_attention_workspace_bytes: the layer's prepared state (its
+ *                  backbone slices D_h = C_h U_d^T of both cells, the rotation) and the chunk states
+ *                  of the split over tokens.
+ *   reuse_prepared 0: the call prepares the state into d_ws first.  1: d_ws already holds the state a
+ *                  previous call prepared for the same blob, picks, seq and layer (a decode loop
+ *                  prepares each layer once and passes 1 on later steps); nothing is checked.
+ * Scores are scaled by 1/sqrt(d_h); no mask.  Value token ranks up to 512.  Asynchronous on the
+ * stream (the argument checks run on the host first; errors as elsewhere). */
+int jolt_decode_attention(const void *d_blob, const jolt_cache_desc *desc, const jolt_params *params,
+                          const jolt_pick *h_picks, int32_t seq, int32_t layer, const float *d_q,
+                          int32_t n_q_heads, const void *d_k_tail, const void *d_v_tail,
+                          int32_t n_tail, const float *d_rope, int32_t n_rope_pos, float *d_out,
+                          void *d_ws, size_t ws_bytes, int32_t reuse_prepared, void *stream);
+
 /* Spectra and token factors only (Sec. 3 ST-HOSVD inputs; Sec. 3.1 randomized token SVD).
  *   d_specT   device double[n_cells][nT]  token spectrum, nT = q_cap+1 (FlashJoLT, last entry
  *             is the tail) or min(T, |g| n_h d_h) (exact).

@@ -2198,6 +2198,198 @@ int jolt_reconstruct(const void *d_blob, const jolt_cache_desc *desc, const jolt
   });
 }
 
+// ----------------------------------------------------------------------------- fused decode
+namespace {
+// One decode step of one layer: its group, the two cells' picks and the launch shape of the chunked
+// attention (about two blocks per CU over the KV heads, chunks of whole 128-token tiles).
+struct AttnPlan {
+  int g, lg, Gg, H, T, D, c, dtype, G, n_chunks, chunk, rtv_ld, PS, kmax, kmd, Kd;
+  const jolt_pick *pk, *pv;
+};
+
+AttnPlan attn_plan(const jolt_cache_desc *d, const jolt_pick *picks, int seq, int layer, int n_q) {
+  JOLT_REQUIRE(d && picks && d->group_start, JOLT_EINVAL, "null argument");
+  JOLT_REQUIRE(d->n_seq >= 1 && d->n_layers >= 1 && d->n_heads >= 1 && d->n_tokens >= 1 && d->n_groups >= 1,
+               JOLT_EINVAL, "cache shape must be positive");
+  JOLT_REQUIRE(d->d_head == 64 || d->d_head == 128, JOLT_EINVAL, "d_head must be 64 or 128");
+  JOLT_REQUIRE(d->dtype == JOLT_F16 || d->dtype == JOLT_BF16 || d->dtype == JOLT_F32, JOLT_EINVAL, "bad dtype");
+  JOLT_REQUIRE(seq >= 0 && seq < d->n_seq && layer >= 0 && layer < d->n_layers, JOLT_EINVAL, "seq or layer out of range");
+  JOLT_REQUIRE(d->group_start[0] == 0 && d->group_start[d->n_groups] == d->n_layers, JOLT_EINVAL,
+               "group_start must run from 0 to n_layers");
+  AttnPlan a;
+  a.g = -1;
+  for (int g = 0; g < d->n_groups; ++g) {
+    JOLT_REQUIRE(d->group_start[g + 1] > d->group_start[g], JOLT_EINVAL, "group_start must be increasing");
+    if (layer >= d->group_start[g] && layer < d->group_start[g + 1]) a.g = g;
+  }
+  a.lg = layer - d->group_start[a.g];
+  a.Gg = d->group_start[a.g + 1] - d->group_start[a.g];
+  a.H = d->n_heads; a.T = d->n_tokens; a.D = d->d_head; a.dtype = d->dtype; a.c = dtype_bytes(d->dtype);
+  JOLT_REQUIRE(n_q >= a.H && n_q % a.H == 0 && n_q / a.H <= kAttnMaxG, JOLT_EINVAL,
+               "n_q_heads must be a multiple of n_heads, at most 8 query heads per KV head");
+  a.G = n_q / a.H;
+  const int cell = 2 * (seq * d->n_groups + a.g);
+  a.pk = &picks[cell];
+  a.pv = &picks[cell + 1];
+  for (const jolt_pick *p : {a.pk, a.pv})
+    JOLT_REQUIRE(p->rT >= 8 && p->rT % 8 == 0 && p->rT <= a.T && p->rd >= 8 && p->rd % 8 == 0 && p->rd <= a.D &&
+                     p->bits >= 0 && p->bits <= 8 && p->offset >= 0 && p->offset % 256 == 0,
+                 JOLT_EINVAL, "bad pick");
+  JOLT_REQUIRE(a.pv->rT <= kAttnMaxRank, JOLT_EINVAL, "value token rank above 512");
+  const int tiles = (a.T + 127) / 128;
+  const int want = std::max(1, std::min(kAttnMaxChunks, 512 / a.H));
+  const int per = (tiles + std::min(want, tiles) - 1) / std::min(want, tiles);
+  a.chunk = per * 128;
+  a.n_chunks = (a.T + a.chunk - 1) / a.chunk;
+  a.rtv_ld = (int)rup(a.pv->rT, 4);
+  a.PS = 2 + a.rtv_ld + a.D;
+  a.kmax = std::max(a.pk->rT, a.pv->rT);
+  a.kmd = std::max(a.pk->rd, a.pv->rd);
+  a.Kd = (int)rup(a.kmax, 8);
+  return a;
+}
+
+struct AttnBufs {
+  float *Udr, *Cr, *Dm, *am, *part;
+  char *params;
+};
+AttnBufs carve_attn(Arena &ar, const AttnPlan &a) {
+  AttnBufs b;
+  b.Udr = ar.take<float>(2LL * a.kmd * a.D);
+  b.Cr = ar.take<float>(2LL * a.H * a.kmax * a.kmd);
+  b.Dm = ar.take<float>(2LL * a.H * a.D * a.Kd);
+  b.am = ar.take<float>(4);
+  b.part = ar.take<float>((long long)a.n_chunks * a.H * a.G * a.PS);
+  b.params = ar.take<char>(64 * 1024 + 2LL * a.D * a.D * 4);
+  return b;
+}
+}  // namespace
+
+size_t jolt_decode_attention_workspace_bytes(const jolt_cache_desc *desc, const jolt_pick *h_picks, int32_t seq,
+                                             int32_t layer, int32_t n_q_heads) {
+  try {
+    AttnPlan a = attn_plan(desc, h_picks, seq, layer, n_q_heads);
+    Arena dry;
+    carve_attn(dry, a);
+    return dry.off;
+  } catch (...) {
+    return 0;
+  }
+}
+
+int jolt_rope_table(int32_t d_head, double base, int32_t n_pos, float *d_table, void *stream) {
+  return guarded([&]() {
+    JOLT_REQUIRE(d_table != nullptr, JOLT_EINVAL, "null table");
+    JOLT_REQUIRE(d_head >= 2 && d_head <= 128 && d_head % 2 == 0, JOLT_EINVAL, "d_head must be even, at most 128");
+    JOLT_REQUIRE(base > 1.0 && isfinite(base) && n_pos >= 0, JOLT_EINVAL, "bad base or position count");
+    std::vector<float> inv(d_head / 2);
+    for (int i = 0; i < d_head / 2; ++i) inv[i] = (float)std::pow(base, -2.0 * i / d_head);
+    rope_table(inv.data(), d_head / 2, n_pos, d_table, S(stream));
+    return 0;
+  });
+}
+
+int jolt_decode_attention(const void *d_blob, const jolt_cache_desc *desc, const jolt_params *params,
+                          const jolt_pick *h_picks, int32_t seq, int32_t layer, const float *d_q, int32_t n_q_heads,
+                          const void *d_k_tail, const void *d_v_tail, int32_t n_tail, const float *d_rope,
+                          int32_t n_rope_pos, float *d_out, void *d_ws, size_t ws_bytes, int32_t reuse_prepared,
+                          void *stream) {
+  return guarded([&]() {
+    JOLT_REQUIRE(d_blob && params && d_q && d_rope && d_out, JOLT_EINVAL, "null argument");
+    const AttnPlan a = attn_plan(desc, h_picks, seq, layer, n_q_heads);
+    JOLT_REQUIRE(n_tail >= 0 && n_tail <= kAttnMaxTail && (n_tail == 0 || (d_k_tail && d_v_tail)), JOLT_EINVAL,
+                 "tail: 0 .. 1024 tokens, both arrays given");
+    JOLT_REQUIRE(n_rope_pos >= a.T + n_tail, JOLT_EINVAL, "the RoPE table must cover positions 0 .. T + n_tail - 1");
+    JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
+    hipStream_t st = S(stream);
+    Arena ar;
+    ar.dry = false;
+    ar.base = (char *)d_ws;
+    ar.cap = ws_bytes;
+    AttnBufs b = carve_attn(ar, a);
+    const int H = a.H, D = a.D;
+    const char *blob = (const char *)d_blob;
+    Upload u;
+    FactorCell fc[2];
+    DecCell dc[2];
+    {
+      const std::vector<double> &Q = rotation(D, params->rot_seed);
+      std::vector<float> qf(Q.size());
+      for (size_t i = 0; i < Q.size(); ++i) qf[i] = (float)Q[i];
+      u.add(qf.data(), qf.size() * 4);  // at offset 0
+    }
+    const float *Qdev = (const float *)b.params;
+    for (int t = 0; t < 2; ++t) {
+      const jolt_pick &p = t == 0 ? *a.pk : *a.pv;
+      const Section sec = layout(a.Gg, H, a.T, D, a.c, p.rT, p.rd, p.bits);
+      const char *base = blob + p.offset;
+      const long long rows0 = (long long)a.lg * H * a.T;  // first residual row of the layer
+      FactorCell &f = fc[t];
+      memset(&f, 0, sizeof(f));
+      f.UT = (void *)(base + sec.off_UT);
+      f.Ud = (void *)(base + sec.off_Ud);
+      f.core = (void *)(base + sec.off_core + (long long)a.lg * H * p.rT * p.rd * a.c);
+      f.rT = p.rT; f.rd = p.rd; f.bits = p.bits;
+      DecCell &d = dc[t];
+      d.UT = f.UT;
+      d.Dm = b.Dm + (long long)t * H * D * a.Kd;
+      d.Q = Qdev;
+      d.d_amax = b.am + t;
+      d.scales = (const float *)(base + sec.off_scales) + rows0;
+      d.codes = (const uint8_t *)(base + sec.off_codes) + rows0 * (D * p.bits / 8);
+      d.out = nullptr;
+      d.GH = H; d.rT = p.rT; d.bits = p.bits; d.Kd = a.Kd;
+    }
+    const size_t o_fc = u.add(fc, sizeof(fc));
+    JOLT_REQUIRE(u.host.size() <= (size_t)(64 * 1024 + 2LL * D * D * 4), JOLT_EWORKSPACE, "parameter area too small");
+    if (!reuse_prepared) {
+      HIP_TRY(hipMemcpyAsync(b.params, u.host.data(), u.host.size(), hipMemcpyHostToDevice, st));
+      // D_h = C_h U_d^T of the layer's heads for both cells (Dm[cell][h][n][r]), and their |max|
+      fill_f32(b.Udr, 2LL * a.kmd * D, 0.f, st);
+      fill_f32(b.Cr, 2LL * H * a.kmax * a.kmd, 0.f, st);
+      get_small(a.dtype, (const FactorCell *)(b.params + o_fc), 2, a.kmax, a.kmd, D, H, b.Udr, b.Cr, st);
+      amax_cells(b.Cr, (long long)H * a.kmax * a.kmd, (long long)H * a.kmax * a.kmd, 2, b.am + 2, st);
+      GemmArgs g = ga();
+      g.A = b.Udr; g.a_ld = D; g.a_bs = (long long)a.kmd * D; g.a_bs2 = 0; g.a_amax_c = 1.f;
+      g.B = b.Cr; g.b_ld = a.kmd; g.b_bs = (long long)H * a.kmax * a.kmd; g.b_bs2 = (long long)a.kmax * a.kmd;
+      g.b_amax = b.am + 2; g.ab_amax_bs = 1;
+      g.inner = H;
+      g.M = D; g.N = a.kmax; g.K = a.kmd;
+      g.C = b.Dm; g.c_ld = a.Kd; g.c_bs = (long long)H * D * a.Kd; g.c_bs2 = (long long)D * a.Kd;
+      gemm(MF_F16, SRC_F32, false, SRC_F32, true, g, 2 * H, 1, st);
+      amax_cells(b.Dm, (long long)H * D * a.Kd, (long long)H * D * a.Kd, 2, b.am, st);
+    }
+    AttnArgs at;
+    at.k = dc[0];
+    at.v = dc[1];
+    at.q = d_q;
+    at.rope = d_rope;
+    at.part = b.part;
+    at.T = a.T; at.D = D; at.H = H; at.G = a.G;
+    at.chunk = a.chunk; at.n_chunks = a.n_chunks; at.rtv_ld = a.rtv_ld; at.PS = a.PS;
+    at.scale = (float)(1.0 / std::sqrt((double)D));
+    {
+      Stage prof("attend_chunks", st);
+      attend_cells(a.dtype, at, st);
+    }
+    AttnMergeArgs m;
+    m.part = b.part;
+    m.n_chunks = a.n_chunks; m.H = H; m.G = a.G; m.D = D; m.T = a.T;
+    m.rTv = a.pv->rT; m.rtv_ld = a.rtv_ld; m.PS = a.PS; m.bits_v = a.pv->bits; m.Kd = a.Kd;
+    m.DmV = b.Dm + (long long)H * D * a.Kd;
+    m.Q = Qdev;
+    m.k_tail = d_k_tail; m.v_tail = d_v_tail; m.n_tail = n_tail;
+    m.q = d_q; m.rope = d_rope;
+    m.scale = at.scale;
+    m.out = d_out;
+    {
+      Stage prof("attend_merge", st);
+      attend_merge(a.dtype, m, st);
+    }
+    return 0;
+  });
+}
+
 size_t jolt_encode_residual_workspace_bytes(int32_t G, int32_t H, int32_t T, int32_t D, int32_t rT, int32_t rd) {
   if (G <= 0 || H <= 0 || T <= 0 || (D != 64 && D != 128) || rT < 8 || rd < 8) return 0;
   const long long GH = (long long)G * H, Kb = rup(D + rT, 32);

@@ -667,28 +667,30 @@ __device__ __forceinline__ void unpack8(const uint8_t *rowp, int k0, int b, floa
 }
 
 template <int MF, int SX, int NB16>
-__global__ void __launch_bounds__(NT) decode_kernel(const DecCell *cells, int T, int D, int ttiles) {
-  constexpr int PA = CPlanes<SX, MF, NB16>::n;  // U_T part; the codes part uses one plane
-  constexpr int PB = CPlanes<SRC_F32, MF, NB16>::n;
-  constexpr int MAXO = (MF == MF_F16) ? (NB16 - 1) : 2;
-  constexpr int ASZ = PA * BM * LDK, BSZ = PB * BN * LDK, STG = ASZ + BSZ;
-  constexpr int SC = (MF == MF_F16) ? SRC_F16 : SRC_BF16;  // small integer codes are exact
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STG];
-  __shared__ float srow[BM];
+struct DecCfg {
+  static constexpr int PA = CPlanes<SX, MF, NB16>::n;  // U_T part; the codes part uses one plane
+  static constexpr int PB = CPlanes<SRC_F32, MF, NB16>::n;
+  static constexpr int MAXO = (MF == MF_F16) ? (NB16 - 1) : 2;
+  static constexpr int ASZ = PA * BM * LDK, BSZ = PB * BN * LDK, STG = ASZ + BSZ;
+};
 
-  const DecCell c = cells[blockIdx.z];
-  const int j = blockIdx.x / ttiles, tt = blockIdx.x % ttiles;
-  if (j >= c.GH) return;
+// Rebuild rows t0 .. t0 + 127 of head slice j of a cell, X_hat_j = s (codes Q^T) + U_T D_j, into the
+// calling wave's accumulators (row wm 64 + 16 i + 4 (lane / 16) + r, column wn 64 + 16 q + lane % 16
+// for wave (wm, wn)), in real units; rows past T come out zero.  lds: 2 STG halves of staging,
+// srow: BM floats.  Every thread of the block calls it (it synchronises the block).
+template <int MF, int SX, int NB16>
+__device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, int T, int D, uint16_t *lds, float *srow,
+                                             f32x4 (&acc)[4][4]) {
+  using C = DecCfg<MF, SX, NB16>;
+  constexpr int PA = C::PA, PB = C::PB, MAXO = C::MAXO, ASZ = C::ASZ, STG = C::STG;
+  constexpr int SC = (MF == MF_F16) ? SRC_F16 : SRC_BF16;  // small integer codes are exact
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int t0 = tt * BM;
-  const int fr = lane & 15;
   const float qscale = (MF == MF_F16) ? f16_split_scale(1.f) : 1.f;
   const float dscale = (MF == MF_F16) ? f16_split_scale(*c.d_amax) : 1.f;
   const int b = c.bits;
   const int rowbytes = D * b / 8;
 
-  f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -787,6 +789,26 @@ __global__ void __launch_bounds__(NT) decode_kernel(const DecCell *cells, int T,
     }
   }
   const float inv = 1.f / dscale;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][q][r] *= inv;
+}
+
+template <int MF, int SX, int NB16>
+__global__ void __launch_bounds__(NT) decode_kernel(const DecCell *cells, int T, int D, int ttiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * DecCfg<MF, SX, NB16>::STG];
+  __shared__ float srow[BM];
+  const DecCell c = cells[blockIdx.z];
+  const int j = blockIdx.x / ttiles, tt = blockIdx.x % ttiles;
+  if (j >= c.GH) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1, fr = lane & 15;
+  const int t0 = tt * BM;
+  f32x4 acc[4][4];
+  rebuild_tile<MF, SX, NB16>(c, j, t0, T, D, lds, srow, acc);
   const long long obase = (long long)j * T * D;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -797,9 +819,300 @@ __global__ void __launch_bounds__(NT) decode_kernel(const DecCell *cells, int T,
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = wn * 64 + q * 16 + fr;
-        if (n < D) store_elem<SX>(c.out, obase + (long long)t * D + n, acc[i][q][r] * inv);
+        if (n < D) store_elem<SX>(c.out, obase + (long long)t * D + n, acc[i][q][r]);
       }
     }
+}
+
+// ------------------------------------------------------------------------------------------ fused decode
+// Code of element n of a packed row (b bits, LSB-first, offset binary) as its signed value; reads the
+// second byte only when the element reaches into it.
+__device__ __forceinline__ float code_at(const uint8_t *rowp, int n, int b) {
+  const int bit = n * b, by = bit >> 3, sh = bit & 7;
+  unsigned w = rowp[by];
+  if (sh + b > 8) w |= (unsigned)rowp[by + 1] << 8;
+  const int u = (int)((w >> sh) & ((1u << b) - 1u));
+  const int qm = (b >= 2) ? ((1 << (b - 1)) - 1) : 1;
+  return (b == 1) ? (u ? 1.f : -1.f) : (float)(u - qm);
+}
+
+__device__ __forceinline__ float warp_sum_f(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Attention of one decode step over a token chunk of one KV head (Sec. 4.5): per 128-token tile the
+// key rows are rebuilt on chip (rebuild_tile: codes de-rotated plus U_T D_h), rotated by RoPE at their
+// positions and scored against the head's G queries; an online softmax state (max m, sum l) is carried
+// over the tiles.  Values stay compressed: the weights are accumulated against the value token factor
+// (z = sum p U_T^V[t], rank space) and against the scaled value codes (w = sum p s_t u_t, rotated frame);
+// the merge expands both once per head.  The block writes its chunk's (m, l, z, w) per query head.
+template <int MF, int SX, int NB16, int D, int G8>
+__global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G8 <= 4 ? 2 : 1, G8 <= 4 ? 2 : 1))) attend_kernel(AttnArgs a) {
+  constexpr int KP = D + 1, H2 = D / 2, NQ = NT / D, ZU = kAttnMaxRank / NT;
+  constexpr int STGB = 2 * DecCfg<MF, SX, NB16>::STG * 2, KTB = BM * KP * 4;
+  constexpr int SMB = STGB > KTB ? STGB : KTB;
+  // the staging of the tile rebuild and the key tile share the memory (one is done when the other starts)
+  __shared__ __attribute__((aligned(16))) char smem[SMB];
+  __shared__ float srow[BM];
+  __shared__ float qs[G8 * D];
+  __shared__ float ps[G8 * BM];
+  __shared__ float alpha_s[G8], m_s[G8], l_s[G8];
+  uint16_t *lds = (uint16_t *)smem;
+  float *kt = (float *)smem;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1, fr = lane & 15;
+  const int h = blockIdx.y, ch = blockIdx.x, G = a.G, T = a.T;
+  const int tbeg = ch * a.chunk, tend = min(T, tbeg + a.chunk);
+  for (int i = tid; i < G * D; i += NT) qs[i] = a.q[(long long)h * G * D + i];
+  if (tid < G) {
+    m_s[tid] = -INFINITY;
+    l_s[tid] = 0.f;
+  }
+  const int rTv = a.v.rT, bv = a.v.bits, rbv = D * bv / 8;
+  const int ncol = tid % D, tg = tid / D;
+  float zr[ZU][G8], wr[G8];
+#pragma unroll
+  for (int g = 0; g < G8; ++g) {
+    wr[g] = 0.f;
+#pragma unroll
+    for (int u = 0; u < ZU; ++u) zr[u][g] = 0.f;
+  }
+  __syncthreads();
+  for (int t0 = tbeg; t0 < tend; t0 += BM) {
+    f32x4 acc[4][4];
+    rebuild_tile<MF, SX, NB16>(a.k, h, t0, T, D, lds, srow, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = wn * 64 + q * 16 + fr;
+          if (n < D) kt[row * KP + n] = acc[i][q][r];
+        }
+      }
+    __syncthreads();
+    // RoPE: the pair (i, i + D/2) of row t turns by the angle of (t, i).  Thread: pair i = tid % H2 of
+    // rows tid / H2 + RS k; the table entries of 8 rows are requested together
+    {
+      constexpr int RS = NT / H2, RR = BM / RS, RB2 = 8;
+      const int i = tid % H2, rbase = tid / H2;
+      const float2 *tab = (const float2 *)a.rope;
+#pragma unroll
+      for (int k0 = 0; k0 < RR; k0 += RB2) {
+        float2 cs[RB2];
+#pragma unroll
+        for (int k = 0; k < RB2; ++k) {
+          const int t = min(t0 + rbase + RS * (k0 + k), tend - 1);
+          cs[k] = tab[(long long)t * H2 + i];
+        }
+#pragma unroll
+        for (int k = 0; k < RB2; ++k) {
+          float *kr = kt + (rbase + RS * (k0 + k)) * KP;
+          const float x0 = kr[i], x1 = kr[i + H2];
+          kr[i] = x0 * cs[k].x - x1 * cs[k].y;
+          kr[i + H2] = x1 * cs[k].x + x0 * cs[k].y;
+        }
+      }
+    }
+    __syncthreads();
+    // scores: thread pair (2 row, 2 row + 1) takes row `row`, each half of the columns for every head
+    // (the key row is read once for all heads; the query reads are the same address across the wave)
+    {
+      const int row = tid >> 1, half = tid & 1;
+      const float *kr = kt + row * KP + half * H2, *qh = qs + half * H2;
+      float d[G8];
+#pragma unroll
+      for (int g = 0; g < G8; ++g) d[g] = 0.f;
+#pragma unroll 4
+      for (int n = 0; n < H2; ++n) {
+        const float kv = kr[n];
+#pragma unroll
+        for (int g = 0; g < G8; ++g)
+          if (g < G) d[g] = fmaf(kv, qh[g * D + n], d[g]);
+      }
+      const bool live = t0 + row < tend;
+#pragma unroll
+      for (int g = 0; g < G8; ++g) {
+        const float v = d[g] + __shfl_xor(d[g], 1, 64);
+        if (g < G && half == 0) ps[g * BM + row] = live ? v * a.scale : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // online softmax per query head (every tile holds at least one token of the chunk)
+    for (int g = wave; g < G; g += NT / 64) {
+      const float v0 = ps[g * BM + lane], v1 = ps[g * BM + 64 + lane];
+      const float mo = m_s[g], mn = fmaxf(mo, warp_max(fmaxf(v0, v1)));
+      const float p0 = expf(v0 - mn), p1 = expf(v1 - mn);
+      ps[g * BM + lane] = p0;
+      ps[g * BM + 64 + lane] = p1;
+      const float sm = warp_sum_f(p0 + p1);
+      if (lane == 0) {
+        const float al = expf(mo - mn);
+        alpha_s[g] = al;
+        l_s[g] = fmaf(l_s[g], al, sm);
+        m_s[g] = mn;
+      }
+    }
+    __syncthreads();
+    float al[G8];
+#pragma unroll
+    for (int g = 0; g < G8; ++g) al[g] = g < G ? alpha_s[g] : 0.f;
+    const int nrow = min(BM, tend - t0);
+    // value token factor, rank space (rows in batches of 8 loads in flight; the weight of a row past
+    // the chunk is exp(-inf) = 0, only its load is skipped)
+    constexpr int RB = 16;
+#pragma unroll
+    for (int u = 0; u < ZU; ++u) {
+      const int k = tid + NT * u;
+#pragma unroll
+      for (int g = 0; g < G8; ++g) zr[u][g] *= al[g];
+      if (k < rTv)
+        for (int r0 = 0; r0 < nrow; r0 += RB) {
+          float uv[RB];
+#pragma unroll
+          for (int i = 0; i < RB; ++i)
+            uv[i] = r0 + i < nrow ? load_elem<SX>(a.v.UT, (long long)(t0 + r0 + i) * rTv + k) : 0.f;
+#pragma unroll
+          for (int i = 0; i < RB; ++i)
+#pragma unroll
+            for (int g = 0; g < G8; ++g)
+              if (g < G) zr[u][g] = fmaf(ps[g * BM + r0 + i], uv[i], zr[u][g]);
+        }
+    }
+    // value residual, rotated frame: column ncol over the rows of token group tg
+#pragma unroll
+    for (int g = 0; g < G8; ++g) wr[g] *= al[g];
+    if (bv > 0)
+      for (int r0 = tg; r0 < nrow; r0 += NQ * RB) {
+        float sv[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int row = r0 + i * NQ;
+          if (row < nrow) {
+            const long long vr = (long long)h * T + t0 + row;
+            sv[i] = a.v.scales[vr] * code_at(a.v.codes + vr * rbv, ncol, bv);
+          } else {
+            sv[i] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int row = min(r0 + i * NQ, BM - 1);
+#pragma unroll
+          for (int g = 0; g < G8; ++g)
+            if (g < G) wr[g] = fmaf(ps[g * BM + row], sv[i], wr[g]);
+        }
+      }
+    __syncthreads();
+  }
+  // the chunk's state; the residual sums of the NQ token groups are added in group order
+#pragma unroll
+  for (int g = 0; g < G8; ++g)
+    if (g < G) kt[(tg * G + g) * D + ncol] = wr[g];
+  __syncthreads();
+  float *P = a.part + (long long)(ch * a.H + h) * G * a.PS;
+  for (int e = tid; e < G * D; e += NT) {
+    const int g = e / D, n = e - g * D;
+    float sum = 0.f;
+    for (int q = 0; q < NQ; ++q) sum += kt[(q * G + g) * D + n];
+    P[(long long)g * a.PS + 2 + a.rtv_ld + n] = sum;
+  }
+#pragma unroll
+  for (int u = 0; u < ZU; ++u) {
+    const int k = tid + NT * u;
+    if (k < rTv)
+#pragma unroll
+      for (int g = 0; g < G8; ++g)
+        if (g < G) P[(long long)g * a.PS + 2 + k] = zr[u][g];
+  }
+  if (tid < G) {
+    P[(long long)tid * a.PS] = m_s[tid];
+    P[(long long)tid * a.PS + 1] = l_s[tid];
+  }
+}
+
+// Merge of the chunk states of one query head (fixed chunk order), with the dense tail (its keys
+// rotated at positions T ..), then the expansion out = (z D_h^V + w Q^T + sum_tail p v) / l.
+template <int SX>
+__global__ void __launch_bounds__(256) attend_merge_kernel(AttnMergeArgs a) {
+  __shared__ float wc[kAttnMaxChunks];
+  __shared__ float ts[kAttnMaxTail];
+  __shared__ float zs[kAttnMaxRank];
+  __shared__ float wsum[128];
+  __shared__ float Ls;
+  const int hg = blockIdx.x, h = hg / a.G, g = hg - h * a.G;
+  const int tid = threadIdx.x, D = a.D, H2 = D / 2;
+  const float *qg = a.q + (long long)hg * D;
+  for (int i = tid; i < a.n_tail; i += 256) {
+    const long long base = ((long long)h * a.n_tail + i) * D;
+    const long long t = a.T + i;
+    float d = 0.f;
+    for (int n = 0; n < H2; ++n) {
+      const float cs = a.rope[(t * H2 + n) * 2], sn = a.rope[(t * H2 + n) * 2 + 1];
+      const float x0 = load_elem<SX>(a.k_tail, base + n), x1 = load_elem<SX>(a.k_tail, base + n + H2);
+      d = fmaf(x0 * cs - x1 * sn, qg[n], d);
+      d = fmaf(x1 * cs + x0 * sn, qg[n + H2], d);
+    }
+    ts[i] = d * a.scale;
+  }
+  __syncthreads();
+  auto part = [&](int c) { return a.part + ((long long)(c * a.H + h) * a.G + g) * a.PS; };
+  if (tid == 0) {
+    float M = -INFINITY;
+    for (int c = 0; c < a.n_chunks; ++c) M = fmaxf(M, part(c)[0]);
+    for (int i = 0; i < a.n_tail; ++i) M = fmaxf(M, ts[i]);
+    float L = 0.f;
+    for (int c = 0; c < a.n_chunks; ++c) {
+      const float e = expf(part(c)[0] - M);
+      wc[c] = e;
+      L = fmaf(e, part(c)[1], L);
+    }
+    for (int i = 0; i < a.n_tail; ++i) {
+      const float e = expf(ts[i] - M);
+      ts[i] = e;
+      L += e;
+    }
+    Ls = L;
+  }
+  __syncthreads();
+  for (int k = tid; k < a.rTv; k += 256) {
+    float z = 0.f;
+    for (int c = 0; c < a.n_chunks; ++c) z = fmaf(wc[c], part(c)[2 + k], z);
+    zs[k] = z;
+  }
+  for (int n = tid; n < D; n += 256) {
+    float w = 0.f;
+    if (a.bits_v > 0)
+      for (int c = 0; c < a.n_chunks; ++c) w = fmaf(wc[c], part(c)[2 + a.rtv_ld + n], w);
+    wsum[n] = w;
+  }
+  __syncthreads();
+  for (int n = tid; n < D; n += 256) {
+    const float *dm = a.DmV + ((long long)h * D + n) * a.Kd;
+    float o = 0.f;
+    for (int k = 0; k < a.rTv; ++k) o = fmaf(zs[k], dm[k], o);
+    if (a.bits_v > 0)
+      for (int k = 0; k < D; ++k) o = fmaf(wsum[k], a.Q[(long long)n * D + k], o);
+    for (int i = 0; i < a.n_tail; ++i) o = fmaf(ts[i], load_elem<SX>(a.v_tail, ((long long)h * a.n_tail + i) * D + n), o);
+    a.out[(long long)hg * D + n] = o / Ls;
+  }
+}
+
+// G8: the number of query heads per KV head the kernel is built for (its registers hold that many
+// states); up to 4 (grouped-query models) or up to 8
+template <int MF, int SX, int NB16>
+void launch_attend(const AttnArgs &a, hipStream_t st) {
+  const dim3 grid(a.n_chunks, a.H);
+  if (a.G <= 4) {
+    if (a.D == 128) hipLaunchKernelGGL((attend_kernel<MF, SX, NB16, 128, 4>), grid, dim3(NT), 0, st, a);
+    else hipLaunchKernelGGL((attend_kernel<MF, SX, NB16, 64, 4>), grid, dim3(NT), 0, st, a);
+  } else {
+    if (a.D == 128) hipLaunchKernelGGL((attend_kernel<MF, SX, NB16, 128, 8>), grid, dim3(NT), 0, st, a);
+    else hipLaunchKernelGGL((attend_kernel<MF, SX, NB16, 64, 8>), grid, dim3(NT), 0, st, a);
+  }
 }
 
 template <int MF, int SX, int TN>
@@ -847,6 +1160,28 @@ void encode_cells(int dtype, const EncArgs &a, int ncells, int T, int D, int GHm
     else if (dtype == JOLT_BF16) launch_enc_dma<MF_BF16, 4, 2>(a, ncells, T, GHmax, st);
     else launch_enc<MF_BF16, SRC_F32, 4>(a, ncells, T, GHmax, st);
   }
+  HIP_LAUNCH_CHECK();
+}
+
+void attend_cells(int dtype, const AttnArgs &a, hipStream_t st) {
+  JOLT_REQUIRE(a.D == 64 || a.D == 128, JOLT_EINVAL, "attention: d_head must be 64 or 128");
+  JOLT_REQUIRE(a.G >= 1 && a.G <= kAttnMaxG && a.v.rT <= kAttnMaxRank && a.n_chunks >= 1 &&
+                   a.n_chunks <= kAttnMaxChunks && a.chunk % BM == 0,
+               JOLT_EINVAL, "attention: launch shape out of range");
+  if (dtype == JOLT_F16) launch_attend<MF_F16, SRC_F16, 2>(a, st);
+  else if (dtype == JOLT_BF16) launch_attend<MF_BF16, SRC_BF16, 2>(a, st);
+  else launch_attend<MF_BF16, SRC_F32, 2>(a, st);
+  HIP_LAUNCH_CHECK();
+}
+
+void attend_merge(int dtype, const AttnMergeArgs &m, hipStream_t st) {
+  JOLT_REQUIRE(m.n_chunks >= 1 && m.n_chunks <= kAttnMaxChunks && m.n_tail >= 0 && m.n_tail <= kAttnMaxTail &&
+                   m.rTv <= kAttnMaxRank && m.D <= 128,
+               JOLT_EINVAL, "attention merge: shape out of range");
+  const dim3 grid(m.H * m.G);
+  if (dtype == JOLT_F16) hipLaunchKernelGGL(attend_merge_kernel<SRC_F16>, grid, dim3(256), 0, st, m);
+  else if (dtype == JOLT_BF16) hipLaunchKernelGGL(attend_merge_kernel<SRC_BF16>, grid, dim3(256), 0, st, m);
+  else hipLaunchKernelGGL(attend_merge_kernel<SRC_F32>, grid, dim3(256), 0, st, m);
   HIP_LAUNCH_CHECK();
 }
 

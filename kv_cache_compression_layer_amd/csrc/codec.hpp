@@ -39,6 +39,34 @@ struct DecCell {
   int GH, rT, bits, Kd;
 };
 
+// One decode step of one layer over its compressed K and V cells (fused decode).  Slice j of either
+// cell is KV head j of the layer (codes, scales and Dm start at the layer's first head).
+constexpr int kAttnMaxG = 8;          // query heads per KV head
+constexpr int kAttnMaxRank = 512;     // value token rank
+constexpr int kAttnMaxChunks = 2048;  // token chunks of the split
+constexpr int kAttnMaxTail = 1024;    // dense tail tokens
+struct AttnArgs {
+  DecCell k, v;
+  const float *q;     // [H G][D] queries, rotated at their position
+  const float *rope;  // [positions][D/2][2] cosine, sine
+  float *part;        // [n_chunks][H][G][PS]: m, l, z[rtv_ld], w[D]
+  int T, D, H, G, chunk, n_chunks, rtv_ld, PS;
+  float scale;        // 1 / sqrt(d_h)
+};
+struct AttnMergeArgs {
+  const float *part;
+  int n_chunks, H, G, D, T, rTv, rtv_ld, PS, bits_v, Kd;
+  const float *DmV;  // [H][D][Kd]: D_h^T of the value backbone
+  const float *Q;    // [D][D] rotation
+  const void *k_tail, *v_tail;  // [H][n_tail][D] cache dtype, keys before RoPE
+  int n_tail;
+  const float *q, *rope;
+  float scale;
+  float *out;  // [H G][D]
+};
+void attend_cells(int dtype, const AttnArgs &a, hipStream_t st);
+void attend_merge(int dtype, const AttnMergeArgs &m, hipStream_t st);
+
 void encode_cells(int dtype, const EncArgs &a, int ncells, int T, int D, int GHmax, hipStream_t st);
 void decode_cells(int dtype, const DecCell *d_cells, int ncells, int T, int D, int GHmax, hipStream_t st);
 

@@ -396,6 +396,36 @@ void bcat_q(float *Bcat, int ncells, int GH, int D, int Kb, const float *Qt, hip
   hipLaunchKernelGGL(bcat_q_kernel, dim3(grid_for(n)), dim3(256), 0, st, Bcat, ncells, GH, D, Kb, Qt);
   HIP_LAUNCH_CHECK();
 }
+namespace {
+struct RopeArgs {
+  float inv[64];
+  int H2;
+  long long n;
+};
+__global__ void rope_table_kernel(RopeArgs r, float *out) {
+  for (long long e = blockIdx.x * (long long)blockDim.x + threadIdx.x; e < r.n; e += (long long)gridDim.x * blockDim.x) {
+    const long long p = e / r.H2;
+    const int i = (int)(e - p * r.H2);
+    const float a = __fmul_rn((float)p, r.inv[i]);
+    float sn, cs;
+    sincosf(a, &sn, &cs);
+    out[2 * e] = cs;
+    out[2 * e + 1] = sn;
+  }
+}
+}  // namespace
+
+void rope_table(const float *inv, int H2, int n_pos, float *out, hipStream_t st) {
+  JOLT_REQUIRE(H2 >= 1 && H2 <= 64 && n_pos >= 0, JOLT_EINVAL, "rope table: bad shape");
+  RopeArgs r;
+  for (int i = 0; i < H2; ++i) r.inv[i] = inv[i];
+  r.H2 = H2;
+  r.n = (long long)n_pos * H2;
+  if (r.n == 0) return;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(grid_for(r.n)), dim3(256), 0, st, r, out);
+  HIP_LAUNCH_CHECK();
+}
+
 void amax_cells(const float *x, long long per, long long bs, int ncells, float *out, hipStream_t st) {
   fill_f32(out, ncells, 0.f, st);
   int g = (int)std::min<long long>((per + 4095) / 4096, 128);  // about 16 elements per thread, at most 128 groups per cell

@@ -38,5 +38,8 @@ void get_small(int dtype, const FactorCell *cells, int ncells, int kmax, int kma
 void write_headers(const FactorCell *cells, int ncells, hipStream_t st);
 void bcat_q(float *Bcat, int ncells, int GH, int D, int Kb, const float *Qt, hipStream_t st);
 void amax_cells(const float *x, long long per, long long bs, int ncells, float *out, hipStream_t st);
+// RoPE cosine / sine table: out[p][i] = {cos a, sin a}, a = fp32(p) * inv[i] rounded to fp32, for
+// p < n_pos and i < H2 (inv: host array of H2 <= 64 inverse frequencies)
+void rope_table(const float *inv, int H2, int n_pos, float *out, hipStream_t st);
 
 }  // namespace jolt

@@ -25,7 +25,8 @@ EXPORTS = ["jolt_workspace_bytes", "jolt_output_bytes", "jolt_allocate", "jolt_c
            "jolt_spectra", "jolt_token_spectrum_len", "jolt_encode_residual",
            "jolt_encode_residual_workspace_bytes", "jolt_rotation", "jolt_eps2", "jolt_last_error", "jolt_profile",
            "jolt_profile_read", "jolt_sketch_matrix", "jolt_test_wait_policy", "jolt_allocate_static", "jolt_layer_groups",
-           "jolt_layer_groups_workspace_bytes"]
+           "jolt_layer_groups_workspace_bytes", "jolt_rope_table", "jolt_decode_attention_workspace_bytes",
+           "jolt_decode_attention"]
 
 
 class JoltError(RuntimeError):
@@ -96,6 +97,10 @@ def load():
                                              ctypes.POINTER(dbl), P, sz, P]),
         "jolt_test_wait_policy": (ctypes.c_int, [ctypes.c_uint32, i32]),
         "jolt_profile_read": (i32, [ctypes.c_char_p, i32, ctypes.POINTER(dbl), ctypes.POINTER(i32), i32]),
+        "jolt_rope_table": (ctypes.c_int, [i32, dbl, i32, P, P]),
+        "jolt_decode_attention_workspace_bytes": (sz, [pd, ctypes.POINTER(Pick), i32, i32, i32]),
+        "jolt_decode_attention": (ctypes.c_int, [P, pd, pp, ctypes.POINTER(Pick), i32, i32, P, i32, P, P, i32, P, i32,
+                                                 P, P, sz, i32, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -211,6 +216,45 @@ def reconstruct(blob, cfg, picks, K_out, V_out, ws=None):
     arr = _picks_array(picks)
     _check(lib.jolt_reconstruct(_ptr(blob), ctypes.byref(cfg.desc), ctypes.byref(cfg.params), arr, _ptr(K_out),
                                 _ptr(V_out), _ptr(ws), ws.numel(), _stream()))
+
+
+def rope_table(d_head, base, n_pos, device="cuda"):
+    """[n_pos][d_head/2][2] float32 device tensor of RoPE cosines and sines (jolt_rope_table)."""
+    lib = load()
+    out = torch.empty(max(n_pos, 1), d_head // 2, 2, dtype=torch.float32, device=device)
+    _check(lib.jolt_rope_table(int(d_head), float(base), int(n_pos), _ptr(out), _stream()))
+    return out
+
+
+def decode_attention(blob, cfg, picks, seq, layer, q, k_tail=None, v_tail=None, rope=None, rope_base=500000.0,
+                     out=None, ws=None, reuse_prepared=False):
+    """One decode step of one layer over the compressed cells (jolt_decode_attention).
+
+    q: [n_q_heads][d_head] float32 (rotated at its position); k_tail / v_tail: [n_heads][n_tail][d_head]
+    in the cache dtype or None; rope: a rope_table covering T + n_tail positions (built if None);
+    reuse_prepared: ws holds the layer's state from an earlier call on the same layer."""
+    lib = load()
+    arr = _picks_array(picks)
+    q = q.contiguous()
+    n_q, D = q.shape
+    T = cfg.desc.n_tokens
+    n_tail = 0 if k_tail is None else int(k_tail.shape[1])
+    if rope is None:
+        rope = rope_table(D, rope_base, T + n_tail, q.device)
+    if out is None:
+        out = torch.empty(n_q, D, dtype=torch.float32, device=q.device)
+    if ws is None:
+        nb = lib.jolt_decode_attention_workspace_bytes(ctypes.byref(cfg.desc), arr, int(seq), int(layer), int(n_q))
+        if nb == 0:
+            raise JoltError(-1, "decode_attention: invalid arguments")
+        ws = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    kt = k_tail.contiguous() if k_tail is not None else None
+    vt = v_tail.contiguous() if v_tail is not None else None
+    _check(lib.jolt_decode_attention(_ptr(blob), ctypes.byref(cfg.desc), ctypes.byref(cfg.params), arr, int(seq),
+                                     int(layer), _ptr(q), int(n_q), _ptr(kt) if kt is not None else None,
+                                     _ptr(vt) if vt is not None else None, n_tail, _ptr(rope), int(rope.shape[0]),
+                                     _ptr(out), _ptr(ws), ws.numel(), int(bool(reuse_prepared)), _stream()))
+    return out
 
 
 def spectra(K, V, cfg, n_vec=0, ws=None):
