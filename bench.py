@@ -44,9 +44,10 @@ def parse():
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="print a per-kernel summary of a rocprofv3 --kernel-trace --output-format csv directory")
-    ap.add_argument("--traffic-from", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="rocprofv3 --pmc csv directories (FETCH_SIZE / WRITE_SIZE of this bench and of "
-                         "--calibrate-copy): write profiles/traffic.json for the dominant kernel and print a summary")
+    ap.add_argument("--traffic-from", nargs=5, metavar=("KERNEL", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="KERNEL: project_gemm or residual_encode (with '@tag' for another workload); then "
+                         "rocprofv3 --pmc csv directories (FETCH_SIZE / WRITE_SIZE of this bench and of "
+                         "--calibrate-copy): add the kernel to profiles/traffic.json and print a summary")
     return ap.parse_args()
 
 
@@ -57,19 +58,23 @@ LAUNCHES_PER_RECORD = {"sketch_gemm": 2, "transpose_x": 2}
 # times the fp16 cache), one launch over the 16 cells
 # (one launch covers all 16 cells, split 4-fold along K = T; the launch shape is set by the
 # library's sequencing, hence api.cpp among the sources whose change invalidates the counters)
-TRAFFIC_KERNEL = {"stage": "project_gemm", "name": "gemm_dma_kernel<0, 2, 1, 3, 8, 3, 4, 2>", "cells_per_launch": 16,
-                  "splits": 4,
-                  "sources": ["kv_cache_compression_layer_amd/csrc/gemm_dma.hip",
-                              "kv_cache_compression_layer_amd/csrc/gemm_core.hpp",
-                              "kv_cache_compression_layer_amd/csrc/common.hpp",
-                              "kv_cache_compression_layer_amd/csrc/api.cpp"]}
-
-
-def project_grid(cells, splits=1, ell=522, M=4096):
-    """Work-items of a projection launch over `cells` cells as the profiler reports them
-    (192 x 256 tiles of 512 threads, one block per tile, K split and cell)."""
-    tiles = -(-ell // 192) * -(-M // 256)
-    return tiles * 512 * cells * splits
+# Kernels whose HBM traffic is read from rocprofv3 counters: the kernel, how to find its dispatches
+# (its grid for the 8B shape, or the largest grid of that kernel) and the sources its code and launch
+# come from (the counters stand only while these hash the same).
+TRAFFIC_KERNELS = {
+    "project_gemm": {"name": "gemm_dma_kernel<0, 2, 1, 3, 8, 3, 4, 2>", "grid": 3 * 16 * 512 * 16 * 4,
+                     "sources": ["kv_cache_compression_layer_amd/csrc/gemm_dma.hip",
+                                 "kv_cache_compression_layer_amd/csrc/gemm_core.hpp",
+                                 "kv_cache_compression_layer_amd/csrc/dma.hpp",
+                                 "kv_cache_compression_layer_amd/csrc/common.hpp",
+                                 "kv_cache_compression_layer_amd/csrc/api.cpp"]},
+    "residual_encode": {"name": "encode_dma_kernel<0, 8, 2, 2>", "grid": None,
+                        "sources": ["kv_cache_compression_layer_amd/csrc/codec.hip",
+                                    "kv_cache_compression_layer_amd/csrc/gemm_core.hpp",
+                                    "kv_cache_compression_layer_amd/csrc/dma.hpp",
+                                    "kv_cache_compression_layer_amd/csrc/common.hpp",
+                                    "kv_cache_compression_layer_amd/csrc/api.cpp"]},
+}
 
 
 def _rows(d, fname):
@@ -103,14 +108,21 @@ def summarize_profile(d):
     return "\n".join(out)
 
 
-def traffic_from(fetch, write, cfetch, cwrite):
-    """HBM bytes per launch of the dominant kernel: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
-    each scaled by what the same counter reads for a plain copy of known size."""
+def traffic_from(key, fetch, write, cfetch, cwrite):
+    """HBM bytes per launch of a kernel (key: a TRAFFIC_KERNELS stage, optionally '@<tag>' for another
+    workload): FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for a plain copy of known size."""
+    stage = key.split("@")[0]
+    tk = TRAFFIC_KERNELS[stage]
+
     def counter(d, pick):
         vals = [float(r["Counter_Value"]) for r in _rows(d, "run_counter_collection.csv") if pick(r)]
         return sum(vals) / len(vals), len(vals)
-    grid = project_grid(TRAFFIC_KERNEL["cells_per_launch"], TRAFFIC_KERNEL["splits"])
-    is_k = lambda r: TRAFFIC_KERNEL["name"] in r["Kernel_Name"] and int(r["Grid_Size"]) == grid
+    grid = tk["grid"]
+    if grid is None:
+        grid = max(int(r["Grid_Size"]) for r in _rows(fetch, "run_counter_collection.csv")
+                   if tk["name"] in r["Kernel_Name"])
+    is_k = lambda r: tk["name"] in r["Kernel_Name"] and int(r["Grid_Size"]) == grid
     is_copy = lambda r: "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower()
     f_kib, nf = counter(fetch, is_k)
     w_kib, nw = counter(write, is_k)
@@ -119,8 +131,8 @@ def traffic_from(fetch, write, cfetch, cwrite):
     fscale = COPY_BYTES / (cf_kib * 1024.0)
     wscale = COPY_BYTES / (cw_kib * 1024.0)
     bytes_per_launch = f_kib * 1024.0 * fscale + w_kib * 1024.0 * wscale
-    ent = {"kernel": TRAFFIC_KERNEL["name"], "grid_items": grid, "sources": TRAFFIC_KERNEL["sources"],
-           "source_hash": source_hash(TRAFFIC_KERNEL["sources"]), "fetch_kib": f_kib, "write_kib": w_kib,
+    ent = {"kernel": tk["name"], "grid_items": grid, "sources": tk["sources"],
+           "source_hash": source_hash(tk["sources"]), "fetch_kib": f_kib, "write_kib": w_kib,
            "fetch_scale": fscale, "write_scale": wscale, "bytes_per_launch": bytes_per_launch,
            "dispatches": [nf, nw]}
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -128,7 +140,7 @@ def traffic_from(fetch, write, cfetch, cwrite):
     if os.path.exists(path):
         with open(path) as f:
             t = json.load(f)
-    t[TRAFFIC_KERNEL["stage"]] = ent
+    t[key] = ent
     with open(path, "w") as f:
         json.dump(t, f, indent=1)
     return ("kernel %s (grid %d work-items), %d/%d dispatches\n"
@@ -470,10 +482,13 @@ def main():
                            n_outliers=4, dtype=a.dtype, seed=0, device="cuda")
     torch.cuda.synchronize()
     gen_s = time.time() - t0
-    rT = list(range(8, 513, 8))
     rd = list(range(8, D + 1, 8))
     bits = [2, 4, 8]
     eps2 = jolt.eps2(D)
+    # token ranks 8 .. q_cap (Eq. (5): 512 at 2x and T = 65536)
+    probe = jolt.Config(1, L, H, T, D, dt, groups, jolt.FLASH, [8], rd, bits, a.ratio)
+    qcap = probe.token_spectrum_len() - 1
+    rT = list(range(8, qcap + 1, 8))
     cfg = jolt.Config(1, L, H, T, D, dt, groups, jolt.FLASH, rT, rd, bits, a.ratio, oversample=10, power_iters=1,
                       eps2={b: eps2[b] for b in range(9)})
     ws = torch.empty(cfg.workspace_bytes(), dtype=torch.uint8, device="cuda")
@@ -500,7 +515,7 @@ def main():
     torch.cuda.synchronize()
     stages = jolt.profile_read()
     jolt.profile(False)
-    ell = min(512 + 10, T)
+    ell = min(qcap + 10, T, G * H * D)
     models = stage_models(T, L, H, D, G, ell, picks, 2)
     table = stage_table(stages, models, a.dtype)
     # The dominant kernel: the stage with the largest time.  Its rate is its algorithmic work over its
@@ -556,7 +571,7 @@ def main():
         "dtype": a.dtype,
         "data": "synthetic",
         "config": {"workload": f"LLaMA-3.1-8B-shaped KV cache, 32 layers (groups of 4) x 8 KV heads x "
-                               f"T={T} x d_head 128, {a.dtype}, FlashJoLT (p=10, 1 power iteration, q_cap=512), "
+                               f"T={T} x d_head 128, {a.dtype}, FlashJoLT (p=10, 1 power iteration, q_cap={qcap}), "
                                f"budget {a.ratio}x",
                    "global_batch": 1, "seq_len": T, "parallelism": "single GPU", "target_ratio": a.ratio,
                    "achieved_ratio": round(dense / max(total_bytes, 1), 3), "lambda": lam,
