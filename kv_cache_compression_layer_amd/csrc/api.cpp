@@ -578,7 +578,13 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   // P'^T = Y^T X_(T) (ell x M) and P' = (P'^T)^T, from the planes of Y^T when they are in b.pln.  K = T
   // is long: the product is split along K (more, shorter blocks fill the last wave of the grid) and
   // the partials are summed in fixed order by the reduction, which writes both layouts and max |P'|.
+  // A basis formed explicitly writes its planes directly (below), split with the scale of this bound:
+  // an orthonormal basis has entries of magnitude at most 1, the bound leaves room for the loss of
+  // orthogonality of one Cholesky-QR pass (a larger entry overflows the fp16 plane and the spectrum
+  // comes out non-finite, reported).
+  constexpr float kBasisBound = 2.f;
   const int pns = project_splits(pl);
+  // q_amax null: Q^T's planes were split with the scale of kBasisBound
   auto project = [&](const float *Qt, const float *q_amax, float *c_amax) {
     if (xready) {
       HIP_TRY(hipStreamWaitEvent(st, xready, 0));
@@ -589,6 +595,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     GemmArgs g = ga();
     g.A = Qt; g.M = (int)ell; g.N = (int)Mf; g.K = (int)T;
     g.a_ld = Tld; g.a_bs = ell * Tld; g.a_amax = q_amax;
+    if (!q_amax) g.a_amax_c = kBasisBound;
     g.B = b.Xt; g.b_ld = Tld; g.b_bs = Mf * Tld;
     g.m_fastest = 1;
     if (pns <= 1) {
@@ -637,23 +644,33 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   // written unless `rows` asks for Q = (Q^T)^T too: the next projection reads nothing else.
   // (Projecting Y and applying R^{-1} afterwards would save this product but amplifies the
   // projection's rounding by the condition of Y.)
-  auto orthonormalise = [&](Pair y, Pair q, bool rows) {
+  // With the basis planes in use and no row layout asked for, Q^T goes straight into b.pln as the
+  // projection's planes (scale of kBasisBound) instead of fp32.  Returns whether it did.
+  auto orthonormalise = [&](Pair y, Pair q, bool rows) -> bool {
     chol_only(y);
     Stage prof("cholqr_tall", st);
-    fill_f32(q.am, nb, 0.f, st);
+    const bool to_planes = tplanes && !rows;
     GemmArgs g = ga();
     g.A = b.RinvT; g.a_ld = ld; g.a_bs = ell * ld; g.a_amax = amR;
     g.B = y.R; g.b_ld = ld; g.b_bs = T * ld; g.b_amax = y.am;
     g.ab_amax_bs = 1;
     g.M = (int)ell; g.N = (int)T; g.K = (int)ell;
-    g.C = q.T; g.c_ld = Tld; g.c_bs = ell * Tld;
-    if (rows) {
-      g.C2 = q.R; g.c2_ld = ld; g.c2_bs = T * ld;
+    g.c_ld = Tld; g.c_bs = ell * Tld;
+    if (to_planes) {
+      g.Cpl = b.pln; g.cpl_ps = ell * Tld; g.cpl_bs = P32 * ell * Tld;
+      g.cpl_amax = kBasisBound; g.cpl_mf = pl.xmf();
+    } else {
+      fill_f32(q.am, nb, 0.f, st);
+      g.C = q.T;
+      g.c_amax = q.am;
+      if (rows) {
+        g.C2 = q.R; g.c2_ld = ld; g.c2_bs = T * ld;
+      }
     }
-    g.c_amax = q.am;
     g.m_fastest = 1;
     g.tri = 4;
     gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
+    return to_planes;
   };
   // The final basis stays implicit: Q = Y R^{-1} is never formed.  Its Gram gives R, the projection
   // runs on Y (P' = Y^T X_(T)), B = Q^T X_(T) = R^{-T} P'^T, and the fit reads Y and R^{-1} instead of
@@ -665,11 +682,11 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   split_basis(Y.T, Y.am);
   for (int it = 0; it < pl.power_iters; ++it) {
     Pair Q = (Y.T == pa.T) ? pb : pa;
-    orthonormalise(Y, Q, false);
+    const bool direct = orthonormalise(Y, Q, false);
     if (it == 0 && mark) HIP_TRY(hipEventRecord(mark, st));
-    split_basis(Q.T, Q.am);
+    if (!direct) split_basis(Q.T, Q.am);
     fill_f32(amP, nb, 0.f, st);
-    project(Q.T, Q.am, amP);
+    project(Q.T, direct ? nullptr : Q.am, amP);
     {
       // Z = orth(P) by Cholesky QR; Z^T feeds the next sketch
       Stage prof_z("cholqr_z", st);
@@ -1548,6 +1565,9 @@ std::vector<Part> split_parts(const jolt_cache_desc *d) {
 bool equal_groups(const jolt_cache_desc *d) { return split_parts(d).size() == 1; }
 
 // Dense reconstruction of the given cells (all of one group size, as pl describes them)
+// The matrix-core type of the residual decode for a cache dtype (fp32 caches decode on bf16 planes).
+int dec_mf(int dtype) { return dtype == JOLT_F16 ? MF_F16 : MF_BF16; }
+
 struct RecCell {
   const jolt_pick *p;
   char *out;  // [G][H][T][D] in the cache dtype
@@ -1569,6 +1589,9 @@ void reconstruct_cells(const Plan &pl, const std::vector<RecCell> &cells, const 
   float *Cr = ar.take<float>((long long)nb * GH * kmax * kmd);
   float *Dm = ar.take<float>((long long)nb * GH * D * Kd);
   float *am = ar.take<float>(2LL * nb);
+  const int dmf = dec_mf(pl.dtype), np = dmf == MF_F16 ? 2 : 3;  // the decode's matrix-core type and planes
+  uint16_t *Dpl = ar.take<uint16_t>((long long)np * nb * GH * D * Kd);
+  uint16_t *Qpl = ar.take<uint16_t>((long long)np * D * D);
   char *params_area = ar.take<char>(64 * 1024 + (long long)nb * (sizeof(FactorCell) + sizeof(DecCell)) + 2LL * D * D * 4);
   Upload u;
   std::vector<FactorCell> fc(nb);
@@ -1592,6 +1615,10 @@ void reconstruct_cells(const Plan &pl, const std::vector<RecCell> &cells, const 
     DecCell &d = dc[c];
     d.UT = f.UT;
     d.Dm = Dm + (long long)c * GH * D * Kd;
+    d.Dpl = Dpl + (long long)c * np * GH * D * Kd;
+    d.dpl_ps = (long long)GH * D * Kd;
+    d.Qpl = Qpl;
+    d.qpl_ps = (long long)D * D;
     d.Q = nullptr;  // bound after upload
     d.d_amax = nullptr;
     d.scales = (const float *)(blob + p.offset + sec.off_scales);
@@ -1622,6 +1649,10 @@ void reconstruct_cells(const Plan &pl, const std::vector<RecCell> &cells, const 
   g.C = Dm; g.c_ld = Kd; g.c_bs = (long long)GH * D * Kd; g.c_bs2 = (long long)D * Kd;
   gemm(MF_F16, SRC_F32, false, SRC_F32, true, g, nb * GH, 1, st);
   amax_cells(Dm, (long long)GH * D * Kd, (long long)GH * D * Kd, nb, am, st);
+  // the 16-bit planes the tile rebuild reads: D_j after the scale of its cell's |max|, Q after that of 1
+  split_planes(dmf, Dm, (long long)GH * D * Kd, Kd, GH * D, Kd, Kd, Dpl, (long long)np * GH * D * Kd,
+               (long long)GH * D * Kd, Kd, am, 1, nb, st);
+  split_planes(dmf, Qdev, 0, D, D, D, D, Qpl, 0, (long long)D * D, D, nullptr, 0, 1, st);
   Stage prof("residual_decode", st);
   decode_cells(pl.dtype, (const DecCell *)(params_area + o_dc), nb, pl.T, D, GH, st);
 }
@@ -2251,6 +2282,7 @@ AttnPlan attn_plan(const jolt_cache_desc *d, const jolt_pick *picks, int seq, in
 
 struct AttnBufs {
   float *Udr, *Cr, *Dm, *am, *part;
+  uint16_t *Dpl, *Qpl;
   char *params;
 };
 AttnBufs carve_attn(Arena &ar, const AttnPlan &a) {
@@ -2258,6 +2290,8 @@ AttnBufs carve_attn(Arena &ar, const AttnPlan &a) {
   b.Udr = ar.take<float>(2LL * a.kmd * a.D);
   b.Cr = ar.take<float>(2LL * a.H * a.kmax * a.kmd);
   b.Dm = ar.take<float>(2LL * a.H * a.D * a.Kd);
+  b.Dpl = ar.take<uint16_t>(3LL * 2 * a.H * a.D * a.Kd);
+  b.Qpl = ar.take<uint16_t>(3LL * a.D * a.D);
   b.am = ar.take<float>(4);
   b.part = ar.take<float>((long long)a.n_chunks * a.H * a.G * a.PS);
   b.params = ar.take<char>(64 * 1024 + 2LL * a.D * a.D * 4);
@@ -2308,6 +2342,7 @@ int jolt_decode_attention(const void *d_blob, const jolt_cache_desc *desc, const
     ar.cap = ws_bytes;
     AttnBufs b = carve_attn(ar, a);
     const int H = a.H, D = a.D;
+    const int dmf = dec_mf(a.dtype), np = dmf == MF_F16 ? 2 : 3;  // the tile rebuild's type and planes
     const char *blob = (const char *)d_blob;
     Upload u;
     FactorCell fc[2];
@@ -2333,6 +2368,10 @@ int jolt_decode_attention(const void *d_blob, const jolt_cache_desc *desc, const
       DecCell &d = dc[t];
       d.UT = f.UT;
       d.Dm = b.Dm + (long long)t * H * D * a.Kd;
+      d.Dpl = b.Dpl + (long long)t * np * H * D * a.Kd;
+      d.dpl_ps = (long long)H * D * a.Kd;
+      d.Qpl = b.Qpl;
+      d.qpl_ps = (long long)D * D;
       d.Q = Qdev;
       d.d_amax = b.am + t;
       d.scales = (const float *)(base + sec.off_scales) + rows0;
@@ -2358,6 +2397,9 @@ int jolt_decode_attention(const void *d_blob, const jolt_cache_desc *desc, const
       g.C = b.Dm; g.c_ld = a.Kd; g.c_bs = (long long)H * D * a.Kd; g.c_bs2 = (long long)D * a.Kd;
       gemm(MF_F16, SRC_F32, false, SRC_F32, true, g, 2 * H, 1, st);
       amax_cells(b.Dm, (long long)H * D * a.Kd, (long long)H * D * a.Kd, 2, b.am, st);
+      split_planes(dmf, b.Dm, (long long)H * D * a.Kd, a.Kd, H * D, a.Kd, a.Kd, b.Dpl, (long long)np * H * D * a.Kd,
+                   (long long)H * D * a.Kd, a.Kd, b.am, 1, 2, st);
+      split_planes(dmf, Qdev, 0, D, D, D, D, b.Qpl, 0, (long long)D * D, D, nullptr, 0, 1, st);
     }
     AttnArgs at;
     at.k = dc[0];

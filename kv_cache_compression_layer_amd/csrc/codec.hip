@@ -699,7 +699,7 @@ __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, in
   // ---- phase 1: codes Q^T, then scale rows ---------------------------------------------------
   if (b > 0) {
     float ca[2][8];
-    Raw8<SRC_F32> rb[2];
+    Raw8<SRC_F16> rb[2][PB];  // Q's planes, raw 16-bit
     auto gload = [&](int k0) {
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
@@ -710,7 +710,9 @@ __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, in
         else
 #pragma unroll
           for (int i = 0; i < 8; ++i) ca[it][i] = 0.f;
-        load_raw8<SRC_F32>(c.Q, (long long)r * D, k0 + kv, D, r < D, 1 << 30, 0, rb[it]);
+#pragma unroll
+        for (int p = 0; p < PB; ++p)
+          load_raw8<SRC_F16>(c.Qpl + p * c.qpl_ps, (long long)r * D, k0 + kv, D, r < D, 1 << 30, 0, rb[it][p]);
       }
     };
     auto lstore = [&](int buf) {
@@ -722,7 +724,9 @@ __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, in
 #pragma unroll
         for (int i = 0; i < 8; ++i) split_planes<SC, MF>(ca[it][i], 1.f, pa[i]);
         lds_store8<1, true>(As, BM, v >> 2, (v & 3) * 8, pa);
-        put8<SRC_F32, MF, PB, NB16>(Bs, BN, v >> 2, (v & 3) * 8, rb[it], qscale);
+#pragma unroll
+        for (int p = 0; p < PB; ++p)
+          *(uint4 *)(Bs + p * BN * LDK + (v >> 2) * LDK + (v & 3) * 8) = rb[it][p].v;
       }
     };
     gload(0);
@@ -752,9 +756,9 @@ __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, in
   }
   // ---- phase 2: + U_T D_j ------------------------------------------------------------------
   {
-    const float *Dj = c.Dm + (long long)j * D * c.Kd;
+    const uint16_t *Dj = c.Dpl + (long long)j * D * c.Kd;
     Raw8<SX> ra[2];
-    Raw8<SRC_F32> rb[2];
+    Raw8<SRC_F16> rb[2][PB];  // D_j's planes, raw 16-bit
     auto gload = [&](int k0) {
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
@@ -762,7 +766,9 @@ __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, in
         int r = v >> 2, kv = (v & 3) * 8;
         int t = t0 + r;
         load_raw8<SX>(c.UT, (long long)t * c.rT, k0 + kv, c.rT, t < T, 1 << 30, 0, ra[it]);
-        load_raw8<SRC_F32>(Dj, (long long)r * c.Kd, k0 + kv, c.rT, r < D, 1 << 30, 0, rb[it]);
+#pragma unroll
+        for (int p = 0; p < PB; ++p)
+          load_raw8<SRC_F16>(Dj + p * c.dpl_ps, (long long)r * c.Kd, k0 + kv, c.rT, r < D, 1 << 30, 0, rb[it][p]);
       }
     };
     auto lstore = [&](int buf) {
@@ -771,7 +777,9 @@ __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, in
       for (int it = 0; it < 2; ++it) {
         int v = tid + it * NT;
         put8<SX, MF, PA, NB16>(As, BM, v >> 2, (v & 3) * 8, ra[it], 1.f);
-        put8<SRC_F32, MF, PB, NB16>(Bs, BN, v >> 2, (v & 3) * 8, rb[it], dscale);
+#pragma unroll
+        for (int p = 0; p < PB; ++p)
+          *(uint4 *)(Bs + p * BN * LDK + (v >> 2) * LDK + (v & 3) * 8) = rb[it][p].v;
       }
     };
     __syncthreads();

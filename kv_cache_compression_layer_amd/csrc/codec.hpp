@@ -27,11 +27,16 @@ struct EncArgs {
   const EncCell *cells;
 };
 
-// One cell of the decode pass.  Dm[j][n][r] = D_j[r][n] (fp32, row pitch Kd); Q row-major.
+// One cell of the decode pass.  Dm[j][n][r] = D_j[r][n] (fp32, row pitch Kd); Q row-major.  The
+// tile rebuild reads both as 16-bit planes split once beforehand (split_planes with the decode's
+// matrix-core type: Dm after the scale of d_amax, Q after the scale of 1).
 struct DecCell {
   const void *UT;      // [T][rT] storage dtype
   const float *Dm;     // [GH][D][Kd]
   const float *Q;      // [D][D] rotation
+  const uint16_t *Dpl; // planes of Dm: [plane][GH][D][Kd], plane stride dpl_ps
+  const uint16_t *Qpl; // planes of Q: [plane][D][D], plane stride qpl_ps
+  long long dpl_ps, qpl_ps;
   const float *d_amax; // device max |Dm|
   const float *scales;
   const uint8_t *codes;

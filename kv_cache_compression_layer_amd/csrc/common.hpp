@@ -161,6 +161,13 @@ struct GemmArgs {
   int tri;
   // operands stored as 16-bit planes (plane-GEMM path): element stride between planes
   long long a_ps, b_ps;
+  // optional (K-contiguous kernel): C written as its 16-bit planes instead of fp32, [plane][M][c_ld]
+  // at plane stride cpl_ps and batch stride cpl_bs, split as split_planes does (type cpl_mf; fp16
+  // planes after the power-of-two scale of the bound cpl_amax on |C|)
+  uint16_t *Cpl;
+  long long cpl_ps, cpl_bs;
+  float cpl_amax;
+  int cpl_mf;
 };
 
 // a_kc: A contiguous along K (else along M); b_kc: B contiguous along K (else along N)

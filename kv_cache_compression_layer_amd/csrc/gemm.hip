@@ -358,6 +358,9 @@ void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int b
   JOLT_REQUIRE(g.tri == 0 || (a_kc && b_kc), JOLT_EINVAL, "gemm: structure flags need K-contiguous operands");
   JOLT_REQUIRE(!(g.tri & 6) || nsplit == 1, JOLT_EINVAL, "gemm: triangular operands need a single split");
   JOLT_REQUIRE(!(g.tri & 1) || g.M == g.N, JOLT_EINVAL, "gemm: upper-triangle output needs a square product");
+  JOLT_REQUIRE(g.Cpl == nullptr || (a_kc && b_kc && nsplit == 1 && g.inner <= 1 && g.C2 == nullptr),
+               JOLT_EINVAL, "gemm: plane output needs K-contiguous operands, one split, no second output");
+  JOLT_REQUIRE(g.Cpl != nullptr || g.C != nullptr, JOLT_EINVAL, "gemm: no output");
   GemmArgs h = g;
   if (nsplit == 1) h.k_chunk = ((g.K + BK - 1) / BK) * BK;
   if (a_kc && b_kc) {

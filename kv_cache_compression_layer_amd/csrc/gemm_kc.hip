@@ -271,8 +271,10 @@ __global__ void __launch_bounds__(KNT) __attribute__((amdgpu_waves_per_eu(W, W))
   }
 
   const float cs = g.alpha / (ascale * bscale);
-  float *Cb = g.C + (long long)batch * g.c_bs + (long long)bin * g.c_bs2 + (long long)split * g.c_split;
+  float *Cb = g.C ? g.C + (long long)batch * g.c_bs + (long long)bin * g.c_bs2 + (long long)split * g.c_split : nullptr;
   float *C2b = g.C2 ? g.C2 + (long long)batch * g.c2_bs : nullptr;
+  uint16_t *Pb = g.Cpl ? g.Cpl + (long long)batch * g.cpl_bs : nullptr;
+  const float pscale = f16_split_scale(g.cpl_amax);
   float lmax = 0.f;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -285,7 +287,22 @@ __global__ void __launch_bounds__(KNT) __attribute__((amdgpu_waves_per_eu(W, W))
         const int m = mb + r;
         if (m < g.M && n < g.N) {
           const float v = acc[i][j][r] * cs;
-          Cb[(long long)m * g.c_ld + n] = v;
+          if (Pb) {
+            uint16_t pl[3];
+            const long long o = (long long)m * g.c_ld + n;
+            if (g.cpl_mf == MF_F16) {
+              split_planes<SRC_F32, MF_F16>(v, pscale, pl);
+              Pb[o] = pl[0];
+              Pb[o + g.cpl_ps] = pl[1];
+            } else {
+              split_planes<SRC_F32, MF_BF16>(v, 1.f, pl);
+              Pb[o] = pl[0];
+              Pb[o + g.cpl_ps] = pl[1];
+              Pb[o + 2 * g.cpl_ps] = pl[2];
+            }
+          } else {
+            Cb[(long long)m * g.c_ld + n] = v;
+          }
           lmax = fmaxf(lmax, fabsf(v));
         }
       }

@@ -67,11 +67,11 @@ def test_mistral7b_shape_flash_full_size(C):
     _properties(Kd, Vd, cfg, picks, rT, rd, bits, C, "f16")
 
 
-def _big(dt, n_seq, L, H, T, D, alpha_v, C, seed=0):
+def _big(dt, n_seq, L, H, T, D, alpha_v, C, seed=0, bits=(2, 4, 8)):
     K, V = synth.power_law(n_seq=n_seq, L=L, H=H, T=T, D=D, dtype=dt, seed=seed, alpha_v=alpha_v, device="cuda")
     groups = list(range(0, L + 1, 4))
     q = oracle.qcap_eq5(T, C)
-    rT, rd, bits = list(range(8, q + 1, 8)), list(range(8, D + 1, 8)), [2, 4, 8]
+    rT, rd, bits = list(range(8, q + 1, 8)), list(range(8, D + 1, 8)), list(bits)
     eps2 = jolt.eps2(D)
     cfg = jolt.Config(n_seq, L, H, T, D, {"f16": jolt.F16, "bf16": jolt.BF16}[dt], groups, jolt.FLASH, rT, rd, bits,
                       C, eps2={b: eps2[b] for b in range(9)})
@@ -88,7 +88,7 @@ def _sampled_oracle(K, groups, sT_gpu, sD_gpu, n2_gpu, dt, flash_omega=None):
     return X, n2
 
 
-@pytest.mark.parametrize("C", [2.0, 5.0])
+@pytest.mark.parametrize("C", [2.0, 3.0, 4.0, 5.0])
 def test_llama31_8b_long_context_full_size(C):
     K, V, groups, cfg, rT, rd, bits = _big("f16", 1, 32, 8, 65536, 128, 0.5, C)
     blob, picks, lam, Ko, Vo = _run(K, V, cfg, groups)
@@ -122,11 +122,23 @@ def test_batched_serving_shape_bf16_full_size():
     _sampled_oracle(K, groups, sT, sD, n2, "bf16")
 
 
-def test_llama2_13b_shape_flash_full_size_sampled_token_spectrum():
-    L, H, T, D, C = 40, 40, 4096, 128, 3.0
-    K, V, groups, cfg, rT, rd, bits = _big("f16", 1, L, H, T, D, 1.0, C)
+@pytest.mark.parametrize("C,bits", [(3.0, (2, 4, 8)), (2.0, (1, 2, 3, 4))])
+def test_llama2_13b_shape_flash_full_size_sampled_token_spectrum(C, bits):
+    """The LLaMA-2-13B shape (40 layers, 40 KV heads, T = 4096) at 3x with {2, 4, 8} and at 2x with
+    the configuration's bit set {1, 2, 3, 4} (odd widths whose codes straddle bytes)."""
+    L, H, T, D = 40, 40, 4096, 128
+    K, V, groups, cfg, rT, rd, bits = _big("f16", 1, L, H, T, D, 1.0, C, bits=bits)
     blob, picks, lam, Ko, Vo = _run(K, V, cfg, groups)
     assert len(picks) == 20
+    dense = 2 * L * H * T * D * 2
+    assert sum(p["bytes"] for p in picks) <= dense / C
+    for p in picks:
+        assert p["rT"] in rT and p["rd"] in rd and p["bits"] in set(bits) | {0}
+    print("picks", [(p["rT"], p["rd"], p["bits"]) for p in picks])
+    for c, p in enumerate(picks):
+        X = (K if c % 2 == 0 else V)[0, groups[c // 2]:groups[c // 2 + 1]].float()
+        Xh = (Ko if c % 2 == 0 else Vo)[0, groups[c // 2]:groups[c // 2 + 1]].float()
+        assert float(torch.linalg.vector_norm(Xh - X) / torch.linalg.vector_norm(X)) < 0.2
     sT, sD, n2, _ = jolt.spectra(K, V, cfg)
     torch.cuda.synchronize()
     sT, sD, n2 = sT.cpu().numpy(), sD.cpu().numpy(), n2.cpu().numpy()
