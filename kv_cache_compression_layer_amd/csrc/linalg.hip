@@ -997,6 +997,12 @@ __global__ void __launch_bounds__(IT) invit_cluster_kernel(const double *d_in, c
   for (int w = 0; w < nt / 64; ++w) tn = fmax(tn, red[w]);
   __syncthreads();
   const double ctol = 1e-7 * fmax(tn, 1e-300);
+  // classical Gram-Schmidt, twice, of each clustered vector against the cluster's earlier vectors:
+  // per pass all coefficients at once (thread per earlier vector, up to CB at a time), then the
+  // update (thread per entry); the tail of a spectrum with a wide dynamic range can form one cluster
+  // of hundreds of vectors, which one reduction per earlier vector would serialise
+  constexpr int CB = 1024;
+  __shared__ double cs[CB];
   for (int j = 1; j < k; ++j) {
     // start of j's cluster, found by every thread (uniform); vectors outside a cluster are final
     // already and need no barrier
@@ -1006,12 +1012,20 @@ __global__ void __launch_bounds__(IT) invit_cluster_kernel(const double *d_in, c
     if (s < j) {
       double *zj = Zb + (long long)j * n;
       for (int pass = 0; pass < 2; ++pass) {
-        for (int i = s; i < j; ++i) {
-          const double *zi = Zb + (long long)i * n;
-          double part = 0.0;
-          for (int q = tid; q < n; q += nt) part += zi[q] * zj[q];
-          double c = block_sum(part, red);
-          for (int q = tid; q < n; q += nt) zj[q] -= c * zi[q];
+        for (int i0 = s; i0 < j; i0 += CB) {
+          const int i1 = min(j, i0 + CB);
+          for (int i = i0 + tid; i < i1; i += nt) {
+            const double *zi = Zb + (long long)i * n;
+            double c = 0.0;
+            for (int q = 0; q < n; ++q) c += zi[q] * zj[q];
+            cs[i - i0] = c;
+          }
+          __syncthreads();
+          for (int q = tid; q < n; q += nt) {
+            double v = zj[q];
+            for (int i = i0; i < i1; ++i) v -= cs[i - i0] * Zb[(long long)i * n + q];
+            zj[q] = v;
+          }
           __syncthreads();
         }
         double part = 0.0;
