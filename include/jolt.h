@@ -190,9 +190,10 @@ int jolt_compress(const void *d_K, const void *d_V, const jolt_cache_desc *desc,
 
 /* Dense reconstruction from a blob (Sec. 3: decoding undoes the rotation and adds the
  * dequantised residual to the low-rank backbone).  d_K_out / d_V_out have the cache layout and
- * dtype of desc.  h_picks are the picks jolt_compress returned: rT, rd, bits and offset of every
- * cell section are read from them (the section headers repeat them for self-description).
- * Only params->rot_seed is used from params.  Fully asynchronous. */
+ * dtype of desc, 16-byte aligned (else JOLT_EINVAL).  h_picks are the picks jolt_compress
+ * returned: rT, rd, bits and offset of every cell section are read from them (the section headers
+ * repeat them for self-description).  Only params->rot_seed is used from params.  Fully
+ * asynchronous. */
 int jolt_reconstruct(const void *d_blob, const jolt_cache_desc *desc, const jolt_params *params,
                      const jolt_pick *h_picks, void *d_K_out, void *d_V_out, void *d_ws,
                      size_t ws_bytes, void *stream);

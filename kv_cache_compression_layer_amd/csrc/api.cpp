@@ -2204,6 +2204,8 @@ int jolt_reconstruct(const void *d_blob, const jolt_cache_desc *desc, const jolt
                      void *stream) {
   return guarded([&]() {
     JOLT_REQUIRE(d_blob && h_picks && d_K_out && d_V_out && desc, JOLT_EINVAL, "null argument");
+    JOLT_REQUIRE(((uintptr_t)d_K_out % 16) == 0 && ((uintptr_t)d_V_out % 16) == 0, JOLT_EINVAL,
+                 "reconstruct: outputs must be 16-byte aligned");
     JOLT_REQUIRE(d_ws != nullptr, JOLT_EWORKSPACE, "null workspace");
     hipStream_t st = S(stream);
     const std::vector<Part> parts = split_parts(desc);

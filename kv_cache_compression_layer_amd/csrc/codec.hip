@@ -678,11 +678,14 @@ struct DecCfg {
 // calling wave's accumulators (row wm 64 + 16 i + 4 (lane / 16) + r, column wn 64 + 16 q + lane % 16
 // for wave (wm, wn)), in real units; rows past T come out zero.  lds: 2 STG halves of staging,
 // srow: BM floats.  Every thread of the block calls it (it synchronises the block).
-template <int MF, int SX, int NB16>
+// QP: planes of Q taken in the codes phase (every caller takes all of them: with the leading plane
+// alone, small elements of a 16-bit reconstruction move by more than their own rounding step)
+template <int MF, int SX, int NB16, int QP>
 __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, int T, int D, uint16_t *lds, float *srow,
                                              f32x4 (&acc)[4][4]) {
   using C = DecCfg<MF, SX, NB16>;
   constexpr int PA = C::PA, PB = C::PB, MAXO = C::MAXO, ASZ = C::ASZ, STG = C::STG;
+  static_assert(QP >= 1 && QP <= PB, "planes of Q");
   constexpr int SC = (MF == MF_F16) ? SRC_F16 : SRC_BF16;  // small integer codes are exact
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -699,7 +702,7 @@ __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, in
   // ---- phase 1: codes Q^T, then scale rows ---------------------------------------------------
   if (b > 0) {
     float ca[2][8];
-    Raw8<SRC_F16> rb[2][PB];  // Q's planes, raw 16-bit
+    Raw8<SRC_F16> rb[2][QP];  // Q's planes, raw 16-bit
     auto gload = [&](int k0) {
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
@@ -711,7 +714,7 @@ __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, in
 #pragma unroll
           for (int i = 0; i < 8; ++i) ca[it][i] = 0.f;
 #pragma unroll
-        for (int p = 0; p < PB; ++p)
+        for (int p = 0; p < QP; ++p)
           load_raw8<SRC_F16>(c.Qpl + p * c.qpl_ps, (long long)r * D, k0 + kv, D, r < D, 1 << 30, 0, rb[it][p]);
       }
     };
@@ -725,7 +728,7 @@ __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, in
         for (int i = 0; i < 8; ++i) split_planes<SC, MF>(ca[it][i], 1.f, pa[i]);
         lds_store8<1, true>(As, BM, v >> 2, (v & 3) * 8, pa);
 #pragma unroll
-        for (int p = 0; p < PB; ++p)
+        for (int p = 0; p < QP; ++p)
           *(uint4 *)(Bs + p * BN * LDK + (v >> 2) * LDK + (v & 3) * 8) = rb[it][p].v;
       }
     };
@@ -736,7 +739,7 @@ __device__ __forceinline__ void rebuild_tile(const DecCell &c, int j, int t0, in
     for (int k0 = 0; k0 < D; k0 += BK) {
       const bool more = k0 + BK < D;
       if (more) gload(k0 + BK);
-      mma_step<MF, 1, PB, MAXO>(lds + buf * STG, lds + buf * STG + ASZ, wm, wn, lane, acc);
+      mma_step<MF, 1, QP, MAXO>(lds + buf * STG, lds + buf * STG + ASZ, wm, wn, lane, acc);
       if (more) lstore(buf ^ 1);
       __syncthreads();
       buf ^= 1;
@@ -816,20 +819,34 @@ __global__ void __launch_bounds__(NT) decode_kernel(const DecCell *cells, int T,
   const int wm = wave >> 1, wn = wave & 1, fr = lane & 15;
   const int t0 = tt * BM;
   f32x4 acc[4][4];
-  rebuild_tile<MF, SX, NB16>(c, j, t0, T, D, lds, srow, acc);
-  const long long obase = (long long)j * T * D;
+  rebuild_tile<MF, SX, NB16, DecCfg<MF, SX, NB16>::PB>(c, j, t0, T, D, lds, srow, acc);
+  // the tile goes through LDS (rounded to the output type, rows padded by 16 bytes) so that every
+  // global store is a whole 16 bytes of a row
+  constexpr int ES = SX == SRC_F32 ? 4 : 2;
+  const int pitch = D * ES + 16;  // bytes
+  char *ob = (char *)lds;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = t0 + wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-      if (t >= T) continue;
+      const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = wn * 64 + q * 16 + fr;
-        if (n < D) store_elem<SX>(c.out, obase + (long long)t * D + n, acc[i][q][r]);
+        if (n < D) {
+          if constexpr (SX == SRC_F32) *(float *)(ob + row * pitch + n * 4) = acc[i][q][r];
+          else if constexpr (SX == SRC_F16) *(uint16_t *)(ob + row * pitch + n * 2) = f32_to_f16_rne(acc[i][q][r]);
+          else *(uint16_t *)(ob + row * pitch + n * 2) = f32_to_bf16_rne(acc[i][q][r]);
+        }
       }
     }
+  __syncthreads();
+  const int cpr = D * ES / 16;  // 16-byte chunks per row
+  char *out = (char *)c.out + ((long long)j * T + t0) * D * ES;
+  for (int w = threadIdx.x; w < BM * cpr; w += NT) {
+    const int row = w / cpr, ch = w - row * cpr;
+    if (t0 + row < T) *(uint4 *)(out + (long long)row * D * ES + ch * 16) = *(const uint4 *)(ob + row * pitch + ch * 16);
+  }
 }
 
 // ------------------------------------------------------------------------------------------ fused decode
@@ -889,7 +906,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G8 <= 4
   __syncthreads();
   for (int t0 = tbeg; t0 < tend; t0 += BM) {
     f32x4 acc[4][4];
-    rebuild_tile<MF, SX, NB16>(a.k, h, t0, T, D, lds, srow, acc);
+    rebuild_tile<MF, SX, NB16, DecCfg<MF, SX, NB16>::PB>(a.k, h, t0, T, D, lds, srow, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
