@@ -269,6 +269,10 @@ int gram_plane_splits(long long rows, long long K, int batch) {
 // chain lose their CUs to the other's), so one chain is used.
 constexpr int kViews = 1;
 
+// Exact mode: token Grams wider than the register-resident one-workgroup reduction take the blocked
+// multi-launch reduction (its panels and partial products need a scratch per cell).
+bool exact_blocked(const Plan &pl) { return pl.mode != JOLT_FLASH && pl.T > 576 && tridiag_blocked_fits((int)pl.T); }
+
 int n_views(const Plan &pl) {
   int v = kViews;
   while (v > 1 && (pl.n_cells % (2 * v) != 0)) --v;  // views hold whole (group, K|V) pairs
@@ -374,6 +378,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
   } else {
     b.bufB = ar.take<float>((long long)nb * sz.kmax * pl.T_ld);  // token factor rows
     b.Zt = ar.take<float>((long long)nb * sz.kmax * pl.M);       // token-projected tensor
+    if (exact_blocked(pl)) b.mwg = ar.take<double>((long long)(tridiag_mwg_bytes((int)pl.T, nb) / sizeof(double)));
   }
   b.Zw = ar.take<double>((long long)nb * sz.kmax * n_tok);
   b.work = ar.take<double>((long long)nb * invit_work_doubles((int)n_tok, sz.kmax));
@@ -778,7 +783,7 @@ void stage_exact(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   });
   reduce_splits(b.part, (long long)ns * T * Tld, T * Tld, ns, 0, (int)T, (int)T, Tld, b.G64, true, T * T, (int)T, nb,
                 st);
-  sym_eigvals(b.G64, T * T, (int)T, (int)T, nb, b.dT, b.eT, b.G64, b.betaT, T, b.specT, pl.nT, true, st);
+  sym_eigvals(b.G64, T * T, (int)T, (int)T, nb, b.dT, b.eT, b.G64, b.betaT, T, b.specT, pl.nT, true, st, b.mwg);
 }
 
 // ----------------------------------------------------------------------------- layer grouping
@@ -1335,6 +1340,8 @@ Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot)
     v.mwg = b.mwg + c0 * (long long)(tridiag_mwg_bytes((int)ell, 1) / sizeof(double));
     v.RinvT = b.RinvT + c0 * ell * ld;
     if (b.pln) v.pln = b.pln + c0 * pl.pln_cell();
+  } else if (b.mwg) {
+    v.mwg = b.mwg + c0 * (long long)(tridiag_mwg_bytes((int)T, 1) / sizeof(double));
   }
   return v;
 }

@@ -775,7 +775,10 @@ __global__ void __launch_bounds__(LT) tridiag_mwg_kernel(const double *A, long l
 // ---------------------------------------------------------------------------------------------
 // Inverse iteration for the k largest eigenvalues of the tridiagonal (d, e); one thread per
 // eigenvector, rows of Z [k][n] (fp64).  Work arrays interleaved [i][j] for coalescing.
-// Then clusters (relative gap <= 1e-7 ||T||) are re-orthogonalised by two passes of Gram-Schmidt.
+// Then clusters (gap <= 1e-9 ||T||) are re-orthogonalised by two passes of Gram-Schmidt: a computed
+// vector is off its eigenvector by about eps ||T|| / gap (backward-stable solves from eigenvalues
+// accurate to a few eps ||T||), so vectors farther apart than that are orthogonal to ~1e-7, well
+// below the fp32 and 16-bit storage of the factors.
 // ---------------------------------------------------------------------------------------------
 constexpr int IT = 512;  // threads of the inverse-iteration kernel (one eigenvector each)
 
@@ -976,7 +979,7 @@ __global__ void __launch_bounds__(64) invit_kernel(const double *d_in, const dou
 }
 
 // Cluster re-orthogonalisation of the inverse-iteration vectors (one workgroup per matrix,
-// sequential over vectors, parallel over entries): eigenvalues closer than 1e-7 ||T|| form a
+// sequential over vectors, parallel over entries): eigenvalues closer than 1e-9 ||T|| form a
 // cluster, whose vectors are orthogonalised in order by two passes of Gram-Schmidt.
 __global__ void __launch_bounds__(IT) invit_cluster_kernel(const double *d_in, const double *e_in, long long t_bs,
                                                            const double *evals_all, long long ev_bs, const int *k_of,
@@ -996,7 +999,7 @@ __global__ void __launch_bounds__(IT) invit_cluster_kernel(const double *d_in, c
   tn = 0.0;
   for (int w = 0; w < nt / 64; ++w) tn = fmax(tn, red[w]);
   __syncthreads();
-  const double ctol = 1e-7 * fmax(tn, 1e-300);
+  const double ctol = 1e-9 * fmax(tn, 1e-300);
   // classical Gram-Schmidt, twice, of each clustered vector against the cluster's earlier vectors:
   // per pass all coefficients at once (thread per earlier vector, up to CB at a time), then the
   // update (thread per entry); the tail of a spectrum with a wide dynamic range can form one cluster
@@ -1041,75 +1044,10 @@ __global__ void __launch_bounds__(IT) invit_cluster_kernel(const double *d_in, c
 }
 
 // ---------------------------------------------------------------------------------------------
-// Back-transformation: z <- H_0 H_1 ... H_{n-3} z for every eigenvector row (block of VB rows
-// held in LDS per workgroup), then sign normalisation (largest-magnitude entry positive) and
-// output as fp64 and/or fp32 rows.
+// Back-transformation z <- H_0 H_1 ... H_{n-3} z of eigenvector rows, then sign normalisation
+// (largest-magnitude entry positive) and output as fp64 and/or fp32 rows.  Matrices above 576
+// take the compact WY blocks of tridiag_blk.hip.
 // ---------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) backtransform_kernel(const double *Zin, long long z_bs, const double *refl,
-                                                            const double *beta, long long t_bs, const int *n_of,
-                                                            int n_fixed, const int *k_of, int vb, double *out64,
-                                                            float *out32, long long out_bs, int out_ld) {
-  extern __shared__ double smem[];
-  const int b = blockIdx.y;
-  const int n = n_of ? n_of[b] : n_fixed;
-  const int k = min(k_of[b], n);
-  const int v0 = blockIdx.x * vb;
-  if (v0 >= k) return;
-  const int nv = min(vb, k - v0);
-  const int tid = threadIdx.x, nt = blockDim.x;
-  double *zs = smem;                  // [nv][n]
-  double *vs = smem + (long long)vb * n;  // reflector
-  double *cs = vs + n;                // per-vector coefficients
-  const double *Zb = Zin + b * z_bs;
-  for (int i = tid; i < nv * n; i += nt) zs[i] = Zb[(long long)(v0 + i / n) * n + (i % n)];
-  const double *Rb = refl + b * t_bs * (long long)n_fixed;
-  const double *bb = beta + b * t_bs;
-  __syncthreads();
-  for (int kk = n - 3; kk >= 0; --kk) {
-    const double bt = bb[kk];
-    if (bt == 0.0) continue;  // uniform across the block
-    const int m = n - kk - 1;
-    for (int i = tid; i < m; i += nt) vs[i] = Rb[(long long)kk * n_fixed + kk + 1 + i];
-    __syncthreads();
-    // one wave per vector computes v^T z
-    const int lane = tid & 63, w = tid >> 6;
-    for (int q = w; q < nv; q += nt / 64) {
-      double s = 0.0;
-      for (int i = lane; i < m; i += 64) s += vs[i] * zs[(long long)q * n + kk + 1 + i];
-      s = warp_sum_d(s);
-      if (lane == 0) cs[q] = bt * s;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < nv * m; idx += nt) {
-      int q = idx / m, i = idx % m;
-      zs[(long long)q * n + kk + 1 + i] -= cs[q] * vs[i];
-    }
-    __syncthreads();
-  }
-  // sign normalisation and output
-  const int lane = tid & 63, w = tid >> 6;
-  for (int q = w; q < nv; q += nt / 64) {
-    double best = -1.0, val = 0.0;
-    int bi = 0;
-    for (int i = lane; i < n; i += 64) {
-      double a = fabs(zs[(long long)q * n + i]);
-      if (a > best) { best = a; bi = i; }
-    }
-    for (int o = 32; o > 0; o >>= 1) {
-      double ob = __shfl_xor(best, o, 64);
-      int oi = __shfl_xor(bi, o, 64);
-      if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-    }
-    val = zs[(long long)q * n + bi];
-    const double sg = (val < 0.0) ? -1.0 : 1.0;
-    for (int i = lane; i < n; i += 64) {
-      double x = sg * zs[(long long)q * n + i];
-      long long o = b * out_bs + (long long)(v0 + q) * out_ld + i;
-      if (out64) out64[o] = x;
-      if (out32) out32[o] = (float)x;
-    }
-  }
-}
 
 // Register variant for n <= 64 NC: each wave owns VPW eigenvector rows, lane l holding entries
 // l + 64 t, and walks all reflectors on its own (no workgroup barriers): per reflector one dot
@@ -1562,14 +1500,16 @@ void ensure_lds_attrs() {
   (void)hipFuncSetAttribute((const void *)tridiag_mwg_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)bisect_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipFuncSetAttribute((const void *)bisect_kernel<16>, hipFuncAttributeMaxDynamicSharedMemorySize, want);
-  (void)hipFuncSetAttribute((const void *)backtransform_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, want);
   (void)hipGetLastError();
   done = true;
 }
 
 size_t tridiag_lds_bytes(int n) { return ((size_t)n * n + 2 * (size_t)n) * sizeof(double); }
 
-size_t tridiag_mwg_bytes(int n, int batch) { return (size_t)batch * (size_t)mwg_doubles(n) * sizeof(double); }
+size_t tridiag_mwg_bytes(int n, int batch) {
+  if (n > 64 * TCH && tridiag_blocked_fits(n)) return (size_t)batch * (size_t)tridiag_blocked_doubles(n) * sizeof(double);
+  return (size_t)batch * (size_t)mwg_doubles(n) * sizeof(double);
+}
 
 namespace {
 
@@ -1615,10 +1555,13 @@ void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d
   ensure_lds_attrs();
   int P = 0, chunk = 0;
   size_t shm_m = 0;
-  const bool multi = lds_full > lds_cap && mwg != nullptr && mwg_plan(n, batch, P, chunk, shm_m);
+  const bool blocked = lds_full > lds_cap && mwg != nullptr && n > 64 * TCH && tridiag_blocked_fits(n);
+  const bool multi = !blocked && lds_full > lds_cap && mwg != nullptr && mwg_plan(n, batch, P, chunk, shm_m);
   if (lds_full <= lds_cap) {
     hipLaunchKernelGGL(tridiag_values_kernel, dim3(batch), dim3(LT), lds_full, st, A, a_bs, lda, (const int *)nullptr,
                        n, d, e, refl, beta, t_bs, evals, ev_bs, clamp ? 1 : 0, 1);
+  } else if (blocked) {
+    tridiag_blocked(A, a_bs, lda, n, batch, d, e, refl, beta, t_bs, mwg, st);
   } else if (multi) {
     const long long ms = mwg_doubles(n);
     const WaitPolicy wp = wait_policy();
@@ -1661,7 +1604,11 @@ void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d
   HIP_LAUNCH_CHECK();
 }
 
-size_t invit_work_doubles(int n, int kmax) { return 6ull * n * kmax + ((size_t)n * kmax + 7) / 8 + 8; }
+// (also the T factors of the WY back-transformation, which runs after inverse iteration)
+size_t invit_work_doubles(int n, int kmax) {
+  const size_t w = 6ull * n * kmax + ((size_t)n * kmax + 7) / 8 + 8;
+  return n > 64 * 9 ? std::max<size_t>(w, (size_t)wy_tfactor_doubles(n)) : w;
+}
 
 void sym_eigvecs(const double *d, const double *e, const double *refl, const double *beta, long long t_bs,
                  const double *evals, long long ev_bs, int n, const int *k_dev, int kmax, int batch, double *Zw,
@@ -1690,13 +1637,9 @@ void sym_eigvecs(const double *d, const double *e, const double *refl, const dou
     HIP_LAUNCH_CHECK();
     return;
   }
-  ensure_lds_attrs();
-  int vb = std::max(1, std::min(32, (int)((60 * 1024) / (n * 8)) - 1));
-  size_t shm = ((size_t)vb * n + n + 64) * sizeof(double);
-  dim3 grid((kmax + vb - 1) / vb, batch);
-  hipLaunchKernelGGL(backtransform_kernel, grid, dim3(256), shm, st, Zw, z_bs, refl, beta, t_bs,
-                     (const int *)nullptr, n, k_dev, vb, out64, out32, out_bs, out_ld);
-  HIP_LAUNCH_CHECK();
+  // larger matrices: reflectors in compact WY blocks (the work array is free again after the
+  // inverse iteration and holds the blocks' T factors)
+  backtransform_wy(Zw, z_bs, refl, beta, t_bs, n, k_dev, kmax, batch, work, w_bs, out64, out32, out_bs, out_ld, st);
 }
 
 long long chol_scratch_doubles(int n) {

@@ -244,3 +244,81 @@ def test_mistral7b_shape_exact_full_size():
         if gap >= 1e-3:
             assert sin <= 1e-3
         assert relx <= tol
+
+
+@pytest.mark.timeout(900)
+def test_llama2_13b_shape_exact_full_size_sampled():
+    """Exact JoLT at the LLaMA-2-13B shape: 20 cells of 4 x 40 x 4096 x 128 fp16, token Grams 4096 x 4096
+    (reduced by the blocked multi-launch tridiagonalisation), token rank grid 8..4096, bits {1, 2, 3, 4},
+    2x.  Every cell: the token spectrum descending and summing to ||X||^2 (the Gram's trace), and the
+    picks and lambda equal to the oracle allocator's on tables built from the GPU's spectra.  The first
+    key cell against the oracle: its exact token spectrum (SVD of the unfolding; relative 1e-4 above
+    1e-7 ||X||^2), the token projector at the picked rank (gap reported) and the oracle's fit, encode and
+    decode on the GPU's factor and picks against the GPU reconstruction."""
+    import time
+    from test_gpu_parity_ranks import xhat_tolerance
+    L, H, T, D, C = 40, 40, 4096, 128, 2.0
+    K, V = synth.power_law(L=L, H=H, T=T, D=D, dtype="f16", seed=0, alpha_v=1.0, device="cuda")
+    groups = list(range(0, L + 1, 4))
+    rT, rd, bits = list(range(8, T + 1, 8)), list(range(8, D + 1, 8)), [1, 2, 3, 4]
+    e = jolt.eps2(D)
+    eps2 = {b: float(e[b]) for b in range(9)}
+    cfg = jolt.Config(1, L, H, T, D, jolt.F16, groups, jolt.EXACT, rT, rd, bits, C, eps2=eps2)
+    torch.cuda.synchronize()
+    t0 = time.time()
+    blob, picks, lam, Ko, Vo = _run(K, V, cfg, groups)
+    print(f"exact compress + reconstruct of the 13B-shaped cache: {time.time() - t0:.2f} s")
+    assert len(picks) == 20
+    dense = 2 * L * H * T * D * 2
+    assert sum(p["bytes"] for p in picks) <= dense / C
+    print("picks", [(p["rT"], p["rd"], p["bits"]) for p in picks])
+    sT, sD, n2, UT = jolt.spectra(K, V, cfg, n_vec=picks[0]["rT"])
+    torch.cuda.synchronize()
+    sT, sD, n2, UT = sT.cpu().numpy(), sD.cpu().numpy(), n2.cpu().numpy(), UT[:1].double().cpu().numpy()
+    assert sT.shape == (20, T)
+    assert np.all(np.diff(sT, axis=1) <= 1e-9 * n2[:, None])
+    assert np.all(np.abs(sT.sum(axis=1) - n2) <= 1e-5 * n2), np.abs(sT.sum(axis=1) / n2 - 1).max()
+    shape = oracle.CellShape(4, H, T, D)
+    allbits = [0] + bits
+    tabs = [oracle.cell_table(shape, 2, sT[c], sD[c], float(n2[c]), rT, rd, allbits, eps2) for c in range(20)]
+    want = oracle.allocate(tabs, dense / C)
+    assert want["status"] == 0 and lam == want["lam"], (lam, want["lam"])
+    for t, i, q in zip(tabs, want["picks"], picks):
+        assert (q["rT"], q["rd"], q["bits"]) == (int(t["rT"][i]), int(t["rd"][i]), int(t["b"][i]))
+    # the first key cell against the oracle
+    X = oracle.to_f64(_np(K[0, groups[0]:groups[1]]), "f16")
+    N2 = float(np.sum(X * X))
+    assert abs(n2[0] - N2) <= 1e-6 * N2
+    assert np.all(np.abs(sD[0] - oracle.feature_spectrum(X)) <= 1e-4 * sD[0] + 1e-7 * N2)
+    t0 = time.time()
+    U, spec = oracle.token_factors_exact(oracle.token_unfolding(X))
+    print(f"oracle SVD of the 4096 x 20480 unfolding: {time.time() - t0:.1f} s")
+    d = np.abs(sT[0] - spec)
+    big = spec > 1e-5 * N2
+    print(f"token spectrum: max |d| {d.max() / N2:.2e} ||X||^2, max rel above 1e-5 ||X||^2 "
+          f"{(d[big] / spec[big]).max():.2e}")
+    assert np.all(d <= 1e-4 * spec + 1e-7 * N2), float(np.max(d - 1e-4 * spec) / N2)
+    p = picks[0]
+    r = p["rT"]
+    gap = (spec[r - 1] - spec[r]) / spec[0]
+    Ug = UT[0][:r].T
+    # orthonormal to the fp32 rounding of the rows (inverse iteration re-orthogonalises only vectors whose
+    # eigenvalues lie within 1e-9 ||T||; the others are orthogonal to about eps ||T|| / gap)
+    orth = np.abs(Ug.T @ Ug - np.eye(r)).max()
+    print(f"cell 0: max |U_T^T U_T - I| over the {r} picked vectors {orth:.2e}")
+    assert orth <= 1e-5
+    sin = np.linalg.norm(Ug @ (Ug.T @ U[:, :r]) - U[:, :r], 2)
+    UTf, Udf, core, _ = oracle.fit_cell(X, Ug, p["rd"])
+    Qrot = oracle.rotation(D, 0)
+    enc = oracle.encode_cell(X, UTf, Udf, core, p["bits"], Qrot, "f16")
+    Xh = oracle.decode_cell(enc["UT"], enc["Ud"], enc["core"], p["bits"], enc.get("u"), enc.get("scales"), Qrot,
+                            X.shape)
+    got = Ko[0, groups[0]:groups[1]].double().cpu().numpy()
+    want_x = oracle.round_to_dtype(Xh, "f16")
+    relx = np.linalg.norm(got - want_x) / np.linalg.norm(want_x)
+    tol = xhat_tolerance(enc.get("scales"), D, np.linalg.norm(want_x), p["bits"]) + 3e-4
+    print(f"cell 0: pick {r, p['rd'], p['bits']}, projector sine {sin:.2e} at gap {gap:.2e}, "
+          f"|Xhat - Xhat_oracle| / |Xhat_oracle| {relx:.2e} (bar {tol:.2e})")
+    if gap >= 1e-3:
+        assert sin <= 1e-3
+    assert relx <= tol
