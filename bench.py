@@ -37,9 +37,10 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dtype", default="f16", choices=["f16", "bf16"])
-    ap.add_argument("--compare-modes", action="store_true",
-                    help="report FlashJoLT against exact JoLT on the Mistral-7B-shaped cache (T = 1024): "
-                         "compression time and relative reconstruction error of K and V at 2x and 3x")
+    ap.add_argument("--compare-modes", nargs="?", const="mistral7b", choices=["mistral7b", "llama2_13b"],
+                    help="report FlashJoLT against exact JoLT on the Mistral-7B-shaped cache (T = 1024, the "
+                         "default) or the LLaMA-2-13B-shaped one (T = 4096): compression time and relative "
+                         "reconstruction error of K and V at 2x and 3x")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -315,15 +316,22 @@ def cpu_baseline(K, V, groups, cfgd, sample_T):
                       f"status {r['status']}"}
 
 
-def compare_modes():
+def compare_modes(shape="mistral7b"):
     """FlashJoLT against exact JoLT on one cache (the pages compare them at 1024-token context): per
     budget and mode, the time of one jolt_compress (median of 5 after a warm-up, HIP events) and the
-    relative Frobenius error of the whole K and V caches after jolt_reconstruct."""
+    relative Frobenius error of the whole K and V caches after jolt_reconstruct.  Shapes: Mistral-7B
+    (32 layers, 8 KV heads, T = 1024, bits {2, 4, 8}) or LLaMA-2-13B (40 layers, 40 KV heads, T = 4096,
+    bits {1, 2, 3, 4}); FlashJoLT's token ranks run to q_cap of Eq. (5), exact ones to T."""
     import torch
     import synth
     from kv_cache_compression_layer_amd import jolt
     torch.cuda.set_device(0)
-    L, H, T, D, G = 32, 8, 1024, 128, 4
+    if shape == "llama2_13b":
+        L, H, T, D, G, bits = 40, 40, 4096, 128, 4, [1, 2, 3, 4]
+        title = "LLaMA-2-13B-shaped KV cache, 40 layers (groups of 4) x 40 KV heads x T=4096"
+    else:
+        L, H, T, D, G, bits = 32, 8, 1024, 128, 4, [2, 4, 8]
+        title = "Mistral-7B-shaped KV cache, 32 layers (groups of 4) x 8 KV heads x T=1024"
     groups = list(range(0, L + 1, G))
     K, V = synth.power_law(n_seq=1, L=L, H=H, T=T, D=D, group=G, alpha_k=1.0, alpha_v=1.0, noise_var=0.02,
                            n_outliers=4, dtype="f16", seed=0, device="cuda")
@@ -332,9 +340,10 @@ def compare_modes():
     rows = {}
     for C in (2.0, 3.0):
         for mode, name in ((jolt.EXACT, "exact"), (jolt.FLASH, "flash")):
-            q = 32 if C <= 4 else 64
+            probe = jolt.Config(1, L, H, T, D, jolt.F16, groups, jolt.FLASH, [8], [8], bits, C)
+            q = probe.token_spectrum_len() - 1
             rT = list(range(8, (T if mode == jolt.EXACT else q) + 1, 8))
-            cfg = jolt.Config(1, L, H, T, D, jolt.F16, groups, mode, rT, list(range(8, D + 1, 8)), [2, 4, 8], C,
+            cfg = jolt.Config(1, L, H, T, D, jolt.F16, groups, mode, rT, list(range(8, D + 1, 8)), bits, C,
                               eps2=eps2)
             ws = torch.empty(cfg.workspace_bytes(), dtype=torch.uint8, device="cuda")
             out = torch.empty(cfg.output_bytes(), dtype=torch.uint8, device="cuda")
@@ -362,8 +371,8 @@ def compare_modes():
         ex, fl = rows[f"exact_{C}"], rows[f"flash_{C}"]
         rows[f"gap_{C}"] = {"dK": round(fl["err_K"] - ex["err_K"], 5), "dV": round(fl["err_V"] - ex["err_V"], 5),
                             "time_ratio_exact_over_flash": round(ex["ms"] / fl["ms"], 3)}
-    print(json.dumps({"workload": "Mistral-7B-shaped KV cache, 32 layers (groups of 4) x 8 KV heads x T=1024 x "
-                                  "d_head 128, f16, synthetic (power law, exponent 1)", "modes": rows}), flush=True)
+    print(json.dumps({"workload": title + " x d_head 128, f16, synthetic (power law, exponent 1)", "modes": rows}),
+          flush=True)
 
 
 def decode_measure(jolt, torch, blob, cfg, picks, T, L, H, D, G, dt, reps=20):
@@ -454,7 +463,7 @@ def decode_measure(jolt, torch, blob, cfg, picks, T, L, H, D, G, dt, reps=20):
 def main():
     a = parse()
     if a.compare_modes:
-        compare_modes()
+        compare_modes(a.compare_modes)
         return
     if a.calibrate_copy:
         calibrate_copy()
