@@ -16,6 +16,7 @@ import oracle
 import synth
 from _checks import lambda_consistency
 from kv_cache_compression_layer_amd import jolt
+from test_gpu_parity_ranks import xhat_tolerance
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +37,12 @@ CASES = {
     "f16_flash_d128": ("pl", "f16", "flash", 1, 8, 4, 700, 128, 2.0, [8, 16, 24, 32], [2, 4, 8]),
     "bf16_flash": ("pl", "bf16", "flash", 1, 4, 2, 1000, 64, 4.0, [8, 16, 24, 32], [1, 2, 3, 4]),
     "f16_flash_two_seqs": ("pl", "f16", "flash", 2, 4, 2, 256, 64, 3.0, [8, 16, 24, 32], [2, 4, 8]),
+    # token Grams wider than 576 (the blocked multi-launch tridiagonalisation and the WY
+    # back-transformation) at ragged sizes: partial 128-wide matvec tiles, a partial panel and a
+    # partial last reflector block
+    "f16_exact_blocked_777": ("pl", "f16", "exact", 1, 4, 2, 777, 128, 2.0, list(range(8, 777, 8)), [2, 4, 8]),
+    "bf16_exact_blocked_1000": ("pl", "bf16", "exact", 1, 8, 2, 1000, 128, 3.0, list(range(8, 1001, 8)),
+                                [1, 2, 3, 4]),
 }
 _cache = {}
 
@@ -211,7 +218,8 @@ def test_compress_end_to_end_matches_oracle(name):
                               oracle.DTYPE_BYTES[c["dt"]], c["rT"], c["rd"], c["bits"], c["p"]["eps2"])
     if ties:
         print("near-tie cells (oracle argmin differs within the spectra difference):", ties)
-    for x in ref["cells"]:
+    gb = blob.cpu().numpy().tobytes()
+    for x, p in zip(ref["cells"], picks):
         got = _cell_view(Ko if x["kv"] == 0 else Vo, x, c["groups"]).double().cpu().numpy()
         X = x["X"]
         err = np.linalg.norm(got - X) / np.linalg.norm(X)
@@ -219,7 +227,17 @@ def test_compress_end_to_end_matches_oracle(name):
         floor = {"f16": 3e-4, "bf16": 2.5e-3, "f32": 1e-6}[c["dt"]]
         assert abs(err - x["rel_err"]) <= 1e-3 + 0.02 * x["rel_err"] + floor, (err, x["rel_err"])
         want = _round(x["Xhat"], c["dt"])
-        assert np.linalg.norm(got - want) / np.linalg.norm(want) <= 1e-3 + floor
+        # the codes come from the GPU's own factors, which round to the storage dtype independently of the
+        # oracle's (a factor entry near a rounding boundary of bf16 takes the neighbouring value): at most
+        # 0.2% of the codes may differ, by one step, and X_hat by what such flips move
+        tol = 1e-3
+        if x["b"] > 0:
+            gu = np.asarray(oracle.read_blob_cell(gb, p["offset"], c["dt"])["u"]).astype(np.int64)
+            ou = np.asarray(oracle.read_blob_cell(ref["blob"], x["offset"], c["dt"])["u"]).astype(np.int64)
+            frac = float(np.mean(gu != ou))
+            assert frac <= 2e-3 and np.abs(gu - ou).max() <= 1, (frac, np.abs(gu - ou).max())
+            tol = xhat_tolerance(x["enc"]["scales"], c["D"], np.linalg.norm(want), x["b"], frac=2e-3)
+        assert np.linalg.norm(got - want) / np.linalg.norm(want) <= tol + floor
 
 
 def test_compress_is_deterministic():

@@ -202,16 +202,17 @@ def _subspace_gap(spec, r):
     return (spec[r - 1] - spec[r]) / spec[0]
 
 
-def xhat_tolerance(scales, D, xhat_norm, b):
-    """Reconstruction bar implied by the code bar: 1e-3 relative, plus what 0.1% of the codes off by one
-    can move X_hat (a flipped code moves its rotated coordinate by one step s of its row, and the rotation
-    keeps norms), i.e. sqrt(1e-3 * D * sum_rows s^2) / ||X_hat||.  b = 0 adds nothing."""
+def xhat_tolerance(scales, D, xhat_norm, b, frac=1e-3):
+    """Reconstruction bar implied by the code bar: 1e-3 relative, plus what a fraction frac (0.1% by
+    default) of the codes off by one can move X_hat (a flipped code moves its rotated coordinate by one
+    step s of its row, and the rotation keeps norms), i.e. sqrt(frac * D * sum_rows s^2) / ||X_hat||.
+    b = 0 adds nothing."""
     if b == 0 or scales is None:
         return 1e-3
     s = np.asarray(scales, dtype=np.float64)
     if b == 1:
         s = 2.0 * s   # a flipped sign code moves the coordinate by 2 absmax
-    return 1e-3 + math.sqrt(1e-3 * D * float(np.sum(s * s))) / xhat_norm
+    return 1e-3 + math.sqrt(frac * D * float(np.sum(s * s))) / xhat_norm
 
 
 @pytest.mark.parametrize("rd,b,C", [(128, 8, 1.2), (64, 4, 2.0)])
