@@ -1591,7 +1591,7 @@ void reconstruct_cells(const Plan &pl, const std::vector<RecCell> &cells, const 
     kmax = std::max(kmax, p.rT);
     kmd = std::max(kmd, p.rd);
   }
-  const int Kd = (int)rup(kmax, 8);
+  const int Kd = (int)rup(kmax, 32);  // whole 32-deep stages of D_j's rows (zero past each cell's r_T)
   float *Udr = ar.take<float>((long long)nb * kmd * D);
   float *Cr = ar.take<float>((long long)nb * GH * kmax * kmd);
   float *Dm = ar.take<float>((long long)nb * GH * D * Kd);
@@ -1646,6 +1646,7 @@ void reconstruct_cells(const Plan &pl, const std::vector<RecCell> &cells, const 
   fill_f32(Cr, (long long)nb * GH * kmax * kmd, 0.f, st);
   get_small(pl.dtype, d_fc, nb, kmax, kmd, D, GH, Udr, Cr, st);
   amax_cells(Cr, (long long)GH * kmax * kmd, (long long)GH * kmax * kmd, nb, am + nb, st);
+  fill_f32(Dm, (long long)nb * GH * D * Kd, 0.f, st);  // the product writes columns < kmax
   // Dm[cell][j][n][r] = sum_kk Udr[kk][n] Cr[j][r][kk]
   GemmArgs g = ga();
   g.A = Udr; g.a_ld = D; g.a_bs = (long long)kmd * D; g.a_bs2 = 0; g.a_amax_c = 1.f;
@@ -2285,7 +2286,7 @@ AttnPlan attn_plan(const jolt_cache_desc *d, const jolt_pick *picks, int seq, in
   a.PS = 2 + a.rtv_ld + a.D;
   a.kmax = std::max(a.pk->rT, a.pv->rT);
   a.kmd = std::max(a.pk->rd, a.pv->rd);
-  a.Kd = (int)rup(a.kmax, 8);
+  a.Kd = (int)rup(a.kmax, 32);  // whole 32-deep stages of D_h's rows (zero past each cell's r_T)
   return a;
 }
 
@@ -2397,6 +2398,7 @@ int jolt_decode_attention(const void *d_blob, const jolt_cache_desc *desc, const
       fill_f32(b.Cr, 2LL * H * a.kmax * a.kmd, 0.f, st);
       get_small(a.dtype, (const FactorCell *)(b.params + o_fc), 2, a.kmax, a.kmd, D, H, b.Udr, b.Cr, st);
       amax_cells(b.Cr, (long long)H * a.kmax * a.kmd, (long long)H * a.kmax * a.kmd, 2, b.am + 2, st);
+      fill_f32(b.Dm, 2LL * H * D * a.Kd, 0.f, st);  // the product writes columns < kmax
       GemmArgs g = ga();
       g.A = b.Udr; g.a_ld = D; g.a_bs = (long long)a.kmd * D; g.a_bs2 = 0; g.a_amax_c = 1.f;
       g.B = b.Cr; g.b_ld = a.kmd; g.b_bs = (long long)H * a.kmax * a.kmd; g.b_bs2 = (long long)a.kmax * a.kmd;

@@ -849,7 +849,385 @@ __global__ void __launch_bounds__(NT) decode_kernel(const DecCell *cells, int T,
   }
 }
 
+// ------------------------------------------------------------------------------- decode (DMA-fed)
+// 16-bit caches.  X_hat_j = s o (C_j Q^T) + U_T D_j as one loop of 32-deep stages over k in
+// [0, D + r_T): B = the planes of Q (k < D, shared by every slice) and then of D_j (k >= D, rows zero
+// from r_T up to the padded pitch), global -> LDS by DMA; A = the codes for k < D (the stage's packed
+// code words go to LDS by DMA and each lane unpacks its fragments: small integers, exact in 16 bits)
+// and the U_T rows for k >= D (DMA; columns past r_T meet the zero rows of B).  After the last codes
+// stage the rows are scaled by s and moved into D_j's split frame, as in rebuild_tile.  Block: 256
+// token rows of one (cell, slice) on four waves of 128 rows x D/2 columns (the encode's tile and block
+// order); each lane stores its four consecutive columns of a row straight from the accumulators.
+template <int MF, int TN>
+struct YCfg {
+  static constexpr int NS = 2, NWR = 2;
+  static constexpr int D = TN * 16, NW = 2 * NWR, NT = 64 * NW, ROWS = 128 * NWR;
+  static constexpr int PB = (MF == MF_F16) ? 2 : 3;    // planes of B
+  static constexpr int MAXO = (MF == MF_F16) ? 1 : 2;  // plane products kept: pb <= MAXO (A has one plane)
+  static constexpr int WR = 128, WC = D / 2, TI = WR / 16, TQ = WC / 16;
+  static constexpr int ASZ = ROWS * dma::DK, BSZ = PB * D * dma::DK, STG = ASZ + BSZ;  // halves per stage
+  static constexpr int NGA = ROWS / 16, NGB = PB * D / 16, NA = NGA / NW, NBS = (NGB + NW - 1) / NW;
+  static_assert(NGA % NW == 0, "A groups split evenly over the waves");
+  static_assert(ROWS * 8 * 4 + 12 <= ASZ * 2, "a stage's code words fit in its A area");
+  static_assert(NS * STG * 2 <= 80 * 1024, "two blocks per CU");
+};
+
+template <int MF, int TN>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_dma_kernel(const DecCell *cells, int T, int ttiles, int GHmax) {
+  using C = YCfg<MF, TN>;
+  using namespace dma;
+  constexpr int D = C::D, PB = C::PB, TI = C::TI, TQ = C::TQ, NW = C::NW, NA = C::NA, NBS = C::NBS;
+  constexpr int NGA = C::NGA, ROWS = C::ROWS;
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[C::NS * C::STG];
+  lds16 *const L0 = (lds16 *)lds_raw, *const L1 = L0 + C::STG;
+
+  int tt, j, cz;
+  {
+    const long long gx = gridDim.x, total = gx * gridDim.z;
+    long long L = blockIdx.x + gx * blockIdx.z;
+    const long long per = total / 8;
+    if (L < per * 8) L = (L % 8) * per + L / 8;
+    cz = (int)(L / gx);
+    const int x = (int)(L % gx);
+    if (x >= GHmax * ttiles) return;
+    enc_order(x, GHmax, ttiles, j, tt);
+  }
+  // block-uniform fields in scalar registers (descriptors built from them stay scalar)
+  const DecCell cv = cells[cz];
+  const int GH = __builtin_amdgcn_readfirstlane(cv.GH), rT = __builtin_amdgcn_readfirstlane(cv.rT);
+  const int b = __builtin_amdgcn_readfirstlane(cv.bits), Kd = __builtin_amdgcn_readfirstlane(cv.Kd);
+  if (j >= GH) return;
+  const char *ut = (const char *)uniform64((long long)cv.UT);
+  const char *dpl = (const char *)uniform64((long long)cv.Dpl);
+  const char *qpl = (const char *)uniform64((long long)cv.Qpl);
+  const long long dpl_ps = uniform64(cv.dpl_ps), qpl_ps = uniform64(cv.qpl_ps);
+  const uint8_t *codes = (const uint8_t *)uniform64((long long)cv.codes);
+  const float *scales = (const float *)uniform64((long long)cv.scales);
+  char *out = (char *)uniform64((long long)cv.out);
+  const float qscale = (MF == MF_F16) ? f16_split_scale(1.f) : 1.f;
+  const float dscale = (MF == MF_F16) ? f16_split_scale(*(const float *)uniform64((long long)cv.d_amax)) : 1.f;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1, fr = lane & 15, fc = lane >> 4;
+  const int t0 = tt * ROWS;
+  const int kbeg = b > 0 ? 0 : D, kend = D + rT;
+  const int nsteps = (kend - kbeg + DK - 1) / DK;
+
+  const i32x4 rsu = make_rsrc(ut, (uint32_t)((long long)T * rT * 2));
+  const i32x4 rsq = make_rsrc(qpl, 0xFFFFFFFFu);
+  const i32x4 rsd = make_rsrc(dpl + (long long)j * D * Kd * 2, 0xFFFFFFFFu);
+  const long long rowbytes = (long long)D * b / 8;  // packed codes per row
+  const i32x4 rsc = make_rsrc(codes + (long long)j * T * rowbytes, (uint32_t)(T * rowbytes));
+  // DMA requests of one stage (offsets formed per request: fewer live registers).  A: lane -> row
+  // lane / 4 of a 16-row group, logical chunk (lane % 4) ^ ((row / 2) % 4); B: group w + NW i of this
+  // wave (past the last group it repeats group w % NGB: the same bytes to the same place as the wave
+  // that owns it).  Codes: request m of wave w covers rows 8 (m NW + w) .. + 7, lane -> row lane / 8,
+  // word lane % 8 of the row's bytes from (k / 8) b on.
+  const int lr = lane >> 2, lp = lane & 3;
+  auto issue = [&](lds16 *dst, int k) __attribute__((always_inline)) {
+    if (k < D) {
+#pragma unroll
+      for (int m = 0; m < ROWS / 8 / NW; ++m) {
+        const int rq = m * NW + wave, row = rq * 8 + (lane >> 3);
+        const long long off = (long long)(t0 + row) * rowbytes + (k / 8) * b + 4 * (lane & 7);
+        raw_buffer_load_lds(rsc, (__attribute__((address_space(3))) uint32_t *)dst + rq * 64, 4,
+                            (int)min(off, 0xFFFFFFF0LL), 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int row = (i * NW + wave) * 16 + lr, ch = (lp ^ (row >> 1)) & 3;
+        const long long t = (long long)t0 + row;  // past T: out of the descriptor's range, reads zero
+        const uint32_t go = (uint32_t)min((t * rT + ch * 8) * 2, 0xFFFFFFF0LL);
+        raw_buffer_load_lds(rsu, (__attribute__((address_space(3))) uint32_t *)(dst + (i * NW + wave) * 16 * DK), 16,
+                            (int)go, (k - D) * 2, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NBS; ++i) {
+      int Gb = i * NW + wave;
+      if (Gb >= C::NGB) Gb = wave % C::NGB;
+      const int plane = Gb / (D / 16), n = (Gb % (D / 16)) * 16 + lr, ch = (lp ^ (n >> 1)) & 3;
+      auto *ld = (__attribute__((address_space(3))) uint32_t *)(dst + (NGA + Gb) * 16 * DK);
+      if (k >= D)
+        raw_buffer_load_lds(rsd, ld, 16, (int)((plane * dpl_ps + (long long)n * Kd + ch * 8) * 2), (k - D) * 2, 0, 0);
+      else
+        raw_buffer_load_lds(rsq, ld, 16, (int)((plane * qpl_ps + (long long)n * D + ch * 8) * 2), k * 2, 0, 0);
+    }
+  };
+  // A fragment of codes: rows 128 wr + 16 i + fr, chunk fc (8 codes, b bytes) from the stage's words
+  // (bits fc 8 b .. of the row; words past the row's b hold bits no code reads)
+  const int qm = (b >= 2) ? ((1 << (b - 1)) - 1) : 1;
+  const int cbit = fc * 8 * b, cdw = cbit >> 5, csh = cbit & 31;
+  const uint64_t cmask = (b >= 8) ? 0xFFull : ((1ull << b) - 1ull);
+  auto cfrag = [&](const lds16 *stage, int i) __attribute__((always_inline)) -> u32x4 {
+    const __attribute__((address_space(3))) uint32_t *cl =
+        (const __attribute__((address_space(3))) uint32_t *)stage + (wr * C::WR + i * 16 + fr) * 8 + cdw;
+    const uint32_t w0 = cl[0], w1 = cl[1], w2 = cl[2];
+    const uint64_t lo = ((uint64_t)w1 << 32) | w0;
+    const uint64_t w = csh ? ((lo >> csh) | ((uint64_t)w2 << (64 - csh))) : lo;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int u = (int)((w >> (e * b)) & cmask);
+      const float v = (b == 1) ? (u ? 1.f : -1.f) : (float)(u - qm);
+      h[e] = (MF == MF_F16) ? (uint32_t)f32_to_f16_rne(v) : (uint32_t)f32_to_bf16_rne(v);
+    }
+    u32x4 r;
+    r[0] = h[0] | (h[1] << 16);
+    r[1] = h[2] | (h[3] << 16);
+    r[2] = h[4] | (h[5] << 16);
+    r[3] = h[6] | (h[7] << 16);
+    return r;
+  };
+
+  const int aoff = dswz(wr * C::WR + fr, fc), boff = C::ASZ + dswz(wc * C::WC + fr, fc);
+  f32x4 acc[TI][TQ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int q = 0; q < TQ; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(L0, kbeg);
+  for (int s = 0; s < nsteps; ++s) {
+    const int k = kbeg + s * DK;
+    lds16 *cur = (s & 1) ? L1 : L0;
+    wait_vm<0>();
+    wait_lgkm0();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const bool last_codes = k + DK == D;
+    float srow[TI];
+    if (last_codes) {  // the row scales, needed after this stage's products
+#pragma unroll
+      for (int i = 0; i < TI; ++i) srow[i] = scales[(long long)j * T + min(t0 + wr * C::WR + i * 16 + fr, T - 1)];
+    }
+    u32x4 af[TI];
+    if (k < D) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) af[i] = cfrag(cur, i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        af[i] = *(const lds_u32x4 *)(cur + aoff + i * 16 * DK);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (s + 1 < nsteps) issue((s & 1) ? L0 : L1, k + DK);
+#pragma unroll
+    for (int pb = PB - 1; pb >= 0; --pb) {
+      if (pb > C::MAXO) continue;
+      u32x4 bf[TQ];
+#pragma unroll
+      for (int q = 0; q < TQ; ++q) {
+        bf[q] = *(const lds_u32x4 *)(cur + boff + pb * D * DK + q * 16 * DK);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int q = 0; q < TQ; ++q) acc[i][q] = mfma16<MF>(bf[q], af[i], acc[i][q]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (last_codes) {  // rows times s, into the frame of D_j's planes
+      const float f = dscale / qscale;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const float si = srow[i] * f;
+#pragma unroll
+        for (int q = 0; q < TQ; ++q)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][q][r] *= si;
+      }
+    }
+  }
+  // lane (fr, fc): columns D/2 wc + 16 q + 4 fc + r (r = 0..3) of token row 128 wr + 16 i + fr
+  const float inv = 1.f / dscale;
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    const int t = t0 + wr * C::WR + i * 16 + fr;
+    if (t >= T) continue;
+    char *orow = out + ((long long)j * T + t) * D * 2;
+#pragma unroll
+    for (int q = 0; q < TQ; ++q) {
+      const int n = wc * C::WC + q * 16 + fc * 4;
+      uint32_t h[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = acc[i][q][r] * inv;
+        h[r] = (MF == MF_F16) ? (uint32_t)f32_to_f16_rne(v) : (uint32_t)f32_to_bf16_rne(v);
+      }
+      uint2 w2;
+      w2.x = h[0] | (h[1] << 16);
+      w2.y = h[2] | (h[3] << 16);
+      *(uint2 *)(orow + n * 2) = w2;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------ fused decode
+// The tile rebuild on the DMA pipeline (16-bit caches): rows t0 .. t0 + 127 of head slice j in
+// rebuild_tile's accumulator layout (row wm 64 + 16 i + 4 (lane / 16) + r, column wn 64 + 16 q +
+// lane % 16 for wave (wm, wn)), real units.  Stages as decode_dma_kernel: the codes' words with Q's
+// planes, then U_T rows with D_j's planes (padded pitch, zero past r_T), two stage buffers of
+// RCfg::STG halves in lds; srow: BM floats.  Every thread of the block calls it (it synchronises the
+// block and leaves lds free).
+template <int MF, int D>
+struct RCfg {
+  static constexpr int NS = 2, ROWS = BM, NW = 4;
+  static constexpr int PB = (MF == MF_F16) ? 2 : 3;
+  static constexpr int MAXO = (MF == MF_F16) ? 1 : 2;
+  static constexpr int ASZ = ROWS * dma::DK, BSZ = PB * D * dma::DK, STG = ASZ + BSZ;
+  static constexpr int NGA = ROWS / 16, NGB = PB * D / 16, NA = NGA / NW, NBS = (NGB + NW - 1) / NW;
+  static_assert(NGA % NW == 0, "A groups split evenly over the waves");
+  static_assert(ROWS * 8 * 4 + 12 <= ASZ * 2, "a stage's code words fit in its A area");
+};
+
+template <int MF, int D>
+__device__ __forceinline__ void rebuild_tile_dma(const DecCell &c, int j, int t0, int T, uint16_t *lds, float *srow,
+                                                 f32x4 (&acc)[4][4]) {
+  using C = RCfg<MF, D>;
+  using namespace dma;
+  constexpr int PB = C::PB, NW = C::NW, NA = C::NA, NBS = C::NBS, NGA = C::NGA, ROWS = C::ROWS;
+  lds16 *const L0 = (lds16 *)lds, *const L1 = L0 + C::STG;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1, fr = lane & 15, fc = lane >> 4;
+  const int rT = c.rT, b = c.bits, Kd = c.Kd;
+  const float qscale = (MF == MF_F16) ? f16_split_scale(1.f) : 1.f;
+  const float dscale = (MF == MF_F16) ? f16_split_scale(*c.d_amax) : 1.f;
+  const int kbeg = b > 0 ? 0 : D, kend = D + rT;
+  const int nsteps = (kend - kbeg + DK - 1) / DK;
+  const long long rowbytes = (long long)D * b / 8;
+  const i32x4 rsu = make_rsrc(c.UT, (uint32_t)((long long)T * rT * 2));
+  const i32x4 rsq = make_rsrc(c.Qpl, 0xFFFFFFFFu);
+  const i32x4 rsd = make_rsrc(c.Dpl + (long long)j * D * Kd, 0xFFFFFFFFu);
+  const i32x4 rsc = make_rsrc(c.codes + (long long)j * T * rowbytes, (uint32_t)(T * rowbytes));
+  const int lr = lane >> 2, lp = lane & 3;
+  auto issue = [&](lds16 *dst, int k) __attribute__((always_inline)) {
+    if (k < D) {
+#pragma unroll
+      for (int m = 0; m < ROWS / 8 / NW; ++m) {
+        const int rq = m * NW + wave, row = rq * 8 + (lane >> 3);
+        const long long off = (long long)(t0 + row) * rowbytes + (k / 8) * b + 4 * (lane & 7);
+        raw_buffer_load_lds(rsc, (__attribute__((address_space(3))) uint32_t *)dst + rq * 64, 4,
+                            (int)min(off, 0xFFFFFFF0LL), 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int row = (i * NW + wave) * 16 + lr, ch = (lp ^ (row >> 1)) & 3;
+        const long long t = (long long)t0 + row;
+        const uint32_t go = (uint32_t)min((t * rT + ch * 8) * 2, 0xFFFFFFF0LL);
+        raw_buffer_load_lds(rsu, (__attribute__((address_space(3))) uint32_t *)(dst + (i * NW + wave) * 16 * DK), 16,
+                            (int)go, (k - D) * 2, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NBS; ++i) {
+      int Gb = i * NW + wave;
+      if (Gb >= C::NGB) Gb = wave % C::NGB;
+      const int plane = Gb / (D / 16), n = (Gb % (D / 16)) * 16 + lr, ch = (lp ^ (n >> 1)) & 3;
+      auto *ld = (__attribute__((address_space(3))) uint32_t *)(dst + (NGA + Gb) * 16 * DK);
+      if (k >= D)
+        raw_buffer_load_lds(rsd, ld, 16, (int)((plane * c.dpl_ps + (long long)n * Kd + ch * 8) * 2), (k - D) * 2, 0, 0);
+      else
+        raw_buffer_load_lds(rsq, ld, 16, (int)((plane * c.qpl_ps + (long long)n * D + ch * 8) * 2), k * 2, 0, 0);
+    }
+  };
+  const int qm = (b >= 2) ? ((1 << (b - 1)) - 1) : 1;
+  const int cbit = fc * 8 * b, cdw = cbit >> 5, csh = cbit & 31;
+  const uint64_t cmask = (b >= 8) ? 0xFFull : ((1ull << b) - 1ull);
+  auto cfrag = [&](const lds16 *stage, int i) __attribute__((always_inline)) -> u32x4 {
+    const __attribute__((address_space(3))) uint32_t *cl =
+        (const __attribute__((address_space(3))) uint32_t *)stage + (wm * 64 + i * 16 + fr) * 8 + cdw;
+    const uint32_t w0 = cl[0], w1 = cl[1], w2 = cl[2];
+    const uint64_t lo = ((uint64_t)w1 << 32) | w0;
+    const uint64_t w = csh ? ((lo >> csh) | ((uint64_t)w2 << (64 - csh))) : lo;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int u = (int)((w >> (e * b)) & cmask);
+      const float v = (b == 1) ? (u ? 1.f : -1.f) : (float)(u - qm);
+      h[e] = (MF == MF_F16) ? (uint32_t)f32_to_f16_rne(v) : (uint32_t)f32_to_bf16_rne(v);
+    }
+    u32x4 r;
+    r[0] = h[0] | (h[1] << 16);
+    r[1] = h[2] | (h[3] << 16);
+    r[2] = h[4] | (h[5] << 16);
+    r[3] = h[6] | (h[7] << 16);
+    return r;
+  };
+  for (int rr = tid; rr < ROWS; rr += NT) srow[rr] = (b > 0 && t0 + rr < T) ? c.scales[(long long)j * T + t0 + rr] : 0.f;
+  const int aoff = dswz(wm * 64 + fr, fc), boff = C::ASZ + dswz(wn * 64 + fr, fc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[i][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // the caller's last use of lds is over
+  issue(L0, kbeg);
+  for (int s = 0; s < nsteps; ++s) {
+    const int k = kbeg + s * DK;
+    lds16 *cur = (s & 1) ? L1 : L0;
+    wait_vm<0>();
+    wait_lgkm0();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    u32x4 af[4];
+    if (k < D) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = cfrag(cur, i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = *(const lds_u32x4 *)(cur + aoff + i * 16 * DK);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (s + 1 < nsteps) issue((s & 1) ? L0 : L1, k + DK);
+    if (wn * 64 < D) {  // (d_h = 64: the second column wave has no columns)
+#pragma unroll
+      for (int pb = PB - 1; pb >= 0; --pb) {
+        if (pb > C::MAXO) continue;
+        u32x4 bf[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf[q] = *(const lds_u32x4 *)(cur + boff + pb * D * DK + q * 16 * DK);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][q] = mfma16<MF>(af[i], bf[q], acc[i][q]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (k + DK == D) {  // rows times s, into the frame of D_j's planes
+      const float f = dscale / qscale;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float si = srow[wm * 64 + i * 16 + fc * 4 + r] * f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[i][q][r] *= si;
+        }
+    }
+  }
+  const float inv = 1.f / dscale;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[i][q][r] *= inv;
+  __syncthreads();  // every wave is done with the stage buffers
+}
+
 // Code of element n of a packed row (b bits, LSB-first, offset binary) as its signed value; reads the
 // second byte only when the element reaches into it.
 __device__ __forceinline__ float code_at(const uint8_t *rowp, int n, int b) {
@@ -875,10 +1253,11 @@ __device__ __forceinline__ float warp_sum_f(float v) {
 template <int MF, int SX, int NB16, int D, int G8>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G8 <= 4 ? 2 : 1, G8 <= 4 ? 2 : 1))) attend_kernel(AttnArgs a) {
   constexpr int KP = D + 1, H2 = D / 2, NQ = NT / D, ZU = kAttnMaxRank / NT;
-  constexpr int STGB = 2 * DecCfg<MF, SX, NB16>::STG * 2, KTB = BM * KP * 4;
+  constexpr int STGB = SX == SRC_F32 ? 2 * DecCfg<MF, SX, NB16>::STG * 2 : RCfg<MF, D>::NS * RCfg<MF, D>::STG * 2;
+  constexpr int KTB = BM * KP * 4;
   constexpr int SMB = STGB > KTB ? STGB : KTB;
   // the staging of the tile rebuild and the key tile share the memory (one is done when the other starts)
-  __shared__ __attribute__((aligned(16))) char smem[SMB];
+  __shared__ __attribute__((aligned(1024))) char smem[SMB];
   __shared__ float srow[BM];
   __shared__ float qs[G8 * D];
   __shared__ float ps[G8 * BM];
@@ -906,7 +1285,8 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G8 <= 4
   __syncthreads();
   for (int t0 = tbeg; t0 < tend; t0 += BM) {
     f32x4 acc[4][4];
-    rebuild_tile<MF, SX, NB16, DecCfg<MF, SX, NB16>::PB>(a.k, h, t0, T, D, lds, srow, acc);
+    if constexpr (SX == SRC_F32) rebuild_tile<MF, SX, NB16, DecCfg<MF, SX, NB16>::PB>(a.k, h, t0, T, D, lds, srow, acc);
+    else rebuild_tile_dma<MF, D>(a.k, h, t0, T, lds, srow, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1163,6 +1543,13 @@ void launch_enc_dma(const EncArgs &a, int ncells, int T, int GHmax, hipStream_t 
                      GHmax);
 }
 
+template <int MF, int TN>
+void launch_dec_dma(const DecCell *cells, int ncells, int T, int GHmax, hipStream_t st) {
+  using C = YCfg<MF, TN>;
+  const int tt = (T + C::ROWS - 1) / C::ROWS;
+  hipLaunchKernelGGL((decode_dma_kernel<MF, TN>), dim3(tt * GHmax, 1, ncells), dim3(C::NT), 0, st, cells, T, tt, GHmax);
+}
+
 template <int MF, int SX, int NB16>
 void launch_dec(const DecCell *cells, int ncells, int T, int D, int GHmax, hipStream_t st) {
   int tt = (T + BM - 1) / BM;
@@ -1212,9 +1599,17 @@ void attend_merge(int dtype, const AttnMergeArgs &m, hipStream_t st) {
 
 void decode_cells(int dtype, const DecCell *d_cells, int ncells, int T, int D, int GHmax, hipStream_t st) {
   JOLT_REQUIRE(D == 64 || D == 128, JOLT_EINVAL, "codec: d_head must be 64 or 128");
-  if (dtype == JOLT_F16) launch_dec<MF_F16, SRC_F16, 2>(d_cells, ncells, T, D, GHmax, st);
-  else if (dtype == JOLT_BF16) launch_dec<MF_BF16, SRC_BF16, 2>(d_cells, ncells, T, D, GHmax, st);
-  else launch_dec<MF_BF16, SRC_F32, 2>(d_cells, ncells, T, D, GHmax, st);
+  // 16-bit caches: the DMA-fed kernel (D_j planes zero-padded to a multiple of 32 columns); fp32
+  // caches keep the register-staged tile rebuild
+  if (dtype == JOLT_F16) {
+    if (D == 128) launch_dec_dma<MF_F16, 8>(d_cells, ncells, T, GHmax, st);
+    else launch_dec_dma<MF_F16, 4>(d_cells, ncells, T, GHmax, st);
+  } else if (dtype == JOLT_BF16) {
+    if (D == 128) launch_dec_dma<MF_BF16, 8>(d_cells, ncells, T, GHmax, st);
+    else launch_dec_dma<MF_BF16, 4>(d_cells, ncells, T, GHmax, st);
+  } else {
+    launch_dec<MF_BF16, SRC_F32, 2>(d_cells, ncells, T, D, GHmax, st);
+  }
   HIP_LAUNCH_CHECK();
 }
 
