@@ -1069,6 +1069,23 @@ decode_dma_kernel(const DecCell *cells, int T, int ttiles, int GHmax) {
 }
 
 // ------------------------------------------------------------------------------------------ fused decode
+// four consecutive elements of a cache-dtype array as floats (one 8- or 16-byte load; idx a multiple of 4)
+template <int SX>
+__device__ __forceinline__ void load4(const void *base, long long idx, float (&v)[4]) {
+  if constexpr (SX == SRC_F32) {
+    const float4 f = *(const float4 *)((const float *)base + idx);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    const uint2 w = *(const uint2 *)((const uint16_t *)base + idx);
+    const uint32_t h[4] = {w.x & 0xFFFFu, w.x >> 16, w.y & 0xFFFFu, w.y >> 16};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (SX == SRC_F16) v[e] = (float)__builtin_bit_cast(_Float16, (uint16_t)h[e]);
+      else v[e] = __builtin_bit_cast(float, h[e] << 16);
+    }
+  }
+}
+
 // The tile rebuild on the DMA pipeline (16-bit caches): rows t0 .. t0 + 127 of head slice j in
 // rebuild_tile's accumulator layout (row wm 64 + 16 i + 4 (lane / 16) + r, column wn 64 + 16 q +
 // lane % 16 for wave (wm, wn)), real units.  Stages as decode_dma_kernel: the codes' words with Q's
@@ -1252,7 +1269,7 @@ __device__ __forceinline__ float warp_sum_f(float v) {
 // the merge expands both once per head.  The block writes its chunk's (m, l, z, w) per query head.
 template <int MF, int SX, int NB16, int D, int G8>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G8 <= 4 ? 2 : 1, G8 <= 4 ? 2 : 1))) attend_kernel(AttnArgs a) {
-  constexpr int KP = D + 1, H2 = D / 2, NQ = NT / D, ZU = kAttnMaxRank / NT;
+  constexpr int KP = D + 1, H2 = D / 2, ZU = kAttnMaxRank / NT;
   constexpr int STGB = SX == SRC_F32 ? 2 * DecCfg<MF, SX, NB16>::STG * 2 : RCfg<MF, D>::NS * RCfg<MF, D>::STG * 2;
   constexpr int KTB = BM * KP * 4;
   constexpr int SMB = STGB > KTB ? STGB : KTB;
@@ -1274,7 +1291,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G8 <= 4
     l_s[tid] = 0.f;
   }
   const int rTv = a.v.rT, bv = a.v.bits, rbv = D * bv / 8;
-  const int ncol = tid % D, tg = tid / D;
+  // running state: z[g][k] for k = tid + NT u in zr; w[g][n] for n = tid < D in wr
   float zr[ZU][G8], wr[G8];
 #pragma unroll
   for (int g = 0; g < G8; ++g) {
@@ -1366,65 +1383,153 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(G8 <= 4
 #pragma unroll
     for (int g = 0; g < G8; ++g) al[g] = g < G ? alpha_s[g] : 0.f;
     const int nrow = min(BM, tend - t0);
-    // value token factor, rank space (rows in batches of 8 loads in flight; the weight of a row past
-    // the chunk is exp(-inf) = 0, only its load is skipped)
-    constexpr int RB = 16;
+    // The tile's value sums, each as one batch of independent wide loads per thread, then reduced in a
+    // fixed order (lanes by shuffles, waves through the dead key tile).
+    float *vpart = kt;  // [4 waves][G8][128]
+    const int lane6 = tid & 63, wv = tid >> 6;
+    // value token factor, rank space: z[g][k] += sum_t p[g][t] U_T^V[t][k]; lane (q4, row group rg):
+    // ranks kb + 4 q4 .. + 3, rows rg + 8 i (i < 16)
+    {
+      const int q4 = tid & 31, rg = tid >> 5;
 #pragma unroll
-    for (int u = 0; u < ZU; ++u) {
-      const int k = tid + NT * u;
+      for (int u = 0; u < ZU; ++u)
 #pragma unroll
-      for (int g = 0; g < G8; ++g) zr[u][g] *= al[g];
-      if (k < rTv)
-        for (int r0 = 0; r0 < nrow; r0 += RB) {
-          float uv[RB];
+        for (int g = 0; g < G8; ++g) zr[u][g] *= al[g];
+      for (int kb = 0; kb < rTv; kb += 128) {
+        const int k4 = kb + 4 * q4;
+        float za[G8][4];
 #pragma unroll
-          for (int i = 0; i < RB; ++i)
-            uv[i] = r0 + i < nrow ? load_elem<SX>(a.v.UT, (long long)(t0 + r0 + i) * rTv + k) : 0.f;
+        for (int g = 0; g < G8; ++g)
 #pragma unroll
-          for (int i = 0; i < RB; ++i)
+          for (int e = 0; e < 4; ++e) za[g][e] = 0.f;
+        if (k4 < rTv) {
+          float uv[16][4];
 #pragma unroll
-            for (int g = 0; g < G8; ++g)
-              if (g < G) zr[u][g] = fmaf(ps[g * BM + r0 + i], uv[i], zr[u][g]);
-        }
-    }
-    // value residual, rotated frame: column ncol over the rows of token group tg
+          for (int i = 0; i < 16; ++i) {
+            const int row = rg + 8 * i;
+            if (row < nrow) load4<SX>(a.v.UT, (long long)(t0 + row) * rTv + k4, uv[i]);
+            else uv[i][0] = uv[i][1] = uv[i][2] = uv[i][3] = 0.f;
+          }
 #pragma unroll
-    for (int g = 0; g < G8; ++g) wr[g] *= al[g];
-    if (bv > 0)
-      for (int r0 = tg; r0 < nrow; r0 += NQ * RB) {
-        float sv[RB];
+          for (int i = 0; i < 16; ++i) {
+            const int row = rg + 8 * i;
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          const int row = r0 + i * NQ;
-          if (row < nrow) {
-            const long long vr = (long long)h * T + t0 + row;
-            sv[i] = a.v.scales[vr] * code_at(a.v.codes + vr * rbv, ncol, bv);
-          } else {
-            sv[i] = 0.f;
+            for (int g = 0; g < G8; ++g) {
+              if (g >= G) continue;
+              const float pg = ps[g * BM + row];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) za[g][e] = fmaf(pg, uv[i][e], za[g][e]);
+            }
           }
         }
 #pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          const int row = min(r0 + i * NQ, BM - 1);
+        for (int g = 0; g < G8; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) za[g][e] += __shfl_xor(za[g][e], 32, 64);
+        if (lane6 < 32 && k4 < rTv)
 #pragma unroll
           for (int g = 0; g < G8; ++g)
-            if (g < G) wr[g] = fmaf(ps[g * BM + row], sv[i], wr[g]);
+            if (g < G)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) vpart[(wv * G8 + g) * 128 + 4 * q4 + e] = za[g][e];
+        __syncthreads();
+        // owner of rank k = kb + c: thread k % NT, slot k / NT
+        const int c = tid - (kb % NT);
+        if (c >= 0 && c < 128 && kb + c < rTv) {
+          const int u = kb / NT;
+#pragma unroll
+          for (int uu = 0; uu < ZU; ++uu)
+            if (uu == u)
+#pragma unroll
+              for (int g = 0; g < G8; ++g)
+                if (g < G)
+                  zr[uu][g] += ((vpart[(0 * G8 + g) * 128 + c] + vpart[(1 * G8 + g) * 128 + c]) +
+                                vpart[(2 * G8 + g) * 128 + c]) + vpart[(3 * G8 + g) * 128 + c];
+        }
+        __syncthreads();
+      }
+    }
+    // value residual, rotated frame: w[g][n] += sum_t p[g][t] s_t c_t[n]; lane (c8, row group rg):
+    // columns 8 c8 .. + 7 (b bytes of a packed row), rows rg + 16 i (i < 8)
+#pragma unroll
+    for (int g = 0; g < G8; ++g) wr[g] *= al[g];
+    if (bv > 0) {
+      const int c8 = tid & 15, rg = tid >> 4;
+      const int qmv = (bv >= 2) ? ((1 << (bv - 1)) - 1) : 1;
+      const uint64_t cmask = (bv >= 8) ? 0xFFull : ((1ull << bv) - 1ull);
+      const int off = c8 * bv, a0 = off & ~3, sh = (off & 3) * 8;
+      float wa[G8][8];
+#pragma unroll
+      for (int g = 0; g < G8; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wa[g][e] = 0.f;
+      if (c8 < D / 8) {
+        uint32_t cw[8][3];
+        float sv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = rg + 16 * i;
+          if (row < nrow) {
+            const long long vr = (long long)h * T + t0 + row;
+            const uint32_t *w = (const uint32_t *)(a.v.codes + vr * rbv + a0);
+            sv[i] = a.v.scales[vr];
+            cw[i][0] = w[0];
+            cw[i][1] = (a0 + 4 < rbv) ? w[1] : 0u;
+            cw[i][2] = (a0 + 8 < rbv) ? w[2] : 0u;
+          } else {
+            sv[i] = 0.f;
+            cw[i][0] = cw[i][1] = cw[i][2] = 0u;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = min(rg + 16 * i, BM - 1);
+          const uint64_t lo = ((uint64_t)cw[i][1] << 32) | cw[i][0];
+          const uint64_t wbits = sh ? ((lo >> sh) | ((uint64_t)cw[i][2] << (64 - sh))) : lo;
+          float cv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int u = (int)((wbits >> (e * bv)) & cmask);
+            cv[e] = (bv == 1) ? (u ? 1.f : -1.f) : (float)(u - qmv);
+          }
+#pragma unroll
+          for (int g = 0; g < G8; ++g) {
+            if (g >= G) continue;
+            const float pg = ps[g * BM + row] * sv[i];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wa[g][e] = fmaf(pg, cv[e], wa[g][e]);
+          }
         }
       }
+#pragma unroll
+      for (int g = 0; g < G8; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          wa[g][e] += __shfl_xor(wa[g][e], 16, 64);
+          wa[g][e] += __shfl_xor(wa[g][e], 32, 64);
+        }
+      if (lane6 < 16 && c8 < D / 8)
+#pragma unroll
+        for (int g = 0; g < G8; ++g)
+          if (g < G)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vpart[(wv * G8 + g) * 128 + 8 * c8 + e] = wa[g][e];
+      __syncthreads();
+      if (tid < D)
+#pragma unroll
+        for (int g = 0; g < G8; ++g)
+          if (g < G)
+            wr[g] += ((vpart[(0 * G8 + g) * 128 + tid] + vpart[(1 * G8 + g) * 128 + tid]) +
+                      vpart[(2 * G8 + g) * 128 + tid]) + vpart[(3 * G8 + g) * 128 + tid];
+    }
     __syncthreads();
   }
-  // the chunk's state; the residual sums of the NQ token groups are added in group order
-#pragma unroll
-  for (int g = 0; g < G8; ++g)
-    if (g < G) kt[(tg * G + g) * D + ncol] = wr[g];
-  __syncthreads();
+  // the chunk's state
   float *P = a.part + (long long)(ch * a.H + h) * G * a.PS;
-  for (int e = tid; e < G * D; e += NT) {
-    const int g = e / D, n = e - g * D;
-    float sum = 0.f;
-    for (int q = 0; q < NQ; ++q) sum += kt[(q * G + g) * D + n];
-    P[(long long)g * a.PS + 2 + a.rtv_ld + n] = sum;
-  }
+  if (tid < D)
+#pragma unroll
+    for (int g = 0; g < G8; ++g)
+      if (g < G) P[(long long)g * a.PS + 2 + a.rtv_ld + tid] = wr[g];
 #pragma unroll
   for (int u = 0; u < ZU; ++u) {
     const int k = tid + NT * u;
