@@ -62,7 +62,7 @@ def _check(ref, blob, cfg, picks, dt, seq, layer, G, n_tail, base, seed):
 
 
 @pytest.mark.parametrize("name", ["tiny_f32_exact", "f16_exact_ragged", "f16_flash_d128", "bf16_flash",
-                                  "f16_flash_two_seqs"])
+                                  "f16_flash_two_seqs", "f16_flash_bits567", "bf16_flash_bits567"])
 def test_decode_attention_matches_oracle(name):
     c = case(name)
     ref = c["ref"]

@@ -43,6 +43,9 @@ CASES = {
     "f16_exact_blocked_777": ("pl", "f16", "exact", 1, 4, 2, 777, 128, 2.0, list(range(8, 777, 8)), [2, 4, 8]),
     "bf16_exact_blocked_1000": ("pl", "bf16", "exact", 1, 8, 2, 1000, 128, 3.0, list(range(8, 1001, 8)),
                                 [1, 2, 3, 4]),
+    # code widths 5-7: a row's 8-code groups start at any byte and a 7-bit group can span three words
+    "f16_flash_bits567": ("pl", "f16", "flash", 1, 4, 2, 520, 128, 2.0, [8, 16, 24, 32], [5, 6, 7]),
+    "bf16_flash_bits567": ("pl", "bf16", "flash", 1, 4, 2, 520, 128, 2.5, [8, 16, 24, 32], [5, 6, 7]),
 }
 _cache = {}
 
@@ -102,7 +105,7 @@ def test_reconstruct_matches_oracle_on_oracle_blob(name):
 
 # ------------------------------------------------------------------------------ residual codes
 @pytest.mark.parametrize("name", ["tiny_f32_exact", "f16_exact_ragged", "f16_flash_d128", "bf16_flash"])
-@pytest.mark.parametrize("b", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_encode_codes_match_oracle_given_oracle_factors(name, b):
     c = case(name)
     Q = oracle.rotation(c["D"], 0)
