@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--summarize-profile", metavar="DIR",
                     help="print a per-kernel summary of a rocprofv3 --kernel-trace --output-format csv directory")
     ap.add_argument("--traffic-from", nargs=5, metavar=("KERNEL", "FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
-                    help="KERNEL: project_gemm or residual_encode (with '@tag' for another workload); then "
+                    help="KERNEL: project_gemm, residual_encode or reconstruct (with '@tag' for another workload); then "
                          "rocprofv3 --pmc csv directories (FETCH_SIZE / WRITE_SIZE of this bench and of "
                          "--calibrate-copy): add the kernel to profiles/traffic.json and print a summary")
     return ap.parse_args()
@@ -75,6 +75,12 @@ TRAFFIC_KERNELS = {
                                     "kv_cache_compression_layer_amd/csrc/dma.hpp",
                                     "kv_cache_compression_layer_amd/csrc/common.hpp",
                                     "kv_cache_compression_layer_amd/csrc/api.cpp"]},
+    # the whole-cache reconstruct (the largest grid of the kernel; the decode measurement launches it per group)
+    "reconstruct": {"name": "decode_dma_kernel<0, 8>", "grid": None,
+                    "sources": ["kv_cache_compression_layer_amd/csrc/codec.hip",
+                                "kv_cache_compression_layer_amd/csrc/dma.hpp",
+                                "kv_cache_compression_layer_amd/csrc/common.hpp",
+                                "kv_cache_compression_layer_amd/csrc/api.cpp"]},
 }
 
 
@@ -555,9 +561,11 @@ def main():
     torch.cuda.synchronize()
     rec_ms = r0.elapsed_time(r1) / 3
     rec_bytes = float(sum(p["bytes"] for p in picks)) + 2.0 * L * H * T * D * 2
+    rec_traffic = traffic_for("reconstruct")
     reconstruct = {"ms": round(rec_ms, 3), "gbyte": round(rec_bytes / 1e9, 3),
                    "gbs": round(rec_bytes / (rec_ms / 1e3) / 1e9, 1),
-                   "hbm_frac": round(rec_bytes / (rec_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+                   "hbm_frac": round(rec_bytes / (rec_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "traffic": None if rec_traffic is None else round(rec_traffic)}
     del Ko, Vo
     decode = decode_measure(jolt, torch, blob, cfg, picks, T, L, H, D, G, a.dtype)
     cpu = None
