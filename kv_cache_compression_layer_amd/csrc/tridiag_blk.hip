@@ -54,6 +54,13 @@ __device__ __forceinline__ double *slot(const TbArgs &a, int b, int X, int S) {
 __device__ __forceinline__ double *dslot(const TbArgs &a, int b, int t) {
   return a.scr + b * a.s_bs + 4LL * kPanel * a.n + (long long)a.nt * a.nt * kTS + (long long)t * 2 * kPanel;
 }
+// p = beta_j A_cur v_j and the panel-corrected row r (both [n]), then one partial p . v per step-A block
+constexpr int kStepA = 256;
+__device__ __forceinline__ double *pvec(const TbArgs &a, int b) {
+  return a.scr + b * a.s_bs + 4LL * kPanel * a.n + (long long)a.nt * a.nt * kTS + (long long)a.nt * 2 * kPanel;
+}
+__device__ __forceinline__ double *xvec(const TbArgs &a, int b) { return pvec(a, b) + a.n; }
+__device__ __forceinline__ double *pdots(const TbArgs &a, int b) { return pvec(a, b) + 2LL * a.n; }
 
 // tile (I, J), I <= J, of the upper triangle of an m x m tile grid, row-major
 __device__ __forceinline__ void upper_tile(int q, int m, int &I, int &J) {
@@ -146,14 +153,58 @@ __global__ void __launch_bounds__(256) tb_symv_kernel(TbArgs a, int r) {
   }
 }
 
-// One workgroup per matrix.  j >= 0: finish reflector j (its symv partials are in the slots):
-// p = beta_j (A_cur v_j) with A_cur the stored matrix minus the panel's earlier rank-2 terms,
-// w_j = p - (beta_j / 2)(p . v_j) v_j.  Then row r = j + 1 of the working matrix (the stored row
-// minus the panel's terms, w_j's included) and its reflector, or for r = n - 2 the last 2 x 2 block.
+// Step A, many workgroups per matrix (j >= 0): for the entries x >= j + 1 of block blockIdx.x,
+// p = beta_j (A_cur v_j) with A_cur the stored matrix minus the panel's earlier rank-2 terms (the symv
+// slots summed in a fixed order, the panel terms from the dots of the diagonal tiles), the panel-
+// corrected row r = j + 1 of the working matrix (without step j's own term), and this block's part
+// of p . v_j.
+__global__ void __launch_bounds__(kStepA) tb_stepA_kernel(TbArgs a, int j) {
+  __shared__ double red[kStepA / 64];
+  __shared__ double coef[4 * kPanel];  // W_i . v, V_i . v, V_i[r], W_i[r]
+  const int b = blockIdx.y, n = a.n, tid = threadIdx.x, r = j + 1, s = r;
+  const int x0 = blockIdx.x * kStepA;
+  if (x0 + kStepA <= s) return;  // uniform: the block lies before the support
+  const int P = (j / kPanel) & 1, c = j % kPanel, t0 = s / kTS;
+  const double *vj = vpan(a, b, P, c);
+  if (tid < 2 * c) {
+    const int q = tid < c ? tid : kPanel + tid - c;
+    double sum = 0.0;
+    for (int t = t0; t < a.nt; ++t) sum += dslot(a, b, t)[q];
+    coef[q] = sum;
+  } else if (tid >= 64 && tid < 64 + c) {
+    coef[2 * kPanel + tid - 64] = vpan(a, b, P, tid - 64)[r];
+    coef[3 * kPanel + tid - 64] = wpan(a, b, P, tid - 64)[r];
+  }
+  __syncthreads();
+  const double bj = a.beta[b * a.t_bs + j];
+  const int xx = x0 + tid;
+  double pd = 0.0;
+  if (xx >= s && xx < n) {
+    const int X = xx / kTS, xo = xx % kTS;
+    double y = 0.0;
+    for (int S = t0; S < a.nt; ++S) y += slot(a, b, X, S)[xo];
+    double pc = 0.0, xc = 0.0;
+    for (int i = 0; i < c; ++i) {
+      const double Vi = vpan(a, b, P, i)[xx], Wi = wpan(a, b, P, i)[xx];
+      pc += Vi * coef[i] + Wi * coef[kPanel + i];
+      xc += coef[2 * kPanel + i] * Wi + coef[3 * kPanel + i] * Vi;
+    }
+    const double p = bj * (y - pc);
+    pvec(a, b)[xx] = p;
+    xvec(a, b)[xx] = a.A[b * a.a_bs + (long long)r * a.lda + xx] - xc;
+    pd = p * vj[xx];
+  }
+  pd = bsum(pd, red);
+  if (tid == 0) pdots(a, b)[blockIdx.x] = pd;
+}
+
+// Step B, one workgroup per matrix.  j >= 0: w_j = p - (beta_j / 2)(p . v_j) v_j (the partial dots
+// summed in block order), then row r = j + 1 of the working matrix gets step j's own term and yields
+// its reflector, or for r = n - 2 the last 2 x 2 block.  j = -1: the reflector of row 0.
 __global__ void __launch_bounds__(kStepT) tb_step_kernel(TbArgs a, int j) {
   extern __shared__ double sm[];
   __shared__ double red[kStepT / 64];
-  __shared__ double coef[4 * kPanel];  // W_i . v, V_i . v, V_i[r], W_i[r]
+  __shared__ double cj_s;
   const int b = blockIdx.x, n = a.n, tid = threadIdx.x;
   double *d = a.d + b * a.t_bs, *e = a.e + b * a.t_bs, *be = a.beta + b * a.t_bs;
   const double *Ab = a.A + b * a.a_bs;
@@ -163,47 +214,27 @@ __global__ void __launch_bounds__(kStepT) tb_step_kernel(TbArgs a, int j) {
   if (j >= 0) {
     P = (j / kPanel) & 1;
     c = j % kPanel;
-    const int s = r, t0 = s / kTS;
+    const int s = r;
     const double *vj = vpan(a, b, P, c);
-    if (tid < 2 * c) {
-      const int q = tid < c ? tid : kPanel + tid - c;
+    if (tid == 0) {
+      const double *pdb = pdots(a, b);
       double sum = 0.0;
-      for (int t = t0; t < a.nt; ++t) sum += dslot(a, b, t)[q];
-      coef[tid < c ? tid : kPanel + tid - c] = sum;
-    } else if (tid >= 64 && tid < 64 + c) {
-      coef[2 * kPanel + tid - 64] = vpan(a, b, P, tid - 64)[r];
-      coef[3 * kPanel + tid - 64] = wpan(a, b, P, tid - 64)[r];
+      for (int q = s / kStepA; q < (n + kStepA - 1) / kStepA; ++q) sum += pdb[q];
+      cj_s = 0.5 * be[j] * sum;
     }
     __syncthreads();
-    const double bj = be[j];
-    const double *row = Ab + (long long)r * a.lda;
-    for (int xx = s + tid; xx < n; xx += kStepT) {
-      const int X = xx / kTS, xo = xx % kTS;
-      double y = 0.0;
-      for (int S = t0; S < a.nt; ++S) y += slot(a, b, X, S)[xo];
-      double pc = 0.0, xc = 0.0;
-      for (int i = 0; i < c; ++i) {
-        const double Vi = vpan(a, b, P, i)[xx], Wi = wpan(a, b, P, i)[xx];
-        pc += Vi * coef[i] + Wi * coef[kPanel + i];
-        xc += coef[2 * kPanel + i] * Wi + coef[3 * kPanel + i] * Vi;
-      }
-      v[xx] = vj[xx];
-      w[xx] = bj * (y - pc);
-      x[xx] = row[xx] - xc;
-    }
-    __syncthreads();
-    double pv = 0.0;
-    for (int xx = s + tid; xx < n; xx += kStepT) pv += w[xx] * v[xx];
-    const double cj = 0.5 * bj * bsum(pv, red);
+    const double cj = cj_s;
+    const double *pv = pvec(a, b), *xv = xvec(a, b);
     double *wj = wpan(a, b, P, c);
     for (int xx = s + tid; xx < n; xx += kStepT) {
-      const double wx = w[xx] - cj * v[xx];
+      const double vx = vj[xx], wx = pv[xx] - cj * vx;
+      v[xx] = vx;
       w[xx] = wx;
       wj[xx] = wx;
     }
     __syncthreads();
     const double vr = v[r], wr = w[r];
-    for (int m = r + tid; m < n; m += kStepT) x[m] -= vr * w[m] + wr * v[m];
+    for (int m = r + tid; m < n; m += kStepT) x[m] = xv[m] - (vr * w[m] + wr * v[m]);
     __syncthreads();
   } else {
     for (int m = tid; m < n; m += kStepT) x[m] = Ab[m];
@@ -513,7 +544,7 @@ void backtransform_wy(double *Zw, long long z_bs, const double *refl, const doub
 
 long long tridiag_blocked_doubles(int n) {
   const long long nt = (n + kTS - 1) / kTS;
-  const long long raw = 4LL * kPanel * n + nt * nt * kTS + nt * 2 * kPanel;
+  const long long raw = 4LL * kPanel * n + nt * nt * kTS + nt * 2 * kPanel + 2LL * n + (n + kStepA - 1) / kStepA;
   return (raw + 31) / 32 * 32;
 }
 
@@ -555,6 +586,8 @@ void tridiag_blocked(double *A, long long a_bs, int lda, int n, int batch, doubl
     }
     const int m = a.nt - (r + 1) / kTS;
     hipLaunchKernelGGL(tb_symv_kernel, dim3(m * (m + 1) / 2, batch), dim3(256), 0, st, a, r);
+    HIP_LAUNCH_CHECK();
+    hipLaunchKernelGGL(tb_stepA_kernel, dim3((n + kStepA - 1) / kStepA, batch), dim3(kStepA), 0, st, a, r);
     HIP_LAUNCH_CHECK();
     hipLaunchKernelGGL(tb_step_kernel, dim3(batch), dim3(kStepT), shm, st, a, r);
     HIP_LAUNCH_CHECK();
