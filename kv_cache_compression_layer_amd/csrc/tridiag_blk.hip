@@ -28,7 +28,6 @@ namespace {
 
 constexpr int kPanel = 32;   // reflectors per deferred update
 constexpr int kTS = 128;     // symv tile side
-constexpr int kTU = 64;      // update tile side
 constexpr int kStepT = 1024; // threads of the per-matrix step
 
 struct TbArgs {
@@ -283,8 +282,9 @@ __global__ void __launch_bounds__(kStepT) tb_step_kernel(TbArgs a, int j) {
 }
 
 // Stored upper triangle, rows and columns >= r + 1: A -= sum_i (V_i W_i^T + W_i V_i^T) over the
-// kPanel steps of panel P.  64 x 64 tiles, 4 x 4 outputs per thread (columns strided by 16 so that
-// a row's loads and stores coalesce).
+// kPanel steps of panel P.  128 x 128 tiles, 8 x 8 outputs per thread (rows 8 ty .. 8 ty + 7, columns
+// tx + 16 q: a row's loads and stores coalesce), the panel's vectors staged through LDS 16 at a time.
+constexpr int kTU = 128, kUK = 16;
 __global__ void __launch_bounds__(256) tb_update_kernel(TbArgs a, int r, int P) {
   const int b = blockIdx.y, n = a.n, s = r + 1;
   const int nu = (n + kTU - 1) / kTU, t0 = s / kTU;
@@ -293,44 +293,47 @@ __global__ void __launch_bounds__(256) tb_update_kernel(TbArgs a, int r, int P) 
   I += t0;
   J += t0;
   const int R0 = I * kTU, C0 = J * kTU, tid = threadIdx.x;
-  __shared__ double Va[kPanel][kTU], Wa[kPanel][kTU], Vb[kPanel][kTU], Wb[kPanel][kTU];
-  for (int idx = tid; idx < kPanel * kTU; idx += 256) {
-    const int i = idx / kTU, o = idx % kTU;
-    const int ra = R0 + o, cb = C0 + o;
-    const bool oa = ra >= s && ra < n, ob = cb >= s && cb < n;
-    Va[i][o] = oa ? vpan(a, b, P, i)[ra] : 0.0;
-    Wa[i][o] = oa ? wpan(a, b, P, i)[ra] : 0.0;
-    Vb[i][o] = ob ? vpan(a, b, P, i)[cb] : 0.0;
-    Wb[i][o] = ob ? wpan(a, b, P, i)[cb] : 0.0;
-  }
-  __syncthreads();
+  __shared__ double Va[kUK][kTU], Wa[kUK][kTU], Vb[kUK][kTU], Wb[kUK][kTU];
   const int ty = tid >> 4, tx = tid & 15;
-  double acc[4][4];
+  double acc[8][8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 8; ++u)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[u][q] = 0.0;
-  for (int i = 0; i < kPanel; ++i) {
-    double av[4], aw[4], bv[4], bw[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      av[u] = Va[i][ty * 4 + u];
-      aw[u] = Wa[i][ty * 4 + u];
-      bv[u] = Vb[i][tx + 16 * u];
-      bw[u] = Wb[i][tx + 16 * u];
+    for (int q = 0; q < 8; ++q) acc[u][q] = 0.0;
+  for (int i0 = 0; i0 < kPanel; i0 += kUK) {
+    __syncthreads();
+    for (int idx = tid; idx < kUK * kTU; idx += 256) {
+      const int i = idx / kTU, o = idx % kTU;
+      const int ra = R0 + o, cb = C0 + o;
+      const bool oa = ra >= s && ra < n, ob = cb >= s && cb < n;
+      Va[i][o] = oa ? vpan(a, b, P, i0 + i)[ra] : 0.0;
+      Wa[i][o] = oa ? wpan(a, b, P, i0 + i)[ra] : 0.0;
+      Vb[i][o] = ob ? vpan(a, b, P, i0 + i)[cb] : 0.0;
+      Wb[i][o] = ob ? wpan(a, b, P, i0 + i)[cb] : 0.0;
     }
+    __syncthreads();
+    for (int i = 0; i < kUK; ++i) {
+      double av[8], aw[8], bv[8], bw[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u) {
+        av[u] = Va[i][ty * 8 + u];
+        aw[u] = Wa[i][ty * 8 + u];
+        bv[u] = Vb[i][tx + 16 * u];
+        bw[u] = Wb[i][tx + 16 * u];
+      }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[u][q] += av[u] * bw[q] + aw[u] * bv[q];
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[u][q] += av[u] * bw[q] + aw[u] * bv[q];
+    }
   }
   double *Ab = a.A + b * a.a_bs;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = R0 + ty * 4 + u;
+  for (int u = 0; u < 8; ++u) {
+    const int row = R0 + ty * 8 + u;
     if (row < s || row >= n) continue;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 8; ++q) {
       const int col = C0 + tx + 16 * q;
       if (col < n && col >= row) Ab[(long long)row * a.lda + col] -= acc[u][q];
     }
