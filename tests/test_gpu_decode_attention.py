@@ -75,6 +75,19 @@ def test_decode_attention_matches_oracle(name):
         _check(ref, blob, c["cfg"], picks, c["dt"], seqs[-1] if i else 0, layer, G, n_tail, base, 100 + i)
 
 
+@pytest.mark.parametrize("name,G", [("f16_flash_d128", 8), ("bf16_flash", 6), ("f16_exact_ragged", 8)])
+def test_decode_attention_more_query_heads_per_kv_head(name, G):
+    """5 to 8 query heads per KV head (the kernel's wider variant, one wave per SIMD), with and without a
+    dense tail, against the oracle."""
+    c = case(name)
+    ref = c["ref"]
+    blob = torch.from_numpy(np.frombuffer(ref["blob"], dtype=np.uint8).copy()).cuda()
+    picks = [{"rT": x["rT"], "rd": x["rd"], "bits": x["b"], "offset": x["offset"]} for x in ref["cells"]]
+    last = c["cfg"].desc.n_layers - 1
+    _check(ref, blob, c["cfg"], picks, c["dt"], 0, last, G, 0, 10000.0, 31)
+    _check(ref, blob, c["cfg"], picks, c["dt"], 0, 0, G, 9, 500000.0, 32)
+
+
 def test_decode_attention_many_chunks_of_several_tiles():
     """8 KV heads, T = 16384: 64 chunks of two 128-token tiles each (the online softmax across tiles of a
     chunk and the merge across chunks), G = 4 as in grouped-query models, a tail of 17 tokens."""
