@@ -53,17 +53,17 @@ def parse():
 
 
 # HIP-event records per stage cover this many kernel launches (K and V cells in separate launches)
-LAUNCHES_PER_RECORD = {"sketch_gemm": 2, "transpose_x": 2}
+LAUNCHES_PER_RECORD = {"sketch_gemm": 2, "project_gemm": 2, "feature_gram": 2}
 
 # the dominant kernel of the workload: the projection P^T = Q^T X (fp32 Q in two fp16 planes
-# times the fp16 cache), one launch over the 16 cells
-# (one launch covers all 16 cells, split 4-fold along K = T; the launch shape is set by the
-# library's sequencing, hence api.cpp among the sources whose change invalidates the counters)
+# times the fp16 cache read token-major), one launch over the 8 K cells and one over the 8 V cells,
+# each split 4-fold along K = T; the launch shape is set by the library's sequencing, hence api.cpp
+# among the sources whose change invalidates the counters
 # Kernels whose HBM traffic is read from rocprofv3 counters: the kernel, how to find its dispatches
 # (its grid for the 8B shape, or the largest grid of that kernel) and the sources its code and launch
 # come from (the counters stand only while these hash the same).
 TRAFFIC_KERNELS = {
-    "project_gemm": {"name": "gemm_dma_kernel<0, 2, 1, 3, 8, 3, 4, 2>", "grid": 3 * 16 * 512 * 16 * 4,
+    "project_gemm": {"name": "gemm_dma_kernel<0, 2, 1, 3, 8, 3, 4, 2, false>", "grid": 3 * 16 * 512 * 8 * 4,
                      "sources": ["kv_cache_compression_layer_amd/csrc/gemm_dma.hip",
                                  "kv_cache_compression_layer_amd/csrc/gemm_core.hpp",
                                  "kv_cache_compression_layer_amd/csrc/dma.hpp",
@@ -191,7 +191,6 @@ def stage_models(T, L, H, D, G, ell, picks, c):
     def add(name, flops, byts, unit):
         m[name] = {"flops": float(flops), "bytes": float(byts), "unit": unit}
 
-    add("transpose_x", 0.0, 2.0 * T * M * c * n, "mfma")
     add("feature_gram", 2.0 * R * D * D * n, T * M * c * n, "mfma")
     # two sketches: Y = X Omega, Y = X Z (fp32 Y written in two layouts)
     add("sketch_gemm", 2 * 2.0 * T * M * ell * n, 2 * (T * M * c + 2 * f4 * T * ell + f4 * M * ell) * n, "mfma")

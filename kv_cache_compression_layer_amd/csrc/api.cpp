@@ -237,8 +237,6 @@ struct Bufs {
   long long *tab_s;
   int *pick;
   AllocOut *aout;
-  // per-(l,h) transposed cache [cell][j][d][T_ld]
-  void *Xt;
   // 16-bit planes of an fp32 operand of the plane GEMM: Q^T for the projection, Z^T for the
   // power-iteration sketch (used one after the other), [cell][plane][ell][max(T_ld, M)]
   uint16_t *pln;
@@ -292,14 +290,14 @@ int project_splits(const Plan &pl) { return (int)std::min<long long>(4, std::max
 
 // split-K partials of the unprojected feature Gram (K = GH T_ld, padding included)
 long long feature_part_elems(const Plan &pl, int nb) {
-  const int ns = nsplit_for((long long)pl.GH * pl.T_ld, 1, nb, 8192);
+  const int ns = nsplit_for((long long)pl.GH * pl.T, 1, nb, 8192);
   return rup((long long)nb * ns * pl.D * pl.D, 64);
 }
 
 long long part_elems_for(const Plan &pl, int kmax, int nb) {
   long long pe = 0;
   {  // feature Gram partials
-    int ns = nsplit_for((long long)pl.GH * pl.T_ld, 1, nb, 8192);  // K of the feature Gram, padding included
+    int ns = nsplit_for((long long)pl.GH * pl.T, 1, nb, 8192);  // K of the feature Gram
     pe = std::max(pe, (long long)nb * ns * pl.D * pl.D);
     int ns2 = nsplit_for((long long)kmax * pl.GH, 1, nb, 1024);
     pe = std::max(pe, (long long)nb * ns2 * pl.D * pl.D);
@@ -343,7 +341,6 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
     b.fpart_elems = std::max(feature_part_elems(pl, nb), nv * feature_part_elems(pv, pv.n_cells));
     b.fpart = ar.take<float>(b.fpart_elems);
   }
-  b.Xt = ar.take<char>((long long)nb * pl.GH * D * pl.T_ld * pl.c);
   b.Gd64 = ar.take<double>((long long)nb * D * D);
   b.dD = ar.take<double>((long long)nb * D);
   b.eD = ar.take<double>((long long)nb * D);
@@ -495,22 +492,26 @@ bool gram_planes(const Plan &pl, Bufs &b, const uint16_t *P, long long ld, long 
 void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st) {
   Stage prof("feature_gram", st);
   const int D = pl.D;
-  const long long Kdim = (long long)pl.GH * pl.T_ld;  // zero padding of Xt contributes nothing
+  const long long Kdim = (long long)pl.GH * pl.T;
   int ns = nsplit_for(Kdim, 1, pl.n_cells, 8192);
   GemmArgs g = ga();
   g.M = D; g.N = D; g.K = (int)Kdim;
   g.k_chunk = (int)rup((Kdim + ns - 1) / ns, 32);
   ns = (int)((Kdim + g.k_chunk - 1) / g.k_chunk);
-  // A(m = d, k = (j, t)) = B(k, n = d) = Xt[j][d][t]
-  g.A = b.Xt; g.B = b.Xt;
-  g.a_ld = pl.T_ld; g.a_blk = pl.T_ld; g.a_blk_stride = (long long)D * pl.T_ld;
-  g.b_ld = pl.T_ld; g.b_blk = pl.T_ld; g.b_blk_stride = (long long)D * pl.T_ld;
-  g.a_bs = g.b_bs = (long long)pl.GH * D * pl.T_ld;
-  g.C = b.fpart; g.c_ld = D; g.c_split = (long long)D * D; g.c_bs = (long long)ns * D * D;
+  // A(m = d, k = (j, t)) = B(k, n = d) = X_j[t][d]: a cell's slices follow one another, so k runs
+  // over the rows of the cache, each contiguous along d
+  g.a_ld = D; g.b_ld = D;
+  g.a_bs = g.b_bs = pl.cell_elems();
+  g.c_ld = D; g.c_split = (long long)D * D; g.c_bs = 2LL * ns * D * D;
   JOLT_REQUIRE((long long)pl.n_cells * ns * D * D <= b.fpart_elems, JOLT_EWORKSPACE, "split-K buffer too small");
-  gemm(pl.xmf(), pl.xsrc(), true, pl.xsrc(), true, g, pl.n_cells, ns, st);
-  (void)K;
-  (void)V;
+  for_kv(K, V, [&](int t, const void *X) {
+    GemmArgs h = g;
+    h.A = X; h.B = X;
+    h.C = b.fpart + (long long)t * ns * D * D;
+    if (pl.c == 2 && xgram_dma(pl.xmf(), X, h.a_bs, (int)Kdim, D, h.C, h.c_bs, g.k_chunk, ns, pl.n_cells / 2, st))
+      return;
+    gemm(pl.xmf(), pl.xsrc(), false, pl.xsrc(), false, h, pl.n_cells / 2, ns, st);
+  });
   reduce_splits(b.fpart, (long long)ns * D * D, (long long)D * D, ns, 0, D, D, D, b.Gd64, true, (long long)D * D, D,
                 pl.n_cells, st);
   trace_f64(b.Gd64, (long long)D * D, D, pl.n_cells, b.norm2, st);
@@ -518,14 +519,15 @@ void stage_feature(const Plan &pl, Bufs &b, const void *K, const void *V, hipStr
 }
 
 // FlashJoLT token spectrum (Sec. 3.1): randomized subspace iteration with Cholesky QR.
-// Every large contraction is K-contiguous on both operands; tall fp32 panels are written in
-// both layouts by the GEMM epilogue so the next consumer never transposes while loading.
+// The cache is read as it is: the sketches contract over its contiguous d (K-contiguous), the
+// projections over tokens (B contiguous along d, fed to the matrix cores by transposing LDS reads);
+// tall fp32 panels are written in both layouts by the GEMM epilogue so the next consumer never
+// transposes while loading.
 // mark (optional) is recorded on st once the first orthonormal basis Q_0 exists; the next spectra
 // chain waits for it, which puts the chains out of phase.
-// side_work (optional): enqueues the transpose of the cache and the feature stage on another
-// stream and returns the event that marks their end; it is called once the Gaussian sketch (which
-// reads the untransposed cache) is queued, and st waits for the event before the first
-// projection, the first reader of their outputs.
+// side_work (optional): enqueues the feature stage on another stream and returns the event that
+// marks its end; it is called once the Gaussian sketch is queued, and st waits for the event
+// before it forms the spectrum, the first use of the feature stage's ||X||^2.
 void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStream_t st, hipEvent_t mark = nullptr,
                  const std::function<hipEvent_t()> &side_work = {}) {
   hipEvent_t xready = nullptr;
@@ -591,44 +593,45 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   const int pns = project_splits(pl);
   // q_amax null: Q^T's planes were split with the scale of kBasisBound
   auto project = [&](const float *Qt, const float *q_amax, float *c_amax) {
-    if (xready) {
-      HIP_TRY(hipStreamWaitEvent(st, xready, 0));
-      xready = nullptr;
-    }
     const bool planes = tplanes;
     Stage prof("project_gemm", st);
     GemmArgs g = ga();
-    g.A = Qt; g.M = (int)ell; g.N = (int)Mf; g.K = (int)T;
-    g.a_ld = Tld; g.a_bs = ell * Tld; g.a_amax = q_amax;
+    g.M = (int)ell; g.N = (int)Mf; g.K = (int)T;
+    g.a_ld = Tld; g.a_bs = 2 * ell * Tld; g.ab_amax_bs = 2;
     if (!q_amax) g.a_amax_c = kBasisBound;
-    g.B = b.Xt; g.b_ld = Tld; g.b_bs = Mf * Tld;
+    // B(k = t, n = (j, d)) = X_j[t][d]: the cache as it is, contiguous along d within a slice
+    g.b_ld = pl.D; g.b_blk = pl.D; g.b_blk_stride = T * pl.D; g.b_bs = cellX;
     g.m_fastest = 1;
-    if (pns <= 1) {
-      g.C = b.Pt; g.c_ld = Mf; g.c_bs = ell * Mf;
-      g.C2 = b.P2; g.c2_ld = ld; g.c2_bs = Mf * ld;
-      g.c_amax = c_amax;
-      if (planes) {
-        GemmArgs h = g;
-        h.A = b.pln; h.a_bs = P32 * ell * Tld; h.a_ps = ell * Tld;
-        if (gemm_dma(pl.xmf(), P32, 1, h, nb, 1, st)) return;
-      }
-      gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, 1, st);
-      return;
+    int ns = 1;
+    if (pns > 1) {
+      g.k_chunk = (int)rup((T + pns - 1) / pns, 32);
+      ns = (int)((T + g.k_chunk - 1) / g.k_chunk);
+      JOLT_REQUIRE((long long)nb * ns * ell * Mf <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
     }
-    g.k_chunk = (int)rup((T + pns - 1) / pns, 32);
-    const int ns = (int)((T + g.k_chunk - 1) / g.k_chunk);
-    JOLT_REQUIRE((long long)nb * ns * ell * Mf <= b.part_elems, JOLT_EWORKSPACE, "split-K buffer too small");
-    g.C = b.part; g.c_ld = Mf; g.c_split = ell * Mf; g.c_bs = (long long)ns * ell * Mf;
-    bool done = false;
-    if (planes) {
+    const long long part_bs = (long long)ns * ell * Mf;
+    for_kv(K, V, [&](int t, const void *X) {
       GemmArgs h = g;
-      h.A = b.pln; h.a_bs = P32 * ell * Tld; h.a_ps = ell * Tld;
-      done = gemm_dma(pl.xmf(), P32, 1, h, nb, ns, st);
-    }
-    if (!done) gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, ns, st);
+      h.B = X;
+      h.a_amax = q_amax ? q_amax + t : nullptr;
+      if (ns <= 1) {
+        h.C = b.Pt + t * ell * Mf; h.c_ld = Mf; h.c_bs = 2 * ell * Mf;
+        h.C2 = b.P2 + t * Mf * ld; h.c2_ld = ld; h.c2_bs = 2 * Mf * ld;
+        h.c_amax = c_amax + t; h.c_amax_bs = 2;
+      } else {
+        h.C = b.part + t * part_bs; h.c_ld = Mf; h.c_split = ell * Mf; h.c_bs = 2 * part_bs;
+      }
+      if (planes) {
+        GemmArgs q = h;
+        q.A = b.pln + t * P32 * ell * Tld; q.a_bs = 2 * P32 * ell * Tld; q.a_ps = ell * Tld;
+        if (gemm_dma(pl.xmf(), P32, 1, q, nkv, ns, st, false)) return;
+      }
+      h.A = Qt + t * ell * Tld;
+      gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), false, h, nkv, ns, st);
+    });
+    if (ns <= 1) return;
     prof.end();
     Stage prof_r("project_reduce", st);
-    reduce_splits_dual(b.part, g.c_bs, g.c_split, ns, (int)ell, (int)Mf, Mf, b.Pt, ell * Mf, Mf, b.P2, Mf * ld, ld,
+    reduce_splits_dual(b.part, part_bs, ell * Mf, ns, (int)ell, (int)Mf, Mf, b.Pt, ell * Mf, Mf, b.P2, Mf * ld, ld,
                        c_amax, nb, st);
   };
   struct Pair {
@@ -752,6 +755,11 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     Stage prof("eigvals_B", st);
     sym_eigvals(b.G64, ell * ell, (int)ell, (int)ell, nb, b.dT, b.eT, b.G64, b.betaT, ell, b.evT, ell, true, st,
                 b.mwg);
+  }
+  // ||X||^2 comes from the feature stage (on the side stream when it runs there)
+  if (xready) {
+    HIP_TRY(hipStreamWaitEvent(st, xready, 0));
+    xready = nullptr;
   }
   flash_spec(b.evT, ell, pl.q, b.norm2, b.specT, pl.nT, nb, st);
   // the fit reads the final basis Y (both layouts) from bufA / bufA2: report it by swapping this
@@ -1149,14 +1157,17 @@ void stage_fit(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const vo
     fill_f32(UTt, (long long)nb * kmax * Tld, 0.f, st);
     sym_eigvecs(b.dT, b.eT, b.G64, b.betaT, T, b.specT, pl.nT, (int)T, d_rT, (int)kmax, nb, b.Zw, kmax * T, b.work,
                 (long long)invit_work_doubles((int)T, (int)kmax), nullptr, UTt, kmax * Tld, (int)Tld, st);
-    GemmArgs g = ga();
-    g.A = UTt; g.a_ld = Tld; g.a_bs = kmax * Tld; g.a_amax_c = 1.f;
-    g.B = b.Xt; g.b_ld = Tld; g.b_bs = Mf * Tld;
-    g.M = (int)kmax; g.N = (int)Mf; g.K = (int)T;
-    g.C = Yp; g.c_ld = Mf; g.c_bs = kmax * Mf;
-    g.C2 = b.YpT; g.c2_ld = kmax; g.c2_bs = Mf * kmax;
-    g.c_amax = amYp; g.m_fastest = 1;
-    gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), true, g, nb, 1, st);
+    // B(k = t, n = (j, d)) = X_j[t][d], the cache as it is (K and V cells in two launches)
+    for_kv(K, V, [&](int t, const void *X) {
+      GemmArgs g = ga();
+      g.A = UTt + t * kmax * Tld; g.a_ld = Tld; g.a_bs = 2 * kmax * Tld; g.a_amax_c = 1.f;
+      g.B = X; g.b_ld = D; g.b_blk = D; g.b_blk_stride = T * D; g.b_bs = pl.cell_elems();
+      g.M = (int)kmax; g.N = (int)Mf; g.K = (int)T;
+      g.C = Yp + t * kmax * Mf; g.c_ld = Mf; g.c_bs = 2 * kmax * Mf;
+      g.C2 = b.YpT + t * Mf * kmax; g.c2_ld = kmax; g.c2_bs = 2 * Mf * kmax;
+      g.c_amax = amYp + t; g.c_amax_bs = 2; g.m_fastest = 1;
+      gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), false, g, nb / 2, 1, st);
+    });
   }
   prof_vec.end();
   // ---- projected feature Gram -> U_d
@@ -1313,7 +1324,6 @@ Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot)
     v.fpart_elems = feature_part_elems(pv, pv.n_cells);
     v.fpart = b.fpart + (long long)slot * v.fpart_elems;
   }
-  v.Xt = (char *)b.Xt + (long long)c0 * pl.GH * D * Tld * pl.c;
   v.Gd64 = b.Gd64 + c0 * D * D;
   v.dD = b.dD + c0 * D;
   v.eD = b.eD + c0 * D;
@@ -1356,19 +1366,10 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
     evs.push_back(e);
     return e;
   };
-  // FlashJoLT with one spectra chain: the transpose of the cache and the feature stage (both
-  // bandwidth-heavy) run on a side stream beside the first Cholesky QR of the token chain (whose
-  // factorisation and triangular-inverse launches leave most of the GPU idle); the token chain
-  // waits for them before its first projection.
+  // FlashJoLT with one spectra chain: the feature stage (bandwidth-heavy) runs on a side stream
+  // beside the first Cholesky QR of the token chain (whose factorisation and triangular-inverse
+  // launches leave most of the GPU idle); the token chain waits for it before it forms the spectrum.
   const bool side = pl.mode == JOLT_FLASH && nv == 1;
-  auto transpose_all = [&](hipStream_t on) {
-    Stage prof("transpose_x", on);
-    const long long cellX = pl.cell_elems(), cellXt = (long long)pl.GH * pl.D * pl.T_ld;
-    for_kv(K, V, [&](int t, const void *X) {
-      transpose_x(X, (char *)b.Xt + (long long)t * cellXt * pl.c, pl.c, pl.T, pl.T_ld, pl.D, pl.GH, pl.n_cells / 2,
-                  cellX, 2 * cellXt, on);
-    });
-  };
   hipEvent_t xready = nullptr;
   std::function<hipEvent_t()> side_work;
   if (side) {
@@ -1377,14 +1378,11 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
       HIP_TRY(hipEventRecord(start, st));
       hipStream_t sx = side_stream(0);
       HIP_TRY(hipStreamWaitEvent(sx, start, 0));
-      transpose_all(sx);
       stage_feature(pl, b, K, V, sx);
       xready = new_event();
       HIP_TRY(hipEventRecord(xready, sx));
       return xready;
     };
-  } else {
-    transpose_all(st);
   }
   if (pl.mode == JOLT_FLASH) {
     gen_omega(b.omegaT, pl.dtype, pl.M, pl.ell, stream_key(pl.sketch_seed, 2), st);
@@ -1424,7 +1422,7 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
     prev_mark = mark;
   }
   // join
-  if (xready) HIP_TRY(hipStreamWaitEvent(st, xready, 0));  // (already waited for by the first projection)
+  if (xready) HIP_TRY(hipStreamWaitEvent(st, xready, 0));  // (already waited for before the spectrum)
   for (int v = 1; v < nv; ++v) {
     hipEvent_t j = new_event();
     HIP_TRY(hipEventRecord(j, streams[v]));

@@ -177,9 +177,15 @@ void gemm(int mf, int sa, bool a_kc, int sb, bool b_kc, const GemmArgs &g, int b
 // the same product for operands that are both contiguous along K (larger wave tiles); called by
 // gemm() after validation
 void gemm_kc(int mf, int sa, int sb, const GemmArgs &g, int batch, int nsplit, hipStream_t st);
-// Products of operands stored as 16-bit planes (pa planes of A at stride a_ps, pb of B), both
-// contiguous along K, fed through LDS by DMA; false (nothing launched) when the shape does not fit.
-bool gemm_dma(int mf, int pa, int pb, const GemmArgs &g, int batch, int nsplit, hipStream_t st);
+// Products of operands stored as 16-bit planes (pa planes of A at stride a_ps, pb of B), A
+// contiguous along K, B along K (b_kc) or along N, fed through LDS by DMA; false (nothing
+// launched) when the shape does not fit.
+bool gemm_dma(int mf, int pa, int pb, const GemmArgs &g, int batch, int nsplit, hipStream_t st, bool b_kc = true);
+// Split-K partials of X^T X for 16-bit row-major X [rows][D] (D = 128; batch stride x_bs elements):
+// C[b][s][m][n] (fp32, batch stride c_bs, split stride D * D) over rows [s k_chunk, (s + 1) k_chunk).
+// False (nothing launched) when the shape does not fit.
+bool xgram_dma(int mf, const void *X, long long x_bs, int rows, int D, float *C, long long c_bs, int k_chunk,
+               int nsplit, int batch, hipStream_t st);
 // fp32 rows [batch][rows][s_ld] -> planes [batch][plane][rows][d_ld] (2 fp16 planes after the
 // power-of-two scale of amax[b * amax_bs], or 3 bf16 planes); columns [cols, cols_pad) zeroed.
 void split_planes(int mf, const float *src, long long s_bs, long long s_ld, int rows, int cols, int cols_pad,

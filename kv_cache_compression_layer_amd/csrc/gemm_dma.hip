@@ -18,6 +18,14 @@
 //     barriers), so a wave's first MFMAs start after two reads instead of after the whole stage.
 // Operands are zero-padded along K to a multiple of 32 in memory; rows past M (N) read a valid
 // row and their results are dropped.
+//
+// B may instead be contiguous along N (BKC = false: B(k, n) at k * b_ld + n, n blocked by b_blk /
+// b_blk_stride), as a token-major cache is for a product that contracts over tokens.  Its stage is
+// then 32 k-rows of the block's 256 columns, each row 16 slots of 16 columns whose order is XOR-
+// permuted by the row (rowswz), and each fragment of 8 consecutive k for one column comes from two
+// transposing LDS reads (ds_read_b64_tr_b16: in every 16-lane group, lane i receives element i % 4
+// of the 64 bits addressed by lane 4 q + i / 4 as its q-th value).  The 16 rows one such read
+// touches sit in 16 different slots, so the reads are free of bank conflicts.
 #include <type_traits>
 
 #include "common.hpp"
@@ -61,6 +69,14 @@ __device__ __forceinline__ void issue(lds16 *__restrict__ dst, i32x4 ra, i32x4 r
   }
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// slot permutation of k-row r of an N-contiguous B stage: any 16 rows {8 g + q + 4 h : g, q < 4}
+// (fixed h) get 16 different values
+__device__ __forceinline__ int rowswz(int r) { return (r & 3) | ((r >> 3) << 2); }
+
 template <class C, int PA, int PB, int TM, int TN>
 struct Frags {
   u32x4 a[PA][TM];
@@ -70,8 +86,8 @@ struct Frags {
 // fragment reads in the order the MFMAs consume them (the first A fragment, the B plane of the
 // first plane product, the rest of that A plane, then the other planes), so the in-order LDS
 // return lets the first MFMAs start after a few reads
-template <class C, int PA, int PB, int TM, int TN>
-__device__ __forceinline__ void read_frags(const lds16 *__restrict__ src, int aoff, int boff,
+template <class C, int PA, int PB, int TM, int TN, bool BKC>
+__device__ __forceinline__ void read_frags(const lds16 *__restrict__ src, int aoff, int boff, const int (&btr)[TN],
                                            Frags<C, PA, PB, TM, TN> &f) {
   constexpr int PB0 = (PB - 1 < C::MAXO - (PA - 1)) ? PB - 1 : (C::MAXO - (PA - 1) > 0 ? C::MAXO - (PA - 1) : 0);
   // (a scheduling barrier after each read pins the issue order, which the scheduler would otherwise
@@ -81,7 +97,15 @@ __device__ __forceinline__ void read_frags(const lds16 *__restrict__ src, int ao
     __builtin_amdgcn_sched_barrier(0);
   };
   auto rb = [&](int p, int j) __attribute__((always_inline)) {
-    f.b[p][j] = *(const lds_u32x4 *)(src + C::ASZ + p * C::BN * DK + j * 16 * DK + boff);
+    if constexpr (BKC) {
+      f.b[p][j] = *(const lds_u32x4 *)(src + C::ASZ + p * C::BN * DK + j * 16 * DK + boff);
+    } else {
+      // k rows r and r + 4 of the lane's 16-lane group (8 consecutive k in all)
+      const lds16 *q = src + C::ASZ + p * C::BN * DK + btr[j];
+      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)q));
+      const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(q + 4 * C::BN)));
+      f.b[p][j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   ra(PA - 1, 0);
@@ -123,10 +147,11 @@ __device__ __forceinline__ void mfmas(const Frags<C, PA, PB, TM, TN> &f, f32x4 (
     }
 }
 
-template <int MF, int PA, int PB, int TM, int TN, int NS, int NWM, int NWN>
+template <int MF, int PA, int PB, int TM, int TN, int NS, int NWM, int NWN, bool BKC>
 __global__ void __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(NWM * NWN / 4, NWM * NWN / 4)))
 gemm_dma_kernel(GemmArgs g) {
   using C = Cfg<MF, PA, PB, TM, TN, NS, NWM, NWN>;
+  static_assert(BKC || C::BN == 256, "an N-contiguous B stage is 16 slots of 16 columns per k-row");
   using F = Frags<C, PA, PB, TM, TN>;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN;
   __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[NS * C::STG];
@@ -187,11 +212,20 @@ gemm_dma_kernel(GemmArgs g) {
         const int c = (p ^ (row >> 1)) & 3;
         const int m = min(m0 + row, g.M - 1);
         go[i] = (uint32_t)((plane * g.a_ps + (long long)m * g.a_ld + c * 8) * 2);
-      } else {
+      } else if constexpr (BKC) {
         const int Gb = G - NGA, plane = Gb / (BN / 16), row = (Gb % (BN / 16)) * 16 + r;
         const int c = (p ^ (row >> 1)) & 3;
         const int n = min(n0 + row, g.N - 1);
         go[i] = (uint32_t)((plane * g.b_ps + (long long)n * g.b_ld + c * 8) * 2);
+      } else {
+        // group = k-rows 2 gb and 2 gb + 1 (512 bytes each); lane l fills 16-byte chunk l % 32 of
+        // row l / 32, i.e. half (l & 1) of physical slot (l % 32) / 2, which holds logical slot
+        // (l % 32) / 2 ^ rowswz(row); columns past N read the last valid chunk (results dropped)
+        const int Gb = G - NGA, plane = Gb / (BN / 16), kr = (Gb % (BN / 16)) * 2 + (lane >> 5);
+        const int ch = lane & 31, slot = (ch >> 1) ^ rowswz(kr);
+        const int n = min(n0 + slot * 16 + (ch & 1) * 8, g.N - 8);
+        const long long nb = (long long)(n / g.b_blk) * g.b_blk_stride + n % g.b_blk;
+        go[i] = (uint32_t)((plane * g.b_ps + (long long)kr * g.b_ld + nb) * 2);
       }
     }
   }
@@ -199,22 +233,34 @@ gemm_dma_kernel(GemmArgs g) {
   // (k -> (k / blk) * stride + k % blk); descriptors cover the whole 32-bit offset range, every
   // offset formed here is inside the operand (checked by the host)
   const i32x4 rsa = make_rsrc(Ab, 0xFFFFFFFFu), rsb = make_rsrc(Bb, 0xFFFFFFFFu);
-  int ak = kbeg % g.a_blk, bk = kbeg % g.b_blk;
+  // (an N-contiguous B advances by 32 rows of b_ld per stage; its blocking is along N)
+  int ak = kbeg % g.a_blk, bk = BKC ? kbeg % g.b_blk : 0;
   uint32_t aso = (uint32_t)(((long long)(kbeg / g.a_blk) * g.a_blk_stride + ak) * 2);
-  uint32_t bso = (uint32_t)(((long long)(kbeg / g.b_blk) * g.b_blk_stride + bk) * 2);
+  uint32_t bso = BKC ? (uint32_t)(((long long)(kbeg / g.b_blk) * g.b_blk_stride + bk) * 2)
+                     : (uint32_t)((long long)kbeg * g.b_ld * 2);
   const uint32_t ajump = (uint32_t)((g.a_blk_stride - g.a_blk) * 2), bjump = (uint32_t)((g.b_blk_stride - g.b_blk) * 2);
+  const uint32_t bstep = BKC ? DK * 2 : (uint32_t)(DK * g.b_ld * 2);
   auto advance = [&]() __attribute__((always_inline)) {
     ak += DK;
     aso += DK * 2;
     if (ak == g.a_blk) { ak = 0; aso += ajump; }
-    bk += DK;
-    bso += DK * 2;
-    if (bk == g.b_blk) { bk = 0; bso += bjump; }
+    bso += bstep;
+    if constexpr (BKC) {
+      bk += DK;
+      if (bk == g.b_blk) { bk = 0; bso += bjump; }
+    }
   };
 
   const int wm = wave / NWN, wn = wave % NWN;
   const int fr = lane & 15, fc = lane >> 4;
   const int aoff = dswz(wm * WM + fr, fc), boff = dswz(wn * WN + fr, fc);
+  // N-contiguous B: half offset of the first transposing read of subtile j (rows 8 (lane / 16) +
+  // (lane / 4) % 4, whose slot permutation is lane / 4; columns 4 (lane % 4) of the slot)
+  int btr[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+    btr[j] = BKC ? 0
+                 : (8 * (lane >> 4) + ((lane >> 2) & 3)) * BN + (((wn * TN + j) ^ (lane >> 2)) << 4) + 4 * (lane & 3);
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -252,7 +298,7 @@ gemm_dma_kernel(GemmArgs g) {
           issue<C>(far, rsa, rsb, aso, bso, go, gi, isa);
           advance();
         }
-        read_frags<C, PA, PB, TM, TN>(cur, aoff, boff, fx);
+        read_frags<C, PA, PB, TM, TN, BKC>(cur, aoff, boff, btr, fx);
         __builtin_amdgcn_sched_barrier(0);
         mfmas<MF, C, PA, PB, TM, TN, 0, TN, true>(fx, acc, 0, 0);
         cur = cur == Llast ? L0 : cur + C::STG;
@@ -299,11 +345,111 @@ gemm_dma_kernel(GemmArgs g) {
   }
 }
 
-template <int MF, int PA, int PB, int TM, int TN, int NS, int NWM, int NWN>
+// Gram C = X^T X of a row-major 16-bit matrix X [rows][128] (one cell of the cache: its slices'
+// token rows one after another), K split over blocks: C[b][s][m][n] = sum over the rows k of split
+// s of X[k][m] X[k][n].  The product contracts over rows, along which X is strided, and both
+// operands are X: each 32-row stage goes global->LDS by DMA once and the fragments of both come
+// from it through transposing LDS reads (as for an N-contiguous B above).  Stage row k keeps its 16
+// chunks of 8 columns with chunk c at position c ^ (2 xsw(k)): the 16 rows one read touches then
+// take 32 different 16-byte positions of a 512-byte window (no bank conflicts).  Rows past `rows`
+// read zero (descriptor bound).  Four waves of 64 x 64 outputs; four stages of 8 KB.
+constexpr int kXgStages = 4;
+__device__ __forceinline__ int xsw(int k) { return ((k >> 1) & 1) | (((k >> 3) & 3) << 1); }
+
+template <int MF>
+__global__ void __launch_bounds__(256) xgram_kernel(const uint16_t *X, long long x_bs, int rows, int k_chunk, float *C,
+                                                    long long c_bs) {
+  constexpr int D = 128, STG = DK * D, NS = kXgStages;  // halves per stage
+  __shared__ __attribute__((aligned(1024))) uint16_t lds_raw[NS * STG];
+  lds16 *const L0 = (lds16 *)lds_raw, *const Llast = L0 + (NS - 1) * STG;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int kbeg = split * k_chunk, kend = min(rows, kbeg + k_chunk);
+  const int nsteps = max(0, (kend - kbeg + DK - 1) / DK);
+  const i32x4 rs = make_rsrc(X + b * x_bs, (uint32_t)((long long)rows * D * 2));
+  // DMA instruction i of a stage (this wave issues i = wave and wave + 4) fills rows 4 i .. 4 i + 3:
+  // lane l writes position l % 16 of row 4 i + l / 16
+  uint32_t go[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int k = 4 * (wave + 4 * u) + (lane >> 4), c = (lane & 15) ^ (2 * xsw(k));
+    go[u] = (uint32_t)(k * D * 2 + c * 16);
+  }
+  uint32_t so = (uint32_t)((long long)kbeg * D * 2);
+  auto issue = [&](lds16 *dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t *)(dst + (wave + 4 * u) * 4 * D), 16,
+                          (int)go[u], (int)so, 0, 0);
+    so += DK * D * 2;
+  };
+  // fragment of 16-column slot s: rows 8 (lane / 16) + (lane / 4) % 4 and 4 below (xsw of both is
+  // lane / 8), columns 4 (lane % 4) .. + 3 of the slot
+  const int wm = wave >> 1, wn = wave & 1;
+  const int rbase = (8 * (lane >> 4) + ((lane >> 2) & 3)) * D + 4 * (lane & 1);
+  int ao[4], bo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ao[i] = rbase + 8 * (2 * ((4 * wm + i) ^ (lane >> 3)) + ((lane >> 1) & 1));
+    bo[i] = rbase + 8 * (2 * ((4 * wn + i) ^ (lane >> 3)) + ((lane >> 1) & 1));
+  }
+  auto frag = [&](const lds16 *q) __attribute__((always_inline)) {
+    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)q));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(q + 4 * D)));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (nsteps > 0) {
+    lds16 *far = L0;
+#pragma unroll
+    for (int q = 0; q < NS - 1; ++q)
+      if (q < nsteps) {
+        issue(far);
+        far += STG;
+      }
+    lds16 *cur = L0;
+    for (int s = 0; s < nsteps; ++s) {
+      wait_stages<2, NS - 2>(min(NS - 2, nsteps - 1 - s));
+      wait_lgkm0();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (s + NS - 1 < nsteps) issue(far);
+      u32x4 a[4], bb[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = frag(cur + ao[i]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bb[j] = frag(cur + bo[j]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<MF>(a[i], bb[j], acc[i][j]);
+      cur = cur == Llast ? L0 : cur + STG;
+      far = far == Llast ? L0 : far + STG;
+    }
+  }
+  float *Cb = C + b * c_bs + (long long)split * D * D;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = 64 * wm + 16 * i + 4 * (lane >> 4), n = 64 * wn + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Cb[(long long)(m + r) * D + n] = acc[i][j][r];
+    }
+}
+
+template <int MF, int PA, int PB, int TM, int TN, int NS, int NWM, int NWN, bool BKC = true>
 void launch_dma(const GemmArgs &g, int batch, int nsplit, hipStream_t st) {
   using C = Cfg<MF, PA, PB, TM, TN, NS, NWM, NWN>;
   const int tiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL((gemm_dma_kernel<MF, PA, PB, TM, TN, NS, NWM, NWN>), dim3(tiles, nsplit, batch), dim3(C::NT), 0, st, g);
+  hipLaunchKernelGGL((gemm_dma_kernel<MF, PA, PB, TM, TN, NS, NWM, NWN, BKC>), dim3(tiles, nsplit, batch), dim3(C::NT), 0,
+                     st, g);
 }
 
 // fp32 rows -> P 16-bit planes with the split of the fp32 GEMM operands (power-of-two scale from
@@ -376,26 +522,38 @@ void split_planes(int mf, const float *src, long long s_bs, long long s_ld, int 
 
 // Returns false (launching nothing) when the product does not fit this path: K ranges must be
 // whole 32-deep stages, every source offset of a batch must fit 32 bits, and only the plane
-// layouts used by the compressor are instantiated.
-bool gemm_dma(int mf, int pa, int pb, const GemmArgs &g0, int batch, int nsplit, hipStream_t st) {
+// layouts used by the compressor are instantiated.  b_kc = false: B(k, n) at k * b_ld plus n
+// blocked by b_blk / b_blk_stride (N a multiple of 8, blocks of whole 8-column chunks).
+bool gemm_dma(int mf, int pa, int pb, const GemmArgs &g0, int batch, int nsplit, hipStream_t st, bool b_kc) {
   GemmArgs g = g0;
   if (nsplit == 1) g.k_chunk = g.K;  // one split covers K (callers leave k_chunk unset then)
   if (g.M <= 0 || g.N <= 0 || batch <= 0 || nsplit <= 0) return true;
   if (g.K % DK != 0 || g.k_chunk <= 0 || g.k_chunk % DK != 0 || (long long)g.k_chunk * nsplit < g.K) return false;
   if (g.inner > 1 || (g.tri & 4)) return false;
-  if (g.a_blk % DK != 0 || g.b_blk % DK != 0) return false;
+  if (g.a_blk % DK != 0 || g.b_blk % (b_kc ? DK : 8) != 0) return false;
+  if (!b_kc && (g.N % 8 != 0 || g.tri != 0)) return false;
   if ((g.a_ld * 2) % 16 != 0 || (g.b_ld * 2) % 16 != 0 || (g.a_ps * 2) % 16 != 0 || (g.b_ps * 2) % 16 != 0) return false;
+  if (!b_kc && (g.b_blk_stride * 2) % 16 != 0) return false;
   auto extent = [](long long rows, long long ld, long long planes, long long ps, long long K, int blk,
                    long long bstride) {
     const long long kmax = (K - 1) / blk * bstride + (K - 1) % blk + 1;
     return ((planes - 1) * ps + (rows - 1) * ld + kmax) * 2;
   };
-  if (extent(g.M, g.a_ld, pa, g.a_ps, g.K, g.a_blk, g.a_blk_stride) >= (1LL << 32) ||
-      extent(g.N, g.b_ld, pb, g.b_ps, g.K, g.b_blk, g.b_blk_stride) >= (1LL << 32))
+  // (an N-contiguous B is the same extent with the roles of rows and K exchanged)
+  const long long bext = b_kc ? extent(g.N, g.b_ld, pb, g.b_ps, g.K, g.b_blk, g.b_blk_stride)
+                              : extent(g.K, g.b_ld, pb, g.b_ps, g.N, g.b_blk, g.b_blk_stride);
+  if (extent(g.M, g.a_ld, pa, g.a_ps, g.K, g.a_blk, g.a_blk_stride) >= (1LL << 32) || bext >= (1LL << 32))
     return false;
   if (((uintptr_t)g.A & 15) || ((uintptr_t)g.B & 15)) return false;
   // 8 waves (4 x 2) of 48 x 128 output each: 192 x 256 blocks; Grams of fp32 rows (both operands
   // in planes) on 48 x 96 wave tiles: 192 x 192 blocks, which tile a 522-row Gram with less padding
+  if (!b_kc) {
+    if (mf == MF_F16 && pa == 2 && pb == 1) launch_dma<MF_F16, 2, 1, 3, 8, 3, 4, 2, false>(g, batch, nsplit, st);
+    else if (mf == MF_BF16 && pa == 3 && pb == 1) launch_dma<MF_BF16, 3, 1, 3, 8, 3, 4, 2, false>(g, batch, nsplit, st);
+    else return false;
+    HIP_LAUNCH_CHECK();
+    return true;
+  }
   if (mf == MF_F16 && pa == 2 && pb == 1) launch_dma<MF_F16, 2, 1, 3, 8, 3, 4, 2>(g, batch, nsplit, st);
   else if (mf == MF_F16 && pa == 2 && pb == 2) launch_dma<MF_F16, 2, 2, 3, 6, 3, 4, 2>(g, batch, nsplit, st);
   else if (mf == MF_BF16 && pa == 3 && pb == 3) launch_dma<MF_BF16, 3, 3, 3, 6, 2, 4, 2>(g, batch, nsplit, st);
@@ -403,6 +561,24 @@ bool gemm_dma(int mf, int pa, int pb, const GemmArgs &g0, int batch, int nsplit,
   else if (mf == MF_BF16 && pa == 3 && pb == 1) launch_dma<MF_BF16, 3, 1, 3, 8, 3, 4, 2>(g, batch, nsplit, st);
   else if (mf == MF_BF16 && pa == 1 && pb == 1) launch_dma<MF_BF16, 1, 1, 3, 8, 4, 4, 2>(g, batch, nsplit, st);
   else return false;
+  HIP_LAUNCH_CHECK();
+  return true;
+}
+
+
+// Gram partials of 16-bit row-major [rows][128] matrices (see xgram_kernel): C[b][s] at
+// b * c_bs + s * 128 * 128, fp32 [128][128].  False (nothing launched) when the shape does not fit.
+bool xgram_dma(int mf, const void *X, long long x_bs, int rows, int D, float *C, long long c_bs, int k_chunk,
+               int nsplit, int batch, hipStream_t st) {
+  if (D != 128 || rows <= 0 || batch <= 0 || nsplit <= 0) return false;
+  if (k_chunk <= 0 || k_chunk % DK != 0 || (long long)k_chunk * nsplit < rows) return false;
+  if ((long long)rows * D * 2 >= (1LL << 31) || ((uintptr_t)X & 15) || (x_bs * 2) % 16 != 0) return false;
+  if (mf == MF_F16)
+    hipLaunchKernelGGL(xgram_kernel<MF_F16>, dim3(nsplit, batch), dim3(256), 0, st, (const uint16_t *)X, x_bs, rows,
+                       k_chunk, C, c_bs);
+  else
+    hipLaunchKernelGGL(xgram_kernel<MF_BF16>, dim3(nsplit, batch), dim3(256), 0, st, (const uint16_t *)X, x_bs, rows,
+                       k_chunk, C, c_bs);
   HIP_LAUNCH_CHECK();
   return true;
 }

@@ -17,9 +17,6 @@ struct FactorCell {
 };
 
 void gen_omega(void *out, int dtype, int M, int ell, uint64_t key, hipStream_t st);
-// per-(l,h) slice transpose of a cell: Xt[b][j][d][t] = X[b][j][t][d], t zero-padded to T_ld
-void transpose_x(const void *X, void *Xt, int elem_bytes, int T, int T_ld, int D, int GH, int batch, long long x_bs,
-                 long long xt_bs, hipStream_t st);
 void fill_f32(float *p, long long n, float v, hipStream_t st);
 // S[s][l] = U_l U_{l+1}^T (k x k, fp64) for consecutive layers of each sequence; U holds k rows of
 // length T (pitch ld) per cell, cells (sequence, layer, K|V) at stride cell_stride
