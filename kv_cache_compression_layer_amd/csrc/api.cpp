@@ -104,6 +104,7 @@ struct Plan {
   int xmf() const { return dtype == JOLT_F16 ? MF_F16 : MF_BF16; }
   int fp32_planes() const { return xmf() == MF_F16 ? 2 : 3; }  // planes of an fp32 operand
   long long pln_cell() const { return (long long)fp32_planes() * ell * std::max<long long>(T_ld, M); }
+  long long apl_cell() const { return (long long)fp32_planes() * ell * rup(ell, 32); }
   int xsrc() const { return dtype == JOLT_F16 ? SRC_F16 : (dtype == JOLT_BF16 ? SRC_BF16 : SRC_F32); }
 };
 
@@ -240,6 +241,9 @@ struct Bufs {
   // 16-bit planes of an fp32 operand of the plane GEMM: Q^T for the projection, Z^T for the
   // power-iteration sketch (used one after the other), [cell][plane][ell][max(T_ld, M)]
   uint16_t *pln;
+  // 16-bit planes of a small fp32 left factor whose product runs on the basis planes (R^{-T} of a
+  // Cholesky-QR apply, the factor rows of U_T): [cell][plane][ell][rup(ell, 32)], columns past ell zero
+  uint16_t *apl;
   // device parameter area
   char *params;
   size_t params_bytes;
@@ -372,6 +376,7 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
     b.Wrows = ar.take<float>((long long)nb * sz.kmax * ld);
     b.Wt = ar.take<float>((long long)nb * sz.kmax * ld);
     b.pln = pl.xsrc() == SRC_F32 ? nullptr : ar.take<uint16_t>((long long)nb * pl.pln_cell());
+    b.apl = pl.xsrc() == SRC_F32 ? nullptr : ar.take<uint16_t>((long long)nb * pl.apl_cell());
   } else {
     b.bufB = ar.take<float>((long long)nb * sz.kmax * pl.T_ld);  // token factor rows
     b.Zt = ar.take<float>((long long)nb * sz.kmax * pl.M);       // token-projected tensor
@@ -591,8 +596,8 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   // comes out non-finite, reported).
   constexpr float kBasisBound = 2.f;
   const int pns = project_splits(pl);
-  // q_amax null: Q^T's planes were split with the scale of kBasisBound
-  auto project = [&](const float *Qt, const float *q_amax, float *c_amax) {
+  // q_amax null: Q^T's planes were split with the scale of kBasisBound; qpl: where they are
+  auto project = [&](const float *Qt, const float *q_amax, float *c_amax, const uint16_t *qpl) {
     const bool planes = tplanes;
     Stage prof("project_gemm", st);
     GemmArgs g = ga();
@@ -622,7 +627,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       }
       if (planes) {
         GemmArgs q = h;
-        q.A = b.pln + t * P32 * ell * Tld; q.a_bs = 2 * P32 * ell * Tld; q.a_ps = ell * Tld;
+        q.A = qpl + t * P32 * ell * Tld; q.a_bs = 2 * P32 * ell * Tld; q.a_ps = ell * Tld;
         if (gemm_dma(pl.xmf(), P32, 1, q, nkv, ns, st, false)) return;
       }
       h.A = Qt + t * ell * Tld;
@@ -652,12 +657,33 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   // written unless `rows` asks for Q = (Q^T)^T too: the next projection reads nothing else.
   // (Projecting Y and applying R^{-1} afterwards would save this product but amplifies the
   // projection's rounding by the condition of Y.)
-  // With the basis planes in use and no row layout asked for, Q^T goes straight into b.pln as the
-  // projection's planes (scale of kBasisBound) instead of fp32.  Returns whether it did.
-  auto orthonormalise = [&](Pair y, Pair q, bool rows) -> bool {
+  // With the basis planes in use and no row layout asked for, Q^T goes straight into 16-bit planes
+  // as the projection's operand (scale of kBasisBound) instead of fp32: on the fp16 plane path the
+  // product reads Y^T from its planes (b.pln) and writes Q^T's planes over q's fp32 buffer (the same
+  // bytes per cell); otherwise it reads Y (fp32) and writes them into b.pln.  Returns where Q^T's
+  // planes are (null: Q^T was written as fp32 to q).
+  auto orthonormalise = [&](Pair y, Pair q, bool rows) -> const uint16_t * {
     chol_only(y);
     Stage prof("cholqr_tall", st);
     const bool to_planes = tplanes && !rows;
+    if (to_planes && pl.xmf() == MF_F16 && P32 == 2 && b.apl) {
+      // A = R^{-T} as planes with K padded to a whole stage (zero columns), B = Y^T's planes (rows past
+      // ell read as its last row, against those zero columns)
+      const long long Kp = rup(ell, 32);
+      split_planes(MF_F16, b.RinvT, ell * ld, ld, (int)ell, (int)ell, (int)Kp, b.apl, 2 * ell * Kp, ell * Kp, Kp, amR,
+                   1, nb, st);
+      uint16_t *qpl = (uint16_t *)q.T;
+      GemmArgs g = ga();
+      g.A = b.apl; g.a_ld = Kp; g.a_ps = ell * Kp; g.a_bs = 2 * ell * Kp; g.a_amax = amR;
+      g.B = b.pln; g.b_ld = Tld; g.b_ps = ell * Tld; g.b_bs = 2 * ell * Tld; g.b_amax = y.am; g.b_krows = (int)ell;
+      g.ab_amax_bs = 1;
+      g.M = (int)ell; g.N = (int)T; g.K = (int)Kp;
+      g.c_ld = Tld;
+      g.Cpl = qpl; g.cpl_ps = ell * Tld; g.cpl_bs = 2 * ell * Tld; g.cpl_amax = kBasisBound; g.cpl_mf = MF_F16;
+      g.m_fastest = 1;
+      g.tri = 4;
+      if (gemm_dma(MF_F16, 2, 2, g, nb, 1, st, false)) return qpl;
+    }
     GemmArgs g = ga();
     g.A = b.RinvT; g.a_ld = ld; g.a_bs = ell * ld; g.a_amax = amR;
     g.B = y.R; g.b_ld = ld; g.b_bs = T * ld; g.b_amax = y.am;
@@ -678,7 +704,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
     g.m_fastest = 1;
     g.tri = 4;
     gemm(MF_F16, SRC_F32, true, SRC_F32, true, g, nb, 1, st);
-    return to_planes;
+    return to_planes ? b.pln : nullptr;
   };
   // The final basis stays implicit: Q = Y R^{-1} is never formed.  Its Gram gives R, the projection
   // runs on Y (P' = Y^T X_(T)), B = Q^T X_(T) = R^{-T} P'^T, and the fit reads Y and R^{-1} instead of
@@ -690,11 +716,11 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   split_basis(Y.T, Y.am);
   for (int it = 0; it < pl.power_iters; ++it) {
     Pair Q = (Y.T == pa.T) ? pb : pa;
-    const bool direct = orthonormalise(Y, Q, false);
+    const uint16_t *qpl = orthonormalise(Y, Q, false);
     if (it == 0 && mark) HIP_TRY(hipEventRecord(mark, st));
-    if (!direct) split_basis(Q.T, Q.am);
+    if (!qpl) split_basis(Q.T, Q.am);
     fill_f32(amP, nb, 0.f, st);
-    project(Q.T, direct ? nullptr : Q.am, amP);
+    project(Q.T, qpl ? nullptr : Q.am, amP, qpl ? qpl : b.pln);
     {
       // Z = orth(P) by Cholesky QR; Z^T feeds the next sketch
       Stage prof_z("cholqr_z", st);
@@ -732,7 +758,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   // B = Q^T X_(T) = R^{-T} P'^T -> H = B B^T (fp64) -> eigenvalues; spectrum = top q + tail entry
   float *amP1 = b.amax + 5 * am;
   fill_f32(amP1, nb, 0.f, st);
-  project(Y.T, Y.am, amP1);
+  project(Y.T, Y.am, amP1, b.pln);
   const float *Bp = b.Zt;
   {
     // B = R^{-T} P'^T ([ell][M]; R^{-T} is lower triangular), into the free Z^T buffer
@@ -1073,7 +1099,24 @@ FactorRows flash_factor_rows(const Plan &pl, Bufs &b, long long kmax, int m, flo
     gemm(MF_F16, SRC_F32, true, SRC_F32, false, w, nb, 1, st);
     fr = FactorRows{b.Wt, amW};
   }
-  // U_T^T = rows^T basis^T (rows of length T); the basis is [T][ell_ld] in bufA2
+  // U_T^T = rows^T basis^T (rows of length T).  On the fp16 plane path the implicit basis Y is read
+  // from its planes (Y^T in b.pln, split with the scale of b.basis_am) and the rows are split into
+  // planes with K padded to a whole stage (zero columns; Y^T rows past ell read as its last row).
+  if (b.basis_implicit && b.pln && b.apl && fr.amax && pl.xmf() == MF_F16 && pl.fp32_planes() == 2 &&
+      pl.T % 32 == 0 && n_views(pl) == 1) {
+    const long long Kp = rup(ell, 32);
+    split_planes(MF_F16, fr.rows, kmax * ld, ld, m, (int)ell, (int)Kp, b.apl, 2 * kmax * Kp, kmax * Kp, Kp, fr.amax,
+                 1, nb, st);
+    GemmArgs g = ga();
+    g.A = b.apl; g.a_ld = Kp; g.a_ps = kmax * Kp; g.a_bs = 2 * kmax * Kp; g.a_amax = fr.amax;
+    g.B = b.pln; g.b_ld = Tld; g.b_ps = ell * Tld; g.b_bs = 2 * ell * Tld; g.b_amax = b.basis_am;
+    g.b_krows = (int)ell;
+    g.ab_amax_bs = 1;
+    g.M = m; g.N = pl.T; g.K = (int)Kp;
+    g.C = UTt; g.c_ld = Tld; g.c_bs = kmax * Tld; g.m_fastest = 1;
+    if (gemm_dma(MF_F16, 2, 2, g, nb, 1, st, false)) return fr;
+  }
+  // otherwise from the fp32 basis, [T][ell_ld] in bufA2
   GemmArgs g = ga();
   g.A = fr.rows; g.a_ld = ld; g.a_bs = kmax * ld; g.a_amax = fr.amax; g.a_amax_c = 1.f;
   g.B = b.bufA2; g.b_ld = ld; g.b_bs = (long long)pl.T * ld;
@@ -1350,6 +1393,7 @@ Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot)
     v.mwg = b.mwg + c0 * (long long)(tridiag_mwg_bytes((int)ell, 1) / sizeof(double));
     v.RinvT = b.RinvT + c0 * ell * ld;
     if (b.pln) v.pln = b.pln + c0 * pl.pln_cell();
+    if (b.apl) v.apl = b.apl + c0 * pl.apl_cell();
   } else if (b.mwg) {
     v.mwg = b.mwg + c0 * (long long)(tridiag_mwg_bytes((int)T, 1) / sizeof(double));
   }

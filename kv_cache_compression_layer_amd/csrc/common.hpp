@@ -168,6 +168,10 @@ struct GemmArgs {
   long long cpl_ps, cpl_bs;
   float cpl_amax;
   int cpl_mf;
+  // (plane-GEMM path, B contiguous along N) rows of B that hold data: 0 = all K rows; else K is that
+  // count rounded up to a whole 32-deep stage, A is zero in the columns past it, and the k-rows of B
+  // past it are read from its last valid row instead (so they never leave B)
+  int b_krows;
 };
 
 // a_kc: A contiguous along K (else along M); b_kc: B contiguous along K (else along N)

@@ -147,7 +147,7 @@ __device__ __forceinline__ void mfmas(const Frags<C, PA, PB, TM, TN> &f, f32x4 (
     }
 }
 
-template <int MF, int PA, int PB, int TM, int TN, int NS, int NWM, int NWN, bool BKC>
+template <int MF, int PA, int PB, int TM, int TN, int NS, int NWM, int NWN, bool BKC, bool OPL>
 __global__ void __launch_bounds__(64 * NWM * NWN) __attribute__((amdgpu_waves_per_eu(NWM * NWN / 4, NWM * NWN / 4)))
 gemm_dma_kernel(GemmArgs g) {
   using C = Cfg<MF, PA, PB, TM, TN, NS, NWM, NWN>;
@@ -183,6 +183,7 @@ gemm_dma_kernel(GemmArgs g) {
   int kend = min(g.K, kbeg + g.k_chunk);
   if (kbeg >= kend && split > 0) return;
   if (g.tri & 2) kend = min(kend, n0 + BN);
+  if (g.tri & 4) kend = min(kend, m0 + BM);         // A lower triangular: A(m, k) = 0 for k > m
   if ((g.tri & 1) && m0 >= n0 + BN) kend = kbeg;  // strictly below the diagonal: zeros
   const int nsteps = max(0, (kend - kbeg + DK - 1) / DK);
 
@@ -262,6 +263,33 @@ gemm_dma_kernel(GemmArgs g) {
     btr[j] = BKC ? 0
                  : (8 * (lane >> 4) + ((lane >> 2) & 3)) * BN + (((wn * TN + j) ^ (lane >> 2)) << 4) + 4 * (lane & 3);
 
+  // Stage q's requests.  An N-contiguous B with fewer valid rows than K (b_krows): in the stage that
+  // holds the last valid row, lanes whose k-row lies past it load that row instead (A is zero in
+  // those columns, so the products add exact zeros and no request leaves B).
+  // (only a B in planes -- a basis, ell rows -- can be ragged; the cache always fills its stages)
+  constexpr bool KCLAMP = !BKC && PB > 1;
+  const int kvalid = (KCLAMP && g.b_krows > 0) ? g.b_krows : 0x7FFFFFFF;
+  const uint32_t brow = (uint32_t)(g.b_ld * 2);
+  auto issue_q = [&](lds16 *dst, int q) __attribute__((always_inline)) {
+    if constexpr (KCLAMP) {
+      const int krem = kvalid - (kbeg + q * DK);  // valid rows in this stage (wave-uniform)
+      if (krem < DK) {
+        uint32_t gt[ND];
+#pragma unroll
+        for (int i = 0; i < ND; ++i) {
+          gt[i] = go[i];
+          if (!((isa >> i) & 1)) {
+            const int kr = ((gi[i] - NGA) % (BN / 16)) * 2 + (lane >> 5);
+            if (kr >= krem) gt[i] -= (uint32_t)(kr - (krem - 1)) * brow;
+          }
+        }
+        issue<C>(dst, rsa, rsb, aso, bso, gt, gi, isa);
+        return;
+      }
+    }
+    issue<C>(dst, rsa, rsb, aso, bso, go, gi, isa);
+  };
+
   f32x4 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -281,7 +309,7 @@ gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
       for (int q = 0; q < NS - 1; ++q)
         if (q < nsteps) {
-          issue<C>(far, rsa, rsb, aso, bso, go, gi, isa);
+          issue_q(far, q);
           advance();
           far += C::STG;
         }
@@ -295,7 +323,7 @@ gemm_dma_kernel(GemmArgs g) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (s + NS - 1 < nsteps) {
-          issue<C>(far, rsa, rsb, aso, bso, go, gi, isa);
+          issue_q(far, s + NS - 1);
           advance();
         }
         read_frags<C, PA, PB, TM, TN, BKC>(cur, aoff, boff, btr, fx);
@@ -308,7 +336,49 @@ gemm_dma_kernel(GemmArgs g) {
   }
 
   const float cs = g.alpha / (ascale * bscale);
-  float *Cb = g.C + (long long)batch * g.c_bs + (long long)bin * g.c_bs2 + (long long)split * g.c_split;
+  if constexpr (OPL) {
+    // Output as two fp16 planes (the split of split_planes, scale of the bound cpl_amax).  The tile is
+    // staged through LDS as fp32 rows (pitch BN + 4: the four rows a store instruction touches fall
+    // in different banks) so that each thread splits 8 consecutive columns of a row and writes 16
+    // bytes to each plane.
+    constexpr int CP = BN + 4;
+    static_assert(BM * CP * 4 <= NS * C::STG * 2, "the output tile fits in the stage buffers");
+    float *ct = (float *)lds_raw;
+    __syncthreads();  // every wave is done reading the last stage
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          ct[(wm * WM + i * 16 + fc * 4 + r) * CP + wn * WN + j * 16 + fr] = acc[i][j][r] * cs;
+    __syncthreads();
+    uint16_t *Pb = g.Cpl + (long long)batch * g.cpl_bs;
+    const float pscale = f16_split_scale(g.cpl_amax);
+    for (int w = tid; w < BM * BN / 8; w += C::NT) {
+      const int row = w / (BN / 8), c8 = (w % (BN / 8)) * 8;
+      const int m = m0 + row, n = n0 + c8;
+      if (m < g.M && n < g.N) {  // (N is a multiple of 8)
+        const float4 x0 = *(const float4 *)(ct + row * CP + c8), x1 = *(const float4 *)(ct + row * CP + c8 + 4);
+        const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        uint16_t h[8][3];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_planes<SRC_F32, MF_F16>(v[e], pscale, h[e]);
+        uint16_t *o = Pb + (long long)m * g.c_ld + n;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          uint4 u;
+          u.x = h[0][p] | ((uint32_t)h[1][p] << 16);
+          u.y = h[2][p] | ((uint32_t)h[3][p] << 16);
+          u.z = h[4][p] | ((uint32_t)h[5][p] << 16);
+          u.w = h[6][p] | ((uint32_t)h[7][p] << 16);
+          *(uint4 *)(o + p * g.cpl_ps) = u;
+        }
+      }
+    }
+    return;
+  }
+  float *Cb = g.C ? g.C + (long long)batch * g.c_bs + (long long)bin * g.c_bs2 + (long long)split * g.c_split : nullptr;
   float *C2b = g.C2 ? g.C2 + (long long)batch * g.c2_bs : nullptr;
   float lmax = 0.f;
 #pragma unroll
@@ -444,12 +514,12 @@ __global__ void __launch_bounds__(256) xgram_kernel(const uint16_t *X, long long
     }
 }
 
-template <int MF, int PA, int PB, int TM, int TN, int NS, int NWM, int NWN, bool BKC = true>
+template <int MF, int PA, int PB, int TM, int TN, int NS, int NWM, int NWN, bool BKC = true, bool OPL = false>
 void launch_dma(const GemmArgs &g, int batch, int nsplit, hipStream_t st) {
   using C = Cfg<MF, PA, PB, TM, TN, NS, NWM, NWN>;
   const int tiles = ((g.M + C::BM - 1) / C::BM) * ((g.N + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL((gemm_dma_kernel<MF, PA, PB, TM, TN, NS, NWM, NWN, BKC>), dim3(tiles, nsplit, batch), dim3(C::NT), 0,
-                     st, g);
+  hipLaunchKernelGGL((gemm_dma_kernel<MF, PA, PB, TM, TN, NS, NWM, NWN, BKC, OPL>), dim3(tiles, nsplit, batch),
+                     dim3(C::NT), 0, st, g);
 }
 
 // fp32 rows -> P 16-bit planes with the split of the fp32 GEMM operands (power-of-two scale from
@@ -529,9 +599,17 @@ bool gemm_dma(int mf, int pa, int pb, const GemmArgs &g0, int batch, int nsplit,
   if (nsplit == 1) g.k_chunk = g.K;  // one split covers K (callers leave k_chunk unset then)
   if (g.M <= 0 || g.N <= 0 || batch <= 0 || nsplit <= 0) return true;
   if (g.K % DK != 0 || g.k_chunk <= 0 || g.k_chunk % DK != 0 || (long long)g.k_chunk * nsplit < g.K) return false;
-  if (g.inner > 1 || (g.tri & 4)) return false;
+  if (g.inner > 1 || ((g.tri & 4) && nsplit != 1)) return false;
   if (g.a_blk % DK != 0 || g.b_blk % (b_kc ? DK : 8) != 0) return false;
-  if (!b_kc && (g.N % 8 != 0 || g.tri != 0)) return false;
+  if (!b_kc && (g.N % 8 != 0 || (g.tri & ~4) != 0)) return false;
+  // ragged B rows: N-contiguous B, one split, K the valid rows rounded up to one stage
+  if (g.b_krows != 0 && (b_kc || pb < 2 || nsplit != 1 || g.b_krows < 1 || g.b_krows > g.K || g.K - g.b_krows >= DK))
+    return false;
+  // plane output: only the N-contiguous fp16 two-plane x two-plane product writes it
+  if (g.Cpl && (g.C2 || g.c_amax || nsplit != 1 || g.cpl_mf != MF_F16 || b_kc || mf != MF_F16 || pa != 2 || pb != 2 ||
+                g.c_ld % 8 != 0 || g.cpl_ps % 8 != 0 || g.cpl_bs % 8 != 0 || ((uintptr_t)g.Cpl & 15)))
+    return false;
+  if (!g.Cpl && !g.C) return false;
   if ((g.a_ld * 2) % 16 != 0 || (g.b_ld * 2) % 16 != 0 || (g.a_ps * 2) % 16 != 0 || (g.b_ps * 2) % 16 != 0) return false;
   if (!b_kc && (g.b_blk_stride * 2) % 16 != 0) return false;
   auto extent = [](long long rows, long long ld, long long planes, long long ps, long long K, int blk,
@@ -548,16 +626,21 @@ bool gemm_dma(int mf, int pa, int pb, const GemmArgs &g0, int batch, int nsplit,
   // 8 waves (4 x 2) of 48 x 128 output each: 192 x 256 blocks; Grams of fp32 rows (both operands
   // in planes) on 48 x 96 wave tiles: 192 x 192 blocks, which tile a 522-row Gram with less padding
   if (!b_kc) {
+    // (fp32 x fp32 products whose B is the basis planes, e.g. R^{-T} Y^T: 128 x 256 blocks, 4 x 2 waves
+    // of 32 x 128, so that three stages of both operands' two planes fit in LDS)
     if (mf == MF_F16 && pa == 2 && pb == 1) launch_dma<MF_F16, 2, 1, 3, 8, 3, 4, 2, false>(g, batch, nsplit, st);
+    else if (mf == MF_F16 && pa == 2 && pb == 2 && g.Cpl)
+      launch_dma<MF_F16, 2, 2, 2, 8, 3, 4, 2, false, true>(g, batch, nsplit, st);
+    else if (mf == MF_F16 && pa == 2 && pb == 2) launch_dma<MF_F16, 2, 2, 2, 8, 3, 4, 2, false>(g, batch, nsplit, st);
     else if (mf == MF_BF16 && pa == 3 && pb == 1) launch_dma<MF_BF16, 3, 1, 3, 8, 3, 4, 2, false>(g, batch, nsplit, st);
     else return false;
     HIP_LAUNCH_CHECK();
     return true;
   }
-  if (mf == MF_F16 && pa == 2 && pb == 1) launch_dma<MF_F16, 2, 1, 3, 8, 3, 4, 2>(g, batch, nsplit, st);
+  if (mf == MF_F16 && pa == 2 && pb == 1) launch_dma<MF_F16, 2, 1, 3, 12, 3, 4, 2>(g, batch, nsplit, st);
   else if (mf == MF_F16 && pa == 2 && pb == 2) launch_dma<MF_F16, 2, 2, 3, 6, 3, 4, 2>(g, batch, nsplit, st);
   else if (mf == MF_BF16 && pa == 3 && pb == 3) launch_dma<MF_BF16, 3, 3, 3, 6, 2, 4, 2>(g, batch, nsplit, st);
-  else if (mf == MF_F16 && pa == 1 && pb == 1) launch_dma<MF_F16, 1, 1, 3, 8, 4, 4, 2>(g, batch, nsplit, st);
+  else if (mf == MF_F16 && pa == 1 && pb == 1) launch_dma<MF_F16, 1, 1, 3, 12, 4, 4, 2>(g, batch, nsplit, st);
   else if (mf == MF_BF16 && pa == 3 && pb == 1) launch_dma<MF_BF16, 3, 1, 3, 8, 3, 4, 2>(g, batch, nsplit, st);
   else if (mf == MF_BF16 && pa == 1 && pb == 1) launch_dma<MF_BF16, 1, 1, 3, 8, 4, 4, 2>(g, batch, nsplit, st);
   else return false;
