@@ -31,11 +31,13 @@
  *     reduces each B B^T matrix with several workgroups that wait for one
  *     another, and the allocation (jolt_compress, jolt_allocate) runs one
  *     workgroup per cell that exchange their picks, so each must have all its
- *     workgroups resident at once.  Those waits are bounded: if the workgroups
- *     cannot all be scheduled in time, the affected cells get NaN spectra
- *     (jolt_compress then fails with JOLT_ENONFINITE) or the allocation fails
- *     with JOLT_EHIP, rather than the call hanging.  One call per device at a
- *     time never meets this.
+ *     workgroups resident at once.  Both are cooperative launches: the runtime
+ *     starts one only if all its workgroups can be resident together, and when
+ *     it refuses, the library runs the one-workgroup form of the same step
+ *     instead (same results, slower).  The waits are also bounded: if the
+ *     workgroups still cannot all be scheduled in time, the affected cells get
+ *     NaN spectra (jolt_compress then fails with JOLT_ENONFINITE) or the
+ *     allocation fails with JOLT_EHIP, rather than the call hanging.
  */
 #ifndef JOLT_H
 #define JOLT_H

@@ -547,11 +547,19 @@ void run_alloc(const AllocArgs &a, hipStream_t st) {
   hipLaunchKernelGGL(alloc_sync_reset_kernel, dim3(1), dim3(1), 0, st, a.out);
   HIP_LAUNCH_CHECK();
   if (multi) {
+    // cooperative launch: the runtime starts it only if all of its workgroups can be resident at once
+    // (each waits for the others' picks after every evaluation); if it refuses, one workgroup runs
+    // the whole allocation (identical decisions and results)
     const WaitPolicy wp = wait_policy();
-    hipLaunchKernelGGL(alloc_mwg_kernel, dim3(a.n_cells), dim3(AT), 0, st, a, wp.spin_limit, wp.target_extra);
-  } else {
-    hipLaunchKernelGGL(alloc_kernel, dim3(1), dim3(AT), 0, st, a);
+    AllocArgs a_ = a;
+    unsigned sl_ = wp.spin_limit, te_ = wp.target_extra;
+    void *args[] = {&a_, &sl_, &te_};
+    if (hipLaunchCooperativeKernel((const void *)alloc_mwg_kernel, dim3(a.n_cells), dim3(AT), args, 0, st) ==
+        hipSuccess)
+      return;
+    (void)hipGetLastError();
   }
+  hipLaunchKernelGGL(alloc_kernel, dim3(1), dim3(AT), 0, st, a);
   HIP_LAUNCH_CHECK();
 }
 

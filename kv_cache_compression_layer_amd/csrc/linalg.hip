@@ -1569,9 +1569,24 @@ void sym_eigvals(double *A, long long a_bs, int lda, int n, int batch, double *d
     HIP_LAUNCH_CHECK();
     for (int b0 = 0; b0 < batch; b0 += chunk) {
       const int nm = std::min(chunk, batch - b0);
-      hipLaunchKernelGGL(tridiag_mwg_kernel, dim3(nm * P), dim3(LT), shm_m, st, A + b0 * a_bs, a_bs, lda, n, P,
-                         d + b0 * t_bs, e + b0 * t_bs, refl + b0 * t_bs * (long long)n, beta + b0 * t_bs, t_bs,
-                         mwg + b0 * ms, wp.spin_limit, wp.target_extra);
+      // cooperative launch: the runtime starts it only if every workgroup of the grid can be resident at
+      // once (the per-step exchange waits on all of a matrix's workgroups); if it refuses, the chunk
+      // takes the one-workgroup-per-matrix reduction (same reflectors up to rounding order)
+      const double *a_ = A + b0 * a_bs;
+      double *d_ = d + b0 * t_bs, *e_ = e + b0 * t_bs, *r_ = refl + b0 * t_bs * (long long)n, *be_ = beta + b0 * t_bs;
+      double *x_ = mwg + b0 * ms;
+      long long a_bs_ = a_bs, t_bs_ = t_bs;
+      int lda_ = lda, n_ = n, P_ = P;
+      unsigned sl_ = wp.spin_limit, te_ = wp.target_extra;
+      void *args[] = {&a_, &a_bs_, &lda_, &n_, &P_, &d_, &e_, &r_, &be_, &t_bs_, &x_, &sl_, &te_};
+      if (hipLaunchCooperativeKernel((const void *)tridiag_mwg_kernel, dim3(nm * P), dim3(LT), args, (unsigned)shm_m,
+                                     st) == hipSuccess)
+        continue;
+      (void)hipGetLastError();
+      const size_t shm_up = (5 * (size_t)n + 64 * TCH * (LT / 64)) * sizeof(double);
+      JOLT_REQUIRE(shm_up <= 150 * 1024, JOLT_EHIP, "eigensolver: cooperative launch refused, no fallback fits");
+      hipLaunchKernelGGL(tridiag_fused_kernel<true>, dim3(nm), dim3(LT), shm_up, st, A + b0 * a_bs, a_bs, lda, n, d_, e_,
+                         r_, be_, t_bs, evals + b0 * ev_bs, ev_bs, clamp ? 1 : 0);
       HIP_LAUNCH_CHECK();
     }
   } else {
