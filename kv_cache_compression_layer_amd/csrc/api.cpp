@@ -105,6 +105,11 @@ struct Plan {
   int fp32_planes() const { return xmf() == MF_F16 ? 2 : 3; }  // planes of an fp32 operand
   long long pln_cell() const { return (long long)fp32_planes() * ell * std::max<long long>(T_ld, M); }
   long long apl_cell() const { return (long long)fp32_planes() * ell * rup(ell, 32); }
+  // FlashJoLT keeps its bases' row layout ([T][ell_ld]) only when some product reads it: with fp16
+  // planes and at least one power iteration, every such product runs on the basis planes instead
+  bool rows_layout() const {
+    return !(xsrc() != SRC_F32 && xmf() == MF_F16 && fp32_planes() == 2 && T % 32 == 0 && power_iters >= 1);
+  }
   int xsrc() const { return dtype == JOLT_F16 ? SRC_F16 : (dtype == JOLT_BF16 ? SRC_BF16 : SRC_F32); }
 };
 
@@ -229,6 +234,8 @@ struct Bufs {
   int basis_implicit;
   float *basis_am;
   float *Wt;
+  // whether the bases' row layout ([T][ell_ld], bufA2 / bufB2) exists (Plan::rows_layout)
+  int rows_layout;
   // fit
   float *Wrows, *Udrows, *Cp, *Udr, *Cr, *Vt, *Bcat, *bamax, *Qf, *Qtf;
   uint16_t *Bpl;  // 16-bit planes of Bcat, [cell][plane][GH][D][Kb]
@@ -365,8 +372,9 @@ Bufs carve(Arena &ar, const Plan &pl, const Sizes &sz) {
     b.omegaT = ar.take<char>(ell * pl.M * pl.c);
     b.bufA = ar.take<float>((long long)nb * ell * pl.T_ld);
     b.bufB = ar.take<float>((long long)nb * ell * pl.T_ld);
-    b.bufA2 = ar.take<float>((long long)nb * pl.T * ld);
-    b.bufB2 = ar.take<float>((long long)nb * pl.T * ld);
+    b.rows_layout = pl.rows_layout();
+    b.bufA2 = b.rows_layout ? ar.take<float>((long long)nb * pl.T * ld) : nullptr;
+    b.bufB2 = b.rows_layout ? ar.take<float>((long long)nb * pl.T * ld) : nullptr;
     b.Pt = ar.take<float>((long long)nb * ell * pl.M);
     b.P2 = ar.take<float>((long long)nb * pl.M * ld);
     b.Zt = ar.take<float>((long long)nb * ell * pl.M);
@@ -543,9 +551,11 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
   float *amY = b.amax, *amR = b.amax + am, *amQ = b.amax + 2 * am, *amP = b.amax + 3 * am, *amZ = b.amax + 4 * am;
   // (Omega is generated and the amax slots are cleared once for all cells by spectra_all)
 
-  // Y^T = A X_(T)^T with A = Omega^T (cache dtype) or Z^T (fp32); also Y = (Y^T)^T.  On the plane
-  // path an fp32 A is first split into its 16-bit planes (the split the GEMM would make on the fly).
+  // Y^T = A X_(T)^T with A = Omega^T (cache dtype) or Z^T (fp32); also Y = (Y^T)^T when the row layout
+  // is kept.  On the plane path an fp32 A is first split into its 16-bit planes (the split the GEMM
+  // would make on the fly).
   const int P32 = pl.fp32_planes();
+  JOLT_REQUIRE(b.rows_layout || (b.pln && b.apl), JOLT_EINVAL, "basis planes missing");
   const bool dma_ok = b.pln != nullptr;
   auto sketch = [&](const void *A, int a_src, long long a_bs, const float *a_amax, float *outT, float *outR,
                     float *c_amax) {
@@ -564,7 +574,9 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       g.a_amax = a_amax ? a_amax + t : nullptr; g.ab_amax_bs = 2;
       g.b_ld = pl.D; g.b_blk = pl.D; g.b_blk_stride = T * pl.D; g.b_bs = cellX;
       g.C = outT + t * ell * Tld; g.c_ld = Tld; g.c_bs = 2 * ell * Tld;
-      g.C2 = outR + t * T * ld; g.c2_ld = ld; g.c2_bs = 2 * T * ld;
+      if (b.rows_layout) {
+        g.C2 = outR + t * T * ld; g.c2_ld = ld; g.c2_bs = 2 * T * ld;
+      }
       g.c_amax = c_amax ? c_amax + t : nullptr; g.c_amax_bs = 2;
       g.m_fastest = 1;
       if (planes) {
@@ -684,6 +696,7 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
       g.tri = 4;
       if (gemm_dma(MF_F16, 2, 2, g, nb, 1, st, false)) return qpl;
     }
+    JOLT_REQUIRE(b.rows_layout, JOLT_EINVAL, "basis apply: the plane product was refused and no row layout exists");
     GemmArgs g = ga();
     g.A = b.RinvT; g.a_ld = ld; g.a_bs = ell * ld; g.a_amax = amR;
     g.B = y.R; g.b_ld = ld; g.b_bs = T * ld; g.b_amax = y.am;
@@ -1117,6 +1130,7 @@ FactorRows flash_factor_rows(const Plan &pl, Bufs &b, long long kmax, int m, flo
     if (gemm_dma(MF_F16, 2, 2, g, nb, 1, st, false)) return fr;
   }
   // otherwise from the fp32 basis, [T][ell_ld] in bufA2
+  JOLT_REQUIRE(b.rows_layout, JOLT_EINVAL, "token factor: the plane product was refused and no row layout exists");
   GemmArgs g = ga();
   g.A = fr.rows; g.a_ld = ld; g.a_bs = kmax * ld; g.a_amax = fr.amax; g.a_amax_c = 1.f;
   g.B = b.bufA2; g.b_ld = ld; g.b_bs = (long long)pl.T * ld;
@@ -1384,8 +1398,8 @@ Bufs cell_view(const Bufs &b, const Plan &pl, const Sizes &sz, int c0, int slot)
   if (pl.mode == JOLT_FLASH) {
     v.bufA = b.bufA + c0 * ell * Tld;
     v.bufB = b.bufB + c0 * ell * Tld;
-    v.bufA2 = b.bufA2 + c0 * T * ld;
-    v.bufB2 = b.bufB2 + c0 * T * ld;
+    v.bufA2 = b.bufA2 ? b.bufA2 + c0 * T * ld : nullptr;
+    v.bufB2 = b.bufB2 ? b.bufB2 + c0 * T * ld : nullptr;
     v.Pt = b.Pt + c0 * ell * M;
     v.P2 = b.P2 + c0 * M * ld;
     v.Zt = b.Zt + c0 * ell * M;
@@ -1459,6 +1473,7 @@ void spectra_all(const Plan &pl, Bufs &b, const Sizes &sz, const void *K, const 
       if (v == 0) {  // every view takes the same path; the amax slot pointers of view 0 span all cells
         b.basis_implicit = bv.basis_implicit;
         b.basis_am = bv.basis_am;
+        b.rows_layout = bv.rows_layout;
       }
     } else {
       stage_exact(pv, bv, Kv, Vv, sv);
