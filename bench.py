@@ -63,7 +63,7 @@ LAUNCHES_PER_RECORD = {"sketch_gemm": 2, "project_gemm": 2, "feature_gram": 2}
 # (its grid for the 8B shape, or the largest grid of that kernel) and the sources its code and launch
 # come from (the counters stand only while these hash the same).
 TRAFFIC_KERNELS = {
-    "project_gemm": {"name": "gemm_dma_kernel<0, 2, 1, 3, 8, 3, 4, 2, false>", "grid": 3 * 16 * 512 * 8 * 4,
+    "project_gemm": {"name": "gemm_dma_kernel<0, 2, 1, 3, 8, 3, 4, 2, false, false>", "grid": 3 * 16 * 512 * 8 * 4,
                      "sources": ["kv_cache_compression_layer_amd/csrc/gemm_dma.hip",
                                  "kv_cache_compression_layer_amd/csrc/gemm_core.hpp",
                                  "kv_cache_compression_layer_amd/csrc/dma.hpp",
