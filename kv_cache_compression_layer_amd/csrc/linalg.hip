@@ -867,89 +867,76 @@ __global__ void __launch_bounds__(64) invit_kernel(const double *d_in, const dou
     double sc = 1.0;
     double scale = 0.0;
     for (int iter = 0; iter < 3; ++iter) {
-      // apply L^{-1} P: za -> zb (the running entry stays in a register); the operands of the
-      // next IP steps are loaded while the current ones are used (deep enough to cover a memory
-      // round trip: the whole chain is one thread's)
-      constexpr int IP = 8;
+      // apply L^{-1} P: za -> zb (the running entry stays in a register).  The operands of row
+      // i + LP are requested as soon as row i has used its slot of a ring of LP (the whole chain is
+      // one thread's, so the depth of that ring is what covers a memory round trip); the iterate is
+      // scaled by sc where it is used, not where it is loaded, so no load is waited for early.
       double cur = za[j] * sc;
       {
-        double cl[IP], cn[IP], nl[IP], nn[IP];
-        unsigned char cp[IP], np[IP];
-        auto fetch = [&](int i0, double (&l)[IP], double (&x)[IP], unsigned char (&pv)[IP]) __attribute__((always_inline)) {
-#pragma unroll
-          for (int t = 0; t < IP; ++t) {
-            const int i = i0 + t;
-            const bool ok = i < n - 1;
-            l[t] = ok ? Xv[(long long)i * kmax + j] : 0.0;
-            x[t] = ok ? za[(long long)(i + 1) * kmax + j] * sc : 0.0;
-            pv[t] = ok ? piv[(long long)i * kmax + j] : (unsigned char)0;
-          }
+        constexpr int LP = 16;
+        double rl[LP], rx[LP];
+        unsigned char rp[LP];
+        // (rows past the last one are clamped to it: always a valid load, never consumed)
+        auto load = [&](int t, int i) __attribute__((always_inline)) {
+          const long long r = min(i, n - 2);
+          rl[t] = Xv[r * kmax + j];
+          rx[t] = za[(r + 1) * kmax + j];
+          rp[t] = piv[r * kmax + j];
         };
-        fetch(0, cl, cn, cp);
-        for (int i0 = 0; i0 < n - 1; i0 += IP) {
-          fetch(i0 + IP, nl, nn, np);
+        if (n >= 2) {
 #pragma unroll
-          for (int t = 0; t < IP; ++t) {
+          for (int t = 0; t < LP; ++t) load(t, t);
+        }
+        for (int i0 = 0; i0 < n - 1; i0 += LP) {
+#pragma unroll
+          for (int t = 0; t < LP; ++t) {
             const int i = i0 + t;
             if (i < n - 1) {
-              if (cp[t]) {
-                zb[(long long)i * kmax + j] = cn[t];
-                cur = cur - cl[t] * cn[t];
+              const double x = rx[t] * sc;
+              if (rp[t]) {
+                zb[(long long)i * kmax + j] = x;
+                cur = cur - rl[t] * x;
               } else {
                 zb[(long long)i * kmax + j] = cur;
-                cur = cn[t] - cl[t] * cur;
+                cur = x - rl[t] * cur;
               }
             }
-          }
-#pragma unroll
-          for (int t = 0; t < IP; ++t) {
-            cl[t] = nl[t];
-            cn[t] = nn[t];
-            cp[t] = np[t];
+            load(t, i + LP);
           }
         }
       }
       zb[(long long)(n - 1) * kmax + j] = cur;
-      // back substitution with U (bands u0, u1, u2): zb -> za, same prefetching
+      // back substitution with U (bands u0, u1, u2): zb -> za, the same ring of row operands
       double z1 = 0.0, z2 = 0.0;  // z[i + 1], z[i + 2]
       scale = 0.0;
       {
-        constexpr int IP = 8;
-        double c0[IP], c1[IP], c2[IP], cz[IP], n0[IP], n1[IP], n2[IP], nz[IP];
-        auto fetch = [&](int i0, double (&u0)[IP], double (&u1)[IP], double (&u2)[IP], double (&x)[IP]) __attribute__((always_inline)) {
-#pragma unroll
-          for (int t = 0; t < IP; ++t) {
-            const int i = i0 - t;
-            const bool ok = i >= 0;
-            u0[t] = ok ? U0[(long long)i * kmax + j] : 1.0;
-            u1[t] = ok ? U1[(long long)i * kmax + j] : 0.0;
-            u2[t] = ok ? U2[(long long)i * kmax + j] : 0.0;
-            x[t] = ok ? zb[(long long)i * kmax + j] : 0.0;
-          }
+        constexpr int UP = 12;
+        double r0[UP], r1[UP], r2[UP], rz[UP];
+        // (rows before the first are clamped to it: always a valid load, never consumed)
+        auto load = [&](int t, int i) __attribute__((always_inline)) {
+          const long long r = max(i, 0);
+          r0[t] = U0[r * kmax + j];
+          r1[t] = U1[r * kmax + j];
+          r2[t] = U2[r * kmax + j];
+          rz[t] = zb[r * kmax + j];
         };
-        fetch(n - 1, c0, c1, c2, cz);
-        for (int i0 = n - 1; i0 >= 0; i0 -= IP) {
-          fetch(i0 - IP, n0, n1, n2, nz);
 #pragma unroll
-          for (int t = 0; t < IP; ++t) {
+        for (int t = 0; t < UP; ++t) load(t, n - 1 - t);
+        for (int i0 = n - 1; i0 >= 0; i0 -= UP) {
+#pragma unroll
+          for (int t = 0; t < UP; ++t) {
             const int i = i0 - t;
             if (i >= 0) {
-              double sv = cz[t];
-              if (i + 1 < n) sv -= c1[t] * z1;
-              if (i + 2 < n) sv -= c2[t] * z2;
-              const double zi = sv * c0[t];
+              double sv = rz[t];
+              if (i + 1 < n) sv -= r1[t] * z1;
+              if (i + 2 < n) sv -= r2[t] * z2;
+              const double zi = sv * r0[t];
               za[(long long)i * kmax + j] = zi;
               scale = fmax(scale, fabs(zi));
               z2 = z1;
               z1 = zi;
             }
-          }
-#pragma unroll
-          for (int t = 0; t < IP; ++t) {
-            c0[t] = n0[t];
-            c1[t] = n1[t];
-            c2[t] = n2[t];
-            cz[t] = nz[t];
+            load(t, i - UP);
           }
         }
       }
