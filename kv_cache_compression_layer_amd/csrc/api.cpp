@@ -642,6 +642,8 @@ void stage_flash(const Plan &pl, Bufs &b, const void *K, const void *V, hipStrea
         q.A = qpl + t * P32 * ell * Tld; q.a_bs = 2 * P32 * ell * Tld; q.a_ps = ell * Tld;
         if (gemm_dma(pl.xmf(), P32, 1, q, nkv, ns, st, false)) return;
       }
+      // (planes written by the apply over Q's buffer have no fp32 copy to fall back on)
+      JOLT_REQUIRE(!planes || qpl == b.pln, JOLT_EINVAL, "projection: the plane product was refused");
       h.A = Qt + t * ell * Tld;
       gemm(pl.xmf(), SRC_F32, true, pl.xsrc(), false, h, nkv, ns, st);
     });
@@ -1116,7 +1118,7 @@ FactorRows flash_factor_rows(const Plan &pl, Bufs &b, long long kmax, int m, flo
   // from its planes (Y^T in b.pln, split with the scale of b.basis_am) and the rows are split into
   // planes with K padded to a whole stage (zero columns; Y^T rows past ell read as its last row).
   if (b.basis_implicit && b.pln && b.apl && fr.amax && pl.xmf() == MF_F16 && pl.fp32_planes() == 2 &&
-      pl.T % 32 == 0 && n_views(pl) == 1) {
+      pl.T % 32 == 0 && n_views(pl) == 1 && kmax <= ell) {
     const long long Kp = rup(ell, 32);
     split_planes(MF_F16, fr.rows, kmax * ld, ld, m, (int)ell, (int)Kp, b.apl, 2 * kmax * Kp, kmax * Kp, Kp, fr.amax,
                  1, nb, st);
