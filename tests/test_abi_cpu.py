@@ -127,3 +127,27 @@ def test_encode_workspace_bytes_validation():
     lib = jolt.load()
     assert lib.jolt_encode_residual_workspace_bytes(1, 2, 128, 64, 16, 16) > 0
     assert lib.jolt_encode_residual_workspace_bytes(1, 2, 128, 96, 16, 16) == 0
+
+
+def test_flash_workspace_drops_the_basis_row_layout_only_on_the_fp16_plane_path():
+    """The FlashJoLT bases ([ell][T] rows) are kept in a second, transposed layout ([T][ell]) only when a
+    product reads it: on the fp16 plane path with at least one power iteration every such product
+    reads the bases' 16-bit planes, so two T x ell_ld fp32 buffers per cell are not allocated."""
+    L, H, T, D = 8, 4, 4096, 128
+    groups = [0, 4, 8]
+    rT, rd, bits = list(range(8, 129, 8)), list(range(8, 129, 8)), [2, 4, 8]
+
+    def ws(dtype, power_iters, tokens=T):
+        return jolt.Config(1, L, H, tokens, D, dtype, groups, jolt.FLASH, rT, rd, bits, 2.0, oversample=10,
+                           power_iters=power_iters).workspace_bytes()
+
+    qcap = jolt.Config(1, L, H, T, D, jolt.F16, groups, jolt.FLASH, rT, rd, bits, 2.0).token_spectrum_len() - 1
+    ell = qcap + 10
+    rows = 2 * 4 * T * ((ell + 15) // 16 * 16) * 4  # two buffers x 4 cells x T x ell_ld fp32
+    f16_1, f16_0, f16_2 = ws(jolt.F16, 1), ws(jolt.F16, 0), ws(jolt.F16, 2)
+    assert f16_1 == f16_2
+    assert f16_0 - f16_1 == rows
+    # bf16 (three planes, products on the fp32 rows) keeps the row layout: same size with or without it
+    assert ws(jolt.BF16, 1) == ws(jolt.BF16, 0)
+    # ragged T (no plane path for the bases) keeps it as well
+    assert ws(jolt.F16, 1, T - 8) > f16_1
