@@ -1069,24 +1069,35 @@ __global__ void __launch_bounds__(256) backtransform_regs_kernel(const double *Z
       v[t] = (kk >= 0 && p > kk && p < n) ? Rb[(long long)kk * n + p] : 0.0;
     }
   };
-  double v[NC], vn[NC];
-  load_v(n - 3, v);
-  for (int kk = n - 3; kk >= 0; --kk) {
-    load_v(kk - 1, vn);
-    const double bt = bb[kk];
-    if (bt != 0.0) {
+  // reflectors and their beta go through a ring of RD slots: reflector kk is requested RD steps
+  // before it is applied (one step's work is far shorter than a memory round trip)
+  constexpr int RD = 6;
+  double vr[RD][NC], br[RD];
+  auto load_b = [&](int kk) __attribute__((always_inline)) { return kk >= 0 ? bb[kk] : 0.0; };
 #pragma unroll
-      for (int q = 0; q < VPW; ++q) {
-        double s = 0.0;
+  for (int u = 0; u < RD; ++u) {
+    load_v(n - 3 - u, vr[u]);
+    br[u] = load_b(n - 3 - u);
+  }
+  for (int k0 = n - 3; k0 >= 0; k0 -= RD) {
 #pragma unroll
-        for (int t = 0; t < NC; ++t) s += v[t] * z[q][t];
-        const double c = bt * warp_sum_d(s);
+    for (int u = 0; u < RD; ++u) {
+      const int kk = k0 - u;
+      const double bt = br[u];
+      if (kk >= 0 && bt != 0.0) {
 #pragma unroll
-        for (int t = 0; t < NC; ++t) z[q][t] -= c * v[t];
+        for (int q = 0; q < VPW; ++q) {
+          double s = 0.0;
+#pragma unroll
+          for (int t = 0; t < NC; ++t) s += vr[u][t] * z[q][t];
+          const double c = bt * warp_sum_d(s);
+#pragma unroll
+          for (int t = 0; t < NC; ++t) z[q][t] -= c * vr[u][t];
+        }
       }
+      load_v(kk - RD, vr[u]);
+      br[u] = load_b(kk - RD);
     }
-#pragma unroll
-    for (int t = 0; t < NC; ++t) v[t] = vn[t];
   }
   // sign normalisation (largest-magnitude entry positive, first index on ties) and output
 #pragma unroll
