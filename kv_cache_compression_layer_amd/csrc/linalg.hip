@@ -1312,13 +1312,20 @@ __global__ void __launch_bounds__(256) chol_update_kernel(double *Rw, long long 
 // X[:, 16 cb .. 16 cb + 15] in LDS, starts from the diagonal-block inverse and walks the block
 // rows upwards, X_i = -Dinv_i (R[i, >i] X[>i, slab]).  Writes (R^{-1})^T rows as fp32 and folds
 // max |entry| into amax[b] (zeroed by the Cholesky kernel).
-constexpr int SW = 16;  // slab width
+constexpr int SW = 16;   // slab width
+constexpr int TKP = 4;   // k parts of a block row's dot products (8 waves: 2 row tiles x 4 parts)
+constexpr int TKS = 32;  // 4-deep k steps whose R entries a lane requests together
+typedef double td4 __attribute__((ext_vector_type(4)));
 __global__ void __launch_bounds__(512) tri_inv_kernel(const double *Rw, long long r_bs, int n, float *RinvT,
                                                       long long o_bs, int ld_out, float *amax) {
   extern __shared__ double sm[];
+  __shared__ double Tp[TKP][CNB][SW];
   __shared__ double Ts[CNB][SW];
   __shared__ float fred[8];
-  const int cb = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  // the longest chains first: block L takes slab ncb - 1 - L / batch of matrix L % batch
+  const int ncb = gridDim.x, batch = gridDim.y;
+  const int L = blockIdx.x + ncb * blockIdx.y;
+  const int cb = ncb - 1 - L / batch, b = L % batch, tid = threadIdx.x;
   const int c0 = cb * SW, cw = min(SW, n - c0);
   const int rd = c0 / CNB, rows = (rd + 1) * CNB;  // slab rows 0 .. rows-1 (zero past n)
   const double *R = Rw + b * r_bs;
@@ -1331,38 +1338,43 @@ __global__ void __launch_bounds__(512) tri_inv_kernel(const double *Rw, long lon
     Xs[idx] = v;
   }
   __syncthreads();
-  const int q = tid / SW, c = tid % SW;  // 32 x 16 threads
+  const int q = tid / SW, c = tid % SW;  // 32 x 16 threads: the diagonal-block products
+  const int wv = tid >> 6, ln = tid & 63, tile = wv & 1, kp = wv >> 1, lr = ln & 15, lk = ln >> 4;
   for (int i = rd - 1; i >= 0; --i) {
     const int i0 = i * CNB, kbeg = i0 + CNB, kend = min(rows, n);
-    const double *Rrow = R + (long long)(i0 + q) * n;
-    // row q of Dinv_i (upper triangular), loaded now for use after the barrier
+    // row q of Dinv_i (upper triangular), loaded now for use after the barriers
     const double *Di = Dinv + (long long)i * CNB * CNB + q * CNB;
     double dv[CNB];
 #pragma unroll
     for (int p = 0; p < CNB; ++p) dv[p] = Di[p];
-    double t0 = 0.0, t1 = 0.0, t2 = 0.0, t3 = 0.0;
-    int k = kbeg;
-    // 16 entries of the row are loaded before any is used (one memory round trip per 16)
-    for (; k + 16 <= kend; k += 16) {
-      double rv[16];
+    // T = R[i0 .. i0 + 31][kbeg .. kend) X[kbeg .. kend)[slab] on the fp64 matrix cores: wave (tile,
+    // kp) takes rows 16 tile .. 16 tile + 15 and the kp-th share of the 4-deep k steps; lane (lr, lk)
+    // supplies A = R[row lr][k + lk] and B = X[k + lk][column lr], and holds T rows 4 v + lk of its
+    // tile in column lr.  Its R entries for up to TKS steps are requested before the first product.
+    const int nk4 = (kend - kbeg + 3) >> 2, per = (nk4 + TKP - 1) / TKP;
+    const int sbeg = kp * per, send = min(nk4, sbeg + per);
+    const double *Ra = R + (long long)(i0 + 16 * tile + lr) * n;
+    td4 acc = {0.0, 0.0, 0.0, 0.0};
+    for (int s0 = sbeg; s0 < send; s0 += TKS) {
+      double a[TKS];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) rv[u] = Rrow[k + u];
+      for (int u = 0; u < TKS; ++u) {
+        const int k = kbeg + 4 * (s0 + u) + lk;
+        a[u] = (s0 + u < send && k < kend) ? Ra[k] : 0.0;
+      }
 #pragma unroll
-      for (int u = 0; u < 16; u += 4) {
-        t0 += rv[u] * Xs[(k + u) * SW + c];
-        t1 += rv[u + 1] * Xs[(k + u + 1) * SW + c];
-        t2 += rv[u + 2] * Xs[(k + u + 2) * SW + c];
-        t3 += rv[u + 3] * Xs[(k + u + 3) * SW + c];
+      for (int u = 0; u < TKS; ++u) {
+        if (s0 + u < send) {  // (wave-uniform)
+          const int k = kbeg + 4 * (s0 + u) + lk;
+          const double x = (k < kend) ? Xs[k * SW + lr] : 0.0;
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a[u], x, acc, 0, 0, 0);
+        }
       }
     }
-    for (; k + 4 <= kend; k += 4) {
-      t0 += Rrow[k] * Xs[k * SW + c];
-      t1 += Rrow[k + 1] * Xs[(k + 1) * SW + c];
-      t2 += Rrow[k + 2] * Xs[(k + 2) * SW + c];
-      t3 += Rrow[k + 3] * Xs[(k + 3) * SW + c];
-    }
-    for (; k < kend; ++k) t0 += Rrow[k] * Xs[k * SW + c];
-    Ts[q][c] = (t0 + t1) + (t2 + t3);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) Tp[kp][16 * tile + 4 * v + lk][lr] = acc[v];
+    __syncthreads();
+    Ts[q][c] = ((Tp[0][q][c] + Tp[1][q][c]) + Tp[2][q][c]) + Tp[3][q][c];  // the parts in fixed order
     __syncthreads();
     double v = 0.0;
 #pragma unroll
