@@ -1145,6 +1145,9 @@ __global__ void __launch_bounds__(256) backtransform_regs_kernel(const double *Z
 // ---------------------------------------------------------------------------------------------
 constexpr int CNB = 32;
 constexpr int CHOL_MAXN_LDS = 544;
+// accumulator of v_mfma_f64_16x16x4 (lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16] and holds
+// C rows 4 v + l / 16 of column l % 16)
+typedef double td4 __attribute__((ext_vector_type(4)));
 constexpr int CT = 1024;
 
 // The Cholesky factorisation G = R^T R split into launches so that the trailing updates, which
@@ -1273,33 +1276,43 @@ __global__ void __launch_bounds__(256) chol_update_kernel(double *Rw, long long 
     Aj[q][x] = (q < kb && cj < rem) ? W[(long long)(k0 + q) * n + base + cj] : 0.0;
   }
   __syncthreads();
-  // solved panel tiles: P[i][x] = sum_{q <= i} (R_kk^{-1})[q][i] A[q][x]
-  for (int e = tid; e < CNB * 32; e += 256) {
-    const int i = e / 32, x = e % 32;
-    double vi = 0.0, vj = 0.0;
-    for (int q = 0; q <= i; ++q) {
-      const double d = Dv[q * 33 + i];
-      vi += d * Ai[q][x];
-      vj += d * Aj[q][x];
+  // On the fp64 matrix cores, wave w owning output tile (w / 2, w % 2) of 16 x 16:
+  // solved panel tiles P[i][x] = sum_{q <= i} (R_kk^{-1})[q][i] A[q][x] (Dv is zero below its diagonal)
+  const int wv = tid >> 6, ln = tid & 63, lr = ln & 15, lk = ln >> 4;
+  const int ot = (wv >> 1) * 16, ox = (wv & 1) * 16;
+  {
+    td4 pi = {0.0, 0.0, 0.0, 0.0}, pj = pi;
+#pragma unroll
+    for (int ks = 0; ks < CNB; ks += 4) {
+      const double a = Dv[(ks + lk) * 33 + ot + lr];
+      pi = __builtin_amdgcn_mfma_f64_16x16x4f64(a, Ai[ks + lk][ox + lr], pi, 0, 0, 0);
+      pj = __builtin_amdgcn_mfma_f64_16x16x4f64(a, Aj[ks + lk][ox + lr], pj, 0, 0, 0);
     }
-    Pi[i][x] = vi;
-    Pj[i][x] = vj;
-    const int cj = tj * 32 + x;
-    if (ti == tj && i < kb && cj < rem) R[(long long)(k0 + i) * n + base + cj] = vj;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      Pi[ot + 4 * v + lk][ox + lr] = pi[v];
+      Pj[ot + 4 * v + lk][ox + lr] = pj[v];
+    }
   }
   __syncthreads();
-  const int r = tid >> 3, c0 = (tid & 7) * 4;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int q = 0; q < kb; ++q) {
-    const double u = Pi[q][r];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) acc[w] += u * Pj[q][c0 + w];
+  if (ti == tj) {  // the solved tile of R's row block
+    for (int e = tid; e < CNB * 32; e += 256) {
+      const int i = e / 32, x = e % 32, cj = tj * 32 + x;
+      if (i < kb && cj < rem) R[(long long)(k0 + i) * n + base + cj] = Pj[i][x];
+    }
   }
-  const int ii = ti * 32 + r;
+  // trailing tile -= Pi^T Pj (rows of Pi and Pj past kb are zero)
+  {
+    td4 u = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int jj = tj * 32 + c0 + w;
-    if (ii < rem && jj < rem && jj >= ii) W[(long long)(base + ii) * n + base + jj] -= acc[w];
+    for (int ks = 0; ks < CNB; ks += 4)
+      u = __builtin_amdgcn_mfma_f64_16x16x4f64(Pi[ks + lk][ot + lr], Pj[ks + lk][ox + lr], u, 0, 0, 0);
+    const int jj = tj * 32 + ox + lr;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int ii = ti * 32 + ot + 4 * v + lk;
+      if (ii < rem && jj < rem && jj >= ii) W[(long long)(base + ii) * n + base + jj] -= u[v];
+    }
   }
   // the first trailing tile is the next panel's diagonal block, complete now: factor it here
   if (blockIdx.x == 0) {
@@ -1315,7 +1328,6 @@ __global__ void __launch_bounds__(256) chol_update_kernel(double *Rw, long long 
 constexpr int SW = 16;   // slab width
 constexpr int TKP = 4;   // k parts of a block row's dot products (8 waves: 2 row tiles x 4 parts)
 constexpr int TKS = 32;  // 4-deep k steps whose R entries a lane requests together
-typedef double td4 __attribute__((ext_vector_type(4)));
 __global__ void __launch_bounds__(512) tri_inv_kernel(const double *Rw, long long r_bs, int n, float *RinvT,
                                                       long long o_bs, int ld_out, float *amax) {
   extern __shared__ double sm[];
